@@ -1,0 +1,215 @@
+"""CPU oracle for paged-KV decode attention and the paged KV append (f64).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package.  The product path (``paged_kv_decode_04_amd``) never imports it, and this package imports
+nothing from the product path: the two share no code.  Only the seeded input generators
+(``paged_kv_decode_04_amd.workloads``, which hold none of the method's arithmetic) serve both.
+
+The arithmetic lives in ``pkv_oracle.c`` (plain C, binary64, fp16 decoded exactly); this module only marshals
+numpy arrays into it.  Definitions and citations are in that file's header.  Every function here is pinned by
+``tests/test_oracle.py`` against closed forms, hand-derived fixtures under ``tests/golden/``, a contiguous
+brute force, and a library routine (torch's CPU ``scaled_dot_product_attention`` in float64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pkv_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_pkv.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = True) -> str:
+    """Compile pkv_oracle.c with gcc (IEEE semantics: no fast-math) into liboracle_pkv.so."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f64.restype = f64
+        lib.oracle_f16_array_to_f64.argtypes = [P, i64, P]
+        lib.oracle_f16_array_to_f64.restype = None
+        lib.oracle_k_index.argtypes = [i32, i32, i32, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.oracle_k_index.restype = i64
+        lib.oracle_v_index.argtypes = [i32, i32, i32, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.oracle_v_index.restype = i64
+        geom = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f64]
+        lib.oracle_decode_attention.argtypes = geom + [P, i64, P, i32]
+        lib.oracle_decode_attention.restype = ctypes.c_int
+        lib.oracle_attention_weights.argtypes = geom + [i32, i32, P, P]
+        lib.oracle_attention_weights.restype = ctypes.c_int
+        lib.oracle_split_count.argtypes = [i32, i32, i32, i32]
+        lib.oracle_split_count.restype = ctypes.c_int
+        lib.oracle_split_partials.argtypes = geom + [i32, i32, P, P, P]
+        lib.oracle_split_partials.restype = ctypes.c_int
+        lib.oracle_split_combine.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
+        lib.oracle_split_combine.restype = ctypes.c_int
+        lib.oracle_paged_kv_append.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P]
+        lib.oracle_paged_kv_append.restype = i64
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _bits(a: np.ndarray) -> np.ndarray:
+    """fp16 array -> contiguous uint16 view of its bits."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    if a.dtype == np.uint16:
+        return a
+    raise TypeError("expected float16 or uint16 bits, got %s" % a.dtype)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def f16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact binary16 -> binary64 decode of an array of fp16 values or bit patterns."""
+    b = _bits(np.asarray(bits))
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_f16_array_to_f64(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def k_index(num_kv_heads, block_size, head_dim, block, head, offset, dim) -> int:
+    """Flat index of K element (block, kv head, row offset, dim) in k_pool[N][Hkv][BS][D]."""
+    return _load().oracle_k_index(num_kv_heads, block_size, head_dim, block, head, offset, dim)
+
+
+def v_index(num_kv_heads, block_size, head_dim, block, head, offset, dim) -> int:
+    """Flat index of V element (block, kv head, row offset, dim) in v_pool[N][Hkv][D][BS]."""
+    return _load().oracle_v_index(num_kv_heads, block_size, head_dim, block, head, offset, dim)
+
+
+def _geometry(q, k_pool, v_pool, block_tables, context_lens):
+    B, Hq, D = q.shape
+    N, Hkv, BS, D2 = k_pool.shape
+    if D2 != D or v_pool.shape != (N, Hkv, D, BS):
+        raise ValueError("pool shapes %s / %s do not match q %s" % (k_pool.shape, v_pool.shape, q.shape))
+    bt = _i32(block_tables)
+    if bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("block_tables must be [B][M]")
+    cl = _i32(context_lens)
+    if cl.shape != (B,):
+        raise ValueError("context_lens must be [B]")
+    return B, Hq, Hkv, D, BS, N, bt.shape[1], bt, cl
+
+
+def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale, units=None, threads=None):
+    """out[B][Hq][D] (or out[len(units)][D] for a list of (s, hq) units) in float64.
+
+    q: [B][Hq][D] fp16; k_pool: [N][Hkv][BS][D] fp16; v_pool: [N][Hkv][D][BS] fp16;
+    block_tables: [B][M] int32; context_lens: [B] int32 (rows including the newest token).
+    """
+    B, Hq, Hkv, D, BS, N, M, bt, cl = _geometry(q, k_pool, v_pool, block_tables, context_lens)
+    qb, kb, vb = _bits(q), _bits(k_pool), _bits(v_pool)
+    if threads is None:
+        threads = os.cpu_count() or 1
+    if units is None:
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rc = _load().oracle_decode_attention(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(bt), _ptr(cl), B, Hq, Hkv, D, BS,
+                                             N, M, float(scale), None, 0, _ptr(out), int(threads))
+    else:
+        u = _i32(units).reshape(-1, 2)
+        out = np.empty((u.shape[0], D), dtype=np.float64)
+        rc = _load().oracle_decode_attention(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(bt), _ptr(cl), B, Hq, Hkv, D, BS,
+                                             N, M, float(scale), _ptr(u), u.shape[0], _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError("oracle_decode_attention failed (%d): bad geometry or a table entry outside the pool" % rc)
+    return out
+
+
+def attention_weights(q, k_pool, v_pool, block_tables, context_lens, scale, s, hq):
+    """(out[D], weights[L]) for one (sequence, query head): the normalised softmax weights over its rows."""
+    B, Hq, Hkv, D, BS, N, M, bt, cl = _geometry(q, k_pool, v_pool, block_tables, context_lens)
+    qb, kb, vb = _bits(q), _bits(k_pool), _bits(v_pool)
+    L = max(int(cl[s]), 0)
+    out = np.empty(D, dtype=np.float64)
+    w = np.empty(max(L, 1), dtype=np.float64)
+    rc = _load().oracle_attention_weights(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(bt), _ptr(cl), B, Hq, Hkv, D, BS, N,
+                                          M, float(scale), int(s), int(hq), _ptr(out), _ptr(w))
+    if rc != 0:
+        raise ValueError("oracle_attention_weights failed (%d)" % rc)
+    return out, w[:L]
+
+
+def split_count(context_len, block_size, num_splits, chunk_blocks=0) -> int:
+    """Number of non-empty splits of a sequence: ceil(nb / chunk), nb = ceil(L / BS)."""
+    return _load().oracle_split_count(int(context_len), int(block_size), int(num_splits), int(chunk_blocks))
+
+
+def split_partials(q, k_pool, v_pool, block_tables, context_lens, scale, num_splits, chunk_blocks=0):
+    """(O[B][Hq][S][D], m[B][Hq][S], l[B][Hq][S]) in float64; m in the natural-log units of z = scale*q.k."""
+    B, Hq, Hkv, D, BS, N, M, bt, cl = _geometry(q, k_pool, v_pool, block_tables, context_lens)
+    qb, kb, vb = _bits(q), _bits(k_pool), _bits(v_pool)
+    S = int(num_splits)
+    O = np.empty((B, Hq, S, D), dtype=np.float64)
+    m = np.empty((B, Hq, S), dtype=np.float64)
+    l = np.empty((B, Hq, S), dtype=np.float64)
+    rc = _load().oracle_split_partials(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(bt), _ptr(cl), B, Hq, Hkv, D, BS, N, M,
+                                       float(scale), S, int(chunk_blocks), _ptr(O), _ptr(m), _ptr(l))
+    if rc != 0:
+        raise ValueError("oracle_split_partials failed (%d)" % rc)
+    return O, m, l
+
+
+def split_combine(O, m, l, context_lens, block_size, chunk_blocks=0):
+    """out[B][Hq][D] (float64) from split partials; entries of splits past ceil(nb/chunk) are never read."""
+    O = np.ascontiguousarray(O, dtype=np.float64)
+    m = np.ascontiguousarray(m, dtype=np.float64)
+    l = np.ascontiguousarray(l, dtype=np.float64)
+    B, Hq, S, D = O.shape
+    cl = _i32(context_lens)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = _load().oracle_split_combine(_ptr(O), _ptr(m), _ptr(l), _ptr(cl), B, Hq, D, int(block_size), S,
+                                      int(chunk_blocks), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_split_combine failed (%d)" % rc)
+    return out
+
+
+def paged_kv_append(k, v, slot_mapping, k_pool, v_pool) -> int:
+    """In-place append of k, v ([T][Hkv][D] fp16) into the pools; returns the number of skipped slots."""
+    kb, vb = _bits(k), _bits(v)
+    T, Hkv, D = kb.shape
+    N, Hkv2, BS, D2 = k_pool.shape
+    if (Hkv2, D2) != (Hkv, D) or v_pool.shape != (N, Hkv, D, BS):
+        raise ValueError("pool shapes do not match k/v")
+    if not (k_pool.flags.c_contiguous and v_pool.flags.c_contiguous):
+        raise ValueError("pools must be C-contiguous (updated in place)")
+    sm = _i32(slot_mapping)
+    if sm.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    kp = k_pool.view(np.uint16)
+    vp = v_pool.view(np.uint16)
+    n = _load().oracle_paged_kv_append(_ptr(kb), _ptr(vb), _ptr(sm), T, Hkv, D, BS, N, _ptr(kp), _ptr(vp))
+    if n < 0:
+        raise ValueError("oracle_paged_kv_append failed")
+    return int(n)

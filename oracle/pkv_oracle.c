@@ -1,0 +1,458 @@
+/*
+ * pkv_oracle.c -- plain, slow, f64 CPU oracle for paged-KV decode attention and
+ * the paged KV append.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The product path (the HIP
+ * library under paged_kv_decode_04_amd/) never links, loads or calls it, and
+ * this file includes no header of the product path: the two share no code.
+ *
+ * What is computed, and where the pages define it:
+ *
+ *  - Paged KV append.  A new token's K and V rows go to the pool position named
+ *    by its slot; slot = physical_block * block_size + position_in_block.
+ *    [kapsl-backends 0.1.1, src/gguf_native.rs: one_token_compute (the
+ *    launch_kv_write call with physical_block / pos_in_block) and
+ *    forward_batch_decode_greedy (launch_batch_kv_write with per-token
+ *    physical_blocks / pos_in_blocks)]
+ *
+ *  - Paged decode attention.  For sequence s and query head hq:
+ *      out = softmax(scale * q . K^T) . V
+ *    over the context_lens[s] rows of the sequence, row t living in physical
+ *    block block_tables[s][t / block_size] at offset t % block_size.
+ *    [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ *    BackendPagedKv::paged_decode_attention and paged_batched_decode_attention;
+ *    kapsl-backends 0.1.1, src/gguf_native.rs: forward_batch_decode_greedy,
+ *    where context_lens counts the rows after the new token was appended]
+ *    Query head hq reads kv head hq / G with G = num_q_heads / num_kv_heads.
+ *    [cortiq-engine 0.8.80, src/gpu_cuda.rs: the heads-per-kv-head grouping]
+ *
+ *  - Split-K ("flash decoding") partials and their log-sum-exp combine.  The
+ *    pages give only the buffer names partial_out / partial_m / partial_l and
+ *    the two launches [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ *    SplitKScratch and paged_batched_flash_dispatch]; the formulas below are
+ *    the plain reading: per split j, m_j = max z, l_j = sum exp(z - m_j),
+ *    O_j = sum exp(z - m_j) v; then out = sum_j e^(m_j - M) O_j /
+ *    sum_j e^(m_j - M) l_j with M = max_j m_j.
+ *
+ * Pool layouts (the pages do not fix one; this library and the HIP library
+ * both document the same two):
+ *    k_pool[num_blocks][num_kv_heads][block_size][head_dim]
+ *    v_pool[num_blocks][num_kv_heads][head_dim][block_size]
+ *
+ * All arithmetic is IEEE binary64; fp16 inputs are decoded exactly.  No
+ * blocking, fusion or reordering beyond the definitions above.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* IEEE 754 binary16 -> binary64, exact.
+ * sign s, 5-bit exponent e, 10-bit fraction f:
+ *   e == 0      : (-1)^s * f * 2^-24            (zero and subnormals)
+ *   0 < e < 31  : (-1)^s * (1024 + f) * 2^(e-25)
+ *   e == 31     : (-1)^s * inf if f == 0, else NaN                         */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int s = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return s ? -v : v;
+}
+
+void oracle_f16_array_to_f64(const uint16_t *src, int64_t n, double *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = oracle_f16_to_f64(src[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Problem description and the two pool index functions.                */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const uint16_t *q;            /* [B][Hq][D] fp16 bits */
+    const uint16_t *k_pool;       /* [N][Hkv][BS][D] fp16 bits */
+    const uint16_t *v_pool;       /* [N][Hkv][D][BS] fp16 bits */
+    const int32_t *block_tables;  /* [B][M] */
+    const int32_t *context_lens;  /* [B] */
+    int32_t B, Hq, Hkv, D, BS, N, M;
+    double scale;
+} oracle_problem;
+
+/* k_pool element (block b, kv head h, row offset o, dim d) */
+static int64_t k_index(const oracle_problem *P, int64_t b, int h, int o, int d)
+{
+    return ((b * P->Hkv + h) * P->BS + o) * (int64_t)P->D + d;
+}
+
+/* v_pool element (block b, kv head h, row offset o, dim d) */
+static int64_t v_index(const oracle_problem *P, int64_t b, int h, int o, int d)
+{
+    return ((b * P->Hkv + h) * P->D + d) * (int64_t)P->BS + o;
+}
+
+int64_t oracle_k_index(int32_t Hkv, int32_t BS, int32_t D, int64_t b, int h, int o, int d)
+{
+    oracle_problem P;
+    memset(&P, 0, sizeof P);
+    P.Hkv = Hkv; P.BS = BS; P.D = D;
+    return k_index(&P, b, h, o, d);
+}
+
+int64_t oracle_v_index(int32_t Hkv, int32_t BS, int32_t D, int64_t b, int h, int o, int d)
+{
+    oracle_problem P;
+    memset(&P, 0, sizeof P);
+    P.Hkv = Hkv; P.BS = BS; P.D = D;
+    return v_index(&P, b, h, o, d);
+}
+
+/* Physical block of row t of sequence s, or -1 when the table does not name
+ * a valid block for it. */
+static int64_t row_block(const oracle_problem *P, int s, int t)
+{
+    int j = t / P->BS;
+    if (j >= P->M)
+        return -1;
+    int32_t p = P->block_tables[(int64_t)s * P->M + j];
+    if (p < 0 || p >= P->N)
+        return -1;
+    return p;
+}
+
+/* z_t = scale * sum_d q[d] * k_t[d] for rows t in [t0, t1).  Returns 0, or -2
+ * when a row's block is not a valid pool block. */
+static int scores(const oracle_problem *P, int s, int hq, int t0, int t1, double *z)
+{
+    int G = P->Hq / P->Hkv;
+    int hk = hq / G;
+    const uint16_t *q = P->q + ((int64_t)s * P->Hq + hq) * P->D;
+    for (int t = t0; t < t1; ++t) {
+        int64_t p = row_block(P, s, t);
+        if (p < 0)
+            return -2;
+        int o = t % P->BS;
+        double acc = 0.0;
+        for (int d = 0; d < P->D; ++d)
+            acc += oracle_f16_to_f64(q[d]) * oracle_f16_to_f64(P->k_pool[k_index(P, p, hk, o, d)]);
+        z[t - t0] = P->scale * acc;
+    }
+    return 0;
+}
+
+/* One output row: out[0..D) for (s, hq); weights[0..L) (optional) receives
+ * the normalised softmax weights.  L <= 0 gives out = 0. */
+static int attention_unit(const oracle_problem *P, int s, int hq, double *out, double *weights)
+{
+    int L = P->context_lens[s];
+    int G = P->Hq / P->Hkv;
+    int hk = hq / G;
+    for (int d = 0; d < P->D; ++d)
+        out[d] = 0.0;
+    if (L <= 0)
+        return 0;
+    double *z = (double *)malloc(sizeof(double) * (size_t)L);
+    if (!z)
+        return -3;
+    int rc = scores(P, s, hq, 0, L, z);
+    if (rc) {
+        free(z);
+        return rc;
+    }
+    double m = -INFINITY;
+    for (int t = 0; t < L; ++t)
+        if (z[t] > m)
+            m = z[t];
+    double l = 0.0;
+    for (int t = 0; t < L; ++t)
+        l += exp(z[t] - m);
+    for (int t = 0; t < L; ++t) {
+        double w = exp(z[t] - m);
+        int64_t p = row_block(P, s, t);
+        int o = t % P->BS;
+        for (int d = 0; d < P->D; ++d)
+            out[d] += w * oracle_f16_to_f64(P->v_pool[v_index(P, p, hk, o, d)]);
+        if (weights)
+            weights[t] = w / l;
+    }
+    for (int d = 0; d < P->D; ++d)
+        out[d] /= l;
+    free(z);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Threaded driver over (sequence, query head) units.                   */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const oracle_problem *P;
+    const int32_t *units;   /* pairs (s, hq); NULL = every unit in order */
+    int64_t n_units;
+    double *out;            /* [n_units][D] */
+    int64_t next;           /* shared work counter */
+    int rc;
+    pthread_mutex_t lock;
+} unit_pool;
+
+static void *unit_worker(void *arg)
+{
+    unit_pool *W = (unit_pool *)arg;
+    for (;;) {
+        pthread_mutex_lock(&W->lock);
+        int64_t u = W->next++;
+        pthread_mutex_unlock(&W->lock);
+        if (u >= W->n_units)
+            break;
+        int s, hq;
+        if (W->units) {
+            s = W->units[2 * u];
+            hq = W->units[2 * u + 1];
+        } else {
+            s = (int)(u / W->P->Hq);
+            hq = (int)(u % W->P->Hq);
+        }
+        int rc = attention_unit(W->P, s, hq, W->out + u * W->P->D, NULL);
+        if (rc) {
+            pthread_mutex_lock(&W->lock);
+            W->rc = rc;
+            pthread_mutex_unlock(&W->lock);
+        }
+    }
+    return NULL;
+}
+
+static int check_geometry(const oracle_problem *P)
+{
+    if (P->B < 0 || P->Hq <= 0 || P->Hkv <= 0 || P->D <= 0 || P->BS <= 0 || P->N < 0 || P->M < 0)
+        return -1;
+    if (P->Hq % P->Hkv)
+        return -1;
+    return 0;
+}
+
+/* Decode attention for the listed (s, hq) units (or all B*Hq of them when
+ * units is NULL), each row of out[n_units][D] in f64. */
+int oracle_decode_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                            int32_t N, int32_t M, double scale,
+                            const int32_t *units, int64_t n_units, double *out, int32_t n_threads)
+{
+    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale};
+    if (check_geometry(&P))
+        return -1;
+    if (!units)
+        n_units = (int64_t)B * Hq;
+    for (int64_t u = 0; units && u < n_units; ++u)
+        if (units[2 * u] < 0 || units[2 * u] >= B || units[2 * u + 1] < 0 || units[2 * u + 1] >= Hq)
+            return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    unit_pool W;
+    W.P = &P; W.units = units; W.n_units = n_units; W.out = out; W.next = 0; W.rc = 0;
+    pthread_mutex_init(&W.lock, NULL);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    int started = 0;
+    for (int i = 0; i < n_threads; ++i)
+        if (pthread_create(&th[i], NULL, unit_worker, &W) == 0)
+            ++started;
+    if (started == 0)
+        unit_worker(&W);
+    for (int i = 0; i < started; ++i)
+        pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&W.lock);
+    return W.rc;
+}
+
+/* Softmax weights of one unit: weights[0..context_lens[s]) sum to 1. */
+int oracle_attention_weights(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                             int32_t N, int32_t M, double scale, int32_t s, int32_t hq,
+                             double *out, double *weights)
+{
+    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale};
+    if (check_geometry(&P) || s < 0 || s >= B || hq < 0 || hq >= Hq)
+        return -1;
+    return attention_unit(&P, s, hq, out, weights);
+}
+
+/* ------------------------------------------------------------------ */
+/* Split-K partials and combine.                                        */
+/* ------------------------------------------------------------------ */
+
+/* The block range of split j of a sequence with L rows.  Blocks are whole:
+ * nb = ceil(L / BS) blocks, chunk = chunk_blocks if > 0 else ceil(nb / S),
+ * split j covers blocks [j*chunk, min(nb, (j+1)*chunk)).  Returns the number
+ * of non-empty splits, ceil(nb / chunk) (0 when L <= 0). */
+static int split_range(int L, int BS, int S, int chunk_blocks, int j, int *b0, int *b1)
+{
+    if (L <= 0) {
+        *b0 = *b1 = 0;
+        return 0;
+    }
+    int nb = (L + BS - 1) / BS;
+    int chunk = chunk_blocks > 0 ? chunk_blocks : (nb + S - 1) / S;
+    int nvalid = (nb + chunk - 1) / chunk;
+    int lo = j * chunk;
+    int hi = (j + 1) * chunk;
+    if (lo > nb) lo = nb;
+    if (hi > nb) hi = nb;
+    *b0 = lo;
+    *b1 = hi;
+    return nvalid;
+}
+
+int oracle_split_count(int32_t L, int32_t BS, int32_t S, int32_t chunk_blocks)
+{
+    int b0, b1;
+    return split_range(L, BS, S, chunk_blocks, 0, &b0, &b1);
+}
+
+/* Partials for every (s, hq, j): O[B][Hq][S][D], m[B][Hq][S], l[B][Hq][S].
+ * An empty split gives m = -inf, l = 0, O = 0.  m is in the units of z
+ * (natural log domain). */
+int oracle_split_partials(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                          const int32_t *block_tables, const int32_t *context_lens,
+                          int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                          int32_t N, int32_t M, double scale, int32_t S, int32_t chunk_blocks,
+                          double *O, double *m_out, double *l_out)
+{
+    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale};
+    if (check_geometry(&P) || S < 1 || chunk_blocks < 0)
+        return -1;
+    int G = Hq / Hkv;
+    for (int s = 0; s < B; ++s) {
+        int L = context_lens[s];
+        for (int hq = 0; hq < Hq; ++hq) {
+            int hk = hq / G;
+            for (int j = 0; j < S; ++j) {
+                int64_t base = ((int64_t)s * Hq + hq) * S + j;
+                double *Oj = O + base * D;
+                int b0, b1;
+                split_range(L, BS, S, chunk_blocks, j, &b0, &b1);
+                int t0 = b0 * BS;
+                int t1 = b1 * BS < L ? b1 * BS : L;
+                for (int d = 0; d < D; ++d)
+                    Oj[d] = 0.0;
+                if (t1 <= t0) {
+                    m_out[base] = -INFINITY;
+                    l_out[base] = 0.0;
+                    continue;
+                }
+                double *z = (double *)malloc(sizeof(double) * (size_t)(t1 - t0));
+                if (!z)
+                    return -3;
+                int rc = scores(&P, s, hq, t0, t1, z);
+                if (rc) {
+                    free(z);
+                    return rc;
+                }
+                double m = -INFINITY;
+                for (int t = t0; t < t1; ++t)
+                    if (z[t - t0] > m)
+                        m = z[t - t0];
+                double l = 0.0;
+                for (int t = t0; t < t1; ++t) {
+                    double w = exp(z[t - t0] - m);
+                    int64_t p = row_block(&P, s, t);
+                    int o = t % BS;
+                    l += w;
+                    for (int d = 0; d < D; ++d)
+                        Oj[d] += w * oracle_f16_to_f64(v_pool[v_index(&P, p, hk, o, d)]);
+                }
+                m_out[base] = m;
+                l_out[base] = l;
+                free(z);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Log-sum-exp combine of the non-empty splits of each (s, hq):
+ *   M = max_j m_j,  out = sum_j e^(m_j - M) O_j / sum_j e^(m_j - M) l_j
+ * over j < ceil(nb / chunk); entries of later splits are never read.  A
+ * sequence with no rows gives out = 0. */
+int oracle_split_combine(const double *O, const double *m_in, const double *l_in,
+                         const int32_t *context_lens, int32_t B, int32_t Hq, int32_t D,
+                         int32_t BS, int32_t S, int32_t chunk_blocks, double *out)
+{
+    if (B < 0 || Hq <= 0 || D <= 0 || BS <= 0 || S < 1 || chunk_blocks < 0)
+        return -1;
+    for (int s = 0; s < B; ++s) {
+        int nvalid = oracle_split_count(context_lens[s], BS, S, chunk_blocks);
+        if (nvalid > S)
+            return -4; /* the grid has fewer splits than the sequence needs */
+        for (int hq = 0; hq < Hq; ++hq) {
+            int64_t row = (int64_t)s * Hq + hq;
+            double *o = out + row * D;
+            for (int d = 0; d < D; ++d)
+                o[d] = 0.0;
+            if (nvalid == 0)
+                continue;
+            double M = -INFINITY;
+            for (int j = 0; j < nvalid; ++j)
+                if (m_in[row * S + j] > M)
+                    M = m_in[row * S + j];
+            double den = 0.0;
+            for (int j = 0; j < nvalid; ++j) {
+                double a = exp(m_in[row * S + j] - M);
+                den += a * l_in[row * S + j];
+                for (int d = 0; d < D; ++d)
+                    o[d] += a * O[(row * S + j) * D + d];
+            }
+            for (int d = 0; d < D; ++d)
+                o[d] /= den;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Paged KV append.                                                      */
+/* ------------------------------------------------------------------ */
+
+/* Copies k[i][h][:] and v[i][h][:] (fp16 bits, [T][Hkv][D]) to the pool
+ * position of slot_mapping[i]: block slot / BS, row offset slot % BS.  Slots
+ * outside [0, N*BS) are skipped (a negative slot marks padding).  Returns the
+ * number of skipped tokens, or -1 on a bad geometry. */
+int64_t oracle_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping,
+                               int32_t T, int32_t Hkv, int32_t D, int32_t BS, int32_t N,
+                               uint16_t *k_pool, uint16_t *v_pool)
+{
+    if (T < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || N < 0)
+        return -1;
+    oracle_problem P;
+    memset(&P, 0, sizeof P);
+    P.Hkv = Hkv; P.BS = BS; P.D = D; P.N = N;
+    int64_t skipped = 0;
+    for (int i = 0; i < T; ++i) {
+        int64_t slot = slot_mapping[i];
+        if (slot < 0 || slot >= (int64_t)N * BS) {
+            ++skipped;
+            continue;
+        }
+        int64_t b = slot / BS;
+        int o = (int)(slot % BS);
+        for (int h = 0; h < Hkv; ++h)
+            for (int d = 0; d < D; ++d) {
+                int64_t src = ((int64_t)i * Hkv + h) * D + d;
+                k_pool[k_index(&P, b, h, o, d)] = k[src];
+                v_pool[v_index(&P, b, h, o, d)] = v[src];
+            }
+    }
+    return skipped;
+}

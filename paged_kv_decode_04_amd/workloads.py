@@ -1,0 +1,280 @@
+"""Seeded synthetic inputs for paged-KV decode attention and the paged KV append.
+
+The tests, the smoke check and the benchmark draw every input here, and the same host arrays feed both the HIP
+library and the CPU oracle.  This module draws random numbers and builds index structures (context lengths, block
+tables, slot mappings); it holds none of the attention arithmetic and imports neither the oracle nor the HIP binding.
+
+Pool layouts, fixed by the library's header:
+    k_pool[N][Hkv][BS][D] fp16      (one row of D per token)
+    v_pool[N][Hkv][D][BS] fp16      (V stored transposed inside each (block, kv head) tile)
+
+Randomness: numpy PCG64 streams keyed by ``SeedSequence([seed, rotation, tag])``; large arrays are filled in fixed
+chunks of ``_CHUNK`` elements, chunk c from ``SeedSequence([seed, rotation, tag, c])``, so the result does not depend
+on the number of threads.  Values are drawn in float32 and rounded to fp16 (round to nearest even).
+
+The five workloads mirror the shapes the pages' Llama-style models run (the pages publish no dataset or benchmark):
+  c1  tiny:            B=1,   Hq=4,  Hkv=2,  D=64,  BS=16, L=37, pool of 8 blocks, table = 3 distinct ids
+  c2  Llama-3-8B layer B=32,  Hq=32, Hkv=8,  D=128, BS=16, L ~ U{512..2048}
+  c3  long context     B=4,   Hq=32, Hkv=8,  D=128, BS=16, L=32768, q ~ 2*N(0,1)
+  c4  mixed serving    B=256, Hq=64, Hkv=8,  D=128, BS=16, L = clip(round(lognormal(ln 1024, 1)), 1, 16384)
+  c5  MHA wide head    B=128, Hq=16, Hkv=16, D=256, BS=32, L=4096, K/V ~ U(-1,1), scale 1/16
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_CHUNK = 1 << 22
+POISON = 60000.0  # fp16-representable marker for a row that the append must overwrite
+
+SEEDS = {"c1": 0xC0FFEE01, "c2": 0xC0FFEE02, "c3": 0xC0FFEE03, "c4": 0xC0FFEE04, "c5": 0xC0FFEE05}
+
+_TAGS = {"q": 1, "k": 2, "v": 3, "lens": 4, "perm": 5, "knew": 6, "vnew": 7, "choice": 8}
+
+
+def _rng(seed: int, rotation: int, tag: str, *extra: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, rotation, _TAGS[tag], *extra])))
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def fill_f16(out: np.ndarray, seed: int, rotation: int, tag: str, dist: str, scale: float = 1.0) -> np.ndarray:
+    """Fill a C-contiguous float16 array in place with i.i.d. draws: dist 'normal' (N(0,1)) or 'uniform' (U(-1,1)),
+    multiplied by ``scale`` in float32, then rounded to fp16."""
+    if out.dtype != np.float16 or not out.flags.c_contiguous:
+        raise ValueError("fill_f16 needs a C-contiguous float16 array")
+    flat = out.reshape(-1)
+    n = flat.size
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+
+    def work(c: int) -> None:
+        lo = c * _CHUNK
+        hi = min(n, lo + _CHUNK)
+        rng = _rng(seed, rotation, tag, c)
+        buf = np.empty(hi - lo, dtype=np.float32)
+        if dist == "normal":
+            rng.standard_normal(out=buf, dtype=np.float32)
+        elif dist == "uniform":
+            rng.random(out=buf, dtype=np.float32)
+            buf *= np.float32(2.0)
+            buf -= np.float32(1.0)
+        else:
+            raise ValueError(dist)
+        if scale != 1.0:
+            buf *= np.float32(scale)
+        np.copyto(flat[lo:hi], buf, casting="same_kind")
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            work(c)
+    else:
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out
+
+
+@dataclass
+class DecodeCase:
+    """One decode step's inputs.  ``block_tables`` rows are padded with -1 past ceil(L/BS) entries."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    BS: int
+    N: int
+    M: int
+    scale: float
+    context_lens: np.ndarray           # [B] int32, rows including the newest token
+    block_tables: np.ndarray           # [B][M] int32
+    q: Optional[np.ndarray] = None      # [B][Hq][D] fp16
+    k_pool: Optional[np.ndarray] = None  # [N][Hkv][BS][D] fp16
+    v_pool: Optional[np.ndarray] = None  # [N][Hkv][D][BS] fp16
+    k_new: Optional[np.ndarray] = None   # [T][Hkv][D] fp16, the rows appended this step
+    v_new: Optional[np.ndarray] = None   # [T][Hkv][D] fp16
+    slot_mapping: Optional[np.ndarray] = None  # [T] int32
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def num_tokens(self) -> int:
+        return 0 if self.slot_mapping is None else int(self.slot_mapping.shape[0])
+
+
+def carve_tables(context_lens: np.ndarray, BS: int, N: int, M: int, perm: np.ndarray) -> np.ndarray:
+    """Block tables taken consecutively from a permutation of the pool's block ids; unused entries are -1."""
+    B = context_lens.shape[0]
+    bt = np.full((B, M), -1, dtype=np.int32)
+    pos = 0
+    for s in range(B):
+        nb = (int(context_lens[s]) + BS - 1) // BS
+        if nb > M:
+            raise ValueError("sequence %d needs %d blocks > M=%d" % (s, nb, M))
+        bt[s, :nb] = perm[pos:pos + nb]
+        pos += nb
+    if pos > N:
+        raise ValueError("pool of %d blocks is too small for %d table entries" % (N, pos))
+    return bt
+
+
+def newest_row_slots(context_lens: np.ndarray, block_tables: np.ndarray, BS: int) -> np.ndarray:
+    """Slot of each sequence's newest row (position L-1), as the callers on the pages form it:
+    slot = block_tables[s][(L-1) / BS] * BS + (L-1) % BS; -1 for an empty sequence."""
+    B = context_lens.shape[0]
+    slots = np.full(B, -1, dtype=np.int32)
+    for s in range(B):
+        L = int(context_lens[s])
+        if L > 0:
+            slots[s] = int(block_tables[s, (L - 1) // BS]) * BS + (L - 1) % BS
+    return slots
+
+
+def poison_rows(k_pool: np.ndarray, v_pool: np.ndarray, slots: np.ndarray, BS: int) -> None:
+    """Overwrite the pool rows at ``slots`` with POISON in every kv head and dim (layouts as in the module doc)."""
+    for slot in slots:
+        if slot < 0:
+            continue
+        b, o = int(slot) // BS, int(slot) % BS
+        k_pool[b, :, o, :] = POISON
+        v_pool[b, :, :, o] = POISON
+
+
+def _alloc_pools(N, Hkv, BS, D):
+    return (np.empty((N, Hkv, BS, D), dtype=np.float16), np.empty((N, Hkv, D, BS), dtype=np.float16))
+
+
+def build_case(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int, context_lens, N: int, M: int, scale: float,
+               seed: int, rotation: int = 0, q_scale: float = 1.0, kv_dist: str = "normal",
+               with_append: bool = True, poison: bool = False, table_ids: Optional[np.ndarray] = None,
+               with_pools: bool = True) -> DecodeCase:
+    """General builder: pools filled i.i.d., tables carved from a seeded permutation of the N block ids (or given),
+    one appended token per non-empty sequence at its newest row when ``with_append``.  ``with_pools=False`` builds
+    only the lengths, tables and slot mapping (q, pools and new rows stay None)."""
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    if table_ids is None:
+        perm = _rng(seed, rotation, "perm").permutation(N).astype(np.int32)
+    else:
+        perm = np.asarray(table_ids, dtype=np.int32)
+    bt = carve_tables(cl, BS, N, M, perm)
+    if not with_pools:
+        case = DecodeCase(name, B, Hq, Hkv, D, BS, N, M, float(scale), cl, bt)
+        if with_append:
+            slots = newest_row_slots(cl, bt, BS)
+            case.slot_mapping = np.ascontiguousarray(slots[slots >= 0])
+        return case
+    q = fill_f16(np.empty((B, Hq, D), dtype=np.float16), seed, rotation, "q", "normal", q_scale)
+    k_pool, v_pool = _alloc_pools(N, Hkv, BS, D)
+    fill_f16(k_pool, seed, rotation, "k", kv_dist)
+    fill_f16(v_pool, seed, rotation, "v", kv_dist)
+    case = DecodeCase(name, B, Hq, Hkv, D, BS, N, M, float(scale), cl, bt, q, k_pool, v_pool)
+    if with_append:
+        slots = newest_row_slots(cl, bt, BS)
+        keep = slots >= 0
+        slots = np.ascontiguousarray(slots[keep])
+        T = int(slots.shape[0])
+        case.k_new = fill_f16(np.empty((T, Hkv, D), dtype=np.float16), seed, rotation, "knew", kv_dist)
+        case.v_new = fill_f16(np.empty((T, Hkv, D), dtype=np.float16), seed, rotation, "vnew", kv_dist)
+        case.slot_mapping = slots
+        if poison:
+            poison_rows(k_pool, v_pool, slots, BS)
+    return case
+
+
+def pool_blocks_for(context_lens: np.ndarray, BS: int, extra: float = 0.10) -> int:
+    """Pool size = ceil((1 + extra) * sum of per-sequence blocks)."""
+    total = int(sum((int(L) + BS - 1) // BS for L in context_lens))
+    return int(math.ceil((1.0 + extra) * total))
+
+
+def config_c1(rotation: int = 0, with_pools: bool = True) -> DecodeCase:
+    """B=1, 4/2 heads, D=64, BS=16, L=37, pool of 8 blocks, table = 3 distinct seeded ids; one appended token.
+
+    The appended token is the sequence's newest row, position 36 = L-1, written through the table
+    (slot = bt[0][2]*16 + 4)."""
+    seed = SEEDS["c1"]
+    ids = _rng(seed, rotation, "choice").choice(8, size=3, replace=False).astype(np.int32)
+    return build_case("c1", 1, 4, 2, 64, 16, [37], 8, 3, 1.0 / 8.0, seed, rotation, table_ids=ids, poison=True,
+                      with_pools=with_pools)
+
+
+def config_c2(rotation: int = 0, with_pools: bool = True) -> DecodeCase:
+    """Llama-3-8B-shaped layer: B=32, 32/8 heads, D=128, BS=16, L ~ U{512..2048}, pool = blocks + 10%, M=128."""
+    seed = SEEDS["c2"]
+    lens = _rng(seed, rotation, "lens").integers(512, 2048, size=32, endpoint=True).astype(np.int32)
+    N = pool_blocks_for(lens, 16)
+    return build_case("c2", 32, 32, 8, 128, 16, lens, N, 128, 1.0 / math.sqrt(128.0), seed, rotation, poison=True,
+                      with_pools=with_pools)
+
+
+def config_c3(rotation: int = 0, with_pools: bool = True) -> DecodeCase:
+    """Long context: B=4, 32/8 heads, D=128, BS=16, L=32768, N=8192, M=2048, q ~ 2*N(0,1)."""
+    seed = SEEDS["c3"]
+    lens = np.full(4, 32768, dtype=np.int32)
+    return build_case("c3", 4, 32, 8, 128, 16, lens, 8192, 2048, 1.0 / math.sqrt(128.0), seed, rotation,
+                      q_scale=2.0, poison=True, with_pools=with_pools)
+
+
+def c4_context_lens(rotation: int = 0) -> np.ndarray:
+    seed = SEEDS["c4"]
+    raw = _rng(seed, rotation, "lens").lognormal(mean=math.log(1024.0), sigma=1.0, size=256)
+    return np.clip(np.rint(raw), 1, 16384).astype(np.int32)
+
+
+def config_c4(rotation: int = 0, with_pools: bool = True) -> DecodeCase:
+    """Mixed serving batch: B=256, 64/8 heads, D=128, BS=16, lognormal lengths (median 1024, sigma 1, clipped
+    to [1, 16384]); the newest row of every sequence is poisoned, then re-written by the append."""
+    seed = SEEDS["c4"]
+    lens = c4_context_lens(rotation)
+    N = pool_blocks_for(lens, 16)
+    M = int((int(lens.max()) + 15) // 16)
+    return build_case("c4", 256, 64, 8, 128, 16, lens, N, M, 1.0 / math.sqrt(128.0), seed, rotation, poison=True,
+                      with_pools=with_pools)
+
+
+def config_c5(rotation: int = 0, with_pools: bool = True) -> DecodeCase:
+    """MHA wide head: B=128, 16/16 heads, D=256, BS=32, L=4096, N=16384, M=128, K/V ~ U(-1,1), q ~ N(0,1),
+    scale = 1/16."""
+    seed = SEEDS["c5"]
+    lens = np.full(128, 4096, dtype=np.int32)
+    return build_case("c5", 128, 16, 16, 256, 32, lens, 16384, 128, 1.0 / 16.0, seed, rotation,
+                      kv_dist="uniform", poison=True, with_pools=with_pools)
+
+
+CONFIGS = {"c1": config_c1, "c2": config_c2, "c3": config_c3, "c4": config_c4, "c5": config_c5}
+
+
+def small_case(seed: int, B: int, Hq: int, Hkv: int, D: int, BS: int, lens, extra_blocks: int = 3,
+               q_scale: float = 1.0, kv_dist: str = "normal", scale: Optional[float] = None,
+               poison: bool = False, M: Optional[int] = None) -> DecodeCase:
+    """A reduced case of the same structure for parity tests the oracle finishes in seconds."""
+    lens = np.asarray(lens, dtype=np.int32)
+    nbs = [(int(L) + BS - 1) // BS for L in lens]
+    N = sum(nbs) + extra_blocks
+    if M is None:
+        M = max(1, max(nbs) if nbs else 1)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return build_case("small", int(B), Hq, Hkv, D, BS, lens, N, M, scale, seed, 0, q_scale=q_scale,
+                      kv_dist=kv_dist, poison=poison)
+
+
+def algorithmic_bytes(case: DecodeCase) -> dict:
+    """Bytes a decode step must move at minimum: K and V rows actually used, q, out, tables and lengths; the append
+    reads and writes 2*T*Hkv*D fp16 values."""
+    rows = int(np.maximum(case.context_lens, 0).sum())
+    kv = rows * case.Hkv * case.D * 2 * 2
+    qo = 2 * case.B * case.Hq * case.D * 2
+    nb = int(sum((max(int(L), 0) + case.BS - 1) // case.BS for L in case.context_lens))
+    idx = nb * 4 + case.B * 4
+    app = 2 * 2 * case.num_tokens * case.Hkv * case.D * 2 + case.num_tokens * 4
+    return {"kv": kv, "q_out": qo, "index": idx, "attention": kv + qo + idx, "append": app}

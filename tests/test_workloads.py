@@ -1,0 +1,105 @@
+"""The seeded input generators: determinism and the structure each workload promises (no GPU)."""
+import hashlib
+import math
+
+import numpy as np
+import pytest
+
+from paged_kv_decode_04_amd import workloads as W
+
+
+def _digest(*arrays):
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+def _check_tables(c):
+    nbs = [(int(L) + c.BS - 1) // c.BS for L in c.context_lens]
+    used = []
+    for s, nb in enumerate(nbs):
+        row = c.block_tables[s]
+        assert np.all(row[:nb] >= 0) and np.all(row[:nb] < c.N)
+        assert np.all(row[nb:] == -1)
+        used.extend(row[:nb].tolist())
+    assert len(used) == len(set(used)), "blocks shared between sequences"
+    return sum(nbs)
+
+
+def test_fill_is_deterministic_and_thread_independent(monkeypatch):
+    a = W.fill_f16(np.empty(3 * W._CHUNK + 17, np.float16), 5, 0, "k", "normal")
+    b = W.fill_f16(np.empty(3 * W._CHUNK + 17, np.float16), 5, 0, "k", "normal")
+    assert _digest(a) == _digest(b)
+    monkeypatch.setattr(W, "_threads", lambda: 1)
+    c = W.fill_f16(np.empty(3 * W._CHUNK + 17, np.float16), 5, 0, "k", "normal")
+    assert _digest(a) == _digest(c)
+    d = W.fill_f16(np.empty(3 * W._CHUNK + 17, np.float16), 5, 1, "k", "normal")
+    assert _digest(a) != _digest(d)
+
+
+def test_distributions():
+    n = W.fill_f16(np.empty(1 << 20, np.float16), 1, 0, "q", "normal").astype(np.float64)
+    assert abs(n.mean()) < 0.01 and abs(n.std() - 1) < 0.01
+    u = W.fill_f16(np.empty(1 << 20, np.float16), 1, 0, "k", "uniform").astype(np.float64)
+    assert u.min() >= -1 and u.max() <= 1 and abs(u.mean()) < 0.01 and abs(u.var() - 1 / 3) < 0.01
+    s = W.fill_f16(np.empty(1 << 20, np.float16), 1, 0, "q", "normal", 2.0).astype(np.float64)
+    assert abs(s.std() - 2) < 0.02
+
+
+def test_c1_structure():
+    c = W.config_c1()
+    assert (c.B, c.Hq, c.Hkv, c.D, c.BS, c.N, c.M) == (1, 4, 2, 64, 16, 8, 3)
+    assert c.context_lens.tolist() == [37]
+    assert c.scale == 1 / 8
+    assert _check_tables(c) == 3
+    # the appended token is position 36 = L-1: block table entry 2, offset 4
+    assert c.slot_mapping.tolist() == [int(c.block_tables[0, 2]) * 16 + 4]
+    assert c.k_new.shape == (1, 2, 64)
+    b, o = divmod(int(c.slot_mapping[0]), 16)
+    assert np.all(c.k_pool[b, :, o, :] == np.float16(W.POISON))
+    assert np.all(c.v_pool[b, :, :, o] == np.float16(W.POISON))
+    assert _digest(c.q, c.k_pool, c.v_pool) == _digest(*(lambda d: (d.q, d.k_pool, d.v_pool))(W.config_c1()))
+
+
+def test_c2_structure():
+    c = W.config_c2(with_pools=False)
+    assert (c.B, c.Hq, c.Hkv, c.D, c.BS, c.M) == (32, 32, 8, 128, 16, 128)
+    assert c.context_lens.min() >= 512 and c.context_lens.max() <= 2048
+    blocks = _check_tables(c)
+    assert c.N == math.ceil(1.1 * blocks)
+    assert c.scale == pytest.approx(1 / math.sqrt(128))
+    assert c.num_tokens == 32
+    r1 = W.config_c2(rotation=1, with_pools=False)
+    assert not np.array_equal(r1.context_lens, c.context_lens)
+
+
+def test_c3_c4_c5_structure():
+    c3 = W.config_c3(with_pools=False)
+    assert c3.N == 8192 and c3.M == 2048 and np.all(c3.context_lens == 32768)
+    assert _check_tables(c3) == 8192
+    c4 = W.config_c4(with_pools=False)
+    assert c4.B == 256 and c4.Hq == 64 and c4.Hkv == 8
+    assert c4.context_lens.min() >= 1 and c4.context_lens.max() <= 16384
+    med = float(np.median(c4.context_lens))
+    assert 600 < med < 1700  # lognormal with median 1024
+    blocks = _check_tables(c4)
+    assert c4.N == math.ceil(1.1 * blocks)
+    assert c4.M == (int(c4.context_lens.max()) + 15) // 16
+    c5 = W.config_c5(with_pools=False)
+    assert (c5.D, c5.BS, c5.N, c5.M, c5.G) == (256, 32, 16384, 128, 1)
+    assert _check_tables(c5) == 16384
+    assert c5.scale == 1 / 16
+
+
+def test_newest_row_slots_are_distinct_and_in_range():
+    c = W.config_c4(with_pools=False)
+    s = c.slot_mapping
+    assert len(set(s.tolist())) == len(s)
+    assert np.all((s >= 0) & (s < c.N * c.BS))
+
+
+def test_algorithmic_bytes_c3():
+    c = W.config_c3(with_pools=False)
+    b = W.algorithmic_bytes(c)
+    assert b["kv"] == 4 * 32768 * 8 * 128 * 4
