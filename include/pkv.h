@@ -1,0 +1,233 @@
+/*
+ * pkv.h -- C ABI of libpkv: paged-KV decode attention and the paged KV append
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the ones the Rust inference backends on the source pages
+ * launch as CUDA kernels:
+ *   - the paged KV append        [kapsl-backends 0.1.1, src/gguf_native.rs:
+ *                                 launch_kv_write / launch_batch_kv_write in
+ *                                 one_token_compute and forward_batch_decode_greedy]
+ *   - single-token paged decode attention with grouped-query heads
+ *                                [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ *                                 BackendPagedKv::paged_decode_attention,
+ *                                 paged_batched_decode_single_pass;
+ *                                 kapsl-backends 0.1.1: launch_paged_attention]
+ *   - its split-K ("flash decoding") form: per-split f32 partials, then a
+ *     log-sum-exp combine       [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ *                                 SplitKScratch, paged_batched_flash_dispatch]
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers named q, k, v, k_pool, v_pool, out, block_tables, context_lens,
+ *    slot_mapping, partial_*, workspace are DEVICE pointers.  The caller owns
+ *    them; the library never frees or reallocates caller memory.
+ *  - fp16 data is IEEE binary16, passed as uint16_t bit patterns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *    asynchronous on that stream: it enqueues kernels and returns; nothing in
+ *    the library synchronises the host on the hot path.
+ *  - Return value: PKV_OK (0) or a negative PKV_E* code; pkv_last_error()
+ *    returns a thread-local message for the last failing call of the thread.
+ *    Argument checks happen on the host before anything is enqueued, so a
+ *    failing call enqueues nothing.
+ *  - Device-resident indices (block_tables, context_lens, slot_mapping) are
+ *    NOT validated on the host (that would need a device->host copy).  The
+ *    kernels still never touch memory outside the arrays they are given:
+ *    a slot outside [0, N*BS) is skipped, a table entry outside [0, N) makes
+ *    its block contribute nothing, a length above M*BS is treated as M*BS and
+ *    a negative length as 0.  Results for such inputs are unspecified.
+ *
+ * Layouts
+ * -------
+ *    q, out        [num_seqs][num_q_heads][head_dim]            fp16
+ *    k_pool        [num_blocks][num_kv_heads][block_size][head_dim]  fp16
+ *    v_pool        [num_blocks][num_kv_heads][head_dim][block_size]  fp16
+ *    block_tables  [num_seqs][max_blocks_per_seq]                int32
+ *    context_lens  [num_seqs]                                    int32
+ *    k, v (append) [num_tokens][num_kv_heads][head_dim]          fp16
+ *    slot_mapping  [num_tokens]                                  int32
+ *  The pages fix no pool layout.  K rows are stored token-major inside each
+ *  (block, kv head) tile; V is stored transposed inside each tile (head_dim
+ *  rows of block_size values) so that the P.V product of the decode kernel
+ *  reads its matrix-core operand straight from memory.  A (block, kv head)
+ *  tile of either pool is one contiguous run of block_size*head_dim values.
+ *
+ *  context_lens[s] counts the rows of sequence s including the token being
+ *  decoded (the length after the append) [kapsl-backends 0.1.1,
+ *  forward_batch_decode_greedy]; the query attends rows 0..L-1, with row t in
+ *  physical block block_tables[s][t / block_size] at offset t % block_size.
+ *  Query head hq reads kv head hq / (num_q_heads / num_kv_heads)
+ *  [cortiq-engine 0.8.80, src/gpu_cuda.rs: heads-per-kv-head grouping].
+ *
+ * Compiled geometries: head_dim in {64, 128, 256}, block_size in {16, 32, 64},
+ * group size G = num_q_heads / num_kv_heads in 1..16.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_EINVAL (-1)       /* a null pointer, a negative size, Hq % Hkv != 0, misaligned buffer, ... */
+#define PKV_EUNSUPPORTED (-2) /* head_dim / block_size / group size not compiled in */
+#define PKV_EWORKSPACE (-3)   /* caller workspace smaller than the plan needs */
+#define PKV_EHIP (-4)         /* a HIP runtime call or kernel launch failed (message names it) */
+#define PKV_ENOMEM (-5)       /* the library could not allocate its own workspace */
+
+/* Geometry of a K/V block pool (both pools share it). */
+typedef struct {
+    int32_t num_kv_heads; /* Hkv */
+    int32_t head_dim;     /* D */
+    int32_t block_size;   /* BS: token rows per block */
+    int32_t num_blocks;   /* N: blocks in each pool */
+} pkv_pool_desc;
+
+/* A launch plan for decode attention (see pkv_plan_decode). */
+typedef struct {
+    int32_t num_splits;      /* splits per (sequence, kv head) in the grid; 1 = single pass */
+    int32_t chunk_blocks;    /* > 0: split j covers blocks [j*chunk_blocks, (j+1)*chunk_blocks);
+                                0: each sequence's nb = ceil(L/BS) blocks are cut into
+                                   num_splits ranges of ceil(nb/num_splits) blocks */
+    int32_t waves_per_group; /* wavefronts per workgroup of the attention kernel */
+    int32_t reserved;
+    size_t workspace_bytes;  /* f32 partial bytes the plan needs (0 for a single pass) */
+} pkv_decode_plan;
+
+/* ---------------------------------------------------------------------------
+ * pkv_paged_kv_append
+ *   For every token i with 0 <= slot_mapping[i] < N*BS, copies k[i][h][:] and
+ *   v[i][h][:] for every kv head h into block slot/BS, row slot%BS of k_pool
+ *   and v_pool (bit copy, no arithmetic).  Tokens with a slot outside that
+ *   range are skipped (a negative slot marks padding).  Two tokens naming one
+ *   slot: which write lands is unspecified.
+ *   [kapsl-backends 0.1.1, src/gguf_native.rs: launch_kv_write (one token at
+ *   physical_block / pos_in_block), launch_batch_kv_write (per-token blocks
+ *   and offsets); the slot = physical_block * block_size + pos_in_block form
+ *   folds the two per-token arrays into one]
+ *   k, v: [num_tokens][Hkv][D] fp16, 16-byte aligned.  num_tokens == 0 is a
+ *   no-op.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED (D not a multiple of 8),
+ *   PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping,
+                        int32_t num_tokens, uint16_t *k_pool, uint16_t *v_pool,
+                        pkv_pool_desc pool, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_paged_decode_attention
+ *   out[s][hq][:] = softmax(scale * q[s][hq] . K_s^T) . V_s over the L_s =
+ *   context_lens[s] rows of sequence s, for every s < num_seqs and every query
+ *   head hq (L_s == 0 gives zeros).  f32 arithmetic with an online max/sum;
+ *   out rounded to fp16 (nearest even).
+ *   [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ *   BackendPagedKv::paged_decode_attention (q_len == 1 path),
+ *   paged_batched_flash_dispatch, paged_batched_decode_single_pass]
+ *   num_splits: 0 = the library's dispatcher chooses (pkv_plan_decode),
+ *     1 = single pass (no partials), > 1 = that many splits per sequence, cut
+ *     by equal block ranges, then the combine.
+ *   max_context_hint: host-side upper bound of context_lens used only by the
+ *     dispatcher; 0 = block_size * max_blocks_per_seq (the table capacity, as
+ *     the pages do).
+ *   Split-K partials go to a workspace the library owns: one grow-only buffer
+ *   per (device, stream), allocated on first need (that call synchronises the
+ *   stream once before replacing a smaller buffer), never freed before
+ *   process exit.  Calls on one stream reuse it in stream order.
+ *   q, k_pool, v_pool, out: 16-byte aligned.  num_seqs == 0 is a no-op.
+ *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_decode_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                               pkv_pool_desc pool, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
+                               int32_t num_splits, int32_t max_context_hint, void *stream);
+
+/* Same as pkv_paged_decode_attention, with the split-K partials in a caller
+ * workspace (device memory, 256-byte aligned) of at least plan.workspace_bytes
+ * bytes for the plan pkv_plan_decode returns for the same arguments; a single
+ * pass needs none (workspace may then be NULL).  The workspace must not be in
+ * use by other queued work.  Errors: as above, plus PKV_EWORKSPACE. */
+int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                  pkv_pool_desc pool, const int32_t *block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
+                                  int32_t num_splits, int32_t max_context_hint, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_plan_decode -- the dispatcher, a pure host function (no device call
+ * when cu_count > 0; cu_count <= 0 queries the current device).
+ *   Picks single pass or a split count from the number of (sequence, kv head)
+ *   tiles, the context bound and the compute-unit count, re-derived for a
+ *   256-CU MI355X from the occupancy argument of [ferrum-kernels 0.7.7,
+ *   src/backend/cuda/paged.rs: paged_batched_flash_dispatch] (which targets
+ *   128 SMs).  num_splits > 0 forces that split count (chunk_blocks = 0).
+ *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP (device query).
+ * ------------------------------------------------------------------------- */
+int pkv_plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_hint,
+                    int32_t num_splits, int32_t cu_count, pkv_decode_plan *plan);
+
+/* Bytes of f32 split-K partials for a grid of num_splits splits:
+ * partial_out [B][Hq][S][D] then partial_m and partial_l [B][Hq][S], each
+ * array starting on a 256-byte boundary.  0 when num_splits <= 1. */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t num_splits);
+
+/* ---------------------------------------------------------------------------
+ * pkv_paged_decode_split_partials -- split-K phase 1 on its own.
+ *   For every sequence s, query head hq and split j with a non-empty block
+ *   range (see pkv_decode_plan.chunk_blocks), writes
+ *     partial_m[s][hq][j]      = m_j = max over the split's rows of z_t,
+ *                                z_t = scale * q[s][hq] . k_t  (natural units)
+ *     partial_l[s][hq][j]      = sum_t exp(z_t - m_j)
+ *     partial_out[s][hq][j][:] = sum_t exp(z_t - m_j) * v_t   (not normalised)
+ *   Entries of empty splits (j >= ceil(nb / chunk)) are not written.
+ *   [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs: paged_batched_flash_dispatch
+ *   phase 1 and the partial_out / partial_m / partial_l buffers of SplitKScratch]
+ *   partial_out: [num_seqs][Hq][num_splits][D] f32; partial_m, partial_l:
+ *   [num_seqs][Hq][num_splits] f32; all 16-byte aligned.
+ *   With chunk_blocks > 0 the caller must give num_splits >= ceil(M / chunk_blocks).
+ *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_decode_split_partials(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                    pkv_pool_desc pool, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, float scale,
+                                    int32_t num_splits, int32_t chunk_blocks, float *partial_out,
+                                    float *partial_m, float *partial_l, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_paged_decode_split_combine -- split-K phase 2 (the reduce) on its own.
+ *   out[s][hq][:] = sum_j e^(m_j - M) O_j / sum_j e^(m_j - M) l_j with
+ *   M = max_j m_j, over the non-empty splits j < ceil(nb / chunk) of sequence
+ *   s (nb from context_lens[s], clamped to max_blocks_per_seq blocks); later
+ *   entries are never read.  No rows (or a zero denominator) gives zeros.
+ *   Rounded to fp16 (nearest even).
+ *   [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs: paged_batched_flash_dispatch
+ *   phase 2, the reduce launch over (num_heads, num_seqs)]
+ *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_decode_split_combine(const float *partial_out, const float *partial_m,
+                                   const float *partial_l, const int32_t *context_lens,
+                                   int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int32_t num_splits, int32_t chunk_blocks, uint16_t *out,
+                                   void *stream);
+
+/* Number of compute units of the current device (hipDeviceProp_t::multiProcessorCount). */
+int pkv_device_cu_count(int32_t *cu_count);
+
+/* Thread-local message for the last non-zero return on this thread ("" if none). */
+const char *pkv_last_error(void);
+
+/* Library version string. */
+const char *pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

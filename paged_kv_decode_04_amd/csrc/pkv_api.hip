@@ -1,0 +1,530 @@
+// pkv_api.hip -- host side of libpkv: argument checks, the split dispatcher,
+// the library-owned split-K workspace and the extern "C" entry points
+// declared in include/pkv.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_error[0] = '\0';
+    return PKV_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(PKV_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ---------------------------------------------------------------------------
+// device facts, cached per device ordinal
+
+struct DeviceFacts {
+    int cu_count = 0;
+    int lds_per_block = 0;
+};
+
+std::mutex g_dev_mutex;
+std::map<int, DeviceFacts> g_dev;
+
+int device_facts(DeviceFacts *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> g(g_dev_mutex);
+    auto it = g_dev.find(dev);
+    if (it != g_dev.end()) {
+        *out = it->second;
+        return PKV_OK;
+    }
+    DeviceFacts f;
+    e = hipDeviceGetAttribute(&f.cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+    e = hipDeviceGetAttribute(&f.lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock)");
+    g_dev[dev] = f;
+    *out = f;
+    return PKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// split-K workspace owned by the library: grow-only, one per (device, stream)
+
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int library_workspace(size_t need, hipStream_t stream, void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> g(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            // queued kernels on this stream may still read the old buffer
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess)
+                return hip_fail(e, "hipStreamSynchronize (workspace growth)");
+            e = hipFree(w.ptr);
+            if (e != hipSuccess)
+                return hip_fail(e, "hipFree (workspace growth)");
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t grown = need + need / 4;  // slack so that small growth does not reallocate every call
+        e = hipMalloc(&w.ptr, grown);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return fail(PKV_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", grown, hipGetErrorString(e));
+        }
+        w.bytes = grown;
+    }
+    *ptr = w.ptr;
+    return PKV_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+    size_t o_off, m_off, l_off, total;
+};
+
+WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t S) {
+    WsLayout L;
+    const size_t o = round256((size_t)(B * Hq * S * D) * sizeof(float));
+    const size_t ml = round256((size_t)(B * Hq * S) * sizeof(float));
+    L.o_off = 0;
+    L.m_off = o;
+    L.l_off = o + ml;
+    L.total = o + 2 * ml;
+    return L;
+}
+
+// ---------------------------------------------------------------------------
+// checks shared by the attention entry points
+
+int check_pool(const pkv_pool_desc &pool) {
+    if (pool.num_kv_heads <= 0 || pool.head_dim <= 0 || pool.block_size <= 0 || pool.num_blocks < 0)
+        return fail(PKV_EINVAL, "bad pool geometry (Hkv=%d, D=%d, BS=%d, N=%d)", pool.num_kv_heads,
+                    pool.head_dim, pool.block_size, pool.num_blocks);
+    return PKV_OK;
+}
+
+int check_decode_geometry(int32_t num_seqs, int32_t num_q_heads, const pkv_pool_desc &pool,
+                          int32_t max_blocks_per_seq) {
+    int rc = check_pool(pool);
+    if (rc)
+        return rc;
+    if (num_seqs < 0)
+        return fail(PKV_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
+    if (num_q_heads <= 0 || num_q_heads % pool.num_kv_heads != 0)
+        return fail(PKV_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", num_q_heads,
+                    pool.num_kv_heads);
+    if (max_blocks_per_seq <= 0)
+        return fail(PKV_EINVAL, "max_blocks_per_seq must be > 0 (got %d)", max_blocks_per_seq);
+    if (!pkv::decode_geometry_supported(pool.head_dim, pool.block_size))
+        return fail(PKV_EUNSUPPORTED, "head_dim %d / block_size %d not compiled (head_dim 64|128|256, "
+                    "block_size 16|32|64)", pool.head_dim, pool.block_size);
+    const int G = num_q_heads / pool.num_kv_heads;
+    if (G > 16)
+        return fail(PKV_EUNSUPPORTED, "group size %d > 16 query heads per kv head is not compiled", G);
+    if ((int64_t)max_blocks_per_seq * pool.block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "max_blocks_per_seq * block_size overflows int32");
+    if ((int64_t)num_seqs * pool.num_kv_heads > INT32_MAX)
+        return fail(PKV_EINVAL, "num_seqs * num_kv_heads overflows the grid");
+    return PKV_OK;
+}
+
+int check_decode_pointers(const void *q, const void *k_pool, const void *v_pool, const void *block_tables,
+                          const void *context_lens, const void *out) {
+    if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
+        return fail(PKV_EINVAL, "null device pointer (q=%p k_pool=%p v_pool=%p block_tables=%p "
+                    "context_lens=%p out=%p)", q, k_pool, v_pool, block_tables, context_lens, out);
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16))
+        return fail(PKV_EINVAL, "q, k_pool, v_pool and out must be 16-byte aligned");
+    if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return fail(PKV_EINVAL, "block_tables and context_lens must be 4-byte aligned");
+    return PKV_OK;
+}
+
+// The dispatcher.  Work per (sequence, kv head) tile is read once, so the
+// question is only how many workgroups the grid needs:
+//  - a tile's KV streams through one workgroup, so a grid of T = B*Hkv tiles
+//    keeps every CU busy only if T is a few times the CU count, and the
+//    longest tile bounds the step when it is much longer than the average;
+//  - splitting costs one extra launch plus G*(D+2)*4 bytes written and read
+//    per split, small next to the split's own KV bytes when a split keeps at
+//    least a few dozen blocks.
+// Auto mode therefore keeps a single pass when the grid already has >= 2
+// workgroups per CU and tiles are short, and otherwise splits enough to reach
+// ~2 workgroups per CU and to cap any split at 256 blocks (4096 rows at
+// BS=16); the pages' 128-SM constants become the device's CU count.
+int plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t max_blocks_per_seq, int32_t max_context_hint, int32_t num_splits, int32_t cu_count,
+                int32_t lds_limit, pkv_decode_plan *plan) {
+    if (!plan)
+        return fail(PKV_EINVAL, "plan is null");
+    if (num_splits < 0)
+        return fail(PKV_EINVAL, "num_splits must be >= 0 (got %d)", num_splits);
+    if (max_context_hint < 0)
+        return fail(PKV_EINVAL, "max_context_hint must be >= 0 (got %d)", max_context_hint);
+    pkv_pool_desc pool = {num_kv_heads, head_dim, block_size, 0};
+    int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
+    if (rc)
+        return rc;
+    const int G = num_q_heads / num_kv_heads;
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    const int64_t lmax = max_context_hint > 0 ? (max_context_hint < cap ? max_context_hint : cap) : cap;
+    const int64_t nbmax = (lmax + block_size - 1) / block_size;
+    const int64_t tiles = (int64_t)num_seqs * num_kv_heads;
+    int S = 1;
+    if (num_splits >= 1) {
+        S = num_splits;
+    } else if (tiles > 0) {
+        const int64_t cu = cu_count > 0 ? cu_count : 256;
+        const bool short_tiles = nbmax <= 8;
+        const bool full_grid = tiles >= 2 * cu && nbmax <= 128;
+        if (!(short_tiles || full_grid)) {
+            int64_t want = (2 * cu + tiles - 1) / tiles;
+            const int64_t cap_split = (nbmax + 255) / 256;
+            if (want < cap_split)
+                want = cap_split;
+            if (want > nbmax)
+                want = nbmax;
+            if (want > 64)
+                want = 64;
+            S = (int)(want < 1 ? 1 : want);
+        }
+    }
+    if (S > 65535)
+        return fail(PKV_EINVAL, "num_splits %d exceeds the grid limit 65535", S);
+    int waves = S == 1 ? 8 : 4;
+    if (waves > pkv::max_waves_per_group())
+        waves = pkv::max_waves_per_group();
+    const size_t limit = lds_limit > 0 ? (size_t)lds_limit : (size_t)65536;
+    while (waves > 1 && pkv::decode_lds_bytes(head_dim, G, waves) > limit)
+        waves >>= 1;
+    if (pkv::decode_lds_bytes(head_dim, G, waves) > limit)
+        return fail(PKV_EUNSUPPORTED, "LDS need %zu exceeds the device limit %zu",
+                    pkv::decode_lds_bytes(head_dim, G, waves), limit);
+    plan->num_splits = S;
+    plan->chunk_blocks = 0;
+    plan->waves_per_group = waves;
+    plan->reserved = 0;
+    plan->workspace_bytes = S > 1 ? ws_layout(num_seqs, num_q_heads, head_dim, S).total : 0;
+    return PKV_OK;
+}
+
+pkv::DecodeParams decode_params(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                const pkv_pool_desc &pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                const int32_t *context_lens, int32_t num_q_heads, float scale) {
+    pkv::DecodeParams p;
+    memset(&p, 0, sizeof p);
+    p.q = reinterpret_cast<const _Float16 *>(q);
+    p.k_pool = reinterpret_cast<const _Float16 *>(k_pool);
+    p.v_pool = reinterpret_cast<const _Float16 *>(v_pool);
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.Hq = num_q_heads;
+    p.Hkv = pool.num_kv_heads;
+    p.G = num_q_heads / pool.num_kv_heads;
+    p.N = pool.num_blocks;
+    p.M = max_blocks_per_seq;
+    p.num_splits = 1;
+    p.chunk_blocks = 0;
+    p.scale_log2 = scale * 1.44269504088896340736f;
+    return p;
+}
+
+int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool, pkv_pool_desc pool,
+                const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
+                int32_t max_context_hint, void *workspace, size_t workspace_bytes, bool library_ws,
+                hipStream_t stream) {
+    int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
+    if (rc)
+        return rc;
+    if (num_splits < 0)
+        return fail(PKV_EINVAL, "num_splits must be >= 0 (got %d)", num_splits);
+    if (!isfinite(scale))
+        return fail(PKV_EINVAL, "scale must be finite");
+    if (num_seqs == 0)
+        return ok();
+    rc = check_decode_pointers(q, k_pool, v_pool, block_tables, context_lens, out);
+    if (rc)
+        return rc;
+    DeviceFacts facts;
+    rc = device_facts(&facts);
+    if (rc)
+        return rc;
+    pkv_decode_plan plan;
+    rc = plan_decode(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, pool.block_size, max_blocks_per_seq,
+                     max_context_hint, num_splits, facts.cu_count, facts.lds_per_block, &plan);
+    if (rc)
+        return rc;
+    pkv::DecodeParams p = decode_params(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
+                                        num_q_heads, scale);
+    p.out = reinterpret_cast<_Float16 *>(out);
+    if (plan.num_splits == 1) {
+        hipError_t e = pkv::launch_decode(p, num_seqs, pool.head_dim, pool.block_size, plan.waves_per_group, false,
+                                          stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "decode kernel launch");
+        return ok();
+    }
+    void *ws = workspace;
+    if (library_ws) {
+        rc = library_workspace(plan.workspace_bytes, stream, &ws);
+        if (rc)
+            return rc;
+    } else {
+        if (!ws || workspace_bytes < plan.workspace_bytes)
+            return fail(PKV_EWORKSPACE, "workspace of %zu bytes at %p; the plan (%d splits) needs %zu",
+                        workspace_bytes, ws, plan.num_splits, plan.workspace_bytes);
+        if (!aligned(ws, 256))
+            return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+    }
+    const WsLayout L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits);
+    char *base = static_cast<char *>(ws);
+    p.part_o = reinterpret_cast<float *>(base + L.o_off);
+    p.part_m = reinterpret_cast<float *>(base + L.m_off);
+    p.part_l = reinterpret_cast<float *>(base + L.l_off);
+    p.num_splits = plan.num_splits;
+    p.chunk_blocks = plan.chunk_blocks;
+    hipError_t e = pkv::launch_decode(p, num_seqs, pool.head_dim, pool.block_size, plan.waves_per_group, true,
+                                      stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "split-K phase-1 kernel launch");
+    pkv::CombineParams c;
+    c.part_o = p.part_o;
+    c.part_m = p.part_m;
+    c.part_l = p.part_l;
+    c.context_lens = context_lens;
+    c.out = p.out;
+    c.B = num_seqs;
+    c.Hq = num_q_heads;
+    c.BS = pool.block_size;
+    c.M = max_blocks_per_seq;
+    c.num_splits = plan.num_splits;
+    c.chunk_blocks = plan.chunk_blocks;
+    e = pkv::launch_combine(c, pool.head_dim, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "split-K combine kernel launch");
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping, int32_t num_tokens,
+                        uint16_t *k_pool, uint16_t *v_pool, pkv_pool_desc pool, void *stream) {
+    int rc = check_pool(pool);
+    if (rc)
+        return rc;
+    if (num_tokens < 0)
+        return fail(PKV_EINVAL, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (pool.head_dim % 8 != 0)
+        return fail(PKV_EUNSUPPORTED, "head_dim %d is not a multiple of 8", pool.head_dim);
+    if (num_tokens == 0)
+        return ok();
+    if (!k || !v || !slot_mapping || !k_pool || !v_pool)
+        return fail(PKV_EINVAL, "null device pointer (k=%p v=%p slot_mapping=%p k_pool=%p v_pool=%p)", k, v,
+                    slot_mapping, k_pool, v_pool);
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 2) ||
+        !aligned(slot_mapping, 4))
+        return fail(PKV_EINVAL, "k, v and k_pool must be 16-byte aligned");
+    if ((int64_t)num_tokens * pool.num_kv_heads * (pool.head_dim / 8) > (int64_t)INT32_MAX * 256)
+        return fail(PKV_EINVAL, "append too large for one launch");
+    pkv::AppendParams p;
+    p.k = reinterpret_cast<const _Float16 *>(k);
+    p.v = reinterpret_cast<const _Float16 *>(v);
+    p.slot_mapping = slot_mapping;
+    p.k_pool = reinterpret_cast<_Float16 *>(k_pool);
+    p.v_pool = reinterpret_cast<_Float16 *>(v_pool);
+    p.T = num_tokens;
+    p.Hkv = pool.num_kv_heads;
+    p.D = pool.head_dim;
+    p.BS = pool.block_size;
+    p.N = pool.num_blocks;
+    hipError_t e = pkv::launch_append(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "append kernel launch");
+    return ok();
+}
+
+int pkv_paged_decode_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                               pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                               uint16_t *out, int32_t num_splits, int32_t max_context_hint, void *stream) {
+    return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, 0, true,
+                       static_cast<hipStream_t>(stream));
+}
+
+int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                  pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                                  uint16_t *out, int32_t num_splits, int32_t max_context_hint, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, out, num_splits, max_context_hint, workspace, workspace_bytes, false,
+                       static_cast<hipStream_t>(stream));
+}
+
+int pkv_plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_hint, int32_t num_splits,
+                    int32_t cu_count, pkv_decode_plan *plan) {
+    int lds = 0;
+    if (cu_count <= 0) {
+        DeviceFacts f;
+        int rc = device_facts(&f);
+        if (rc)
+            return rc;
+        cu_count = f.cu_count;
+        lds = f.lds_per_block;
+    }
+    int rc = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                         max_context_hint, num_splits, cu_count, lds, plan);
+    return rc ? rc : ok();
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t num_splits) {
+    if (num_splits <= 1 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0)
+        return 0;
+    return ws_layout(num_seqs, num_q_heads, head_dim, num_splits).total;
+}
+
+int pkv_paged_decode_split_partials(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                    pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                    float scale, int32_t num_splits, int32_t chunk_blocks, float *partial_out,
+                                    float *partial_m, float *partial_l, void *stream) {
+    int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
+    if (rc)
+        return rc;
+    if (num_splits < 1 || num_splits > 65535)
+        return fail(PKV_EINVAL, "num_splits must be in [1, 65535] (got %d)", num_splits);
+    if (chunk_blocks < 0)
+        return fail(PKV_EINVAL, "chunk_blocks must be >= 0 (got %d)", chunk_blocks);
+    if (chunk_blocks > 0 && (int64_t)num_splits * chunk_blocks < max_blocks_per_seq)
+        return fail(PKV_EINVAL, "num_splits * chunk_blocks (%d * %d) does not cover max_blocks_per_seq %d",
+                    num_splits, chunk_blocks, max_blocks_per_seq);
+    if (!isfinite(scale))
+        return fail(PKV_EINVAL, "scale must be finite");
+    if (num_seqs == 0)
+        return ok();
+    rc = check_decode_pointers(q, k_pool, v_pool, block_tables, context_lens, q);
+    if (rc)
+        return rc;
+    if (!partial_out || !partial_m || !partial_l || !aligned(partial_out, 16) || !aligned(partial_m, 4) ||
+        !aligned(partial_l, 4))
+        return fail(PKV_EINVAL, "partial buffers must be non-null (partial_out 16-byte aligned)");
+    DeviceFacts facts;
+    rc = device_facts(&facts);
+    if (rc)
+        return rc;
+    pkv_decode_plan plan;
+    rc = plan_decode(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, pool.block_size, max_blocks_per_seq,
+                     0, num_splits > 1 ? num_splits : 2, facts.cu_count, facts.lds_per_block, &plan);
+    if (rc)
+        return rc;
+    pkv::DecodeParams p = decode_params(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
+                                        num_q_heads, scale);
+    p.part_o = partial_out;
+    p.part_m = partial_m;
+    p.part_l = partial_l;
+    p.num_splits = num_splits;
+    p.chunk_blocks = chunk_blocks;
+    hipError_t e = pkv::launch_decode(p, num_seqs, pool.head_dim, pool.block_size, plan.waves_per_group, true,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "split-K phase-1 kernel launch");
+    return ok();
+}
+
+int pkv_paged_decode_split_combine(const float *partial_out, const float *partial_m, const float *partial_l,
+                                   const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                   int32_t num_splits, int32_t chunk_blocks, uint16_t *out, void *stream) {
+    if (num_seqs < 0 || num_q_heads <= 0 || block_size <= 0 || max_blocks_per_seq <= 0)
+        return fail(PKV_EINVAL, "bad geometry (num_seqs=%d Hq=%d BS=%d M=%d)", num_seqs, num_q_heads, block_size,
+                    max_blocks_per_seq);
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+        return fail(PKV_EUNSUPPORTED, "head_dim %d not compiled (64|128|256)", head_dim);
+    if (num_splits < 1 || chunk_blocks < 0)
+        return fail(PKV_EINVAL, "num_splits must be >= 1 and chunk_blocks >= 0");
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX || (int64_t)num_seqs * num_q_heads > INT32_MAX)
+        return fail(PKV_EINVAL, "geometry overflows int32");
+    if (num_seqs == 0)
+        return ok();
+    if (!partial_out || !partial_m || !partial_l || !context_lens || !out)
+        return fail(PKV_EINVAL, "null device pointer");
+    if (!aligned(out, 2) || !aligned(partial_out, 4))
+        return fail(PKV_EINVAL, "misaligned buffer");
+    pkv::CombineParams c;
+    c.part_o = partial_out;
+    c.part_m = partial_m;
+    c.part_l = partial_l;
+    c.context_lens = context_lens;
+    c.out = reinterpret_cast<_Float16 *>(out);
+    c.B = num_seqs;
+    c.Hq = num_q_heads;
+    c.BS = block_size;
+    c.M = max_blocks_per_seq;
+    c.num_splits = num_splits;
+    c.chunk_blocks = chunk_blocks;
+    hipError_t e = pkv::launch_combine(c, head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "split-K combine kernel launch");
+    return ok();
+}
+
+int pkv_device_cu_count(int32_t *cu_count) {
+    if (!cu_count)
+        return fail(PKV_EINVAL, "cu_count is null");
+    DeviceFacts f;
+    int rc = device_facts(&f);
+    if (rc)
+        return rc;
+    *cu_count = f.cu_count;
+    return ok();
+}
+
+const char *pkv_last_error(void) { return g_error; }
+
+const char *pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+
+}  // extern "C"

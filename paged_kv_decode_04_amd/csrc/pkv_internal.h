@@ -1,0 +1,59 @@
+// pkv_internal.h -- private interface between the host API (pkv_api.hip) and
+// the kernels (pkv_kernels.hip).  Not installed; callers use include/pkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Arguments of the decode-attention kernel (single pass and split-K phase 1).
+struct DecodeParams {
+    const _Float16 *q;            // [B][Hq][D]
+    const _Float16 *k_pool;       // [N][Hkv][BS][D]
+    const _Float16 *v_pool;       // [N][Hkv][D][BS]
+    const int32_t *block_tables;  // [B][M]
+    const int32_t *context_lens;  // [B]
+    _Float16 *out;                // [B][Hq][D]            (single pass)
+    float *part_o;                // [B][Hq][S][D]         (split-K)
+    float *part_m;                // [B][Hq][S]
+    float *part_l;                // [B][Hq][S]
+    int32_t Hq, Hkv, G, N, M;
+    int32_t num_splits;           // grid splits S (1 for a single pass)
+    int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(nb / S) per sequence
+    float scale_log2;             // scale * log2(e)
+};
+
+struct CombineParams {
+    const float *part_o;
+    const float *part_m;
+    const float *part_l;
+    const int32_t *context_lens;
+    _Float16 *out;
+    int32_t B, Hq, BS, M;
+    int32_t num_splits, chunk_blocks;
+};
+
+struct AppendParams {
+    const _Float16 *k;            // [T][Hkv][D]
+    const _Float16 *v;
+    const int32_t *slot_mapping;  // [T]
+    _Float16 *k_pool;
+    _Float16 *v_pool;
+    int32_t T, Hkv, D, BS, N;
+};
+
+// LDS bytes the decode kernel needs for `waves` wavefronts and group size G.
+size_t decode_lds_bytes(int head_dim, int G, int waves);
+
+// Kernel launchers: enqueue on `stream`, return the hipError_t of the launch.
+hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size, int waves,
+                         bool split, hipStream_t stream);
+hipError_t launch_combine(const CombineParams &p, int head_dim, hipStream_t stream);
+hipError_t launch_append(const AppendParams &p, hipStream_t stream);
+
+// Geometry support of the compiled kernels.
+bool decode_geometry_supported(int head_dim, int block_size);
+int max_waves_per_group();
+
+}  // namespace pkv

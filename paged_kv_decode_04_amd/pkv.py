@@ -1,0 +1,258 @@
+"""Thin Python binding of libpkv (include/pkv.h): argument marshalling only.
+
+Each function calls the C entry point of the same name (``pkv_`` prefix dropped) with the device pointers of torch
+tensors and the current HIP stream; every step of the computation runs in the library's gfx950 kernels.  PyTorch
+only supplies device memory and streams.  There is no fallback: if ``libpkv.so`` is missing or fails to load, every
+call raises.
+
+Tensor layouts (all C-contiguous, on the GPU):
+    q, out        [num_seqs][num_q_heads][head_dim]                 float16
+    k_pool        [num_blocks][num_kv_heads][block_size][head_dim]  float16
+    v_pool        [num_blocks][num_kv_heads][head_dim][block_size]  float16
+    block_tables  [num_seqs][max_blocks_per_seq]                    int32
+    context_lens  [num_seqs]                                        int32
+    k, v          [num_tokens][num_kv_heads][head_dim]              float16
+    slot_mapping  [num_tokens]                                      int32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+_lib = None
+_lock = threading.Lock()
+
+PKV_OK = 0
+PKV_EINVAL = -1
+PKV_EUNSUPPORTED = -2
+PKV_EWORKSPACE = -3
+PKV_EHIP = -4
+PKV_ENOMEM = -5
+
+EXPORTED = [
+    "pkv_paged_kv_append",
+    "pkv_paged_decode_attention",
+    "pkv_paged_decode_attention_ws",
+    "pkv_plan_decode",
+    "pkv_decode_workspace_bytes",
+    "pkv_paged_decode_split_partials",
+    "pkv_paged_decode_split_combine",
+    "pkv_device_cu_count",
+    "pkv_last_error",
+    "pkv_version",
+]
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("libpkv error %d: %s" % (code, message))
+        self.code = code
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32)]
+
+
+class DecodePlan(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("chunk_blocks", ctypes.c_int32),
+                ("waves_per_group", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libpkv.so (once) and declare the signatures; raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise PkvError(PKV_EINVAL, "%s is not built; run __graft_entry__.build() or "
+                           "python -m paged_kv_decode_04_amd.build" % p)
+        lib = ctypes.CDLL(p)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        lib.pkv_paged_kv_append.argtypes = [vp, vp, vp, i32, vp, vp, PoolDesc, vp]
+        attn = [vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, vp, i32, i32]
+        lib.pkv_paged_decode_attention.argtypes = attn + [vp]
+        lib.pkv_paged_decode_attention_ws.argtypes = attn + [vp, sz, vp]
+        lib.pkv_plan_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodePlan)]
+        lib.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.pkv_decode_workspace_bytes.restype = sz
+        lib.pkv_paged_decode_split_partials.argtypes = [vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, i32, i32,
+                                                        vp, vp, vp, vp]
+        lib.pkv_paged_decode_split_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+        lib.pkv_device_cu_count.argtypes = [ctypes.POINTER(i32)]
+        lib.pkv_last_error.restype = ctypes.c_char_p
+        lib.pkv_version.restype = ctypes.c_char_p
+        for name in EXPORTED:
+            if name not in ("pkv_decode_workspace_bytes", "pkv_last_error", "pkv_version"):
+                getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _check(rc: int) -> None:
+    if rc != PKV_OK:
+        raise PkvError(rc, load().pkv_last_error().decode())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t, dtype, name: str, ndim: Optional[int] = None):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    return t
+
+
+def _pool(k_pool, v_pool) -> PoolDesc:
+    import torch
+    _dev(k_pool, torch.float16, "k_pool", 4)
+    _dev(v_pool, torch.float16, "v_pool", 4)
+    N, Hkv, BS, D = k_pool.shape
+    if tuple(v_pool.shape) != (N, Hkv, D, BS):
+        raise ValueError("v_pool must be [N][Hkv][D][BS] = %s, got %s" % ((N, Hkv, D, BS), tuple(v_pool.shape)))
+    return PoolDesc(Hkv, D, BS, N)
+
+
+def version() -> str:
+    return load().pkv_version().decode()
+
+
+def last_error() -> str:
+    return load().pkv_last_error().decode()
+
+
+def device_cu_count() -> int:
+    n = ctypes.c_int32(0)
+    _check(load().pkv_device_cu_count(ctypes.byref(n)))
+    return n.value
+
+
+def paged_kv_append(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
+    """Copy each token's K/V rows into the pools at its slot (pkv_paged_kv_append)."""
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(k, torch.float16, "k", 3)
+    _dev(v, torch.float16, "v", 3)
+    _dev(slot_mapping, torch.int32, "slot_mapping", 1)
+    T = int(slot_mapping.shape[0])
+    if tuple(k.shape) != (T, pool.num_kv_heads, pool.head_dim) or k.shape != v.shape:
+        raise ValueError("k and v must be [T][Hkv][D] = %s" % ((T, pool.num_kv_heads, pool.head_dim),))
+    _check(load().pkv_paged_kv_append(_ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_pool), _ptr(v_pool), pool,
+                                      _stream(stream)))
+
+
+def _attn_args(q, k_pool, v_pool, block_tables, context_lens):
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(q, torch.float16, "q", 3)
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    _dev(context_lens, torch.int32, "context_lens", 1)
+    B, Hq, D = q.shape
+    if D != pool.head_dim:
+        raise ValueError("q head_dim %d != pool head_dim %d" % (D, pool.head_dim))
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens must have num_seqs = %d rows" % B)
+    return pool, int(B), int(Hq), int(block_tables.shape[1])
+
+
+def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale: float, out=None,
+                           num_splits: int = 0, max_context_hint: int = 0, workspace=None, stream=None):
+    """out = softmax(scale * q.K^T).V per (sequence, query head) over the paged pools.
+
+    num_splits: 0 = dispatcher, 1 = single pass, > 1 = forced split count.  With ``workspace`` (a uint8 GPU tensor)
+    the _ws entry point is called and the partials go there; otherwise the library's own workspace is used."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, torch.float16, "out", 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    lib = load()
+    args = [_ptr(q), _ptr(k_pool), _ptr(v_pool), pool, _ptr(block_tables), M, _ptr(context_lens), B, Hq,
+            float(scale), _ptr(out), int(num_splits), int(max_context_hint)]
+    if workspace is None:
+        _check(lib.pkv_paged_decode_attention(*args, _stream(stream)))
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(lib.pkv_paged_decode_attention_ws(*args, _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def plan_decode(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                max_blocks_per_seq: int, max_context_hint: int = 0, num_splits: int = 0, cu_count: int = 0) -> dict:
+    """The dispatcher's plan (pkv_plan_decode); cu_count > 0 keeps it a pure host computation."""
+    plan = DecodePlan()
+    _check(load().pkv_plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                  max_context_hint, num_splits, cu_count, ctypes.byref(plan)))
+    return {"num_splits": plan.num_splits, "chunk_blocks": plan.chunk_blocks,
+            "waves_per_group": plan.waves_per_group, "workspace_bytes": int(plan.workspace_bytes)}
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_splits))
+
+
+def paged_decode_split_partials(q, k_pool, v_pool, block_tables, context_lens, scale: float, num_splits: int,
+                                chunk_blocks: int, partial_out, partial_m, partial_l, stream=None) -> None:
+    """Split-K phase 1 (pkv_paged_decode_split_partials) into caller float32 buffers
+    partial_out [B][Hq][S][D], partial_m / partial_l [B][Hq][S]."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    S = int(num_splits)
+    _dev(partial_out, torch.float32, "partial_out", 4)
+    _dev(partial_m, torch.float32, "partial_m", 3)
+    _dev(partial_l, torch.float32, "partial_l", 3)
+    if tuple(partial_out.shape) != (B, Hq, S, pool.head_dim) or tuple(partial_m.shape) != (B, Hq, S) \
+            or tuple(partial_l.shape) != (B, Hq, S):
+        raise ValueError("partial buffers must be [B][Hq][S][D] and [B][Hq][S]")
+    _check(load().pkv_paged_decode_split_partials(_ptr(q), _ptr(k_pool), _ptr(v_pool), pool, _ptr(block_tables), M,
+                                                  _ptr(context_lens), B, Hq, float(scale), S, int(chunk_blocks),
+                                                  _ptr(partial_out), _ptr(partial_m), _ptr(partial_l),
+                                                  _stream(stream)))
+
+
+def paged_decode_split_combine(partial_out, partial_m, partial_l, context_lens, block_size: int,
+                               max_blocks_per_seq: int, chunk_blocks: int, out=None, stream=None):
+    """Split-K phase 2 (pkv_paged_decode_split_combine): log-sum-exp combine into fp16 out [B][Hq][D]."""
+    import torch
+    _dev(partial_out, torch.float32, "partial_out", 4)
+    _dev(partial_m, torch.float32, "partial_m", 3)
+    _dev(partial_l, torch.float32, "partial_l", 3)
+    _dev(context_lens, torch.int32, "context_lens", 1)
+    B, Hq, S, D = partial_out.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=partial_out.device)
+    _dev(out, torch.float16, "out", 3)
+    _check(load().pkv_paged_decode_split_combine(_ptr(partial_out), _ptr(partial_m), _ptr(partial_l),
+                                                 _ptr(context_lens), int(B), int(Hq), int(D), int(block_size),
+                                                 int(max_blocks_per_seq), int(S), int(chunk_blocks), _ptr(out),
+                                                 _stream(stream)))
+    return out
