@@ -1,0 +1,224 @@
+"""Benchmark: one decode step of the paged-KV hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: the paged KV append of every sequence's newest row, then
+paged decode attention (single pass, or split-K phase 1 + combine, as the workload's dispatch mode says).  Inputs
+are seeded synthetic data already resident in HBM; R independent copies rotate between steps so that the ~256 MB
+Infinity Cache cannot hold a step's working set (R=4 for c2).
+
+    python bench.py [--steps K] [--warmup W] [--config c2] [--splits S] [--rotations R] [--no-cpu-baseline]
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value        algorithmic HBM bytes of a step / measured step time, in GB/s (whole job, one GPU)
+  roofline     the attention kernel(s) alone: algorithmic bytes / average duration from HIP events recorded around
+               each attention call inside the timed region, against the 8 TB/s HBM peak; `traffic` is the measured
+               HBM bytes per launch from the committed rocprofv3 counter summary when it was taken on the current
+               kernel source, else null
+  cpu_baseline the CPU oracle (f64, threads = the host cores it used) on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + calls/s, 1 MI355X"
+PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    "c1": ("tiny paged decode: B=1, Hq=4, Hkv=2, D=64, BS=16, L=37, pool of 8 blocks", 0, 1),
+    "c2": ("Llama-3-8B-shaped layer: B=32, Hq=32, Hkv=8, D=128, BS=16, L~U[512,2048], single pass", 1, 4),
+    "c3": ("long-context split-K: B=4, Hq=32, Hkv=8, D=128, BS=16, L=32768, q~2N(0,1)", 16, 2),
+    "c4": ("mixed serving (70B-layer-shaped, one GPU's share): B=256, Hq=64, Hkv=8, D=128, BS=16, "
+           "L=lognormal(median 1024, sigma 1) clipped to [1,16384], auto dispatch", 0, 1),
+    "c5": ("MHA wide head: B=128, Hq=Hkv=16, D=256, BS=32, L=4096, K/V~U(-1,1), scale 1/16", 0, 1),
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("pkv_kernels.hip", "pkv_api.hip", "pkv_internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_decode_04_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config: str, splits: int):
+    """HBM bytes per attention launch from profiles/traffic_<config>_s<splits>.json, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_s%d.json" % (config, splits))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_step")
+
+
+def cpu_baseline(case, seconds: float):
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    from paged_kv_decode_04_amd import workloads as W
+    nbytes = W.algorithmic_bytes(case)["attention"]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_attention(case.q, case.k_pool, case.v_pool, case.block_tables, case.context_lens, case.scale,
+                                threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full decode-attention call(s) of the workload (all %d sequences x %d heads, f64) in %.1f s; "
+                      "%.3f calls/s" % (reps, case.B, case.Hq, el, reps / el)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--splits", type=int, default=None, help="num_splits (default: the workload's mode)")
+    ap.add_argument("--rotations", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the decode-attention hot path has no cross-GPU "
+              "exchange); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from paged_kv_decode_04_amd import pkv
+    from paged_kv_decode_04_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    desc, default_splits, default_rot = WORKLOADS[args.config]
+    splits = default_splits if args.splits is None else args.splits
+    R = default_rot if args.rotations is None else args.rotations
+    make = W.CONFIGS[args.config]
+
+    log("building %d rotation set(s) of %s" % (R, args.config))
+    sets = []
+    host0 = None
+    for r in range(R):
+        c = make(rotation=r)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        d = dict(q=t(c.q), k_pool=t(c.k_pool), v_pool=t(c.v_pool), bt=t(c.block_tables), cl=t(c.context_lens),
+                 k_new=t(c.k_new), v_new=t(c.v_new), slots=t(c.slot_mapping), case=c)
+        d["out"] = torch.empty_like(d["q"])
+        d["bytes"] = W.algorithmic_bytes(c)
+        if r == 0:
+            host0 = c
+        else:
+            c.k_pool = c.v_pool = None  # only set 0 stays on the host (for the CPU baseline)
+        sets.append(d)
+    torch.cuda.synchronize()
+    c0 = sets[0]["case"]
+    plan = pkv.plan_decode(c0.B, c0.Hq, c0.Hkv, c0.D, c0.BS, c0.M, num_splits=splits)
+    log("plan: %s, %s" % (plan, pkv.version()))
+
+    def step(d, ev=None):
+        pkv.paged_kv_append(d["k_new"], d["v_new"], d["slots"], d["k_pool"], d["v_pool"])
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"], d["case"].scale,
+                                   out=d["out"], num_splits=splits)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        step(sets[i % R], evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = total_ms / K
+
+    # bytes per step, averaged over the rotation sets
+    step_bytes = np.mean([d["bytes"]["attention"] + d["bytes"]["append"] for d in sets])
+    attn_bytes = np.mean([d["bytes"]["attention"] for d in sets])
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    attn_avg_ms = float(attn_ms.mean())
+    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    calls_per_s = 1e3 / attn_avg_ms
+    log("step %.4f ms (%.1f GB/s); attention avg %.4f ms median %.4f p90 %.4f -> %.1f GB/s, %.0f calls/s"
+        % (ms_per_step, value, attn_avg_ms, float(np.median(attn_ms)), float(np.percentile(attn_ms, 90)),
+           achieved, calls_per_s))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same workload for ~%.0f s" % args.cpu_seconds)
+        cpu = cpu_baseline(host0, args.cpu_seconds)
+        log("cpu baseline: %s" % cpu)
+
+    result = {
+        "metric": METRIC,
+        "value": round(float(value), 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(ms_per_step), 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: %s" % (args.config, desc),
+            "num_seqs": c0.B, "num_q_heads": c0.Hq, "num_kv_heads": c0.Hkv, "head_dim": c0.D,
+            "block_size": c0.BS, "num_splits": splits, "plan": plan, "rotations": R,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * float(value) / PEAK_GBS, 2),
+        "calls_per_s": round(calls_per_s, 1),
+        "tokens_per_s": round(calls_per_s * c0.B, 1),
+        "attention_ms": {"mean": round(attn_avg_ms, 5), "median": round(float(np.median(attn_ms)), 5),
+                         "p90": round(float(np.percentile(attn_ms, 90)), 5)},
+        "bytes_per_step": {"attention": int(attn_bytes), "append": int(np.mean([d["bytes"]["append"] for d in sets]))},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(float(achieved), 2),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(float(achieved) / PEAK_GBS, 4),
+            "traffic": measured_traffic(args.config, splits),
+        },
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
