@@ -39,17 +39,20 @@
  * Layouts
  * -------
  *    q, out        [num_seqs][num_q_heads][head_dim]            fp16
- *    k_pool        [num_blocks][num_kv_heads][block_size][head_dim]  fp16
- *    v_pool        [num_blocks][num_kv_heads][head_dim][block_size]  fp16
+ *    k_pool        [num_blocks][num_kv_heads][block_size/16][head_dim/8][16][8]  fp16
+ *    v_pool        [num_blocks][num_kv_heads][block_size/16][head_dim][16]       fp16
  *    block_tables  [num_seqs][max_blocks_per_seq]                int32
  *    context_lens  [num_seqs]                                    int32
  *    k, v (append) [num_tokens][num_kv_heads][head_dim]          fp16
  *    slot_mapping  [num_tokens]                                  int32
- *  The pages fix no pool layout.  K rows are stored token-major inside each
- *  (block, kv head) tile; V is stored transposed inside each tile (head_dim
- *  rows of block_size values) so that the P.V product of the decode kernel
- *  reads its matrix-core operand straight from memory.  A (block, kv head)
- *  tile of either pool is one contiguous run of block_size*head_dim values.
+ *  The pages fix no pool layout.  Each (block, kv head) tile is one contiguous
+ *  run of block_size*head_dim values, stored as block_size/16 panels of 16
+ *  rows.  A K panel holds the 16 rows' dims in 8-wide pieces, piece-major
+ *  (element (row r, dim d) at ((d/8)*16 + r)*8 + d%8); a V panel holds V
+ *  transposed (element (r, d) at d*16 + r).  With this layout every operand
+ *  the decode kernel feeds to the matrix cores is a contiguous run in memory
+ *  (1 KB per K load, 512 B per V load of a wavefront).  K/V row t of a tile
+ *  is in panel t/16, row t%16.
  *
  *  context_lens[s] counts the rows of sequence s including the token being
  *  decoded (the length after the append) [kapsl-backends 0.1.1,
@@ -59,7 +62,8 @@
  *  [cortiq-engine 0.8.80, src/gpu_cuda.rs: heads-per-kv-head grouping].
  *
  * Compiled geometries: head_dim in {64, 128, 256}, block_size in {16, 32, 64},
- * group size G = num_q_heads / num_kv_heads in 1..16.
+ * group size G = num_q_heads / num_kv_heads in 1..16.  The append needs
+ * head_dim % 8 == 0 and block_size % 16 == 0.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -109,7 +113,8 @@ typedef struct {
  *   and offsets); the slot = physical_block * block_size + pos_in_block form
  *   folds the two per-token arrays into one]
  *   k, v: [num_tokens][Hkv][D] fp16, 16-byte aligned.  num_tokens == 0 is a
- *   no-op.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED (D not a multiple of 8),
+ *   no-op.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED (D not a multiple of 8 or BS not a
+ *   multiple of 16),
  *   PKV_EHIP.
  * ------------------------------------------------------------------------- */
 int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping,
@@ -155,6 +160,21 @@ int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, con
                                   int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
                                   int32_t num_splits, int32_t max_context_hint, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* Same computation with a caller-chosen launch plan (from pkv_plan_decode, or
+ * tuned by the caller: split count, fixed-size block chunks, waves per
+ * workgroup).  The plan is checked (PKV_EINVAL / PKV_EUNSUPPORTED): num_splits
+ * in [1, 65535], chunk_blocks >= 0 and, for num_splits > 1 with chunk_blocks > 0,
+ * num_splits * chunk_blocks >= max_blocks_per_seq; waves_per_group in
+ * {1, 2, 4, 8}.  workspace == NULL uses the library-owned workspace, otherwise
+ * it must hold plan->workspace_bytes as computed by pkv_decode_workspace_bytes
+ * for plan->num_splits (PKV_EWORKSPACE). */
+int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                       pkv_pool_desc pool, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                       int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
+                                       const pkv_decode_plan *plan, void *workspace, size_t workspace_bytes,
+                                       void *stream);
 
 /* ---------------------------------------------------------------------------
  * pkv_plan_decode -- the dispatcher, a pure host function (no device call

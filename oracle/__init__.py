@@ -99,19 +99,20 @@ def f16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def k_index(num_kv_heads, block_size, head_dim, block, head, offset, dim) -> int:
-    """Flat index of K element (block, kv head, row offset, dim) in k_pool[N][Hkv][BS][D]."""
+    """Flat index of K element (block, kv head, row offset, dim) in k_pool[N][Hkv][BS/16][D/8][16][8]."""
     return _load().oracle_k_index(num_kv_heads, block_size, head_dim, block, head, offset, dim)
 
 
 def v_index(num_kv_heads, block_size, head_dim, block, head, offset, dim) -> int:
-    """Flat index of V element (block, kv head, row offset, dim) in v_pool[N][Hkv][D][BS]."""
+    """Flat index of V element (block, kv head, row offset, dim) in v_pool[N][Hkv][BS/16][D][16]."""
     return _load().oracle_v_index(num_kv_heads, block_size, head_dim, block, head, offset, dim)
 
 
 def _geometry(q, k_pool, v_pool, block_tables, context_lens):
     B, Hq, D = q.shape
-    N, Hkv, BS, D2 = k_pool.shape
-    if D2 != D or v_pool.shape != (N, Hkv, D, BS):
+    N, Hkv, NP, D8, sixteen, eight = k_pool.shape
+    BS = NP * 16
+    if (sixteen, eight) != (16, 8) or D8 * 8 != D or v_pool.shape != (N, Hkv, NP, D, 16):
         raise ValueError("pool shapes %s / %s do not match q %s" % (k_pool.shape, v_pool.shape, q.shape))
     bt = _i32(block_tables)
     if bt.ndim != 2 or bt.shape[0] != B:
@@ -125,7 +126,7 @@ def _geometry(q, k_pool, v_pool, block_tables, context_lens):
 def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale, units=None, threads=None):
     """out[B][Hq][D] (or out[len(units)][D] for a list of (s, hq) units) in float64.
 
-    q: [B][Hq][D] fp16; k_pool: [N][Hkv][BS][D] fp16; v_pool: [N][Hkv][D][BS] fp16;
+    q: [B][Hq][D] fp16; k_pool: [N][Hkv][BS/16][D/8][16][8] fp16; v_pool: [N][Hkv][BS/16][D][16] fp16;
     block_tables: [B][M] int32; context_lens: [B] int32 (rows including the newest token).
     """
     B, Hq, Hkv, D, BS, N, M, bt, cl = _geometry(q, k_pool, v_pool, block_tables, context_lens)
@@ -199,8 +200,9 @@ def paged_kv_append(k, v, slot_mapping, k_pool, v_pool) -> int:
     """In-place append of k, v ([T][Hkv][D] fp16) into the pools; returns the number of skipped slots."""
     kb, vb = _bits(k), _bits(v)
     T, Hkv, D = kb.shape
-    N, Hkv2, BS, D2 = k_pool.shape
-    if (Hkv2, D2) != (Hkv, D) or v_pool.shape != (N, Hkv, D, BS):
+    N, Hkv2, NP, D8, sixteen, eight = k_pool.shape
+    BS = NP * 16
+    if (Hkv2, D8 * 8, sixteen, eight) != (Hkv, D, 16, 8) or v_pool.shape != (N, Hkv, NP, D, 16):
         raise ValueError("pool shapes do not match k/v")
     if not (k_pool.flags.c_contiguous and v_pool.flags.c_contiguous):
         raise ValueError("pools must be C-contiguous (updated in place)")

@@ -36,9 +36,14 @@
  *    sum_j e^(m_j - M) l_j with M = max_j m_j.
  *
  * Pool layouts (the pages do not fix one; this library and the HIP library
- * both document the same two):
- *    k_pool[num_blocks][num_kv_heads][block_size][head_dim]
- *    v_pool[num_blocks][num_kv_heads][head_dim][block_size]
+ * both document the same two).  Each block of block_size rows is stored as
+ * block_size/16 panels of 16 rows:
+ *    k_pool[num_blocks][num_kv_heads][block_size/16][head_dim/8][16][8]
+ *           (a panel holds each row's dims in 8-wide pieces: piece 0 of the
+ *           16 rows, then piece 1, ...)
+ *    v_pool[num_blocks][num_kv_heads][block_size/16][head_dim][16]
+ *           (a panel holds V transposed: dim-major, 16 rows per dim)
+ * head_dim must be a multiple of 8 and block_size a multiple of 16.
  *
  * All arithmetic is IEEE binary64; fp16 inputs are decoded exactly.  No
  * blocking, fusion or reordering beyond the definitions above.
@@ -81,24 +86,26 @@ void oracle_f16_array_to_f64(const uint16_t *src, int64_t n, double *dst)
 
 typedef struct {
     const uint16_t *q;            /* [B][Hq][D] fp16 bits */
-    const uint16_t *k_pool;       /* [N][Hkv][BS][D] fp16 bits */
-    const uint16_t *v_pool;       /* [N][Hkv][D][BS] fp16 bits */
+    const uint16_t *k_pool;       /* [N][Hkv][BS/16][D/8][16][8] fp16 bits */
+    const uint16_t *v_pool;       /* [N][Hkv][BS/16][D][16] fp16 bits */
     const int32_t *block_tables;  /* [B][M] */
     const int32_t *context_lens;  /* [B] */
     int32_t B, Hq, Hkv, D, BS, N, M;
     double scale;
 } oracle_problem;
 
-/* k_pool element (block b, kv head h, row offset o, dim d) */
+/* k_pool element (block b, kv head h, row offset o, dim d): panel o / 16, piece d / 8, row o % 16, lane d % 8 */
 static int64_t k_index(const oracle_problem *P, int64_t b, int h, int o, int d)
 {
-    return ((b * P->Hkv + h) * P->BS + o) * (int64_t)P->D + d;
+    int64_t panel = (b * P->Hkv + h) * (P->BS / 16) + o / 16;
+    return ((panel * (P->D / 8) + d / 8) * 16 + o % 16) * 8 + d % 8;
 }
 
-/* v_pool element (block b, kv head h, row offset o, dim d) */
+/* v_pool element (block b, kv head h, row offset o, dim d): panel o / 16, dim d, row o % 16 */
 static int64_t v_index(const oracle_problem *P, int64_t b, int h, int o, int d)
 {
-    return ((b * P->Hkv + h) * P->D + d) * (int64_t)P->BS + o;
+    int64_t panel = (b * P->Hkv + h) * (P->BS / 16) + o / 16;
+    return (panel * P->D + d) * 16 + o % 16;
 }
 
 int64_t oracle_k_index(int32_t Hkv, int32_t BS, int32_t D, int64_t b, int h, int o, int d)
@@ -236,7 +243,7 @@ static int check_geometry(const oracle_problem *P)
 {
     if (P->B < 0 || P->Hq <= 0 || P->Hkv <= 0 || P->D <= 0 || P->BS <= 0 || P->N < 0 || P->M < 0)
         return -1;
-    if (P->Hq % P->Hkv)
+    if (P->Hq % P->Hkv || P->D % 8 || P->BS % 16)
         return -1;
     return 0;
 }
@@ -433,7 +440,7 @@ int64_t oracle_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32
                                int32_t T, int32_t Hkv, int32_t D, int32_t BS, int32_t N,
                                uint16_t *k_pool, uint16_t *v_pool)
 {
-    if (T < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || N < 0)
+    if (T < 0 || Hkv <= 0 || D <= 0 || D % 8 || BS <= 0 || BS % 16 || N < 0)
         return -1;
     oracle_problem P;
     memset(&P, 0, sizeof P);

@@ -230,6 +230,8 @@ int plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int
     }
     if (S > 65535)
         return fail(PKV_EINVAL, "num_splits %d exceeds the grid limit 65535", S);
+    if ((int64_t)num_seqs * num_kv_heads * S > INT32_MAX)
+        return fail(PKV_EINVAL, "num_seqs * num_kv_heads * num_splits overflows the grid");
     int waves = S == 1 ? 8 : 4;
     if (waves > pkv::max_waves_per_group())
         waves = pkv::max_waves_per_group();
@@ -268,32 +270,34 @@ pkv::DecodeParams decode_params(const uint16_t *q, const uint16_t *k_pool, const
     return p;
 }
 
-int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool, pkv_pool_desc pool,
-                const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
-                int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
-                int32_t max_context_hint, void *workspace, size_t workspace_bytes, bool library_ws,
-                hipStream_t stream) {
-    int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
-    if (rc)
-        return rc;
-    if (num_splits < 0)
-        return fail(PKV_EINVAL, "num_splits must be >= 0 (got %d)", num_splits);
-    if (!isfinite(scale))
-        return fail(PKV_EINVAL, "scale must be finite");
-    if (num_seqs == 0)
-        return ok();
-    rc = check_decode_pointers(q, k_pool, v_pool, block_tables, context_lens, out);
-    if (rc)
-        return rc;
-    DeviceFacts facts;
-    rc = device_facts(&facts);
-    if (rc)
-        return rc;
-    pkv_decode_plan plan;
-    rc = plan_decode(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, pool.block_size, max_blocks_per_seq,
-                     max_context_hint, num_splits, facts.cu_count, facts.lds_per_block, &plan);
-    if (rc)
-        return rc;
+// Checks a plan against the geometry and the device; S == 1 is a single pass (chunk ignored).
+int check_plan(const pkv_decode_plan &plan, int32_t num_seqs, int32_t num_q_heads, const pkv_pool_desc &pool,
+               int32_t max_blocks_per_seq, int lds_limit) {
+    if (plan.num_splits < 1 || plan.num_splits > 65535)
+        return fail(PKV_EINVAL, "plan.num_splits must be in [1, 65535] (got %d)", plan.num_splits);
+    if (plan.chunk_blocks < 0)
+        return fail(PKV_EINVAL, "plan.chunk_blocks must be >= 0 (got %d)", plan.chunk_blocks);
+    if (plan.num_splits > 1 && plan.chunk_blocks > 0 &&
+        (int64_t)plan.num_splits * plan.chunk_blocks < max_blocks_per_seq)
+        return fail(PKV_EINVAL, "plan: num_splits * chunk_blocks (%d * %d) does not cover max_blocks_per_seq %d",
+                    plan.num_splits, plan.chunk_blocks, max_blocks_per_seq);
+    if ((int64_t)num_seqs * pool.num_kv_heads * plan.num_splits > INT32_MAX)
+        return fail(PKV_EINVAL, "num_seqs * num_kv_heads * num_splits overflows the grid");
+    const int w = plan.waves_per_group;
+    if (w != 1 && w != 2 && w != 4 && w != 8)
+        return fail(PKV_EINVAL, "plan.waves_per_group must be 1, 2, 4 or 8 (got %d)", w);
+    const size_t need = pkv::decode_lds_bytes(pool.head_dim, num_q_heads / pool.num_kv_heads, w);
+    const size_t limit = lds_limit > 0 ? (size_t)lds_limit : (size_t)65536;
+    if (need > limit)
+        return fail(PKV_EUNSUPPORTED, "plan needs %zu LDS bytes per workgroup, the device allows %zu", need, limit);
+    return PKV_OK;
+}
+
+// Enqueues the kernels of a checked plan.
+int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+             const pkv_pool_desc &pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+             const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
+             void *workspace, size_t workspace_bytes, bool library_ws, hipStream_t stream) {
     pkv::DecodeParams p = decode_params(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
                                         num_q_heads, scale);
     p.out = reinterpret_cast<_Float16 *>(out);
@@ -304,19 +308,19 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
             return hip_fail(e, "decode kernel launch");
         return ok();
     }
+    const WsLayout L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits);
     void *ws = workspace;
     if (library_ws) {
-        rc = library_workspace(plan.workspace_bytes, stream, &ws);
+        int rc = library_workspace(L.total, stream, &ws);
         if (rc)
             return rc;
     } else {
-        if (!ws || workspace_bytes < plan.workspace_bytes)
+        if (!ws || workspace_bytes < L.total)
             return fail(PKV_EWORKSPACE, "workspace of %zu bytes at %p; the plan (%d splits) needs %zu",
-                        workspace_bytes, ws, plan.num_splits, plan.workspace_bytes);
+                        workspace_bytes, ws, plan.num_splits, L.total);
         if (!aligned(ws, 256))
             return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
     }
-    const WsLayout L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits);
     char *base = static_cast<char *>(ws);
     p.part_o = reinterpret_cast<float *>(base + L.o_off);
     p.part_m = reinterpret_cast<float *>(base + L.m_off);
@@ -345,6 +349,42 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     return ok();
 }
 
+int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool, pkv_pool_desc pool,
+                const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
+                int32_t max_context_hint, const pkv_decode_plan *given, void *workspace, size_t workspace_bytes,
+                bool library_ws, hipStream_t stream) {
+    int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
+    if (rc)
+        return rc;
+    if (num_splits < 0)
+        return fail(PKV_EINVAL, "num_splits must be >= 0 (got %d)", num_splits);
+    if (!isfinite(scale))
+        return fail(PKV_EINVAL, "scale must be finite");
+    if (num_seqs == 0)
+        return ok();
+    rc = check_decode_pointers(q, k_pool, v_pool, block_tables, context_lens, out);
+    if (rc)
+        return rc;
+    DeviceFacts facts;
+    rc = device_facts(&facts);
+    if (rc)
+        return rc;
+    pkv_decode_plan plan;
+    if (given) {
+        plan = *given;
+        rc = check_plan(plan, num_seqs, num_q_heads, pool, max_blocks_per_seq, facts.lds_per_block);
+    } else {
+        rc = plan_decode(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, pool.block_size,
+                         max_blocks_per_seq, max_context_hint, num_splits, facts.cu_count, facts.lds_per_block,
+                         &plan);
+    }
+    if (rc)
+        return rc;
+    return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -356,8 +396,9 @@ int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slo
         return rc;
     if (num_tokens < 0)
         return fail(PKV_EINVAL, "num_tokens must be >= 0 (got %d)", num_tokens);
-    if (pool.head_dim % 8 != 0)
-        return fail(PKV_EUNSUPPORTED, "head_dim %d is not a multiple of 8", pool.head_dim);
+    if (pool.head_dim % 8 != 0 || pool.block_size % 16 != 0)
+        return fail(PKV_EUNSUPPORTED, "head_dim %d must be a multiple of 8 and block_size %d a multiple of 16",
+                    pool.head_dim, pool.block_size);
     if (num_tokens == 0)
         return ok();
     if (!k || !v || !slot_mapping || !k_pool || !v_pool)
@@ -390,7 +431,7 @@ int pkv_paged_decode_attention(const uint16_t *q, const uint16_t *k_pool, const 
                                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                                uint16_t *out, int32_t num_splits, int32_t max_context_hint, void *stream) {
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, 0, true,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -400,7 +441,19 @@ int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, con
                                   uint16_t *out, int32_t num_splits, int32_t max_context_hint, void *workspace,
                                   size_t workspace_bytes, void *stream) {
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_q_heads, scale, out, num_splits, max_context_hint, workspace, workspace_bytes, false,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, workspace, workspace_bytes,
+                       false, static_cast<hipStream_t>(stream));
+}
+
+int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                       pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                       float scale, uint16_t *out, const pkv_decode_plan *plan, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+    if (!plan)
+        return fail(PKV_EINVAL, "plan is null");
+    return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, out, 0, 0, plan, workspace, workspace_bytes, workspace == nullptr,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -439,6 +492,8 @@ int pkv_paged_decode_split_partials(const uint16_t *q, const uint16_t *k_pool, c
         return fail(PKV_EINVAL, "num_splits must be in [1, 65535] (got %d)", num_splits);
     if (chunk_blocks < 0)
         return fail(PKV_EINVAL, "chunk_blocks must be >= 0 (got %d)", chunk_blocks);
+    if ((int64_t)num_seqs * pool.num_kv_heads * num_splits > INT32_MAX)
+        return fail(PKV_EINVAL, "num_seqs * num_kv_heads * num_splits overflows the grid");
     if (chunk_blocks > 0 && (int64_t)num_splits * chunk_blocks < max_blocks_per_seq)
         return fail(PKV_EINVAL, "num_splits * chunk_blocks (%d * %d) does not cover max_blocks_per_seq %d",
                     num_splits, chunk_blocks, max_blocks_per_seq);

@@ -52,18 +52,35 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegBig = -1.0e30f;
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr int kMaxWaves = 8;
+constexpr int kTableWindow = 2048;  // block ids staged in LDS at a time (8 KB)
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
-// Block id of the wave's i-th unit: lane j of `window` holds the id for unit
-// index base + j, refreshed every 64 units.
-template <int SPB>
-__device__ __forceinline__ int table_window(const int32_t *bt, int u_first, int stride, int i_base, int u_end,
-                                            int lane) {
-    const int u = u_first + stride * (i_base + lane);
-    return (u < u_end) ? bt[u / SPB] : -1;
+// Reductions over the four 16-lane rows that hold the same MFMA column (lanes r, r+16, r+32, r+48), on the VALU
+// (v_permlane16_swap / v_permlane32_swap): no LDS traffic and no wait on the lgkm counter.  Every lane gets the
+// same value, summed in the same order.
+__device__ __forceinline__ float rows_max(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Block tables and lengths are read with wave-uniform indices through the constant address space, so they become
+// scalar (SMEM) loads: their waits count on the lgkm counter and never hold back the K/V vector loads in flight.
+typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
+
+__device__ __forceinline__ int uniform_load(const int32_t *p, int64_t i) {
+    return ((const_i32_ptr)p)[i];
 }
 
 template <int D, int BS>
@@ -74,27 +91,46 @@ struct Frag {
     f16x4 v[VC];
 };
 
-// Loads unit u (16 rows) of physical block `blk` for kv head hk.
+// Loads one 16-row unit with buffer loads.  Every block is stored as panels of 16 rows; a unit is one panel:
+//   K panel [D/8][16][8]: the A-operand fragment of lane (g4, r) -- row r, dims 32c + 8*g4 .. +8, i.e. piece
+//     4c + g4 -- sits at byte 1024*c + 16*(16*g4 + r) = 1024*c + 16*lane: each wave load is one contiguous 1 KB
+//     run of whole cache lines (a row-major tile would touch sixteen half lines per load, which caps one CU at
+//     about a third of the rate it reaches on whole lines);
+//   V panel [D][16] (V transposed): lane (g4, r) reads dims 16c + r, rows 4*g4 .. +3 at byte
+//     512*c + 32*r + 8*g4: each wave load is one contiguous 512-byte run.
+// kb / vb are wave-uniform pointers to the panel; each becomes a buffer resource built on the scalar unit, and the
+// lane's loop-invariant byte offsets (k_lane, v_lane) are the only VGPR operands, so no per-unit address arithmetic
+// lands in vector registers that loads in flight still own.  The resource's record count is the panel's size: an
+// offset past it reads 0.
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, no swizzle (gfx9 family)
+#ifndef PKV_KV_LOAD_POLICY
+#define PKV_KV_LOAD_POLICY 2  // nt: K/V are streamed once per step; keep them from displacing reused lines
+#endif
+constexpr int kKvLoadPolicy = PKV_KV_LOAD_POLICY;  // cache-policy bits of the streamed K/V loads
+
 template <int D, int BS>
-__device__ __forceinline__ void load_unit(Frag<D, BS> &f, const DecodeParams &p, int blk, int hk, int u, int r,
-                                          int g4) {
-    constexpr int SPB = BS / 16;
-    const int sub = u % SPB;
-    const int64_t tile = ((int64_t)blk * p.Hkv + hk) * (int64_t)(BS * D);
-    const _Float16 *kb = p.k_pool + tile + (int64_t)(sub * 16 + r) * D + 8 * g4;
+__device__ __forceinline__ void load_unit(Frag<D, BS> &f, const _Float16 *kb, const _Float16 *vb, uint32_t k_lane,
+                                          uint32_t v_lane) {
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(kb), 0, 32 * D,
+                                                                        kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(vb), 0, 32 * D,
+                                                                        kRsrcWord3);
 #pragma unroll
     for (int c = 0; c < Frag<D, BS>::KC; ++c)
-        f.k[c] = *reinterpret_cast<const f16x8 *>(kb + 32 * c);
-    const _Float16 *vb = p.v_pool + tile + (int64_t)r * BS + sub * 16 + 4 * g4;
+        f.k[c] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, k_lane, 1024 * c,
+                                                                                 kKvLoadPolicy));
 #pragma unroll
     for (int c = 0; c < Frag<D, BS>::VC; ++c)
-        f.v[c] = *reinterpret_cast<const f16x4 *>(vb + 16 * c * BS);
+        f.v[c] = __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(vr, v_lane, 512 * c,
+                                                                                kKvLoadPolicy));
 }
 
-// One 16-row unit: scores, online-softmax update, P.V accumulation.
+// One 16-row unit: scores, online-softmax update, P.V accumulation.  A dead unit (its block id names no pool
+// block) is computed with every row masked, so that the loads of every unit are consumed on every path.
 template <int D, int BS>
 __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D / 32], f32x4 (&o)[D / 16],
-                                             float &m_run, float &l_run, int u, int L, int g4, float scale_log2) {
+                                             float &m_run, float &l_run, int u, int L, bool dead, int g4,
+                                             float scale_log2) {
     constexpr int KC = Frag<D, BS>::KC;
     constexpr int VC = Frag<D, BS>::VC;
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -106,19 +142,17 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
     for (int e = 0; e < 4; ++e)
         y[e] = sc[e] * scale_log2;
     const int t0 = u * 16 + 4 * g4;  // row of y[0] in the sequence
-    if (u * 16 + 16 > L) {           // the unit holding row L-1 (wave-uniform branch)
+    if (dead || u * 16 + 16 > L) {   // the unit holding row L-1, or a dead unit (wave-uniform branch)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bool live = (t0 + e) < L;
+            const bool live = !dead && (t0 + e) < L;
             y[e] = live ? y[e] : -INFINITY;
 #pragma unroll
             for (int c = 0; c < VC; ++c)
                 f.v[c][e] = live ? f.v[c][e] : (_Float16)0.0f;  // rows past L may hold anything
         }
     }
-    float bm = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
-    bm = fmaxf(bm, xor_lane(bm, 16));
-    bm = fmaxf(bm, xor_lane(bm, 32));
+    const float bm = rows_max(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])));
     const float m_new = fmaxf(m_run, bm);
     const float alpha = exp2_fast(m_run - m_new);
     float pe[4];
@@ -146,17 +180,36 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     constexpr int DP = D + 4;  // padded LDS row of one head's output
     extern __shared__ float smem[];
 
-    const int tile = blockIdx.x;
+    // 1-D grid.  With splits, the S splits of one (sequence, kv head) tile are consecutive workgroup ids: the
+    // dispatcher deals consecutive ids to different XCDs and CUs, so a long tile's splits stream through many CUs
+    // (each CU's outstanding-miss budget, not HBM, bounds one workgroup), and each CU's co-resident workgroups come
+    // from unrelated tiles.
+    const int tile = SPLIT ? (int)(blockIdx.x / (unsigned)p.num_splits) : (int)blockIdx.x;
+    const int split = SPLIT ? (int)(blockIdx.x - (unsigned)tile * p.num_splits) : 0;
     const int s = tile / p.Hkv;
     const int hk = tile - s * p.Hkv;
-    const int split = SPLIT ? (int)blockIdx.y : 0;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int r = lane & 15;
     const int g4 = lane >> 4;
 
-    int L = p.context_lens[s];
+    int *sm_bt = reinterpret_cast<int *>(smem);
+    const int32_t *bt = p.block_tables + (int64_t)s * p.M;
+    // When the first block of the range is known from the launch alone (a single pass starts at block 0, a
+    // fixed-size split j at j*chunk_blocks), the first window of block ids is staged before the length arrives,
+    // so the two dependent loads (length, then table) overlap.  Entries past the sequence are never used.
+    const int b0_known = SPLIT ? split * p.chunk_blocks : 0;
+    const bool staged_early = (!SPLIT || p.chunk_blocks > 0) && b0_known < p.M;
+    if (staged_early) {
+        const int n_early = min(min(p.M - b0_known, kTableWindow), SPLIT ? p.chunk_blocks : kTableWindow);
+        for (int i = threadIdx.x; i < n_early; i += NW * 64)
+            sm_bt[i] = bt[b0_known + i];
+    }
+
+    int L = uniform_load(p.context_lens, s);
     L = L < 0 ? 0 : (L > p.M * BS ? p.M * BS : L);
+    if (p.N <= 0)
+        L = 0;  // an empty pool holds no rows
     const int nb = (L + BS - 1) / BS;
     int b0 = 0, b1 = nb;
     if (SPLIT) {
@@ -168,7 +221,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     }
     const int u_begin = b0 * SPB;
     const int u_end = min(b1 * SPB, (L + 15) >> 4);
-    const int32_t *bt = p.block_tables + (int64_t)s * p.M;
 
     // Q^T as the B operand: lane (g4, r) holds head r, dims 32c + 8*g4 .. +8.
     f16x8 qf[KC];
@@ -189,57 +241,74 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     float m_run = kNegBig;
     float l_run = 0.f;
 
-    int u = u_begin + wave;
-    if (u < u_end) {
-        int window = table_window<SPB>(bt, u_begin + wave, NW, 0, u_end, lane);
-        int i = 0;
+    const uint32_t k_lane = (uint32_t)(16 * lane);            // bytes into a K panel
+    const uint32_t v_lane = (uint32_t)(32 * r + 8 * g4);      // bytes into a V panel
+    const int64_t head_off = (int64_t)hk * (BS * D);
+    const int64_t block_stride = (int64_t)p.Hkv * (BS * D);
+
+    // The workgroup's block ids go through LDS in windows of kTableWindow entries; wave w takes the window's
+    // 16-row units w, w+NW, ... and double-buffers them: unit k+1 is in flight while unit k is computed.
+    for (int wb = b0; wb < b1; wb += kTableWindow) {
+        const int we = min(b1, wb + kTableWindow);
+        if (wb != b0)
+            __syncthreads();  // every wave is done with the previous window
+        if (wb != b0 || !staged_early)
+            for (int i = threadIdx.x; i < we - wb; i += NW * 64)
+                sm_bt[i] = bt[wb + i];
+        __syncthreads();
+        const int wu_end = min(we * SPB, u_end);
+        const int u_first = wb * SPB + wave;
+        const int n_units = u_first < wu_end ? (wu_end - u_first + NW - 1) / NW : 0;
+        if (n_units == 0)
+            continue;
+        // Block id of unit u from the staged window, clamped to block 0 when the table names no pool block (the
+        // unit is then computed fully masked).
+        auto raw_block = [&](int u) -> int { return sm_bt[u / SPB - wb]; };
+        auto resolve = [&](int raw, bool &dead) -> int {
+            const int b = __builtin_amdgcn_readfirstlane(raw);
+            dead = (unsigned)b >= (unsigned)p.N;
+            return dead ? 0 : b;
+        };
+        auto k_ptr = [&](int blk, int u) {
+            return p.k_pool + (int64_t)blk * block_stride + head_off + (u % SPB) * (16 * D);
+        };
+        auto v_ptr = [&](int blk, int u) {
+            return p.v_pool + (int64_t)blk * block_stride + head_off + (u % SPB) * (16 * D);
+        };
+        // Every iteration issues its prefetch unconditionally -- after a wave's last unit it re-loads that unit
+        // (an L2 hit, never used) -- so the wait counts the compiler derives are exact on every path and unit k+1
+        // stays in flight during the whole computation of unit k.
         Frag<D, BS> fa, fb;
-        int blk_a = __builtin_amdgcn_readlane(window, 0);
-        bool ok_a = (unsigned)blk_a < (unsigned)p.N;
-        if (ok_a)
-            load_unit<D, BS>(fa, p, blk_a, hk, u, r, g4);
+        bool dead_a, dead_b;
+        int ua = u_first;
+        int blk_a = resolve(raw_block(ua), dead_a);
+        load_unit<D, BS>(fa, k_ptr(blk_a, ua), v_ptr(blk_a, ua), k_lane, v_lane);
+        int ub = n_units > 1 ? ua + NW : ua;
+        int raw_b = raw_block(ub);
+        int k = 0;
         for (;;) {
-            // prefetch the next unit into fb, then compute fa
-            int un = u + NW;
-            bool has_b = un < u_end;
-            int blk_b = -1;
-            if (has_b) {
-                ++i;
-                if ((i & 63) == 0)
-                    window = table_window<SPB>(bt, u_begin + wave, NW, i, u_end, lane);
-                blk_b = __builtin_amdgcn_readlane(window, i & 63);
-                if ((unsigned)blk_b < (unsigned)p.N)
-                    load_unit<D, BS>(fb, p, blk_b, hk, un, r, g4);
-            }
-            if (ok_a)
-                compute_unit<D, BS>(fa, qf, o, m_run, l_run, u, L, g4, p.scale_log2);
-            if (!has_b)
+            int blk_b = resolve(raw_b, dead_b);
+            load_unit<D, BS>(fb, k_ptr(blk_b, ub), v_ptr(blk_b, ub), k_lane, v_lane);
+            int ua_next = k + 2 < n_units ? ub + NW : ub;
+            int raw_a = raw_block(ua_next);
+            compute_unit<D, BS>(fa, qf, o, m_run, l_run, ua, L, dead_a, g4, p.scale_log2);
+            if (++k >= n_units)
                 break;
-            u = un;
-            bool ok_b = (unsigned)blk_b < (unsigned)p.N;
-            // prefetch the next unit into fa, then compute fb
-            un = u + NW;
-            bool has_a = un < u_end;
-            if (has_a) {
-                ++i;
-                if ((i & 63) == 0)
-                    window = table_window<SPB>(bt, u_begin + wave, NW, i, u_end, lane);
-                blk_a = __builtin_amdgcn_readlane(window, i & 63);
-                if ((unsigned)blk_a < (unsigned)p.N)
-                    load_unit<D, BS>(fa, p, blk_a, hk, un, r, g4);
-            }
-            if (ok_b)
-                compute_unit<D, BS>(fb, qf, o, m_run, l_run, u, L, g4, p.scale_log2);
-            if (!has_a)
+            ua = ua_next;
+            blk_a = resolve(raw_a, dead_a);
+            load_unit<D, BS>(fa, k_ptr(blk_a, ua), v_ptr(blk_a, ua), k_lane, v_lane);
+            int ub_next = k + 2 < n_units ? ua + NW : ua;
+            raw_b = raw_block(ub_next);
+            compute_unit<D, BS>(fb, qf, o, m_run, l_run, ub, L, dead_b, g4, p.scale_log2);
+            if (++k >= n_units)
                 break;
-            u = un;
-            ok_a = (unsigned)blk_a < (unsigned)p.N;
+            ub = ub_next;
         }
     }
+    __syncthreads();  // the table window's LDS is reused below
 
     // l over the four lane groups that hold the same head
-    l_run += xor_lane(l_run, 16);
-    l_run += xor_lane(l_run, 32);
+    l_run = rows_sum(l_run);
 
     float *sm_m = smem;
     float *sm_l = smem + NW * 16;
@@ -339,8 +408,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 
 // Paged KV append [kapsl-backends 0.1.1, src/gguf_native.rs: launch_kv_write,
 // launch_batch_kv_write]: one thread per (token, kv head, 8-dim piece).  The K
-// piece is one 16-byte store into its row; the V piece is 8 two-byte stores,
-// one per transposed row of the tile.
+// piece is one 16-byte store into the row's panel ([D/8][16][8]); the V piece is
+// 8 two-byte stores into the transposed panel ([D][16]).
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int pieces = p.D / 8;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -359,20 +428,24 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int64_t src = th * p.D + 8 * c;
     const uint4 kv = *reinterpret_cast<const uint4 *>(p.k + src);
     const uint4 vv = *reinterpret_cast<const uint4 *>(p.v + src);
-    const int64_t tile = (blk * p.Hkv + h) * (int64_t)p.BS * p.D;
-    *reinterpret_cast<uint4 *>(p.k_pool + tile + (int64_t)off * p.D + 8 * c) = kv;
+    // the row's 16-row panel inside the (block, kv head) tile
+    const int64_t panel = (blk * p.Hkv + h) * (int64_t)p.BS * p.D + (int64_t)(off / 16) * 16 * p.D;
+    const int row = off % 16;
+    *reinterpret_cast<uint4 *>(p.k_pool + panel + ((int64_t)c * 16 + row) * 8) = kv;  // K panel [D/8][16][8]
     const uint16_t *vh = reinterpret_cast<const uint16_t *>(&vv);
-    uint16_t *vdst = reinterpret_cast<uint16_t *>(p.v_pool + tile + (int64_t)(8 * c) * p.BS + off);
+    uint16_t *vdst = reinterpret_cast<uint16_t *>(p.v_pool + panel + (int64_t)(8 * c) * 16 + row);  // [D][16]
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        vdst[(int64_t)e * p.BS] = vh[e];
+        vdst[e * 16] = vh[e];
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 
 size_t decode_lds_bytes(int head_dim, int G, int waves) {
-    return sizeof(float) * ((size_t)2 * waves * 16 + (size_t)waves * G * (head_dim + 4));
+    const size_t combine = sizeof(float) * ((size_t)2 * waves * 16 + (size_t)waves * G * (head_dim + 4));
+    const size_t table = sizeof(int) * (size_t)kTableWindow;
+    return combine > table ? combine : table;
 }
 
 bool decode_geometry_supported(int head_dim, int block_size) {
@@ -384,7 +457,7 @@ int max_waves_per_group() { return kMaxWaves; }
 
 template <int D, int BS, int NW>
 static hipError_t launch_decode_t(const DecodeParams &p, int num_seqs, bool split, hipStream_t stream) {
-    dim3 grid((unsigned)(num_seqs * p.Hkv), split ? (unsigned)p.num_splits : 1u, 1u);
+    dim3 grid((unsigned)((int64_t)num_seqs * p.Hkv * (split ? p.num_splits : 1)), 1u, 1u);
     dim3 block(NW * 64);
     const size_t lds = decode_lds_bytes(D, p.G, NW);
     if (split)

@@ -7,8 +7,8 @@ call raises.
 
 Tensor layouts (all C-contiguous, on the GPU):
     q, out        [num_seqs][num_q_heads][head_dim]                 float16
-    k_pool        [num_blocks][num_kv_heads][block_size][head_dim]  float16
-    v_pool        [num_blocks][num_kv_heads][head_dim][block_size]  float16
+    k_pool        [num_blocks][num_kv_heads][block_size/16][head_dim/8][16][8]  float16
+    v_pool        [num_blocks][num_kv_heads][block_size/16][head_dim][16]       float16
     block_tables  [num_seqs][max_blocks_per_seq]                    int32
     context_lens  [num_seqs]                                        int32
     k, v          [num_tokens][num_kv_heads][head_dim]              float16
@@ -37,6 +37,7 @@ EXPORTED = [
     "pkv_paged_kv_append",
     "pkv_paged_decode_attention",
     "pkv_paged_decode_attention_ws",
+    "pkv_paged_decode_attention_planned",
     "pkv_plan_decode",
     "pkv_decode_workspace_bytes",
     "pkv_paged_decode_split_partials",
@@ -80,6 +81,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         attn = [vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, vp, i32, i32]
         lib.pkv_paged_decode_attention.argtypes = attn + [vp]
         lib.pkv_paged_decode_attention_ws.argtypes = attn + [vp, sz, vp]
+        lib.pkv_paged_decode_attention_planned.argtypes = attn[:11] + [ctypes.POINTER(DecodePlan), vp, sz, vp]
         lib.pkv_plan_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodePlan)]
         lib.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.pkv_decode_workspace_bytes.restype = sz
@@ -129,11 +131,15 @@ def _dev(t, dtype, name: str, ndim: Optional[int] = None):
 
 def _pool(k_pool, v_pool) -> PoolDesc:
     import torch
-    _dev(k_pool, torch.float16, "k_pool", 4)
-    _dev(v_pool, torch.float16, "v_pool", 4)
-    N, Hkv, BS, D = k_pool.shape
-    if tuple(v_pool.shape) != (N, Hkv, D, BS):
-        raise ValueError("v_pool must be [N][Hkv][D][BS] = %s, got %s" % ((N, Hkv, D, BS), tuple(v_pool.shape)))
+    _dev(k_pool, torch.float16, "k_pool", 6)
+    _dev(v_pool, torch.float16, "v_pool", 5)
+    N, Hkv, NP, D8, sixteen, eight = k_pool.shape
+    D, BS = D8 * 8, NP * 16
+    if (sixteen, eight) != (16, 8):
+        raise ValueError("k_pool must be [N][Hkv][BS/16][D/8][16][8], got %s" % (tuple(k_pool.shape),))
+    if tuple(v_pool.shape) != (N, Hkv, NP, D, 16):
+        raise ValueError("v_pool must be [N][Hkv][BS/16][D][16] = %s, got %s"
+                         % ((N, Hkv, NP, D, 16), tuple(v_pool.shape)))
     return PoolDesc(Hkv, D, BS, N)
 
 
@@ -203,6 +209,23 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale:
             raise ValueError("workspace must be a contiguous GPU tensor")
         nbytes = workspace.numel() * workspace.element_size()
         _check(lib.pkv_paged_decode_attention_ws(*args, _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def paged_decode_attention_planned(q, k_pool, v_pool, block_tables, context_lens, scale: float, plan: dict,
+                                   out=None, workspace=None, stream=None):
+    """Decode attention with an explicit launch plan (pkv_paged_decode_attention_planned); ``plan`` has the keys
+    num_splits, chunk_blocks, waves_per_group.  workspace=None uses the library's own."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.float16, "out", 3)
+    pl = DecodePlan(int(plan["num_splits"]), int(plan.get("chunk_blocks", 0)), int(plan["waves_per_group"]), 0, 0)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().pkv_paged_decode_attention_planned(_ptr(q), _ptr(k_pool), _ptr(v_pool), pool, _ptr(block_tables),
+                                                     M, _ptr(context_lens), B, Hq, float(scale), _ptr(out),
+                                                     ctypes.byref(pl), _ptr(workspace), nbytes, _stream(stream)))
     return out
 
 

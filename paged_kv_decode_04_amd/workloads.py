@@ -4,9 +4,10 @@ The tests, the smoke check and the benchmark draw every input here, and the same
 library and the CPU oracle.  This module draws random numbers and builds index structures (context lengths, block
 tables, slot mappings); it holds none of the attention arithmetic and imports neither the oracle nor the HIP binding.
 
-Pool layouts, fixed by the library's header:
-    k_pool[N][Hkv][BS][D] fp16      (one row of D per token)
-    v_pool[N][Hkv][D][BS] fp16      (V stored transposed inside each (block, kv head) tile)
+Pool layouts, fixed by the library's header (each block is BS/16 panels of 16 rows):
+    k_pool[N][Hkv][BS/16][D/8][16][8] fp16  (a panel holds each row's dims in 8-wide pieces, piece-major)
+    v_pool[N][Hkv][BS/16][D][16] fp16       (a panel holds V transposed, dim-major)
+Use k_row / v_row / set_k_row / set_v_row to address one token row.
 
 Randomness: numpy PCG64 streams keyed by ``SeedSequence([seed, rotation, tag])``; large arrays are filled in fixed
 chunks of ``_CHUNK`` elements, chunk c from ``SeedSequence([seed, rotation, tag, c])``, so the result does not depend
@@ -95,8 +96,8 @@ class DecodeCase:
     context_lens: np.ndarray           # [B] int32, rows including the newest token
     block_tables: np.ndarray           # [B][M] int32
     q: Optional[np.ndarray] = None      # [B][Hq][D] fp16
-    k_pool: Optional[np.ndarray] = None  # [N][Hkv][BS][D] fp16
-    v_pool: Optional[np.ndarray] = None  # [N][Hkv][D][BS] fp16
+    k_pool: Optional[np.ndarray] = None  # [N][Hkv][BS/16][D/8][16][8] fp16
+    v_pool: Optional[np.ndarray] = None  # [N][Hkv][BS/16][D][16] fp16
     k_new: Optional[np.ndarray] = None   # [T][Hkv][D] fp16, the rows appended this step
     v_new: Optional[np.ndarray] = None   # [T][Hkv][D] fp16
     slot_mapping: Optional[np.ndarray] = None  # [T] int32
@@ -145,12 +146,34 @@ def poison_rows(k_pool: np.ndarray, v_pool: np.ndarray, slots: np.ndarray, BS: i
         if slot < 0:
             continue
         b, o = int(slot) // BS, int(slot) % BS
-        k_pool[b, :, o, :] = POISON
-        v_pool[b, :, :, o] = POISON
+        k_pool[b, :, o // 16, :, o % 16, :] = POISON
+        v_pool[b, :, o // 16, :, o % 16] = POISON
 
 
 def _alloc_pools(N, Hkv, BS, D):
-    return (np.empty((N, Hkv, BS, D), dtype=np.float16), np.empty((N, Hkv, D, BS), dtype=np.float16))
+    if BS % 16 or D % 8:
+        raise ValueError("block_size must be a multiple of 16 and head_dim a multiple of 8")
+    return (np.empty((N, Hkv, BS // 16, D // 8, 16, 8), dtype=np.float16),
+            np.empty((N, Hkv, BS // 16, D, 16), dtype=np.float16))
+
+
+def k_row(k_pool: np.ndarray, block: int, head: int, offset: int) -> np.ndarray:
+    """The D values of K row `offset` of (block, head), read through the panel layout."""
+    return k_pool[block, head, offset // 16, :, offset % 16, :].reshape(-1)
+
+
+def v_row(v_pool: np.ndarray, block: int, head: int, offset: int) -> np.ndarray:
+    return v_pool[block, head, offset // 16, :, offset % 16]
+
+
+def set_k_row(k_pool: np.ndarray, block: int, head, offset: int, row) -> None:
+    """Write K row(s) of D values at (block, head(s), offset)."""
+    r = np.asarray(row, dtype=np.float16)
+    k_pool[block, head, offset // 16, :, offset % 16, :] = r.reshape(r.shape[:-1] + (-1, 8))
+
+
+def set_v_row(v_pool: np.ndarray, block: int, head, offset: int, row) -> None:
+    v_pool[block, head, offset // 16, :, offset % 16] = np.asarray(row, dtype=np.float16)
 
 
 def build_case(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int, context_lens, N: int, M: int, scale: float,

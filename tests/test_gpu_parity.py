@@ -74,8 +74,8 @@ def test_append_bit_exact_small(torch_cuda):
     rng = np.random.default_rng(5)
     for (N, Hkv, BS, D, T) in [(9, 3, 16, 64, 20), (40, 8, 16, 128, 64), (5, 16, 32, 256, 7), (4, 2, 64, 128, 30)]:
         say("append N=%d Hkv=%d BS=%d D=%d T=%d" % (N, Hkv, BS, D, T))
-        k_pool = rng.standard_normal((N, Hkv, BS, D)).astype(np.float16)
-        v_pool = rng.standard_normal((N, Hkv, D, BS)).astype(np.float16)
+        k_pool = rng.standard_normal((N, Hkv, BS // 16, D // 8, 16, 8)).astype(np.float16)
+        v_pool = rng.standard_normal((N, Hkv, BS // 16, D, 16)).astype(np.float16)
         slots = rng.choice(N * BS, size=T, replace=False).astype(np.int32)
         slots[1] = -1
         slots[-1] = N * BS + 3  # out of range: skipped
@@ -223,7 +223,7 @@ def test_single_row_returns_v_bitwise_at_any_split(torch_cuda):
         for s in range(c.B):
             b = int(c.block_tables[s, 0])
             for hq in range(c.Hq):
-                assert np.array_equal(out[s, hq].view(np.uint16), c.v_pool[b, hq // c.G, :, 0].view(np.uint16))
+                assert np.array_equal(out[s, hq].view(np.uint16), W.v_row(c.v_pool, b, hq // c.G, 0).view(np.uint16))
 
 
 def test_block_shuffle_is_bitwise_invariant(torch_cuda):

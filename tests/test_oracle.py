@@ -31,13 +31,27 @@ def _nums(a):
     return _num(a)
 
 
+def _pad8(x, D):
+    """Zero-pad the last axis from D to the next multiple of 8 (the K layout needs D % 8 == 0); zero dims change
+    no dot product, and the outputs on them are sums of zeros."""
+    x = np.asarray(x, dtype=np.float64)
+    Dp = (D + 7) // 8 * 8
+    pad = [(0, 0)] * (x.ndim - 1) + [(0, Dp - D)]
+    return np.pad(x, pad)
+
+
+def _zero_pools(N, Hkv, BS, D):
+    return (np.zeros((N, Hkv, BS // 16, D // 8, 16, 8), dtype=np.float16),
+            np.zeros((N, Hkv, BS // 16, D, 16), dtype=np.float16))
+
+
 def _pools_from_rows(case):
     N, Hkv, BS, D = case["N"], case["Hkv"], case["BS"], case["D"]
-    k_pool = np.zeros((N, Hkv, BS, D), dtype=np.float16)
-    v_pool = np.zeros((N, Hkv, D, BS), dtype=np.float16)
+    Dp = (D + 7) // 8 * 8
+    k_pool, v_pool = _zero_pools(N, Hkv, BS, Dp)
     for r in case["rows"]:
-        k_pool[r["block"], r["head"], r["offset"], :] = np.array(r["k"], dtype=np.float16)
-        v_pool[r["block"], r["head"], :, r["offset"]] = np.array(r["v"], dtype=np.float16)
+        W.set_k_row(k_pool, r["block"], r["head"], r["offset"], _pad8(r["k"], D))
+        W.set_v_row(v_pool, r["block"], r["head"], r["offset"], _pad8(r["v"], D))
     return k_pool, v_pool
 
 
@@ -57,13 +71,26 @@ def test_f16_decode_matches_numpy_on_every_bit_pattern():
 
 def test_pool_index_functions_match_numpy_strides():
     rng = np.random.default_rng(7)
-    for (N, Hkv, BS, D) in [(5, 3, 16, 64), (2, 1, 32, 256), (7, 8, 16, 128)]:
-        k = np.empty((N, Hkv, BS, D), dtype=np.float16)
-        v = np.empty((N, Hkv, D, BS), dtype=np.float16)
+    for (N, Hkv, BS, D) in [(5, 3, 16, 64), (2, 1, 32, 256), (7, 8, 16, 128), (3, 2, 64, 8)]:
+        k = np.empty((N, Hkv, BS // 16, D // 8, 16, 8), dtype=np.float16)
+        v = np.empty((N, Hkv, BS // 16, D, 16), dtype=np.float16)
         for _ in range(50):
             b, h, o, d = (int(rng.integers(N)), int(rng.integers(Hkv)), int(rng.integers(BS)), int(rng.integers(D)))
-            assert oracle.k_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(k.strides, (b, h, o, d))
-            assert oracle.v_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(v.strides, (b, h, d, o))
+            assert oracle.k_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(k.strides, (b, h, o // 16, d // 8, o % 16, d % 8))
+            assert oracle.v_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(v.strides, (b, h, o // 16, d, o % 16))
+
+
+def test_row_helpers_round_trip():
+    rng = np.random.default_rng(8)
+    k, v = _zero_pools(3, 2, 32, 32)
+    row = rng.standard_normal(32).astype(np.float16)
+    W.set_k_row(k, 1, 1, 21, row)
+    W.set_v_row(v, 1, 1, 21, row)
+    assert np.array_equal(W.k_row(k, 1, 1, 21), row) and np.array_equal(W.v_row(v, 1, 1, 21), row)
+    assert np.count_nonzero(k) == np.count_nonzero(row) == np.count_nonzero(v)
+    for d in range(32):
+        assert k.reshape(-1)[oracle.k_index(2, 32, 32, 1, 1, 21, d)] == row[d]
+        assert v.reshape(-1)[oracle.v_index(2, 32, 32, 1, 1, 21, d)] == row[d]
 
 
 # --------------------------------------------------------------------------------------------------------------
@@ -78,12 +105,12 @@ def _golden_attention_cases():
 @pytest.mark.parametrize("case", _golden_attention_cases(), ids=lambda c: c["name"])
 def test_golden_attention(case):
     k_pool, v_pool = _pools_from_rows(case)
-    q = np.array(case["q"], dtype=np.float16)
+    q = _pad8(case["q"], case["D"]).astype(np.float16)
     bt = np.array(case["block_tables"], dtype=np.int32)
     cl = np.array(case["context_lens"], dtype=np.int32)
     scale = _num(case["scale"])
     out = oracle.decode_attention(q, k_pool, v_pool, bt, cl, scale, threads=2)
-    np.testing.assert_allclose(out, np.array(case["expected"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(out, _pad8(case["expected"], case["D"]), rtol=1e-14, atol=1e-14)
     if "weights" in case:
         for s, wexp in enumerate(case["weights"]):
             _, w = oracle.attention_weights(q, k_pool, v_pool, bt, cl, scale, s, 0)
@@ -113,13 +140,18 @@ def test_golden_append():
     with open(os.path.join(GOLDEN, "append_hand.json")) as f:
         cases = json.load(f)["cases"]
     for c in cases:
-        k_pool = np.zeros((c["N"], c["Hkv"], c["BS"], c["D"]), dtype=np.float16)
-        v_pool = np.zeros((c["N"], c["Hkv"], c["D"], c["BS"]), dtype=np.float16)
+        N, Hkv, BS, D = c["N"], c["Hkv"], c["BS"], c["D"]
+        k_pool, v_pool = _zero_pools(N, Hkv, BS, D)
         skipped = oracle.paged_kv_append(np.array(c["k"], np.float16), np.array(c["v"], np.float16),
                                          c["slot_mapping"], k_pool, v_pool)
         assert skipped == c["expected_skipped"]
-        assert np.array_equal(k_pool, np.array(c["expected_k_pool"], np.float16))
-        assert np.array_equal(v_pool, np.array(c["expected_v_pool"], np.float16))
+        k_exp = np.zeros_like(k_pool)
+        v_exp = np.zeros_like(v_pool)
+        for r in c["expected_rows"]:
+            W.set_k_row(k_exp, r["block"], r["head"], r["offset"], r["k"])
+            W.set_v_row(v_exp, r["block"], r["head"], r["offset"], r["v"])
+        assert np.array_equal(k_pool, k_exp)
+        assert np.array_equal(v_pool, v_exp)
 
 
 # --------------------------------------------------------------------------------------------------------------
@@ -141,8 +173,8 @@ def _rows(c, s, hk):
     ks, vs = [], []
     for t in range(L):
         b = int(c.block_tables[s, t // c.BS])
-        ks.append(c.k_pool[b, hk, t % c.BS, :].astype(np.float64))
-        vs.append(c.v_pool[b, hk, :, t % c.BS].astype(np.float64))
+        ks.append(W.k_row(c.k_pool, b, hk, t % c.BS).astype(np.float64))
+        vs.append(W.v_row(c.v_pool, b, hk, t % c.BS).astype(np.float64))
     return np.array(ks).reshape(L, c.D), np.array(vs).reshape(L, c.D)
 
 
@@ -209,7 +241,9 @@ def test_one_dominant_key_returns_its_value():
     q = np.zeros_like(c.q)
     q[s, :, 0] = np.float16(64.0)
     c.k_pool[...] = np.float16(0.0)
-    c.k_pool[b, 0, target % c.BS, 0] = np.float16(64.0)  # z = 4096 * scale = 512 vs 0 for every other row
+    row = np.zeros(c.D, np.float16)
+    row[0] = 64.0  # z = 64 * 64 * scale = 512 against 0 for every other row
+    W.set_k_row(c.k_pool, b, 0, target % c.BS, row)
     out = _run(c, q=q)
     _, v = _rows(c, s, 0)
     np.testing.assert_allclose(out[s, 0], v[target], rtol=1e-15, atol=1e-15)
@@ -243,8 +277,8 @@ def _contiguous_problem(seed, B, Hq, Hkv, D, BS, lens, scale):
     M = max(nbs)
     perm = rng.permutation(N).astype(np.int32)
     bt = np.full((B, M), -1, np.int32)
-    k_pool = rng.standard_normal((N, Hkv, BS, D)).astype(np.float16)
-    v_pool = rng.standard_normal((N, Hkv, D, BS)).astype(np.float16)
+    k_pool = rng.standard_normal((N, Hkv, BS // 16, D // 8, 16, 8)).astype(np.float16)
+    v_pool = rng.standard_normal((N, Hkv, BS // 16, D, 16)).astype(np.float16)
     q = rng.standard_normal((B, Hq, D)).astype(np.float16)
     Kc, Vc = [], []
     pos = 0
@@ -255,8 +289,8 @@ def _contiguous_problem(seed, B, Hq, Hkv, D, BS, lens, scale):
         vs = rng.standard_normal((Hkv, L, D)).astype(np.float16)
         for t in range(L):
             b = bt[s, t // BS]
-            k_pool[b, :, t % BS, :] = ks[:, t, :]
-            v_pool[b, :, :, t % BS] = vs[:, t, :]
+            W.set_k_row(k_pool, b, slice(None), t % BS, ks[:, t, :])
+            W.set_v_row(v_pool, b, slice(None), t % BS, vs[:, t, :])
         Kc.append(ks)
         Vc.append(vs)
     return q, k_pool, v_pool, bt, np.array(lens, np.int32), Kc, Vc, G
@@ -266,7 +300,7 @@ def _contiguous_problem(seed, B, Hq, Hkv, D, BS, lens, scale):
     (2, 4, 2, 64, 16, (37, 90), 0.125),
     (3, 8, 1, 128, 16, (1, 17, 48), 1 / math.sqrt(128)),
     (2, 4, 4, 256, 32, (33, 70), 1 / 16),
-    (1, 16, 2, 32, 8, (25,), 0.3),
+    (1, 16, 2, 32, 64, (90,), 0.3),
 ])
 def test_paged_equals_contiguous_brute_force_and_torch_sdpa(geom):
     import torch
@@ -356,9 +390,9 @@ def test_combine_never_reads_past_the_valid_splits():
 
 def test_append_writes_rows_and_leaves_everything_else():
     rng = np.random.default_rng(31)
-    N, Hkv, BS, D, T = 9, 3, 16, 64, 20
-    k_pool = rng.standard_normal((N, Hkv, BS, D)).astype(np.float16)
-    v_pool = rng.standard_normal((N, Hkv, D, BS)).astype(np.float16)
+    N, Hkv, BS, D, T = 9, 3, 32, 64, 20
+    k_pool = rng.standard_normal((N, Hkv, BS // 16, D // 8, 16, 8)).astype(np.float16)
+    v_pool = rng.standard_normal((N, Hkv, BS // 16, D, 16)).astype(np.float16)
     k0, v0 = k_pool.copy(), v_pool.copy()
     slots = rng.choice(N * BS, size=T, replace=False).astype(np.int32)
     slots[3] = -1
@@ -372,13 +406,15 @@ def test_append_writes_rows_and_leaves_everything_else():
         if 0 <= sl < N * BS:
             b, o = divmod(int(sl), BS)
             touched[b, o] = True
-            assert np.array_equal(k_pool[b, :, o, :].view(np.uint16), k[i].view(np.uint16))
-            assert np.array_equal(v_pool[b, :, :, o].view(np.uint16), v[i].view(np.uint16))
+            for h in range(Hkv):
+                assert np.array_equal(W.k_row(k_pool, b, h, o).view(np.uint16), k[i, h].view(np.uint16))
+                assert np.array_equal(W.v_row(v_pool, b, h, o).view(np.uint16), v[i, h].view(np.uint16))
     for b in range(N):
         for o in range(BS):
             if not touched[b, o]:
-                assert np.array_equal(k_pool[b, :, o, :].view(np.uint16), k0[b, :, o, :].view(np.uint16))
-                assert np.array_equal(v_pool[b, :, :, o].view(np.uint16), v0[b, :, :, o].view(np.uint16))
+                for h in range(Hkv):
+                    assert np.array_equal(W.k_row(k_pool, b, h, o), W.k_row(k0, b, h, o))
+                    assert np.array_equal(W.v_row(v_pool, b, h, o), W.v_row(v0, b, h, o))
 
 
 def test_append_then_attention_sees_the_new_row():

@@ -57,8 +57,9 @@ def test_c1_structure():
     assert c.slot_mapping.tolist() == [int(c.block_tables[0, 2]) * 16 + 4]
     assert c.k_new.shape == (1, 2, 64)
     b, o = divmod(int(c.slot_mapping[0]), 16)
-    assert np.all(c.k_pool[b, :, o, :] == np.float16(W.POISON))
-    assert np.all(c.v_pool[b, :, :, o] == np.float16(W.POISON))
+    for h in range(c.Hkv):
+        assert np.all(W.k_row(c.k_pool, b, h, o) == np.float16(W.POISON))
+        assert np.all(W.v_row(c.v_pool, b, h, o) == np.float16(W.POISON))
     assert _digest(c.q, c.k_pool, c.v_pool) == _digest(*(lambda d: (d.q, d.k_pool, d.v_pool))(W.config_c1()))
 
 
