@@ -6,6 +6,8 @@ are seeded synthetic data already resident in HBM; R independent copies rotate b
 Infinity Cache cannot hold a step's working set (R=4 for c2).
 
     python bench.py [--steps K] [--warmup W] [--config c2] [--splits S] [--rotations R] [--no-cpu-baseline]
+    python bench.py --copy-calibration-mib 512 ...     also runs a plain copy kernel (torch.neg, out=) of known size
+    python bench.py --summarize-pmc FETCH.csv WRITE.csv --config c2   writes profiles/traffic_<config>_s<S>.json
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value        algorithmic HBM bytes of a step / measured step time, in GB/s (whole job, one GPU)
@@ -67,6 +69,53 @@ def measured_traffic(config: str, splits: int):
     return rec.get("hbm_bytes_per_step")
 
 
+def _pmc_per_dispatch(path: str, counter: str) -> dict:
+    """{dispatch id: (kernel name, counter value)} from a rocprofv3 --pmc CSV (values summed over the counter's
+    instances)."""
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name", counter) != counter:
+                continue
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            name, val = rows.get(key, (r.get("Kernel_Name", ""), 0.0))
+            rows[key] = (name, val + float(r["Counter_Value"]))
+    return rows
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy_mib: float) -> dict:
+    """HBM traffic per decode step from two counter passes (FETCH_SIZE then WRITE_SIZE, KiB per dispatch), each
+    scaled by what the same counter reads for the plain copy kernel (reads and writes copy_mib MiB)."""
+    out = {"config": config, "num_splits": splits, "kernel_source_hash": kernel_source_hash()}
+    factors = {}
+    per_kernel = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_per_dispatch(path, counter)
+        copy = [v for n, v in rows.values() if "neg" in n.lower()]
+        if not copy:
+            raise SystemExit("no copy-calibration dispatches (torch.neg) in %s" % path)
+        measured_kib = sum(copy) / len(copy)
+        factors[counter] = copy_mib * 1024.0 / measured_kib
+        for n, v in rows.values():
+            if "pkv::" in n:
+                short = n.split("(")[0].replace("void ", "")
+                per_kernel.setdefault(short, {}).setdefault(counter, []).append(v)
+    step_bytes = 0.0
+    kern = {}
+    for short, cnt in per_kernel.items():
+        f = sum(cnt.get("FETCH_SIZE", [0])) / max(1, len(cnt.get("FETCH_SIZE", [0])))
+        w = sum(cnt.get("WRITE_SIZE", [0])) / max(1, len(cnt.get("WRITE_SIZE", [0])))
+        fb = f * 1024 * factors["FETCH_SIZE"]
+        wb = w * 1024 * factors["WRITE_SIZE"]
+        kern[short] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": len(cnt.get("FETCH_SIZE", []))}
+        if "append" not in short:
+            step_bytes += fb + wb
+    out.update({"copy_calibration_mib": copy_mib, "scale_factors": factors, "kernels": kern,
+                "hbm_bytes_per_step": round(step_bytes)})
+    return out
+
+
 def cpu_baseline(case, seconds: float):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -95,7 +144,20 @@ def main(argv=None) -> int:
     ap.add_argument("--rotations", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=float, default=0.0,
+                    help="also run a plain copy kernel over this many MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args(argv)
+
+    if args.summarize_pmc:
+        splits = WORKLOADS[args.config][1] if args.splits is None else args.splits
+        rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config, splits,
+                            args.copy_calibration_mib or 512.0)
+        path = os.path.join(ROOT, "profiles", "traffic_%s_s%d.json" % (args.config, splits))
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -145,6 +207,16 @@ def main(argv=None) -> int:
                                    out=d["out"], num_splits=splits)
         if ev is not None:
             ev[1].record()
+
+    if args.copy_calibration_mib > 0:
+        n = int(args.copy_calibration_mib * (1 << 20)) // 2
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log("ran the copy calibration kernel (%.0f MiB read + written) 10 times" % args.copy_calibration_mib)
 
     for i in range(args.warmup):
         step(sets[i % R])
