@@ -1,7 +1,9 @@
 """Benchmark: one decode step of the paged-KV hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: the paged KV append of every sequence's newest row, then
-paged decode attention (single pass, or split-K phase 1 + combine, as the workload's dispatch mode says).  Inputs
+paged decode attention (single pass, or split-K phase 1 + combine, as the workload's dispatch mode says).  By default
+the step is the library's fused decode step (pkv_paged_decode_step: append and attention in one launch); --unfused
+times the two separate entry points (pkv_paged_kv_append, then pkv_paged_decode_attention).  Inputs
 are seeded synthetic data already resident in HBM; R independent copies rotate between steps so that the ~256 MB
 Infinity Cache cannot hold a step's working set (R=4 for c2).
 
@@ -11,10 +13,10 @@ Infinity Cache cannot hold a step's working set (R=4 for c2).
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value        algorithmic HBM bytes of a step / measured step time, in GB/s (whole job, one GPU)
-  roofline     the attention kernel(s) alone: algorithmic bytes / average duration from HIP events recorded around
-               each attention call inside the timed region, against the 8 TB/s HBM peak; `traffic` is the measured
-               HBM bytes per launch from the committed rocprofv3 counter summary when it was taken on the current
-               kernel source, else null
+  roofline     the dominant kernel: algorithmic bytes / its average duration from HIP events on its stream in the
+               timed region (a fused single-pass step is one launch: region time / K; otherwise an event pair
+               around each attention call), against the 8 TB/s HBM peak; `traffic` is the measured HBM bytes per launch from the committed
+               rocprofv3 counter summary when it was taken on the current kernel source, else null
   cpu_baseline the CPU oracle (f64, threads = the host cores it used) on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -57,9 +59,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config: str, splits: int):
-    """HBM bytes per attention launch from profiles/traffic_<config>_s<splits>.json, if taken on this source."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s_s%d.json" % (config, splits))
+def traffic_path(config: str, splits: int, fused: bool) -> str:
+    return os.path.join(ROOT, "profiles", "traffic_%s_s%d%s.json" % (config, splits, "_fused" if fused else ""))
+
+
+def measured_traffic(config: str, splits: int, fused: bool):
+    """HBM bytes per launch of the dominant kernel from its traffic summary under profiles/, if taken on this
+    source."""
+    path = traffic_path(config, splits, fused)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -147,13 +154,15 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration-mib", type=float, default=0.0,
                     help="also run a plain copy kernel over this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--unfused", action="store_true",
+                    help="append and attention as two launches instead of the fused decode step")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
         splits = WORKLOADS[args.config][1] if args.splits is None else args.splits
         rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config, splits,
                             args.copy_calibration_mib or 512.0)
-        path = os.path.join(ROOT, "profiles", "traffic_%s_s%d.json" % (args.config, splits))
+        path = traffic_path(args.config, splits, not args.unfused)
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
@@ -187,6 +196,12 @@ def main(argv=None) -> int:
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         d = dict(q=t(c.q), k_pool=t(c.k_pool), v_pool=t(c.v_pool), bt=t(c.block_tables), cl=t(c.context_lens),
                  k_new=t(c.k_new), v_new=t(c.v_new), slots=t(c.slot_mapping), case=c)
+        # one new row per sequence for the fused step (rows of empty sequences are never written)
+        kn = np.zeros((c.B, c.Hkv, c.D), np.float16)
+        vn = np.zeros_like(kn)
+        nz = np.nonzero(c.context_lens > 0)[0]
+        kn[nz], vn[nz] = c.k_new, c.v_new
+        d["k_new_all"], d["v_new_all"] = t(kn), t(vn)
         d["out"] = torch.empty_like(d["q"])
         d["bytes"] = W.algorithmic_bytes(c)
         if r == 0:
@@ -199,12 +214,24 @@ def main(argv=None) -> int:
     plan = pkv.plan_decode(c0.B, c0.Hq, c0.Hkv, c0.D, c0.BS, c0.M, num_splits=splits)
     log("plan: %s, %s" % (plan, pkv.version()))
 
+    fused = not args.unfused
+    # arguments marshalled once per rotation set (the binding's prepared calls): per-step Python marshalling would
+    # otherwise outlast the kernel and leave the GPU idle between steps
+    for d in sets:
+        if fused:
+            d["call"] = pkv.prepare_decode_step(d["q"], d["k_new_all"], d["v_new_all"], d["k_pool"], d["v_pool"],
+                                                d["bt"], d["cl"], d["case"].scale, d["out"], num_splits=splits)
+        else:
+            d["append"] = pkv.prepare_paged_kv_append(d["k_new"], d["v_new"], d["slots"], d["k_pool"], d["v_pool"])
+            d["call"] = pkv.prepare_paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
+                                                           d["case"].scale, d["out"], num_splits=splits)
+
     def step(d, ev=None):
-        pkv.paged_kv_append(d["k_new"], d["v_new"], d["slots"], d["k_pool"], d["v_pool"])
+        if not fused:
+            d["append"]()
         if ev is not None:
             ev[0].record()
-        pkv.paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"], d["case"].scale,
-                                   out=d["out"], num_splits=splits)
+        d["call"]()
         if ev is not None:
             ev[1].record()
 
@@ -223,27 +250,33 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # When a step is one launch (the fused single-pass step), the kernel's average duration is the timed region / K
+    # and no per-launch events are recorded (an event pair costs ~7 us of stream time per step here, more than the
+    # launch gaps it would exclude); otherwise an event pair brackets the attention call of every step.
+    one_launch = fused and plan["num_splits"] == 1
+    evs = None if one_launch else [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                                   for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
-        step(sets[i % R], evs[i])
+        step(sets[i % R], None if evs is None else evs[i])
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
     ms_per_step = total_ms / K
+    attn_ms = np.array([ms_per_step] if evs is None else [a.elapsed_time(b) for a, b in evs])
 
     # bytes per step, averaged over the rotation sets
     step_bytes = np.mean([d["bytes"]["attention"] + d["bytes"]["append"] for d in sets])
     attn_bytes = np.mean([d["bytes"]["attention"] for d in sets])
+    kernel_bytes = step_bytes if fused else attn_bytes  # algorithmic bytes of one launch of the dominant kernel
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     attn_avg_ms = float(attn_ms.mean())
-    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    achieved = kernel_bytes / (attn_avg_ms * 1e-3) / 1e9
     calls_per_s = 1e3 / attn_avg_ms
-    log("step %.4f ms (%.1f GB/s); attention avg %.4f ms median %.4f p90 %.4f -> %.1f GB/s, %.0f calls/s"
-        % (ms_per_step, value, attn_avg_ms, float(np.median(attn_ms)), float(np.percentile(attn_ms, 90)),
+    log("step %.4f ms (%.1f GB/s); %s avg %.4f ms median %.4f p90 %.4f -> %.1f GB/s, %.0f calls/s"
+        % (ms_per_step, value, "fused step kernel" if fused else "attention", attn_avg_ms, float(np.median(attn_ms)), float(np.percentile(attn_ms, 90)),
            achieved, calls_per_s))
 
     cpu = None
@@ -269,13 +302,15 @@ def main(argv=None) -> int:
             "workload": "%s: %s" % (args.config, desc),
             "num_seqs": c0.B, "num_q_heads": c0.Hq, "num_kv_heads": c0.Hkv, "head_dim": c0.D,
             "block_size": c0.BS, "num_splits": splits, "plan": plan, "rotations": R,
+            "step": "fused (pkv_paged_decode_step)" if fused else "pkv_paged_kv_append + pkv_paged_decode_attention",
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100.0 * float(value) / PEAK_GBS, 2),
         "calls_per_s": round(calls_per_s, 1),
         "tokens_per_s": round(calls_per_s * c0.B, 1),
-        "attention_ms": {"mean": round(attn_avg_ms, 5), "median": round(float(np.median(attn_ms)), 5),
-                         "p90": round(float(np.percentile(attn_ms, 90)), 5)},
+        "kernel_ms": {"mean": round(attn_avg_ms, 5), "median": round(float(np.median(attn_ms)), 5),
+                      "p90": round(float(np.percentile(attn_ms, 90)), 5),
+                      "timing": "region / steps (one launch per step)" if evs is None else "event pair per launch"},
         "bytes_per_step": {"attention": int(attn_bytes), "append": int(np.mean([d["bytes"]["append"] for d in sets]))},
         "roofline": {
             "bound": "hbm",
@@ -283,7 +318,7 @@ def main(argv=None) -> int:
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(float(achieved) / PEAK_GBS, 4),
-            "traffic": measured_traffic(args.config, splits),
+            "traffic": measured_traffic(args.config, splits, fused),
         },
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),

@@ -161,12 +161,32 @@ int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, con
                                   int32_t num_splits, int32_t max_context_hint, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * pkv_paged_decode_step -- the decode step fused into one launch: for every
+ *   sequence s with L_s = context_lens[s] > 0, first writes k_new[s][h][:] and
+ *   v_new[s][h][:] (every kv head h) to row L_s - 1 of the sequence -- block
+ *   block_tables[s][(L_s-1)/BS], row (L_s-1)%BS, the slot the callers on
+ *   [kapsl-backends 0.1.1, src/gguf_native.rs: forward_batch_decode_greedy]
+ *   form for launch_batch_kv_write -- then computes exactly what
+ *   pkv_paged_decode_attention computes over the updated pools.  A row whose
+ *   table entry names no pool block is not written.
+ *   k_new, v_new: [num_seqs][Hkv][D] fp16 (k_new 16-byte aligned).  The block
+ *   holding each sequence's newest row must belong to that sequence alone (no
+ *   other sequence of the batch may read it).  Other arguments, workspace and
+ *   errors as pkv_paged_decode_attention.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                          uint16_t *v_pool, pkv_pool_desc pool, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                          int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
+                          int32_t max_context_hint, void *stream);
+
 /* Same computation with a caller-chosen launch plan (from pkv_plan_decode, or
  * tuned by the caller: split count, fixed-size block chunks, waves per
  * workgroup).  The plan is checked (PKV_EINVAL / PKV_EUNSUPPORTED): num_splits
  * in [1, 65535], chunk_blocks >= 0 and, for num_splits > 1 with chunk_blocks > 0,
  * num_splits * chunk_blocks >= max_blocks_per_seq; waves_per_group in
- * {1, 2, 4, 8}.  workspace == NULL uses the library-owned workspace, otherwise
+ * {1, 2, 4, 8}, and at most 4 for head_dim 256 (PKV_EUNSUPPORTED).  workspace == NULL uses the library-owned workspace, otherwise
  * it must hold plan->workspace_bytes as computed by pkv_decode_workspace_bytes
  * for plan->num_splits (PKV_EWORKSPACE). */
 int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,

@@ -6,8 +6,9 @@ Every HIP translation unit is compiled with packed-FP32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns that
 it does not know the feature, which is harmless.  After linking, the gfx950
 assembly of the kernels is generated once more and searched for packed-FP32
-arithmetic (v_pk_add_f32 / v_pk_mul_f32 / v_pk_fma_f32); the build fails if
-any appears.
+arithmetic (v_pk_add_f32 / v_pk_mul_f32 / v_pk_fma_f32), and the kernel
+metadata for private (scratch) segments: the build fails if packed-FP32
+arithmetic appears or if any kernel spills registers to scratch memory.
 """
 from __future__ import annotations
 
@@ -31,6 +32,7 @@ COMMON = ["-std=c++17", "-O3", "--offload-arch=" + ARCH, "-fPIC", "-Wall",
           "-I", INCLUDE, "-I", CSRC]
 
 _PACKED_F32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
+_KERNEL_META = re.compile(r"^\s+\.name:\s+(\S+)\s*$|^\s+\.private_segment_fixed_size:\s+(\d+)", re.M)
 
 
 def _run(cmd):
@@ -51,6 +53,16 @@ def check_no_packed_fp32() -> None:
             hits = sorted(set(m.group(0) for m in _PACKED_F32.finditer(text)))
             if hits:
                 raise RuntimeError("packed-FP32 instructions in %s: %s" % (src, ", ".join(hits)))
+            spills, name = [], None
+            for m in _KERNEL_META.finditer(text):  # each kernel's .name precedes its segment size
+                if m.group(1) is not None:
+                    name = m.group(1)
+                elif name is not None:
+                    if int(m.group(2)):
+                        spills.append("%s (%s B)" % (name, m.group(2)))
+                    name = None
+            if spills:
+                raise RuntimeError("kernels using scratch memory in %s: %s" % (src, ", ".join(spills)))
 
 
 def build(verbose: bool = False) -> str:

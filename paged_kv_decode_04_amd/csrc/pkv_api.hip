@@ -233,8 +233,8 @@ int plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int
     if ((int64_t)num_seqs * num_kv_heads * S > INT32_MAX)
         return fail(PKV_EINVAL, "num_seqs * num_kv_heads * num_splits overflows the grid");
     int waves = S == 1 ? 8 : 4;
-    if (waves > pkv::max_waves_per_group())
-        waves = pkv::max_waves_per_group();
+    if (waves > pkv::max_waves_per_group(head_dim))
+        waves = pkv::max_waves_per_group(head_dim);
     const size_t limit = lds_limit > 0 ? (size_t)lds_limit : (size_t)65536;
     while (waves > 1 && pkv::decode_lds_bytes(head_dim, G, waves) > limit)
         waves >>= 1;
@@ -286,6 +286,9 @@ int check_plan(const pkv_decode_plan &plan, int32_t num_seqs, int32_t num_q_head
     const int w = plan.waves_per_group;
     if (w != 1 && w != 2 && w != 4 && w != 8)
         return fail(PKV_EINVAL, "plan.waves_per_group must be 1, 2, 4 or 8 (got %d)", w);
+    if (w > pkv::max_waves_per_group(pool.head_dim))
+        return fail(PKV_EUNSUPPORTED, "plan.waves_per_group %d exceeds the %d compiled for head_dim %d", w,
+                    pkv::max_waves_per_group(pool.head_dim), pool.head_dim);
     const size_t need = pkv::decode_lds_bytes(pool.head_dim, num_q_heads / pool.num_kv_heads, w);
     const size_t limit = lds_limit > 0 ? (size_t)lds_limit : (size_t)65536;
     if (need > limit)
@@ -297,10 +300,17 @@ int check_plan(const pkv_decode_plan &plan, int32_t num_seqs, int32_t num_q_head
 int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
              const pkv_pool_desc &pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
-             void *workspace, size_t workspace_bytes, bool library_ws, hipStream_t stream) {
+             void *workspace, size_t workspace_bytes, bool library_ws, hipStream_t stream,
+             const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr) {
     pkv::DecodeParams p = decode_params(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
                                         num_q_heads, scale);
     p.out = reinterpret_cast<_Float16 *>(out);
+    if (k_new) {  // fused decode step: the pools are written too
+        p.k_new = reinterpret_cast<const _Float16 *>(k_new);
+        p.v_new = reinterpret_cast<const _Float16 *>(v_new);
+        p.k_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
+        p.v_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
+    }
     if (plan.num_splits == 1) {
         hipError_t e = pkv::launch_decode(p, num_seqs, pool.head_dim, pool.block_size, plan.waves_per_group, false,
                                           stream);
@@ -353,7 +363,8 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
                 const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
                 int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
                 int32_t max_context_hint, const pkv_decode_plan *given, void *workspace, size_t workspace_bytes,
-                bool library_ws, hipStream_t stream) {
+                bool library_ws, hipStream_t stream, const uint16_t *k_new = nullptr,
+                const uint16_t *v_new = nullptr) {
     int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
     if (rc)
         return rc;
@@ -382,7 +393,7 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     if (rc)
         return rc;
     return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream);
+                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, k_new, v_new);
 }
 
 }  // namespace
@@ -455,6 +466,20 @@ int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                        num_q_heads, scale, out, 0, 0, plan, workspace, workspace_bytes, workspace == nullptr,
                        static_cast<hipStream_t>(stream));
+}
+
+int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                          uint16_t *v_pool, pkv_pool_desc pool, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                          int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
+                          int32_t max_context_hint, void *stream) {
+    if (num_seqs > 0 && (!k_new || !v_new))
+        return fail(PKV_EINVAL, "null device pointer (k_new=%p v_new=%p)", k_new, v_new);
+    if (num_seqs > 0 && (!aligned(k_new, 16) || !aligned(v_new, 2)))
+        return fail(PKV_EINVAL, "k_new must be 16-byte aligned");
+    return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
+                       static_cast<hipStream_t>(stream), k_new, v_new);
 }
 
 int pkv_plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -10,8 +10,8 @@ namespace pkv {
 // Arguments of the decode-attention kernel (single pass and split-K phase 1).
 struct DecodeParams {
     const _Float16 *q;            // [B][Hq][D]
-    const _Float16 *k_pool;       // [N][Hkv][BS][D]
-    const _Float16 *v_pool;       // [N][Hkv][D][BS]
+    const _Float16 *k_pool;       // [N][Hkv][BS/16][D/8][16][8]
+    const _Float16 *v_pool;       // [N][Hkv][BS/16][D][16]
     const int32_t *block_tables;  // [B][M]
     const int32_t *context_lens;  // [B]
     _Float16 *out;                // [B][Hq][D]            (single pass)
@@ -22,6 +22,12 @@ struct DecodeParams {
     int32_t num_splits;           // grid splits S (1 for a single pass)
     int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(nb / S) per sequence
     float scale_log2;             // scale * log2(e)
+    // fused decode step: when k_new is non-null, row L-1 of every sequence is first written from
+    // k_new / v_new ([B][Hkv][D]) into k_dst / v_dst (the same pools)
+    const _Float16 *k_new;
+    const _Float16 *v_new;
+    _Float16 *k_dst;
+    _Float16 *v_dst;
 };
 
 struct CombineParams {
@@ -54,6 +60,6 @@ hipError_t launch_append(const AppendParams &p, hipStream_t stream);
 
 // Geometry support of the compiled kernels.
 bool decode_geometry_supported(int head_dim, int block_size);
-int max_waves_per_group();
+int max_waves_per_group(int head_dim);  // largest compiled waves per workgroup
 
 }  // namespace pkv

@@ -127,12 +127,34 @@ __device__ __forceinline__ void load_unit(Frag<D, BS> &f, const _Float16 *kb, co
 
 // One 16-row unit: scores, online-softmax update, P.V accumulation.  A dead unit (its block id names no pool
 // block) is computed with every row masked, so that the loads of every unit are consumed on every path.
+//
+// prow >= 0 (fused decode step only): row prow of this unit is the token appended by this same launch; its K and V
+// come from registers loaded at kernel start (kpatch: lanes with r == prow hold its 8-dim pieces 4c + g4; vpatch:
+// lanes with g4 == prow / 4 hold dims 16c + r) instead of the loaded fragment, so the result never depends on when
+// the store of that row becomes visible, and no load sits on the last unit's critical path.
 template <int D, int BS>
 __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D / 32], f32x4 (&o)[D / 16],
-                                             float &m_run, float &l_run, int u, int L, bool dead, int g4,
-                                             float scale_log2) {
+                                             float &m_run, float &l_run, int u, int L, bool dead, int r, int g4,
+                                             float scale_log2, int prow, const f16x8 (&kpatch)[D / 32],
+                                             const _Float16 (&vpatch)[D / 16]) {
     constexpr int KC = Frag<D, BS>::KC;
     constexpr int VC = Frag<D, BS>::VC;
+    if (prow >= 0) {  // wave-uniform
+        if (r == prow) {
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                f.k[c] = kpatch[c];
+        }
+        if (g4 == (prow >> 2)) {
+            const int e = prow & 3;  // selects with constant element indices keep the fragment in registers
+#pragma unroll
+            for (int c = 0; c < VC; ++c) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    f.v[c][j] = (j == e) ? vpatch[c] : f.v[c][j];
+            }
+        }
+    }
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KC; ++c)
@@ -222,6 +244,51 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const int u_begin = b0 * SPB;
     const int u_end = min(b1 * SPB, (L + 15) >> 4);
 
+    // Fused decode step: the workgroup whose range holds row L-1 writes the sequence's new K/V row there (the slot
+    // the callers form from the table: block bt[(L-1)/BS], row (L-1)%BS).  The wave that will compute the unit
+    // holding that row loads the row into registers at start, stores it to the pool from them and later uses them
+    // in place of what it loads for that row (see compute_unit); no barrier waits on the stores.
+    const bool appending = p.k_new != nullptr && L > 0 && (L - 1) / BS >= b0 && (L - 1) / BS < b1;
+    const int patch_unit = appending ? (L - 1) >> 4 : -1;
+    const int prow_row = (L - 1) & 15;
+    f16x8 kpatch[KC];
+    _Float16 vpatch[VC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+        kpatch[c] = (f16x8)(_Float16)0.0f;
+#pragma unroll
+    for (int c = 0; c < VC; ++c)
+        vpatch[c] = (_Float16)0.0f;
+    // unit u is computed by wave (u - u_begin) % NW in every table window (a window is a multiple of NW units)
+    if (appending && wave == (patch_unit - u_begin) % NW) {
+        const _Float16 *kn = p.k_new + ((int64_t)s * p.Hkv + hk) * D;
+        const _Float16 *vn = p.v_new + ((int64_t)s * p.Hkv + hk) * D;
+        if (r == prow_row) {
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                kpatch[c] = *reinterpret_cast<const f16x8 *>(kn + 32 * c + 8 * g4);
+        }
+        if (g4 == (prow_row >> 2)) {
+#pragma unroll
+            for (int c = 0; c < VC; ++c)
+                vpatch[c] = vn[16 * c + r];
+        }
+        const int blk = uniform_load(bt, (L - 1) / BS);
+        if ((unsigned)blk < (unsigned)p.N) {
+            const int64_t panel = ((int64_t)blk * p.Hkv + hk) * (BS * D) + (((L - 1) % BS) / 16) * (16 * D);
+            if (r == prow_row) {  // K panel [D/8][16][8]: pieces 4c + g4 of the row
+#pragma unroll
+                for (int c = 0; c < KC; ++c)
+                    *reinterpret_cast<f16x8 *>(p.k_dst + panel + ((4 * c + g4) * 16 + prow_row) * 8) = kpatch[c];
+            }
+            if (g4 == (prow_row >> 2)) {  // V panel [D][16]: dims 16c + r of the row
+#pragma unroll
+                for (int c = 0; c < VC; ++c)
+                    p.v_dst[panel + (16 * c + r) * 16 + prow_row] = vpatch[c];
+            }
+        }
+    }
+
     // Q^T as the B operand: lane (g4, r) holds head r, dims 32c + 8*g4 .. +8.
     f16x8 qf[KC];
     {
@@ -291,7 +358,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
             load_unit<D, BS>(fb, k_ptr(blk_b, ub), v_ptr(blk_b, ub), k_lane, v_lane);
             int ua_next = k + 2 < n_units ? ub + NW : ub;
             int raw_a = raw_block(ua_next);
-            compute_unit<D, BS>(fa, qf, o, m_run, l_run, ua, L, dead_a, g4, p.scale_log2);
+            compute_unit<D, BS>(fa, qf, o, m_run, l_run, ua, L, dead_a, r, g4, p.scale_log2,
+                                ua == patch_unit ? prow_row : -1, kpatch, vpatch);
             if (++k >= n_units)
                 break;
             ua = ua_next;
@@ -299,7 +367,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
             load_unit<D, BS>(fa, k_ptr(blk_a, ua), v_ptr(blk_a, ua), k_lane, v_lane);
             int ub_next = k + 2 < n_units ? ua + NW : ua;
             raw_b = raw_block(ub_next);
-            compute_unit<D, BS>(fb, qf, o, m_run, l_run, ub, L, dead_b, g4, p.scale_log2);
+            compute_unit<D, BS>(fb, qf, o, m_run, l_run, ub, L, dead_b, r, g4, p.scale_log2,
+                                ub == patch_unit ? prow_row : -1, kpatch, vpatch);
             if (++k >= n_units)
                 break;
             ub = ub_next;
@@ -453,7 +522,9 @@ bool decode_geometry_supported(int head_dim, int block_size) {
            (block_size == 16 || block_size == 32 || block_size == 64);
 }
 
-int max_waves_per_group() { return kMaxWaves; }
+// Two K/V fragment sets of head dim 256 need more registers than a wave of an 8-wave group has, so that variant
+// would spill and is not compiled.
+int max_waves_per_group(int head_dim) { return head_dim >= 256 ? 4 : kMaxWaves; }
 
 template <int D, int BS, int NW>
 static hipError_t launch_decode_t(const DecodeParams &p, int num_seqs, bool split, hipStream_t stream) {
@@ -473,7 +544,11 @@ static hipError_t launch_decode_w(const DecodeParams &p, int num_seqs, int waves
     case 1: return launch_decode_t<D, BS, 1>(p, num_seqs, split, stream);
     case 2: return launch_decode_t<D, BS, 2>(p, num_seqs, split, stream);
     case 4: return launch_decode_t<D, BS, 4>(p, num_seqs, split, stream);
-    case 8: return launch_decode_t<D, BS, 8>(p, num_seqs, split, stream);
+    case 8:
+        if constexpr (D >= 256)
+            return hipErrorInvalidValue;
+        else
+            return launch_decode_t<D, BS, 8>(p, num_seqs, split, stream);
     default: return hipErrorInvalidValue;
     }
 }

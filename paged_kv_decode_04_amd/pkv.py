@@ -38,6 +38,7 @@ EXPORTED = [
     "pkv_paged_decode_attention",
     "pkv_paged_decode_attention_ws",
     "pkv_paged_decode_attention_planned",
+    "pkv_paged_decode_step",
     "pkv_plan_decode",
     "pkv_decode_workspace_bytes",
     "pkv_paged_decode_split_partials",
@@ -82,6 +83,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.pkv_paged_decode_attention.argtypes = attn + [vp]
         lib.pkv_paged_decode_attention_ws.argtypes = attn + [vp, sz, vp]
         lib.pkv_paged_decode_attention_planned.argtypes = attn[:11] + [ctypes.POINTER(DecodePlan), vp, sz, vp]
+        lib.pkv_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, vp, i32, i32,
+                                              vp]
         lib.pkv_plan_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodePlan)]
         lib.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.pkv_decode_workspace_bytes.restype = sz
@@ -229,6 +232,24 @@ def paged_decode_attention_planned(q, k_pool, v_pool, block_tables, context_lens
     return out
 
 
+def paged_decode_step(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale: float, out=None,
+                      num_splits: int = 0, max_context_hint: int = 0, stream=None):
+    """Fused decode step (pkv_paged_decode_step): write each sequence's new K/V row at position L-1, then attend."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    _dev(k_new, torch.float16, "k_new", 3)
+    _dev(v_new, torch.float16, "v_new", 3)
+    if tuple(k_new.shape) != (B, pool.num_kv_heads, pool.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must be [B][Hkv][D] = %s" % ((B, pool.num_kv_heads, pool.head_dim),))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.float16, "out", 3)
+    _check(load().pkv_paged_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), pool,
+                                        _ptr(block_tables), M, _ptr(context_lens), B, Hq, float(scale), _ptr(out),
+                                        int(num_splits), int(max_context_hint), _stream(stream)))
+    return out
+
+
 def plan_decode(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
                 max_blocks_per_seq: int, max_context_hint: int = 0, num_splits: int = 0, cu_count: int = 0) -> dict:
     """The dispatcher's plan (pkv_plan_decode); cu_count > 0 keeps it a pure host computation."""
@@ -279,3 +300,70 @@ def paged_decode_split_combine(partial_out, partial_m, partial_l, context_lens, 
                                                  int(max_blocks_per_seq), int(S), int(chunk_blocks), _ptr(out),
                                                  _stream(stream)))
     return out
+
+
+class PreparedCall:
+    """A C entry point with its arguments marshalled once (device pointers, geometry, stream).  Calling it costs one
+    ctypes call and no Python-side checks: for tight decode loops where per-call marshalling would outlast the
+    kernel.  The tensors must stay alive, keep their storage, and the stream stay valid while the object is used."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep  # tensors referenced by the pointers
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != PKV_OK:
+            _check(rc)
+
+
+def prepare_decode_step(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale: float, out,
+                        num_splits: int = 0, max_context_hint: int = 0, stream=None) -> PreparedCall:
+    """pkv_paged_decode_step with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, torch.float16, n, 3)
+        if tuple(t.shape) != (B, pool.num_kv_heads, pool.head_dim):
+            raise ValueError("%s must be [B][Hkv][D]" % n)
+    _dev(out, torch.float16, "out", 3)
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(q)), ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
+            ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool, ctypes.c_void_p(_ptr(block_tables)),
+            ctypes.c_int32(M), ctypes.c_void_p(_ptr(context_lens)), ctypes.c_int32(B), ctypes.c_int32(Hq),
+            ctypes.c_float(scale), ctypes.c_void_p(_ptr(out)), ctypes.c_int32(num_splits),
+            ctypes.c_int32(max_context_hint), ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_paged_decode_step, args, (q, k_new, v_new, k_pool, v_pool, block_tables,
+                                                          context_lens, out))
+
+
+def prepare_paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,
+                                   num_splits: int = 0, max_context_hint: int = 0, stream=None) -> PreparedCall:
+    """pkv_paged_decode_attention with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    _dev(out, torch.float16, "out", 3)
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(q)), ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool,
+            ctypes.c_void_p(_ptr(block_tables)), ctypes.c_int32(M), ctypes.c_void_p(_ptr(context_lens)),
+            ctypes.c_int32(B), ctypes.c_int32(Hq), ctypes.c_float(scale), ctypes.c_void_p(_ptr(out)),
+            ctypes.c_int32(num_splits), ctypes.c_int32(max_context_hint), ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_paged_decode_attention, args, (q, k_pool, v_pool, block_tables, context_lens, out))
+
+
+def prepare_paged_kv_append(k, v, slot_mapping, k_pool, v_pool, stream=None) -> PreparedCall:
+    """pkv_paged_kv_append with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(k, torch.float16, "k", 3)
+    _dev(v, torch.float16, "v", 3)
+    _dev(slot_mapping, torch.int32, "slot_mapping", 1)
+    T = int(slot_mapping.shape[0])
+    if tuple(k.shape) != (T, pool.num_kv_heads, pool.head_dim) or k.shape != v.shape:
+        raise ValueError("k and v must be [T][Hkv][D]")
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(k)), ctypes.c_void_p(_ptr(v)), ctypes.c_void_p(_ptr(slot_mapping)),
+            ctypes.c_int32(T), ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool,
+            ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_paged_kv_append, args, (k, v, slot_mapping, k_pool, v_pool))

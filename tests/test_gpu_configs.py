@@ -54,6 +54,7 @@ def _step_and_check(torch, c, splits, units=None, whole_pool_check=False):
     say("%s: B=%d Hq=%d Hkv=%d D=%d BS=%d N=%d M=%d sum(L)=%d" % (c.name, c.B, c.Hq, c.Hkv, c.D, c.BS, c.N, c.M,
                                                                  int(c.context_lens.sum())))
     kp, vp = _dev(torch, c.k_pool), _dev(torch, c.v_pool)
+    poisoned = (c.k_pool.copy(), c.v_pool.copy())
     slots = _dev(torch, c.slot_mapping)
     pkv.paged_kv_append(_dev(torch, c.k_new), _dev(torch, c.v_new), slots, kp, vp)
     # the oracle applies the same append to the host pools
@@ -84,6 +85,26 @@ def _step_and_check(torch, c, splits, units=None, whole_pool_check=False):
         if units is not None:
             o = o[units[:, 0], units[:, 1]]
         _check(o, ref, "%s num_splits=%d" % (c.name, S))
+    del kp, vp
+    torch.cuda.empty_cache()
+    # the fused decode step (what bench.py times) on the poisoned pools: same pools, same outputs
+    kn = np.zeros((c.B, c.Hkv, c.D), np.float16)
+    vn = np.zeros_like(kn)
+    nz = np.nonzero(c.context_lens > 0)[0]
+    kn[nz], vn[nz] = c.k_new, c.v_new
+    poisoned_k, poisoned_v = poisoned
+    kp, vp = _dev(torch, poisoned_k), _dev(torch, poisoned_v)
+    del poisoned
+    out = pkv.paged_decode_step(q, _dev(torch, kn), _dev(torch, vn), kp, vp, bt, cl, c.scale, num_splits=splits[0])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    if units is not None:
+        o = o[units[:, 0], units[:, 1]]
+    _check(o, ref, "%s fused step num_splits=%d" % (c.name, splits[0]))
+    if whole_pool_check:
+        assert np.array_equal(kp.cpu().numpy().view(np.uint16), c.k_pool.view(np.uint16))
+        assert np.array_equal(vp.cpu().numpy().view(np.uint16), c.v_pool.view(np.uint16))
+        say("%s: fused step wrote both pools bit-exactly" % c.name)
     del kp, vp
     torch.cuda.empty_cache()
 

@@ -255,3 +255,71 @@ def test_split_counts_agree(torch_cuda):
         assert_close(o, ref, "S=%d" % S)
         # every split count lands within one fp16 rounding step of the single pass
         assert np.max(np.abs(o.astype(np.float64) - outs[1].astype(np.float64))) <= 1e-3
+
+
+# --------------------------------------------------------------------------------------------------------------
+# the fused decode step: append of every sequence's newest row + attention in one launch
+
+
+def full_new_rows(c):
+    """[B][Hkv][D] new K/V rows, one per sequence (the workload holds them only for non-empty sequences)."""
+    k = np.zeros((c.B, c.Hkv, c.D), np.float16)
+    v = np.zeros((c.B, c.Hkv, c.D), np.float16)
+    nz = np.nonzero(c.context_lens > 0)[0]
+    k[nz] = c.k_new
+    v[nz] = c.v_new
+    return k, v
+
+
+STEP_GEOMS = [
+    (3, 8, 2, 64, 16, (1, 16, 17)),
+    (4, 32, 8, 128, 16, (300, 129, 0, 32)),
+    (3, 40, 8, 128, 16, (200, 33, 15)),
+    (2, 16, 16, 256, 32, (257, 48)),
+    (2, 8, 2, 128, 64, (130, 64)),
+]
+
+
+@pytest.mark.parametrize("geom", STEP_GEOMS, ids=lambda g: "B%d_Hq%d_Hkv%d_D%d_BS%d" % g[:5])
+@pytest.mark.parametrize("num_splits", [1, 3, 0])
+def test_fused_step_matches_append_then_attention(torch_cuda, geom, num_splits):
+    torch = torch_cuda
+    from paged_kv_decode_04_amd import pkv
+    B, Hq, Hkv, D, BS, lens = geom
+    c = W.small_case(313 + D + BS, B, Hq, Hkv, D, BS, lens, poison=True, extra_blocks=4)
+    say("fused step %s S=%d" % (geom, num_splits))
+    kn, vn = full_new_rows(c)
+    dk, dv = _dev(torch, c.k_pool), _dev(torch, c.v_pool)
+    out = pkv.paged_decode_step(_dev(torch, c.q), _dev(torch, kn), _dev(torch, vn), dk, dv,
+                                _dev(torch, c.block_tables), _dev(torch, c.context_lens), c.scale,
+                                num_splits=num_splits)
+    torch.cuda.synchronize()
+    kp, vp = c.k_pool.copy(), c.v_pool.copy()
+    oracle.paged_kv_append(c.k_new, c.v_new, c.slot_mapping, kp, vp)
+    assert np.array_equal(dk.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+    assert np.array_equal(dv.cpu().numpy().view(np.uint16), vp.view(np.uint16))
+    ref = oracle.decode_attention(c.q, kp, vp, c.block_tables, c.context_lens, c.scale)
+    assert_close(out.cpu().numpy(), ref, "fused step %s S=%d" % (geom, num_splits))
+
+
+def test_prepared_calls_match_direct_calls(torch_cuda):
+    torch = torch_cuda
+    from paged_kv_decode_04_amd import pkv
+    c = W.small_case(401, 3, 16, 4, 128, 16, (300, 40, 17), poison=True)
+    kn, vn = full_new_rows(c)
+    d = _upload(torch, c)
+    d2 = _upload(torch, c)
+    out1 = pkv.paged_decode_step(d["q"], _dev(torch, kn), _dev(torch, vn), d["k_pool"], d["v_pool"],
+                                 d["block_tables"], d["context_lens"], c.scale)
+    out2 = torch.empty_like(out1)
+    call = pkv.prepare_decode_step(d2["q"], _dev(torch, kn), _dev(torch, vn), d2["k_pool"], d2["v_pool"],
+                                   d2["block_tables"], d2["context_lens"], c.scale, out2)
+    for _ in range(3):  # repeated steps re-write the same rows: idempotent
+        call()
+    out3 = torch.empty_like(out1)
+    pkv.prepare_paged_decode_attention(d2["q"], d2["k_pool"], d2["v_pool"], d2["block_tables"], d2["context_lens"],
+                                       c.scale, out3)()
+    torch.cuda.synchronize()
+    assert np.array_equal(out1.cpu().numpy().view(np.uint16), out2.cpu().numpy().view(np.uint16))
+    assert np.array_equal(out1.cpu().numpy().view(np.uint16), out3.cpu().numpy().view(np.uint16))
+    assert torch.equal(d["k_pool"], d2["k_pool"]) and torch.equal(d["v_pool"], d2["v_pool"])
