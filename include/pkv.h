@@ -58,6 +58,9 @@
  *  decoded (the length after the append) [kapsl-backends 0.1.1,
  *  forward_batch_decode_greedy]; the query attends rows 0..L-1, with row t in
  *  physical block block_tables[s][t / block_size] at offset t % block_size.
+ *  Every row of block_tables must be max_blocks_per_seq readable entries: the
+ *  decode kernels may read entries past ceil(L/block_size) ahead of knowing L,
+ *  but their values never affect a result (any value is allowed there).
  *  Query head hq reads kv head hq / (num_q_heads / num_kv_heads)
  *  [cortiq-engine 0.8.80, src/gpu_cuda.rs: heads-per-kv-head grouping].
  *

@@ -8,24 +8,25 @@
 namespace pkv {
 
 // Arguments of the decode-attention kernel (single pass and split-K phase 1).
+// Fields the kernel needs first (before any K/V load) lead, so they arrive in its first kernel-argument loads.
 struct DecodeParams {
     const _Float16 *q;            // [B][Hq][D]
-    const _Float16 *k_pool;       // [N][Hkv][BS/16][D/8][16][8]
-    const _Float16 *v_pool;       // [N][Hkv][BS/16][D][16]
     const int32_t *block_tables;  // [B][M]
     const int32_t *context_lens;  // [B]
-    _Float16 *out;                // [B][Hq][D]            (single pass)
-    float *part_o;                // [B][Hq][S][D]         (split-K)
-    float *part_m;                // [B][Hq][S]
-    float *part_l;                // [B][Hq][S]
-    int32_t Hq, Hkv, G, N, M;
-    int32_t num_splits;           // grid splits S (1 for a single pass)
-    int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(nb / S) per sequence
-    float scale_log2;             // scale * log2(e)
     // fused decode step: when k_new is non-null, row L-1 of every sequence is first written from
     // k_new / v_new ([B][Hkv][D]) into k_dst / v_dst (the same pools)
     const _Float16 *k_new;
     const _Float16 *v_new;
+    int32_t Hq, Hkv, G, N, M;
+    int32_t num_splits;           // grid splits S (1 for a single pass)
+    int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(nb / S) per sequence
+    float scale_log2;             // scale * log2(e)
+    const _Float16 *k_pool;       // [N][Hkv][BS/16][D/8][16][8]
+    const _Float16 *v_pool;       // [N][Hkv][BS/16][D][16]
+    _Float16 *out;                // [B][Hq][D]            (single pass)
+    float *part_o;                // [B][Hq][S][D]         (split-K)
+    float *part_m;                // [B][Hq][S]
+    float *part_l;                // [B][Hq][S]
     _Float16 *k_dst;
     _Float16 *v_dst;
 };

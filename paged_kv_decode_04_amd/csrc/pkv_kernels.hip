@@ -52,7 +52,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegBig = -1.0e30f;
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr int kMaxWaves = 8;
-constexpr int kTableWindow = 2048;  // block ids staged in LDS at a time (8 KB)
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -136,7 +135,7 @@ template <int D, int BS>
 __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D / 32], f32x4 (&o)[D / 16],
                                              float &m_run, float &l_run, int u, int L, bool dead, int r, int g4,
                                              float scale_log2, int prow, const f16x8 (&kpatch)[D / 32],
-                                             const _Float16 (&vpatch)[D / 16]) {
+                                             const uint32_t (&vpatch)[D / 16]) {
     constexpr int KC = Frag<D, BS>::KC;
     constexpr int VC = Frag<D, BS>::VC;
     if (prow >= 0) {  // wave-uniform
@@ -149,9 +148,10 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
             const int e = prow & 3;  // selects with constant element indices keep the fragment in registers
 #pragma unroll
             for (int c = 0; c < VC; ++c) {
+                const _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)vpatch[c]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    f.v[c][j] = (j == e) ? vpatch[c] : f.v[c][j];
+                    f.v[c][j] = (j == e) ? x : f.v[c][j];
             }
         }
     }
@@ -194,10 +194,25 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
     }
 }
 
-template <int D, int BS, int NW, bool SPLIT>
+#ifndef PKV_STAGES_WIDE
+#define PKV_STAGES_WIDE 2  // pipeline depth of 8-wave groups
+#endif
+#ifndef PKV_STAGES_NARROW
+#define PKV_STAGES_NARROW 2  // pipeline depth of groups of 4 or fewer waves
+#endif
+// Units in flight per wave (NS - 1 while one is computed).  Head dim 256 keeps two stages: its fragments are
+// twice as large.
+template <int D, int NW>
+constexpr int pipeline_stages() {
+    return D >= 256 ? 2 : (NW >= 8 ? PKV_STAGES_WIDE : PKV_STAGES_NARROW);
+}
+
+// FUSED: the fused decode step (p.k_new / p.v_new hold each sequence's new row); otherwise attention alone.
+template <int D, int BS, int NW, bool SPLIT, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     constexpr int KC = D / 32;
     constexpr int VC = D / 16;
+    constexpr int NS = pipeline_stages<D, NW>();
     constexpr int SPB = BS / 16;
     constexpr int DP = D + 4;  // padded LDS row of one head's output
     extern __shared__ float smem[];
@@ -215,20 +230,61 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const int r = lane & 15;
     const int g4 = lane >> 4;
 
-    int *sm_bt = reinterpret_cast<int *>(smem);
     const int32_t *bt = p.block_tables + (int64_t)s * p.M;
-    // When the first block of the range is known from the launch alone (a single pass starts at block 0, a
-    // fixed-size split j at j*chunk_blocks), the first window of block ids is staged before the length arrives,
-    // so the two dependent loads (length, then table) overlap.  Entries past the sequence are never used.
-    const int b0_known = SPLIT ? split * p.chunk_blocks : 0;
-    const bool staged_early = (!SPLIT || p.chunk_blocks > 0) && b0_known < p.M;
-    if (staged_early) {
-        const int n_early = min(min(p.M - b0_known, kTableWindow), SPLIT ? p.chunk_blocks : kTableWindow);
-        for (int i = threadIdx.x; i < n_early; i += NW * 64)
-            sm_bt[i] = bt[b0_known + i];
+    const int max_units = p.M * SPB;  // units the table can name
+    // Block ids are read with scalar loads (wave-uniform index), one pipeline step ahead of the unit that needs
+    // them.  When the range start is known from the launch alone (a single pass starts at block 0, a fixed-size
+    // split j at j*chunk_blocks), the ids of this wave's first NS units are requested together with the length,
+    // so the first K/V loads wait for one dependent load, not two.
+    const bool start_known = !SPLIT || p.chunk_blocks > 0;
+    const int u_known = (SPLIT ? split * p.chunk_blocks : 0) * SPB + wave;
+    int spec_raw[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+        spec_raw[j] = start_known ? uniform_load(bt, min(u_known + j * NW, max_units - 1) / SPB) : -1;
+    int L = uniform_load(p.context_lens, s);
+
+    // Q^T as the B operand: lane (g4, r) holds head r, dims 32c + 8*g4 .. +8.  Columns r >= G (no such head in
+    // the group) repeat head 0; every column of the matrix-core tiles is independent and those are never stored.
+    f16x8 qf[KC];
+    {
+        const _Float16 *qrow = p.q + ((int64_t)s * p.Hq + hk * p.G + (r < p.G ? r : 0)) * D + 8 * g4;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            qf[c] = *reinterpret_cast<const f16x8 *>(qrow + 32 * c);
     }
 
-    int L = uniform_load(p.context_lens, s);
+    // Fused decode step: the workgroup whose range holds row L-1 writes the sequence's new K/V row there (the slot
+    // the callers form from the table: block bt[(L-1)/BS], row (L-1)%BS).  Every lane loads its pieces of the new
+    // row up front (they do not depend on L); the wave that computes the unit holding row L-1 uses them in place
+    // of what it loads for that row (see compute_unit) and stores the row to the pools after its last unit.
+    // V halves are kept one per register, so nothing waits for these loads before the patch needs them.
+    f16x8 kpatch[KC];
+    uint32_t vpatch[VC];
+    if constexpr (FUSED) {
+        const _Float16 *kn = p.k_new + ((int64_t)s * p.Hkv + hk) * D;
+        const uint16_t *vn = reinterpret_cast<const uint16_t *>(p.v_new) + ((int64_t)s * p.Hkv + hk) * D;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            kpatch[c] = *reinterpret_cast<const f16x8 *>(kn + 32 * c + 8 * g4);  // piece 4c + g4
+#pragma unroll
+        for (int c = 0; c < VC; ++c)
+            vpatch[c] = vn[16 * c + r];  // dim 16c + r
+    } else {
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            kpatch[c] = (f16x8)(_Float16)0.0f;
+#pragma unroll
+        for (int c = 0; c < VC; ++c)
+            vpatch[c] = 0u;
+    }
+    // Every request above depends on the launch alone; an empty asm statement that reads L and the first block
+    // ids keeps them all ahead of the first use of the length, so one wait covers all the scalar loads.
+    static_assert(NS <= 4, "the barrier below names at most four block ids");
+    asm volatile("" ::"s"(L), "s"(spec_raw[0]), "s"(spec_raw[NS > 1 ? 1 : 0]), "s"(spec_raw[NS > 2 ? 2 : 0]),
+                 "s"(spec_raw[NS > 3 ? 3 : 0])
+                 : "memory");
+
     L = L < 0 ? 0 : (L > p.M * BS ? p.M * BS : L);
     if (p.N <= 0)
         L = 0;  // an empty pool holds no rows
@@ -243,63 +299,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     }
     const int u_begin = b0 * SPB;
     const int u_end = min(b1 * SPB, (L + 15) >> 4);
-
-    // Fused decode step: the workgroup whose range holds row L-1 writes the sequence's new K/V row there (the slot
-    // the callers form from the table: block bt[(L-1)/BS], row (L-1)%BS).  The wave that will compute the unit
-    // holding that row loads the row into registers at start, stores it to the pool from them and later uses them
-    // in place of what it loads for that row (see compute_unit); no barrier waits on the stores.
-    const bool appending = p.k_new != nullptr && L > 0 && (L - 1) / BS >= b0 && (L - 1) / BS < b1;
+    const int u_first = u_begin + wave;  // wave w takes units u_begin + w, + w + NW, ...
+    const int n_units = u_first < u_end ? (u_end - u_first + NW - 1) / NW : 0;
+    const bool appending = FUSED && L > 0 && (L - 1) / BS >= b0 && (L - 1) / BS < b1;
     const int patch_unit = appending ? (L - 1) >> 4 : -1;
     const int prow_row = (L - 1) & 15;
-    f16x8 kpatch[KC];
-    _Float16 vpatch[VC];
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-        kpatch[c] = (f16x8)(_Float16)0.0f;
-#pragma unroll
-    for (int c = 0; c < VC; ++c)
-        vpatch[c] = (_Float16)0.0f;
-    // unit u is computed by wave (u - u_begin) % NW in every table window (a window is a multiple of NW units)
-    if (appending && wave == (patch_unit - u_begin) % NW) {
-        const _Float16 *kn = p.k_new + ((int64_t)s * p.Hkv + hk) * D;
-        const _Float16 *vn = p.v_new + ((int64_t)s * p.Hkv + hk) * D;
-        if (r == prow_row) {
-#pragma unroll
-            for (int c = 0; c < KC; ++c)
-                kpatch[c] = *reinterpret_cast<const f16x8 *>(kn + 32 * c + 8 * g4);
-        }
-        if (g4 == (prow_row >> 2)) {
-#pragma unroll
-            for (int c = 0; c < VC; ++c)
-                vpatch[c] = vn[16 * c + r];
-        }
-        const int blk = uniform_load(bt, (L - 1) / BS);
-        if ((unsigned)blk < (unsigned)p.N) {
-            const int64_t panel = ((int64_t)blk * p.Hkv + hk) * (BS * D) + (((L - 1) % BS) / 16) * (16 * D);
-            if (r == prow_row) {  // K panel [D/8][16][8]: pieces 4c + g4 of the row
-#pragma unroll
-                for (int c = 0; c < KC; ++c)
-                    *reinterpret_cast<f16x8 *>(p.k_dst + panel + ((4 * c + g4) * 16 + prow_row) * 8) = kpatch[c];
-            }
-            if (g4 == (prow_row >> 2)) {  // V panel [D][16]: dims 16c + r of the row
-#pragma unroll
-                for (int c = 0; c < VC; ++c)
-                    p.v_dst[panel + (16 * c + r) * 16 + prow_row] = vpatch[c];
-            }
-        }
-    }
-
-    // Q^T as the B operand: lane (g4, r) holds head r, dims 32c + 8*g4 .. +8.
-    f16x8 qf[KC];
-    {
-        const bool head_ok = r < p.G;
-        const _Float16 *qrow = p.q + ((int64_t)s * p.Hq + hk * p.G + (head_ok ? r : 0)) * D + 8 * g4;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            f16x8 x = *reinterpret_cast<const f16x8 *>(qrow + 32 * c);
-            qf[c] = head_ok ? x : (f16x8)(_Float16)0.0f;
-        }
-    }
+    const bool patch_owner = appending && wave == (patch_unit - u_begin) % NW;
 
     f32x4 o[VC];
 #pragma unroll
@@ -313,24 +318,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const int64_t head_off = (int64_t)hk * (BS * D);
     const int64_t block_stride = (int64_t)p.Hkv * (BS * D);
 
-    // The workgroup's block ids go through LDS in windows of kTableWindow entries; wave w takes the window's
-    // 16-row units w, w+NW, ... and double-buffers them: unit k+1 is in flight while unit k is computed.
-    for (int wb = b0; wb < b1; wb += kTableWindow) {
-        const int we = min(b1, wb + kTableWindow);
-        if (wb != b0)
-            __syncthreads();  // every wave is done with the previous window
-        if (wb != b0 || !staged_early)
-            for (int i = threadIdx.x; i < we - wb; i += NW * 64)
-                sm_bt[i] = bt[wb + i];
-        __syncthreads();
-        const int wu_end = min(we * SPB, u_end);
-        const int u_first = wb * SPB + wave;
-        const int n_units = u_first < wu_end ? (wu_end - u_first + NW - 1) / NW : 0;
-        if (n_units == 0)
-            continue;
-        // Block id of unit u from the staged window, clamped to block 0 when the table names no pool block (the
-        // unit is then computed fully masked).
-        auto raw_block = [&](int u) -> int { return sm_bt[u / SPB - wb]; };
+    if (n_units > 0) {
+        // Block id of unit u, clamped to block 0 when the table names no pool block (the unit is then computed
+        // fully masked).
+        auto raw_block = [&](int u) -> int { return uniform_load(bt, min(u, max_units - 1) / SPB); };
         auto resolve = [&](int raw, bool &dead) -> int {
             const int b = __builtin_amdgcn_readfirstlane(raw);
             dead = (unsigned)b >= (unsigned)p.N;
@@ -342,39 +333,56 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         auto v_ptr = [&](int blk, int u) {
             return p.v_pool + (int64_t)blk * block_stride + head_off + (u % SPB) * (16 * D);
         };
-        // Every iteration issues its prefetch unconditionally -- after a wave's last unit it re-loads that unit
-        // (an L2 hit, never used) -- so the wait counts the compiler derives are exact on every path and unit k+1
-        // stays in flight during the whole computation of unit k.
-        Frag<D, BS> fa, fb;
-        bool dead_a, dead_b;
-        int ua = u_first;
-        int blk_a = resolve(raw_block(ua), dead_a);
-        load_unit<D, BS>(fa, k_ptr(blk_a, ua), v_ptr(blk_a, ua), k_lane, v_lane);
-        int ub = n_units > 1 ? ua + NW : ua;
-        int raw_b = raw_block(ub);
+        // NS-stage pipeline: while unit k is computed, units k+1 .. k+NS-1 are in flight.  Every step issues its
+        // prefetch unconditionally -- past a wave's last unit it re-loads that unit (an L2 hit, never used) -- so
+        // the wait counts the compiler derives are exact on every path.  The slot index is a compile-time constant
+        // in the unrolled step loop, so every fragment stays in registers.  A prologue slot past the wave's last
+        // unit is loaded (from an in-range block) but never computed.
+        Frag<D, BS> f[NS];
+        bool dead[NS];
+        int uu[NS];
+#pragma unroll
+        for (int j = 0; j < NS - 1; ++j) {
+            uu[j] = u_first + j * NW;
+            const int blk = resolve(start_known ? spec_raw[j] : raw_block(uu[j]), dead[j]);
+            load_unit<D, BS>(f[j], k_ptr(blk, uu[j]), v_ptr(blk, uu[j]), k_lane, v_lane);
+        }
+        int raw_next = (start_known && NS - 1 < n_units) ? spec_raw[NS - 1]
+                                                         : raw_block(u_first + min(NS - 1, n_units - 1) * NW);
         int k = 0;
         for (;;) {
-            int blk_b = resolve(raw_b, dead_b);
-            load_unit<D, BS>(fb, k_ptr(blk_b, ub), v_ptr(blk_b, ub), k_lane, v_lane);
-            int ua_next = k + 2 < n_units ? ub + NW : ub;
-            int raw_a = raw_block(ua_next);
-            compute_unit<D, BS>(fa, qf, o, m_run, l_run, ua, L, dead_a, r, g4, p.scale_log2,
-                                ua == patch_unit ? prow_row : -1, kpatch, vpatch);
-            if (++k >= n_units)
-                break;
-            ua = ua_next;
-            blk_a = resolve(raw_a, dead_a);
-            load_unit<D, BS>(fa, k_ptr(blk_a, ua), v_ptr(blk_a, ua), k_lane, v_lane);
-            int ub_next = k + 2 < n_units ? ua + NW : ua;
-            raw_b = raw_block(ub_next);
-            compute_unit<D, BS>(fb, qf, o, m_run, l_run, ub, L, dead_b, r, g4, p.scale_log2,
-                                ub == patch_unit ? prow_row : -1, kpatch, vpatch);
-            if (++k >= n_units)
-                break;
-            ub = ub_next;
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const int jn = (j + NS - 1) % NS;  // the slot freed by the unit computed one step ago
+                uu[jn] = u_first + min(k + NS - 1, n_units - 1) * NW;
+                const int blk = resolve(raw_next, dead[jn]);
+                load_unit<D, BS>(f[jn], k_ptr(blk, uu[jn]), v_ptr(blk, uu[jn]), k_lane, v_lane);
+                raw_next = raw_block(u_first + min(k + NS, n_units - 1) * NW);
+                compute_unit<D, BS>(f[j], qf, o, m_run, l_run, uu[j], L, dead[j], r, g4, p.scale_log2,
+                                    uu[j] == patch_unit ? prow_row : -1, kpatch, vpatch);
+                if (++k >= n_units)
+                    goto units_done;
+            }
+        }
+    units_done:;
+    }
+
+    if (patch_owner) {  // store the new row (its unit has been computed from the registers)
+        const int blk = uniform_load(bt, (L - 1) / BS);
+        if ((unsigned)blk < (unsigned)p.N) {
+            const int64_t panel = ((int64_t)blk * p.Hkv + hk) * (BS * D) + (((L - 1) % BS) / 16) * (16 * D);
+            if (r == prow_row) {  // K panel [D/8][16][8]: pieces 4c + g4 of the row
+#pragma unroll
+                for (int c = 0; c < KC; ++c)
+                    *reinterpret_cast<f16x8 *>(p.k_dst + panel + ((4 * c + g4) * 16 + prow_row) * 8) = kpatch[c];
+            }
+            if (g4 == (prow_row >> 2)) {  // V panel [D][16]: dims 16c + r of the row
+#pragma unroll
+                for (int c = 0; c < VC; ++c)
+                    reinterpret_cast<uint16_t *>(p.v_dst)[panel + (16 * c + r) * 16 + prow_row] = (uint16_t)vpatch[c];
+            }
         }
     }
-    __syncthreads();  // the table window's LDS is reused below
 
     // l over the four lane groups that hold the same head
     l_run = rows_sum(l_run);
@@ -512,9 +520,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // launchers
 
 size_t decode_lds_bytes(int head_dim, int G, int waves) {
-    const size_t combine = sizeof(float) * ((size_t)2 * waves * 16 + (size_t)waves * G * (head_dim + 4));
-    const size_t table = sizeof(int) * (size_t)kTableWindow;
-    return combine > table ? combine : table;
+    return sizeof(float) * ((size_t)2 * waves * 16 + (size_t)waves * G * (head_dim + 4));
 }
 
 bool decode_geometry_supported(int head_dim, int block_size) {
@@ -531,10 +537,15 @@ static hipError_t launch_decode_t(const DecodeParams &p, int num_seqs, bool spli
     dim3 grid((unsigned)((int64_t)num_seqs * p.Hkv * (split ? p.num_splits : 1)), 1u, 1u);
     dim3 block(NW * 64);
     const size_t lds = decode_lds_bytes(D, p.G, NW);
-    if (split)
-        hipLaunchKernelGGL((decode_kernel<D, BS, NW, true>), grid, block, lds, stream, p);
+    const bool fused = p.k_new != nullptr;
+    if (split && fused)
+        hipLaunchKernelGGL((decode_kernel<D, BS, NW, true, true>), grid, block, lds, stream, p);
+    else if (split)
+        hipLaunchKernelGGL((decode_kernel<D, BS, NW, true, false>), grid, block, lds, stream, p);
+    else if (fused)
+        hipLaunchKernelGGL((decode_kernel<D, BS, NW, false, true>), grid, block, lds, stream, p);
     else
-        hipLaunchKernelGGL((decode_kernel<D, BS, NW, false>), grid, block, lds, stream, p);
+        hipLaunchKernelGGL((decode_kernel<D, BS, NW, false, false>), grid, block, lds, stream, p);
     return hipGetLastError();
 }
 
