@@ -82,6 +82,10 @@ __device__ __forceinline__ int uniform_load(const int32_t *p, int64_t i) {
     return ((const_i32_ptr)p)[i];
 }
 
+// Floats of the decode kernel's cross-wave merge area: per wave, the running max and sum of 16 columns, then the
+// G heads' D-wide partial outputs (rows padded to D + 4).
+__host__ __device__ constexpr int merge_floats(int D, int G, int NW) { return 2 * NW * 16 + NW * G * (D + 4); }
+
 template <int D, int BS>
 struct Frag {
     static constexpr int KC = D / 32;  // 16x16x32 steps over the head dim
@@ -107,12 +111,17 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, no swizzle (gfx9 f
 #endif
 constexpr int kKvLoadPolicy = PKV_KV_LOAD_POLICY;  // cache-policy bits of the streamed K/V loads
 
+//
+// live == false (a pipeline slot past the wave's last unit, or a unit whose block id names no pool block) gives the
+// resources a record count of 0: the same instructions issue, so the wait counts stay exact, but every load returns
+// zeros without a memory access -- in particular the final prefetches of a wave never hold up its epilogue.
 template <int D, int BS>
 __device__ __forceinline__ void load_unit(Frag<D, BS> &f, const _Float16 *kb, const _Float16 *vb, uint32_t k_lane,
-                                          uint32_t v_lane) {
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(kb), 0, 32 * D,
+                                          uint32_t v_lane, bool live) {
+    const int nbytes = live ? 32 * D : 0;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(kb), 0, nbytes,
                                                                         kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(vb), 0, 32 * D,
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(vb), 0, nbytes,
                                                                         kRsrcWord3);
 #pragma unroll
     for (int c = 0; c < Frag<D, BS>::KC; ++c)
@@ -128,27 +137,25 @@ __device__ __forceinline__ void load_unit(Frag<D, BS> &f, const _Float16 *kb, co
 // block) is computed with every row masked, so that the loads of every unit are consumed on every path.
 //
 // prow >= 0 (fused decode step only): row prow of this unit is the token appended by this same launch; its K and V
-// come from registers loaded at kernel start (kpatch: lanes with r == prow hold its 8-dim pieces 4c + g4; vpatch:
-// lanes with g4 == prow / 4 hold dims 16c + r) instead of the loaded fragment, so the result never depends on when
-// the store of that row becomes visible, and no load sits on the last unit's critical path.
+// come from the workgroup's LDS copy of the new row (pk, pv: D halves each, natural order) instead of the loaded
+// fragment, so the result never depends on when the store of that row becomes visible.
 template <int D, int BS>
 __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D / 32], f32x4 (&o)[D / 16],
                                              float &m_run, float &l_run, int u, int L, bool dead, int r, int g4,
-                                             float scale_log2, int prow, const f16x8 (&kpatch)[D / 32],
-                                             const uint32_t (&vpatch)[D / 16]) {
+                                             float scale_log2, int prow, const _Float16 *pk, const _Float16 *pv) {
     constexpr int KC = Frag<D, BS>::KC;
     constexpr int VC = Frag<D, BS>::VC;
     if (prow >= 0) {  // wave-uniform
-        if (r == prow) {
+        if (r == prow) {  // K pieces 4c + g4
 #pragma unroll
             for (int c = 0; c < KC; ++c)
-                f.k[c] = kpatch[c];
+                f.k[c] = *reinterpret_cast<const f16x8 *>(pk + 32 * c + 8 * g4);
         }
-        if (g4 == (prow >> 2)) {
+        if (g4 == (prow >> 2)) {  // V dims 16c + r
             const int e = prow & 3;  // selects with constant element indices keep the fragment in registers
 #pragma unroll
             for (int c = 0; c < VC; ++c) {
-                const _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)vpatch[c]);
+                const _Float16 x = pv[16 * c + r];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     f.v[c][j] = (j == e) ? x : f.v[c][j];
@@ -238,9 +245,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     // so the first K/V loads wait for one dependent load, not two.
     const bool start_known = !SPLIT || p.chunk_blocks > 0;
     const int u_known = (SPLIT ? split * p.chunk_blocks : 0) * SPB + wave;
-    int spec_raw[NS];
+    constexpr int NSPEC = 2 * NS - 1;  // the prologue's NS-1 units and the NS block ids requested ahead
+    int spec_raw[NSPEC];
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
+    for (int j = 0; j < NSPEC; ++j)
         spec_raw[j] = start_known ? uniform_load(bt, min(u_known + j * NW, max_units - 1) / SPB) : -1;
     int L = uniform_load(p.context_lens, s);
 
@@ -254,35 +262,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
             qf[c] = *reinterpret_cast<const f16x8 *>(qrow + 32 * c);
     }
 
-    // Fused decode step: the workgroup whose range holds row L-1 writes the sequence's new K/V row there (the slot
-    // the callers form from the table: block bt[(L-1)/BS], row (L-1)%BS).  Every lane loads its pieces of the new
-    // row up front (they do not depend on L); the wave that computes the unit holding row L-1 uses them in place
-    // of what it loads for that row (see compute_unit) and stores the row to the pools after its last unit.
-    // V halves are kept one per register, so nothing waits for these loads before the patch needs them.
-    f16x8 kpatch[KC];
-    uint32_t vpatch[VC];
-    if constexpr (FUSED) {
-        const _Float16 *kn = p.k_new + ((int64_t)s * p.Hkv + hk) * D;
-        const uint16_t *vn = reinterpret_cast<const uint16_t *>(p.v_new) + ((int64_t)s * p.Hkv + hk) * D;
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-            kpatch[c] = *reinterpret_cast<const f16x8 *>(kn + 32 * c + 8 * g4);  // piece 4c + g4
-#pragma unroll
-        for (int c = 0; c < VC; ++c)
-            vpatch[c] = vn[16 * c + r];  // dim 16c + r
-    } else {
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-            kpatch[c] = (f16x8)(_Float16)0.0f;
-#pragma unroll
-        for (int c = 0; c < VC; ++c)
-            vpatch[c] = 0u;
-    }
     // Every request above depends on the launch alone; an empty asm statement that reads L and the first block
     // ids keeps them all ahead of the first use of the length, so one wait covers all the scalar loads.
-    static_assert(NS <= 4, "the barrier below names at most four block ids");
-    asm volatile("" ::"s"(L), "s"(spec_raw[0]), "s"(spec_raw[NS > 1 ? 1 : 0]), "s"(spec_raw[NS > 2 ? 2 : 0]),
-                 "s"(spec_raw[NS > 3 ? 3 : 0])
+    static_assert(NSPEC <= 5, "the barrier below names at most five block ids");
+    asm volatile("" ::"s"(L), "s"(spec_raw[0]), "s"(spec_raw[NSPEC > 1 ? 1 : 0]), "s"(spec_raw[NSPEC > 2 ? 2 : 0]),
+                 "s"(spec_raw[NSPEC > 3 ? 3 : 0]), "s"(spec_raw[NSPEC > 4 ? 4 : 0])
                  : "memory");
 
     L = L < 0 ? 0 : (L > p.M * BS ? p.M * BS : L);
@@ -301,6 +285,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const int u_end = min(b1 * SPB, (L + 15) >> 4);
     const int u_first = u_begin + wave;  // wave w takes units u_begin + w, + w + NW, ...
     const int n_units = u_first < u_end ? (u_end - u_first + NW - 1) / NW : 0;
+    // Fused decode step: the workgroup whose range holds row L-1 writes the sequence's new K/V row there (the slot
+    // the callers form from the table: block bt[(L-1)/BS], row (L-1)%BS).  The wave that computes the unit holding
+    // row L-1 loads the row, keeps a copy in LDS for that unit (see compute_unit) and stores it to the pools.
     const bool appending = FUSED && L > 0 && (L - 1) / BS >= b0 && (L - 1) / BS < b1;
     const int patch_unit = appending ? (L - 1) >> 4 : -1;
     const int prow_row = (L - 1) & 15;
@@ -318,9 +305,38 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const int64_t head_off = (int64_t)hk * (BS * D);
     const int64_t block_stride = (int64_t)p.Hkv * (BS * D);
 
+    // LDS copy of the new row (fused step): K then V, D halves each, after the merge area (which other waves may
+    // fill while the owner wave still computes).
+    _Float16 *sm_pk = reinterpret_cast<_Float16 *>(smem + merge_floats(D, p.G, NW));
+    _Float16 *sm_pv = sm_pk + D;
+    // Owner wave: load the new row (lane t < D/8 takes dims 8t .. 8t+7 of K and of V) ahead of its first K/V loads,
+    // then copy it to LDS and store it to the pools.  The unit holding the row is computed from the LDS copy, so
+    // nothing waits for these stores.
+    f16x8 new_k = (f16x8)(_Float16)0.0f, new_v = (f16x8)(_Float16)0.0f;
+    if (patch_owner && lane < D / 8) {
+        const int64_t row_off = ((int64_t)s * p.Hkv + hk) * D + 8 * lane;
+        new_k = *reinterpret_cast<const f16x8 *>(p.k_new + row_off);
+        new_v = *reinterpret_cast<const f16x8 *>(p.v_new + row_off);
+    }
+    auto store_new_row = [&]() {
+        const int blk = uniform_load(bt, (L - 1) / BS);
+        if (lane < D / 8) {
+            *reinterpret_cast<f16x8 *>(sm_pk + 8 * lane) = new_k;
+            *reinterpret_cast<f16x8 *>(sm_pv + 8 * lane) = new_v;
+            if ((unsigned)blk < (unsigned)p.N) {
+                const int64_t panel = ((int64_t)blk * p.Hkv + hk) * (BS * D) + (((L - 1) % BS) / 16) * (16 * D);
+                // K panel [D/8][16][8]: piece `lane` of the row; V panel [D][16]: dims 8*lane .. +8 of the row
+                *reinterpret_cast<f16x8 *>(p.k_dst + panel + (lane * 16 + prow_row) * 8) = new_k;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    p.v_dst[panel + (8 * lane + e) * 16 + prow_row] = new_v[e];
+            }
+        }
+    };
+
     if (n_units > 0) {
-        // Block id of unit u, clamped to block 0 when the table names no pool block (the unit is then computed
-        // fully masked).
+        // Block id of unit u, clamped to block 0 when the table names no pool block (the unit is then loaded as
+        // zeros and computed fully masked).
         auto raw_block = [&](int u) -> int { return uniform_load(bt, min(u, max_units - 1) / SPB); };
         auto resolve = [&](int raw, bool &dead) -> int {
             const int b = __builtin_amdgcn_readfirstlane(raw);
@@ -333,33 +349,39 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         auto v_ptr = [&](int blk, int u) {
             return p.v_pool + (int64_t)blk * block_stride + head_off + (u % SPB) * (16 * D);
         };
-        // NS-stage pipeline: while unit k is computed, units k+1 .. k+NS-1 are in flight.  Every step issues its
-        // prefetch unconditionally -- past a wave's last unit it re-loads that unit (an L2 hit, never used) -- so
-        // the wait counts the compiler derives are exact on every path.  The slot index is a compile-time constant
-        // in the unrolled step loop, so every fragment stays in registers.  A prologue slot past the wave's last
-        // unit is loaded (from an in-range block) but never computed.
+        // NS-stage pipeline: while unit k is computed, units k+1 .. k+NS-1 are in flight, and the block ids of the
+        // next NS units to issue are already requested (ring raw_q, slot k % NS holds unit k+NS-1's id at step k).
+        // Every step issues its prefetch unconditionally -- past a wave's last unit as loads that touch no memory
+        // (see load_unit) -- so the wait counts the compiler derives are exact on every path.  Slot indices are
+        // compile-time constants in the unrolled step loop, so every fragment stays in registers.  Pipeline slots
+        // past the wave's last unit are never computed, so their block ids may be anything in range.
         Frag<D, BS> f[NS];
         bool dead[NS];
         int uu[NS];
+        int raw_q[NS];
 #pragma unroll
         for (int j = 0; j < NS - 1; ++j) {
             uu[j] = u_first + j * NW;
             const int blk = resolve(start_known ? spec_raw[j] : raw_block(uu[j]), dead[j]);
-            load_unit<D, BS>(f[j], k_ptr(blk, uu[j]), v_ptr(blk, uu[j]), k_lane, v_lane);
+            load_unit<D, BS>(f[j], k_ptr(blk, uu[j]), v_ptr(blk, uu[j]), k_lane, v_lane, j < n_units && !dead[j]);
         }
-        int raw_next = (start_known && NS - 1 < n_units) ? spec_raw[NS - 1]
-                                                         : raw_block(u_first + min(NS - 1, n_units - 1) * NW);
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+            raw_q[j] = start_known ? spec_raw[NS - 1 + j] : raw_block(u_first + min(NS - 1 + j, n_units - 1) * NW);
+        if (patch_owner)
+            store_new_row();
         int k = 0;
         for (;;) {
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
                 const int jn = (j + NS - 1) % NS;  // the slot freed by the unit computed one step ago
                 uu[jn] = u_first + min(k + NS - 1, n_units - 1) * NW;
-                const int blk = resolve(raw_next, dead[jn]);
-                load_unit<D, BS>(f[jn], k_ptr(blk, uu[jn]), v_ptr(blk, uu[jn]), k_lane, v_lane);
-                raw_next = raw_block(u_first + min(k + NS, n_units - 1) * NW);
+                const int blk = resolve(raw_q[j], dead[jn]);
+                load_unit<D, BS>(f[jn], k_ptr(blk, uu[jn]), v_ptr(blk, uu[jn]), k_lane, v_lane,
+                                 k + NS - 1 < n_units && !dead[jn]);
+                raw_q[j] = raw_block(u_first + min(k + 2 * NS - 1, n_units - 1) * NW);
                 compute_unit<D, BS>(f[j], qf, o, m_run, l_run, uu[j], L, dead[j], r, g4, p.scale_log2,
-                                    uu[j] == patch_unit ? prow_row : -1, kpatch, vpatch);
+                                    uu[j] == patch_unit ? prow_row : -1, sm_pk, sm_pv);
                 if (++k >= n_units)
                     goto units_done;
             }
@@ -367,24 +389,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     units_done:;
     }
 
-    if (patch_owner) {  // store the new row (its unit has been computed from the registers)
-        const int blk = uniform_load(bt, (L - 1) / BS);
-        if ((unsigned)blk < (unsigned)p.N) {
-            const int64_t panel = ((int64_t)blk * p.Hkv + hk) * (BS * D) + (((L - 1) % BS) / 16) * (16 * D);
-            if (r == prow_row) {  // K panel [D/8][16][8]: pieces 4c + g4 of the row
-#pragma unroll
-                for (int c = 0; c < KC; ++c)
-                    *reinterpret_cast<f16x8 *>(p.k_dst + panel + ((4 * c + g4) * 16 + prow_row) * 8) = kpatch[c];
-            }
-            if (g4 == (prow_row >> 2)) {  // V panel [D][16]: dims 16c + r of the row
-#pragma unroll
-                for (int c = 0; c < VC; ++c)
-                    reinterpret_cast<uint16_t *>(p.v_dst)[panel + (16 * c + r) * 16 + prow_row] = (uint16_t)vpatch[c];
-            }
-        }
-    }
-
-    // l over the four lane groups that hold the same head
     l_run = rows_sum(l_run);
 
     float *sm_m = smem;
@@ -520,7 +524,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // launchers
 
 size_t decode_lds_bytes(int head_dim, int G, int waves) {
-    return sizeof(float) * ((size_t)2 * waves * 16 + (size_t)waves * G * (head_dim + 4));
+    // the merge area, then the fused step's copy of the new row (K and V, head_dim halves each)
+    return sizeof(float) * merge_floats(head_dim, G, waves) + 4 * (size_t)head_dim;
 }
 
 bool decode_geometry_supported(int head_dim, int block_size) {

@@ -352,6 +352,24 @@ def prepare_paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens
     return PreparedCall(lib.pkv_paged_decode_attention, args, (q, k_pool, v_pool, block_tables, context_lens, out))
 
 
+def prepare_paged_decode_attention_planned(q, k_pool, v_pool, block_tables, context_lens, scale: float, plan: dict,
+                                           out, workspace=None, stream=None) -> PreparedCall:
+    """pkv_paged_decode_attention_planned with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    _dev(out, torch.float16, "out", 3)
+    pl = DecodePlan(int(plan["num_splits"]), int(plan.get("chunk_blocks", 0)), int(plan["waves_per_group"]), 0, 0)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(q)), ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool,
+            ctypes.c_void_p(_ptr(block_tables)), ctypes.c_int32(M), ctypes.c_void_p(_ptr(context_lens)),
+            ctypes.c_int32(B), ctypes.c_int32(Hq), ctypes.c_float(scale), ctypes.c_void_p(_ptr(out)),
+            ctypes.byref(pl), ctypes.c_void_p(_ptr(workspace)), ctypes.c_size_t(nbytes),
+            ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_paged_decode_attention_planned, args,
+                        (q, k_pool, v_pool, block_tables, context_lens, out, workspace, pl))
+
+
 def prepare_paged_kv_append(k, v, slot_mapping, k_pool, v_pool, stream=None) -> PreparedCall:
     """pkv_paged_kv_append with its arguments marshalled once (see PreparedCall)."""
     import torch
