@@ -165,7 +165,7 @@ int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, con
                                   size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
- * pkv_paged_decode_step -- the decode step fused into one launch: for every
+ * pkv_paged_decode_step -- the decode step (append + attention): for every
  *   sequence s with L_s = context_lens[s] > 0, first writes k_new[s][h][:] and
  *   v_new[s][h][:] (every kv head h) to row L_s - 1 of the sequence -- block
  *   block_tables[s][(L_s-1)/BS], row (L_s-1)%BS, the slot the callers on
@@ -173,10 +173,15 @@ int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, con
  *   form for launch_batch_kv_write -- then computes exactly what
  *   pkv_paged_decode_attention computes over the updated pools.  A row whose
  *   table entry names no pool block is not written.
- *   k_new, v_new: [num_seqs][Hkv][D] fp16 (k_new 16-byte aligned).  The block
+ *   Launches: when the attention grid (num_seqs * Hkv * splits workgroups)
+ *   fits one round of the device's CUs, a single fused launch whose workgroups
+ *   write the new rows themselves (the 16-row panel holding a new row is
+ *   written back whole, its other rows unchanged); otherwise the append kernel
+ *   then attention, in stream order.  Results are identical either way.
+ *   k_new, v_new: [num_seqs][Hkv][D] fp16, 16-byte aligned.  The block
  *   holding each sequence's newest row must belong to that sequence alone (no
- *   other sequence of the batch may read it).  Other arguments, workspace and
- *   errors as pkv_paged_decode_attention.
+ *   other sequence of the batch may read or write it).  Other arguments,
+ *   workspace and errors as pkv_paged_decode_attention.
  * ------------------------------------------------------------------------- */
 int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
                           uint16_t *v_pool, pkv_pool_desc pool, const int32_t *block_tables,

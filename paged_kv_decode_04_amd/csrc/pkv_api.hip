@@ -213,16 +213,16 @@ int plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int
     if (num_splits >= 1) {
         S = num_splits;
     } else if (tiles > 0) {
+        // One workgroup streams at most ~50 GB/s (one CU's share of outstanding misses), so a single pass needs
+        // about half the CUs busy to reach the HBM roofline; with fewer tiles, split each into about CUs / tiles
+        // ranges (one round of the CUs; each range at least 8 blocks).  Measured on MI355X: with as many tiles as
+        // CUs or more, a single pass beats every split (the combine launch and the partials cost more than the
+        // ragged tail they remove).
         const int64_t cu = cu_count > 0 ? cu_count : 256;
-        const bool short_tiles = nbmax <= 8;
-        const bool full_grid = tiles >= 2 * cu && nbmax <= 128;
-        if (!(short_tiles || full_grid)) {
-            int64_t want = (2 * cu + tiles - 1) / tiles;
-            const int64_t cap_split = (nbmax + 255) / 256;
-            if (want < cap_split)
-                want = cap_split;
-            if (want > nbmax)
-                want = nbmax;
+        if (nbmax > 8 && 2 * tiles < cu) {
+            int64_t want = (cu + tiles - 1) / tiles;
+            if (want > nbmax / 8)
+                want = nbmax / 8;
             if (want > 64)
                 want = 64;
             S = (int)(want < 1 ? 1 : want);
@@ -232,7 +232,7 @@ int plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int
         return fail(PKV_EINVAL, "num_splits %d exceeds the grid limit 65535", S);
     if ((int64_t)num_seqs * num_kv_heads * S > INT32_MAX)
         return fail(PKV_EINVAL, "num_seqs * num_kv_heads * num_splits overflows the grid");
-    int waves = S == 1 ? 8 : 4;
+    int waves = 8;  // measured best for head_dim <= 128, single pass and splits alike
     if (waves > pkv::max_waves_per_group(head_dim))
         waves = pkv::max_waves_per_group(head_dim);
     const size_t limit = lds_limit > 0 ? (size_t)lds_limit : (size_t)65536;
@@ -392,6 +392,28 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     }
     if (rc)
         return rc;
+    if (k_new && (int64_t)num_seqs * pool.num_kv_heads * plan.num_splits > facts.cu_count) {
+        // Decode step over more workgroups than one round of the device's CUs: the append kernel, then attention.
+        // Writes issued from inside a long, read-saturated launch cost far more than a launch of their own.
+        pkv::AppendParams a;
+        memset(&a, 0, sizeof a);
+        a.k = reinterpret_cast<const _Float16 *>(k_new);
+        a.v = reinterpret_cast<const _Float16 *>(v_new);
+        a.block_tables = block_tables;
+        a.context_lens = context_lens;
+        a.k_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
+        a.v_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
+        a.T = num_seqs;
+        a.Hkv = pool.num_kv_heads;
+        a.D = pool.head_dim;
+        a.BS = pool.block_size;
+        a.N = pool.num_blocks;
+        a.M = max_blocks_per_seq;
+        hipError_t e = pkv::launch_append_newest(a, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "append kernel launch");
+        k_new = v_new = nullptr;
+    }
     return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                     num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, k_new, v_new);
 }
@@ -421,6 +443,7 @@ int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slo
     if ((int64_t)num_tokens * pool.num_kv_heads * (pool.head_dim / 8) > (int64_t)INT32_MAX * 256)
         return fail(PKV_EINVAL, "append too large for one launch");
     pkv::AppendParams p;
+    memset(&p, 0, sizeof p);
     p.k = reinterpret_cast<const _Float16 *>(k);
     p.v = reinterpret_cast<const _Float16 *>(v);
     p.slot_mapping = slot_mapping;
@@ -475,8 +498,8 @@ int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16
                           int32_t max_context_hint, void *stream) {
     if (num_seqs > 0 && (!k_new || !v_new))
         return fail(PKV_EINVAL, "null device pointer (k_new=%p v_new=%p)", k_new, v_new);
-    if (num_seqs > 0 && (!aligned(k_new, 16) || !aligned(v_new, 2)))
-        return fail(PKV_EINVAL, "k_new must be 16-byte aligned");
+    if (num_seqs > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16)))
+        return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                        num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
                        static_cast<hipStream_t>(stream), k_new, v_new);

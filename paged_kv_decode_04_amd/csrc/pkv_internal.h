@@ -44,10 +44,12 @@ struct CombineParams {
 struct AppendParams {
     const _Float16 *k;            // [T][Hkv][D]
     const _Float16 *v;
-    const int32_t *slot_mapping;  // [T]
+    const int32_t *slot_mapping;  // [T]                 (launch_append)
+    const int32_t *block_tables;  // [T][M]              (launch_append_newest: token i = sequence i's newest row)
+    const int32_t *context_lens;  // [T]                 (launch_append_newest)
     _Float16 *k_pool;
     _Float16 *v_pool;
-    int32_t T, Hkv, D, BS, N;
+    int32_t T, Hkv, D, BS, N, M;
 };
 
 // LDS bytes the decode kernel needs for `waves` wavefronts and group size G.
@@ -58,6 +60,7 @@ hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int 
                          bool split, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_append(const AppendParams &p, hipStream_t stream);
+hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream);
 
 // Geometry support of the compiled kernels.
 bool decode_geometry_supported(int head_dim, int block_size);

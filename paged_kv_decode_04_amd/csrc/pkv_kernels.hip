@@ -138,11 +138,14 @@ __device__ __forceinline__ void load_unit(Frag<D, BS> &f, const _Float16 *kb, co
 //
 // prow >= 0 (fused decode step only): row prow of this unit is the token appended by this same launch; its K and V
 // come from the workgroup's LDS copy of the new row (pk, pv: D halves each, natural order) instead of the loaded
-// fragment, so the result never depends on when the store of that row becomes visible.
+// fragment.  The patched fragment -- the unit's 16 rows as loaded, with row prow replaced -- is then written back
+// to the unit's panels (wb_k, wb_v): the pool update is whole cache lines, and no row but prow changes value.
+// A unit whose block id names no pool block (dead) is neither written nor used.
 template <int D, int BS>
 __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D / 32], f32x4 (&o)[D / 16],
                                              float &m_run, float &l_run, int u, int L, bool dead, int r, int g4,
-                                             float scale_log2, int prow, const _Float16 *pk, const _Float16 *pv) {
+                                             float scale_log2, int prow, const _Float16 *pk, const _Float16 *pv,
+                                             _Float16 *wb_k, _Float16 *wb_v, uint32_t k_lane, uint32_t v_lane) {
     constexpr int KC = Frag<D, BS>::KC;
     constexpr int VC = Frag<D, BS>::VC;
     if (prow >= 0) {  // wave-uniform
@@ -160,6 +163,14 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
                 for (int j = 0; j < 4; ++j)
                     f.v[c][j] = (j == e) ? x : f.v[c][j];
             }
+        }
+        if (!dead) {  // the pool update: the patched panel written back whole, before any row is masked
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                *reinterpret_cast<f16x8 *>(reinterpret_cast<char *>(wb_k) + k_lane + 1024 * c) = f.k[c];
+#pragma unroll
+            for (int c = 0; c < VC; ++c)
+                *reinterpret_cast<f16x4 *>(reinterpret_cast<char *>(wb_v) + v_lane + 512 * c) = f.v[c];
         }
     }
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -287,7 +298,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const int n_units = u_first < u_end ? (u_end - u_first + NW - 1) / NW : 0;
     // Fused decode step: the workgroup whose range holds row L-1 writes the sequence's new K/V row there (the slot
     // the callers form from the table: block bt[(L-1)/BS], row (L-1)%BS).  The wave that computes the unit holding
-    // row L-1 loads the row, keeps a copy in LDS for that unit (see compute_unit) and stores it to the pools.
+    // row L-1 loads the row, keeps a copy in LDS and, when it computes that unit, writes the unit's panels back
+    // with the row in place (see compute_unit).
     const bool appending = FUSED && L > 0 && (L - 1) / BS >= b0 && (L - 1) / BS < b1;
     const int patch_unit = appending ? (L - 1) >> 4 : -1;
     const int prow_row = (L - 1) & 15;
@@ -309,28 +321,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     // fill while the owner wave still computes).
     _Float16 *sm_pk = reinterpret_cast<_Float16 *>(smem + merge_floats(D, p.G, NW));
     _Float16 *sm_pv = sm_pk + D;
-    // Owner wave: load the new row (lane t < D/8 takes dims 8t .. 8t+7 of K and of V) ahead of its first K/V loads,
-    // then copy it to LDS and store it to the pools.  The unit holding the row is computed from the LDS copy, so
-    // nothing waits for these stores.
+    // Owner wave: load the new row (lane t < D/8 takes dims 8t .. 8t+7 of K and of V) ahead of its first K/V loads
+    // and copy it to LDS for the unit that holds it (see compute_unit).
     f16x8 new_k = (f16x8)(_Float16)0.0f, new_v = (f16x8)(_Float16)0.0f;
     if (patch_owner && lane < D / 8) {
         const int64_t row_off = ((int64_t)s * p.Hkv + hk) * D + 8 * lane;
         new_k = *reinterpret_cast<const f16x8 *>(p.k_new + row_off);
         new_v = *reinterpret_cast<const f16x8 *>(p.v_new + row_off);
     }
-    auto store_new_row = [&]() {
-        const int blk = uniform_load(bt, (L - 1) / BS);
+    auto copy_new_row = [&]() {
         if (lane < D / 8) {
             *reinterpret_cast<f16x8 *>(sm_pk + 8 * lane) = new_k;
             *reinterpret_cast<f16x8 *>(sm_pv + 8 * lane) = new_v;
-            if ((unsigned)blk < (unsigned)p.N) {
-                const int64_t panel = ((int64_t)blk * p.Hkv + hk) * (BS * D) + (((L - 1) % BS) / 16) * (16 * D);
-                // K panel [D/8][16][8]: piece `lane` of the row; V panel [D][16]: dims 8*lane .. +8 of the row
-                *reinterpret_cast<f16x8 *>(p.k_dst + panel + (lane * 16 + prow_row) * 8) = new_k;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    p.v_dst[panel + (8 * lane + e) * 16 + prow_row] = new_v[e];
-            }
         }
     };
 
@@ -359,17 +361,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         bool dead[NS];
         int uu[NS];
         int raw_q[NS];
+        int bk[NS];  // block of each slot (the fused step writes the patched panel back there)
 #pragma unroll
         for (int j = 0; j < NS - 1; ++j) {
             uu[j] = u_first + j * NW;
             const int blk = resolve(start_known ? spec_raw[j] : raw_block(uu[j]), dead[j]);
+            bk[j] = blk;
             load_unit<D, BS>(f[j], k_ptr(blk, uu[j]), v_ptr(blk, uu[j]), k_lane, v_lane, j < n_units && !dead[j]);
         }
 #pragma unroll
         for (int j = 0; j < NS; ++j)
             raw_q[j] = start_known ? spec_raw[NS - 1 + j] : raw_block(u_first + min(NS - 1 + j, n_units - 1) * NW);
         if (patch_owner)
-            store_new_row();
+            copy_new_row();
         int k = 0;
         for (;;) {
 #pragma unroll
@@ -377,11 +381,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
                 const int jn = (j + NS - 1) % NS;  // the slot freed by the unit computed one step ago
                 uu[jn] = u_first + min(k + NS - 1, n_units - 1) * NW;
                 const int blk = resolve(raw_q[j], dead[jn]);
+                bk[jn] = blk;
                 load_unit<D, BS>(f[jn], k_ptr(blk, uu[jn]), v_ptr(blk, uu[jn]), k_lane, v_lane,
                                  k + NS - 1 < n_units && !dead[jn]);
                 raw_q[j] = raw_block(u_first + min(k + 2 * NS - 1, n_units - 1) * NW);
                 compute_unit<D, BS>(f[j], qf, o, m_run, l_run, uu[j], L, dead[j], r, g4, p.scale_log2,
-                                    uu[j] == patch_unit ? prow_row : -1, sm_pk, sm_pv);
+                                    FUSED && uu[j] == patch_unit ? prow_row : -1, sm_pk, sm_pv,
+                                    FUSED ? p.k_dst + (k_ptr(bk[j], uu[j]) - p.k_pool) : nullptr,
+                                    FUSED ? p.v_dst + (v_ptr(bk[j], uu[j]) - p.v_pool) : nullptr, k_lane, v_lane);
                 if (++k >= n_units)
                     goto units_done;
             }
@@ -520,6 +527,45 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         vdst[e * 16] = vh[e];
 }
 
+// The decode step's append as its own launch: the new row of sequence s (block bt[s][(L-1)/BS], row (L-1)%BS, as
+// the fused step places it) for every kv head.  One workgroup per (sequence, kv head) rewrites the two 16-row
+// panels holding the row whole -- each thread one 16-byte chunk: read, replace the row's part, write back -- so the
+// pools see only full-line writes (scattered 2- and 16-byte row stores cost far more at the memory than their
+// bytes).  Valid only because the block holding a sequence's newest row belongs to that sequence alone.
+__global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
+    const int s = (int)(blockIdx.x / (unsigned)p.Hkv);
+    const int h = (int)(blockIdx.x - (unsigned)s * p.Hkv);
+    int L = p.context_lens[s];
+    L = L > p.M * p.BS ? p.M * p.BS : L;
+    if (L <= 0)
+        return;
+    const int b = p.block_tables[(int64_t)s * p.M + (L - 1) / p.BS];
+    if (b < 0 || b >= p.N)
+        return;
+    const int off = (L - 1) % p.BS;
+    const int row = off % 16;
+    const int64_t panel = ((int64_t)b * p.Hkv + h) * p.BS * p.D + (int64_t)(off / 16) * 16 * p.D;
+    const _Float16 *kn = p.k + ((int64_t)s * p.Hkv + h) * p.D;
+    const _Float16 *vn = p.v + ((int64_t)s * p.Hkv + h) * p.D;
+    const int chunks = 2 * p.D;  // 16-byte chunks of one 16-row panel (16 * D halves)
+    for (int q = threadIdx.x; q < chunks; q += 256) {
+        // K panel [D/8][16][8]: chunk q is piece q/16 of row q%16
+        f16x8 kc = *reinterpret_cast<const f16x8 *>(p.k_pool + panel + 8 * q);
+        if (q % 16 == row)
+            kc = *reinterpret_cast<const f16x8 *>(kn + 8 * (q / 16));
+        *reinterpret_cast<f16x8 *>(p.k_pool + panel + 8 * q) = kc;
+        // V panel [D][16]: chunk q is dim q/2, rows 8*(q%2) .. +8
+        f16x8 vc = *reinterpret_cast<const f16x8 *>(p.v_pool + panel + 8 * q);
+        if ((q & 1) == row / 8) {
+            const _Float16 x = vn[q / 2];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                vc[e] = (e == row % 8) ? x : vc[e];
+        }
+        *reinterpret_cast<f16x8 *>(p.v_pool + panel + 8 * q) = vc;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 
@@ -600,6 +646,13 @@ hipError_t launch_combine(const CombineParams &p, int head_dim, hipStream_t stre
     case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream) {
+    if (p.T <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(append_newest_kernel, dim3((unsigned)((int64_t)p.T * p.Hkv)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

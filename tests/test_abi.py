@@ -73,6 +73,16 @@ def test_dispatcher_auto_is_a_function_of_shape_and_cu_count():
     # the hint shrinks the assumed context
     assert _plan(num_seqs=4, max_blocks_per_seq=2048, max_context_hint=64)["num_splits"] <= \
         _plan(num_seqs=4, max_blocks_per_seq=2048)["num_splits"]
+    # measured choices on 256 CUs: as many tiles as CUs or more run a single pass with 8 waves (head_dim <= 128)
+    assert _plan(num_seqs=32, max_blocks_per_seq=128) == dict(num_splits=1, chunk_blocks=0, waves_per_group=8,
+                                                              workspace_bytes=0)
+    assert _plan(num_seqs=256, num_q_heads=64, max_blocks_per_seq=1024)["num_splits"] == 1
+    # few long tiles split into about CUs / tiles ranges
+    p = _plan(num_seqs=4, max_blocks_per_seq=2048)
+    assert (p["num_splits"], p["waves_per_group"]) == (8, 8)
+    # head_dim 256 keeps at most 4 waves
+    assert _plan(num_seqs=128, num_q_heads=16, num_kv_heads=16, head_dim=256, block_size=32,
+                 max_blocks_per_seq=128)["waves_per_group"] <= 4
     for kw in [dict(), dict(num_seqs=256, num_q_heads=64, max_blocks_per_seq=1024), dict(num_seqs=1)]:
         p = _plan(**kw)
         assert 1 <= p["num_splits"] <= 64

@@ -271,12 +271,16 @@ def full_new_rows(c):
     return k, v
 
 
+# The step runs as one fused launch while num_seqs * Hkv * splits fits the device's CUs in one round (256 on
+# MI355X), otherwise as the append kernel then attention: the last two geometries take the second route.
 STEP_GEOMS = [
     (3, 8, 2, 64, 16, (1, 16, 17)),
     (4, 32, 8, 128, 16, (300, 129, 0, 32)),
     (3, 40, 8, 128, 16, (200, 33, 15)),
     (2, 16, 16, 256, 32, (257, 48)),
     (2, 8, 2, 128, 64, (130, 64)),
+    (40, 16, 8, 128, 16, tuple((37 * i) % 600 for i in range(40))),
+    (24, 16, 16, 256, 32, tuple(1 + (91 * i) % 700 for i in range(24))),
 ]
 
 
@@ -300,6 +304,11 @@ def test_fused_step_matches_append_then_attention(torch_cuda, geom, num_splits):
     assert np.array_equal(dv.cpu().numpy().view(np.uint16), vp.view(np.uint16))
     ref = oracle.decode_attention(c.q, kp, vp, c.block_tables, c.context_lens, c.scale)
     assert_close(out.cpu().numpy(), ref, "fused step %s S=%d" % (geom, num_splits))
+    # either route gives exactly what attention computes over the appended pools
+    att = pkv.paged_decode_attention(_dev(torch, c.q), _dev(torch, kp), _dev(torch, vp), _dev(torch, c.block_tables),
+                                     _dev(torch, c.context_lens), c.scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), att.cpu().numpy().view(np.uint16))
 
 
 def test_prepared_calls_match_direct_calls(torch_cuda):
