@@ -40,7 +40,7 @@ PEAK_GBS = 8000.0
 WORKLOADS = {
     "c1": ("tiny paged decode: B=1, Hq=4, Hkv=2, D=64, BS=16, L=37, pool of 8 blocks", 0, 1),
     "c2": ("Llama-3-8B-shaped layer: B=32, Hq=32, Hkv=8, D=128, BS=16, L~U[512,2048], single pass", 1, 4),
-    "c3": ("long-context split-K: B=4, Hq=32, Hkv=8, D=128, BS=16, L=32768, q~2N(0,1)", 16, 2),
+    "c3": ("long-context split-K: B=4, Hq=32, Hkv=8, D=128, BS=16, L=32768, q~2N(0,1)", 8, 2),
     "c4": ("mixed serving (70B-layer-shaped, one GPU's share): B=256, Hq=64, Hkv=8, D=128, BS=16, "
            "L=lognormal(median 1024, sigma 1) clipped to [1,16384], auto dispatch", 0, 1),
     "c5": ("MHA wide head: B=128, Hq=Hkv=16, D=256, BS=32, L=4096, K/V~U(-1,1), scale 1/16", 0, 1),
@@ -119,7 +119,11 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy
         if "append" not in short:
             step_bytes += fb + wb
     out.update({"copy_calibration_mib": copy_mib, "scale_factors": factors, "kernels": kern,
-                "hbm_bytes_per_step": round(step_bytes)})
+                "hbm_bytes_per_step": round(step_bytes),
+                "note": "Counters are KiB per dispatch; each is scaled by its reading for the calibration copy kernel "
+                        "(torch.neg over %g MiB, which reads and writes %g MiB). hbm_bytes_per_step sums the "
+                        "attention kernels of one step (a separate append launch, if any, excluded)."
+                        % (copy_mib, copy_mib)})
     return out
 
 
@@ -162,6 +166,17 @@ def main(argv=None) -> int:
         splits = WORKLOADS[args.config][1] if args.splits is None else args.splits
         rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config, splits,
                             args.copy_calibration_mib or 512.0)
+        extra = " --unfused" if args.unfused else ""
+        rec["commands"] = [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o %s -- python3 bench.py --config %s "
+            "--steps 50 --warmup 10 --no-cpu-baseline --copy-calibration-mib %g%s"
+            % (args.config, args.config, rec["copy_calibration_mib"], extra),
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o %s -- python3 bench.py --config %s "
+            "--steps 50 --warmup 10 --no-cpu-baseline --copy-calibration-mib %g%s"
+            % (args.config, args.config, rec["copy_calibration_mib"], extra),
+            "python bench.py --summarize-pmc gpurun_out/pmc_fetch/%s_counter_collection.csv "
+            "gpurun_out/pmc_write/%s_counter_collection.csv --config %s%s" % (args.config, args.config, args.config, extra),
+        ]
         path = traffic_path(args.config, splits, not args.unfused)
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
