@@ -68,6 +68,9 @@ def _load():
         lib.oracle_split_combine.restype = ctypes.c_int
         lib.oracle_paged_kv_append.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P]
         lib.oracle_paged_kv_append.restype = i64
+        lib.oracle_varlen_attention.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f64,
+                                                P, i64, P, i32]
+        lib.oracle_varlen_attention.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -215,3 +218,39 @@ def paged_kv_append(k, v, slot_mapping, k_pool, v_pool) -> int:
     if n < 0:
         raise ValueError("oracle_paged_kv_append failed")
     return int(n)
+
+
+def varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, scale, units=None, threads=None):
+    """Paged varlen attention in float64: out[T][Hq][D] (or out[len(units)][D] for (token, hq) pairs).
+
+    q: [T][Hq][D] fp16, token-major; sequence s owns tokens cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1, its i-th token
+    at position pos_offsets[s] + i attends rows 0 .. pos_offsets[s] + i.  Pools and block_tables as decode_attention.
+    """
+    T, Hq, D = q.shape
+    N, Hkv, NP, D8, sixteen, eight = k_pool.shape
+    BS = NP * 16
+    if (sixteen, eight) != (16, 8) or D8 * 8 != D or v_pool.shape != (N, Hkv, NP, D, 16):
+        raise ValueError("pool shapes %s / %s do not match q %s" % (k_pool.shape, v_pool.shape, q.shape))
+    bt = _i32(block_tables)
+    cu = _i32(cu_seqlens_q)
+    pos = _i32(pos_offsets)
+    B = pos.shape[0]
+    if bt.ndim != 2 or bt.shape[0] != B or cu.shape != (B + 1,):
+        raise ValueError("block_tables must be [B][M], cu_seqlens_q [B+1], pos_offsets [B]")
+    M = bt.shape[1]
+    qb, kb, vb = _bits(q), _bits(k_pool), _bits(v_pool)
+    if threads is None:
+        threads = os.cpu_count() or 1
+    if units is None:
+        out = np.empty((T, Hq, D), dtype=np.float64)
+        up, n = None, 0
+    else:
+        u = _i32(units).reshape(-1, 2)
+        out = np.empty((u.shape[0], D), dtype=np.float64)
+        up, n = _ptr(u), u.shape[0]
+    rc = _load().oracle_varlen_attention(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(bt), _ptr(cu), _ptr(pos), B, T, Hq, Hkv,
+                                         D, BS, N, M, float(scale), up, n, _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError("oracle_varlen_attention failed (%d): bad geometry, prefix sums or positions, or a table "
+                         "entry outside the pool" % rc)
+    return out

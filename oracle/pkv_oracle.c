@@ -27,6 +27,10 @@
  *    Query head hq reads kv head hq / G with G = num_q_heads / num_kv_heads.
  *    [cortiq-engine 0.8.80, src/gpu_cuda.rs: the heads-per-kv-head grouping]
  *
+ *  - Paged varlen attention: several new query rows per sequence, each
+ *    attending the rows up to and including its own position (see
+ *    oracle_varlen_attention for the passages).
+ *
  *  - Split-K ("flash decoding") partials and their log-sum-exp combine.  The
  *    pages give only the buffer names partial_out / partial_m / partial_l and
  *    the two launches [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
@@ -137,13 +141,11 @@ static int64_t row_block(const oracle_problem *P, int s, int t)
     return p;
 }
 
-/* z_t = scale * sum_d q[d] * k_t[d] for rows t in [t0, t1).  Returns 0, or -2
- * when a row's block is not a valid pool block. */
-static int scores(const oracle_problem *P, int s, int hq, int t0, int t1, double *z)
+/* z_t = scale * sum_d q[d] * k_t[d] for rows t in [t0, t1) of sequence s,
+ * kv head hk, with q the D-vector of one query head.  Returns 0, or -2 when a
+ * row's block is not a valid pool block. */
+static int scores_for(const oracle_problem *P, int s, const uint16_t *q, int hk, int t0, int t1, double *z)
 {
-    int G = P->Hq / P->Hkv;
-    int hk = hq / G;
-    const uint16_t *q = P->q + ((int64_t)s * P->Hq + hq) * P->D;
     for (int t = t0; t < t1; ++t) {
         int64_t p = row_block(P, s, t);
         if (p < 0)
@@ -157,13 +159,18 @@ static int scores(const oracle_problem *P, int s, int hq, int t0, int t1, double
     return 0;
 }
 
-/* One output row: out[0..D) for (s, hq); weights[0..L) (optional) receives
- * the normalised softmax weights.  L <= 0 gives out = 0. */
-static int attention_unit(const oracle_problem *P, int s, int hq, double *out, double *weights)
+/* z for decode query (s, hq). */
+static int scores(const oracle_problem *P, int s, int hq, int t0, int t1, double *z)
 {
-    int L = P->context_lens[s];
     int G = P->Hq / P->Hkv;
-    int hk = hq / G;
+    return scores_for(P, s, P->q + ((int64_t)s * P->Hq + hq) * P->D, hq / G, t0, t1, z);
+}
+
+/* softmax(z) . V over rows 0..L-1 of sequence s, kv head hk, for one query
+ * vector q: out[0..D); weights[0..L) (optional) receives the normalised
+ * softmax weights.  L <= 0 gives out = 0. */
+static int attend(const oracle_problem *P, int s, const uint16_t *q, int hk, int L, double *out, double *weights)
+{
     for (int d = 0; d < P->D; ++d)
         out[d] = 0.0;
     if (L <= 0)
@@ -171,7 +178,7 @@ static int attention_unit(const oracle_problem *P, int s, int hq, double *out, d
     double *z = (double *)malloc(sizeof(double) * (size_t)L);
     if (!z)
         return -3;
-    int rc = scores(P, s, hq, 0, L, z);
+    int rc = scores_for(P, s, q, hk, 0, L, z);
     if (rc) {
         free(z);
         return rc;
@@ -196,6 +203,13 @@ static int attention_unit(const oracle_problem *P, int s, int hq, double *out, d
         out[d] /= l;
     free(z);
     return 0;
+}
+
+/* One decode output row: (s, hq) over the context_lens[s] rows of sequence s. */
+static int attention_unit(const oracle_problem *P, int s, int hq, double *out, double *weights)
+{
+    int G = P->Hq / P->Hkv;
+    return attend(P, s, P->q + ((int64_t)s * P->Hq + hq) * P->D, hq / G, P->context_lens[s], out, weights);
 }
 
 /* ------------------------------------------------------------------ */
@@ -462,4 +476,116 @@ int64_t oracle_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32
             }
     }
     return skipped;
+}
+
+/* ------------------------------------------------------------------ */
+/* Paged varlen attention (several new query rows per sequence).        */
+/* ------------------------------------------------------------------ */
+
+/* Sequence s owns query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of the
+ * token-major q[T][Hq][D] (and of out); its i-th new row sits at absolute
+ * position pos_offsets[s] + i of the sequence and attends rows
+ * 0 .. pos_offsets[s] + i (itself included, nothing after it).  The pool must
+ * already hold the new rows' K/V.
+ * [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs: paged_varlen_attention
+ * (q token-major [M_total][heads][dim]) and the q_len > 1 branch of
+ * paged_decode_attention, which passes cu_seqlens_q = [0, q_len] and
+ * pos_offsets = [final_kv_len - q_len]]
+ *
+ * units: NULL = every (token, head) in order, else n_units pairs
+ * (token, hq).  Returns 0; -1 for bad geometry, prefix sums that do not run
+ * 0 = cu[0] <= cu[1] <= ... <= cu[B] = T, a negative position, or a row past
+ * the table capacity M*BS; -2 for a table entry outside the pool. */
+typedef struct {
+    const oracle_problem *P;
+    const int32_t *cu, *pos;
+    int32_t T;
+    const int32_t *units;
+    int64_t n_units;
+    double *out;
+    int64_t next;
+    int rc;
+    pthread_mutex_t lock;
+} varlen_pool;
+
+static int varlen_row(const varlen_pool *W, int32_t tok, int32_t hq, double *out)
+{
+    const oracle_problem *P = W->P;
+    int s = 0;
+    while (s < P->B && W->cu[s + 1] <= tok)
+        ++s;
+    int i = tok - W->cu[s];
+    int G = P->Hq / P->Hkv;
+    return attend(P, s, P->q + ((int64_t)tok * P->Hq + hq) * P->D, hq / G, W->pos[s] + i + 1, out, NULL);
+}
+
+static void *varlen_worker(void *arg)
+{
+    varlen_pool *W = (varlen_pool *)arg;
+    for (;;) {
+        pthread_mutex_lock(&W->lock);
+        int64_t u = W->next++;
+        pthread_mutex_unlock(&W->lock);
+        if (u >= W->n_units)
+            break;
+        int32_t tok, hq;
+        if (W->units) {
+            tok = W->units[2 * u];
+            hq = W->units[2 * u + 1];
+        } else {
+            tok = (int32_t)(u / W->P->Hq);
+            hq = (int32_t)(u % W->P->Hq);
+        }
+        int rc = varlen_row(W, tok, hq, W->out + u * W->P->D);
+        if (rc) {
+            pthread_mutex_lock(&W->lock);
+            W->rc = rc;
+            pthread_mutex_unlock(&W->lock);
+        }
+    }
+    return NULL;
+}
+
+int oracle_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                            const int32_t *block_tables, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
+                            int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                            int32_t N, int32_t M, double scale,
+                            const int32_t *units, int64_t n_units, double *out, int32_t n_threads)
+{
+    oracle_problem P = {q, k_pool, v_pool, block_tables, NULL, B, Hq, Hkv, D, BS, N, M, scale};
+    if (check_geometry(&P) || T < 0)
+        return -1;
+    if (B > 0 && (cu_seqlens_q[0] != 0 || cu_seqlens_q[B] != T))
+        return -1;
+    if (B == 0 && T != 0)
+        return -1;
+    for (int s = 0; s < B; ++s) {
+        if (cu_seqlens_q[s + 1] < cu_seqlens_q[s] || pos_offsets[s] < 0)
+            return -1;
+        if ((int64_t)pos_offsets[s] + (cu_seqlens_q[s + 1] - cu_seqlens_q[s]) > (int64_t)M * BS)
+            return -1;
+    }
+    if (!units)
+        n_units = (int64_t)T * Hq;
+    for (int64_t u = 0; units && u < n_units; ++u)
+        if (units[2 * u] < 0 || units[2 * u] >= T || units[2 * u + 1] < 0 || units[2 * u + 1] >= Hq)
+            return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    varlen_pool W;
+    W.P = &P; W.cu = cu_seqlens_q; W.pos = pos_offsets; W.T = T; W.units = units; W.n_units = n_units;
+    W.out = out; W.next = 0; W.rc = 0;
+    pthread_mutex_init(&W.lock, NULL);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    int started = 0;
+    for (int i = 0; i < n_threads; ++i)
+        if (pthread_create(&th[i], NULL, varlen_worker, &W) == 0)
+            ++started;
+    if (started == 0)
+        varlen_worker(&W);
+    for (int i = 0; i < started; ++i)
+        pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&W.lock);
+    return W.rc;
 }

@@ -301,3 +301,86 @@ def algorithmic_bytes(case: DecodeCase) -> dict:
     idx = nb * 4 + case.B * 4
     app = 2 * 2 * case.num_tokens * case.Hkv * case.D * 2 + case.num_tokens * 4
     return {"kv": kv, "q_out": qo, "index": idx, "attention": kv + qo + idx, "append": app}
+
+
+@dataclass
+class VarlenCase:
+    """Inputs of paged varlen attention: sequence s owns the query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1
+    (token-major q[T][Hq][D]); its i-th new row sits at position pos_offsets[s] + i.  The new rows' K/V
+    (k_new / v_new, at slot_mapping) are written into the pools before attention; with ``poison_new`` the pools hold
+    POISON there until that append.  Rows of a sequence's last block past its final length hold POISON."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    BS: int
+    N: int
+    M: int
+    scale: float
+    q_lens: np.ndarray        # [B] int32
+    pos_offsets: np.ndarray   # [B] int32
+    cu_seqlens_q: np.ndarray  # [B+1] int32
+    block_tables: np.ndarray  # [B][M] int32, -1 past the used entries
+    q: np.ndarray             # [T][Hq][D] fp16
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    k_new: np.ndarray         # [T][Hkv][D] fp16
+    v_new: np.ndarray
+    slot_mapping: np.ndarray  # [T] int32
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def final_lens(self) -> np.ndarray:
+        return (self.pos_offsets + self.q_lens).astype(np.int32)
+
+
+def build_varlen_case(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int, q_lens, pos_offsets, seed: int,
+                      rotation: int = 0, extra_blocks: int = 3, scale: Optional[float] = None, q_scale: float = 1.0,
+                      kv_dist: str = "normal", poison_new: bool = True, M: Optional[int] = None) -> VarlenCase:
+    ql = np.ascontiguousarray(np.asarray(q_lens, dtype=np.int32))
+    po = np.ascontiguousarray(np.asarray(pos_offsets, dtype=np.int32))
+    final = ql + po
+    nbs = (final + BS - 1) // BS
+    if M is None:
+        M = max(1, int(nbs.max()) if B else 1)
+    N = int(nbs.sum()) + extra_blocks
+    perm = _rng(seed, rotation, "perm").permutation(N).astype(np.int32)
+    bt = carve_tables(final, BS, N, M, perm)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(ql)
+    T = int(cu[-1])
+    q = fill_f16(np.empty((max(T, 0), Hq, D), dtype=np.float16), seed, rotation, "q", "normal", q_scale)
+    k_pool, v_pool = _alloc_pools(N, Hkv, BS, D)
+    fill_f16(k_pool, seed, rotation, "k", kv_dist)
+    fill_f16(v_pool, seed, rotation, "v", kv_dist)
+    k_new = fill_f16(np.empty((T, Hkv, D), dtype=np.float16), seed, rotation, "knew", kv_dist)
+    v_new = fill_f16(np.empty((T, Hkv, D), dtype=np.float16), seed, rotation, "vnew", kv_dist)
+    slots = np.empty(T, dtype=np.int32)
+    for s in range(B):
+        for i in range(int(ql[s])):
+            t = int(po[s]) + i
+            slots[cu[s] + i] = int(bt[s, t // BS]) * BS + t % BS
+    tail = []
+    for s in range(B):
+        for t in range(int(final[s]), int(nbs[s]) * BS):
+            tail.append(int(bt[s, t // BS]) * BS + t % BS)
+    poison_rows(k_pool, v_pool, np.asarray(tail, dtype=np.int64), BS)
+    if poison_new:
+        poison_rows(k_pool, v_pool, slots, BS)
+    else:
+        for j, slot in enumerate(slots):
+            b, o = int(slot) // BS, int(slot) % BS
+            set_k_row(k_pool, b, slice(None), o, k_new[j])
+            set_v_row(v_pool, b, slice(None), o, v_new[j])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return VarlenCase(name, B, Hq, Hkv, D, BS, N, M, float(scale), ql, po, cu, bt, q, k_pool, v_pool, k_new, v_new,
+                      slots)

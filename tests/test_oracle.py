@@ -427,3 +427,98 @@ def test_append_then_attention_sees_the_new_row():
         K, V = _rows(c, s, 0)
         assert np.array_equal(K[-1].astype(np.float16), c.k_new[s, 0])
     assert np.max(np.abs(before)) > 100 and np.max(np.abs(after)) < 10
+
+
+# --------------------------------------------------------------------------------------------------------------
+# paged varlen attention (several new rows per sequence, causal within them)
+
+
+def _golden_varlen_cases():
+    with open(os.path.join(GOLDEN, "varlen_hand.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_varlen_cases(), ids=lambda c: c["name"])
+def test_golden_varlen(case):
+    k_pool, v_pool = _pools_from_rows(case)
+    q = _pad8(case["q"], case["D"]).astype(np.float16)
+    out = oracle.varlen_attention(q, k_pool, v_pool, case["block_tables"], case["cu_seqlens_q"],
+                                  case["pos_offsets"], _num(case["scale"]), threads=2)
+    np.testing.assert_allclose(out, _pad8(case["expected"], case["D"]), rtol=1e-14, atol=1e-14)
+
+
+def _varlen(c, threads=4, units=None, k_pool=None, v_pool=None):
+    return oracle.varlen_attention(c.q, c.k_pool if k_pool is None else k_pool, c.v_pool if v_pool is None else v_pool,
+                                   c.block_tables, c.cu_seqlens_q, c.pos_offsets, c.scale, units=units, threads=threads)
+
+
+def test_varlen_rows_are_decode_attention_at_their_position():
+    # reduction to the decode oracle: row i of sequence s is decode attention of that query over pos + i + 1 rows
+    c = W.build_varlen_case("v", 3, 8, 2, 64, 16, (3, 1, 6), (20, 0, 45), 31, poison_new=False)
+    out = _varlen(c)
+    for s in range(c.B):
+        for i in range(int(c.q_lens[s])):
+            t = int(c.cu_seqlens_q[s]) + i
+            ref = oracle.decode_attention(c.q[t:t + 1], c.k_pool, c.v_pool, c.block_tables[s:s + 1],
+                                          [int(c.pos_offsets[s]) + i + 1], c.scale, threads=1)
+            assert np.array_equal(out[t], ref[0])
+
+
+def test_varlen_matches_torch_causal_sdpa_on_gathered_rows():
+    torch = pytest.importorskip("torch")
+    for (Hq, Hkv, D, BS, ql, po) in [(8, 2, 64, 16, (4, 1, 7), (13, 0, 40)), (4, 4, 128, 32, (2, 9), (31, 64)),
+                                     (16, 2, 64, 64, (5,), (70,))]:
+        c = W.build_varlen_case("v", len(ql), Hq, Hkv, D, BS, ql, po, 100 + D + BS, poison_new=False)
+        out = _varlen(c)
+        for s in range(c.B):
+            n_kv = int(c.final_lens[s])
+            ks = np.empty((c.Hkv, n_kv, c.D))
+            vs = np.empty((c.Hkv, n_kv, c.D))
+            for t in range(n_kv):
+                b = int(c.block_tables[s, t // c.BS])
+                for h in range(c.Hkv):
+                    ks[h, t] = W.k_row(c.k_pool, b, h, t % c.BS)
+                    vs[h, t] = W.v_row(c.v_pool, b, h, t % c.BS)
+            t0, t1 = int(c.cu_seqlens_q[s]), int(c.cu_seqlens_q[s + 1])
+            qs = torch.from_numpy(c.q[t0:t1].astype(np.float64)).transpose(0, 1)        # [Hq][q_len][D]
+            kk = torch.from_numpy(ks).repeat_interleave(c.G, dim=0)                      # [Hq][n_kv][D]
+            vv = torch.from_numpy(vs).repeat_interleave(c.G, dim=0)
+            allowed = torch.arange(n_kv)[None, :] <= (int(c.pos_offsets[s]) + torch.arange(t1 - t0))[:, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(qs, kk, vv, attn_mask=allowed, scale=c.scale)
+            np.testing.assert_allclose(out[t0:t1], ref.transpose(0, 1).numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_varlen_row_ignores_every_later_row():
+    c = W.build_varlen_case("v", 2, 4, 2, 64, 16, (5, 3), (10, 29), 41, poison_new=False)
+    out = _varlen(c)
+    kp, vp = c.k_pool.copy(), c.v_pool.copy()
+    # scramble every new row but the first of each sequence: each sequence's first new row must not move
+    for s in range(c.B):
+        for i in range(1, int(c.q_lens[s])):
+            slot = int(c.slot_mapping[int(c.cu_seqlens_q[s]) + i])
+            b, o = slot // c.BS, slot % c.BS
+            W.set_k_row(kp, b, slice(None), o, np.full((c.Hkv, c.D), 7.0))
+            W.set_v_row(vp, b, slice(None), o, np.full((c.Hkv, c.D), -9.0))
+    out2 = _varlen(c, k_pool=kp, v_pool=vp)
+    for s in range(c.B):
+        t0 = int(c.cu_seqlens_q[s])
+        assert np.array_equal(out[t0], out2[t0])
+        assert not np.array_equal(out[t0 + 1], out2[t0 + 1])
+
+
+def test_varlen_sequences_without_new_rows_and_units():
+    c = W.build_varlen_case("v", 3, 4, 2, 64, 16, (2, 0, 3), (5, 9, 0), 43, poison_new=False)
+    out = _varlen(c)
+    assert out.shape == (5, 4, 64)
+    units = np.array([[4, 3], [0, 1], [2, 0]], dtype=np.int32)
+    part = _varlen(c, units=units)
+    for j, (t, h) in enumerate(units):
+        assert np.array_equal(part[j], out[t, h])
+
+
+@pytest.mark.parametrize("cu,pos", [([1, 2, 3], [0, 0]), ([0, 2, 1], [0, 0]), ([0, 1, 3], [-1, 0]),
+                                    ([0, 1, 3], [0, 47])])
+def test_varlen_rejects_bad_prefix_sums_and_positions(cu, pos):
+    c = W.build_varlen_case("v", 2, 4, 2, 64, 16, (1, 2), (3, 4), 44, poison_new=False, M=3)
+    with pytest.raises(ValueError):
+        oracle.varlen_attention(c.q, c.k_pool, c.v_pool, c.block_tables, cu, pos, c.scale)
