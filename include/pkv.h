@@ -205,6 +205,42 @@ int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool
                                        void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_paged_varlen_attention -- attention for several new query rows per
+ *   sequence (speculative verification, chunked prefill): sequence s owns the
+ *   rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of q and out; its i-th new row
+ *   sits at position pos_offsets[s] + i and attends rows 0 .. pos_offsets[s] + i
+ *   of the sequence (itself included, nothing after it), gathered through
+ *   block_tables[s] as in pkv_paged_decode_attention.  The pools must already
+ *   hold the new rows (pkv_paged_kv_append them first).
+ *   [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs: paged_varlen_attention,
+ *   paged_varlen_split_k_dispatch, and the q_len > 1 branch of
+ *   paged_decode_attention: cu_seqlens_q = [0, q_len],
+ *   pos_offsets = [final_kv_len - q_len]]
+ *   q, out: [total_q_tokens][num_q_heads][head_dim] fp16, token-major,
+ *     16-byte aligned.  cu_seqlens_q: [num_seqs + 1] int32 prefix sums,
+ *     cu_seqlens_q[0] = 0, non-decreasing, cu_seqlens_q[num_seqs] =
+ *     total_q_tokens.  pos_offsets: [num_seqs] int32, >= 0, with
+ *     pos_offsets[s] + (new rows of s) <= block_size * max_blocks_per_seq.
+ *     Device-resident and not validated: values outside these rules never
+ *     make a kernel touch memory outside the arrays, but results are then
+ *     unspecified.
+ *   num_splits: 0 = the library chooses from the grid size (a single pass
+ *     once the workgroups fill about half the CUs), 1 = single pass, > 1 = that
+ *     many splits per tile of new rows, then the combine (partials in the
+ *     library-owned workspace, as pkv_paged_decode_attention).
+ *   max_q_len: host upper bound of the new rows of any sequence, used only to
+ *     size the grid (0 = total_q_tokens); a smaller value stays correct, the
+ *     workgroups then loop.  max_context_hint: as pkv_paged_decode_attention.
+ *   num_seqs == 0 or total_q_tokens == 0 is a no-op.
+ *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                               pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *cu_seqlens_q, const int32_t *pos_offsets, int32_t num_seqs,
+                               int32_t total_q_tokens, int32_t num_q_heads, float scale, uint16_t *out,
+                               int32_t num_splits, int32_t max_q_len, int32_t max_context_hint, void *stream);
+
+/* ---------------------------------------------------------------------------
  * pkv_plan_decode -- the dispatcher, a pure host function (no device call
  * when cu_count > 0; cu_count <= 0 queries the current device).
  *   Picks single pass or a split count from the number of (sequence, kv head)

@@ -180,17 +180,14 @@ int check_decode_pointers(const void *q, const void *k_pool, const void *v_pool,
 }
 
 // The dispatcher.  Work per (sequence, kv head) tile is read once, so the
-// question is only how many workgroups the grid needs:
-//  - a tile's KV streams through one workgroup, so a grid of T = B*Hkv tiles
-//    keeps every CU busy only if T is a few times the CU count, and the
-//    longest tile bounds the step when it is much longer than the average;
-//  - splitting costs one extra launch plus G*(D+2)*4 bytes written and read
-//    per split, small next to the split's own KV bytes when a split keeps at
-//    least a few dozen blocks.
-// Auto mode therefore keeps a single pass when the grid already has >= 2
-// workgroups per CU and tiles are short, and otherwise splits enough to reach
-// ~2 workgroups per CU and to cap any split at 256 blocks (4096 rows at
-// BS=16); the pages' 128-SM constants become the device's CU count.
+// question is only how many workgroups the grid needs.  One workgroup streams
+// at most ~50 GB/s (one CU's share of outstanding misses), so a single pass
+// reaches the HBM roofline once about half the CUs hold a tile; with fewer
+// tiles each is split into about CUs / tiles ranges (one round of the CUs, each
+// range at least 8 blocks).  A split costs a combine launch and
+// G*(D+2)*4 bytes written and read per split.  The pages' 128-SM constants
+// become the device's CU count; the rules and waves per workgroup come from
+// measurements on MI355X.
 int plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                 int32_t max_blocks_per_seq, int32_t max_context_hint, int32_t num_splits, int32_t cu_count,
                 int32_t lds_limit, pkv_decode_plan *plan) {
@@ -418,6 +415,126 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
                     num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, k_new, v_new);
 }
 
+// Paged varlen attention (several new query rows per sequence): plan, checks, launches.
+int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool, pkv_pool_desc pool,
+                const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q,
+                const int32_t *pos_offsets, int32_t num_seqs, int32_t total_q, int32_t num_q_heads, float scale,
+                uint16_t *out, int32_t num_splits, int32_t max_q_len, int32_t max_context_hint, hipStream_t stream) {
+    int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
+    if (rc)
+        return rc;
+    if (total_q < 0 || num_splits < 0 || max_q_len < 0 || max_context_hint < 0)
+        return fail(PKV_EINVAL, "total_q_tokens, num_splits, max_q_len and max_context_hint must be >= 0 "
+                    "(got %d, %d, %d, %d)", total_q, num_splits, max_q_len, max_context_hint);
+    if (!isfinite(scale))
+        return fail(PKV_EINVAL, "scale must be finite");
+    if (num_seqs == 0 || total_q == 0)
+        return ok();
+    if (!q || !k_pool || !v_pool || !block_tables || !cu_seqlens_q || !pos_offsets || !out)
+        return fail(PKV_EINVAL, "null device pointer (q=%p k_pool=%p v_pool=%p block_tables=%p cu_seqlens_q=%p "
+                    "pos_offsets=%p out=%p)", q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, out);
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16))
+        return fail(PKV_EINVAL, "q, k_pool, v_pool and out must be 16-byte aligned");
+    if (!aligned(block_tables, 4) || !aligned(cu_seqlens_q, 4) || !aligned(pos_offsets, 4))
+        return fail(PKV_EINVAL, "block_tables, cu_seqlens_q and pos_offsets must be 4-byte aligned");
+    DeviceFacts facts;
+    rc = device_facts(&facts);
+    if (rc)
+        return rc;
+    const int G = num_q_heads / pool.num_kv_heads;
+    const int R = 16 / G;
+    const int64_t qmax = max_q_len > 0 && max_q_len < total_q ? max_q_len : total_q;
+    const int64_t tiles_per_seq = (qmax + R - 1) / R;
+    // workgroups that find work: at most one per R new rows plus one partial tile per sequence
+    int64_t active = (int64_t)num_seqs * tiles_per_seq;
+    const int64_t bound = ((int64_t)total_q + R - 1) / R + num_seqs;
+    if (active > bound)
+        active = bound;
+    active *= pool.num_kv_heads;
+    const int64_t cap = (int64_t)max_blocks_per_seq * pool.block_size;
+    const int64_t lmax = max_context_hint > 0 && max_context_hint < cap ? max_context_hint : cap;
+    const int64_t nbmax = (lmax + pool.block_size - 1) / pool.block_size;
+    int S = num_splits;
+    if (S == 0) {
+        S = 1;
+        const int64_t cu = facts.cu_count > 0 ? facts.cu_count : 256;
+        if (nbmax > 8 && 2 * active < cu) {
+            int64_t want = (cu + active - 1) / active;
+            if (want > nbmax / 8)
+                want = nbmax / 8;
+            if (want > 64)
+                want = 64;
+            S = (int)(want < 1 ? 1 : want);
+        }
+    }
+    if ((int64_t)num_seqs * tiles_per_seq * pool.num_kv_heads * S > INT32_MAX || S > 65535)
+        return fail(PKV_EINVAL, "varlen grid (%d sequences x %lld tiles x %d kv heads x %d splits) is too large",
+                    num_seqs, (long long)tiles_per_seq, pool.num_kv_heads, S);
+    int waves = pkv::max_waves_per_group(pool.head_dim);
+    const size_t limit = facts.lds_per_block > 0 ? (size_t)facts.lds_per_block : (size_t)65536;
+    while (waves > 1 && pkv::varlen_lds_bytes(pool.head_dim, waves) > limit)
+        waves >>= 1;
+    if (pkv::varlen_lds_bytes(pool.head_dim, waves) > limit)
+        return fail(PKV_EUNSUPPORTED, "varlen needs %zu LDS bytes, the device allows %zu",
+                    pkv::varlen_lds_bytes(pool.head_dim, waves), limit);
+
+    pkv::VarlenParams p;
+    memset(&p, 0, sizeof p);
+    p.q = reinterpret_cast<const _Float16 *>(q);
+    p.block_tables = block_tables;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.pos_offsets = pos_offsets;
+    p.Hq = num_q_heads;
+    p.Hkv = pool.num_kv_heads;
+    p.G = G;
+    p.N = pool.num_blocks;
+    p.M = max_blocks_per_seq;
+    p.T = total_q;
+    p.R = R;
+    p.tiles_per_seq = (int32_t)tiles_per_seq;
+    p.num_splits = S;
+    p.chunk_blocks = 0;
+    p.scale_log2 = scale * 1.44269504088896340736f;
+    p.k_pool = reinterpret_cast<const _Float16 *>(k_pool);
+    p.v_pool = reinterpret_cast<const _Float16 *>(v_pool);
+    p.out = reinterpret_cast<_Float16 *>(out);
+    if (S == 1) {
+        hipError_t e = pkv::launch_varlen(p, num_seqs, pool.head_dim, pool.block_size, waves, false, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "varlen kernel launch");
+        return ok();
+    }
+    const WsLayout L = ws_layout(total_q, num_q_heads, pool.head_dim, S);
+    void *ws = nullptr;
+    rc = library_workspace(L.total, stream, &ws);
+    if (rc)
+        return rc;
+    char *base = static_cast<char *>(ws);
+    p.part_o = reinterpret_cast<float *>(base + L.o_off);
+    p.part_m = reinterpret_cast<float *>(base + L.m_off);
+    p.part_l = reinterpret_cast<float *>(base + L.l_off);
+    hipError_t e = pkv::launch_varlen(p, num_seqs, pool.head_dim, pool.block_size, waves, true, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "varlen split phase-1 kernel launch");
+    pkv::CombineParams c;
+    memset(&c, 0, sizeof c);
+    c.part_o = p.part_o;
+    c.part_m = p.part_m;
+    c.part_l = p.part_l;
+    c.context_lens = nullptr;  // every split of every row was written
+    c.out = p.out;
+    c.B = total_q;
+    c.Hq = num_q_heads;
+    c.BS = pool.block_size;
+    c.M = max_blocks_per_seq;
+    c.num_splits = S;
+    c.chunk_blocks = 0;
+    e = pkv::launch_combine(c, pool.head_dim, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "varlen combine kernel launch");
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -630,4 +747,15 @@ const char *pkv_last_error(void) { return g_error; }
 
 const char *pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
 
+int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                               pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *cu_seqlens_q, const int32_t *pos_offsets, int32_t num_seqs,
+                               int32_t total_q_tokens, int32_t num_q_heads, float scale, uint16_t *out,
+                               int32_t num_splits, int32_t max_q_len, int32_t max_context_hint, void *stream) {
+    return varlen_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, cu_seqlens_q, pos_offsets, num_seqs,
+                       total_q_tokens, num_q_heads, scale, out, num_splits, max_q_len, max_context_hint,
+                       static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"
+

@@ -31,11 +31,31 @@ struct DecodeParams {
     _Float16 *v_dst;
 };
 
+// Arguments of the varlen attention kernel (several new query rows per sequence).
+struct VarlenParams {
+    const _Float16 *q;            // [T][Hq][D] token-major
+    const int32_t *block_tables;  // [B][M]
+    const int32_t *cu_seqlens_q;  // [B+1]
+    const int32_t *pos_offsets;   // [B]
+    int32_t Hq, Hkv, G, N, M, T;
+    int32_t R;                    // new rows per tile (16 / G)
+    int32_t tiles_per_seq;        // tile slots per (sequence, kv head) in the grid
+    int32_t num_splits;           // 1 = one pass
+    int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(nb / S) per tile
+    float scale_log2;
+    const _Float16 *k_pool;
+    const _Float16 *v_pool;
+    _Float16 *out;                // [T][Hq][D]                (one pass)
+    float *part_o;                // [T][Hq][S][D]             (splits)
+    float *part_m;                // [T][Hq][S]
+    float *part_l;                // [T][Hq][S]
+};
+
 struct CombineParams {
     const float *part_o;
     const float *part_m;
     const float *part_l;
-    const int32_t *context_lens;
+    const int32_t *context_lens;  // null: every split of every row was written (varlen)
     _Float16 *out;
     int32_t B, Hq, BS, M;
     int32_t num_splits, chunk_blocks;
@@ -59,6 +79,9 @@ size_t decode_lds_bytes(int head_dim, int G, int waves);
 hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size, int waves,
                          bool split, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int head_dim, hipStream_t stream);
+size_t varlen_lds_bytes(int head_dim, int waves);
+hipError_t launch_varlen(const VarlenParams &p, int num_seqs, int head_dim, int block_size, int waves, bool split,
+                         hipStream_t stream);
 hipError_t launch_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream);
 

@@ -133,6 +133,15 @@ __device__ __forceinline__ void load_unit(Frag<D, BS> &f, const _Float16 *kb, co
                                                                                 kKvLoadPolicy));
 }
 
+// Last row each score column may attend.  col: this lane's column (per lane); first: the smallest over the tile's
+// columns; all: the largest (V rows past it are never used by any column and are zeroed).  A decode tile has one
+// limit, L - 1, for every column; a varlen tile gives each (query row, head) column the position of its row.
+struct RowLimits {
+    int col;
+    int first;
+    int all;
+};
+
 // One 16-row unit: scores, online-softmax update, P.V accumulation.  A dead unit (its block id names no pool
 // block) is computed with every row masked, so that the loads of every unit are consumed on every path.
 //
@@ -143,7 +152,8 @@ __device__ __forceinline__ void load_unit(Frag<D, BS> &f, const _Float16 *kb, co
 // A unit whose block id names no pool block (dead) is neither written nor used.
 template <int D, int BS>
 __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D / 32], f32x4 (&o)[D / 16],
-                                             float &m_run, float &l_run, int u, int L, bool dead, int r, int g4,
+                                             float &m_run, float &l_run, int u, const RowLimits &lim, bool dead,
+                                             int r, int g4,
                                              float scale_log2, int prow, const _Float16 *pk, const _Float16 *pv,
                                              _Float16 *wb_k, _Float16 *wb_v, uint32_t k_lane, uint32_t v_lane) {
     constexpr int KC = Frag<D, BS>::KC;
@@ -182,14 +192,14 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
     for (int e = 0; e < 4; ++e)
         y[e] = sc[e] * scale_log2;
     const int t0 = u * 16 + 4 * g4;  // row of y[0] in the sequence
-    if (dead || u * 16 + 16 > L) {   // the unit holding row L-1, or a dead unit (wave-uniform branch)
+    if (dead || u * 16 + 15 > lim.first) {  // a unit past some column's last row, or a dead unit (wave-uniform)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bool live = !dead && (t0 + e) < L;
-            y[e] = live ? y[e] : -INFINITY;
+            y[e] = (!dead && (t0 + e) <= lim.col) ? y[e] : -INFINITY;
+            const bool row_ok = !dead && (t0 + e) <= lim.all;
 #pragma unroll
             for (int c = 0; c < VC; ++c)
-                f.v[c][e] = live ? f.v[c][e] : (_Float16)0.0f;  // rows past L may hold anything
+                f.v[c][e] = row_ok ? f.v[c][e] : (_Float16)0.0f;  // rows past every column's last may hold anything
         }
     }
     const float bm = rows_max(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])));
@@ -294,6 +304,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     }
     const int u_begin = b0 * SPB;
     const int u_end = min(b1 * SPB, (L + 15) >> 4);
+    const RowLimits lim = {L - 1, L - 1, L - 1};
     const int u_first = u_begin + wave;  // wave w takes units u_begin + w, + w + NW, ...
     const int n_units = u_first < u_end ? (u_end - u_first + NW - 1) / NW : 0;
     // Fused decode step: the workgroup whose range holds row L-1 writes the sequence's new K/V row there (the slot
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
                 load_unit<D, BS>(f[jn], k_ptr(blk, uu[jn]), v_ptr(blk, uu[jn]), k_lane, v_lane,
                                  k + NS - 1 < n_units && !dead[jn]);
                 raw_q[j] = raw_block(u_first + min(k + 2 * NS - 1, n_units - 1) * NW);
-                compute_unit<D, BS>(f[j], qf, o, m_run, l_run, uu[j], L, dead[j], r, g4, p.scale_log2,
+                compute_unit<D, BS>(f[j], qf, o, m_run, l_run, uu[j], lim, dead[j], r, g4, p.scale_log2,
                                     FUSED && uu[j] == patch_unit ? prow_row : -1, sm_pk, sm_pv,
                                     FUSED ? p.k_dst + (k_ptr(bk[j], uu[j]) - p.k_pool) : nullptr,
                                     FUSED ? p.v_dst + (v_ptr(bk[j], uu[j]) - p.v_pool) : nullptr, k_lane, v_lane);
@@ -445,6 +456,190 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     }
 }
 
+// Paged varlen attention [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs: paged_varlen_attention,
+// paged_varlen_split_k_dispatch and the tiled_q4 variant's shared KV reads]: sequence s owns query rows
+// cu[s] .. cu[s+1]-1 of the token-major q, its i-th new row at position pos[s] + i attending rows 0 .. pos[s] + i.
+// One workgroup per (sequence, tile slot, kv head[, split]).  A tile is R = 16 / G consecutive new rows of one
+// sequence; its 16 matrix-core columns are the (row, head) pairs c = row * G + head, so every K/V byte a workgroup
+// loads serves all R rows and the whole GQA group; each column carries its own causal limit (RowLimits).  Tile slot
+// j takes the sequence's tiles j, j + tiles_per_seq, ... (any q length is covered whatever the host's estimate).
+// With splits, phase 1 writes every split of every valid column -- an empty one as m = -1e30, l = 0, O = 0 -- so
+// the combine needs no per-row split count.
+template <int D, int BS, int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
+    constexpr int KC = D / 32;
+    constexpr int VC = D / 16;
+    constexpr int SPB = BS / 16;
+    constexpr int DP = D + 4;
+    constexpr int NS = pipeline_stages<D, NW>();
+    extern __shared__ float smem[];
+
+    unsigned id = blockIdx.x;
+    const int split = SPLIT ? (int)(id % (unsigned)p.num_splits) : 0;
+    if (SPLIT)
+        id /= (unsigned)p.num_splits;
+    const int hk = (int)(id % (unsigned)p.Hkv);
+    id /= (unsigned)p.Hkv;
+    const int slot = (int)(id % (unsigned)p.tiles_per_seq);
+    const int s = (int)(id / (unsigned)p.tiles_per_seq);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int r = lane & 15;
+    const int g4 = lane >> 4;
+
+    const int32_t *bt = p.block_tables + (int64_t)s * p.M;
+    const int max_units = p.M * SPB;
+    const int cap = p.M * BS;  // rows the table can name
+    int q0 = uniform_load(p.cu_seqlens_q, s);
+    int q1 = uniform_load(p.cu_seqlens_q, s + 1);
+    int pos = uniform_load(p.pos_offsets, s);
+    q0 = q0 < 0 ? 0 : (q0 > p.T ? p.T : q0);
+    q1 = q1 < q0 ? q0 : (q1 > p.T ? p.T : q1);
+    pos = pos < 0 ? 0 : (pos > cap ? cap : pos);
+    if (p.N <= 0)
+        q1 = q0;  // an empty pool holds no rows
+    const int qlen = q1 - q0;
+
+    const uint32_t k_lane = (uint32_t)(16 * lane);
+    const uint32_t v_lane = (uint32_t)(32 * r + 8 * g4);
+    const int64_t head_off = (int64_t)hk * (BS * D);
+    const int64_t block_stride = (int64_t)p.Hkv * (BS * D);
+    auto raw_block = [&](int u) -> int { return uniform_load(bt, min(u, max_units - 1) / SPB); };
+    auto resolve = [&](int raw, bool &dead) -> int {
+        const int b = __builtin_amdgcn_readfirstlane(raw);
+        dead = (unsigned)b >= (unsigned)p.N;
+        return dead ? 0 : b;
+    };
+    auto k_ptr = [&](int blk, int u) {
+        return p.k_pool + (int64_t)blk * block_stride + head_off + (u % SPB) * (16 * D);
+    };
+    auto v_ptr = [&](int blk, int u) {
+        return p.v_pool + (int64_t)blk * block_stride + head_off + (u % SPB) * (16 * D);
+    };
+    float *sm_m = smem;
+    float *sm_l = smem + NW * 16;
+    float *sm_o = smem + 2 * NW * 16;
+
+    for (int tile = slot; tile * p.R < qlen; tile += p.tiles_per_seq) {
+        const int i0 = tile * p.R;
+        const int nrows = min(p.R, qlen - i0);
+        const int ncols = nrows * p.G;
+        // column r of this lane: new row i0 + r / G, query head hk * G + r % G
+        const int crow = r / p.G;
+        const bool col_ok = r < ncols;
+        RowLimits lim;
+        lim.first = min(pos + i0, cap - 1);
+        lim.all = min(pos + i0 + nrows - 1, cap - 1);
+        lim.col = col_ok ? min(pos + i0 + crow, cap - 1) : -1;
+        const int nb = (lim.all + 1 + BS - 1) / BS;
+        int b0 = 0, b1 = nb;
+        if (SPLIT) {
+            const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (nb + p.num_splits - 1) / p.num_splits;
+            b0 = min(split * chunk, nb);
+            b1 = min(nb, b0 + chunk);
+        }
+        const int u_begin = b0 * SPB;
+        const int u_end = min(b1 * SPB, (lim.all + 1 + 15) >> 4);
+        const int u_first = u_begin + wave;
+        const int n_units = u_first < u_end ? (u_end - u_first + NW - 1) / NW : 0;
+
+        f16x8 qf[KC];
+        {
+            const int tok = q0 + i0 + (col_ok ? crow : 0);
+            const int hq = hk * p.G + (col_ok ? r % p.G : 0);
+            const _Float16 *qrow = p.q + ((int64_t)tok * p.Hq + hq) * D + 8 * g4;
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                qf[c] = *reinterpret_cast<const f16x8 *>(qrow + 32 * c);
+        }
+        f32x4 o[VC];
+#pragma unroll
+        for (int c = 0; c < VC; ++c)
+            o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        float m_run = kNegBig;
+        float l_run = 0.f;
+
+        if (n_units > 0) {
+            Frag<D, BS> f[NS];
+            bool dead[NS];
+            int uu[NS];
+            int raw_q[NS];
+#pragma unroll
+            for (int j = 0; j < NS - 1; ++j) {
+                uu[j] = u_first + j * NW;
+                const int blk = resolve(raw_block(uu[j]), dead[j]);
+                load_unit<D, BS>(f[j], k_ptr(blk, uu[j]), v_ptr(blk, uu[j]), k_lane, v_lane,
+                                 j < n_units && !dead[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+                raw_q[j] = raw_block(u_first + min(NS - 1 + j, n_units - 1) * NW);
+            int k = 0;
+            for (;;) {
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    const int jn = (j + NS - 1) % NS;
+                    uu[jn] = u_first + min(k + NS - 1, n_units - 1) * NW;
+                    const int blk = resolve(raw_q[j], dead[jn]);
+                    load_unit<D, BS>(f[jn], k_ptr(blk, uu[jn]), v_ptr(blk, uu[jn]), k_lane, v_lane,
+                                     k + NS - 1 < n_units && !dead[jn]);
+                    raw_q[j] = raw_block(u_first + min(k + 2 * NS - 1, n_units - 1) * NW);
+                    compute_unit<D, BS>(f[j], qf, o, m_run, l_run, uu[j], lim, dead[j], r, g4, p.scale_log2, -1,
+                                        nullptr, nullptr, nullptr, nullptr, k_lane, v_lane);
+                    if (++k >= n_units)
+                        goto tile_done;
+                }
+            }
+        tile_done:;
+        }
+
+        l_run = rows_sum(l_run);
+        if (tile != slot)
+            __syncthreads();  // the previous tile's merge has read the LDS
+        if (g4 == 0) {
+            sm_m[wave * 16 + r] = m_run;
+            sm_l[wave * 16 + r] = l_run;
+        }
+        if (col_ok) {
+            float *dst = sm_o + (wave * 16 + r) * DP + 4 * g4;
+#pragma unroll
+            for (int c = 0; c < VC; ++c) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[16 * c + e] = o[c][e];
+            }
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < ncols * D; idx += NW * 64) {
+            const int c = idx / D;
+            const int d = idx - c * D;
+            float M = kNegBig;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                M = fmaxf(M, sm_m[w * 16 + c]);
+            float den = 0.f, num = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float a = exp2_fast(sm_m[w * 16 + c] - M);
+                den += a * sm_l[w * 16 + c];
+                num += a * sm_o[(w * 16 + c) * DP + d];
+            }
+            const int64_t row = (int64_t)(q0 + i0 + c / p.G) * p.Hq + hk * p.G + c % p.G;  // token * Hq + hq
+            if (!SPLIT) {
+                p.out[row * D + d] = (_Float16)(den > 0.f ? num / den : 0.f);
+            } else {
+                const int64_t base = row * p.num_splits + split;
+                const bool empty = b0 >= b1;
+                p.part_o[base * D + d] = empty ? 0.f : num;
+                if (d == 0) {
+                    p.part_m[base] = empty ? kNegBig : M * kLn2;
+                    p.part_l[base] = empty ? 0.f : den;
+                }
+            }
+        }
+    }
+}
+
 // Split-K phase 2: one wavefront per (sequence, query head), lanes over dims.
 // out = sum_j e^(m_j - M) O_j / sum_j e^(m_j - M) l_j over the non-empty splits.
 template <int D>
@@ -455,13 +650,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     if (row >= p.B * p.Hq)
         return;
     const int s = row / p.Hq;
-    int L = p.context_lens[s];
-    L = L < 0 ? 0 : (L > p.M * p.BS ? p.M * p.BS : L);
-    const int nb = (L + p.BS - 1) / p.BS;
-    int nvalid = 0;
-    if (nb > 0) {
-        const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (nb + p.num_splits - 1) / p.num_splits;
-        nvalid = min(p.num_splits, (nb + chunk - 1) / chunk);
+    int nvalid = p.num_splits;  // no lengths: every split was written (varlen phase 1)
+    if (p.context_lens != nullptr) {
+        int L = p.context_lens[s];
+        L = L < 0 ? 0 : (L > p.M * p.BS ? p.M * p.BS : L);
+        const int nb = (L + p.BS - 1) / p.BS;
+        nvalid = 0;
+        if (nb > 0) {
+            const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (nb + p.num_splits - 1) / p.num_splits;
+            nvalid = min(p.num_splits, (nb + chunk - 1) / chunk);
+        }
     }
     const int64_t base = (int64_t)row * p.num_splits;
     float M = kNegBig;
@@ -632,6 +830,55 @@ hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int 
     case 64: return launch_decode_d<64>(p, num_seqs, block_size, waves, split, stream);
     case 128: return launch_decode_d<128>(p, num_seqs, block_size, waves, split, stream);
     case 256: return launch_decode_d<256>(p, num_seqs, block_size, waves, split, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+size_t varlen_lds_bytes(int head_dim, int waves) {
+    return sizeof(float) * (size_t)merge_floats(head_dim, 16, waves);
+}
+
+template <int D, int BS, int NW>
+static hipError_t launch_varlen_t(const VarlenParams &p, int num_seqs, bool split, hipStream_t stream) {
+    dim3 grid((unsigned)((int64_t)num_seqs * p.tiles_per_seq * p.Hkv * (split ? p.num_splits : 1)), 1u, 1u);
+    dim3 block(NW * 64);
+    const size_t lds = varlen_lds_bytes(D, NW);
+    if (split)
+        hipLaunchKernelGGL((varlen_kernel<D, BS, NW, true>), grid, block, lds, stream, p);
+    else
+        hipLaunchKernelGGL((varlen_kernel<D, BS, NW, false>), grid, block, lds, stream, p);
+    return hipGetLastError();
+}
+template <int D, int BS>
+static hipError_t launch_varlen_w(const VarlenParams &p, int num_seqs, int waves, bool split, hipStream_t stream) {
+    switch (waves) {
+    case 1: return launch_varlen_t<D, BS, 1>(p, num_seqs, split, stream);
+    case 2: return launch_varlen_t<D, BS, 2>(p, num_seqs, split, stream);
+    case 4: return launch_varlen_t<D, BS, 4>(p, num_seqs, split, stream);
+    case 8:
+        if constexpr (D >= 256)
+            return hipErrorInvalidValue;
+        else
+            return launch_varlen_t<D, BS, 8>(p, num_seqs, split, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+template <int D>
+static hipError_t launch_varlen_d(const VarlenParams &p, int num_seqs, int block_size, int waves, bool split,
+                                  hipStream_t stream) {
+    switch (block_size) {
+    case 16: return launch_varlen_w<D, 16>(p, num_seqs, waves, split, stream);
+    case 32: return launch_varlen_w<D, 32>(p, num_seqs, waves, split, stream);
+    case 64: return launch_varlen_w<D, 64>(p, num_seqs, waves, split, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+hipError_t launch_varlen(const VarlenParams &p, int num_seqs, int head_dim, int block_size, int waves, bool split,
+                         hipStream_t stream) {
+    switch (head_dim) {
+    case 64: return launch_varlen_d<64>(p, num_seqs, block_size, waves, split, stream);
+    case 128: return launch_varlen_d<128>(p, num_seqs, block_size, waves, split, stream);
+    case 256: return launch_varlen_d<256>(p, num_seqs, block_size, waves, split, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -39,6 +39,7 @@ EXPORTED = [
     "pkv_paged_decode_attention_ws",
     "pkv_paged_decode_attention_planned",
     "pkv_paged_decode_step",
+    "pkv_paged_varlen_attention",
     "pkv_plan_decode",
     "pkv_decode_workspace_bytes",
     "pkv_paged_decode_split_partials",
@@ -85,6 +86,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.pkv_paged_decode_attention_planned.argtypes = attn[:11] + [ctypes.POINTER(DecodePlan), vp, sz, vp]
         lib.pkv_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, vp, i32, i32,
                                               vp]
+        lib.pkv_paged_varlen_attention.argtypes = [vp, vp, vp, PoolDesc, vp, i32, vp, vp, i32, i32, i32, f32, vp, i32,
+                                                   i32, i32, vp]
         lib.pkv_plan_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodePlan)]
         lib.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.pkv_decode_workspace_bytes.restype = sz
@@ -299,6 +302,34 @@ def paged_decode_split_combine(partial_out, partial_m, partial_l, context_lens, 
                                                  _ptr(context_lens), int(B), int(Hq), int(D), int(block_size),
                                                  int(max_blocks_per_seq), int(S), int(chunk_blocks), _ptr(out),
                                                  _stream(stream)))
+    return out
+
+
+def paged_varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, scale: float, out=None,
+                           num_splits: int = 0, max_q_len: int = 0, max_context_hint: int = 0, stream=None):
+    """Attention of several new query rows per sequence (pkv_paged_varlen_attention): q and out are token-major
+    [T][Hq][D]; sequence s owns rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1, its i-th new row at position
+    pos_offsets[s] + i attending rows 0 .. pos_offsets[s] + i.  The pools must already hold the new rows."""
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(q, torch.float16, "q", 3)
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1)
+    _dev(pos_offsets, torch.int32, "pos_offsets", 1)
+    T, Hq, D = q.shape
+    B = int(pos_offsets.shape[0])
+    if D != pool.head_dim:
+        raise ValueError("q head_dim %d != pool head_dim %d" % (D, pool.head_dim))
+    if block_tables.shape[0] != B or cu_seqlens_q.shape[0] != B + 1:
+        raise ValueError("block_tables must have num_seqs = %d rows and cu_seqlens_q num_seqs + 1 entries" % B)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, torch.float16, "out", 3)
+    _check(load().pkv_paged_varlen_attention(_ptr(q), _ptr(k_pool), _ptr(v_pool), pool, _ptr(block_tables),
+                                             int(block_tables.shape[1]), _ptr(cu_seqlens_q), _ptr(pos_offsets), B,
+                                             int(T), int(Hq), float(scale), _ptr(out), int(num_splits),
+                                             int(max_q_len), int(max_context_hint), _stream(stream)))
     return out
 
 

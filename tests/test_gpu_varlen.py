@@ -1,0 +1,87 @@
+"""GPU parity of paged varlen attention (several new query rows per sequence, causal within them) against the
+CPU oracle, through the C ABI: the new rows are appended with pkv_paged_kv_append, then attended; the oracle
+applies the same append to its copy of the pools.  Bar: max|gpu - ref| <= 2e-3 and <= 1e-2 of max|ref|.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_decode_04_amd import workloads as W
+from test_gpu_parity import assert_close, say, torch_cuda, _dev  # noqa: F401  (fixture and helpers)
+
+pytestmark = pytest.mark.gpu
+
+# (Hq, Hkv, D, BS, new rows per sequence, positions of their first new row).  Tiles hold 16 / G new rows, so these
+# cover G = 4 (4 rows per tile, ragged tiles, a sequence without new rows, 16 rows = 4 tiles), G = 1 with D = 256
+# (16 rows per tile), G = 16 (one row per tile), G = 3 (5 rows, 15 of 16 columns) and speculative-verify shapes.
+VARLEN_GEOMS = [
+    (8, 2, 64, 16, (1, 4, 7, 0, 16), (0, 30, 100, 12, 3)),
+    (32, 8, 128, 16, (4, 4, 4, 4), (511, 1000, 63, 2040)),
+    (16, 16, 256, 32, (3, 17), (40, 100)),
+    (32, 2, 128, 64, (2, 5), (64, 130)),
+    (12, 4, 128, 32, (5, 6), (20, 77)),
+    (8, 8, 64, 16, (33,), (0,)),
+]
+
+
+def _run_case(torch, c, num_splits, max_q_len=0):
+    from paged_kv_decode_04_amd import pkv
+    kp, vp = _dev(torch, c.k_pool), _dev(torch, c.v_pool)
+    pkv.paged_kv_append(_dev(torch, c.k_new), _dev(torch, c.v_new), _dev(torch, c.slot_mapping), kp, vp)
+    out = pkv.paged_varlen_attention(_dev(torch, c.q), kp, vp, _dev(torch, c.block_tables),
+                                     _dev(torch, c.cu_seqlens_q), _dev(torch, c.pos_offsets), c.scale,
+                                     num_splits=num_splits, max_q_len=max_q_len)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _reference(c):
+    kp, vp = c.k_pool.copy(), c.v_pool.copy()
+    oracle.paged_kv_append(c.k_new, c.v_new, c.slot_mapping, kp, vp)
+    return oracle.varlen_attention(c.q, kp, vp, c.block_tables, c.cu_seqlens_q, c.pos_offsets, c.scale)
+
+
+@pytest.mark.parametrize("geom", VARLEN_GEOMS, ids=lambda g: "Hq%d_Hkv%d_D%d_BS%d_T%d" % (g[:4] + (sum(g[4]),)))
+@pytest.mark.parametrize("num_splits", [1, 3, 0])
+def test_varlen_matches_oracle(torch_cuda, geom, num_splits):
+    Hq, Hkv, D, BS, ql, po = geom
+    c = W.build_varlen_case("varlen", len(ql), Hq, Hkv, D, BS, ql, po, 900 + D + BS + Hq)
+    say("varlen %s S=%d" % (geom, num_splits))
+    out = _run_case(torch_cuda, c, num_splits)
+    assert_close(out, _reference(c), "varlen %s S=%d" % (geom, num_splits))
+
+
+def test_varlen_small_grid_estimate_still_covers_every_row(torch_cuda):
+    # max_q_len = 1 sizes the grid for one tile per sequence; the workgroups loop over the remaining tiles
+    c = W.build_varlen_case("varlen", 3, 8, 2, 128, 16, (9, 1, 14), (5, 200, 31), 951)
+    ref = _reference(c)
+    for S in (1, 2):
+        out = _run_case(torch_cuda, c, S, max_q_len=1)
+        assert_close(out, ref, "varlen max_q_len=1 S=%d" % S)
+
+
+def test_varlen_one_new_row_is_decode_attention(torch_cuda):
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    lens = (300, 17, 1, 129)
+    c = W.build_varlen_case("varlen", 4, 32, 8, 128, 16, (1, 1, 1, 1), tuple(L - 1 for L in lens), 952,
+                            poison_new=False)
+    out = _run_case(torch, c, 1)
+    dec = pkv.paged_decode_attention(_dev(torch, c.q), _dev(torch, c.k_pool), _dev(torch, c.v_pool),
+                                     _dev(torch, c.block_tables), _dev(torch, np.array(lens, np.int32)), c.scale,
+                                     num_splits=1)
+    torch.cuda.synchronize()
+    dec = dec.cpu().numpy()
+    assert_close(out, dec.astype(np.float64), "varlen q_len=1 vs decode")
+    say("varlen q_len=1 bit-identical to decode: %s" % np.array_equal(out.view(np.uint16), dec.view(np.uint16)))
+
+
+def test_varlen_empty_batch_is_a_no_op(torch_cuda):
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    c = W.build_varlen_case("varlen", 2, 8, 2, 64, 16, (0, 0), (3, 9), 953)
+    q = torch.zeros((0, 8, 64), dtype=torch.float16, device="cuda")
+    out = pkv.paged_varlen_attention(q, _dev(torch, c.k_pool), _dev(torch, c.v_pool), _dev(torch, c.block_tables),
+                                     _dev(torch, c.cu_seqlens_q), _dev(torch, c.pos_offsets), c.scale)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 8, 64)
