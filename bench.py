@@ -13,9 +13,9 @@ Infinity Cache cannot hold a step's working set (R=4 for c2).
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value        algorithmic HBM bytes of a step / measured step time, in GB/s (whole job, one GPU)
-  roofline     the dominant kernel: algorithmic bytes / its average duration from HIP events on its stream in the
-               timed region (a fused single-pass step is one launch: region time / K; otherwise an event pair
-               around each attention call), against the 8 TB/s HBM peak; `traffic` is the measured HBM bytes per launch from the committed
+  roofline     the dominant kernel: algorithmic bytes / its average duration from HIP events on its stream (a fused
+               single-pass step is one launch: step region / K; otherwise a second region of K back-to-back
+               attention calls), against the 8 TB/s HBM peak; `traffic` is the measured HBM bytes per launch from the committed
                rocprofv3 counter summary when it was taken on the current kernel source, else null
   cpu_baseline the CPU oracle (f64, threads = the host cores it used) on a bounded sample of the same workload
 """
@@ -44,6 +44,8 @@ WORKLOADS = {
     "c4": ("mixed serving (70B-layer-shaped, one GPU's share): B=256, Hq=64, Hkv=8, D=128, BS=16, "
            "L=lognormal(median 1024, sigma 1) clipped to [1,16384], auto dispatch", 0, 1),
     "c5": ("MHA wide head: B=128, Hq=Hkv=16, D=256, BS=32, L=4096, K/V~U(-1,1), scale 1/16", 0, 1),
+    "v1": ("speculative verification, varlen (Llama-3-8B-shaped batch): B=32, Hq=32, Hkv=8, D=128, BS=16, 4 new rows "
+           "per sequence, final L~U[512,2048]", 0, 4),
 }
 
 
@@ -131,18 +133,24 @@ def cpu_baseline(case, seconds: float):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     from paged_kv_decode_04_amd import workloads as W
-    nbytes = W.algorithmic_bytes(case)["attention"]
+    varlen = isinstance(case, W.VarlenCase)
+    nbytes = (W.algorithmic_bytes_varlen(case) if varlen else W.algorithmic_bytes(case))["attention"]
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.decode_attention(case.q, case.k_pool, case.v_pool, case.block_tables, case.context_lens, case.scale,
-                                threads=threads)
+        if varlen:
+            oracle.varlen_attention(case.q, case.k_pool, case.v_pool, case.block_tables, case.cu_seqlens_q,
+                                    case.pos_offsets, case.scale, threads=threads)
+        else:
+            oracle.decode_attention(case.q, case.k_pool, case.v_pool, case.block_tables, case.context_lens,
+                                    case.scale, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
     return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d full decode-attention call(s) of the workload (all %d sequences x %d heads, f64) in %.1f s; "
-                      "%.3f calls/s" % (reps, case.B, case.Hq, el, reps / el)}
+            "sample": "%d full %s call(s) of the workload (all %d sequences x %d heads, f64) in %.1f s; "
+                      "%.3f calls/s" % (reps, "varlen-attention" if varlen else "decode-attention", case.B, case.Hq,
+                                        el, reps / el)}
 
 
 def main(argv=None) -> int:
@@ -166,7 +174,7 @@ def main(argv=None) -> int:
         splits = WORKLOADS[args.config][1] if args.splits is None else args.splits
         rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config, splits,
                             args.copy_calibration_mib or 512.0)
-        extra = " --unfused" if args.unfused else ""
+        extra = " --unfused" if args.unfused and not args.config.startswith("v") else ""
         rec["commands"] = [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o %s -- python3 bench.py --config %s "
             "--steps 50 --warmup 10 --no-cpu-baseline --copy-calibration-mib %g%s"
@@ -177,7 +185,7 @@ def main(argv=None) -> int:
             "python bench.py --summarize-pmc gpurun_out/pmc_fetch/%s_counter_collection.csv "
             "gpurun_out/pmc_write/%s_counter_collection.csv --config %s%s" % (args.config, args.config, args.config, extra),
         ]
-        path = traffic_path(args.config, splits, not args.unfused)
+        path = traffic_path(args.config, splits, not args.unfused and not args.config.startswith("v"))
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
@@ -201,24 +209,30 @@ def main(argv=None) -> int:
     desc, default_splits, default_rot = WORKLOADS[args.config]
     splits = default_splits if args.splits is None else args.splits
     R = default_rot if args.rotations is None else args.rotations
-    make = W.CONFIGS[args.config]
+    varlen = args.config in W.VARLEN_CONFIGS
+    make = W.VARLEN_CONFIGS[args.config] if varlen else W.CONFIGS[args.config]
 
     log("building %d rotation set(s) of %s" % (R, args.config))
     sets = []
     host0 = None
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     for r in range(R):
         c = make(rotation=r)
-        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-        d = dict(q=t(c.q), k_pool=t(c.k_pool), v_pool=t(c.v_pool), bt=t(c.block_tables), cl=t(c.context_lens),
-                 k_new=t(c.k_new), v_new=t(c.v_new), slots=t(c.slot_mapping), case=c)
-        # one new row per sequence for the fused step (rows of empty sequences are never written)
-        kn = np.zeros((c.B, c.Hkv, c.D), np.float16)
-        vn = np.zeros_like(kn)
-        nz = np.nonzero(c.context_lens > 0)[0]
-        kn[nz], vn[nz] = c.k_new, c.v_new
-        d["k_new_all"], d["v_new_all"] = t(kn), t(vn)
+        d = dict(q=t(c.q), k_pool=t(c.k_pool), v_pool=t(c.v_pool), bt=t(c.block_tables), k_new=t(c.k_new),
+                 v_new=t(c.v_new), slots=t(c.slot_mapping), case=c)
+        if varlen:
+            d["cu"], d["pos"] = t(c.cu_seqlens_q), t(c.pos_offsets)
+            d["bytes"] = W.algorithmic_bytes_varlen(c)
+        else:
+            d["cl"] = t(c.context_lens)
+            # one new row per sequence for the fused step (rows of empty sequences are never written)
+            kn = np.zeros((c.B, c.Hkv, c.D), np.float16)
+            vn = np.zeros_like(kn)
+            nz = np.nonzero(c.context_lens > 0)[0]
+            kn[nz], vn[nz] = c.k_new, c.v_new
+            d["k_new_all"], d["v_new_all"] = t(kn), t(vn)
+            d["bytes"] = W.algorithmic_bytes(c)
         d["out"] = torch.empty_like(d["q"])
-        d["bytes"] = W.algorithmic_bytes(c)
         if r == 0:
             host0 = c
         else:
@@ -226,29 +240,33 @@ def main(argv=None) -> int:
         sets.append(d)
     torch.cuda.synchronize()
     c0 = sets[0]["case"]
-    plan = pkv.plan_decode(c0.B, c0.Hq, c0.Hkv, c0.D, c0.BS, c0.M, num_splits=splits)
+    if varlen:
+        plan = {"num_splits": splits, "note": "varlen: 0 = the library chooses from the grid size"}
+    else:
+        plan = pkv.plan_decode(c0.B, c0.Hq, c0.Hkv, c0.D, c0.BS, c0.M, num_splits=splits)
     log("plan: %s, %s" % (plan, pkv.version()))
 
-    fused = not args.unfused
+    fused = not args.unfused and not varlen  # the varlen step is the append, then varlen attention
     # arguments marshalled once per rotation set (the binding's prepared calls): per-step Python marshalling would
     # otherwise outlast the kernel and leave the GPU idle between steps
     for d in sets:
         if fused:
             d["call"] = pkv.prepare_decode_step(d["q"], d["k_new_all"], d["v_new_all"], d["k_pool"], d["v_pool"],
                                                 d["bt"], d["cl"], d["case"].scale, d["out"], num_splits=splits)
+        elif varlen:
+            d["append"] = pkv.prepare_paged_kv_append(d["k_new"], d["v_new"], d["slots"], d["k_pool"], d["v_pool"])
+            d["call"] = pkv.prepare_paged_varlen_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cu"],
+                                                           d["pos"], d["case"].scale, d["out"], num_splits=splits,
+                                                           max_q_len=int(d["case"].q_lens.max()))
         else:
             d["append"] = pkv.prepare_paged_kv_append(d["k_new"], d["v_new"], d["slots"], d["k_pool"], d["v_pool"])
             d["call"] = pkv.prepare_paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
                                                            d["case"].scale, d["out"], num_splits=splits)
 
-    def step(d, ev=None):
+    def step(d):
         if not fused:
             d["append"]()
-        if ev is not None:
-            ev[0].record()
         d["call"]()
-        if ev is not None:
-            ev[1].record()
 
     if args.copy_calibration_mib > 0:
         n = int(args.copy_calibration_mib * (1 << 20)) // 2
@@ -265,22 +283,24 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     K = args.steps
-    # When a step is one launch (the fused single-pass step), the kernel's average duration is the timed region / K
-    # and no per-launch events are recorded (an event pair costs ~7 us of stream time per step here, more than the
-    # launch gaps it would exclude); otherwise an event pair brackets the attention call of every step.
+
+    def timed(fn):
+        """Milliseconds per iteration of K back-to-back calls of fn(i), between two events on the current stream."""
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(K):
+            fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K
+
+    # No event inside a timed region: an event pair costs ~7 us of stream time here, more than a kernel's launch gap.
+    # The step region gives value; when a step is one launch (the fused single-pass step) that launch's average
+    # duration is the same region / K, otherwise a second region of K back-to-back attention calls gives it.
+    ms_per_step = timed(lambda i: step(sets[i % R]))
     one_launch = fused and plan["num_splits"] == 1
-    evs = None if one_launch else [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                                   for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(K):
-        step(sets[i % R], None if evs is None else evs[i])
-    end.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
-    attn_ms = np.array([ms_per_step] if evs is None else [a.elapsed_time(b) for a, b in evs])
+    attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["call"]())])
 
     # bytes per step, averaged over the rotation sets
     step_bytes = np.mean([d["bytes"]["attention"] + d["bytes"]["append"] for d in sets])
@@ -290,9 +310,8 @@ def main(argv=None) -> int:
     attn_avg_ms = float(attn_ms.mean())
     achieved = kernel_bytes / (attn_avg_ms * 1e-3) / 1e9
     calls_per_s = 1e3 / attn_avg_ms
-    log("step %.4f ms (%.1f GB/s); %s avg %.4f ms median %.4f p90 %.4f -> %.1f GB/s, %.0f calls/s"
-        % (ms_per_step, value, "fused step kernel" if fused else "attention", attn_avg_ms, float(np.median(attn_ms)), float(np.percentile(attn_ms, 90)),
-           achieved, calls_per_s))
+    log("step %.4f ms (%.1f GB/s); %s avg %.4f ms -> %.1f GB/s, %.0f calls/s"
+        % (ms_per_step, value, "fused step kernel" if fused else "attention call", attn_avg_ms, achieved, calls_per_s))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -317,15 +336,17 @@ def main(argv=None) -> int:
             "workload": "%s: %s" % (args.config, desc),
             "num_seqs": c0.B, "num_q_heads": c0.Hq, "num_kv_heads": c0.Hkv, "head_dim": c0.D,
             "block_size": c0.BS, "num_splits": splits, "plan": plan, "rotations": R,
-            "step": "fused (pkv_paged_decode_step)" if fused else "pkv_paged_kv_append + pkv_paged_decode_attention",
+            "step": ("fused (pkv_paged_decode_step)" if fused else
+                     "pkv_paged_kv_append + pkv_paged_varlen_attention" if varlen else
+                     "pkv_paged_kv_append + pkv_paged_decode_attention"),
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100.0 * float(value) / PEAK_GBS, 2),
         "calls_per_s": round(calls_per_s, 1),
-        "tokens_per_s": round(calls_per_s * c0.B, 1),
-        "kernel_ms": {"mean": round(attn_avg_ms, 5), "median": round(float(np.median(attn_ms)), 5),
-                      "p90": round(float(np.percentile(attn_ms, 90)), 5),
-                      "timing": "region / steps (one launch per step)" if evs is None else "event pair per launch"},
+        "tokens_per_s": round(calls_per_s * (c0.T if varlen else c0.B), 1),
+        "kernel_ms": {"mean": round(attn_avg_ms, 5),
+                      "timing": ("step region / steps (one launch per step)" if one_launch else
+                                 "region of back-to-back attention calls / calls")},
         "bytes_per_step": {"attention": int(attn_bytes), "append": int(np.mean([d["bytes"]["append"] for d in sets]))},
         "roofline": {
             "bound": "hbm",

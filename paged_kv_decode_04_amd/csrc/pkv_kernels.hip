@@ -409,6 +409,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 
     l_run = rows_sum(l_run);
 
+    // Cross-wave merge.  Each lane first forms its column's merged max M and denominator from every wave's (m, l),
+    // then scales its own registers by a = 2^(m - M) (and by 1 / denominator for a single pass), so the final pass
+    // is a plain sum over the waves per output element.
     float *sm_m = smem;
     float *sm_l = smem + NW * 16;
     float *sm_o = smem + 2 * NW * 16;
@@ -416,13 +419,31 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         sm_m[wave * 16 + r] = m_run;
         sm_l[wave * 16 + r] = l_run;
     }
-    if (r < p.G) {
-        float *dst = sm_o + (wave * p.G + r) * DP + 4 * g4;
+    __syncthreads();
+    float Mc = kNegBig;
 #pragma unroll
-        for (int c = 0; c < VC; ++c) {
+    for (int w = 0; w < NW; ++w)
+        Mc = fmaxf(Mc, sm_m[w * 16 + r]);
+    float den = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                dst[16 * c + e] = o[c][e];
+    for (int w = 0; w < NW; ++w)
+        den += exp2_fast(sm_m[w * 16 + r] - Mc) * sm_l[w * 16 + r];
+    {
+        const float a = exp2_fast(m_run - Mc);
+        const float f = SPLIT ? a : (den > 0.f ? a / den : 0.f);
+        if (r < p.G) {
+            float *dst = sm_o + (wave * p.G + r) * DP + 4 * g4;
+#pragma unroll
+            for (int c = 0; c < VC; ++c) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[16 * c + e] = o[c][e] * f;
+            }
+        }
+        if (SPLIT && wave == 0 && g4 == 0 && r < p.G) {
+            const int64_t base = ((int64_t)s * p.Hq + hk * p.G + r) * p.num_splits + split;
+            p.part_m[base] = Mc * kLn2;
+            p.part_l[base] = den;
         }
     }
     __syncthreads();
@@ -431,28 +452,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     for (int idx = threadIdx.x; idx < total; idx += NW * 64) {
         const int h = idx / D;
         const int d = idx - h * D;
-        float M = kNegBig;
+        float num = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w)
-            M = fmaxf(M, sm_m[w * 16 + h]);
-        float den = 0.f, num = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float a = exp2_fast(sm_m[w * 16 + h] - M);
-            den += a * sm_l[w * 16 + h];
-            num += a * sm_o[(w * p.G + h) * DP + d];
-        }
+            num += sm_o[(w * p.G + h) * DP + d];
         const int64_t row = (int64_t)s * p.Hq + hk * p.G + h;
-        if (!SPLIT) {
-            p.out[row * D + d] = (_Float16)(den > 0.f ? num / den : 0.f);
-        } else {
-            const int64_t base = row * p.num_splits + split;
-            p.part_o[base * D + d] = num;
-            if (d == 0) {
-                p.part_m[base] = M * kLn2;
-                p.part_l[base] = den;
-            }
-        }
+        if (!SPLIT)
+            p.out[row * D + d] = (_Float16)num;
+        else
+            p.part_o[(row * p.num_splits + split) * D + d] = num;
     }
 }
 
@@ -490,9 +498,22 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
     const int32_t *bt = p.block_tables + (int64_t)s * p.M;
     const int max_units = p.M * SPB;
     const int cap = p.M * BS;  // rows the table can name
+    // Every tile's key range starts at row 0 (in split mode with fixed chunks, at split * chunk_blocks), so the
+    // block ids of this wave's first units are requested together with the prefix sums and the position.
+    const bool start_known = !SPLIT || p.chunk_blocks > 0;
+    const int u_known = (SPLIT ? split * p.chunk_blocks : 0) * SPB + wave;
+    constexpr int NSPEC = 2 * NS - 1;
+    int spec_raw[NSPEC];
+#pragma unroll
+    for (int j = 0; j < NSPEC; ++j)
+        spec_raw[j] = start_known ? uniform_load(bt, min(u_known + j * NW, max_units - 1) / SPB) : -1;
     int q0 = uniform_load(p.cu_seqlens_q, s);
     int q1 = uniform_load(p.cu_seqlens_q, s + 1);
     int pos = uniform_load(p.pos_offsets, s);
+    static_assert(NSPEC <= 3, "the barrier below names at most three block ids");
+    asm volatile("" ::"s"(q0), "s"(q1), "s"(pos), "s"(spec_raw[0]), "s"(spec_raw[NSPEC > 1 ? 1 : 0]),
+                 "s"(spec_raw[NSPEC > 2 ? 2 : 0])
+                 : "memory");
     q0 = q0 < 0 ? 0 : (q0 > p.T ? p.T : q0);
     q1 = q1 < q0 ? q0 : (q1 > p.T ? p.T : q1);
     pos = pos < 0 ? 0 : (pos > cap ? cap : pos);
@@ -567,13 +588,14 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
 #pragma unroll
             for (int j = 0; j < NS - 1; ++j) {
                 uu[j] = u_first + j * NW;
-                const int blk = resolve(raw_block(uu[j]), dead[j]);
+                const int blk = resolve(start_known ? spec_raw[j] : raw_block(uu[j]), dead[j]);
                 load_unit<D, BS>(f[j], k_ptr(blk, uu[j]), v_ptr(blk, uu[j]), k_lane, v_lane,
                                  j < n_units && !dead[j]);
             }
 #pragma unroll
             for (int j = 0; j < NS; ++j)
-                raw_q[j] = raw_block(u_first + min(NS - 1 + j, n_units - 1) * NW);
+                raw_q[j] = start_known ? spec_raw[NS - 1 + j]
+                                       : raw_block(u_first + min(NS - 1 + j, n_units - 1) * NW);
             int k = 0;
             for (;;) {
 #pragma unroll
@@ -596,46 +618,52 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
         l_run = rows_sum(l_run);
         if (tile != slot)
             __syncthreads();  // the previous tile's merge has read the LDS
+        // cross-wave merge, as in decode_kernel
         if (g4 == 0) {
             sm_m[wave * 16 + r] = m_run;
             sm_l[wave * 16 + r] = l_run;
         }
-        if (col_ok) {
-            float *dst = sm_o + (wave * 16 + r) * DP + 4 * g4;
+        __syncthreads();
+        float Mc = kNegBig;
 #pragma unroll
-            for (int c = 0; c < VC; ++c) {
+        for (int w = 0; w < NW; ++w)
+            Mc = fmaxf(Mc, sm_m[w * 16 + r]);
+        float den = 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dst[16 * c + e] = o[c][e];
+        for (int w = 0; w < NW; ++w)
+            den += exp2_fast(sm_m[w * 16 + r] - Mc) * sm_l[w * 16 + r];
+        const int64_t my_row = (int64_t)(q0 + i0 + crow) * p.Hq + hk * p.G + r % p.G;  // token * Hq + hq
+        {
+            const float a = exp2_fast(m_run - Mc);
+            const float f = SPLIT ? a : (den > 0.f ? a / den : 0.f);
+            if (col_ok) {
+                float *dst = sm_o + (wave * 16 + r) * DP + 4 * g4;
+#pragma unroll
+                for (int c = 0; c < VC; ++c) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dst[16 * c + e] = o[c][e] * f;
+                }
+            }
+            if (SPLIT && wave == 0 && g4 == 0 && col_ok) {
+                // a split without rows (b0 >= b1) leaves M = -1e30 and l = 0: weight 0 in the combine
+                p.part_m[my_row * p.num_splits + split] = Mc * kLn2;
+                p.part_l[my_row * p.num_splits + split] = den;
             }
         }
         __syncthreads();
         for (int idx = threadIdx.x; idx < ncols * D; idx += NW * 64) {
             const int c = idx / D;
             const int d = idx - c * D;
-            float M = kNegBig;
+            float num = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w)
-                M = fmaxf(M, sm_m[w * 16 + c]);
-            float den = 0.f, num = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float a = exp2_fast(sm_m[w * 16 + c] - M);
-                den += a * sm_l[w * 16 + c];
-                num += a * sm_o[(w * 16 + c) * DP + d];
-            }
+                num += sm_o[(w * 16 + c) * DP + d];
             const int64_t row = (int64_t)(q0 + i0 + c / p.G) * p.Hq + hk * p.G + c % p.G;  // token * Hq + hq
-            if (!SPLIT) {
-                p.out[row * D + d] = (_Float16)(den > 0.f ? num / den : 0.f);
-            } else {
-                const int64_t base = row * p.num_splits + split;
-                const bool empty = b0 >= b1;
-                p.part_o[base * D + d] = empty ? 0.f : num;
-                if (d == 0) {
-                    p.part_m[base] = empty ? kNegBig : M * kLn2;
-                    p.part_l[base] = empty ? 0.f : den;
-                }
-            }
+            if (!SPLIT)
+                p.out[row * D + d] = (_Float16)num;
+            else
+                p.part_o[(row * p.num_splits + split) * D + d] = num;
         }
     }
 }

@@ -401,6 +401,26 @@ def prepare_paged_decode_attention_planned(q, k_pool, v_pool, block_tables, cont
                         (q, k_pool, v_pool, block_tables, context_lens, out, workspace, pl))
 
 
+def prepare_paged_varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, scale: float, out,
+                                   num_splits: int = 0, max_q_len: int = 0, max_context_hint: int = 0,
+                                   stream=None) -> PreparedCall:
+    """pkv_paged_varlen_attention with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(q, torch.float16, "q", 3)
+    _dev(out, torch.float16, "out", 3)
+    B = int(pos_offsets.shape[0])
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(q)), ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool,
+            ctypes.c_void_p(_ptr(block_tables)), ctypes.c_int32(int(block_tables.shape[1])),
+            ctypes.c_void_p(_ptr(cu_seqlens_q)), ctypes.c_void_p(_ptr(pos_offsets)), ctypes.c_int32(B),
+            ctypes.c_int32(int(q.shape[0])), ctypes.c_int32(int(q.shape[1])), ctypes.c_float(scale),
+            ctypes.c_void_p(_ptr(out)), ctypes.c_int32(num_splits), ctypes.c_int32(max_q_len),
+            ctypes.c_int32(max_context_hint), ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_paged_varlen_attention, args,
+                        (q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, out))
+
+
 def prepare_paged_kv_append(k, v, slot_mapping, k_pool, v_pool, stream=None) -> PreparedCall:
     """pkv_paged_kv_append with its arguments marshalled once (see PreparedCall)."""
     import torch

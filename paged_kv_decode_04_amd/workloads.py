@@ -384,3 +384,34 @@ def build_varlen_case(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int, q_l
         scale = 1.0 / math.sqrt(D)
     return VarlenCase(name, B, Hq, Hkv, D, BS, N, M, float(scale), ql, po, cu, bt, q, k_pool, v_pool, k_new, v_new,
                       slots)
+
+
+SEEDS["v1"] = 0xC0FFEE11
+
+
+def config_v1(rotation: int = 0) -> VarlenCase:
+    """Speculative verification on the Llama-3-8B-shaped batch: B=32, 32/8 heads, D=128, BS=16, 4 new rows per
+    sequence whose final lengths are U{512..2048} (positions L-4 .. L-1), pool = blocks + 10%.  The new rows are
+    poisoned in the pools until the step's append writes them."""
+    seed = SEEDS["v1"]
+    final = _rng(seed, rotation, "lens").integers(512, 2048, size=32, endpoint=True).astype(np.int32)
+    ql = np.full(32, 4, dtype=np.int32)
+    nblocks = int(sum((int(L) + 15) // 16 for L in final))
+    return build_varlen_case("v1", 32, 32, 8, 128, 16, ql, final - ql, seed, rotation,
+                             extra_blocks=int(math.ceil(0.10 * nblocks)), M=128)
+
+
+VARLEN_CONFIGS = {"v1": config_v1}
+
+
+def algorithmic_bytes_varlen(case: VarlenCase) -> dict:
+    """Bytes a varlen step must move at minimum: each sequence's K and V rows up to its final length read once
+    (every tile of new rows shares them), q and out, tables, prefix sums and positions; the append reads and writes
+    2*T*Hkv*D fp16 values."""
+    final = case.final_lens
+    kv = int(final.sum()) * case.Hkv * case.D * 2 * 2
+    qo = 2 * case.T * case.Hq * case.D * 2
+    nb = int(sum((int(L) + case.BS - 1) // case.BS for L in final))
+    idx = nb * 4 + (2 * case.B + 1) * 4
+    app = 2 * 2 * case.T * case.Hkv * case.D * 2 + case.T * 4
+    return {"kv": kv, "q_out": qo, "index": idx, "attention": kv + qo + idx, "append": app}
