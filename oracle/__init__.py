@@ -71,6 +71,8 @@ def _load():
         lib.oracle_varlen_attention.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f64,
                                                 P, i64, P, i32]
         lib.oracle_varlen_attention.restype = ctypes.c_int
+        lib.oracle_decode_attention_window.argtypes = geom + [i32, P, i64, P, i32]
+        lib.oracle_decode_attention_window.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -126,11 +128,12 @@ def _geometry(q, k_pool, v_pool, block_tables, context_lens):
     return B, Hq, Hkv, D, BS, N, bt.shape[1], bt, cl
 
 
-def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale, units=None, threads=None):
+def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale, units=None, threads=None, window=0):
     """out[B][Hq][D] (or out[len(units)][D] for a list of (s, hq) units) in float64.
 
     q: [B][Hq][D] fp16; k_pool: [N][Hkv][BS/16][D/8][16][8] fp16; v_pool: [N][Hkv][BS/16][D][16] fp16;
     block_tables: [B][M] int32; context_lens: [B] int32 (rows including the newest token).
+    window > 0: each new row attends only its sequence's last `window` rows (sliding-window decode).
     """
     B, Hq, Hkv, D, BS, N, M, bt, cl = _geometry(q, k_pool, v_pool, block_tables, context_lens)
     qb, kb, vb = _bits(q), _bits(k_pool), _bits(v_pool)
@@ -138,13 +141,18 @@ def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale, units
         threads = os.cpu_count() or 1
     if units is None:
         out = np.empty((B, Hq, D), dtype=np.float64)
-        rc = _load().oracle_decode_attention(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(bt), _ptr(cl), B, Hq, Hkv, D, BS,
-                                             N, M, float(scale), None, 0, _ptr(out), int(threads))
+        up, n = None, 0
     else:
         u = _i32(units).reshape(-1, 2)
         out = np.empty((u.shape[0], D), dtype=np.float64)
+        up, n = _ptr(u), u.shape[0]
+    if window:
+        rc = _load().oracle_decode_attention_window(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(bt), _ptr(cl), B, Hq, Hkv, D,
+                                                    BS, N, M, float(scale), int(window), up, n, _ptr(out),
+                                                    int(threads))
+    else:
         rc = _load().oracle_decode_attention(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(bt), _ptr(cl), B, Hq, Hkv, D, BS,
-                                             N, M, float(scale), _ptr(u), u.shape[0], _ptr(out), int(threads))
+                                             N, M, float(scale), up, n, _ptr(out), int(threads))
     if rc != 0:
         raise ValueError("oracle_decode_attention failed (%d): bad geometry or a table entry outside the pool" % rc)
     return out

@@ -96,6 +96,7 @@ typedef struct {
     const int32_t *context_lens;  /* [B] */
     int32_t B, Hq, Hkv, D, BS, N, M;
     double scale;
+    int32_t window;               /* sliding window: > 0 attends only the last `window` rows; 0 = all rows */
 } oracle_problem;
 
 /* k_pool element (block b, kv head h, row offset o, dim d): panel o / 16, piece d / 8, row o % 16, lane d % 8 */
@@ -166,38 +167,43 @@ static int scores(const oracle_problem *P, int s, int hq, int t0, int t1, double
     return scores_for(P, s, P->q + ((int64_t)s * P->Hq + hq) * P->D, hq / G, t0, t1, z);
 }
 
-/* softmax(z) . V over rows 0..L-1 of sequence s, kv head hk, for one query
- * vector q: out[0..D); weights[0..L) (optional) receives the normalised
- * softmax weights.  L <= 0 gives out = 0. */
-static int attend(const oracle_problem *P, int s, const uint16_t *q, int hk, int L, double *out, double *weights)
+/* softmax(z) . V over rows lo..L-1 of sequence s, kv head hk, for one query
+ * vector q: out[0..D); weights[0..L-lo) (optional) receives the normalised
+ * softmax weights.  An empty range gives out = 0. */
+static int attend_range(const oracle_problem *P, int s, const uint16_t *q, int hk, int lo, int L, double *out,
+                        double *weights)
 {
     for (int d = 0; d < P->D; ++d)
         out[d] = 0.0;
-    if (L <= 0)
+    if (lo < 0)
+        lo = 0;
+    if (L <= lo)
         return 0;
-    double *z = (double *)malloc(sizeof(double) * (size_t)L);
+    int n = L - lo;
+    double *z = (double *)malloc(sizeof(double) * (size_t)n);
     if (!z)
         return -3;
-    int rc = scores_for(P, s, q, hk, 0, L, z);
+    int rc = scores_for(P, s, q, hk, lo, L, z);
     if (rc) {
         free(z);
         return rc;
     }
     double m = -INFINITY;
-    for (int t = 0; t < L; ++t)
-        if (z[t] > m)
-            m = z[t];
+    for (int i = 0; i < n; ++i)
+        if (z[i] > m)
+            m = z[i];
     double l = 0.0;
-    for (int t = 0; t < L; ++t)
-        l += exp(z[t] - m);
-    for (int t = 0; t < L; ++t) {
-        double w = exp(z[t] - m);
+    for (int i = 0; i < n; ++i)
+        l += exp(z[i] - m);
+    for (int i = 0; i < n; ++i) {
+        double w = exp(z[i] - m);
+        int t = lo + i;
         int64_t p = row_block(P, s, t);
         int o = t % P->BS;
         for (int d = 0; d < P->D; ++d)
             out[d] += w * oracle_f16_to_f64(P->v_pool[v_index(P, p, hk, o, d)]);
         if (weights)
-            weights[t] = w / l;
+            weights[i] = w / l;
     }
     for (int d = 0; d < P->D; ++d)
         out[d] /= l;
@@ -205,11 +211,22 @@ static int attend(const oracle_problem *P, int s, const uint16_t *q, int hk, int
     return 0;
 }
 
-/* One decode output row: (s, hq) over the context_lens[s] rows of sequence s. */
+/* softmax(z) . V over rows 0..L-1 (see attend_range). */
+static int attend(const oracle_problem *P, int s, const uint16_t *q, int hk, int L, double *out, double *weights)
+{
+    return attend_range(P, s, q, hk, 0, L, out, weights);
+}
+
+/* One decode output row: (s, hq) over the context_lens[s] rows of sequence s,
+ * or with a sliding window W > 0 over its last W rows only: rows
+ * max(0, L - W) .. L - 1 [cortiq-engine 0.8.80, src/gpu_cuda.rs: the decode
+ * attend, first = stored - window (saturating), the KvMirror window]. */
 static int attention_unit(const oracle_problem *P, int s, int hq, double *out, double *weights)
 {
     int G = P->Hq / P->Hkv;
-    return attend(P, s, P->q + ((int64_t)s * P->Hq + hq) * P->D, hq / G, P->context_lens[s], out, weights);
+    int L = P->context_lens[s];
+    int lo = (P->window > 0 && L > P->window) ? L - P->window : 0;
+    return attend_range(P, s, P->q + ((int64_t)s * P->Hq + hq) * P->D, hq / G, lo, L, out, weights);
 }
 
 /* ------------------------------------------------------------------ */
@@ -270,7 +287,7 @@ int oracle_decode_attention(const uint16_t *q, const uint16_t *k_pool, const uin
                             int32_t N, int32_t M, double scale,
                             const int32_t *units, int64_t n_units, double *out, int32_t n_threads)
 {
-    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale};
+    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale, 0};
     if (check_geometry(&P))
         return -1;
     if (!units)
@@ -304,7 +321,7 @@ int oracle_attention_weights(const uint16_t *q, const uint16_t *k_pool, const ui
                              int32_t N, int32_t M, double scale, int32_t s, int32_t hq,
                              double *out, double *weights)
 {
-    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale};
+    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale, 0};
     if (check_geometry(&P) || s < 0 || s >= B || hq < 0 || hq >= Hq)
         return -1;
     return attention_unit(&P, s, hq, out, weights);
@@ -351,7 +368,7 @@ int oracle_split_partials(const uint16_t *q, const uint16_t *k_pool, const uint1
                           int32_t N, int32_t M, double scale, int32_t S, int32_t chunk_blocks,
                           double *O, double *m_out, double *l_out)
 {
-    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale};
+    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale, 0};
     if (check_geometry(&P) || S < 1 || chunk_blocks < 0)
         return -1;
     int G = Hq / Hkv;
@@ -552,7 +569,7 @@ int oracle_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const uin
                             int32_t N, int32_t M, double scale,
                             const int32_t *units, int64_t n_units, double *out, int32_t n_threads)
 {
-    oracle_problem P = {q, k_pool, v_pool, block_tables, NULL, B, Hq, Hkv, D, BS, N, M, scale};
+    oracle_problem P = {q, k_pool, v_pool, block_tables, NULL, B, Hq, Hkv, D, BS, N, M, scale, 0};
     if (check_geometry(&P) || T < 0)
         return -1;
     if (B > 0 && (cu_seqlens_q[0] != 0 || cu_seqlens_q[B] != T))
@@ -583,6 +600,47 @@ int oracle_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const uin
             ++started;
     if (started == 0)
         varlen_worker(&W);
+    for (int i = 0; i < started; ++i)
+        pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&W.lock);
+    return W.rc;
+}
+
+
+/* ------------------------------------------------------------------ */
+/* Sliding-window decode attention.                                     */
+/* ------------------------------------------------------------------ */
+
+/* Decode attention where sequence s's new row attends only its last `window`
+ * rows (window > 0), rows max(0, L - window) .. L - 1; window = 0 is plain
+ * decode attention.  Same arguments and output as oracle_decode_attention. */
+int oracle_decode_attention_window(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                   const int32_t *block_tables, const int32_t *context_lens,
+                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                                   int32_t N, int32_t M, double scale, int32_t window,
+                                   const int32_t *units, int64_t n_units, double *out, int32_t n_threads)
+{
+    oracle_problem P = {q, k_pool, v_pool, block_tables, context_lens, B, Hq, Hkv, D, BS, N, M, scale, window};
+    if (check_geometry(&P) || window < 0)
+        return -1;
+    if (!units)
+        n_units = (int64_t)B * Hq;
+    for (int64_t u = 0; units && u < n_units; ++u)
+        if (units[2 * u] < 0 || units[2 * u] >= B || units[2 * u + 1] < 0 || units[2 * u + 1] >= Hq)
+            return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    unit_pool W;
+    W.P = &P; W.units = units; W.n_units = n_units; W.out = out; W.next = 0; W.rc = 0;
+    pthread_mutex_init(&W.lock, NULL);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    int started = 0;
+    for (int i = 0; i < n_threads; ++i)
+        if (pthread_create(&th[i], NULL, unit_worker, &W) == 0)
+            ++started;
+    if (started == 0)
+        unit_worker(&W);
     for (int i = 0; i < started; ++i)
         pthread_join(th[i], NULL);
     free(th);

@@ -522,3 +522,69 @@ def test_varlen_rejects_bad_prefix_sums_and_positions(cu, pos):
     c = W.build_varlen_case("v", 2, 4, 2, 64, 16, (1, 2), (3, 4), 44, poison_new=False, M=3)
     with pytest.raises(ValueError):
         oracle.varlen_attention(c.q, c.k_pool, c.v_pool, c.block_tables, cu, pos, c.scale)
+
+
+# --------------------------------------------------------------------------------------------------------------
+# sliding-window decode
+
+
+def _golden_window_cases():
+    with open(os.path.join(GOLDEN, "window_hand.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_window_cases(), ids=lambda c: c["name"])
+def test_golden_window(case):
+    k_pool, v_pool = _pools_from_rows(case)
+    q = _pad8(case["q"], case["D"]).astype(np.float16)
+    out = oracle.decode_attention(q, k_pool, v_pool, case["block_tables"], case["context_lens"], _num(case["scale"]),
+                                  threads=2, window=case["window"])
+    np.testing.assert_allclose(out, _pad8(case["expected"], case["D"]), rtol=1e-14, atol=1e-14)
+
+
+def test_window_at_least_the_context_is_plain_decode_and_one_row_returns_v():
+    c = _rand_case(61, lens=(37, 16, 5))
+    plain = _run(c)
+    assert np.array_equal(oracle.decode_attention(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
+                                                  threads=4, window=37), plain)
+    one = oracle.decode_attention(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale, threads=4,
+                                  window=1)
+    for s in range(c.B):
+        for hq in range(c.Hq):
+            _, v = _rows(c, s, hq // c.G)
+            assert np.array_equal(one[s, hq], v[-1])
+
+
+def test_window_matches_torch_sdpa_over_the_last_rows():
+    torch = pytest.importorskip("torch")
+    for W_, lens, G, BS in [(5, (37, 16, 5, 2), 4, 16), (40, (100, 41, 39), 2, 32), (17, (64,), 1, 64)]:
+        c = _rand_case(62 + W_, B=len(lens), Hq=4 * G, Hkv=4, BS=BS, lens=lens)
+        out = oracle.decode_attention(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale, threads=4,
+                                      window=W_)
+        for s in range(c.B):
+            for hk in range(c.Hkv):
+                ks, vs = _rows(c, s, hk)
+                lo = max(0, len(ks) - W_)
+                q = torch.from_numpy(c.q[s, hk * c.G:(hk + 1) * c.G].astype(np.float64))[:, None, :]
+                kk = torch.from_numpy(ks[lo:])[None].expand(c.G, -1, -1)
+                vv = torch.from_numpy(vs[lo:])[None].expand(c.G, -1, -1)
+                ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, scale=c.scale)[:, 0]
+                np.testing.assert_allclose(out[s, hk * c.G:(hk + 1) * c.G], ref.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_window_ignores_rows_before_it():
+    c = _rand_case(63, lens=(70, 33, 20))
+    W_ = 20
+    out = oracle.decode_attention(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale, threads=4,
+                                  window=W_)
+    kp, vp = c.k_pool.copy(), c.v_pool.copy()
+    for s in range(c.B):
+        L = int(c.context_lens[s])
+        for t in range(0, max(0, L - W_)):
+            b = int(c.block_tables[s, t // c.BS])
+            W.set_k_row(kp, b, slice(None), t % c.BS, np.full((c.Hkv, c.D), 30.0))
+            W.set_v_row(vp, b, slice(None), t % c.BS, np.full((c.Hkv, c.D), -50.0))
+    out2 = oracle.decode_attention(c.q, kp, vp, c.block_tables, c.context_lens, c.scale, threads=4, window=W_)
+    assert np.array_equal(out, out2)
+    assert not np.array_equal(_run(c), oracle.decode_attention(c.q, kp, vp, c.block_tables, c.context_lens, c.scale,
+                                                               threads=4))
