@@ -205,6 +205,23 @@ int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool
                                        void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_paged_decode_attention_window -- sliding-window decode attention: as
+ *   pkv_paged_decode_attention, but with window > 0 the new row of sequence s
+ *   attends only rows max(0, L_s - window) .. L_s - 1; blocks wholly before
+ *   the window are never read, so their table entries may name anything.
+ *   window = 0 is pkv_paged_decode_attention.  Split ranges start at the
+ *   window's first block; the dispatcher plans for at most `window` rows.
+ *   [cortiq-engine 0.8.80, src/gpu_cuda.rs: the decode attend, first row =
+ *   stored - window (saturating), and the KvMirror window]
+ *   Errors: as pkv_paged_decode_attention; window < 0 is PKV_EINVAL.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_decode_attention_window(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                      pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                      float scale, uint16_t *out, int32_t num_splits, int32_t window,
+                                      int32_t max_context_hint, void *stream);
+
+/* ---------------------------------------------------------------------------
  * pkv_paged_varlen_attention -- attention for several new query rows per
  *   sequence (speculative verification, chunked prefill): sequence s owns the
  *   rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of q and out; its i-th new row

@@ -298,9 +298,10 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
              const pkv_pool_desc &pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
              void *workspace, size_t workspace_bytes, bool library_ws, hipStream_t stream,
-             const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr) {
+             const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr, int32_t window = 0) {
     pkv::DecodeParams p = decode_params(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
                                         num_q_heads, scale);
+    p.window = window;
     p.out = reinterpret_cast<_Float16 *>(out);
     if (k_new) {  // fused decode step: the pools are written too
         p.k_new = reinterpret_cast<const _Float16 *>(k_new);
@@ -350,6 +351,7 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
     c.M = max_blocks_per_seq;
     c.num_splits = plan.num_splits;
     c.chunk_blocks = plan.chunk_blocks;
+    c.window = window;
     e = pkv::launch_combine(c, pool.head_dim, stream);
     if (e != hipSuccess)
         return hip_fail(e, "split-K combine kernel launch");
@@ -361,10 +363,14 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
                 int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
                 int32_t max_context_hint, const pkv_decode_plan *given, void *workspace, size_t workspace_bytes,
                 bool library_ws, hipStream_t stream, const uint16_t *k_new = nullptr,
-                const uint16_t *v_new = nullptr) {
+                const uint16_t *v_new = nullptr, int32_t window = 0) {
     int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
     if (rc)
         return rc;
+    if (window < 0)
+        return fail(PKV_EINVAL, "window must be >= 0 (got %d)", window);
+    if (window > 0 && (max_context_hint == 0 || max_context_hint > window))
+        max_context_hint = window;  // the dispatcher sizes splits for at most `window` rows per sequence
     if (num_splits < 0)
         return fail(PKV_EINVAL, "num_splits must be >= 0 (got %d)", num_splits);
     if (!isfinite(scale))
@@ -412,7 +418,7 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
         k_new = v_new = nullptr;
     }
     return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, k_new, v_new);
+                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, k_new, v_new, window);
 }
 
 // Paged varlen attention (several new query rows per sequence): plan, checks, launches.
@@ -746,6 +752,16 @@ int pkv_device_cu_count(int32_t *cu_count) {
 const char *pkv_last_error(void) { return g_error; }
 
 const char *pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+
+int pkv_paged_decode_attention_window(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                      pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                      float scale, uint16_t *out, int32_t num_splits, int32_t window,
+                                      int32_t max_context_hint, void *stream) {
+    return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
+                       static_cast<hipStream_t>(stream), nullptr, nullptr, window);
+}
 
 int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                                pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,

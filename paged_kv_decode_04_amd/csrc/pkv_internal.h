@@ -19,8 +19,9 @@ struct DecodeParams {
     const _Float16 *v_new;
     int32_t Hq, Hkv, G, N, M;
     int32_t num_splits;           // grid splits S (1 for a single pass)
-    int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(nb / S) per sequence
+    int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(blocks in range / S) per sequence
     float scale_log2;             // scale * log2(e)
+    int32_t window;               // > 0: attend only the last `window` rows of each sequence; 0 = all rows
     const _Float16 *k_pool;       // [N][Hkv][BS/16][D/8][16][8]
     const _Float16 *v_pool;       // [N][Hkv][BS/16][D][16]
     _Float16 *out;                // [B][Hq][D]            (single pass)
@@ -59,6 +60,7 @@ struct CombineParams {
     _Float16 *out;
     int32_t B, Hq, BS, M;
     int32_t num_splits, chunk_blocks;
+    int32_t window;               // as DecodeParams::window (the split ranges start at the window's block)
 };
 
 struct AppendParams {

@@ -133,13 +133,15 @@ __device__ __forceinline__ void load_unit(Frag<D, BS> &f, const _Float16 *kb, co
                                                                                 kKvLoadPolicy));
 }
 
-// Last row each score column may attend.  col: this lane's column (per lane); first: the smallest over the tile's
-// columns; all: the largest (V rows past it are never used by any column and are zeroed).  A decode tile has one
+// Rows each score column may attend: lo .. col.  col: this lane's column's last row (per lane); first: the
+// smallest last row over the tile's columns; all: the largest (V rows outside lo .. all are never used by any column
+// and are zeroed).  A decode tile has one
 // limit, L - 1, for every column; a varlen tile gives each (query row, head) column the position of its row.
 struct RowLimits {
     int col;
     int first;
     int all;
+    int lo;  // first row any column may attend (a sliding window's start; 0 otherwise)
 };
 
 // One 16-row unit: scores, online-softmax update, P.V accumulation.  A dead unit (its block id names no pool
@@ -192,11 +194,12 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
     for (int e = 0; e < 4; ++e)
         y[e] = sc[e] * scale_log2;
     const int t0 = u * 16 + 4 * g4;  // row of y[0] in the sequence
-    if (dead || u * 16 + 15 > lim.first) {  // a unit past some column's last row, or a dead unit (wave-uniform)
+    if (dead || u * 16 + 15 > lim.first || u * 16 < lim.lo) {  // a unit crossing a limit, or dead (wave-uniform)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            y[e] = (!dead && (t0 + e) <= lim.col) ? y[e] : -INFINITY;
-            const bool row_ok = !dead && (t0 + e) <= lim.all;
+            const bool in_lo = (t0 + e) >= lim.lo;
+            y[e] = (!dead && in_lo && (t0 + e) <= lim.col) ? y[e] : -INFINITY;
+            const bool row_ok = !dead && in_lo && (t0 + e) <= lim.all;
 #pragma unroll
             for (int c = 0; c < VC; ++c)
                 f.v[c][e] = row_ok ? f.v[c][e] : (_Float16)0.0f;  // rows past every column's last may hold anything
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     // them.  When the range start is known from the launch alone (a single pass starts at block 0, a fixed-size
     // split j at j*chunk_blocks), the ids of this wave's first NS units are requested together with the length,
     // so the first K/V loads wait for one dependent load, not two.
-    const bool start_known = !SPLIT || p.chunk_blocks > 0;
+    const bool start_known = (!SPLIT || p.chunk_blocks > 0) && p.window <= 0;
     const int u_known = (SPLIT ? split * p.chunk_blocks : 0) * SPB + wave;
     constexpr int NSPEC = 2 * NS - 1;  // the prologue's NS-1 units and the NS block ids requested ahead
     int spec_raw[NSPEC];
@@ -294,17 +297,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     if (p.N <= 0)
         L = 0;  // an empty pool holds no rows
     const int nb = (L + BS - 1) / BS;
-    int b0 = 0, b1 = nb;
+    // sliding window: rows lo .. L-1, from block lo / BS [cortiq-engine 0.8.80, src/gpu_cuda.rs: the decode
+    // attend's first row, stored - window]
+    const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
+    const int b_lo = lo / BS;
+    int b0 = b_lo, b1 = nb;
     if (SPLIT) {
-        const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (nb + p.num_splits - 1) / p.num_splits;
-        b0 = split * chunk;
+        const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (nb - b_lo + p.num_splits - 1) / p.num_splits;
+        b0 = b_lo + split * chunk;
         b1 = min(nb, b0 + chunk);
         if (b0 >= b1)
             return;  // empty split: the combine never reads it
     }
-    const int u_begin = b0 * SPB;
+    const int u_begin = max(b0 * SPB, lo >> 4);  // units wholly before the window are skipped
     const int u_end = min(b1 * SPB, (L + 15) >> 4);
-    const RowLimits lim = {L - 1, L - 1, L - 1};
+    const RowLimits lim = {L - 1, L - 1, L - 1, lo};
     const int u_first = u_begin + wave;  // wave w takes units u_begin + w, + w + NW, ...
     const int n_units = u_first < u_end ? (u_end - u_first + NW - 1) / NW : 0;
     // Fused decode step: the workgroup whose range holds row L-1 writes the sequence's new K/V row there (the slot
@@ -549,6 +556,7 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
         const int crow = r / p.G;
         const bool col_ok = r < ncols;
         RowLimits lim;
+        lim.lo = 0;
         lim.first = min(pos + i0, cap - 1);
         lim.all = min(pos + i0 + nrows - 1, cap - 1);
         lim.col = col_ok ? min(pos + i0 + crow, cap - 1) : -1;
@@ -683,10 +691,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
         int L = p.context_lens[s];
         L = L < 0 ? 0 : (L > p.M * p.BS ? p.M * p.BS : L);
         const int nb = (L + p.BS - 1) / p.BS;
+        const int b_lo = ((p.window > 0 && L > p.window) ? L - p.window : 0) / p.BS;
         nvalid = 0;
-        if (nb > 0) {
-            const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (nb + p.num_splits - 1) / p.num_splits;
-            nvalid = min(p.num_splits, (nb + chunk - 1) / chunk);
+        if (nb > b_lo) {
+            const int n = nb - b_lo;
+            const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (n + p.num_splits - 1) / p.num_splits;
+            nvalid = min(p.num_splits, (n + chunk - 1) / chunk);
         }
     }
     const int64_t base = (int64_t)row * p.num_splits;

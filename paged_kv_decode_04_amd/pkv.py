@@ -40,6 +40,7 @@ EXPORTED = [
     "pkv_paged_decode_attention_planned",
     "pkv_paged_decode_step",
     "pkv_paged_varlen_attention",
+    "pkv_paged_decode_attention_window",
     "pkv_plan_decode",
     "pkv_decode_workspace_bytes",
     "pkv_paged_decode_split_partials",
@@ -86,6 +87,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.pkv_paged_decode_attention_planned.argtypes = attn[:11] + [ctypes.POINTER(DecodePlan), vp, sz, vp]
         lib.pkv_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, vp, i32, i32,
                                               vp]
+        lib.pkv_paged_decode_attention_window.argtypes = attn[:12] + [i32, i32, vp]
         lib.pkv_paged_varlen_attention.argtypes = [vp, vp, vp, PoolDesc, vp, i32, vp, vp, i32, i32, i32, f32, vp, i32,
                                                    i32, i32, vp]
         lib.pkv_plan_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodePlan)]
@@ -302,6 +304,23 @@ def paged_decode_split_combine(partial_out, partial_m, partial_l, context_lens, 
                                                  _ptr(context_lens), int(B), int(Hq), int(D), int(block_size),
                                                  int(max_blocks_per_seq), int(S), int(chunk_blocks), _ptr(out),
                                                  _stream(stream)))
+    return out
+
+
+def paged_decode_attention_window(q, k_pool, v_pool, block_tables, context_lens, scale: float, window: int,
+                                  out=None, num_splits: int = 0, max_context_hint: int = 0, stream=None):
+    """Sliding-window decode attention (pkv_paged_decode_attention_window): each sequence's new row attends only its
+    last ``window`` rows (window = 0: all rows)."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, torch.float16, "out", 3)
+    _check(load().pkv_paged_decode_attention_window(_ptr(q), _ptr(k_pool), _ptr(v_pool), pool, _ptr(block_tables),
+                                                    M, _ptr(context_lens), B, Hq, float(scale), _ptr(out),
+                                                    int(num_splits), int(window), int(max_context_hint),
+                                                    _stream(stream)))
     return out
 
 
