@@ -46,7 +46,16 @@ WORKLOADS = {
     "c5": ("MHA wide head: B=128, Hq=Hkv=16, D=256, BS=32, L=4096, K/V~U(-1,1), scale 1/16", 0, 1),
     "v1": ("speculative verification, varlen (Llama-3-8B-shaped batch): B=32, Hq=32, Hkv=8, D=128, BS=16, 4 new rows "
            "per sequence, final L~U[512,2048]", 0, 4),
+    "w1": ("sliding-window decode on the Llama-3-8B-shaped batch: B=32, Hq=32, Hkv=8, D=128, BS=16, L~U[512,2048], "
+           "window 512", 0, 8),
 }
+WINDOWS = {"w1": 512}  # workloads run with pkv_paged_decode_attention_window, and their window
+
+
+def step_is_fused(config: str, unfused: bool) -> bool:
+    """Whether bench.py times the workload's step as the fused decode step (varlen and sliding-window steps are the
+    append, then attention)."""
+    return not unfused and not config.startswith("v") and config not in WINDOWS
 
 
 def log(*a):
@@ -129,12 +138,12 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy
     return out
 
 
-def cpu_baseline(case, seconds: float):
+def cpu_baseline(case, seconds: float, window: int = 0):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     from paged_kv_decode_04_amd import workloads as W
     varlen = isinstance(case, W.VarlenCase)
-    nbytes = (W.algorithmic_bytes_varlen(case) if varlen else W.algorithmic_bytes(case))["attention"]
+    nbytes = (W.algorithmic_bytes_varlen(case) if varlen else W.algorithmic_bytes(case, window))["attention"]
     reps, t0 = 0, time.perf_counter()
     while True:
         if varlen:
@@ -142,7 +151,7 @@ def cpu_baseline(case, seconds: float):
                                     case.pos_offsets, case.scale, threads=threads)
         else:
             oracle.decode_attention(case.q, case.k_pool, case.v_pool, case.block_tables, case.context_lens,
-                                    case.scale, threads=threads)
+                                    case.scale, threads=threads, window=window)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -174,7 +183,7 @@ def main(argv=None) -> int:
         splits = WORKLOADS[args.config][1] if args.splits is None else args.splits
         rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config, splits,
                             args.copy_calibration_mib or 512.0)
-        extra = " --unfused" if args.unfused and not args.config.startswith("v") else ""
+        extra = " --unfused" if args.unfused and step_is_fused(args.config, False) else ""
         rec["commands"] = [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o %s -- python3 bench.py --config %s "
             "--steps 50 --warmup 10 --no-cpu-baseline --copy-calibration-mib %g%s"
@@ -185,7 +194,7 @@ def main(argv=None) -> int:
             "python bench.py --summarize-pmc gpurun_out/pmc_fetch/%s_counter_collection.csv "
             "gpurun_out/pmc_write/%s_counter_collection.csv --config %s%s" % (args.config, args.config, args.config, extra),
         ]
-        path = traffic_path(args.config, splits, not args.unfused and not args.config.startswith("v"))
+        path = traffic_path(args.config, splits, step_is_fused(args.config, args.unfused))
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
@@ -210,7 +219,9 @@ def main(argv=None) -> int:
     splits = default_splits if args.splits is None else args.splits
     R = default_rot if args.rotations is None else args.rotations
     varlen = args.config in W.VARLEN_CONFIGS
-    make = W.VARLEN_CONFIGS[args.config] if varlen else W.CONFIGS[args.config]
+    window = WINDOWS.get(args.config, 0)
+    make = (W.VARLEN_CONFIGS[args.config] if varlen else
+            (lambda rotation: W.config_c2(rotation=rotation)) if window else W.CONFIGS[args.config])
 
     log("building %d rotation set(s) of %s" % (R, args.config))
     sets = []
@@ -231,7 +242,7 @@ def main(argv=None) -> int:
             nz = np.nonzero(c.context_lens > 0)[0]
             kn[nz], vn[nz] = c.k_new, c.v_new
             d["k_new_all"], d["v_new_all"] = t(kn), t(vn)
-            d["bytes"] = W.algorithmic_bytes(c)
+            d["bytes"] = W.algorithmic_bytes(c, window)
         d["out"] = torch.empty_like(d["q"])
         if r == 0:
             host0 = c
@@ -246,13 +257,18 @@ def main(argv=None) -> int:
         plan = pkv.plan_decode(c0.B, c0.Hq, c0.Hkv, c0.D, c0.BS, c0.M, num_splits=splits)
     log("plan: %s, %s" % (plan, pkv.version()))
 
-    fused = not args.unfused and not varlen  # the varlen step is the append, then varlen attention
+    fused = step_is_fused(args.config, args.unfused)  # varlen / window steps: the append, then attention
     # arguments marshalled once per rotation set (the binding's prepared calls): per-step Python marshalling would
     # otherwise outlast the kernel and leave the GPU idle between steps
     for d in sets:
         if fused:
             d["call"] = pkv.prepare_decode_step(d["q"], d["k_new_all"], d["v_new_all"], d["k_pool"], d["v_pool"],
                                                 d["bt"], d["cl"], d["case"].scale, d["out"], num_splits=splits)
+        elif window:
+            d["append"] = pkv.prepare_paged_kv_append(d["k_new"], d["v_new"], d["slots"], d["k_pool"], d["v_pool"])
+            d["call"] = pkv.prepare_paged_decode_attention_window(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
+                                                                  d["case"].scale, d["out"], window,
+                                                                  num_splits=splits)
         elif varlen:
             d["append"] = pkv.prepare_paged_kv_append(d["k_new"], d["v_new"], d["slots"], d["k_pool"], d["v_pool"])
             d["call"] = pkv.prepare_paged_varlen_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cu"],
@@ -316,7 +332,7 @@ def main(argv=None) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same workload for ~%.0f s" % args.cpu_seconds)
-        cpu = cpu_baseline(host0, args.cpu_seconds)
+        cpu = cpu_baseline(host0, args.cpu_seconds, window)
         log("cpu baseline: %s" % cpu)
 
     result = {
@@ -338,6 +354,7 @@ def main(argv=None) -> int:
             "block_size": c0.BS, "num_splits": splits, "plan": plan, "rotations": R,
             "step": ("fused (pkv_paged_decode_step)" if fused else
                      "pkv_paged_kv_append + pkv_paged_varlen_attention" if varlen else
+                     "pkv_paged_kv_append + pkv_paged_decode_attention_window (window %d)" % window if window else
                      "pkv_paged_kv_append + pkv_paged_decode_attention"),
             "parallelism": "single GPU",
         },

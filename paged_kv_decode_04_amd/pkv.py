@@ -440,6 +440,23 @@ def prepare_paged_varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q
                         (q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, out))
 
 
+def prepare_paged_decode_attention_window(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,
+                                          window: int, num_splits: int = 0, max_context_hint: int = 0,
+                                          stream=None) -> PreparedCall:
+    """pkv_paged_decode_attention_window with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    _dev(out, torch.float16, "out", 3)
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(q)), ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool,
+            ctypes.c_void_p(_ptr(block_tables)), ctypes.c_int32(M), ctypes.c_void_p(_ptr(context_lens)),
+            ctypes.c_int32(B), ctypes.c_int32(Hq), ctypes.c_float(scale), ctypes.c_void_p(_ptr(out)),
+            ctypes.c_int32(num_splits), ctypes.c_int32(window), ctypes.c_int32(max_context_hint),
+            ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_paged_decode_attention_window, args,
+                        (q, k_pool, v_pool, block_tables, context_lens, out))
+
+
 def prepare_paged_kv_append(k, v, slot_mapping, k_pool, v_pool, stream=None) -> PreparedCall:
     """pkv_paged_kv_append with its arguments marshalled once (see PreparedCall)."""
     import torch

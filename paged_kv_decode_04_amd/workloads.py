@@ -291,13 +291,16 @@ def small_case(seed: int, B: int, Hq: int, Hkv: int, D: int, BS: int, lens, extr
                       kv_dist=kv_dist, poison=poison)
 
 
-def algorithmic_bytes(case: DecodeCase) -> dict:
-    """Bytes a decode step must move at minimum: K and V rows actually used, q, out, tables and lengths; the append
-    reads and writes 2*T*Hkv*D fp16 values."""
-    rows = int(np.maximum(case.context_lens, 0).sum())
+def algorithmic_bytes(case: DecodeCase, window: int = 0) -> dict:
+    """Bytes a decode step must move at minimum: K and V rows actually used (with a sliding window W > 0, each
+    sequence's last W rows), q, out, tables and lengths; the append reads and writes 2*T*Hkv*D fp16 values."""
+    lens = np.maximum(case.context_lens, 0)
+    if window > 0:
+        lens = np.minimum(lens, window)
+    rows = int(lens.sum())
     kv = rows * case.Hkv * case.D * 2 * 2
     qo = 2 * case.B * case.Hq * case.D * 2
-    nb = int(sum((max(int(L), 0) + case.BS - 1) // case.BS for L in case.context_lens))
+    nb = int(sum((int(L) + case.BS - 1) // case.BS for L in lens))
     idx = nb * 4 + case.B * 4
     app = 2 * 2 * case.num_tokens * case.Hkv * case.D * 2 + case.num_tokens * 4
     return {"kv": kv, "q_out": qo, "index": idx, "attention": kv + qo + idx, "append": app}
