@@ -143,6 +143,12 @@ int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slo
  *   per (device, stream), allocated on first need (that call synchronises the
  *   stream once before replacing a smaller buffer), never freed before
  *   process exit.  Calls on one stream reuse it in stream order.
+ *   Graph capture: every entry point reads lengths, tables and positions on
+ *   the device and sizes its launches from host arguments only, so a captured
+ *   call replays correctly with new device-resident values.  A workspace that
+ *   would have to grow while its stream is being captured is PKV_EWORKSPACE:
+ *   make one call with the same shape on that stream before capturing, or
+ *   use a _ws variant with a workspace allocated beforehand.
  *   q, k_pool, v_pool, out: 16-byte aligned.  num_seqs == 0 is a no-op.
  *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EHIP.
  * ------------------------------------------------------------------------- */

@@ -92,6 +92,16 @@ int library_workspace(size_t need, hipStream_t stream, void **ptr) {
     std::lock_guard<std::mutex> g(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
     if (w.bytes < need) {
+        // Growing allocates and synchronises, which a stream under graph capture must not do: the caller warms the
+        // workspace up with one call on this stream before capturing, or passes its own (the _ws variants).
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cap);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipStreamIsCapturing");
+        if (cap != hipStreamCaptureStatusNone)
+            return fail(PKV_EWORKSPACE, "the library workspace of this stream holds %zu bytes, the call needs %zu, and "
+                        "the stream is being captured: make one call on this stream before capture, or pass a "
+                        "workspace", w.bytes, need);
         if (w.ptr) {
             // queued kernels on this stream may still read the old buffer
             e = hipStreamSynchronize(stream);
