@@ -177,6 +177,8 @@ def main(argv=None) -> int:
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--unfused", action="store_true",
                     help="append and attention as two launches instead of the fused decode step")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph holding 32 consecutive steps instead of eager launches")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
@@ -258,6 +260,9 @@ def main(argv=None) -> int:
     log("plan: %s, %s" % (plan, pkv.version()))
 
     fused = step_is_fused(args.config, args.unfused)  # varlen / window steps: the append, then attention
+    if args.graph:
+        # prepared calls are bound to the stream current when they are made: make it the capture stream
+        torch.cuda.set_stream(torch.cuda.Stream())
     # arguments marshalled once per rotation set (the binding's prepared calls): per-step Python marshalling would
     # otherwise outlast the kernel and leave the GPU idle between steps
     for d in sets:
@@ -314,9 +319,29 @@ def main(argv=None) -> int:
     # No event inside a timed region: an event pair costs ~7 us of stream time here, more than a kernel's launch gap.
     # The step region gives value; when a step is one launch (the fused single-pass step) that launch's average
     # duration is the same region / K, otherwise a second region of K back-to-back attention calls gives it.
-    ms_per_step = timed(lambda i: step(sets[i % R]))
     one_launch = fused and plan["num_splits"] == 1
-    attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["call"]())])
+    if args.graph:
+        # 32 consecutive steps over the rotation sets captured once (the capture stream's workspace is sized by an
+        # eager step on it first) and replayed; every replay rewrites the same new rows, so the state is stable.
+        G = 32
+        cap = torch.cuda.current_stream()
+        for i in range(R):
+            step(sets[i])
+        cap.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(G):
+                step(sets[i % R])
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        K = (K + G - 1) // G * G
+        ms_per_step = timed(lambda i: graph.replay() if i % G == 0 else None)
+        attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["call"]())])
+        log("graph of %d steps, %d replays" % (G, K // G))
+    else:
+        ms_per_step = timed(lambda i: step(sets[i % R]))
+        attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["call"]())])
 
     # bytes per step, averaged over the rotation sets
     step_bytes = np.mean([d["bytes"]["attention"] + d["bytes"]["append"] for d in sets])
@@ -357,6 +382,7 @@ def main(argv=None) -> int:
                      "pkv_paged_kv_append + pkv_paged_decode_attention_window (window %d)" % window if window else
                      "pkv_paged_kv_append + pkv_paged_decode_attention"),
             "parallelism": "single GPU",
+            "launch": "HIP graph replay (32 steps per graph)" if args.graph else "eager launches",
         },
         "pct_of_peak": round(100.0 * float(value) / PEAK_GBS, 2),
         "calls_per_s": round(calls_per_s, 1),
