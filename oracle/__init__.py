@@ -1,4 +1,4 @@
-"""CPU oracle for paged-KV decode attention and the paged KV append (f64).
+"""CPU oracle for paged-KV decode attention, the paged KV append and the QKV-to-cache step (f64).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
 may import this package.  The product path (``paged_kv_decode_04_amd``) never imports it, and this package imports
@@ -73,6 +73,9 @@ def _load():
         lib.oracle_varlen_attention.restype = ctypes.c_int
         lib.oracle_decode_attention_window.argtypes = geom + [i32, P, i64, P, i32]
         lib.oracle_decode_attention_window.restype = ctypes.c_int
+        lib.oracle_qkv_norm_rope_paged.argtypes = [P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                                   i32, f64, i32, P, P, P, P]
+        lib.oracle_qkv_norm_rope_paged.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -262,3 +265,51 @@ def varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets,
         raise ValueError("oracle_varlen_attention failed (%d): bad geometry, prefix sums or positions, or a table "
                          "entry outside the pool" % rc)
     return out
+
+
+def qkv_norm_rope_paged(qkv, q_norm_w, k_norm_w, cos, sin, cu_seqlens_q, rope_pos, cache_pos, block_tables,
+                        k_pool, v_pool, eps, qk_mode):
+    """Split QKV, q/k RMSNorm (qk_mode 1) or none (0), RoPE, and the paged-cache write, in float64.
+
+    qkv: [T][(Hq + 2*Hkv)*D] fp16; q_norm_w, k_norm_w: [D] fp16 (ignored when qk_mode == 0, may be None);
+    cos, sin: [P][D/2] float32 tables; sequence s owns tokens cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1, its i-th at
+    RoPE position rope_pos[s] + i and cache row cache_pos[s] + i; eps is taken as a float32 (as the step receives
+    it).  k_pool gives the geometry only; v_pool
+    (C-contiguous fp16) receives the value rows in place.  Returns (q_out [T][Hq][D] f64, k_rows [T][Hkv][D] f64,
+    slots [T] int64 = block * BS + offset of each token's cache row).
+    """
+    qb = _bits(qkv)
+    T, width = qb.shape
+    N, Hkv, NP, D8, sixteen, eight = k_pool.shape
+    BS, D = NP * 16, D8 * 8
+    if (sixteen, eight) != (16, 8) or v_pool.shape != (N, Hkv, NP, D, 16) or width % D:
+        raise ValueError("pool shapes %s / %s do not match qkv %s" % (k_pool.shape, v_pool.shape, qb.shape))
+    Hq = width // D - 2 * Hkv
+    if Hq <= 0:
+        raise ValueError("qkv rows hold no query heads")
+    if not v_pool.flags.c_contiguous:
+        raise ValueError("v_pool must be C-contiguous (updated in place)")
+    cos = np.ascontiguousarray(cos, dtype=np.float32)
+    sin = np.ascontiguousarray(sin, dtype=np.float32)
+    if cos.ndim != 2 or cos.shape[1] != D // 2 or sin.shape != cos.shape:
+        raise ValueError("cos and sin must be [P][D/2] float32")
+    zeros = np.zeros(D, dtype=np.float16)
+    qw = _bits(zeros if q_norm_w is None else np.asarray(q_norm_w, dtype=np.float16).reshape(D))
+    kw = _bits(zeros if k_norm_w is None else np.asarray(k_norm_w, dtype=np.float16).reshape(D))
+    bt = _i32(block_tables)
+    cu, rp, cp = _i32(cu_seqlens_q), _i32(rope_pos), _i32(cache_pos)
+    B = rp.shape[0]
+    if bt.ndim != 2 or bt.shape[0] != B or cu.shape != (B + 1,) or cp.shape != (B,):
+        raise ValueError("block_tables must be [B][M], cu_seqlens_q [B+1], rope_pos and cache_pos [B]")
+    q_out = np.empty((T, Hq, D), dtype=np.float64)
+    k_out = np.empty((T, Hkv, D), dtype=np.float64)
+    slots = np.empty(T, dtype=np.int64)
+    rc = _load().oracle_qkv_norm_rope_paged(_ptr(qb), _ptr(qw), _ptr(kw), _ptr(cos), _ptr(sin), cos.shape[0],
+                                            _ptr(cu), _ptr(rp), _ptr(cp), _ptr(bt), B, T, Hq, Hkv, D, BS, N,
+                                            bt.shape[1], float(np.float32(eps)), int(qk_mode), _ptr(q_out), _ptr(k_out),
+                                            _ptr(slots), _ptr(v_pool.view(np.uint16)))
+    if rc != 0:
+        raise ValueError("oracle_qkv_norm_rope_paged failed (%d): bad geometry or mode, prefix sums, a position "
+                         "outside the tables, a row past the table capacity, or a table entry outside the pool"
+                         % rc)
+    return q_out, k_out, slots

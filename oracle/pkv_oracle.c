@@ -27,6 +27,9 @@
  *    Query head hq reads kv head hq / G with G = num_q_heads / num_kv_heads.
  *    [cortiq-engine 0.8.80, src/gpu_cuda.rs: the heads-per-kv-head grouping]
  *
+ *  - Split QKV, q/k RMSNorm, RoPE and the paged-cache write: the step that
+ *    produces the rows the attention reads (see oracle_qkv_norm_rope_paged).
+ *
  *  - Paged varlen attention: several new query rows per sequence, each
  *    attending the rows up to and including its own position (see
  *    oracle_varlen_attention for the passages).
@@ -646,4 +649,119 @@ int oracle_decode_attention_window(const uint16_t *q, const uint16_t *k_pool, co
     free(th);
     pthread_mutex_destroy(&W.lock);
     return W.rc;
+}
+
+
+/* ------------------------------------------------------------------ */
+/* Split QKV, q/k RMSNorm, RoPE and the paged-cache write.              */
+/* ------------------------------------------------------------------ */
+
+/* The step before attention in a decode or prefill layer: one call takes the
+ * fused QKV projection rows and leaves the rotated queries in q_out and the
+ * new K and V rows in the paged cache.
+ * [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ * split_qkv_norm_rope_into_paged_cache (one sequence: tokens, pos_offset,
+ * cache_len, block_table) and split_qkv_norm_rope_into_paged_cache_varlen
+ * (cu_seqlens_q, pos_offsets, block_tables); one launch covers
+ * q_heads + 2 * kv_heads heads per token.  ferrum-kernels 0.7.1, cuda.rs:
+ * qk_norm_rope (norm weight, cos, sin, pos_offset, eps, mode)]
+ *
+ * The pages give the arguments, not the arithmetic; the readings here:
+ *  - qkv[T][(Hq + 2*Hkv) * D] fp16, token-major; a row holds the Hq query
+ *    heads, then the Hkv key heads, then the Hkv value heads, D dims each;
+ *  - token i of sequence s (tokens cu[s] .. cu[s+1]-1) takes RoPE position
+ *    rope_pos[s] + (i - cu[s]) and goes to row cache_pos[s] + (i - cu[s]) of
+ *    the sequence, i.e. block block_tables[s][row / BS], offset row % BS
+ *    (the varlen form passes pos_offsets for both; the one-sequence form
+ *    passes pos_offset and cache_len);
+ *  - qk_mode 1: each query and key head is RMS-normalised over its D dims and
+ *    scaled by the norm weight, x_d <- x_d / sqrt(mean_e(x_e^2) + eps) * w_d
+ *    (q_norm_w for query heads, k_norm_w for key heads); qk_mode 0: no norm;
+ *  - RoPE rotates dim j with dim j + D/2 (j < D/2) by the angle whose cosine
+ *    and sine are cos_t[p][j], sin_t[p][j] (tables of D/2 floats per
+ *    position p):  (a, b) -> (a*c - b*s, b*c + a*s);
+ *  - value heads are copied unchanged.
+ *
+ * Outputs: q_out[T][Hq][D] and k_out[T][Hkv][D] in f64 (the rotated query
+ * rows and key rows, unrounded), slots[T] = block * BS + offset of the row
+ * each token went to, and v_pool with each token's value rows stored (fp16
+ * bits, exact copies) at its slot.  k_pool is not written: the key rows are
+ * real-valued here and are compared against the pool by the caller.
+ *
+ * Returns 0; -1 for a bad geometry or mode, prefix sums that do not run
+ * 0 = cu[0] <= ... <= cu[B] = T, a position outside [0, P) or a cache row
+ * outside [0, M*BS); -2 for a table entry outside the pool. */
+int oracle_qkv_norm_rope_paged(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w,
+                               const float *cos_t, const float *sin_t, int32_t P_rows,
+                               const int32_t *cu_seqlens_q, const int32_t *rope_pos, const int32_t *cache_pos,
+                               const int32_t *block_tables, int32_t B, int32_t T, int32_t Hq, int32_t Hkv,
+                               int32_t D, int32_t BS, int32_t N, int32_t M, double eps, int32_t qk_mode,
+                               double *q_out, double *k_out, int64_t *slots, uint16_t *v_pool)
+{
+    if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || D % 8 || BS <= 0 || BS % 16 || N < 0 || M < 0)
+        return -1;
+    if ((qk_mode != 0 && qk_mode != 1) || (B == 0 && T != 0) || eps < 0.0)
+        return -1;
+    if (B > 0 && (cu_seqlens_q[0] != 0 || cu_seqlens_q[B] != T))
+        return -1;
+    oracle_problem P;
+    memset(&P, 0, sizeof P);
+    P.Hkv = Hkv; P.BS = BS; P.D = D; P.N = N;
+    const int width = (Hq + 2 * Hkv) * D;
+    const int half = D / 2;
+    double *x = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!x)
+        return -3;
+    int rc = 0;
+    for (int s = 0; s < B && rc == 0; ++s) {
+        if (cu_seqlens_q[s + 1] < cu_seqlens_q[s]) {
+            rc = -1;
+            break;
+        }
+        for (int i = cu_seqlens_q[s]; i < cu_seqlens_q[s + 1]; ++i) {
+            int64_t p = (int64_t)rope_pos[s] + (i - cu_seqlens_q[s]);
+            int64_t row = (int64_t)cache_pos[s] + (i - cu_seqlens_q[s]);
+            if (p < 0 || p >= P_rows || row < 0 || row >= (int64_t)M * BS) {
+                rc = -1;
+                break;
+            }
+            int32_t blk = block_tables[(int64_t)s * M + row / BS];
+            if (blk < 0 || blk >= N) {
+                rc = -2;
+                break;
+            }
+            int off = (int)(row % BS);
+            slots[i] = (int64_t)blk * BS + off;
+            /* query heads 0..Hq-1, then key heads Hq..Hq+Hkv-1: norm (mode 1), then rotate */
+            for (int h = 0; h < Hq + Hkv; ++h) {
+                const uint16_t *src = qkv + (int64_t)i * width + (int64_t)h * D;
+                for (int d = 0; d < D; ++d)
+                    x[d] = oracle_f16_to_f64(src[d]);
+                if (qk_mode == 1) {
+                    const uint16_t *w = h < Hq ? q_norm_w : k_norm_w;
+                    double ss = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        ss += x[d] * x[d];
+                    double r = sqrt(ss / D + eps);
+                    for (int d = 0; d < D; ++d)
+                        x[d] = x[d] / r * oracle_f16_to_f64(w[d]);
+                }
+                double *dst = h < Hq ? q_out + ((int64_t)i * Hq + h) * D : k_out + ((int64_t)i * Hkv + (h - Hq)) * D;
+                for (int j = 0; j < half; ++j) {
+                    double c = (double)cos_t[p * half + j], sn = (double)sin_t[p * half + j];
+                    double a = x[j], b = x[j + half];
+                    dst[j] = a * c - b * sn;
+                    dst[j + half] = b * c + a * sn;
+                }
+            }
+            /* value heads: copied into the pool row */
+            for (int h = 0; h < Hkv; ++h) {
+                const uint16_t *src = qkv + (int64_t)i * width + (int64_t)(Hq + Hkv + h) * D;
+                for (int d = 0; d < D; ++d)
+                    v_pool[v_index(&P, blk, h, off, d)] = src[d];
+            }
+        }
+    }
+    free(x);
+    return rc;
 }

@@ -35,7 +35,7 @@ POISON = 60000.0  # fp16-representable marker for a row that the append must ove
 
 SEEDS = {"c1": 0xC0FFEE01, "c2": 0xC0FFEE02, "c3": 0xC0FFEE03, "c4": 0xC0FFEE04, "c5": 0xC0FFEE05}
 
-_TAGS = {"q": 1, "k": 2, "v": 3, "lens": 4, "perm": 5, "knew": 6, "vnew": 7, "choice": 8}
+_TAGS = {"q": 1, "k": 2, "v": 3, "lens": 4, "perm": 5, "knew": 6, "vnew": 7, "choice": 8, "qkv": 9, "normw": 10}
 
 
 def _rng(seed: int, rotation: int, tag: str, *extra: int) -> np.random.Generator:
@@ -418,3 +418,94 @@ def algorithmic_bytes_varlen(case: VarlenCase) -> dict:
     idx = nb * 4 + (2 * case.B + 1) * 4
     app = 2 * 2 * case.T * case.Hkv * case.D * 2 + case.T * 4
     return {"kv": kv, "q_out": qo, "index": idx, "attention": kv + qo + idx, "append": app}
+
+
+def rope_tables(num_positions: int, head_dim: int, theta: float):
+    """cos and sin tables [num_positions][head_dim/2] float32 of the usual rotary frequencies: entry (p, j) is the
+    angle p * theta^(-2j/head_dim), evaluated in float64 and rounded once.  These are the caller's tables (a model's
+    configuration), inputs to the QKV step."""
+    half = head_dim // 2
+    inv = theta ** (-2.0 * np.arange(half, dtype=np.float64) / head_dim)
+    ang = np.arange(num_positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+@dataclass
+class QkvCase:
+    """Inputs of the QKV-to-cache step followed by attention.  ``qkv`` [T][(Hq + 2*Hkv)*D] fp16 holds each new
+    token's query heads, key heads and value heads; ``varlen`` carries the batch geometry (sequences, new rows at
+    positions pos_offsets[s] + i, block tables, pools whose new rows hold POISON until the step writes them)."""
+    name: str
+    varlen: VarlenCase
+    qkv: np.ndarray
+    q_norm_w: np.ndarray   # [D] fp16
+    k_norm_w: np.ndarray   # [D] fp16
+    cos: np.ndarray        # [P][D/2] float32
+    sin: np.ndarray
+    eps: float
+    qk_mode: int
+
+
+def build_qkv_case(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int, q_lens, pos_offsets, seed: int,
+                   qk_mode: int = 1, eps: float = 1e-6, theta: float = 1.0e6, qkv_scale: float = 1.0,
+                   rotation: int = 0, extra_blocks: int = 3, M: Optional[int] = None,
+                   num_positions: Optional[int] = None) -> QkvCase:
+    """qkv ~ qkv_scale * N(0,1), norm weights ~ 1 + 0.25 * N(0,1) (both rounded to fp16), rotary tables for
+    ``theta`` covering every position the batch reaches (or ``num_positions`` rows)."""
+    vc = build_varlen_case(name, B, Hq, Hkv, D, BS, q_lens, pos_offsets, seed, rotation, extra_blocks=extra_blocks,
+                           poison_new=True, M=M)
+    T = vc.T
+    qkv = fill_f16(np.empty((T, (Hq + 2 * Hkv) * D), dtype=np.float16), seed, rotation, "qkv", "normal", qkv_scale)
+    rng = _rng(seed, rotation, "normw")
+    w = (1.0 + 0.25 * rng.standard_normal((2, D), dtype=np.float32)).astype(np.float16)
+    if num_positions is None:
+        num_positions = max(1, int(vc.final_lens.max()) if B else 1)
+    cos, sin = rope_tables(num_positions, D, theta)
+    return QkvCase(name, vc, qkv, np.ascontiguousarray(w[0]), np.ascontiguousarray(w[1]), cos, sin, float(eps),
+                   int(qk_mode))
+
+
+SEEDS["r1"] = 0xC0FFEE21
+SEEDS["r2"] = 0xC0FFEE22
+
+
+def config_r1(rotation: int = 0) -> QkvCase:
+    """Decode step of a Qwen3-8B-shaped layer (32/8 heads, D=128, q/k RMSNorm): B=32, BS=16, one new token per
+    sequence whose final lengths are U{512..2048} as in the Llama-3-8B-shaped batch, pool = blocks + 10%, M=128,
+    rotary theta 1e6, eps 1e-6.  The QKV step writes q and the new K/V rows, then single-pass attention reads
+    them."""
+    seed = SEEDS["r1"]
+    final = _rng(seed, rotation, "lens").integers(512, 2048, size=32, endpoint=True).astype(np.int32)
+    ql = np.ones(32, dtype=np.int32)
+    nblocks = int(sum((int(L) + 15) // 16 for L in final))
+    return build_qkv_case("r1", 32, 32, 8, 128, 16, ql, final - ql, seed, qk_mode=1,
+                          extra_blocks=int(math.ceil(0.10 * nblocks)), M=128, rotation=rotation)
+
+
+def config_r2(rotation: int = 0) -> QkvCase:
+    """Chunked prefill of the same layer: B=4 sequences each adding 512 new rows after a cached prefix of
+    U{0..1024} rows (so chunks start mid-block), BS=16, pool = blocks + 10%.  The QKV step writes 2048 tokens'
+    q and K/V rows, then varlen attention reads them."""
+    seed = SEEDS["r2"]
+    pre = _rng(seed, rotation, "lens").integers(0, 1024, size=4, endpoint=True).astype(np.int32)
+    ql = np.full(4, 512, dtype=np.int32)
+    final = pre + ql
+    nblocks = int(sum((int(L) + 15) // 16 for L in final))
+    return build_qkv_case("r2", 4, 32, 8, 128, 16, ql, pre, seed, qk_mode=1,
+                          extra_blocks=int(math.ceil(0.10 * nblocks)), rotation=rotation)
+
+
+QKV_CONFIGS = {"r1": config_r1, "r2": config_r2}
+
+
+def algorithmic_bytes_qkv(case: QkvCase) -> int:
+    """Bytes the QKV step must move at minimum: the qkv rows read, q written, the new K and V rows written, the norm
+    weights and each token's cos/sin row read, tables and positions."""
+    vc = case.varlen
+    T, D = vc.T, vc.D
+    qkv = T * (vc.Hq + 2 * vc.Hkv) * D * 2
+    q_out = T * vc.Hq * D * 2
+    kv = 2 * T * vc.Hkv * D * 2
+    rope = 2 * T * (D // 2) * 4
+    idx = (2 * vc.B + 1) * 4 + T * 4
+    return qkv + q_out + kv + rope + 2 * D * 2 + idx

@@ -588,3 +588,183 @@ def test_window_ignores_rows_before_it():
     assert np.array_equal(out, out2)
     assert not np.array_equal(_run(c), oracle.decode_attention(c.q, kp, vp, c.block_tables, c.context_lens, c.scale,
                                                                threads=4))
+
+
+# --------------------------------------------------------------------------------------------------------------
+# QKV-to-cache step: split QKV, q/k RMSNorm, RoPE, paged-cache write
+
+def _golden_qkv_cases():
+    with open(os.path.join(GOLDEN, "qkv_rope_hand.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_qkv_cases(), ids=lambda c: c["name"])
+def test_golden_qkv(case):
+    D, BS, N, Hkv = case["D"], case["BS"], case["N"], case["Hkv"]
+    qkv = np.asarray(case["qkv"], dtype=np.float16)
+    T = qkv.shape[0]
+    qkv = np.ascontiguousarray(qkv.reshape(T, -1))
+    k_pool, v_pool = _zero_pools(N, Hkv, BS, D)
+    k_pool[...] = 0.25
+    v_pool[...] = 0.25
+    qw = None if case["q_norm_w"] is None else np.asarray(case["q_norm_w"], dtype=np.float16)
+    kw = None if case["k_norm_w"] is None else np.asarray(case["k_norm_w"], dtype=np.float16)
+    q, k, slots = oracle.qkv_norm_rope_paged(qkv, qw, kw, np.asarray(case["cos"], np.float32),
+                                             np.asarray(case["sin"], np.float32), case["cu_seqlens_q"],
+                                             case["rope_pos"], case["cache_pos"], case["block_tables"], k_pool,
+                                             v_pool, case["eps"], case["qk_mode"])
+    np.testing.assert_allclose(q, np.asarray(case["expected_q"], dtype=np.float64), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(k, np.asarray(case["expected_k"], dtype=np.float64), rtol=0, atol=1e-6)
+    assert slots.tolist() == case["expected_slots"]
+    ref = np.full_like(v_pool, 0.25)
+    for r in case["expected_v_rows"]:
+        W.set_v_row(ref, r["block"], r["head"], r["offset"], r["v"])
+    assert np.array_equal(v_pool.view(np.uint16), ref.view(np.uint16))
+    assert np.all(k_pool == np.float16(0.25)), "the oracle leaves k_pool to the caller"
+
+
+def _qkv_small(seed=11, qk_mode=0, q_lens=(3, 1, 5), pos=(0, 17, 30), B=3, Hq=4, Hkv=2, D=64, BS=16, **kw):
+    return W.build_qkv_case("small", B, Hq, Hkv, D, BS, list(q_lens), list(pos), seed, qk_mode=qk_mode, **kw)
+
+
+def _qkv_run(c, cos=None, sin=None, qk_mode=None, v_pool=None):
+    vc = c.varlen
+    vp = vc.v_pool.copy() if v_pool is None else v_pool
+    return oracle.qkv_norm_rope_paged(c.qkv, c.q_norm_w, c.k_norm_w, c.cos if cos is None else cos,
+                                      c.sin if sin is None else sin, vc.cu_seqlens_q, vc.pos_offsets,
+                                      vc.pos_offsets, vc.block_tables, vc.k_pool, vp, c.eps,
+                                      c.qk_mode if qk_mode is None else qk_mode) + (vp,)
+
+
+def _token_positions(vc):
+    pos = np.empty(vc.T, dtype=np.int64)
+    for s in range(vc.B):
+        for i in range(int(vc.q_lens[s])):
+            pos[vc.cu_seqlens_q[s] + i] = vc.pos_offsets[s] + i
+    return pos
+
+
+def _heads(c):
+    vc = c.varlen
+    return oracle.f16_to_f64(c.qkv).reshape(vc.T, vc.Hq + 2 * vc.Hkv, vc.D)
+
+
+@pytest.mark.parametrize("D", [8, 64, 128, 256])
+def test_qkv_rope_is_a_complex_rotation(D):
+    """Without the norm, each head's dims j and j + D/2 form the complex number a + ib, which RoPE multiplies by
+    cos + i sin of the token's table row (numpy complex arithmetic as the independent second opinion)."""
+    c = _qkv_small(seed=21 + D, D=D, theta=1.0e4)
+    vc = c.varlen
+    q, k, _, _ = _qkv_run(c)
+    x = _heads(c)
+    half = D // 2
+    z = x[..., :half] + 1j * x[..., half:]
+    pos = _token_positions(vc)
+    rot = (c.cos.astype(np.float64) + 1j * c.sin.astype(np.float64))[pos][:, None, :]
+    want = z * rot
+    got = np.concatenate([q, k], axis=1)
+    np.testing.assert_allclose(got[..., :half], want.real[:, :vc.Hq + vc.Hkv], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[..., half:], want.imag[:, :vc.Hq + vc.Hkv], rtol=0, atol=1e-12)
+
+
+def test_qkv_norm_is_torch_rms_norm():
+    """With identity tables (cos 1, sin 0) the step is the RMS norm alone: torch's CPU rms_norm in float64, with the
+    query weight on query heads and the key weight on key heads."""
+    import torch
+    import torch.nn.functional as F
+    c = _qkv_small(seed=31, qk_mode=1, D=128, qkv_scale=3.0, eps=1e-3)
+    vc = c.varlen
+    ones, zeros = np.ones_like(c.cos), np.zeros_like(c.sin)
+    q, k, _, _ = _qkv_run(c, cos=ones, sin=zeros)
+    x = torch.from_numpy(_heads(c))
+    qw = torch.from_numpy(oracle.f16_to_f64(c.q_norm_w))
+    kw = torch.from_numpy(oracle.f16_to_f64(c.k_norm_w))
+    eps = float(np.float32(c.eps))
+    want_q = F.rms_norm(x[:, :vc.Hq], (vc.D,), qw, eps).numpy()
+    want_k = F.rms_norm(x[:, vc.Hq:vc.Hq + vc.Hkv], (vc.D,), kw, eps).numpy()
+    np.testing.assert_allclose(q, want_q, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(k, want_k, rtol=1e-13, atol=1e-13)
+
+
+def test_qkv_position_zero_is_identity_and_pairs_keep_their_length():
+    c = _qkv_small(seed=41, q_lens=(4, 2), pos=(0, 9), B=2, theta=1.0e4)
+    vc = c.varlen
+    q, k, _, _ = _qkv_run(c)
+    x = _heads(c)
+    # token 0 of sequence 0 sits at position 0: cos 1, sin 0 exactly
+    assert np.array_equal(q[0], x[0, :vc.Hq]) and np.array_equal(k[0], x[0, vc.Hq:vc.Hq + vc.Hkv])
+    half = vc.D // 2
+    got = np.concatenate([q, k], axis=1)
+    src = x[:, :vc.Hq + vc.Hkv]
+    n_got = np.hypot(got[..., :half], got[..., half:])
+    n_src = np.hypot(src[..., :half], src[..., half:])
+    np.testing.assert_allclose(n_got, n_src, rtol=2e-7, atol=1e-12)  # float32 tables: cos^2 + sin^2 = 1 +- 1e-7
+
+
+def test_qkv_scores_depend_only_on_relative_position():
+    """RoPE's defining property: q at position p and k at p' give the score of q at p + d and k at p' + d.
+    Sequence 1 repeats sequence 0's rows 37 positions later."""
+    c = _qkv_small(seed=51, q_lens=(3, 3), pos=(2, 39), B=2, D=128, theta=1.0e4)
+    vc = c.varlen
+    c.qkv[3:6] = c.qkv[0:3]
+    q, k, _, _ = _qkv_run(c)
+    G = vc.Hq // vc.Hkv
+    for i in range(3):
+        for j in range(3):
+            for hq in range(vc.Hq):
+                a = q[i, hq] @ k[j, hq // G]
+                b = q[3 + i, hq] @ k[3 + j, hq // G]
+                scale = np.linalg.norm(q[i, hq]) * np.linalg.norm(k[j, hq // G])
+                assert abs(a - b) <= 2e-6 * scale, (i, j, hq, a, b)
+
+
+def test_qkv_value_rows_land_at_the_append_slots_and_nothing_else_changes():
+    """The cache rows are the ones the paged append would use (the slot mapping the input generator derives from
+    the tables); value rows are bit copies; every other pool element is untouched."""
+    c = _qkv_small(seed=61, q_lens=(20, 1, 33), pos=(5, 16, 31), D=64, BS=32)
+    vc = c.varlen
+    before = vc.v_pool.copy()
+    _, _, slots, vp = _qkv_run(c)
+    assert np.array_equal(slots, vc.slot_mapping.astype(np.int64))
+    x = c.qkv.reshape(vc.T, vc.Hq + 2 * vc.Hkv, vc.D)
+    ref = before.copy()
+    for t, slot in enumerate(vc.slot_mapping):
+        W.set_v_row(ref, int(slot) // vc.BS, slice(None), int(slot) % vc.BS, x[t, vc.Hq + vc.Hkv:])
+    assert np.array_equal(vp.view(np.uint16), ref.view(np.uint16))
+
+
+def test_qkv_batched_call_equals_one_sequence_at_a_time():
+    c = _qkv_small(seed=71, qk_mode=1, q_lens=(3, 0, 5), pos=(0, 7, 30))
+    vc = c.varlen
+    q, k, slots, vp = _qkv_run(c)
+    vp1 = vc.v_pool.copy()
+    for s in range(vc.B):
+        a, b = int(vc.cu_seqlens_q[s]), int(vc.cu_seqlens_q[s + 1])
+        q1, k1, sl1 = oracle.qkv_norm_rope_paged(np.ascontiguousarray(c.qkv[a:b]), c.q_norm_w, c.k_norm_w, c.cos,
+                                                 c.sin, [0, b - a], vc.pos_offsets[s:s + 1],
+                                                 vc.pos_offsets[s:s + 1], vc.block_tables[s:s + 1], vc.k_pool, vp1,
+                                                 c.eps, c.qk_mode)
+        assert np.array_equal(q1, q[a:b]) and np.array_equal(k1, k[a:b]) and np.array_equal(sl1, slots[a:b])
+    assert np.array_equal(vp1.view(np.uint16), vp.view(np.uint16))
+
+
+def test_qkv_rejects_bad_mode_positions_rows_and_tables():
+    c = _qkv_small(seed=81)
+    vc = c.varlen
+    with pytest.raises(ValueError):
+        _qkv_run(c, qk_mode=2)
+    assert c.cos.shape[0] == 35  # the last token sits at position 34
+    with pytest.raises(ValueError):
+        _qkv_run(c, cos=c.cos[:34], sin=c.sin[:34])
+    bad = vc.block_tables.copy()
+    bad[2, 2] = -1
+    with pytest.raises(ValueError):
+        oracle.qkv_norm_rope_paged(c.qkv, c.q_norm_w, c.k_norm_w, c.cos, c.sin, vc.cu_seqlens_q, vc.pos_offsets,
+                                   vc.pos_offsets, bad, vc.k_pool, vc.v_pool.copy(), c.eps, c.qk_mode)
+    with pytest.raises(ValueError):  # cache rows past M * BS
+        oracle.qkv_norm_rope_paged(c.qkv, c.q_norm_w, c.k_norm_w, c.cos, c.sin, vc.cu_seqlens_q, vc.pos_offsets,
+                                   vc.pos_offsets + 64, vc.block_tables, vc.k_pool, vc.v_pool.copy(), c.eps,
+                                   c.qk_mode)
+    with pytest.raises(ValueError):
+        oracle.qkv_norm_rope_paged(c.qkv, c.q_norm_w, c.k_norm_w, c.cos, c.sin, [0, 3, 2, 9], vc.pos_offsets,
+                                   vc.pos_offsets, vc.block_tables, vc.k_pool, vc.v_pool.copy(), c.eps, c.qk_mode)
