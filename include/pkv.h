@@ -15,6 +15,9 @@
  *   - its split-K ("flash decoding") form: per-split f32 partials, then a
  *     log-sum-exp combine       [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
  *                                 SplitKScratch, paged_batched_flash_dispatch]
+ *   - the step that feeds it: split QKV, q/k RMS norm, RoPE and the
+ *     paged-cache write         [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ *                                 split_qkv_norm_rope_into_paged_cache(_varlen)]
  *
  * Conventions for every entry point
  * ---------------------------------
@@ -262,6 +265,77 @@ int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const 
                                const int32_t *cu_seqlens_q, const int32_t *pos_offsets, int32_t num_seqs,
                                int32_t total_q_tokens, int32_t num_q_heads, float scale, uint16_t *out,
                                int32_t num_splits, int32_t max_q_len, int32_t max_context_hint, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_split_qkv_norm_rope_into_paged_cache_varlen -- the step that feeds
+ *   paged attention: from the fused QKV projection rows, RMS-normalise the
+ *   query and key heads (qk_mode 1), rotate them (RoPE), write the queries to
+ *   q_out and the new K and V rows into the paged pools.
+ *   [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ *   split_qkv_norm_rope_into_paged_cache_varlen (one launch over
+ *   q_heads + 2 * kv_heads heads per token, cu_seqlens_q / pos_offsets /
+ *   block_tables); ferrum-kernels 0.7.1, cuda.rs: qk_norm_rope]
+ *   The pages give the arguments, not the arithmetic; computed here, for the
+ *   i-th new token of sequence s (token cu_seqlens_q[s] + i) at position
+ *   p = pos_offsets[s] + i:
+ *     - qkv row = [num_q_heads query heads | Hkv key heads | Hkv value heads],
+ *       head_dim values each;
+ *     - qk_mode 1: each query/key head x <- x / sqrt(mean(x^2) + eps) * w
+ *       (w = q_norm_w for query heads, k_norm_w for key heads); qk_mode 0:
+ *       no norm (the weights are not read and may be NULL);
+ *     - RoPE turns dim j with dim j + head_dim/2 (j < head_dim/2):
+ *       (a, b) -> (a*c - b*s, b*c + a*s), c = cos_table[p][j],
+ *       s = sin_table[p][j];
+ *     - the query heads go to q_out[token][hq][:]; the key head h and value
+ *       head h (copied unchanged) go to row p of the sequence in kv head h:
+ *       block block_tables[s][p / block_size], row p % block_size.
+ *   f32 arithmetic, each output rounded once to fp16 (nearest even).  The
+ *   16-row pool panels that receive new rows are rewritten whole, their other
+ *   rows with their own values: the blocks receiving a sequence's new rows
+ *   must belong to that sequence alone during the call.
+ *   qkv: [total_tokens][(num_q_heads + 2*Hkv) * head_dim] fp16.
+ *   q_norm_w, k_norm_w: [head_dim] fp16.  cos_table, sin_table:
+ *   [max_positions][head_dim/2] float32.  q_out: [total_tokens][num_q_heads]
+ *   [head_dim] fp16, token-major (what pkv_paged_varlen_attention and, for one
+ *   token per sequence, pkv_paged_decode_attention read).  cu_seqlens_q,
+ *   pos_offsets, block_tables: as pkv_paged_varlen_attention.  qkv, q_out,
+ *   pools, tables and weights 16-byte aligned.
+ *   Device-resident values are not validated: a token whose cache row has no
+ *   pool block is not written to the cache (q_out still is); a 16-row unit of
+ *   new rows whose positions leave [0, max_positions) is not written at all.
+ *   num_seqs == 0 or total_tokens == 0 is a no-op.
+ *   Errors: PKV_EINVAL (null pointers, misalignment, qk_mode not 0 or 1,
+ *   eps negative or not finite, max_positions <= 0, ...), PKV_EUNSUPPORTED
+ *   (head_dim not 64, 128 or 256; block_size not a multiple of 16), PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+int pkv_split_qkv_norm_rope_into_paged_cache_varlen(const uint16_t *qkv, const uint16_t *q_norm_w,
+                                                    const uint16_t *k_norm_w, const float *cos_table,
+                                                    const float *sin_table, int32_t max_positions, uint16_t *q_out,
+                                                    uint16_t *k_pool, uint16_t *v_pool, pkv_pool_desc pool,
+                                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                                    const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
+                                                    int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
+                                                    float eps, int32_t qk_mode, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_split_qkv_norm_rope_into_paged_cache -- the one-sequence form: token i
+ *   (of num_tokens) takes RoPE position pos_offset + i and goes to cache row
+ *   cache_len + i of the sequence whose table is block_table
+ *   [max_blocks_per_seq].  Both are host values, checked here:
+ *   pos_offset + num_tokens <= max_positions and cache_len + num_tokens <=
+ *   block_size * max_blocks_per_seq (PKV_EINVAL otherwise).  Everything else
+ *   as pkv_split_qkv_norm_rope_into_paged_cache_varlen.
+ *   [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ *   split_qkv_norm_rope_into_paged_cache (tokens, pos_offset, cache_len,
+ *   block_size, max_blocks_per_seq)]
+ * ------------------------------------------------------------------------- */
+int pkv_split_qkv_norm_rope_into_paged_cache(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w,
+                                             const float *cos_table, const float *sin_table, int32_t max_positions,
+                                             uint16_t *q_out, uint16_t *k_pool, uint16_t *v_pool,
+                                             pkv_pool_desc pool, const int32_t *block_table,
+                                             int32_t max_blocks_per_seq, int32_t num_tokens, int32_t num_q_heads,
+                                             int32_t pos_offset, int32_t cache_len, float eps, int32_t qk_mode,
+                                             void *stream);
 
 /* ---------------------------------------------------------------------------
  * pkv_plan_decode -- the dispatcher, a pure host function (no device call

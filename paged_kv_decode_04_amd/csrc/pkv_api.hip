@@ -551,6 +551,93 @@ int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     return ok();
 }
 
+// Split QKV + q/k RMSNorm + RoPE + paged-cache write: checks and the launch.  varlen == false is the one-sequence
+// form (no cu_seqlens_q / pos_offsets; rope_base / cache_base are host values, checked here).
+int qkv_impl(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w, const float *cos_table,
+             const float *sin_table, int32_t max_positions, uint16_t *q_out, uint16_t *k_pool, uint16_t *v_pool,
+             pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+             const int32_t *cu_seqlens_q, const int32_t *pos_offsets, int32_t num_seqs, int32_t total_tokens,
+             int32_t num_q_heads, bool varlen, int32_t rope_base, int32_t cache_base, float eps,
+             int32_t qk_mode, hipStream_t stream) {
+    int rc = check_pool(pool);
+    if (rc)
+        return rc;
+    if (num_seqs < 0 || total_tokens < 0)
+        return fail(PKV_EINVAL, "num_seqs and the token count must be >= 0 (got %d, %d)", num_seqs, total_tokens);
+    if (num_q_heads <= 0 || num_q_heads % pool.num_kv_heads != 0)
+        return fail(PKV_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", num_q_heads,
+                    pool.num_kv_heads);
+    if (pool.head_dim != 64 && pool.head_dim != 128 && pool.head_dim != 256)
+        return fail(PKV_EUNSUPPORTED, "head_dim %d not compiled (64|128|256)", pool.head_dim);
+    if (pool.block_size % 16 != 0)
+        return fail(PKV_EUNSUPPORTED, "block_size %d must be a multiple of 16", pool.block_size);
+    if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * pool.block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "max_blocks_per_seq must be > 0 with max_blocks_per_seq * block_size in int32 "
+                    "(got %d)", max_blocks_per_seq);
+    if (max_positions <= 0)
+        return fail(PKV_EINVAL, "max_positions must be > 0 (got %d)", max_positions);
+    if (qk_mode != 0 && qk_mode != 1)
+        return fail(PKV_EINVAL, "qk_mode must be 0 (rotate only) or 1 (RMS norm, then rotate); got %d", qk_mode);
+    if (!(eps >= 0.f) || !isfinite(eps))
+        return fail(PKV_EINVAL, "eps must be finite and >= 0");
+    if (!varlen) {
+        if (rope_base < 0 || (int64_t)rope_base + total_tokens > max_positions)
+            return fail(PKV_EINVAL, "positions %d .. %d + %d exceed the %d table rows", rope_base, rope_base,
+                        total_tokens, max_positions);
+        if (cache_base < 0 || (int64_t)cache_base + total_tokens > (int64_t)max_blocks_per_seq * pool.block_size)
+            return fail(PKV_EINVAL, "cache rows %d .. %d + %d exceed the table capacity %lld", cache_base,
+                        cache_base, total_tokens, (long long)max_blocks_per_seq * pool.block_size);
+    }
+    if (num_seqs == 0 || total_tokens == 0)
+        return ok();
+    if (!qkv || !cos_table || !sin_table || !q_out || !k_pool || !v_pool || !block_tables ||
+        (qk_mode == 1 && (!q_norm_w || !k_norm_w)) || (varlen && (!cu_seqlens_q || !pos_offsets)))
+        return fail(PKV_EINVAL, "null device pointer (qkv=%p cos=%p sin=%p q_out=%p k_pool=%p v_pool=%p "
+                    "block_tables=%p q_norm_w=%p k_norm_w=%p cu_seqlens_q=%p pos_offsets=%p)", qkv, cos_table,
+                    sin_table, q_out, k_pool, v_pool, block_tables, q_norm_w, k_norm_w, cu_seqlens_q, pos_offsets);
+    if (!aligned(qkv, 16) || !aligned(q_out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+        !aligned(cos_table, 16) || !aligned(sin_table, 16) ||
+        (qk_mode == 1 && (!aligned(q_norm_w, 16) || !aligned(k_norm_w, 16))))
+        return fail(PKV_EINVAL, "qkv, q_out, the pools, the cos/sin tables and the norm weights must be 16-byte "
+                    "aligned");
+    if (!aligned(block_tables, 4) || (varlen && (!aligned(cu_seqlens_q, 4) || !aligned(pos_offsets, 4))))
+        return fail(PKV_EINVAL, "block_tables, cu_seqlens_q and pos_offsets must be 4-byte aligned");
+    if ((int64_t)total_tokens * pool.num_kv_heads > INT32_MAX)
+        return fail(PKV_EINVAL, "total_tokens * num_kv_heads overflows the grid");
+    if ((int64_t)total_tokens * (num_q_heads + 2 * pool.num_kv_heads) * pool.head_dim > INT32_MAX)
+        return fail(PKV_EINVAL, "qkv holds more than 2^31 values");
+    pkv::QkvParams p;
+    memset(&p, 0, sizeof p);
+    p.qkv = reinterpret_cast<const _Float16 *>(qkv);
+    p.q_norm_w = reinterpret_cast<const _Float16 *>(q_norm_w);
+    p.k_norm_w = reinterpret_cast<const _Float16 *>(k_norm_w);
+    p.cos_t = cos_table;
+    p.sin_t = sin_table;
+    p.cu_seqlens_q = varlen ? cu_seqlens_q : nullptr;
+    p.pos_offsets = varlen ? pos_offsets : nullptr;
+    p.block_tables = block_tables;
+    p.B = num_seqs;
+    p.T = total_tokens;
+    p.Hq = num_q_heads;
+    p.Hkv = pool.num_kv_heads;
+    p.G = num_q_heads / pool.num_kv_heads;
+    p.N = pool.num_blocks;
+    p.M = max_blocks_per_seq;
+    p.BS = pool.block_size;
+    p.P = max_positions;
+    p.qk_mode = qk_mode;
+    p.rope_base = rope_base;
+    p.cache_base = cache_base;
+    p.eps = eps;
+    p.q_out = reinterpret_cast<_Float16 *>(q_out);
+    p.k_pool = reinterpret_cast<_Float16 *>(k_pool);
+    p.v_pool = reinterpret_cast<_Float16 *>(v_pool);
+    hipError_t e = pkv::launch_qkv_cache(p, pool.head_dim, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "qkv-to-cache kernel launch");
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -746,6 +833,31 @@ int pkv_paged_decode_split_combine(const float *partial_out, const float *partia
     if (e != hipSuccess)
         return hip_fail(e, "split-K combine kernel launch");
     return ok();
+}
+
+int pkv_split_qkv_norm_rope_into_paged_cache_varlen(const uint16_t *qkv, const uint16_t *q_norm_w,
+                                                    const uint16_t *k_norm_w, const float *cos_table,
+                                                    const float *sin_table, int32_t max_positions, uint16_t *q_out,
+                                                    uint16_t *k_pool, uint16_t *v_pool, pkv_pool_desc pool,
+                                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                                    const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
+                                                    int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
+                                                    float eps, int32_t qk_mode, void *stream) {
+    return qkv_impl(qkv, q_norm_w, k_norm_w, cos_table, sin_table, max_positions, q_out, k_pool, v_pool, pool,
+                    block_tables, max_blocks_per_seq, cu_seqlens_q, pos_offsets, num_seqs, total_tokens,
+                    num_q_heads, true, 0, 0, eps, qk_mode, static_cast<hipStream_t>(stream));
+}
+
+int pkv_split_qkv_norm_rope_into_paged_cache(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w,
+                                             const float *cos_table, const float *sin_table, int32_t max_positions,
+                                             uint16_t *q_out, uint16_t *k_pool, uint16_t *v_pool,
+                                             pkv_pool_desc pool, const int32_t *block_table,
+                                             int32_t max_blocks_per_seq, int32_t num_tokens, int32_t num_q_heads,
+                                             int32_t pos_offset, int32_t cache_len, float eps, int32_t qk_mode,
+                                             void *stream) {
+    return qkv_impl(qkv, q_norm_w, k_norm_w, cos_table, sin_table, max_positions, q_out, k_pool, v_pool, pool,
+                    block_table, max_blocks_per_seq, nullptr, nullptr, 1, num_tokens, num_q_heads, false,
+                    pos_offset, cache_len, eps, qk_mode, static_cast<hipStream_t>(stream));
 }
 
 int pkv_device_cu_count(int32_t *cu_count) {

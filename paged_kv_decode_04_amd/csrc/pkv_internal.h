@@ -1,5 +1,5 @@
 // pkv_internal.h -- private interface between the host API (pkv_api.hip) and
-// the kernels (pkv_kernels.hip).  Not installed; callers use include/pkv.h.
+// the kernels (pkv_kernels.hip, pkv_qkv.hip).  Not installed; callers use include/pkv.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -74,6 +74,25 @@ struct AppendParams {
     int32_t T, Hkv, D, BS, N, M;
 };
 
+// Arguments of the QKV-to-cache kernel (split QKV, q/k RMSNorm, RoPE, paged-cache write).
+struct QkvParams {
+    const _Float16 *qkv;          // [T][(Hq + 2*Hkv) * D]: query heads, key heads, value heads
+    const _Float16 *q_norm_w;     // [D] (qk_mode 1)
+    const _Float16 *k_norm_w;     // [D] (qk_mode 1)
+    const float *cos_t;           // [P][D/2]
+    const float *sin_t;           // [P][D/2]
+    const int32_t *cu_seqlens_q;  // [B+1]; null: one sequence of T tokens at rope_base / cache_base
+    const int32_t *pos_offsets;   // [B]: first new token's RoPE position and cache row
+    const int32_t *block_tables;  // [B][M]
+    int32_t B, T, Hq, Hkv, G, N, M, BS, P;
+    int32_t qk_mode;              // 1: RMS-normalise query and key heads first; 0: rotate only
+    int32_t rope_base, cache_base;
+    float eps;
+    _Float16 *q_out;              // [T][Hq][D]
+    _Float16 *k_pool;
+    _Float16 *v_pool;
+};
+
 // LDS bytes the decode kernel needs for `waves` wavefronts and group size G.
 size_t decode_lds_bytes(int head_dim, int G, int waves);
 
@@ -86,6 +105,7 @@ hipError_t launch_varlen(const VarlenParams &p, int num_seqs, int head_dim, int 
                          hipStream_t stream);
 hipError_t launch_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream);
+hipError_t launch_qkv_cache(const QkvParams &p, int head_dim, hipStream_t stream);
 
 // Geometry support of the compiled kernels.
 bool decode_geometry_supported(int head_dim, int block_size);

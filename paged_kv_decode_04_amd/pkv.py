@@ -13,6 +13,8 @@ Tensor layouts (all C-contiguous, on the GPU):
     context_lens  [num_seqs]                                        int32
     k, v          [num_tokens][num_kv_heads][head_dim]              float16
     slot_mapping  [num_tokens]                                      int32
+    qkv           [num_tokens][(num_q_heads + 2*num_kv_heads)*head_dim]  float16
+    cos, sin      [max_positions][head_dim/2]                       float32
 """
 from __future__ import annotations
 
@@ -41,6 +43,8 @@ EXPORTED = [
     "pkv_paged_decode_step",
     "pkv_paged_varlen_attention",
     "pkv_paged_decode_attention_window",
+    "pkv_split_qkv_norm_rope_into_paged_cache_varlen",
+    "pkv_split_qkv_norm_rope_into_paged_cache",
     "pkv_plan_decode",
     "pkv_decode_workspace_bytes",
     "pkv_paged_decode_split_partials",
@@ -90,6 +94,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.pkv_paged_decode_attention_window.argtypes = attn[:12] + [i32, i32, vp]
         lib.pkv_paged_varlen_attention.argtypes = [vp, vp, vp, PoolDesc, vp, i32, vp, vp, i32, i32, i32, f32, vp, i32,
                                                    i32, i32, vp]
+        qkv = [vp, vp, vp, vp, vp, i32, vp, vp, vp, PoolDesc, vp, i32]
+        lib.pkv_split_qkv_norm_rope_into_paged_cache_varlen.argtypes = qkv + [vp, vp, i32, i32, i32, f32, i32, vp]
+        lib.pkv_split_qkv_norm_rope_into_paged_cache.argtypes = qkv + [i32, i32, i32, i32, f32, i32, vp]
         lib.pkv_plan_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodePlan)]
         lib.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.pkv_decode_workspace_bytes.restype = sz
@@ -352,6 +359,73 @@ def paged_varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_of
     return out
 
 
+def _qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, num_q_heads: int, qk_mode: int):
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(qkv, torch.float16, "qkv", 2)
+    _dev(cos, torch.float32, "cos", 2)
+    _dev(sin, torch.float32, "sin", 2)
+    _dev(q_out, torch.float16, "q_out", 3)
+    D, Hkv, Hq = pool.head_dim, pool.num_kv_heads, int(num_q_heads)
+    T = int(qkv.shape[0])
+    if qkv.shape[1] != (Hq + 2 * Hkv) * D:
+        raise ValueError("qkv rows must hold (Hq + 2*Hkv) * D = %d values" % ((Hq + 2 * Hkv) * D))
+    if tuple(q_out.shape) != (T, Hq, D):
+        raise ValueError("q_out must be [T][Hq][D] = %s" % ((T, Hq, D),))
+    if cos.shape[1] != D // 2 or cos.shape != sin.shape:
+        raise ValueError("cos and sin must be [max_positions][D/2]")
+    for w, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if w is not None:
+            _dev(w, torch.float16, n, 1)
+            if w.shape[0] != D:
+                raise ValueError("%s must hold head_dim values" % n)
+        elif qk_mode == 1:
+            raise ValueError("qk_mode 1 needs %s" % n)
+    return pool, T, int(cos.shape[0])
+
+
+def split_qkv_norm_rope_into_paged_cache_varlen(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool, block_tables,
+                                                cu_seqlens_q, pos_offsets, num_q_heads: int, eps: float,
+                                                qk_mode: int = 1, q_out=None, stream=None):
+    """The step before attention (pkv_split_qkv_norm_rope_into_paged_cache_varlen): from qkv [T][(Hq+2Hkv)*D],
+    RMS-normalise (qk_mode 1) and rotate the query and key heads, write q_out [T][Hq][D] and each token's K/V rows
+    into the pools at row pos_offsets[s] + i of its sequence.  Returns q_out."""
+    import torch
+    if q_out is None:
+        q_out = torch.empty((qkv.shape[0], int(num_q_heads), k_pool.shape[3] * 8), dtype=torch.float16,
+                            device=qkv.device)
+    pool, T, P = _qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, num_q_heads, qk_mode)
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1)
+    _dev(pos_offsets, torch.int32, "pos_offsets", 1)
+    B = int(pos_offsets.shape[0])
+    if block_tables.shape[0] != B or cu_seqlens_q.shape[0] != B + 1:
+        raise ValueError("block_tables must have num_seqs = %d rows and cu_seqlens_q num_seqs + 1 entries" % B)
+    _check(load().pkv_split_qkv_norm_rope_into_paged_cache_varlen(
+        _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(cos), _ptr(sin), P, _ptr(q_out), _ptr(k_pool), _ptr(v_pool),
+        pool, _ptr(block_tables), int(block_tables.shape[1]), _ptr(cu_seqlens_q), _ptr(pos_offsets), B, T,
+        int(num_q_heads), float(eps), int(qk_mode), _stream(stream)))
+    return q_out
+
+
+def split_qkv_norm_rope_into_paged_cache(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool, block_table,
+                                         num_q_heads: int, pos_offset: int, cache_len: int, eps: float,
+                                         qk_mode: int = 1, q_out=None, stream=None):
+    """One-sequence form (pkv_split_qkv_norm_rope_into_paged_cache): token i takes RoPE position pos_offset + i and
+    cache row cache_len + i of the sequence whose table is block_table [M].  Returns q_out."""
+    import torch
+    if q_out is None:
+        q_out = torch.empty((qkv.shape[0], int(num_q_heads), k_pool.shape[3] * 8), dtype=torch.float16,
+                            device=qkv.device)
+    pool, T, P = _qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, num_q_heads, qk_mode)
+    _dev(block_table, torch.int32, "block_table", 1)
+    _check(load().pkv_split_qkv_norm_rope_into_paged_cache(
+        _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(cos), _ptr(sin), P, _ptr(q_out), _ptr(k_pool), _ptr(v_pool),
+        pool, _ptr(block_table), int(block_table.shape[0]), T, int(num_q_heads), int(pos_offset), int(cache_len),
+        float(eps), int(qk_mode), _stream(stream)))
+    return q_out
+
+
 class PreparedCall:
     """A C entry point with its arguments marshalled once (device pointers, geometry, stream).  Calling it costs one
     ctypes call and no Python-side checks: for tight decode loops where per-call marshalling would outlast the
@@ -472,3 +546,24 @@ def prepare_paged_kv_append(k, v, slot_mapping, k_pool, v_pool, stream=None) -> 
             ctypes.c_int32(T), ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool,
             ctypes.c_void_p(_stream(stream)))
     return PreparedCall(lib.pkv_paged_kv_append, args, (k, v, slot_mapping, k_pool, v_pool))
+
+
+def prepare_split_qkv_norm_rope_into_paged_cache_varlen(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool,
+                                                        block_tables, cu_seqlens_q, pos_offsets, num_q_heads: int,
+                                                        eps: float, qk_mode: int, q_out,
+                                                        stream=None) -> PreparedCall:
+    """pkv_split_qkv_norm_rope_into_paged_cache_varlen with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    pool, T, P = _qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, num_q_heads, qk_mode)
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    B = int(pos_offsets.shape[0])
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(qkv)), ctypes.c_void_p(_ptr(q_norm_w)), ctypes.c_void_p(_ptr(k_norm_w)),
+            ctypes.c_void_p(_ptr(cos)), ctypes.c_void_p(_ptr(sin)), ctypes.c_int32(P), ctypes.c_void_p(_ptr(q_out)),
+            ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool, ctypes.c_void_p(_ptr(block_tables)),
+            ctypes.c_int32(int(block_tables.shape[1])), ctypes.c_void_p(_ptr(cu_seqlens_q)),
+            ctypes.c_void_p(_ptr(pos_offsets)), ctypes.c_int32(B), ctypes.c_int32(T), ctypes.c_int32(num_q_heads),
+            ctypes.c_float(eps), ctypes.c_int32(qk_mode), ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_split_qkv_norm_rope_into_paged_cache_varlen, args,
+                        (qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, block_tables, cu_seqlens_q,
+                         pos_offsets))

@@ -140,6 +140,38 @@ def test_entry_points_validate_before_touching_a_device():
                                               None) == pkv.PKV_OK
 
 
+def test_qkv_entry_points_validate_before_touching_a_device():
+    lib = pkv.load()
+    pool = pkv.PoolDesc(8, 128, 16, 100)
+    varlen = lib.pkv_split_qkv_norm_rope_into_paged_cache_varlen
+    one = lib.pkv_split_qkv_norm_rope_into_paged_cache
+    # qkv, qn, kn, cos, sin, P, q_out, kp, vp, pool, bt, M, cu, pos, B, T, Hq, eps, mode, stream
+    assert varlen(None, None, None, None, None, 64, None, None, None, pool, None, 128, None, None, 4, 8, 32, 1e-6, 1,
+                  None) == pkv.PKV_EINVAL
+    assert varlen(None, None, None, None, None, 64, None, None, None, pool, None, 128, None, None, 0, 8, 32, 1e-6, 1,
+                  None) == pkv.PKV_OK  # no sequences: a no-op
+    assert varlen(None, None, None, None, None, 64, None, None, None, pool, None, 128, None, None, 4, 8, 32, 1e-6, 2,
+                  None) == pkv.PKV_EINVAL and "qk_mode" in pkv.last_error()
+    assert varlen(None, None, None, None, None, 64, None, None, None, pool, None, 128, None, None, 4, 8, 32, -1.0, 1,
+                  None) == pkv.PKV_EINVAL
+    assert varlen(None, None, None, None, None, 0, None, None, None, pool, None, 128, None, None, 4, 8, 32, 1e-6, 1,
+                  None) == pkv.PKV_EINVAL
+    assert varlen(None, None, None, None, None, 64, None, None, None, pkv.PoolDesc(8, 96, 16, 100), None, 128, None,
+                  None, 4, 8, 32, 1e-6, 1, None) == pkv.PKV_EUNSUPPORTED
+    assert varlen(None, None, None, None, None, 64, None, None, None, pool, None, 128, None, None, 4, 8, 30, 1e-6, 1,
+                  None) == pkv.PKV_EINVAL  # 30 query heads over 8 kv heads
+    # qkv, qn, kn, cos, sin, P, q_out, kp, vp, pool, bt, M, T, Hq, pos_offset, cache_len, eps, mode, stream
+    assert one(None, None, None, None, None, 64, None, None, None, pool, None, 4, 8, 32, 60, 0, 1e-6, 0,
+               None) == pkv.PKV_EINVAL and "table rows" in pkv.last_error()  # positions 60..67 of 64
+    assert one(None, None, None, None, None, 64, None, None, None, pool, None, 4, 8, 32, 0, 60, 1e-6, 0,
+               None) == pkv.PKV_EINVAL and "capacity" in pkv.last_error()  # rows 60..67 of 4 * 16
+    assert one(None, None, None, None, None, 64, None, None, None, pool, None, 4, 0, 32, 0, 0, 1e-6, 0,
+               None) == pkv.PKV_OK
+    # misaligned (non-null, never dereferenced)
+    rc = one(8, 16, 16, 16, 16, 64, 16, 16, 16, pool, 4, 4, 8, 32, 0, 0, 1e-6, 1, None)
+    assert rc == pkv.PKV_EINVAL and "aligned" in pkv.last_error()
+
+
 def test_workspace_bytes_layout():
     assert pkv.decode_workspace_bytes(4, 32, 128, 1) == 0
     n = pkv.decode_workspace_bytes(4, 32, 128, 16)

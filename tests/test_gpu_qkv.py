@@ -1,0 +1,242 @@
+"""GPU parity of the QKV-to-cache step (split QKV, q/k RMS norm, RoPE, paged-cache write) against the CPU oracle,
+through the C ABI.
+
+Bar, from the arithmetic: the kernel computes in f32 and rounds each output once to fp16, the oracle stays in f64.
+Every q and K element must lie within half an fp16 ulp of the f64 value plus 4e-6 of its head row's largest
+magnitude (the f32 norm and rotation chain is good to a few 1e-7 of that), and at most 1% of them may differ from
+the f64 value rounded to nearest-even fp16 (the ones whose f64 value sits within f32 error of a rounding midpoint).
+V rows are bit copies: the whole V pool must equal the oracle's bit for bit.  Every K element outside the new rows
+must be bit-identical to what the pool held before.  Attention after the step is held to the attention bar
+(max|err| <= 2e-3 and <= 1e-2 of max|ref|) against the oracle run on the oracle's own step outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_decode_04_amd import workloads as W
+from test_gpu_parity import assert_close, say, torch_cuda, _dev  # noqa: F401  (fixture and helpers)
+
+pytestmark = pytest.mark.gpu
+
+
+def _ulp16(x):
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    return 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -14))) - 10)
+
+
+def assert_fp16_of(gpu16, ref64, what):
+    """gpu16 (fp16) is ref64 (f64) rounded once from an f32 computation; rows are the last axis."""
+    g = np.asarray(gpu16, dtype=np.float64)
+    assert np.all(np.isfinite(g)), "%s: non-finite output" % what
+    R = np.max(np.abs(ref64), axis=-1, keepdims=True) if ref64.size else ref64
+    err = np.abs(g - ref64)
+    tol = 0.5 * _ulp16(ref64) + 4e-6 * np.maximum(R, 1.0)
+    worst = float((err / tol).max()) if err.size else 0.0
+    mism = float(np.mean(np.asarray(gpu16, np.float16).view(np.uint16) != ref64.astype(np.float16).view(np.uint16))) \
+        if err.size else 0.0
+    say("%s: max err/tol %.3f, not the nearest fp16: %.4f%%" % (what, worst, 100 * mism))
+    assert worst <= 1.0, "%s: error %.3e exceeds tolerance at %s" % (what, float(err.max()),
+                                                                    np.unravel_index(np.argmax(err / tol), err.shape))
+    assert mism <= 0.01, "%s: %.2f%% of elements are not the nearest fp16" % (what, 100 * mism)
+
+
+def _reference(c):
+    """The oracle's step outputs: q and K rows in f64, the slots, and the V pool with the new value rows."""
+    vc = c.varlen
+    v_ref = vc.v_pool.copy()
+    q, k, slots = oracle.qkv_norm_rope_paged(c.qkv, c.q_norm_w, c.k_norm_w, c.cos, c.sin, vc.cu_seqlens_q,
+                                             vc.pos_offsets, vc.pos_offsets, vc.block_tables, vc.k_pool, v_ref,
+                                             c.eps, c.qk_mode)
+    return q, k, slots, v_ref
+
+
+def _run(torch, c, prepared=False):
+    from paged_kv_decode_04_amd import pkv
+    vc = c.varlen
+    kp, vp = _dev(torch, vc.k_pool), _dev(torch, vc.v_pool)
+    args = (_dev(torch, c.qkv), _dev(torch, c.q_norm_w), _dev(torch, c.k_norm_w), _dev(torch, c.cos),
+            _dev(torch, c.sin), kp, vp, _dev(torch, vc.block_tables), _dev(torch, vc.cu_seqlens_q),
+            _dev(torch, vc.pos_offsets), vc.Hq, c.eps, c.qk_mode)
+    if prepared:
+        q = torch.empty((vc.T, vc.Hq, vc.D), dtype=torch.float16, device="cuda")
+        pkv.prepare_split_qkv_norm_rope_into_paged_cache_varlen(*args, q)()
+    else:
+        q = pkv.split_qkv_norm_rope_into_paged_cache_varlen(*args)
+    torch.cuda.synchronize()
+    return q, kp, vp
+
+
+def _check_step(c, q, kp, vp, what):
+    vc = c.varlen
+    q_ref, k_ref, slots, v_ref = _reference(c)
+    assert np.array_equal(slots, vc.slot_mapping.astype(np.int64))
+    assert_fp16_of(q, q_ref, what + " q")
+    got_k = np.stack([W.k_row(kp, int(s) // vc.BS, h, int(s) % vc.BS) for s in slots for h in range(vc.Hkv)])
+    assert_fp16_of(got_k.reshape(k_ref.shape), k_ref, what + " K rows")
+    rest = kp.copy()
+    for s in slots:
+        b, o = int(s) // vc.BS, int(s) % vc.BS
+        for h in range(vc.Hkv):
+            W.set_k_row(rest, b, h, o, W.k_row(vc.k_pool, b, h, o))
+    assert np.array_equal(rest.view(np.uint16), vc.k_pool.view(np.uint16)), what + ": K rows outside the step moved"
+    assert np.array_equal(vp.view(np.uint16), v_ref.view(np.uint16)), what + ": V pool differs"
+    return q_ref, k_ref, slots, v_ref
+
+
+# (Hq, Hkv, D, BS, new rows per sequence, first new row of each, qk_mode).  Units of 16 cache rows are written by one
+# workgroup each: these cover single new rows (decode), runs that start and end inside a unit, whole units, runs
+# across block edges, every head size, group sizes 1, 3, 4, 8 and 16, and a sequence with no new rows.
+QKV_GEOMS = [
+    (8, 2, 64, 16, (1, 4, 7, 0, 16), (0, 30, 100, 12, 3), 1),
+    (32, 8, 128, 16, (1, 1, 1, 1, 1, 1), (511, 1000, 63, 2040, 15, 16), 1),
+    (16, 16, 256, 32, (3, 17), (40, 100), 1),
+    (32, 2, 128, 64, (2, 35), (64, 130), 0),
+    (12, 4, 128, 32, (5, 6), (20, 77), 1),
+    (8, 8, 64, 16, (48,), (0,), 0),
+    (64, 8, 128, 16, (33, 1), (5, 0), 1),
+]
+
+
+@pytest.mark.parametrize("geom", QKV_GEOMS, ids=lambda g: "Hq%d_Hkv%d_D%d_BS%d_T%d_m%d" % (g[:4] + (sum(g[4]),
+                                                                                                     g[6])))
+def test_qkv_step_matches_oracle(torch_cuda, geom):
+    Hq, Hkv, D, BS, ql, po, mode = geom
+    c = W.build_qkv_case("qkv", len(ql), Hq, Hkv, D, BS, ql, po, 1200 + D + BS + Hq, qk_mode=mode,
+                         qkv_scale=2.0, eps=1e-5)
+    say("qkv %s" % (geom,))
+    q, kp, vp = _run(torch_cuda, c)
+    _check_step(c, q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), "qkv %s" % (geom,))
+
+
+def test_qkv_prepared_call_matches(torch_cuda):
+    c = W.build_qkv_case("qkv", 3, 32, 8, 128, 16, (1, 20, 2), (7, 30, 200), 1301)
+    q, kp, vp = _run(torch_cuda, c, prepared=True)
+    _check_step(c, q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), "qkv prepared")
+
+
+def test_qkv_one_sequence_form(torch_cuda):
+    """pkv_split_qkv_norm_rope_into_paged_cache: RoPE positions pos_offset + i, cache rows cache_len + i (here they
+    differ), one block table."""
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    T, pos_offset, cache_len = 21, 40, 27
+    c = W.build_qkv_case("qkv1", 1, 16, 4, 128, 16, (T,), (cache_len,), 1302, num_positions=pos_offset + T)
+    vc = c.varlen
+    kp, vp = _dev(torch, vc.k_pool), _dev(torch, vc.v_pool)
+    q = pkv.split_qkv_norm_rope_into_paged_cache(_dev(torch, c.qkv), _dev(torch, c.q_norm_w),
+                                                 _dev(torch, c.k_norm_w), _dev(torch, c.cos), _dev(torch, c.sin), kp,
+                                                 vp, _dev(torch, vc.block_tables[0]), vc.Hq, pos_offset, cache_len,
+                                                 c.eps, c.qk_mode)
+    torch.cuda.synchronize()
+    v_ref = vc.v_pool.copy()
+    q_ref, k_ref, slots = oracle.qkv_norm_rope_paged(c.qkv, c.q_norm_w, c.k_norm_w, c.cos, c.sin, [0, T],
+                                                     [pos_offset], [cache_len], vc.block_tables, vc.k_pool, v_ref,
+                                                     c.eps, c.qk_mode)
+    assert_fp16_of(q.cpu().numpy(), q_ref, "one-sequence q")
+    kpn = kp.cpu().numpy()
+    got_k = np.stack([W.k_row(kpn, int(s) // 16, h, int(s) % 16) for s in slots for h in range(vc.Hkv)])
+    assert_fp16_of(got_k.reshape(k_ref.shape), k_ref, "one-sequence K rows")
+    assert np.array_equal(vp.cpu().numpy().view(np.uint16), v_ref.view(np.uint16))
+
+
+def test_qkv_rope_only_accepts_null_weights(torch_cuda):
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    c = W.build_qkv_case("qkv", 2, 8, 2, 64, 16, (3, 1), (10, 40), 1303, qk_mode=0)
+    vc = c.varlen
+    kp, vp = _dev(torch, vc.k_pool), _dev(torch, vc.v_pool)
+    q = pkv.split_qkv_norm_rope_into_paged_cache_varlen(_dev(torch, c.qkv), None, None, _dev(torch, c.cos),
+                                                        _dev(torch, c.sin), kp, vp, _dev(torch, vc.block_tables),
+                                                        _dev(torch, vc.cu_seqlens_q), _dev(torch, vc.pos_offsets),
+                                                        vc.Hq, c.eps, 0)
+    torch.cuda.synchronize()
+    _check_step(c, q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), "qkv rope-only, null weights")
+
+
+def test_qkv_row_without_a_pool_block_writes_q_only(torch_cuda):
+    """A table entry outside the pool (device data, not validated): that unit's cache rows are not written; q_out
+    still is, and the other sequences are unaffected."""
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    c = W.build_qkv_case("qkv", 2, 8, 2, 64, 16, (2, 3), (17, 40), 1304)
+    vc = c.varlen
+    bt = vc.block_tables.copy()
+    bt[0, 1] = -1  # rows 17, 18 of sequence 0 live in its block 1
+    kp, vp = _dev(torch, vc.k_pool), _dev(torch, vc.v_pool)
+    q = pkv.split_qkv_norm_rope_into_paged_cache_varlen(_dev(torch, c.qkv), _dev(torch, c.q_norm_w),
+                                                        _dev(torch, c.k_norm_w), _dev(torch, c.cos),
+                                                        _dev(torch, c.sin), kp, vp, _dev(torch, bt),
+                                                        _dev(torch, vc.cu_seqlens_q), _dev(torch, vc.pos_offsets),
+                                                        vc.Hq, c.eps, c.qk_mode)
+    torch.cuda.synchronize()
+    q_ref, k_ref, slots, v_ref = _reference(c)
+    assert_fp16_of(q.cpu().numpy(), q_ref, "q with a missing block")
+    kpn, vpn = kp.cpu().numpy(), vp.cpu().numpy()
+    for t, s in enumerate(slots):
+        b, o = int(s) // 16, int(s) % 16
+        for h in range(vc.Hkv):
+            if t < 2:  # sequence 0: untouched
+                assert np.array_equal(W.k_row(kpn, b, h, o).view(np.uint16), W.k_row(vc.k_pool, b, h, o).view(np.uint16))
+                assert np.array_equal(W.v_row(vpn, b, h, o).view(np.uint16), W.v_row(vc.v_pool, b, h, o).view(np.uint16))
+            else:
+                assert_fp16_of(W.k_row(kpn, b, h, o)[None], k_ref[t, h][None], "sequence 1 K row")
+                assert np.array_equal(W.v_row(vpn, b, h, o).view(np.uint16), W.v_row(v_ref, b, h, o).view(np.uint16))
+
+
+def test_qkv_no_tokens_is_a_no_op(torch_cuda):
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    c = W.build_qkv_case("qkv", 2, 8, 2, 64, 16, (0, 0), (3, 9), 1305)
+    vc = c.varlen
+    kp, vp = _dev(torch, vc.k_pool), _dev(torch, vc.v_pool)
+    qkv = torch.zeros((0, 12 * 64), dtype=torch.float16, device="cuda")
+    q = pkv.split_qkv_norm_rope_into_paged_cache_varlen(qkv, _dev(torch, c.q_norm_w), _dev(torch, c.k_norm_w),
+                                                        _dev(torch, c.cos), _dev(torch, c.sin), kp, vp,
+                                                        _dev(torch, vc.block_tables), _dev(torch, vc.cu_seqlens_q),
+                                                        _dev(torch, vc.pos_offsets), vc.Hq, c.eps, 1)
+    torch.cuda.synchronize()
+    assert q.shape == (0, 8, 64)
+    assert np.array_equal(kp.cpu().numpy().view(np.uint16), vc.k_pool.view(np.uint16))
+
+
+def _oracle_pools(c, k_ref, slots, v_ref):
+    """The pools as the oracle's step leaves them: its K rows rounded to fp16, its V pool."""
+    vc = c.varlen
+    kp = vc.k_pool.copy()
+    k16 = k_ref.astype(np.float16)
+    for t, s in enumerate(slots):
+        W.set_k_row(kp, int(s) // vc.BS, slice(None), int(s) % vc.BS, k16[t])
+    return kp, v_ref
+
+
+@pytest.mark.parametrize("name", ["r1", "r2"])
+def test_qkv_then_attention_full_size(torch_cuda, name):
+    """The bench workloads at full size: the step, then attention on its outputs (decode attention for r1, one new
+    token per sequence; varlen attention for r2), against the oracle's step followed by the oracle's attention."""
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    c = W.QKV_CONFIGS[name]()
+    vc = c.varlen
+    say("qkv %s full size: T=%d" % (name, vc.T))
+    q, kp, vp = _run(torch, c)
+    q_ref, k_ref, slots, v_ref = _check_step(c, q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), name)
+    kp_ref, vp_ref = _oracle_pools(c, k_ref, slots, v_ref)
+    q16 = q_ref.astype(np.float16)
+    if name == "r1":
+        lens = vc.final_lens
+        out = pkv.paged_decode_attention(q, kp, vp, _dev(torch, vc.block_tables), _dev(torch, lens), vc.scale,
+                                         num_splits=1)
+        torch.cuda.synchronize()
+        ref = oracle.decode_attention(q16, kp_ref, vp_ref, vc.block_tables, lens, vc.scale)
+        assert_close(out.cpu().numpy(), ref, "r1 step then decode attention")
+    else:
+        out = pkv.paged_varlen_attention(q, kp, vp, _dev(torch, vc.block_tables), _dev(torch, vc.cu_seqlens_q),
+                                         _dev(torch, vc.pos_offsets), vc.scale)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(7)
+        units = np.stack([rng.integers(0, vc.T, 256), rng.integers(0, vc.Hq, 256)], axis=1).astype(np.int32)
+        units[:4] = [[0, 0], [vc.T - 1, vc.Hq - 1], [511, 3], [512, 17]]
+        ref = oracle.varlen_attention(q16, kp_ref, vp_ref, vc.block_tables, vc.cu_seqlens_q, vc.pos_offsets,
+                                      vc.scale, units=units)
+        got = out.cpu().numpy()[units[:, 0], units[:, 1]]
+        assert_close(got, ref, "r2 step then varlen attention (256 sampled rows)")
