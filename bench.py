@@ -3,7 +3,9 @@
 A step is one pass of the whole path over one batch: the paged KV append of every sequence's newest row, then
 paged decode attention (single pass, or split-K phase 1 + combine, as the workload's dispatch mode says).  By default
 the step is the library's fused decode step (pkv_paged_decode_step: append and attention in one launch); --unfused
-times the two separate entry points (pkv_paged_kv_append, then pkv_paged_decode_attention).  Inputs
+times the two separate entry points (pkv_paged_kv_append, then pkv_paged_decode_attention).  The r workloads start
+one step earlier, from the QKV projection rows: the QKV-to-cache step (split QKV, q/k RMS norm, RoPE, paged-cache
+write), then attention (r1); r2 times that step alone on a chunked-prefill batch.  Inputs
 are seeded synthetic data already resident in HBM; R independent copies rotate between steps so that the ~256 MB
 Infinity Cache cannot hold a step's working set (R=4 for c2).
 
@@ -48,14 +50,22 @@ WORKLOADS = {
            "per sequence, final L~U[512,2048]", 0, 4),
     "w1": ("sliding-window decode on the Llama-3-8B-shaped batch: B=32, Hq=32, Hkv=8, D=128, BS=16, L~U[512,2048], "
            "window 512", 0, 8),
+    "r1": ("Qwen3-8B-shaped decode step from the QKV projection: split QKV + q/k RMSNorm + RoPE + paged-cache write, "
+           "then single-pass attention; B=32, Hq=32, Hkv=8, D=128, BS=16, final L~U[512,2048]", 1, 4),
+    "r2": ("chunked-prefill QKV-to-cache step of the same layer: 4 sequences x 512 new rows after cached prefixes "
+           "U[0,1024], split QKV + q/k RMSNorm + RoPE + paged-cache write (2048 tokens)", 1, 2),
 }
 WINDOWS = {"w1": 512}  # workloads run with pkv_paged_decode_attention_window, and their window
 
 
+QKV_ONLY = {"r2"}  # QKV-step workloads whose step is that kernel alone (a 512-row prefill chunk's attention is not
+#                    decode work)
+
+
 def step_is_fused(config: str, unfused: bool) -> bool:
-    """Whether bench.py times the workload's step as the fused decode step (varlen and sliding-window steps are the
-    append, then attention)."""
-    return not unfused and not config.startswith("v") and config not in WINDOWS
+    """Whether bench.py times the workload's step as the fused decode step (varlen, sliding-window and QKV-step
+    workloads launch their kernels one after the other)."""
+    return not unfused and config[0] not in "vr" and config not in WINDOWS
 
 
 def log(*a):
@@ -64,7 +74,7 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("pkv_kernels.hip", "pkv_api.hip", "pkv_internal.h"):
+    for name in ("pkv_kernels.hip", "pkv_qkv.hip", "pkv_api.hip", "pkv_internal.h"):
         with open(os.path.join(ROOT, "paged_kv_decode_04_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -102,6 +112,14 @@ def _pmc_per_dispatch(path: str, counter: str) -> dict:
     return rows
 
 
+def dominant(config: str, kernel: str) -> bool:
+    """Whether a pkv kernel is part of the workload's dominant kernel (the one `roofline` reports): the QKV kernel
+    for QKV-only workloads, the attention kernels otherwise."""
+    if config in QKV_ONLY:
+        return "qkv" in kernel
+    return "append" not in kernel and "qkv" not in kernel
+
+
 def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy_mib: float) -> dict:
     """HBM traffic per decode step from two counter passes (FETCH_SIZE then WRITE_SIZE, KiB per dispatch), each
     scaled by what the same counter reads for the plain copy kernel (reads and writes copy_mib MiB)."""
@@ -117,7 +135,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy
         factors[counter] = copy_mib * 1024.0 / measured_kib
         for n, v in rows.values():
             if "pkv::" in n:
-                short = n.split("(")[0].replace("void ", "")
+                short = n.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
                 per_kernel.setdefault(short, {}).setdefault(counter, []).append(v)
     step_bytes = 0.0
     kern = {}
@@ -127,15 +145,46 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy
         fb = f * 1024 * factors["FETCH_SIZE"]
         wb = w * 1024 * factors["WRITE_SIZE"]
         kern[short] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": len(cnt.get("FETCH_SIZE", []))}
-        if "append" not in short:
+        if dominant(config, short):
             step_bytes += fb + wb
     out.update({"copy_calibration_mib": copy_mib, "scale_factors": factors, "kernels": kern,
                 "hbm_bytes_per_step": round(step_bytes),
                 "note": "Counters are KiB per dispatch; each is scaled by its reading for the calibration copy kernel "
                         "(torch.neg over %g MiB, which reads and writes %g MiB). hbm_bytes_per_step sums the "
-                        "attention kernels of one step (a separate append launch, if any, excluded)."
-                        % (copy_mib, copy_mib)})
+                        "dominant kernels of one step (%s)."
+                        % (copy_mib, copy_mib, "the QKV-to-cache kernel" if config in QKV_ONLY else
+                           "attention; a separate append or QKV launch, if any, excluded")})
     return out
+
+
+def cpu_baseline_qkv(case, seconds: float, with_attention: bool):
+    """The oracle's QKV step (and, for a decode step, its decode attention on the step's outputs) on the host."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    from paged_kv_decode_04_amd import workloads as W
+    vc = case.varlen
+    nbytes = W.algorithmic_bytes_qkv(case) + (W.algorithmic_bytes_varlen(vc)["attention"] if with_attention else 0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        vp = vc.v_pool.copy()
+        q, k, slots = oracle.qkv_norm_rope_paged(case.qkv, case.q_norm_w, case.k_norm_w, case.cos, case.sin,
+                                                 vc.cu_seqlens_q, vc.pos_offsets, vc.pos_offsets, vc.block_tables,
+                                                 vc.k_pool, vp, case.eps, case.qk_mode)
+        if with_attention:
+            kp = vc.k_pool.copy()
+            k16 = k.astype(np.float16)
+            for t, slot in enumerate(slots):
+                W.set_k_row(kp, int(slot) // vc.BS, slice(None), int(slot) % vc.BS, k16[t])
+            oracle.decode_attention(q.astype(np.float16), kp, vp, vc.block_tables, vc.final_lens, vc.scale,
+                                    threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full step(s) of the workload (QKV step of %d tokens%s, f64) in %.1f s; %.3f steps/s; the "
+                      "QKV step is single-threaded" % (reps, vc.T, ", then decode attention of all %d sequences x %d "
+                      "heads" % (vc.B, vc.Hq) if with_attention else "", el, reps / el)}
 
 
 def cpu_baseline(case, seconds: float, window: int = 0):
@@ -221,8 +270,10 @@ def main(argv=None) -> int:
     splits = default_splits if args.splits is None else args.splits
     R = default_rot if args.rotations is None else args.rotations
     varlen = args.config in W.VARLEN_CONFIGS
+    qkv = args.config in W.QKV_CONFIGS
+    qkv_only = args.config in QKV_ONLY
     window = WINDOWS.get(args.config, 0)
-    make = (W.VARLEN_CONFIGS[args.config] if varlen else
+    make = (W.VARLEN_CONFIGS[args.config] if varlen else W.QKV_CONFIGS[args.config] if qkv else
             (lambda rotation: W.config_c2(rotation=rotation)) if window else W.CONFIGS[args.config])
 
     log("building %d rotation set(s) of %s" % (R, args.config))
@@ -231,12 +282,22 @@ def main(argv=None) -> int:
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     for r in range(R):
         c = make(rotation=r)
-        d = dict(q=t(c.q), k_pool=t(c.k_pool), v_pool=t(c.v_pool), bt=t(c.block_tables), k_new=t(c.k_new),
-                 v_new=t(c.v_new), slots=t(c.slot_mapping), case=c)
+        if qkv:
+            vc = c.varlen
+            d = dict(qkv=t(c.qkv), qw=t(c.q_norm_w), kw=t(c.k_norm_w), cos=t(c.cos), sin=t(c.sin),
+                     k_pool=t(vc.k_pool), v_pool=t(vc.v_pool), bt=t(vc.block_tables), cu=t(vc.cu_seqlens_q),
+                     pos=t(vc.pos_offsets), cl=t(vc.final_lens), case=vc, qkv_case=c)
+            d["q"] = torch.empty((vc.T, vc.Hq, vc.D), dtype=torch.float16, device=dev)
+            d["qkv_bytes"] = W.algorithmic_bytes_qkv(c)
+            d["bytes"] = {"attention": 0 if qkv_only else W.algorithmic_bytes_varlen(vc)["attention"],
+                          "append": d["qkv_bytes"]}
+        else:
+            d = dict(q=t(c.q), k_pool=t(c.k_pool), v_pool=t(c.v_pool), bt=t(c.block_tables), k_new=t(c.k_new),
+                     v_new=t(c.v_new), slots=t(c.slot_mapping), case=c)
         if varlen:
             d["cu"], d["pos"] = t(c.cu_seqlens_q), t(c.pos_offsets)
             d["bytes"] = W.algorithmic_bytes_varlen(c)
-        else:
+        elif not qkv:
             d["cl"] = t(c.context_lens)
             # one new row per sequence for the fused step (rows of empty sequences are never written)
             kn = np.zeros((c.B, c.Hkv, c.D), np.float16)
@@ -248,12 +309,14 @@ def main(argv=None) -> int:
         d["out"] = torch.empty_like(d["q"])
         if r == 0:
             host0 = c
+        elif qkv:
+            c.varlen.k_pool = c.varlen.v_pool = None
         else:
             c.k_pool = c.v_pool = None  # only set 0 stays on the host (for the CPU baseline)
         sets.append(d)
     torch.cuda.synchronize()
     c0 = sets[0]["case"]
-    if varlen:
+    if varlen or qkv_only:
         plan = {"num_splits": splits, "note": "varlen: 0 = the library chooses from the grid size"}
     else:
         plan = pkv.plan_decode(c0.B, c0.Hq, c0.Hkv, c0.D, c0.BS, c0.M, num_splits=splits)
@@ -266,7 +329,15 @@ def main(argv=None) -> int:
     # arguments marshalled once per rotation set (the binding's prepared calls): per-step Python marshalling would
     # otherwise outlast the kernel and leave the GPU idle between steps
     for d in sets:
-        if fused:
+        if qkv:
+            qc = d["qkv_case"]
+            d["append"] = pkv.prepare_split_qkv_norm_rope_into_paged_cache_varlen(
+                d["qkv"], d["qw"], d["kw"], d["cos"], d["sin"], d["k_pool"], d["v_pool"], d["bt"], d["cu"], d["pos"],
+                qc.varlen.Hq, qc.eps, qc.qk_mode, d["q"])
+            d["call"] = (d["append"] if qkv_only else
+                         pkv.prepare_paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
+                                                            qc.varlen.scale, d["out"], num_splits=splits))
+        elif fused:
             d["call"] = pkv.prepare_decode_step(d["q"], d["k_new_all"], d["v_new_all"], d["k_pool"], d["v_pool"],
                                                 d["bt"], d["cl"], d["case"].scale, d["out"], num_splits=splits)
         elif window:
@@ -285,7 +356,7 @@ def main(argv=None) -> int:
                                                            d["case"].scale, d["out"], num_splits=splits)
 
     def step(d):
-        if not fused:
+        if not fused and not qkv_only:
             d["append"]()
         d["call"]()
 
@@ -319,7 +390,7 @@ def main(argv=None) -> int:
     # No event inside a timed region: an event pair costs ~7 us of stream time here, more than a kernel's launch gap.
     # The step region gives value; when a step is one launch (the fused single-pass step) that launch's average
     # duration is the same region / K, otherwise a second region of K back-to-back attention calls gives it.
-    one_launch = fused and plan["num_splits"] == 1
+    one_launch = (fused and plan["num_splits"] == 1) or qkv_only
     if args.graph:
         # 32 consecutive steps over the rotation sets captured once (the capture stream's workspace is sized by an
         # eager step on it first) and replayed; every replay rewrites the same new rows, so the state is stable.
@@ -343,10 +414,21 @@ def main(argv=None) -> int:
         ms_per_step = timed(lambda i: step(sets[i % R]))
         attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["call"]())])
 
+    qkv_info = None
+    if qkv:
+        qkv_ms = ms_per_step if qkv_only else timed(lambda i: sets[i % R]["append"]())
+        qb = float(np.mean([d["qkv_bytes"] for d in sets]))
+        qkv_info = {"kernel": "qkv_cache_kernel (pkv_split_qkv_norm_rope_into_paged_cache_varlen)",
+                    "ms": round(float(qkv_ms), 5), "algorithmic_bytes": int(qb),
+                    "achieved_GBs": round(qb / (qkv_ms * 1e-3) / 1e9, 2),
+                    "frac": round(qb / (qkv_ms * 1e-3) / 1e9 / PEAK_GBS, 4),
+                    "timing": "step region / steps" if qkv_only else "region of back-to-back QKV-step calls / calls"}
+        log("qkv step kernel: %s" % qkv_info)
+
     # bytes per step, averaged over the rotation sets
     step_bytes = np.mean([d["bytes"]["attention"] + d["bytes"]["append"] for d in sets])
     attn_bytes = np.mean([d["bytes"]["attention"] for d in sets])
-    kernel_bytes = step_bytes if fused else attn_bytes  # algorithmic bytes of one launch of the dominant kernel
+    kernel_bytes = step_bytes if fused or qkv_only else attn_bytes  # algorithmic bytes of one dominant launch
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     attn_avg_ms = float(attn_ms.mean())
     achieved = kernel_bytes / (attn_avg_ms * 1e-3) / 1e9
@@ -357,7 +439,8 @@ def main(argv=None) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same workload for ~%.0f s" % args.cpu_seconds)
-        cpu = cpu_baseline(host0, args.cpu_seconds, window)
+        cpu = (cpu_baseline_qkv(host0, args.cpu_seconds, not qkv_only) if qkv else
+               cpu_baseline(host0, args.cpu_seconds, window))
         log("cpu baseline: %s" % cpu)
 
     result = {
@@ -377,7 +460,9 @@ def main(argv=None) -> int:
             "workload": "%s: %s" % (args.config, desc),
             "num_seqs": c0.B, "num_q_heads": c0.Hq, "num_kv_heads": c0.Hkv, "head_dim": c0.D,
             "block_size": c0.BS, "num_splits": splits, "plan": plan, "rotations": R,
-            "step": ("fused (pkv_paged_decode_step)" if fused else
+            "step": ("pkv_split_qkv_norm_rope_into_paged_cache_varlen" if qkv_only else
+                     "pkv_split_qkv_norm_rope_into_paged_cache_varlen + pkv_paged_decode_attention" if qkv else
+                     "fused (pkv_paged_decode_step)" if fused else
                      "pkv_paged_kv_append + pkv_paged_varlen_attention" if varlen else
                      "pkv_paged_kv_append + pkv_paged_decode_attention_window (window %d)" % window if window else
                      "pkv_paged_kv_append + pkv_paged_decode_attention"),
@@ -386,11 +471,13 @@ def main(argv=None) -> int:
         },
         "pct_of_peak": round(100.0 * float(value) / PEAK_GBS, 2),
         "calls_per_s": round(calls_per_s, 1),
-        "tokens_per_s": round(calls_per_s * (c0.T if varlen else c0.B), 1),
+        "tokens_per_s": round(calls_per_s * (c0.T if varlen or qkv else c0.B), 1),
         "kernel_ms": {"mean": round(attn_avg_ms, 5),
-                      "timing": ("step region / steps (one launch per step)" if one_launch else
+                      "timing": ("step region / steps (one launch per step)" if one_launch or qkv_only else
                                  "region of back-to-back attention calls / calls")},
-        "bytes_per_step": {"attention": int(attn_bytes), "append": int(np.mean([d["bytes"]["append"] for d in sets]))},
+        "bytes_per_step": {"attention": int(attn_bytes),
+                           ("qkv_step" if qkv else "append"): int(np.mean([d["bytes"]["append"] for d in sets]))},
+        "qkv_kernel": qkv_info,
         "roofline": {
             "bound": "hbm",
             "achieved": round(float(achieved), 2),

@@ -569,6 +569,9 @@ int qkv_impl(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_no
                     pool.num_kv_heads);
     if (pool.head_dim != 64 && pool.head_dim != 128 && pool.head_dim != 256)
         return fail(PKV_EUNSUPPORTED, "head_dim %d not compiled (64|128|256)", pool.head_dim);
+    if (num_q_heads / pool.num_kv_heads > 16)
+        return fail(PKV_EUNSUPPORTED, "group size %d > 16 query heads per kv head is not compiled",
+                    num_q_heads / pool.num_kv_heads);
     if (pool.block_size % 16 != 0)
         return fail(PKV_EUNSUPPORTED, "block_size %d must be a multiple of 16", pool.block_size);
     if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * pool.block_size > INT32_MAX)
@@ -602,8 +605,8 @@ int qkv_impl(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_no
                     "aligned");
     if (!aligned(block_tables, 4) || (varlen && (!aligned(cu_seqlens_q, 4) || !aligned(pos_offsets, 4))))
         return fail(PKV_EINVAL, "block_tables, cu_seqlens_q and pos_offsets must be 4-byte aligned");
-    if ((int64_t)total_tokens * pool.num_kv_heads > INT32_MAX)
-        return fail(PKV_EINVAL, "total_tokens * num_kv_heads overflows the grid");
+    if ((int64_t)total_tokens + 32 * (int64_t)num_seqs > INT32_MAX || pool.num_kv_heads * 18 > 65535)
+        return fail(PKV_EINVAL, "total_tokens + 32 * num_seqs or num_kv_heads overflows the grid");
     if ((int64_t)total_tokens * (num_q_heads + 2 * pool.num_kv_heads) * pool.head_dim > INT32_MAX)
         return fail(PKV_EINVAL, "qkv holds more than 2^31 values");
     pkv::QkvParams p;
@@ -628,6 +631,16 @@ int qkv_impl(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_no
     p.qk_mode = qk_mode;
     p.rope_base = rope_base;
     p.cache_base = cache_base;
+    // Head slots per workgroup: all G + 2 of a kv head when units hold a row or two (decode), else about four
+    // passes of 256 threads over a full 16-row unit (hpp * 16 rows * head_dim/8 lanes <= 1024).
+    {
+        const int G = p.G;
+        const int cap = 1024 / (2 * pool.head_dim);
+        const bool decode_like = (int64_t)total_tokens <= 2 * (int64_t)num_seqs;
+        int parts = decode_like ? 1 : (G + 2 + cap - 1) / cap;
+        p.hpp = (G + 2 + parts - 1) / parts;
+        p.parts = (G + 2 + p.hpp - 1) / p.hpp;
+    }
     p.eps = eps;
     p.q_out = reinterpret_cast<_Float16 *>(q_out);
     p.k_pool = reinterpret_cast<_Float16 *>(k_pool);

@@ -87,6 +87,7 @@ struct QkvParams {
     int32_t B, T, Hq, Hkv, G, N, M, BS, P;
     int32_t qk_mode;              // 1: RMS-normalise query and key heads first; 0: rotate only
     int32_t rope_base, cache_base;
+    int32_t hpp, parts;           // head slots (query heads, K, V) per workgroup, workgroups per (unit, kv head)
     float eps;
     _Float16 *q_out;              // [T][Hq][D]
     _Float16 *k_pool;

@@ -13,15 +13,21 @@
 // f32 arithmetic, each output rounded once to fp16 (nearest even).
 //
 // Work decomposition (MI355X-first: the pool's 16-row panels are written whole):
-//   * one workgroup per (16-row cache unit holding new rows, kv head h).  The grid has one workgroup per (token,
-//     kv head); the workgroup of the first new token of each unit does the unit, the others return at once.  Its
-//     items are the (new row, head) pairs of the unit: the G query heads of h, key head h and value head h;
-//   * a head row is D/8 lanes, each holding one 16-byte piece.  The sum of squares is reduced across those lanes,
-//     and RoPE's partner dim j + D/2 sits D/16 lanes away, so both are lane exchanges inside the group;
-//   * q goes straight to q_out (16-byte stores, coalesced per head row).  The unit's new K and V rows are staged
-//     in LDS in the pool's panel layout (K [D/8][16][8], V [D][16]); each thread then writes 16-byte chunks of
-//     the two panels, taking rows outside the new range from the old panel, which it loaded at the start (so that
-//     load overlaps everything else).  The pools thus see only whole 16-byte chunks of whole panels -- scattered
+//   * one workgroup per (16-row cache unit holding new rows, kv head h).  The grid's x runs over unit slots, at
+//     least floor(n_s / 16) + 2 of them per sequence (enough for the units its n_s new rows touch, wherever the
+//     first starts); a slot finds its sequence by a wave-wide search of the prefix sums, and slots past a
+//     sequence's last unit return at once.  The unit's head slots of kv head h (its G query heads, key head h,
+//     value head h) are split over `parts` workgroups of `hpp` slots each (the host picks them: one part when
+//     units hold a row or two, as in decode; a few, about four passes of 256 threads each, when units are full);
+//     items are (new row, head slot) pairs.  The first loads are issued at once (the old panels, the unit's rows
+//     of the cos/sin tables and the norm weights into LDS, each thread's qkv pieces of the first pass);
+//   * a head row is D/8 lanes; lane l holds dims 4l .. 4l+3 and D/2 + 4l .. +3, so each RoPE pair (j, j + D/2)
+//     lives in one lane.  The sum of squares is reduced across the group's lanes on the VALU (DPP row rotations,
+//     and a v_permlane16_swap for 32-lane groups);
+//   * q goes straight to q_out (8-byte stores, coalesced per half head row).  The unit's new K rows are staged in
+//     LDS in the pool's panel layout (rows XOR-swizzled per piece), its V rows row-major (padded rows); each
+//     thread then writes 16-byte chunks of the two panels (V transposed on the way), taking rows outside the new
+//     range from the old panel, which it loaded at the start (so that load overlaps everything else).  The pools thus see only whole 16-byte chunks of whole panels -- scattered
 //     2-byte V stores and 16-byte K row pieces cost far more at the memory than their bytes.
 //
 // A unit's other rows are rewritten with their own values: no other work may write the panel meanwhile (the
@@ -40,153 +46,298 @@ namespace pkv {
 namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+// DPP lane patterns (GFX9 encodings of the dpp_ctrl field)
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor = 0x120;     // row_ror:n = 0x120 + n (rotate within a row of 16 lanes)
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror (lane i <-> 7 - i within each 8)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LPR lanes of a head row (aligned groups of 8, 16 or 32 lanes), on the VALU: DPP within 16-lane rows,
+// v_permlane16_swap across the two rows of a 32-lane group.  Every lane of the group gets the total.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+    if (LPR == 8) {
+        x += dpp<kDppHalfMirror>(x);  // x_i + x_{7-i}: symmetric within the 8
+        x += dpp<kDppXor1>(x);
+        x += dpp<kDppXor2>(x);         // the quad and its mirror: all 8
+    } else {
+        x += dpp<kDppRowRor + 8>(x);
+        x += dpp<kDppRowRor + 4>(x);
+        x += dpp<kDppRowRor + 2>(x);
+        x += dpp<kDppRowRor + 1>(x);   // all 16 of the row
+        if (LPR == 32) {
+            auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+        }
+    }
+    return x;
+}
+
+constexpr int kThreads = 256;
+constexpr int kBatch = 1;  // passes whose qkv pieces are loaded together (more measured no faster)
+
+// Sequence s's unit slots are [V_s / 16, V_{s+1} / 16) with V_s = cu[s] + 32 s: at least floor(n_s / 16) + 2 slots
+// for its n_s new rows, enough for the 16-row cache units they touch wherever the first one starts.  The slot
+// count is (T + 32 B) / 16, a host value, and a slot finds its sequence without a table.
+__device__ __forceinline__ int slot_key(const int32_t *cu, int s) { return cu[s] + 32 * s; }
+
+// The sequence of unit slot g -- the last s in [0, B] with slot_key(s) <= 16 g + 15 -- with its first token, new
+// token count and first position.  The 64 lanes of the wave test 64 evenly spaced candidates per round; with
+// B < 64 one round loads every candidate and its position at once, and the answer's neighbours come from lane
+// exchanges.  Keys increase, so the lanes that pass are a prefix; with malformed prefix sums s still lies in
+// [0, B].
+struct SeqOfSlot {
+    int s, first, n, pos;
+};
+
+__device__ __forceinline__ SeqOfSlot find_sequence(const int32_t *cu, const int32_t *pos, int B, int g) {
+    const int lane = threadIdx.x & 63;
+    const int target = 16 * g + 15;
+    SeqOfSlot r;
+    if (B < 64) {
+        const int c = cu[lane <= B ? lane : B];
+        const int q = pos[lane < B ? lane : B - 1];
+        const bool pass = lane <= B && c + 32 * lane <= target;
+        int k = __popcll(__ballot(pass)) - 1;
+        k = k > 0 ? k : 0;
+        r.s = k;
+        r.first = __shfl(c, k, 64);
+        r.n = __shfl(c, k + 1 <= B ? k + 1 : B, 64) - r.first;
+        r.pos = __shfl(q, k < B ? k : B - 1, 64);
+        return r;
+    }
+    int lo = 0, hi = B;
+    while (lo < hi) {
+        const int stride = (hi - lo + 64) / 64;
+        const int idx = lo + lane * stride;
+        const bool pass = idx <= hi && slot_key(cu, idx) <= target;
+        const int k = __popcll(__ballot(pass)) - 1;
+        lo += (k > 0 ? k : 0) * stride;
+        hi = min(hi, lo + stride - 1);
+    }
+    r.s = lo;
+    if (lo < B) {
+        r.first = cu[lo];
+        r.n = cu[lo + 1] - r.first;
+        r.pos = pos[lo];
+    }
+    return r;
+}
 
 template <int D>
-__global__ __launch_bounds__(256) void qkv_cache_kernel(QkvParams p) {
-    constexpr int LPR = D / 8;       // lanes per head row, one 16-byte piece each
-    constexpr int PARTNER = D / 16;  // lane distance from dim j to dim j + D/2
+__global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
+    constexpr int LPR = D / 8;       // lanes per head row, 8 dims each
     constexpr int HALF = D / 2;
     constexpr int CHUNKS = 2 * D;    // 16-byte chunks of one 16-row panel (16 * D halves)
-    constexpr int CPT = (CHUNKS + 255) / 256;
-    __shared__ __attribute__((aligned(16))) _Float16 sk[16 * D];  // new K rows, panel layout [D/8][16][8]
-    __shared__ __attribute__((aligned(16))) _Float16 sv[16 * D];  // new V rows, panel layout [D][16]
+    constexpr int CPT = (CHUNKS + kThreads - 1) / kThreads;
+    constexpr int TAB = 16 * HALF / 4;  // float4 chunks of 16 rows of one table
+    constexpr int VS = D + 4;  // row stride of the V staging (the pad spreads a dim's 16 rows over distinct banks)
+    // new K rows in the panel layout [D/8][16][8], row r of piece c kept in slot r ^ (c % 16) so that one row's
+    // pieces (written by one head row's lanes) and one piece's rows (read back per 16-byte chunk) hit distinct banks
+    __shared__ __attribute__((aligned(16))) _Float16 sk[16 * D];
+    __shared__ __attribute__((aligned(16))) _Float16 sv[16 * VS];  // new V rows, row-major [16][D + 4]
+    __shared__ __attribute__((aligned(16))) float scos[16 * HALF];  // the unit's rows of the tables
+    __shared__ __attribute__((aligned(16))) float ssin[16 * HALF];
+    __shared__ __attribute__((aligned(16))) _Float16 sw[2 * D];     // q_norm_w, k_norm_w
 
-    const int m = (int)(blockIdx.x / (unsigned)p.Hkv);
-    const int h = (int)(blockIdx.x - (unsigned)m * p.Hkv);
+    const int g = (int)blockIdx.x;                  // unit slot
+    const int h = (int)blockIdx.y / p.parts;        // kv head
+    const int part = (int)blockIdx.y - h * p.parts;  // which of its head slots (G query heads, K, V) this group does
     int s = 0, first = 0, n = p.T, rope0 = p.rope_base, cache0 = p.cache_base;
     if (p.cu_seqlens_q) {
-        // the sequence of token m: the last s with cu[s] <= m
-        int lo = 0, hi = p.B;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.cu_seqlens_q[mid] <= m)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        s = lo;
-        if (s >= p.B)
+        const SeqOfSlot q = find_sequence(p.cu_seqlens_q, p.pos_offsets, p.B, g);
+        if (q.s >= p.B)
             return;
-        first = p.cu_seqlens_q[s];
-        n = p.cu_seqlens_q[s + 1] - first;
-        rope0 = cache0 = p.pos_offsets[s];
+        s = q.s;
+        first = q.first;
+        n = q.n;
+        rope0 = cache0 = q.pos;
     }
-    const int i = m - first;
-    if (i < 0 || i >= n)
+    // this slot's 16-row cache unit and the new rows in it
+    const int j = g - ((first + 32 * s) >> 4);
+    const int64_t u = (int64_t)(cache0 >> 4) + j;
+    const int64_t lo = max((int64_t)cache0, 16 * u);
+    const int64_t hi = min((int64_t)cache0 + n, 16 * u + 16);
+    if (j < 0 || lo >= hi)
         return;
-    const int row = cache0 + i;  // cache row of token m
-    const int r0 = row & 15;     // its row inside the 16-row unit
-    if (i > 0 && r0 != 0)
-        return;                  // not the unit's first new token: another workgroup writes this unit
-    int rows = 16 - r0;          // new rows of the unit, from r0 on
-    rows = rows < n - i ? rows : n - i;
-    rows = rows < p.T - m ? rows : p.T - m;
-    const int64_t rp0 = (int64_t)rope0 + i;
-    if (rp0 < 0 || rp0 + rows > p.P)
-        return;                  // positions outside the tables: the unit's tokens are not written
+    const int r0 = (int)(lo - 16 * u);  // first new row inside the unit
+    int rows = (int)(hi - lo);
+    const int i0 = (int)(lo - cache0);  // its index among the sequence's new tokens
+    const int m0 = first + i0;          // its token
+    rows = rows < p.T - m0 ? rows : p.T - m0;
+    const int64_t rp0 = (int64_t)rope0 + i0;
+    if (m0 < 0 || rows <= 0 || rp0 < 0 || rp0 + rows > p.P)
+        return;  // positions outside the tables (or malformed prefix sums): the unit's tokens are not written
 
-    int64_t panel = -1;          // the unit's panel (element offset of its first half) in both pools
-    if (row >= 0 && (int64_t)row < (int64_t)p.M * p.BS) {
+    // head slots [hs0, hs1) of kv head h: < G query heads, G the key head, G + 1 the value head
+    const int hs0 = part * p.hpp;
+    const int hs1 = min(hs0 + p.hpp, p.G + 2);
+    const int nh = hs1 - hs0;
+    const bool has_k = hs0 <= p.G && p.G < hs1;
+    const bool has_v = hs1 == p.G + 2;
+    int64_t panel = -1;  // the unit's panel (element offset of its first half) in both pools
+    if ((has_k || has_v) && lo >= 0 && lo < (int64_t)p.M * p.BS) {
+        const int row = (int)lo;
         const int blk = p.block_tables[(int64_t)s * p.M + row / p.BS];
         if (blk >= 0 && blk < p.N)
             panel = (((int64_t)blk * p.Hkv + h) * p.BS + (row % p.BS - r0)) * D;
     }
     const bool whole = r0 == 0 && rows == 16;
     const int tid = threadIdx.x;
+    const int width = (p.Hq + 2 * p.Hkv) * D;
+    const int lanes = rows * nh * LPR;
+    const bool rotates = hs0 <= p.G;  // the group holds a query or key head
 
-    // old panel contents first: rows outside [r0, r0 + rows) are written back unchanged
+    auto source = [&](int idx, int &rr, int &hs, int &piece) {
+        const int item = idx / LPR;
+        piece = idx - item * LPR;
+        rr = item / nh;
+        hs = hs0 + (item - rr * nh);
+    };
+    // lane `piece` of a head row holds dims 4 piece .. +4 and D/2 + 4 piece .. +4: each RoPE pair in one lane
+    auto fetch = [&](int idx) {
+        int rr, hs, piece;
+        source(idx, rr, hs, piece);
+        const int head = hs < p.G ? h * p.G + hs : (hs == p.G ? p.Hq + h : p.Hq + p.Hkv + h);
+        const _Float16 *src = p.qkv + (int64_t)(m0 + rr) * width + (int64_t)head * D + 4 * piece;
+        const h4 a = *reinterpret_cast<const h4 *>(src);
+        const h4 b = *reinterpret_cast<const h4 *>(src + HALF);
+        return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    };
+
+    // The first batch of global loads at once: the old panels (rows outside [r0, r0 + rows) are written back
+    // unchanged), the unit's rows of the cos/sin tables and the norm weights (to LDS), this thread's qkv pieces.
     h8 ok[CPT], ov[CPT];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int c = tid + 256 * j;
-        if (panel >= 0 && !whole && c < CHUNKS) {
-            ok[j] = *reinterpret_cast<const h8 *>(p.k_pool + panel + 8 * c);
-            ov[j] = *reinterpret_cast<const h8 *>(p.v_pool + panel + 8 * c);
+    for (int c = 0; c < CPT; ++c) {
+        const int q = tid + kThreads * c;
+        if (panel >= 0 && !whole && q < CHUNKS) {
+            if (has_k)
+                ok[c] = *reinterpret_cast<const h8 *>(p.k_pool + panel + 8 * q);
+            if (has_v)
+                ov[c] = *reinterpret_cast<const h8 *>(p.v_pool + panel + 8 * q);
         }
     }
+    if (rotates) {
+        for (int c = tid; c < 2 * TAB; c += kThreads) {
+            const int t = c < TAB ? c : c - TAB;  // float4 t of the unit's 16 table rows
+            if (t < rows * (HALF / 4)) {
+                const float *src = (c < TAB ? p.cos_t : p.sin_t) + rp0 * HALF + 4 * t;
+                *reinterpret_cast<float4 *>((c < TAB ? scos : ssin) + 4 * t) =
+                    *reinterpret_cast<const float4 *>(src);
+            }
+        }
+        if (p.qk_mode == 1 && tid < 2 * LPR)
+            *reinterpret_cast<h8 *>(sw + 8 * tid) =
+                *reinterpret_cast<const h8 *>((tid < LPR ? p.q_norm_w : p.k_norm_w) + 8 * (tid % LPR));
+    }
+    h8 raw[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+        if (b * kThreads + tid < lanes)
+            raw[b] = fetch(b * kThreads + tid);
+    __syncthreads();
 
-    const int width = (p.Hq + 2 * p.Hkv) * D;
-    const int heads = p.G + 2;
-    const int lanes = rows * heads * LPR;
     const float inv_d = 1.0f / (float)D;
-    for (int base = 0; base < lanes; base += 256) {
-        const int idx = base + tid;
-        if (idx >= lanes)
-            break;  // lanes >= idx form whole head-row groups, so every exchange below has its partner
-        const int item = idx / LPR;
-        const int piece = idx - item * LPR;
-        const int rr = item / heads;
-        const int hh = item - rr * heads;
-        const int tok = m + rr;
-        const int rin = r0 + rr;
-        const int head = hh < p.G ? h * p.G + hh : (hh == p.G ? p.Hq + h : p.Hq + p.Hkv + h);
-        const h8 raw = *reinterpret_cast<const h8 *>(p.qkv + (int64_t)tok * width + (int64_t)head * D + 8 * piece);
-        if (hh > p.G) {
-            // value head: copied into the staged V panel (dim-major, 16 rows per dim)
+    for (int base = 0; base < lanes; base += kBatch * kThreads) {
+        if (base > 0) {
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                if (base + b * kThreads + tid < lanes)
+                    raw[b] = fetch(base + b * kThreads + tid);
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int idx = base + b * kThreads + tid;
+            if (idx >= lanes)
+                break;  // lanes below `lanes` form whole head-row groups, so every group sum has all its lanes
+            int rr, hs, piece;
+            source(idx, rr, hs, piece);
+            const int rin = r0 + rr;
+            if (hs > p.G) {
+                // value head: staged row-major, transposed into the panel layout on the way out
+                const h8 v = raw[b];
+                *reinterpret_cast<h4 *>(sv + rin * VS + 4 * piece) = h4{v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<h4 *>(sv + rin * VS + HALF + 4 * piece) = h4{v[4], v[5], v[6], v[7]};
+                continue;
+            }
+            float x[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                sv[(8 * piece + e) * 16 + rin] = raw[e];
-            continue;
+                x[e] = (float)raw[b][e];
+            if (p.qk_mode == 1) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ss += x[e] * x[e];
+                const float r = rsqrtf(group_sum<LPR>(ss) * inv_d + p.eps);
+                const _Float16 *wp = sw + (hs < p.G ? 0 : D) + 4 * piece;
+                const h4 wa = *reinterpret_cast<const h4 *>(wp);
+                const h4 wb = *reinterpret_cast<const h4 *>(wp + HALF);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = x[e] * r * (float)wa[e];
+                    x[4 + e] = x[4 + e] * r * (float)wb[e];
+                }
+            }
+            const float4 c = *reinterpret_cast<const float4 *>(scos + rr * HALF + 4 * piece);
+            const float4 sn = *reinterpret_cast<const float4 *>(ssin + rr * HALF + 4 * piece);
+            const float cs[4] = {c.x, c.y, c.z, c.w};
+            const float ss4[4] = {sn.x, sn.y, sn.z, sn.w};
+            h4 ya, yb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ya[e] = (_Float16)(x[e] * cs[e] - x[4 + e] * ss4[e]);
+                yb[e] = (_Float16)(x[4 + e] * cs[e] + x[e] * ss4[e]);
+            }
+            if (hs < p.G) {
+                _Float16 *dst = p.q_out + ((int64_t)(m0 + rr) * p.Hq + h * p.G + hs) * D + 4 * piece;
+                *reinterpret_cast<h4 *>(dst) = ya;
+                *reinterpret_cast<h4 *>(dst + HALF) = yb;
+            } else {
+                // K panel [D/8][16][8]: dims 4 piece .. +4 are half of 8-wide piece (4 piece) / 8
+                const int ca = (4 * piece) / 8, cb = (HALF + 4 * piece) / 8;
+                *reinterpret_cast<h4 *>(sk + (ca * 16 + (rin ^ (ca & 15))) * 8 + (4 * piece) % 8) = ya;
+                *reinterpret_cast<h4 *>(sk + (cb * 16 + (rin ^ (cb & 15))) * 8 + (4 * piece) % 8) = yb;
+            }
         }
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            x[e] = (float)raw[e];
-        if (p.qk_mode == 1) {
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                ss += x[e] * x[e];
-#pragma unroll
-            for (int o = 1; o < LPR; o <<= 1)
-                ss += __shfl_xor(ss, o, 64);
-            const float r = rsqrtf(ss * inv_d + p.eps);
-            const h8 w = *reinterpret_cast<const h8 *>((hh < p.G ? p.q_norm_w : p.k_norm_w) + 8 * piece);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                x[e] = x[e] * r * (float)w[e];
-        }
-        const int64_t t0 = (rp0 + rr) * HALF + (8 * piece) % HALF;
-        const float4 c0 = *reinterpret_cast<const float4 *>(p.cos_t + t0);
-        const float4 c1 = *reinterpret_cast<const float4 *>(p.cos_t + t0 + 4);
-        const float4 s0 = *reinterpret_cast<const float4 *>(p.sin_t + t0);
-        const float4 s1 = *reinterpret_cast<const float4 *>(p.sin_t + t0 + 4);
-        const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const bool low = piece < PARTNER;  // this lane holds dims j < D/2; its partner holds j + D/2
-        h8 y;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xp = __shfl_xor(x[e], PARTNER, 64);
-            y[e] = (_Float16)(low ? x[e] * cs[e] - xp * sn[e] : x[e] * cs[e] + xp * sn[e]);
-        }
-        if (hh < p.G)
-            *reinterpret_cast<h8 *>(p.q_out + ((int64_t)tok * p.Hq + head) * D + 8 * piece) = y;
-        else
-            *reinterpret_cast<h8 *>(sk + (piece * 16 + rin) * 8) = y;
     }
     __syncthreads();
     if (panel < 0)
         return;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int c = tid + 256 * j;
-        if (c >= CHUNKS)
+    for (int c = 0; c < CPT; ++c) {
+        const int q = tid + kThreads * c;
+        if (q >= CHUNKS)
             break;
-        // K chunk c: piece c / 16 of row c % 16
-        const int kr = c & 15;
-        const h8 kn = *reinterpret_cast<const h8 *>(sk + 8 * c);
-        const bool knew = whole || (kr >= r0 && kr < r0 + rows);
-        *reinterpret_cast<h8 *>(p.k_pool + panel + 8 * c) = knew ? kn : ok[j];
-        // V chunk c: dim c / 2, rows 8 * (c % 2) .. + 8
-        h8 vn = *reinterpret_cast<const h8 *>(sv + 8 * c);
-        if (!whole) {
-            const int vr = 8 * (c & 1);
+        if (has_k) {
+            // K chunk q: piece q / 16 of row q % 16
+            const int kr = q & 15, kc = q >> 4;
+            const h8 kn = *reinterpret_cast<const h8 *>(sk + (kc * 16 + (kr ^ (kc & 15))) * 8);
+            const bool knew = whole || (kr >= r0 && kr < r0 + rows);
+            *reinterpret_cast<h8 *>(p.k_pool + panel + 8 * q) = knew ? kn : ok[c];
+        }
+        if (has_v) {
+            // V chunk q: dim q / 2, rows 8 * (q % 2) .. + 8
+            const int vd = q >> 1, vr = 8 * (q & 1);
+            h8 vn;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                vn[e] = (vr + e >= r0 && vr + e < r0 + rows) ? vn[e] : ov[j][e];
+                vn[e] = sv[(vr + e) * VS + vd];
+            if (!whole) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    vn[e] = (vr + e >= r0 && vr + e < r0 + rows) ? vn[e] : ov[c][e];
+            }
+            *reinterpret_cast<h8 *>(p.v_pool + panel + 8 * q) = vn;
         }
-        *reinterpret_cast<h8 *>(p.v_pool + panel + 8 * c) = vn;
     }
 }
 
@@ -195,7 +346,8 @@ __global__ __launch_bounds__(256) void qkv_cache_kernel(QkvParams p) {
 hipError_t launch_qkv_cache(const QkvParams &p, int head_dim, hipStream_t stream) {
     if (p.T <= 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((int64_t)p.T * p.Hkv)), block(256);
+    const int64_t slots = ((int64_t)p.T + 32 * (int64_t)(p.cu_seqlens_q ? p.B : 1)) / 16;
+    const dim3 grid((unsigned)slots, (unsigned)(p.Hkv * p.parts)), block(kThreads);
     switch (head_dim) {
     case 64: hipLaunchKernelGGL(qkv_cache_kernel<64>, grid, block, 0, stream, p); break;
     case 128: hipLaunchKernelGGL(qkv_cache_kernel<128>, grid, block, 0, stream, p); break;
