@@ -4,8 +4,9 @@ A step is one pass of the whole path over one batch: the paged KV append of ever
 paged decode attention (single pass, or split-K phase 1 + combine, as the workload's dispatch mode says).  By default
 the step is the library's fused decode step (pkv_paged_decode_step: append and attention in one launch); --unfused
 times the two separate entry points (pkv_paged_kv_append, then pkv_paged_decode_attention).  The r workloads start
-one step earlier, from the QKV projection rows: the QKV-to-cache step (split QKV, q/k RMS norm, RoPE, paged-cache
-write), then attention (r1); r2 times that step alone on a chunked-prefill batch.  Inputs
+one step earlier, from the QKV projection rows: r1 is the decode step from those rows in one launch
+(pkv_paged_decode_step_qkv: q/k RMS norm, RoPE, the new K/V rows written, attention; --unfused: the QKV-to-cache
+kernel, then attention); r2 times the QKV-to-cache kernel alone on a chunked-prefill batch.  Inputs
 are seeded synthetic data already resident in HBM; R independent copies rotate between steps so that the ~256 MB
 Infinity Cache cannot hold a step's working set (R=4 for c2).
 
@@ -63,9 +64,10 @@ QKV_ONLY = {"r2"}  # QKV-step workloads whose step is that kernel alone (a 512-r
 
 
 def step_is_fused(config: str, unfused: bool) -> bool:
-    """Whether bench.py times the workload's step as the fused decode step (varlen, sliding-window and QKV-step
-    workloads launch their kernels one after the other)."""
-    return not unfused and config[0] not in "vr" and config not in WINDOWS
+    """Whether bench.py times the workload's step as one fused launch (pkv_paged_decode_step, or
+    pkv_paged_decode_step_qkv for a decode step from QKV rows); varlen, sliding-window and QKV-only workloads launch
+    their kernels one after the other."""
+    return not unfused and config[0] != "v" and config not in WINDOWS and config not in QKV_ONLY
 
 
 def log(*a):
@@ -334,9 +336,15 @@ def main(argv=None) -> int:
             d["append"] = pkv.prepare_split_qkv_norm_rope_into_paged_cache_varlen(
                 d["qkv"], d["qw"], d["kw"], d["cos"], d["sin"], d["k_pool"], d["v_pool"], d["bt"], d["cu"], d["pos"],
                 qc.varlen.Hq, qc.eps, qc.qk_mode, d["q"])
-            d["call"] = (d["append"] if qkv_only else
-                         pkv.prepare_paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
-                                                            qc.varlen.scale, d["out"], num_splits=splits))
+            if qkv_only:
+                d["call"] = d["append"]
+            elif fused:  # one launch: q and the new K/V rows formed in the attention kernel's prologue
+                d["call"] = pkv.prepare_decode_step_qkv(d["qkv"], d["qw"], d["kw"], d["cos"], d["sin"], d["k_pool"],
+                                                        d["v_pool"], d["bt"], d["cl"], qc.varlen.Hq, qc.varlen.scale,
+                                                        qc.eps, qc.qk_mode, d["q"], d["out"], num_splits=splits)
+            else:
+                d["call"] = pkv.prepare_paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
+                                                               qc.varlen.scale, d["out"], num_splits=splits)
         elif fused:
             d["call"] = pkv.prepare_decode_step(d["q"], d["k_new_all"], d["v_new_all"], d["k_pool"], d["v_pool"],
                                                 d["bt"], d["cl"], d["case"].scale, d["out"], num_splits=splits)
@@ -416,6 +424,7 @@ def main(argv=None) -> int:
 
     qkv_info = None
     if qkv:
+        # the QKV kernel on its own (for a fused step: what the step's prologue replaces)
         qkv_ms = ms_per_step if qkv_only else timed(lambda i: sets[i % R]["append"]())
         qb = float(np.mean([d["qkv_bytes"] for d in sets]))
         qkv_info = {"kernel": "qkv_cache_kernel (pkv_split_qkv_norm_rope_into_paged_cache_varlen)",
@@ -461,6 +470,7 @@ def main(argv=None) -> int:
             "num_seqs": c0.B, "num_q_heads": c0.Hq, "num_kv_heads": c0.Hkv, "head_dim": c0.D,
             "block_size": c0.BS, "num_splits": splits, "plan": plan, "rotations": R,
             "step": ("pkv_split_qkv_norm_rope_into_paged_cache_varlen" if qkv_only else
+                     "fused (pkv_paged_decode_step_qkv)" if qkv and fused else
                      "pkv_split_qkv_norm_rope_into_paged_cache_varlen + pkv_paged_decode_attention" if qkv else
                      "fused (pkv_paged_decode_step)" if fused else
                      "pkv_paged_kv_append + pkv_paged_varlen_attention" if varlen else

@@ -198,6 +198,40 @@ int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16
                           int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
                           int32_t max_context_hint, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * pkv_paged_decode_step_qkv -- the decode step from the QKV projection rows:
+ *   exactly pkv_split_qkv_norm_rope_into_paged_cache_varlen with one new token
+ *   per sequence (token s = sequence s, at position L_s - 1 where L_s =
+ *   context_lens[s] counts the rows after the append), followed by
+ *   pkv_paged_decode_attention over the updated pools with the rotated q.
+ *   [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ *   split_qkv_norm_rope_into_paged_cache_varlen, then paged_decode_attention;
+ *   kapsl-backends 0.1.1, src/gguf_native.rs: forward_batch_decode_greedy,
+ *   where the new token's row is written before the attention reads it]
+ *   qkv: [num_seqs][(num_q_heads + 2*Hkv) * head_dim] fp16; q_norm_w,
+ *   k_norm_w, cos_table, sin_table, max_positions, eps, qk_mode as in
+ *   pkv_split_qkv_norm_rope_into_paged_cache_varlen.  q_out: [num_seqs]
+ *   [num_q_heads][head_dim] fp16, receives the rotated queries.  Other
+ *   arguments as pkv_paged_decode_attention.  Sequences with L_s = 0 are
+ *   skipped (no row written, q_out row untouched, output zeros); L_s past
+ *   max_positions gives unspecified results (never an access outside the
+ *   tables).
+ *   Launches: when the attention grid fits one round of the device's CUs, one
+ *   launch forms q and the new K/V rows in its prologue (the 16-row panel
+ *   holding each new row is written back whole, as in pkv_paged_decode_step);
+ *   otherwise the QKV kernel, then attention.  The two routes agree to within
+ *   f32 summation order (the RMS sums are reduced in different orders), not
+ *   bit for bit.  The block holding each sequence's newest row must belong to
+ *   that sequence alone.
+ *   Errors: as pkv_paged_decode_attention, plus those of the QKV arguments.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_decode_step_qkv(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w,
+                              const float *cos_table, const float *sin_table, int32_t max_positions, float eps,
+                              int32_t qk_mode, uint16_t *q_out, uint16_t *k_pool, uint16_t *v_pool,
+                              pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                              uint16_t *out, int32_t num_splits, int32_t max_context_hint, void *stream);
+
 /* Same computation with a caller-chosen launch plan (from pkv_plan_decode, or
  * tuned by the caller: split count, fixed-size block chunks, waves per
  * workgroup).  The plan is checked (PKV_EINVAL / PKV_EUNSUPPORTED): num_splits

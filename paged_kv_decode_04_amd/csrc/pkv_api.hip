@@ -303,16 +303,66 @@ int check_plan(const pkv_decode_plan &plan, int32_t num_seqs, int32_t num_q_head
     return PKV_OK;
 }
 
+// Where the decode step from QKV rows takes q and the new K/V rows (pkv_paged_decode_step_qkv).
+struct QkvSource {
+    const uint16_t *qkv;
+    const uint16_t *q_norm_w;
+    const uint16_t *k_norm_w;
+    const float *cos_t;
+    const float *sin_t;
+    int32_t P;
+    int32_t qk_mode;
+    float eps;
+    uint16_t *q_out;
+};
+
+// Checks of the QKV-row arguments shared by the QKV entry points.
+int check_qkv_source(const QkvSource &q, int32_t head_dim) {
+    if (q.P <= 0)
+        return fail(PKV_EINVAL, "max_positions must be > 0 (got %d)", q.P);
+    if (q.qk_mode != 0 && q.qk_mode != 1)
+        return fail(PKV_EINVAL, "qk_mode must be 0 (rotate only) or 1 (RMS norm, then rotate); got %d", q.qk_mode);
+    if (!(q.eps >= 0.f) || !isfinite(q.eps))
+        return fail(PKV_EINVAL, "eps must be finite and >= 0");
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+        return fail(PKV_EUNSUPPORTED, "head_dim %d not compiled (64|128|256)", head_dim);
+    return PKV_OK;
+}
+
+int check_qkv_pointers(const QkvSource &q) {
+    if (!q.qkv || !q.cos_t || !q.sin_t || !q.q_out || (q.qk_mode == 1 && (!q.q_norm_w || !q.k_norm_w)))
+        return fail(PKV_EINVAL, "null device pointer (qkv=%p cos=%p sin=%p q_out=%p q_norm_w=%p k_norm_w=%p)", q.qkv,
+                    q.cos_t, q.sin_t, q.q_out, q.q_norm_w, q.k_norm_w);
+    if (!aligned(q.qkv, 16) || !aligned(q.q_out, 16) || !aligned(q.cos_t, 16) || !aligned(q.sin_t, 16) ||
+        (q.qk_mode == 1 && (!aligned(q.q_norm_w, 16) || !aligned(q.k_norm_w, 16))))
+        return fail(PKV_EINVAL, "qkv, q_out, the cos/sin tables and the norm weights must be 16-byte aligned");
+    return PKV_OK;
+}
+
 // Enqueues the kernels of a checked plan.
 int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
              const pkv_pool_desc &pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
              void *workspace, size_t workspace_bytes, bool library_ws, hipStream_t stream,
-             const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr, int32_t window = 0) {
+             const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr, int32_t window = 0,
+             const QkvSource *qsrc = nullptr) {
     pkv::DecodeParams p = decode_params(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
                                         num_q_heads, scale);
     p.window = window;
     p.out = reinterpret_cast<_Float16 *>(out);
+    if (qsrc) {  // decode step from QKV rows, one launch: q and the new rows are formed in the kernel
+        p.qkv = reinterpret_cast<const _Float16 *>(qsrc->qkv);
+        p.q_norm_w = reinterpret_cast<const _Float16 *>(qsrc->q_norm_w);
+        p.k_norm_w = reinterpret_cast<const _Float16 *>(qsrc->k_norm_w);
+        p.cos_t = qsrc->cos_t;
+        p.sin_t = qsrc->sin_t;
+        p.P = qsrc->P;
+        p.qk_mode = qsrc->qk_mode;
+        p.eps = qsrc->eps;
+        p.q_out = reinterpret_cast<_Float16 *>(qsrc->q_out);
+        p.k_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
+        p.v_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
+    }
     if (k_new) {  // fused decode step: the pools are written too
         p.k_new = reinterpret_cast<const _Float16 *>(k_new);
         p.v_new = reinterpret_cast<const _Float16 *>(v_new);
@@ -373,7 +423,7 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
                 int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
                 int32_t max_context_hint, const pkv_decode_plan *given, void *workspace, size_t workspace_bytes,
                 bool library_ws, hipStream_t stream, const uint16_t *k_new = nullptr,
-                const uint16_t *v_new = nullptr, int32_t window = 0) {
+                const uint16_t *v_new = nullptr, int32_t window = 0, const QkvSource *qsrc = nullptr) {
     int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
     if (rc)
         return rc;
@@ -405,6 +455,39 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     }
     if (rc)
         return rc;
+    if (qsrc && (int64_t)num_seqs * pool.num_kv_heads * plan.num_splits > facts.cu_count) {
+        // The step from QKV rows over more than one round of CUs: the QKV kernel (one new token per sequence, at
+        // row L-1), then attention reading its q_out.
+        pkv::QkvParams a;
+        memset(&a, 0, sizeof a);
+        a.qkv = reinterpret_cast<const _Float16 *>(qsrc->qkv);
+        a.q_norm_w = reinterpret_cast<const _Float16 *>(qsrc->q_norm_w);
+        a.k_norm_w = reinterpret_cast<const _Float16 *>(qsrc->k_norm_w);
+        a.cos_t = qsrc->cos_t;
+        a.sin_t = qsrc->sin_t;
+        a.block_tables = block_tables;
+        a.decode_lens = context_lens;
+        a.B = a.T = num_seqs;
+        a.Hq = num_q_heads;
+        a.Hkv = pool.num_kv_heads;
+        a.G = num_q_heads / pool.num_kv_heads;
+        a.N = pool.num_blocks;
+        a.M = max_blocks_per_seq;
+        a.BS = pool.block_size;
+        a.P = qsrc->P;
+        a.qk_mode = qsrc->qk_mode;
+        a.eps = qsrc->eps;
+        a.hpp = a.G + 2;
+        a.parts = 1;
+        a.q_out = reinterpret_cast<_Float16 *>(qsrc->q_out);
+        a.k_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
+        a.v_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
+        hipError_t e = pkv::launch_qkv_cache(a, pool.head_dim, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "qkv-to-cache kernel launch");
+        q = qsrc->q_out;
+        qsrc = nullptr;
+    }
     if (k_new && (int64_t)num_seqs * pool.num_kv_heads * plan.num_splits > facts.cu_count) {
         // Decode step over more workgroups than one round of the device's CUs: the append kernel, then attention.
         // Writes issued from inside a long, read-saturated launch cost far more than a launch of their own.
@@ -428,7 +511,8 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
         k_new = v_new = nullptr;
     }
     return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, k_new, v_new, window);
+                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, k_new, v_new, window,
+                    qsrc);
 }
 
 // Paged varlen attention (several new query rows per sequence): plan, checks, launches.
@@ -871,6 +955,29 @@ int pkv_split_qkv_norm_rope_into_paged_cache(const uint16_t *qkv, const uint16_t
     return qkv_impl(qkv, q_norm_w, k_norm_w, cos_table, sin_table, max_positions, q_out, k_pool, v_pool, pool,
                     block_table, max_blocks_per_seq, nullptr, nullptr, 1, num_tokens, num_q_heads, false,
                     pos_offset, cache_len, eps, qk_mode, static_cast<hipStream_t>(stream));
+}
+
+int pkv_paged_decode_step_qkv(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w,
+                              const float *cos_table, const float *sin_table, int32_t max_positions, float eps,
+                              int32_t qk_mode, uint16_t *q_out, uint16_t *k_pool, uint16_t *v_pool,
+                              pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                              uint16_t *out, int32_t num_splits, int32_t max_context_hint, void *stream) {
+    const QkvSource src = {qkv, q_norm_w, k_norm_w, cos_table, sin_table, max_positions, qk_mode, eps, q_out};
+    int rc = check_pool(pool);
+    if (rc)
+        return rc;
+    rc = check_qkv_source(src, pool.head_dim);
+    if (rc)
+        return rc;
+    if (num_seqs > 0) {
+        rc = check_qkv_pointers(src);
+        if (rc)
+            return rc;
+    }
+    return decode_impl(q_out, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
+                       static_cast<hipStream_t>(stream), nullptr, nullptr, 0, &src);
 }
 
 int pkv_device_cu_count(int32_t *cu_count) {

@@ -17,6 +17,10 @@ struct DecodeParams {
     // k_new / v_new ([B][Hkv][D]) into k_dst / v_dst (the same pools)
     const _Float16 *k_new;
     const _Float16 *v_new;
+    // decode step from the QKV projection rows (qkv non-null, fused launch only): q and each sequence's new K/V row
+    // come from qkv[B][(Hq + 2*Hkv) * D], the query and key heads RMS-normalised (qk_mode 1) and rotated at
+    // position L-1 (see the fields at the end); q_out receives the rotated queries
+    const _Float16 *qkv;
     int32_t Hq, Hkv, G, N, M;
     int32_t num_splits;           // grid splits S (1 for a single pass)
     int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(blocks in range / S) per sequence
@@ -30,6 +34,14 @@ struct DecodeParams {
     float *part_l;                // [B][Hq][S]
     _Float16 *k_dst;
     _Float16 *v_dst;
+    const _Float16 *q_norm_w;     // [D]
+    const _Float16 *k_norm_w;     // [D]
+    const float *cos_t;           // [P][D/2]
+    const float *sin_t;           // [P][D/2]
+    int32_t P;
+    int32_t qk_mode;
+    float eps;
+    _Float16 *q_out;              // [B][Hq][D]
 };
 
 // Arguments of the varlen attention kernel (several new query rows per sequence).
@@ -84,6 +96,7 @@ struct QkvParams {
     const int32_t *cu_seqlens_q;  // [B+1]; null: one sequence of T tokens at rope_base / cache_base
     const int32_t *pos_offsets;   // [B]: first new token's RoPE position and cache row
     const int32_t *block_tables;  // [B][M]
+    const int32_t *decode_lens;   // [B] or null: token s is sequence s's new row, at position decode_lens[s] - 1
     int32_t B, T, Hq, Hkv, G, N, M, BS, P;
     int32_t qk_mode;              // 1: RMS-normalise query and key heads first; 0: rotate only
     int32_t rope_base, cache_base;

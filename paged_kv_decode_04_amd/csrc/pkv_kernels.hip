@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include "pkv_internal.h"
+#include "pkv_lanes.h"
 
 namespace pkv {
 
@@ -239,7 +240,10 @@ constexpr int pipeline_stages() {
 }
 
 // FUSED: the fused decode step (p.k_new / p.v_new hold each sequence's new row); otherwise attention alone.
-template <int D, int BS, int NW, bool SPLIT, bool FUSED>
+// QKV (with FUSED): the decode step from the QKV projection rows -- q and the new K/V rows are taken from p.qkv,
+// the query and key heads RMS-normalised (qk_mode 1) and rotated at position L-1 in the prologue [ferrum-kernels
+// 0.7.7, src/backend/cuda/paged.rs: split_qkv_norm_rope_into_paged_cache_varlen, then paged_decode_attention].
+template <int D, int BS, int NW, bool SPLIT, bool FUSED, bool QKV = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     constexpr int KC = D / 32;
     constexpr int VC = D / 16;
@@ -278,12 +282,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 
     // Q^T as the B operand: lane (g4, r) holds head r, dims 32c + 8*g4 .. +8.  Columns r >= G (no such head in
     // the group) repeat head 0; every column of the matrix-core tiles is independent and those are never stored.
+    // From QKV rows (QKV): the raw query head, rotated below once the position is known.
+    const int64_t qkv_row = (int64_t)s * (p.Hq + 2 * p.Hkv) * D;  // QKV: sequence s's row (its one new token)
     f16x8 qf[KC];
     {
-        const _Float16 *qrow = p.q + ((int64_t)s * p.Hq + hk * p.G + (r < p.G ? r : 0)) * D + 8 * g4;
+        const int hq = hk * p.G + (r < p.G ? r : 0);
+        const _Float16 *qrow = (QKV ? p.qkv + qkv_row + (int64_t)hq * D : p.q + ((int64_t)s * p.Hq + hq) * D) + 8 * g4;
 #pragma unroll
         for (int c = 0; c < KC; ++c)
             qf[c] = *reinterpret_cast<const f16x8 *>(qrow + 32 * c);
+    }
+    f16x8 qw[KC];  // QKV, qk_mode 1: the query norm weights of this lane's dims
+    if (QKV && p.qk_mode == 1) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            qw[c] = *reinterpret_cast<const f16x8 *>(p.q_norm_w + 32 * c + 8 * g4);
     }
 
     // Every request above depends on the launch alone; an empty asm statement that reads L and the first block
@@ -340,15 +353,134 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     _Float16 *sm_pk = reinterpret_cast<_Float16 *>(smem + merge_floats(D, p.G, NW));
     _Float16 *sm_pv = sm_pk + D;
     // Owner wave: load the new row (lane t < D/8 takes dims 8t .. 8t+7 of K and of V) ahead of its first K/V loads
-    // and copy it to LDS for the unit that holds it (see compute_unit).
-    f16x8 new_k = (f16x8)(_Float16)0.0f, new_v = (f16x8)(_Float16)0.0f;
-    if (patch_owner && lane < D / 8) {
-        const int64_t row_off = ((int64_t)s * p.Hkv + hk) * D + 8 * lane;
-        new_k = *reinterpret_cast<const f16x8 *>(p.k_new + row_off);
-        new_v = *reinterpret_cast<const f16x8 *>(p.v_new + row_off);
+    // and copy it to LDS for the unit that holds it (see compute_unit).  From QKV rows, lane t < D/16 takes K dims
+    // 8t .. 8t+7 and D/2 + 8t .. +7 instead, so that each rotated pair (j, j + D/2) is in one lane.
+    f16x8 new_k = (f16x8)(_Float16)0.0f, new_v = (f16x8)(_Float16)0.0f, new_k2 = (f16x8)(_Float16)0.0f;
+    f16x8 kwa = new_k, kwb = new_k;  // QKV, qk_mode 1: the key norm weights of those dims
+    if (patch_owner) {
+        if (QKV) {
+            const _Float16 *krow = p.qkv + qkv_row + (int64_t)(p.Hq + hk) * D;
+            if (lane < D / 16) {
+                new_k = *reinterpret_cast<const f16x8 *>(krow + 8 * lane);
+                new_k2 = *reinterpret_cast<const f16x8 *>(krow + D / 2 + 8 * lane);
+                if (p.qk_mode == 1) {
+                    kwa = *reinterpret_cast<const f16x8 *>(p.k_norm_w + 8 * lane);
+                    kwb = *reinterpret_cast<const f16x8 *>(p.k_norm_w + D / 2 + 8 * lane);
+                }
+            }
+            if (lane < D / 8)
+                new_v = *reinterpret_cast<const f16x8 *>(p.qkv + qkv_row + (int64_t)(p.Hq + p.Hkv + hk) * D + 8 * lane);
+        } else if (lane < D / 8) {
+            const int64_t row_off = ((int64_t)s * p.Hkv + hk) * D + 8 * lane;
+            new_k = *reinterpret_cast<const f16x8 *>(p.k_new + row_off);
+            new_v = *reinterpret_cast<const f16x8 *>(p.v_new + row_off);
+        }
     }
+    // QKV: the rotation's table row is position L-1 (clamped into the table: a length past it gives unspecified
+    // results, never an access outside it).  Query lanes need cos/sin of dims 32c + 8*g4 .. +8 (c < KC/2), the
+    // owner's key lanes those of dims 8t .. 8t+7.
+    float4 qcs[KC / 2][2], qsn[KC / 2][2], kcs[2], ksn[2];
+    if (QKV) {
+        const int64_t trow = (int64_t)min(max(L - 1, 0), p.P - 1) * (D / 2);
+#pragma unroll
+        for (int c = 0; c < KC / 2; ++c) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                qcs[c][h] = *reinterpret_cast<const float4 *>(p.cos_t + trow + 32 * c + 8 * g4 + 4 * h);
+                qsn[c][h] = *reinterpret_cast<const float4 *>(p.sin_t + trow + 32 * c + 8 * g4 + 4 * h);
+            }
+        }
+        if (patch_owner && lane < D / 16) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                kcs[h] = *reinterpret_cast<const float4 *>(p.cos_t + trow + 8 * lane + 4 * h);
+                ksn[h] = *reinterpret_cast<const float4 *>(p.sin_t + trow + 8 * lane + 4 * h);
+            }
+        }
+    }
+    // QKV: norm (qk_mode 1) and rotation of this lane's query dims; the first wave of the first split also stores
+    // the rotated heads to q_out.  Dims 32c + 8*g4 + e and 32(c + KC/2) + 8*g4 + e are a RoPE pair (D/2 apart).
+    auto rotate_q = [&]() {
+        float x[KC][8];
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                x[c][e] = (float)qf[c][e];
+        if (p.qk_mode == 1) {
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ss += x[c][e] * x[c][e];
+            const float rn = rsqrtf(rows_sum(ss) * (1.0f / D) + p.eps);  // lanes r, r+16, r+32, r+48: head r
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    x[c][e] = x[c][e] * rn * (float)qw[c][e];
+        }
+#pragma unroll
+        for (int c = 0; c < KC / 2; ++c) {
+            const float cs[8] = {qcs[c][0].x, qcs[c][0].y, qcs[c][0].z, qcs[c][0].w,
+                                 qcs[c][1].x, qcs[c][1].y, qcs[c][1].z, qcs[c][1].w};
+            const float sn[8] = {qsn[c][0].x, qsn[c][0].y, qsn[c][0].z, qsn[c][0].w,
+                                 qsn[c][1].x, qsn[c][1].y, qsn[c][1].z, qsn[c][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a = x[c][e], b = x[c + KC / 2][e];
+                x[c][e] = a * cs[e] - b * sn[e];
+                x[c + KC / 2][e] = b * cs[e] + a * sn[e];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                qf[c][e] = (_Float16)x[c][e];
+        if (wave == 0 && split == 0 && r < p.G) {
+            _Float16 *qo = p.q_out + ((int64_t)s * p.Hq + hk * p.G + r) * D + 8 * g4;
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                *reinterpret_cast<f16x8 *>(qo + 32 * c) = qf[c];
+        }
+    };
     auto copy_new_row = [&]() {
-        if (lane < D / 8) {
+        if (QKV) {
+            if (lane < D / 16) {
+                float a[8], b[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    a[e] = (float)new_k[e];
+                    b[e] = (float)new_k2[e];
+                }
+                if (p.qk_mode == 1) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        ss += a[e] * a[e] + b[e] * b[e];
+                    const float rn = rsqrtf(lanes_sum<D / 16>(ss) * (1.0f / D) + p.eps);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        a[e] = a[e] * rn * (float)kwa[e];
+                        b[e] = b[e] * rn * (float)kwb[e];
+                    }
+                }
+                const float cs[8] = {kcs[0].x, kcs[0].y, kcs[0].z, kcs[0].w, kcs[1].x, kcs[1].y, kcs[1].z, kcs[1].w};
+                const float sn[8] = {ksn[0].x, ksn[0].y, ksn[0].z, ksn[0].w, ksn[1].x, ksn[1].y, ksn[1].z, ksn[1].w};
+                f16x8 ya, yb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ya[e] = (_Float16)(a[e] * cs[e] - b[e] * sn[e]);
+                    yb[e] = (_Float16)(b[e] * cs[e] + a[e] * sn[e]);
+                }
+                *reinterpret_cast<f16x8 *>(sm_pk + 8 * lane) = ya;
+                *reinterpret_cast<f16x8 *>(sm_pk + D / 2 + 8 * lane) = yb;
+            }
+            if (lane < D / 8)
+                *reinterpret_cast<f16x8 *>(sm_pv + 8 * lane) = new_v;
+        } else if (lane < D / 8) {
             *reinterpret_cast<f16x8 *>(sm_pk + 8 * lane) = new_k;
             *reinterpret_cast<f16x8 *>(sm_pv + 8 * lane) = new_v;
         }
@@ -390,6 +522,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int j = 0; j < NS; ++j)
             raw_q[j] = start_known ? spec_raw[NS - 1 + j] : raw_block(u_first + min(NS - 1 + j, n_units - 1) * NW);
+        if (QKV)
+            rotate_q();
         if (patch_owner)
             copy_new_row();
         int k = 0;
@@ -825,7 +959,12 @@ static hipError_t launch_decode_t(const DecodeParams &p, int num_seqs, bool spli
     dim3 block(NW * 64);
     const size_t lds = decode_lds_bytes(D, p.G, NW);
     const bool fused = p.k_new != nullptr;
-    if (split && fused)
+    if (p.qkv != nullptr) {  // the decode step from QKV rows
+        if (split)
+            hipLaunchKernelGGL((decode_kernel<D, BS, NW, true, true, true>), grid, block, lds, stream, p);
+        else
+            hipLaunchKernelGGL((decode_kernel<D, BS, NW, false, true, true>), grid, block, lds, stream, p);
+    } else if (split && fused)
         hipLaunchKernelGGL((decode_kernel<D, BS, NW, true, true>), grid, block, lds, stream, p);
     else if (split)
         hipLaunchKernelGGL((decode_kernel<D, BS, NW, true, false>), grid, block, lds, stream, p);

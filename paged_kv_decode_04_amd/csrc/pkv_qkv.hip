@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include "pkv_internal.h"
+#include "pkv_lanes.h"
 
 namespace pkv {
 
@@ -47,38 +48,6 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-
-// DPP lane patterns (GFX9 encodings of the dpp_ctrl field)
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
-constexpr int kDppRowRor = 0x120;     // row_ror:n = 0x120 + n (rotate within a row of 16 lanes)
-constexpr int kDppHalfMirror = 0x141; // row_half_mirror (lane i <-> 7 - i within each 8)
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the LPR lanes of a head row (aligned groups of 8, 16 or 32 lanes), on the VALU: DPP within 16-lane rows,
-// v_permlane16_swap across the two rows of a 32-lane group.  Every lane of the group gets the total.
-template <int LPR>
-__device__ __forceinline__ float group_sum(float x) {
-    if (LPR == 8) {
-        x += dpp<kDppHalfMirror>(x);  // x_i + x_{7-i}: symmetric within the 8
-        x += dpp<kDppXor1>(x);
-        x += dpp<kDppXor2>(x);         // the quad and its mirror: all 8
-    } else {
-        x += dpp<kDppRowRor + 8>(x);
-        x += dpp<kDppRowRor + 4>(x);
-        x += dpp<kDppRowRor + 2>(x);
-        x += dpp<kDppRowRor + 1>(x);   // all 16 of the row
-        if (LPR == 32) {
-            auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-            x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-        }
-    }
-    return x;
-}
 
 constexpr int kThreads = 256;
 constexpr int kBatch = 1;  // passes whose qkv pieces are loaded together (more measured no faster)
@@ -151,17 +120,27 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
     const int h = (int)blockIdx.y / p.parts;        // kv head
     const int part = (int)blockIdx.y - h * p.parts;  // which of its head slots (G query heads, K, V) this group does
     int s = 0, first = 0, n = p.T, rope0 = p.rope_base, cache0 = p.cache_base;
-    if (p.cu_seqlens_q) {
-        const SeqOfSlot q = find_sequence(p.cu_seqlens_q, p.pos_offsets, p.B, g);
-        if (q.s >= p.B)
-            return;
-        s = q.s;
-        first = q.first;
-        n = q.n;
-        rope0 = cache0 = q.pos;
+    int j;  // index of this slot's cache unit among the sequence's units
+    if (p.decode_lens) {
+        // one new token per sequence: slot g is sequence g, its row at position L - 1
+        s = first = g;
+        const int L = p.decode_lens[s];
+        n = L > 0 ? 1 : 0;
+        rope0 = cache0 = L - 1;
+        j = 0;
+    } else {
+        if (p.cu_seqlens_q) {
+            const SeqOfSlot q = find_sequence(p.cu_seqlens_q, p.pos_offsets, p.B, g);
+            if (q.s >= p.B)
+                return;
+            s = q.s;
+            first = q.first;
+            n = q.n;
+            rope0 = cache0 = q.pos;
+        }
+        j = g - ((first + 32 * s) >> 4);
     }
     // this slot's 16-row cache unit and the new rows in it
-    const int j = g - ((first + 32 * s) >> 4);
     const int64_t u = (int64_t)(cache0 >> 4) + j;
     const int64_t lo = max((int64_t)cache0, 16 * u);
     const int64_t hi = min((int64_t)cache0 + n, 16 * u + 16);
@@ -277,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     ss += x[e] * x[e];
-                const float r = rsqrtf(group_sum<LPR>(ss) * inv_d + p.eps);
+                const float r = rsqrtf(lanes_sum<LPR>(ss) * inv_d + p.eps);
                 const _Float16 *wp = sw + (hs < p.G ? 0 : D) + 4 * piece;
                 const h4 wa = *reinterpret_cast<const h4 *>(wp);
                 const h4 wb = *reinterpret_cast<const h4 *>(wp + HALF);
@@ -346,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
 hipError_t launch_qkv_cache(const QkvParams &p, int head_dim, hipStream_t stream) {
     if (p.T <= 0)
         return hipSuccess;
-    const int64_t slots = ((int64_t)p.T + 32 * (int64_t)(p.cu_seqlens_q ? p.B : 1)) / 16;
+    const int64_t slots = p.decode_lens ? p.B : ((int64_t)p.T + 32 * (int64_t)(p.cu_seqlens_q ? p.B : 1)) / 16;
     const dim3 grid((unsigned)slots, (unsigned)(p.Hkv * p.parts)), block(kThreads);
     switch (head_dim) {
     case 64: hipLaunchKernelGGL(qkv_cache_kernel<64>, grid, block, 0, stream, p); break;

@@ -41,6 +41,7 @@ EXPORTED = [
     "pkv_paged_decode_attention_ws",
     "pkv_paged_decode_attention_planned",
     "pkv_paged_decode_step",
+    "pkv_paged_decode_step_qkv",
     "pkv_paged_varlen_attention",
     "pkv_paged_decode_attention_window",
     "pkv_split_qkv_norm_rope_into_paged_cache_varlen",
@@ -91,6 +92,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.pkv_paged_decode_attention_planned.argtypes = attn[:11] + [ctypes.POINTER(DecodePlan), vp, sz, vp]
         lib.pkv_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, vp, i32, i32,
                                               vp]
+        lib.pkv_paged_decode_step_qkv.argtypes = [vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, PoolDesc, vp, i32, vp,
+                                                  i32, i32, f32, vp, i32, i32, vp]
         lib.pkv_paged_decode_attention_window.argtypes = attn[:12] + [i32, i32, vp]
         lib.pkv_paged_varlen_attention.argtypes = [vp, vp, vp, PoolDesc, vp, i32, vp, vp, i32, i32, i32, f32, vp, i32,
                                                    i32, i32, vp]
@@ -260,6 +263,40 @@ def paged_decode_step(q, k_new, v_new, k_pool, v_pool, block_tables, context_len
                                         _ptr(block_tables), M, _ptr(context_lens), B, Hq, float(scale), _ptr(out),
                                         int(num_splits), int(max_context_hint), _stream(stream)))
     return out
+
+
+def _step_qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool, block_tables, context_lens, num_q_heads,
+                   qk_mode, q_out):
+    import torch
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    _dev(context_lens, torch.int32, "context_lens", 1)
+    pool, T, P = _qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, num_q_heads, qk_mode)
+    B = int(context_lens.shape[0])
+    if T != B or block_tables.shape[0] != B:
+        raise ValueError("qkv, block_tables and context_lens must have num_seqs = %d rows" % B)
+    return pool, B, P
+
+
+def paged_decode_step_qkv(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool, block_tables, context_lens,
+                          num_q_heads: int, scale: float, eps: float, qk_mode: int = 1, q_out=None, out=None,
+                          num_splits: int = 0, max_context_hint: int = 0, stream=None):
+    """Decode step from the QKV projection rows (pkv_paged_decode_step_qkv): RMS norm (qk_mode 1) and RoPE of each
+    sequence's new token at position L-1, its K/V rows written to row L-1, then decode attention.  Returns
+    (out, q_out)."""
+    import torch
+    B, D = int(context_lens.shape[0]), k_pool.shape[3] * 8
+    if q_out is None:
+        q_out = torch.empty((B, int(num_q_heads), D), dtype=torch.float16, device=qkv.device)
+    if out is None:
+        out = torch.empty_like(q_out)
+    _dev(out, torch.float16, "out", 3)
+    pool, B, P = _step_qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool, block_tables, context_lens,
+                                num_q_heads, qk_mode, q_out)
+    _check(load().pkv_paged_decode_step_qkv(
+        _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(cos), _ptr(sin), P, float(eps), int(qk_mode), _ptr(q_out),
+        _ptr(k_pool), _ptr(v_pool), pool, _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
+        int(num_q_heads), float(scale), _ptr(out), int(num_splits), int(max_context_hint), _stream(stream)))
+    return out, q_out
 
 
 def plan_decode(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
@@ -567,3 +604,23 @@ def prepare_split_qkv_norm_rope_into_paged_cache_varlen(qkv, q_norm_w, k_norm_w,
     return PreparedCall(lib.pkv_split_qkv_norm_rope_into_paged_cache_varlen, args,
                         (qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, block_tables, cu_seqlens_q,
                          pos_offsets))
+
+
+def prepare_decode_step_qkv(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool, block_tables, context_lens,
+                            num_q_heads: int, scale: float, eps: float, qk_mode: int, q_out, out, num_splits: int = 0,
+                            max_context_hint: int = 0, stream=None) -> PreparedCall:
+    """pkv_paged_decode_step_qkv with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    _dev(out, torch.float16, "out", 3)
+    pool, B, P = _step_qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool, block_tables, context_lens,
+                                num_q_heads, qk_mode, q_out)
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(qkv)), ctypes.c_void_p(_ptr(q_norm_w)), ctypes.c_void_p(_ptr(k_norm_w)),
+            ctypes.c_void_p(_ptr(cos)), ctypes.c_void_p(_ptr(sin)), ctypes.c_int32(P), ctypes.c_float(eps),
+            ctypes.c_int32(qk_mode), ctypes.c_void_p(_ptr(q_out)), ctypes.c_void_p(_ptr(k_pool)),
+            ctypes.c_void_p(_ptr(v_pool)), pool, ctypes.c_void_p(_ptr(block_tables)),
+            ctypes.c_int32(int(block_tables.shape[1])), ctypes.c_void_p(_ptr(context_lens)), ctypes.c_int32(B),
+            ctypes.c_int32(num_q_heads), ctypes.c_float(scale), ctypes.c_void_p(_ptr(out)), ctypes.c_int32(num_splits),
+            ctypes.c_int32(max_context_hint), ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_paged_decode_step_qkv, args,
+                        (qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, block_tables, context_lens, out))

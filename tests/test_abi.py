@@ -170,6 +170,18 @@ def test_qkv_entry_points_validate_before_touching_a_device():
     # misaligned (non-null, never dereferenced)
     rc = one(8, 16, 16, 16, 16, 64, 16, 16, 16, pool, 4, 4, 8, 32, 0, 0, 1e-6, 1, None)
     assert rc == pkv.PKV_EINVAL and "aligned" in pkv.last_error()
+    step = lib.pkv_paged_decode_step_qkv
+    # qkv, qn, kn, cos, sin, P, eps, mode, q_out, kp, vp, pool, bt, M, cl, B, Hq, scale, out, S, hint, stream
+    assert step(None, None, None, None, None, 64, 1e-6, 1, None, None, None, pool, None, 128, None, 4, 32, 0.1, None,
+                0, 0, None) == pkv.PKV_EINVAL and "null" in pkv.last_error()
+    assert step(None, None, None, None, None, 64, 1e-6, 3, None, None, None, pool, None, 128, None, 4, 32, 0.1, None,
+                0, 0, None) == pkv.PKV_EINVAL and "qk_mode" in pkv.last_error()
+    assert step(None, None, None, None, None, 0, 1e-6, 1, None, None, None, pool, None, 128, None, 4, 32, 0.1, None,
+                0, 0, None) == pkv.PKV_EINVAL
+    assert step(None, None, None, None, None, 64, 1e-6, 1, None, None, None, pool, None, 128, None, 0, 32, 0.1, None,
+                0, 0, None) == pkv.PKV_OK  # no sequences
+    assert step(None, None, None, None, None, 64, 1e-6, 1, None, None, None, pkv.PoolDesc(8, 96, 16, 100), None, 128,
+                None, 4, 32, 0.1, None, 0, 0, None) == pkv.PKV_EUNSUPPORTED
 
 
 def test_workspace_bytes_layout():

@@ -240,3 +240,103 @@ def test_qkv_then_attention_full_size(torch_cuda, name):
                                       vc.scale, units=units)
         got = out.cpu().numpy()[units[:, 0], units[:, 1]]
         assert_close(got, ref, "r2 step then varlen attention (256 sampled rows)")
+
+
+# The decode step from QKV rows (pkv_paged_decode_step_qkv): (B, Hq, Hkv, D, BS, context lengths, num_splits,
+# qk_mode).  The first four run as one launch (the grid fits the CUs: single pass for every head size, and split
+# phase 1 with two splits); the last, 40 sequences x 8 kv heads = 320 workgroups, runs the QKV kernel and then
+# attention.
+STEP_GEOMS = [
+    (4, 8, 2, 64, 16, (37, 16, 1, 100), 1, 1),
+    (3, 16, 16, 256, 32, (70, 33, 5), 1, 1),
+    (5, 32, 2, 128, 64, (130, 64, 1, 200, 17), 1, 0),
+    (8, 32, 8, 128, 16, (300, 129, 5, 70, 16, 17, 1000, 2), 2, 1),
+    (40, 32, 8, 128, 16, tuple(int(x) for x in np.random.default_rng(3).integers(1, 400, 40)), 1, 1),
+]
+
+
+def _step_case(B, Hq, Hkv, D, BS, lens, seed, qk_mode):
+    lens = np.asarray(lens, dtype=np.int32)
+    return W.build_qkv_case("step", B, Hq, Hkv, D, BS, np.ones(B, np.int32), lens - 1, seed, qk_mode=qk_mode,
+                            qkv_scale=2.0, eps=1e-5)
+
+
+def _run_step(torch, c, num_splits, lens=None):
+    from paged_kv_decode_04_amd import pkv
+    vc = c.varlen
+    kp, vp = _dev(torch, vc.k_pool), _dev(torch, vc.v_pool)
+    cl = vc.final_lens if lens is None else np.asarray(lens, np.int32)
+    out, q = pkv.paged_decode_step_qkv(_dev(torch, c.qkv), _dev(torch, c.q_norm_w), _dev(torch, c.k_norm_w),
+                                       _dev(torch, c.cos), _dev(torch, c.sin), kp, vp, _dev(torch, vc.block_tables),
+                                       _dev(torch, cl), vc.Hq, vc.scale, c.eps, c.qk_mode, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy()
+
+
+def _step_reference(c, units=None):
+    """The oracle's QKV step followed by the oracle's decode attention on its (fp16-rounded) outputs."""
+    vc = c.varlen
+    q_ref, k_ref, slots, v_ref = _reference(c)
+    kp_ref, vp_ref = _oracle_pools(c, k_ref, slots, v_ref)
+    out = oracle.decode_attention(q_ref.astype(np.float16), kp_ref, vp_ref, vc.block_tables, vc.final_lens,
+                                  vc.scale, units=units)
+    return out, q_ref, k_ref, slots, v_ref
+
+
+@pytest.mark.parametrize("geom", STEP_GEOMS, ids=lambda g: "B%d_Hq%d_Hkv%d_D%d_BS%d_S%d_m%d" % (g[:5] + g[6:]))
+def test_decode_step_qkv_matches_oracle(torch_cuda, geom):
+    B, Hq, Hkv, D, BS, lens, S, mode = geom
+    c = _step_case(B, Hq, Hkv, D, BS, lens, 1400 + D + BS + Hq + B, mode)
+    say("decode step from qkv %s" % (geom[:5] + geom[6:],))
+    out, q, kp, vp = _run_step(torch_cuda, c, S)
+    ref, q_ref, k_ref, slots, v_ref = _step_reference(c)
+    what = "step_qkv %s" % (geom[:5] + geom[6:],)
+    assert_close(out, ref, what + " out")
+    assert_fp16_of(q, q_ref, what + " q_out")
+    vc = c.varlen
+    got_k = np.stack([W.k_row(kp, int(s) // vc.BS, h, int(s) % vc.BS) for s in slots for h in range(vc.Hkv)])
+    assert_fp16_of(got_k.reshape(k_ref.shape), k_ref, what + " K rows")
+    rest = kp.copy()
+    for s in slots:
+        b, o = int(s) // vc.BS, int(s) % vc.BS
+        for h in range(vc.Hkv):
+            W.set_k_row(rest, b, h, o, W.k_row(vc.k_pool, b, h, o))
+    assert np.array_equal(rest.view(np.uint16), vc.k_pool.view(np.uint16)), what + ": K rows outside the step moved"
+    assert np.array_equal(vp.view(np.uint16), v_ref.view(np.uint16)), what + ": V pool differs"
+
+
+def test_decode_step_qkv_skips_empty_sequences(torch_cuda):
+    """A sequence with L = 0 has no new row: nothing is written for it, its output is zero and its q_out row is left
+    as it was; the others are unaffected."""
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    c = _step_case(3, 8, 2, 128, 16, (40, 9, 17), 1450, 1)
+    vc = c.varlen
+    lens = vc.final_lens.copy()
+    lens[1] = 0
+    kp, vp = _dev(torch, vc.k_pool), _dev(torch, vc.v_pool)
+    q_out = torch.full((3, 8, 128), 7.0, dtype=torch.float16, device="cuda")
+    out, _ = pkv.paged_decode_step_qkv(_dev(torch, c.qkv), _dev(torch, c.q_norm_w), _dev(torch, c.k_norm_w),
+                                       _dev(torch, c.cos), _dev(torch, c.sin), kp, vp, _dev(torch, vc.block_tables),
+                                       _dev(torch, lens), vc.Hq, vc.scale, c.eps, 1, q_out=q_out)
+    torch.cuda.synchronize()
+    out, q, kpn, vpn = out.cpu().numpy(), q_out.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy()
+    assert np.all(out[1] == 0) and np.all(q[1] == np.float16(7.0))
+    slot1 = int(vc.slot_mapping[1])
+    b, o = slot1 // 16, slot1 % 16
+    for h in range(vc.Hkv):
+        assert np.array_equal(W.k_row(kpn, b, h, o).view(np.uint16), W.k_row(vc.k_pool, b, h, o).view(np.uint16))
+        assert np.array_equal(W.v_row(vpn, b, h, o).view(np.uint16), W.v_row(vc.v_pool, b, h, o).view(np.uint16))
+    ref, q_ref, _, _, _ = _step_reference(c, units=np.array([[0, h] for h in range(8)] + [[2, h] for h in range(8)],
+                                                            np.int32))
+    assert_close(np.concatenate([out[0], out[2]]), ref, "step_qkv with an empty sequence")
+    assert_fp16_of(q[[0, 2]], q_ref[[0, 2]], "step_qkv q_out of the non-empty sequences")
+
+
+def test_decode_step_qkv_r1_full_size(torch_cuda):
+    """The r1 workload as bench.py times it: one launch per step."""
+    c = W.config_r1()
+    out, q, kp, vp = _run_step(torch_cuda, c, 1)
+    ref, q_ref, _, _, _ = _step_reference(c)
+    assert_close(out, ref, "r1 decode step from qkv")
+    assert_fp16_of(q, q_ref, "r1 decode step q_out")
