@@ -1,7 +1,8 @@
 """Graph-replayable decode: a decode step captured once in a HIP graph (torch.cuda.graph) replays correctly while
-the device-resident state moves on -- the context lengths grow by one each step, new q and new K/V rows arrive --
-with the program's own eager work and synchronisations between replays.  Every replay is checked bit for bit
-against the same step run eagerly on a separate copy of the state, and the last one against the oracle.
+the device-resident state moves on -- the context lengths grow by one each step, new q and new K/V rows (or new QKV
+rows) arrive -- with the program's own eager work and synchronisations between replays.  Every replay is checked bit
+for bit against the same step run eagerly on a separate copy of the state, and the last one against the oracle run
+on a state the oracle evolved itself over the same steps.
 """
 import numpy as np
 import pytest
@@ -47,6 +48,8 @@ def test_decode_step_graph_replays_follow_device_state(torch_cuda, num_splits):
     # capture records work without running it: restore the state a first replay must start from
     for k in ("kp", "vp", "out"):
         g_state[k].copy_(e_state[k])
+    kp_o, vp_o = c.k_pool.copy(), c.v_pool.copy()  # the oracle's own pools, advanced by the oracle's append
+    lens = lens0.copy()
     for i in range(STEPS):
         q = rng.standard_normal((c.B, c.Hq, c.D)).astype(np.float16)
         kn = rng.standard_normal((c.B, c.Hkv, c.D)).astype(np.float16)
@@ -64,11 +67,79 @@ def test_decode_step_graph_replays_follow_device_state(torch_cuda, num_splits):
         for k in ("out", "kp", "vp"):
             assert torch.equal(g_state[k].view(torch.int16), e_state[k].view(torch.int16)), "replay %d: %s" % (i, k)
         say("graph S=%d replay %d: bit-identical to the eager step" % (num_splits, i))
-    # the last replay against the oracle, over the pools as the replays left them
-    cl = g_state["cl"].cpu().numpy()
-    ref = oracle.decode_attention(q, g_state["kp"].cpu().numpy(), g_state["vp"].cpu().numpy(), c.block_tables, cl,
-                                  c.scale)
+        lens += 1
+        oracle.paged_kv_append(kn, vn, W.newest_row_slots(lens, c.block_tables, c.BS), kp_o, vp_o)
+    # the last replay against the oracle on the state it advanced itself
+    assert np.array_equal(g_state["cl"].cpu().numpy(), lens)
+    ref = oracle.decode_attention(q, kp_o, vp_o, c.block_tables, lens, c.scale)
     assert_close(g_state["out"].cpu().numpy(), ref, "graph S=%d last replay" % num_splits)
+    assert np.array_equal(g_state["kp"].cpu().numpy().view(np.uint16), kp_o.view(np.uint16))
+    assert np.array_equal(g_state["vp"].cpu().numpy().view(np.uint16), vp_o.view(np.uint16))
+
+
+@pytest.mark.parametrize("B", [4, 40])
+def test_decode_step_qkv_graph_replays_follow_device_state(torch_cuda, B):
+    """pkv_paged_decode_step_qkv captured once and replayed with new QKV rows and growing lengths: one launch for 4
+    sequences, the QKV kernel then attention for 40 (320 workgroups)."""
+    from paged_kv_decode_04_amd import pkv
+    from test_gpu_qkv import assert_fp16_of
+    torch = torch_cuda
+    rng = np.random.default_rng(830 + B)
+    lens0 = rng.integers(16, 120, B).astype(np.int32)
+    c = W.build_qkv_case("graph", B, 32, 8, 128, 16, np.ones(B, np.int32), lens0 + STEPS - 1, 831 + B)
+    vc = c.varlen
+    width = (vc.Hq + 2 * vc.Hkv) * vc.D
+
+    def state():
+        return dict(qkv=torch.zeros((B, width), dtype=torch.float16, device="cuda"), qw=_dev(torch, c.q_norm_w),
+                    kw=_dev(torch, c.k_norm_w), cos=_dev(torch, c.cos), sin=_dev(torch, c.sin),
+                    kp=_dev(torch, vc.k_pool), vp=_dev(torch, vc.v_pool), bt=_dev(torch, vc.block_tables),
+                    cl=_dev(torch, lens0), q=torch.zeros((B, vc.Hq, vc.D), dtype=torch.float16, device="cuda"),
+                    out=torch.empty((B, vc.Hq, vc.D), dtype=torch.float16, device="cuda"))
+
+    def step(st):
+        pkv.paged_decode_step_qkv(st["qkv"], st["qw"], st["kw"], st["cos"], st["sin"], st["kp"], st["vp"], st["bt"],
+                                  st["cl"], vc.Hq, vc.scale, c.eps, c.qk_mode, q_out=st["q"], out=st["out"],
+                                  num_splits=1)
+
+    g_state, e_state = state(), state()
+    stream = torch.cuda.Stream()
+    warm = state()
+    with torch.cuda.stream(stream):
+        step(warm)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step(g_state)
+    torch.cuda.synchronize()
+    for k in ("kp", "vp", "out", "q"):
+        g_state[k].copy_(e_state[k])
+    kp_o, vp_o = vc.k_pool.copy(), vc.v_pool.copy()
+    lens = lens0.copy()
+    for i in range(STEPS):
+        qkv = (2.0 * rng.standard_normal((B, width))).astype(np.float16)
+        for st in (g_state, e_state):
+            st["cl"].add_(1)
+            st["qkv"].copy_(torch.from_numpy(qkv))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e_state)
+        torch.cuda.synchronize()
+        for k in ("out", "q", "kp", "vp"):
+            assert torch.equal(g_state[k].view(torch.int16), e_state[k].view(torch.int16)), "replay %d: %s" % (i, k)
+        say("graph step_qkv B=%d replay %d: bit-identical to the eager step" % (B, i))
+        # the oracle's own step on its own state
+        lens += 1
+        q64, k64, slots = oracle.qkv_norm_rope_paged(qkv, c.q_norm_w, c.k_norm_w, c.cos, c.sin,
+                                                     np.arange(B + 1, dtype=np.int32), lens - 1, lens - 1,
+                                                     vc.block_tables, kp_o, vp_o, c.eps, c.qk_mode)
+        k16 = k64.astype(np.float16)
+        for t, slot in enumerate(slots):
+            W.set_k_row(kp_o, int(slot) // vc.BS, slice(None), int(slot) % vc.BS, k16[t])
+    ref = oracle.decode_attention(q64.astype(np.float16), kp_o, vp_o, vc.block_tables, lens, vc.scale)
+    assert_close(g_state["out"].cpu().numpy(), ref, "graph step_qkv B=%d last replay" % B)
+    assert_fp16_of(g_state["q"].cpu().numpy(), q64, "graph step_qkv B=%d last q_out" % B)
 
 
 def test_capture_needing_a_new_workspace_fails_cleanly(torch_cuda):
