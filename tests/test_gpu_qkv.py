@@ -108,6 +108,20 @@ def test_qkv_step_matches_oracle(torch_cuda, geom):
     _check_step(c, q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), "qkv %s" % (geom,))
 
 
+@pytest.mark.parametrize("B", [63, 64, 300])
+def test_qkv_step_many_sequences(torch_cuda, B):
+    """A unit slot finds its sequence in one ballot round up to 63 sequences and in several rounds beyond; ragged
+    new-row counts (zeros included) and positions."""
+    rng = np.random.default_rng(1250 + B)
+    ql = rng.integers(0, 21, B)
+    ql[::7] = 0
+    po = rng.integers(0, 100, B)
+    c = W.build_qkv_case("qkv", B, 8, 2, 64, 16, ql, po, 1251 + B, qk_mode=1, qkv_scale=2.0, eps=1e-5)
+    say("qkv B=%d T=%d" % (B, c.varlen.T))
+    q, kp, vp = _run(torch_cuda, c)
+    _check_step(c, q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), "qkv B=%d" % B)
+
+
 def test_qkv_prepared_call_matches(torch_cuda):
     c = W.build_qkv_case("qkv", 3, 32, 8, 128, 16, (1, 20, 2), (7, 30, 200), 1301)
     q, kp, vp = _run(torch_cuda, c, prepared=True)
