@@ -651,8 +651,10 @@ int qkv_impl(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_no
     if (num_q_heads <= 0 || num_q_heads % pool.num_kv_heads != 0)
         return fail(PKV_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", num_q_heads,
                     pool.num_kv_heads);
-    if (pool.head_dim != 64 && pool.head_dim != 128 && pool.head_dim != 256)
-        return fail(PKV_EUNSUPPORTED, "head_dim %d not compiled (64|128|256)", pool.head_dim);
+    const QkvSource src = {qkv, q_norm_w, k_norm_w, cos_table, sin_table, max_positions, qk_mode, eps, q_out};
+    rc = check_qkv_source(src, pool.head_dim);
+    if (rc)
+        return rc;
     if (num_q_heads / pool.num_kv_heads > 16)
         return fail(PKV_EUNSUPPORTED, "group size %d > 16 query heads per kv head is not compiled",
                     num_q_heads / pool.num_kv_heads);
@@ -661,12 +663,6 @@ int qkv_impl(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_no
     if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * pool.block_size > INT32_MAX)
         return fail(PKV_EINVAL, "max_blocks_per_seq must be > 0 with max_blocks_per_seq * block_size in int32 "
                     "(got %d)", max_blocks_per_seq);
-    if (max_positions <= 0)
-        return fail(PKV_EINVAL, "max_positions must be > 0 (got %d)", max_positions);
-    if (qk_mode != 0 && qk_mode != 1)
-        return fail(PKV_EINVAL, "qk_mode must be 0 (rotate only) or 1 (RMS norm, then rotate); got %d", qk_mode);
-    if (!(eps >= 0.f) || !isfinite(eps))
-        return fail(PKV_EINVAL, "eps must be finite and >= 0");
     if (!varlen) {
         if (rope_base < 0 || (int64_t)rope_base + total_tokens > max_positions)
             return fail(PKV_EINVAL, "positions %d .. %d + %d exceed the %d table rows", rope_base, rope_base,
@@ -677,16 +673,14 @@ int qkv_impl(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_no
     }
     if (num_seqs == 0 || total_tokens == 0)
         return ok();
-    if (!qkv || !cos_table || !sin_table || !q_out || !k_pool || !v_pool || !block_tables ||
-        (qk_mode == 1 && (!q_norm_w || !k_norm_w)) || (varlen && (!cu_seqlens_q || !pos_offsets)))
-        return fail(PKV_EINVAL, "null device pointer (qkv=%p cos=%p sin=%p q_out=%p k_pool=%p v_pool=%p "
-                    "block_tables=%p q_norm_w=%p k_norm_w=%p cu_seqlens_q=%p pos_offsets=%p)", qkv, cos_table,
-                    sin_table, q_out, k_pool, v_pool, block_tables, q_norm_w, k_norm_w, cu_seqlens_q, pos_offsets);
-    if (!aligned(qkv, 16) || !aligned(q_out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
-        !aligned(cos_table, 16) || !aligned(sin_table, 16) ||
-        (qk_mode == 1 && (!aligned(q_norm_w, 16) || !aligned(k_norm_w, 16))))
-        return fail(PKV_EINVAL, "qkv, q_out, the pools, the cos/sin tables and the norm weights must be 16-byte "
-                    "aligned");
+    rc = check_qkv_pointers(src);
+    if (rc)
+        return rc;
+    if (!k_pool || !v_pool || !block_tables || (varlen && (!cu_seqlens_q || !pos_offsets)))
+        return fail(PKV_EINVAL, "null device pointer (k_pool=%p v_pool=%p block_tables=%p cu_seqlens_q=%p "
+                    "pos_offsets=%p)", k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets);
+    if (!aligned(k_pool, 16) || !aligned(v_pool, 16))
+        return fail(PKV_EINVAL, "k_pool and v_pool must be 16-byte aligned");
     if (!aligned(block_tables, 4) || (varlen && (!aligned(cu_seqlens_q, 4) || !aligned(pos_offsets, 4))))
         return fail(PKV_EINVAL, "block_tables, cu_seqlens_q and pos_offsets must be 4-byte aligned");
     if ((int64_t)total_tokens + 32 * (int64_t)num_seqs > INT32_MAX || pool.num_kv_heads * 18 > 65535)

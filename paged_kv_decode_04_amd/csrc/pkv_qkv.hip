@@ -13,7 +13,7 @@
 // f32 arithmetic, each output rounded once to fp16 (nearest even).
 //
 // Work decomposition (MI355X-first: the pool's 16-row panels are written whole):
-//   * one workgroup per (16-row cache unit holding new rows, kv head h).  The grid's x runs over unit slots, at
+//   * one workgroup per (16-row cache unit holding new rows, kv head h, part).  The grid's x runs over unit slots, at
 //     least floor(n_s / 16) + 2 of them per sequence (enough for the units its n_s new rows touch, wherever the
 //     first starts); a slot finds its sequence by a wave-wide search of the prefix sums, and slots past a
 //     sequence's last unit return at once.  The unit's head slots of kv head h (its G query heads, key head h,
@@ -27,8 +27,11 @@
 //   * q goes straight to q_out (8-byte stores, coalesced per half head row).  The unit's new K rows are staged in
 //     LDS in the pool's panel layout (rows XOR-swizzled per piece), its V rows row-major (padded rows); each
 //     thread then writes 16-byte chunks of the two panels (V transposed on the way), taking rows outside the new
-//     range from the old panel, which it loaded at the start (so that load overlaps everything else).  The pools thus see only whole 16-byte chunks of whole panels -- scattered
-//     2-byte V stores and 16-byte K row pieces cost far more at the memory than their bytes.
+//     range from the old panel, which it loaded at the start (so that load overlaps everything else).  The pools
+//     thus see only whole 16-byte chunks of whole panels -- scattered 2-byte V stores and 16-byte K row pieces
+//     cost far more at the memory than their bytes;
+//   * decode mode (decode_lens set): slot g is sequence g, whose one new token sits at row decode_lens[g] - 1 --
+//     the QKV half of the decode step from QKV rows when it runs as two launches.
 //
 // A unit's other rows are rewritten with their own values: no other work may write the panel meanwhile (the
 // block holding a sequence's new rows belongs to that sequence alone).
