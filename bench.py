@@ -54,7 +54,7 @@ WORKLOADS = {
     "r1": ("Qwen3-8B-shaped decode step from the QKV projection: split QKV + q/k RMSNorm + RoPE + paged-cache write, "
            "then single-pass attention; B=32, Hq=32, Hkv=8, D=128, BS=16, final L~U[512,2048]", 1, 4),
     "r2": ("chunked-prefill QKV-to-cache step of the same layer: 4 sequences x 512 new rows after cached prefixes "
-           "U[0,1024], split QKV + q/k RMSNorm + RoPE + paged-cache write (2048 tokens)", 1, 2),
+           "U[0,1024], split QKV + q/k RMSNorm + RoPE + paged-cache write (2048 tokens)", 1, 6),
 }
 WINDOWS = {"w1": 512}  # workloads run with pkv_paged_decode_attention_window, and their window
 

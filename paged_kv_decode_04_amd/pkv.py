@@ -80,6 +80,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         if _lib is not None:
             return _lib
         p = path or LIB_PATH
+        # torch first: its HIP runtime must be the one libpkv binds to (loading libpkv first would bring in a
+        # second runtime from the system ROCm that does not share torch's device state)
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(p):
             raise PkvError(PKV_EINVAL, "%s is not built; run __graft_entry__.build() or "
                            "python -m paged_kv_decode_04_amd.build" % p)
