@@ -81,6 +81,9 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility; only the entry points below are exported. */
+#define PKV_API __attribute__((visibility("default")))
+
 #define PKV_OK 0
 #define PKV_EINVAL (-1)       /* a null pointer, a negative size, Hq % Hkv != 0, misaligned buffer, ... */
 #define PKV_EUNSUPPORTED (-2) /* head_dim / block_size / group size not compiled in */
@@ -123,7 +126,7 @@ typedef struct {
  *   multiple of 16),
  *   PKV_EHIP.
  * ------------------------------------------------------------------------- */
-int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping,
+PKV_API int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping,
                         int32_t num_tokens, uint16_t *k_pool, uint16_t *v_pool,
                         pkv_pool_desc pool, void *stream);
 
@@ -155,7 +158,7 @@ int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slo
  *   q, k_pool, v_pool, out: 16-byte aligned.  num_seqs == 0 is a no-op.
  *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EHIP.
  * ------------------------------------------------------------------------- */
-int pkv_paged_decode_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+PKV_API int pkv_paged_decode_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                                pkv_pool_desc pool, const int32_t *block_tables,
                                int32_t max_blocks_per_seq, const int32_t *context_lens,
                                int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
@@ -166,7 +169,7 @@ int pkv_paged_decode_attention(const uint16_t *q, const uint16_t *k_pool, const 
  * bytes for the plan pkv_plan_decode returns for the same arguments; a single
  * pass needs none (workspace may then be NULL).  The workspace must not be in
  * use by other queued work.  Errors: as above, plus PKV_EWORKSPACE. */
-int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+PKV_API int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                                   pkv_pool_desc pool, const int32_t *block_tables,
                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
                                   int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
@@ -192,7 +195,7 @@ int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, con
  *   other sequence of the batch may read or write it).  Other arguments,
  *   workspace and errors as pkv_paged_decode_attention.
  * ------------------------------------------------------------------------- */
-int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+PKV_API int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
                           uint16_t *v_pool, pkv_pool_desc pool, const int32_t *block_tables,
                           int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
                           int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
@@ -225,7 +228,7 @@ int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16
  *   that sequence alone.
  *   Errors: as pkv_paged_decode_attention, plus those of the QKV arguments.
  * ------------------------------------------------------------------------- */
-int pkv_paged_decode_step_qkv(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w,
+PKV_API int pkv_paged_decode_step_qkv(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w,
                               const float *cos_table, const float *sin_table, int32_t max_positions, float eps,
                               int32_t qk_mode, uint16_t *q_out, uint16_t *k_pool, uint16_t *v_pool,
                               pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
@@ -240,7 +243,7 @@ int pkv_paged_decode_step_qkv(const uint16_t *qkv, const uint16_t *q_norm_w, con
  * {1, 2, 4, 8}, and at most 4 for head_dim 256 (PKV_EUNSUPPORTED).  workspace == NULL uses the library-owned workspace, otherwise
  * it must hold plan->workspace_bytes as computed by pkv_decode_workspace_bytes
  * for plan->num_splits (PKV_EWORKSPACE). */
-int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+PKV_API int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                                        pkv_pool_desc pool, const int32_t *block_tables,
                                        int32_t max_blocks_per_seq, const int32_t *context_lens,
                                        int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
@@ -258,7 +261,7 @@ int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool
  *   stored - window (saturating), and the KvMirror window]
  *   Errors: as pkv_paged_decode_attention; window < 0 is PKV_EINVAL.
  * ------------------------------------------------------------------------- */
-int pkv_paged_decode_attention_window(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+PKV_API int pkv_paged_decode_attention_window(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                                       pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
                                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
                                       float scale, uint16_t *out, int32_t num_splits, int32_t window,
@@ -294,7 +297,7 @@ int pkv_paged_decode_attention_window(const uint16_t *q, const uint16_t *k_pool,
  *   num_seqs == 0 or total_q_tokens == 0 is a no-op.
  *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EHIP.
  * ------------------------------------------------------------------------- */
-int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+PKV_API int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                                pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
                                const int32_t *cu_seqlens_q, const int32_t *pos_offsets, int32_t num_seqs,
                                int32_t total_q_tokens, int32_t num_q_heads, float scale, uint16_t *out,
@@ -342,7 +345,7 @@ int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const 
  *   eps negative or not finite, max_positions <= 0, ...), PKV_EUNSUPPORTED
  *   (head_dim not 64, 128 or 256; block_size not a multiple of 16), PKV_EHIP.
  * ------------------------------------------------------------------------- */
-int pkv_split_qkv_norm_rope_into_paged_cache_varlen(const uint16_t *qkv, const uint16_t *q_norm_w,
+PKV_API int pkv_split_qkv_norm_rope_into_paged_cache_varlen(const uint16_t *qkv, const uint16_t *q_norm_w,
                                                     const uint16_t *k_norm_w, const float *cos_table,
                                                     const float *sin_table, int32_t max_positions, uint16_t *q_out,
                                                     uint16_t *k_pool, uint16_t *v_pool, pkv_pool_desc pool,
@@ -363,7 +366,7 @@ int pkv_split_qkv_norm_rope_into_paged_cache_varlen(const uint16_t *qkv, const u
  *   split_qkv_norm_rope_into_paged_cache (tokens, pos_offset, cache_len,
  *   block_size, max_blocks_per_seq)]
  * ------------------------------------------------------------------------- */
-int pkv_split_qkv_norm_rope_into_paged_cache(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w,
+PKV_API int pkv_split_qkv_norm_rope_into_paged_cache(const uint16_t *qkv, const uint16_t *q_norm_w, const uint16_t *k_norm_w,
                                              const float *cos_table, const float *sin_table, int32_t max_positions,
                                              uint16_t *q_out, uint16_t *k_pool, uint16_t *v_pool,
                                              pkv_pool_desc pool, const int32_t *block_table,
@@ -381,14 +384,14 @@ int pkv_split_qkv_norm_rope_into_paged_cache(const uint16_t *qkv, const uint16_t
  *   128 SMs).  num_splits > 0 forces that split count (chunk_blocks = 0).
  *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP (device query).
  * ------------------------------------------------------------------------- */
-int pkv_plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+PKV_API int pkv_plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_hint,
                     int32_t num_splits, int32_t cu_count, pkv_decode_plan *plan);
 
 /* Bytes of f32 split-K partials for a grid of num_splits splits:
  * partial_out [B][Hq][S][D] then partial_m and partial_l [B][Hq][S], each
  * array starting on a 256-byte boundary.  0 when num_splits <= 1. */
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+PKV_API size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t num_splits);
 
 /* ---------------------------------------------------------------------------
@@ -407,7 +410,7 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   With chunk_blocks > 0 the caller must give num_splits >= ceil(M / chunk_blocks).
  *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
  * ------------------------------------------------------------------------- */
-int pkv_paged_decode_split_partials(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+PKV_API int pkv_paged_decode_split_partials(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                                     pkv_pool_desc pool, const int32_t *block_tables,
                                     int32_t max_blocks_per_seq, const int32_t *context_lens,
                                     int32_t num_seqs, int32_t num_q_heads, float scale,
@@ -425,21 +428,61 @@ int pkv_paged_decode_split_partials(const uint16_t *q, const uint16_t *k_pool, c
  *   phase 2, the reduce launch over (num_heads, num_seqs)]
  *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
  * ------------------------------------------------------------------------- */
-int pkv_paged_decode_split_combine(const float *partial_out, const float *partial_m,
+PKV_API int pkv_paged_decode_split_combine(const float *partial_out, const float *partial_m,
                                    const float *partial_l, const int32_t *context_lens,
                                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t block_size, int32_t max_blocks_per_seq,
                                    int32_t num_splits, int32_t chunk_blocks, uint16_t *out,
                                    void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Input checks (cold path, for debugging).  The hot-path entry points read
+ * device-resident indices without validating them (see the conventions
+ * above); these calls check the same arrays on the device and report through
+ * `report`, a device array of 4 int32 the call overwrites:
+ *   report[0]  lengths (decode), or prefix sums / positions (varlen), that
+ *              break the entry point's rules;
+ *   report[1]  table entries outside [0, num_blocks) among those a call with
+ *              these lengths would read;
+ *   report[2]  the first sequence (slot check: token) with a problem, or
+ *              INT32_MAX when there is none;
+ *   report[3]  slots at or past num_blocks * block_size (slot check only;
+ *              negative slots are padding and allowed).
+ * Asynchronous on `stream`: synchronise before reading the report.  No host
+ * synchronisation and no allocation (the cold-path counterpart of the check
+ * in [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs:
+ * paged_decode_attention], which copies the final lengths to the host).
+ * Errors: PKV_EINVAL (null or misaligned arrays, negative sizes),
+ * PKV_EUNSUPPORTED (block_size not a multiple of 16), PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+
+/* Decode: 0 <= context_lens[s] <= block_size * max_blocks_per_seq; the table
+ * entries of blocks [max(0, L - window) / block_size, ceil(L / block_size))
+ * (window = 0: from block 0) must name pool blocks. */
+PKV_API int pkv_check_decode_inputs(const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t num_seqs, pkv_pool_desc pool, int32_t window, int32_t *report, void *stream);
+
+/* Varlen: cu_seqlens_q[0] = 0, non-decreasing, cu_seqlens_q[num_seqs] =
+ * total_q_tokens; pos_offsets[s] >= 0 with pos_offsets[s] + (new rows of s)
+ * <= block_size * max_blocks_per_seq; the entries of blocks
+ * [0, ceil((pos + new rows) / block_size)) must name pool blocks. */
+PKV_API int pkv_check_varlen_inputs(const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q,
+                            const int32_t *pos_offsets, int32_t num_seqs, int32_t total_q_tokens, pkv_pool_desc pool,
+                            int32_t *report, void *stream);
+
+/* Slot mapping of pkv_paged_kv_append: slots must be < num_blocks *
+ * block_size (negative = padding). */
+PKV_API int pkv_check_slot_mapping(const int32_t *slot_mapping, int32_t num_tokens, pkv_pool_desc pool, int32_t *report,
+                           void *stream);
+
 /* Number of compute units of the current device (hipDeviceProp_t::multiProcessorCount). */
-int pkv_device_cu_count(int32_t *cu_count);
+PKV_API int pkv_device_cu_count(int32_t *cu_count);
 
 /* Thread-local message for the last non-zero return on this thread ("" if none). */
-const char *pkv_last_error(void);
+PKV_API const char *pkv_last_error(void);
 
 /* Library version string. */
-const char *pkv_version(void);
+PKV_API const char *pkv_version(void);
 
 #ifdef __cplusplus
 }

@@ -23,11 +23,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["pkv_kernels.hip", "pkv_qkv.hip", "pkv_api.hip"]
+SOURCES = ["pkv_kernels.hip", "pkv_qkv.hip", "pkv_check.hip", "pkv_api.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-COMMON = ["-std=c++17", "-O3", "--offload-arch=" + ARCH, "-fPIC", "-Wall",
+COMMON = ["-std=c++17", "-O3", "--offload-arch=" + ARCH, "-fPIC", "-fvisibility=hidden", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", INCLUDE, "-I", CSRC]
 

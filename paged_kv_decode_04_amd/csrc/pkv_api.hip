@@ -974,6 +974,98 @@ int pkv_paged_decode_step_qkv(const uint16_t *qkv, const uint16_t *q_norm_w, con
                        static_cast<hipStream_t>(stream), nullptr, nullptr, 0, &src);
 }
 
+// ---------------------------------------------------------------------------
+// cold-path input checks
+
+static int check_common(const pkv_pool_desc &pool, int32_t *report) {
+    int rc = check_pool(pool);
+    if (rc)
+        return rc;
+    if (!report || !aligned(report, 4))
+        return fail(PKV_EINVAL, "report must be a 4-byte aligned device array of 4 int32");
+    if (pool.block_size % 16 != 0)
+        return fail(PKV_EUNSUPPORTED, "block_size %d must be a multiple of 16", pool.block_size);
+    return PKV_OK;
+}
+
+static int run_check(const pkv::CheckParams &c, hipStream_t stream) {
+    hipError_t e = pkv::launch_check(c, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "input check kernel launch");
+    return ok();
+}
+
+int pkv_check_decode_inputs(const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t num_seqs, pkv_pool_desc pool, int32_t window, int32_t *report, void *stream) {
+    int rc = check_common(pool, report);
+    if (rc)
+        return rc;
+    if (num_seqs < 0 || max_blocks_per_seq <= 0 || window < 0 ||
+        (int64_t)max_blocks_per_seq * pool.block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "num_seqs and window must be >= 0 and max_blocks_per_seq > 0 (got %d, %d, %d)",
+                    num_seqs, window, max_blocks_per_seq);
+    if (num_seqs > 0 && (!block_tables || !context_lens || !aligned(block_tables, 4) || !aligned(context_lens, 4)))
+        return fail(PKV_EINVAL, "block_tables and context_lens must be non-null, 4-byte aligned device arrays");
+    pkv::CheckParams c;
+    memset(&c, 0, sizeof c);
+    c.block_tables = block_tables;
+    c.context_lens = context_lens;
+    c.B = num_seqs;
+    c.M = max_blocks_per_seq;
+    c.N = pool.num_blocks;
+    c.BS = pool.block_size;
+    c.window = window;
+    c.report = report;
+    return run_check(c, static_cast<hipStream_t>(stream));
+}
+
+int pkv_check_varlen_inputs(const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q,
+                            const int32_t *pos_offsets, int32_t num_seqs, int32_t total_q_tokens, pkv_pool_desc pool,
+                            int32_t *report, void *stream) {
+    int rc = check_common(pool, report);
+    if (rc)
+        return rc;
+    if (num_seqs < 0 || total_q_tokens < 0 || max_blocks_per_seq <= 0 ||
+        (int64_t)max_blocks_per_seq * pool.block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "num_seqs and total_q_tokens must be >= 0 and max_blocks_per_seq > 0 (got %d, %d, %d)",
+                    num_seqs, total_q_tokens, max_blocks_per_seq);
+    if (num_seqs > 0 && (!block_tables || !cu_seqlens_q || !pos_offsets || !aligned(block_tables, 4) ||
+                         !aligned(cu_seqlens_q, 4) || !aligned(pos_offsets, 4)))
+        return fail(PKV_EINVAL, "block_tables, cu_seqlens_q and pos_offsets must be non-null, 4-byte aligned device "
+                    "arrays");
+    pkv::CheckParams c;
+    memset(&c, 0, sizeof c);
+    c.block_tables = block_tables;
+    c.cu_seqlens_q = cu_seqlens_q;
+    c.pos_offsets = pos_offsets;
+    c.B = num_seqs;
+    c.T = total_q_tokens;
+    c.M = max_blocks_per_seq;
+    c.N = pool.num_blocks;
+    c.BS = pool.block_size;
+    c.report = report;
+    return run_check(c, static_cast<hipStream_t>(stream));
+}
+
+int pkv_check_slot_mapping(const int32_t *slot_mapping, int32_t num_tokens, pkv_pool_desc pool, int32_t *report,
+                           void *stream) {
+    int rc = check_common(pool, report);
+    if (rc)
+        return rc;
+    if (num_tokens < 0)
+        return fail(PKV_EINVAL, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (num_tokens > 0 && (!slot_mapping || !aligned(slot_mapping, 4)))
+        return fail(PKV_EINVAL, "slot_mapping must be a non-null, 4-byte aligned device array");
+    pkv::CheckParams c;
+    memset(&c, 0, sizeof c);
+    c.slot_mapping = slot_mapping ? slot_mapping : reinterpret_cast<const int32_t *>(report);  // marks the mode
+    c.T = num_tokens;
+    c.N = pool.num_blocks;
+    c.BS = pool.block_size;
+    c.report = report;
+    return run_check(c, static_cast<hipStream_t>(stream));
+}
+
 int pkv_device_cu_count(int32_t *cu_count) {
     if (!cu_count)
         return fail(PKV_EINVAL, "cu_count is null");

@@ -1,5 +1,5 @@
 // pkv_internal.h -- private interface between the host API (pkv_api.hip) and
-// the kernels (pkv_kernels.hip, pkv_qkv.hip).  Not installed; callers use include/pkv.h.
+// the kernels (pkv_kernels.hip, pkv_qkv.hip, pkv_check.hip).  Not installed; callers use include/pkv.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -107,6 +107,19 @@ struct QkvParams {
     _Float16 *v_pool;
 };
 
+// Arguments of the input checks (cold path): block tables with either context lengths (decode) or prefix sums and
+// positions (varlen), or a slot mapping alone.
+struct CheckParams {
+    const int32_t *block_tables;  // [B][M]
+    const int32_t *context_lens;  // [B] (decode) or null
+    const int32_t *cu_seqlens_q;  // [B+1] (varlen) or null
+    const int32_t *pos_offsets;   // [B] (varlen)
+    const int32_t *slot_mapping;  // [T] (slot check) or null
+    int32_t B, M, N, BS, T;
+    int32_t window;               // decode: > 0 reads only the last `window` rows' blocks
+    int32_t *report;              // [4]
+};
+
 // LDS bytes the decode kernel needs for `waves` wavefronts and group size G.
 size_t decode_lds_bytes(int head_dim, int G, int waves);
 
@@ -120,6 +133,7 @@ hipError_t launch_varlen(const VarlenParams &p, int num_seqs, int head_dim, int 
 hipError_t launch_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream);
 hipError_t launch_qkv_cache(const QkvParams &p, int head_dim, hipStream_t stream);
+hipError_t launch_check(const CheckParams &p, hipStream_t stream);
 
 // Geometry support of the compiled kernels.
 bool decode_geometry_supported(int head_dim, int block_size);

@@ -50,6 +50,9 @@ EXPORTED = [
     "pkv_decode_workspace_bytes",
     "pkv_paged_decode_split_partials",
     "pkv_paged_decode_split_combine",
+    "pkv_check_decode_inputs",
+    "pkv_check_varlen_inputs",
+    "pkv_check_slot_mapping",
     "pkv_device_cu_count",
     "pkv_last_error",
     "pkv_version",
@@ -112,6 +115,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.pkv_paged_decode_split_partials.argtypes = [vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, i32, i32,
                                                         vp, vp, vp, vp]
         lib.pkv_paged_decode_split_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+        lib.pkv_check_decode_inputs.argtypes = [vp, i32, vp, i32, PoolDesc, i32, vp, vp]
+        lib.pkv_check_varlen_inputs.argtypes = [vp, i32, vp, vp, i32, i32, PoolDesc, vp, vp]
+        lib.pkv_check_slot_mapping.argtypes = [vp, i32, PoolDesc, vp, vp]
         lib.pkv_device_cu_count.argtypes = [ctypes.POINTER(i32)]
         lib.pkv_last_error.restype = ctypes.c_char_p
         lib.pkv_version.restype = ctypes.c_char_p
@@ -467,6 +473,56 @@ def split_qkv_norm_rope_into_paged_cache(qkv, q_norm_w, k_norm_w, cos, sin, k_po
         pool, _ptr(block_table), int(block_table.shape[0]), T, int(num_q_heads), int(pos_offset), int(cache_len),
         float(eps), int(qk_mode), _stream(stream)))
     return q_out
+
+
+def _report(report, device):
+    import torch
+    if report is None:
+        return torch.empty(4, dtype=torch.int32, device=device)
+    _dev(report, torch.int32, "report", 1)
+    if report.shape[0] < 4:
+        raise ValueError("report must hold 4 int32")
+    return report
+
+
+def check_decode_inputs(k_pool, v_pool, block_tables, context_lens, window: int = 0, report=None, stream=None):
+    """Device-side check of decode inputs (pkv_check_decode_inputs); returns the int32[4] report tensor (read it
+    after synchronising: bad lengths, bad table entries, first bad sequence or INT32_MAX)."""
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    _dev(context_lens, torch.int32, "context_lens", 1)
+    report = _report(report, block_tables.device)
+    _check(load().pkv_check_decode_inputs(_ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
+                                          int(context_lens.shape[0]), pool, int(window), _ptr(report),
+                                          _stream(stream)))
+    return report
+
+
+def check_varlen_inputs(k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, total_q_tokens: int, report=None,
+                        stream=None):
+    """Device-side check of varlen inputs (pkv_check_varlen_inputs); returns the int32[4] report tensor."""
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1)
+    _dev(pos_offsets, torch.int32, "pos_offsets", 1)
+    report = _report(report, block_tables.device)
+    _check(load().pkv_check_varlen_inputs(_ptr(block_tables), int(block_tables.shape[1]), _ptr(cu_seqlens_q),
+                                          _ptr(pos_offsets), int(pos_offsets.shape[0]), int(total_q_tokens), pool,
+                                          _ptr(report), _stream(stream)))
+    return report
+
+
+def check_slot_mapping(k_pool, v_pool, slot_mapping, report=None, stream=None):
+    """Device-side check of an append's slot mapping (pkv_check_slot_mapping); returns the int32[4] report."""
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(slot_mapping, torch.int32, "slot_mapping", 1)
+    report = _report(report, slot_mapping.device)
+    _check(load().pkv_check_slot_mapping(_ptr(slot_mapping), int(slot_mapping.shape[0]), pool, _ptr(report),
+                                         _stream(stream)))
+    return report
 
 
 class PreparedCall:

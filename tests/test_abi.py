@@ -31,6 +31,9 @@ def test_library_exports_every_declared_symbol():
                          check=True).stdout
     exported = set(re.findall(r"\bT (pkv_\w+)", out))
     assert set(_declared()) <= exported
+    # nothing else: the library is built with hidden visibility
+    others = [l for l in out.splitlines() if " T " in l and not re.search(r"\bT pkv_", l)]
+    assert not others, others[:5]
 
 
 def test_library_has_gfx950_code_object():
@@ -182,6 +185,21 @@ def test_qkv_entry_points_validate_before_touching_a_device():
                 0, 0, None) == pkv.PKV_OK  # no sequences
     assert step(None, None, None, None, None, 64, 1e-6, 1, None, None, None, pkv.PoolDesc(8, 96, 16, 100), None, 128,
                 None, 4, 32, 0.1, None, 0, 0, None) == pkv.PKV_EUNSUPPORTED
+
+
+def test_check_entry_points_validate_arguments():
+    lib = pkv.load()
+    pool = pkv.PoolDesc(8, 128, 16, 100)
+    assert lib.pkv_check_decode_inputs(None, 128, None, 4, pool, 0, None, None) == pkv.PKV_EINVAL  # no report
+    assert lib.pkv_check_decode_inputs(None, 128, None, 4, pool, 0, 64, None) == pkv.PKV_EINVAL  # null arrays
+    assert lib.pkv_check_decode_inputs(4, 128, 4, 4, pool, -1, 64, None) == pkv.PKV_EINVAL  # negative window
+    assert lib.pkv_check_decode_inputs(4, 128, 4, 4, pkv.PoolDesc(8, 128, 24, 100), 0, 64,
+                                       None) == pkv.PKV_EUNSUPPORTED
+    assert lib.pkv_check_varlen_inputs(None, 128, None, None, 4, 8, pool, 64, None) == pkv.PKV_EINVAL
+    assert lib.pkv_check_varlen_inputs(4, 128, 4, 4, 4, -1, pool, 64, None) == pkv.PKV_EINVAL
+    assert lib.pkv_check_slot_mapping(None, 3, pool, 64, None) == pkv.PKV_EINVAL
+    assert lib.pkv_check_slot_mapping(None, -1, pool, 64, None) == pkv.PKV_EINVAL
+    assert lib.pkv_check_slot_mapping(2, 3, pool, 64, None) == pkv.PKV_EINVAL  # misaligned
 
 
 def test_workspace_bytes_layout():
