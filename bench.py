@@ -331,6 +331,10 @@ def main(argv=None) -> int:
     # arguments marshalled once per rotation set (the binding's prepared calls): per-step Python marshalling would
     # otherwise outlast the kernel and leave the GPU idle between steps
     for d in sets:
+        if not qkv:
+            # the append alone, timed for the record (the fused step does it inside its launch)
+            d["append_only"] = pkv.prepare_paged_kv_append(d["k_new"], d["v_new"], d["slots"], d["k_pool"],
+                                                           d["v_pool"])
         if qkv:
             qc = d["qkv_case"]
             d["append"] = pkv.prepare_split_qkv_norm_rope_into_paged_cache_varlen(
@@ -384,16 +388,19 @@ def main(argv=None) -> int:
 
     K = args.steps
 
-    def timed(fn):
-        """Milliseconds per iteration of K back-to-back calls of fn(i), between two events on the current stream."""
+    def timed_n(fn, n):
+        """Milliseconds per iteration of n back-to-back calls of fn(i), between two events on the current stream."""
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
-        for i in range(K):
+        for i in range(n):
             fn(i)
         end.record()
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / K
+        return start.elapsed_time(end) / n
+
+    def timed(fn):
+        return timed_n(fn, K)
 
     # No event inside a timed region: an event pair costs ~7 us of stream time here, more than a kernel's launch gap.
     # The step region gives value; when a step is one launch (the fused single-pass step) that launch's average
@@ -421,6 +428,30 @@ def main(argv=None) -> int:
     else:
         ms_per_step = timed(lambda i: step(sets[i % R]))
         attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["call"]())])
+
+    # Per-step spread: REPS regions of C back-to-back steps each (an event pair per region), median and p90 of
+    # the per-step times.
+    REPS = 20
+    C = max(1, min(100, K // REPS))
+    per_step = []
+    if not args.graph:
+        for rr in range(REPS):
+            per_step.append(timed_n(lambda i: step(sets[(rr * C + i) % R]), C))
+    spread = None
+    if per_step:
+        spread = {"median_ms": round(float(np.median(per_step)), 5),
+                  "p90_ms": round(float(np.percentile(per_step, 90)), 5),
+                  "regions": REPS, "steps_per_region": C}
+
+    append_info = None
+    if not qkv:
+        ab = float(np.mean([d["bytes"]["append"] for d in sets]))
+        app_ms = timed(lambda i: sets[i % R]["append_only"]())
+        append_info = {"kernel": "append_kernel (pkv_paged_kv_append)", "ms": round(float(app_ms), 5),
+                       "algorithmic_bytes": int(ab), "achieved_GBs": round(ab / (app_ms * 1e-3) / 1e9, 2),
+                       "calls_per_s": round(1e3 / app_ms, 1),
+                       "timing": "region of back-to-back append calls / calls"}
+        log("append alone: %s" % append_info)
 
     qkv_info = None
     if qkv:
@@ -488,6 +519,8 @@ def main(argv=None) -> int:
         "bytes_per_step": {"attention": int(attn_bytes),
                            ("qkv_step" if qkv else "append"): int(np.mean([d["bytes"]["append"] for d in sets]))},
         "qkv_kernel": qkv_info,
+        "append_kernel": append_info,
+        "step_spread": spread,
         "roofline": {
             "bound": "hbm",
             "achieved": round(float(achieved), 2),
