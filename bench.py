@@ -49,6 +49,8 @@ WORKLOADS = {
     "c5": ("MHA wide head: B=128, Hq=Hkv=16, D=256, BS=32, L=4096, K/V~U(-1,1), scale 1/16", 0, 1),
     "v1": ("speculative verification, varlen (Llama-3-8B-shaped batch): B=32, Hq=32, Hkv=8, D=128, BS=16, 4 new rows "
            "per sequence, final L~U[512,2048]", 0, 4),
+    "v2": ("speculative verification of 8 draft tokens, varlen (Llama-3-8B-shaped batch): B=32, Hq=32, Hkv=8, D=128, "
+           "BS=16, 8 new rows per sequence, final L~U[512,2048]", 0, 4),
     "w1": ("sliding-window decode on the Llama-3-8B-shaped batch: B=32, Hq=32, Hkv=8, D=128, BS=16, L~U[512,2048], "
            "window 512", 0, 8),
     "r1": ("Qwen3-8B-shaped decode step from the QKV projection: split QKV + q/k RMSNorm + RoPE + paged-cache write, "

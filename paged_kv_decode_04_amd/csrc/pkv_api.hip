@@ -544,10 +544,12 @@ int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     const int G = num_q_heads / pool.num_kv_heads;
     const int R = 16 / G;
     const int64_t qmax = max_q_len > 0 && max_q_len < total_q ? max_q_len : total_q;
-    const int64_t tiles_per_seq = (qmax + R - 1) / R;
-    // workgroups that find work: at most one per R new rows plus one partial tile per sequence
+    // Two tiles per workgroup (one K/V stream for both) once a sequence can have more than one tile.
+    const int QT = qmax > R ? 2 : 1;
+    const int64_t tiles_per_seq = (qmax + QT * R - 1) / (QT * R);  // tile-group slots
+    // workgroups that find work: at most one per QT * R new rows plus one partial group per sequence
     int64_t active = (int64_t)num_seqs * tiles_per_seq;
-    const int64_t bound = ((int64_t)total_q + R - 1) / R + num_seqs;
+    const int64_t bound = ((int64_t)total_q + QT * R - 1) / (QT * R) + num_seqs;
     if (active > bound)
         active = bound;
     active *= pool.num_kv_heads;
@@ -591,6 +593,7 @@ int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     p.M = max_blocks_per_seq;
     p.T = total_q;
     p.R = R;
+    p.QT = QT;
     p.tiles_per_seq = (int32_t)tiles_per_seq;
     p.num_splits = S;
     p.chunk_blocks = 0;

@@ -52,7 +52,8 @@ struct VarlenParams {
     const int32_t *pos_offsets;   // [B]
     int32_t Hq, Hkv, G, N, M, T;
     int32_t R;                    // new rows per tile (16 / G)
-    int32_t tiles_per_seq;        // tile slots per (sequence, kv head) in the grid
+    int32_t QT;                   // tiles per workgroup sharing each K/V load (1 or 2)
+    int32_t tiles_per_seq;        // tile-group slots per (sequence, kv head) in the grid
     int32_t num_splits;           // 1 = one pass
     int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(nb / S) per tile
     float scale_log2;

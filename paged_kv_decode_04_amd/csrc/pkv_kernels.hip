@@ -611,10 +611,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 // One workgroup per (sequence, tile slot, kv head[, split]).  A tile is R = 16 / G consecutive new rows of one
 // sequence; its 16 matrix-core columns are the (row, head) pairs c = row * G + head, so every K/V byte a workgroup
 // loads serves all R rows and the whole GQA group; each column carries its own causal limit (RowLimits).  Tile slot
-// j takes the sequence's tiles j, j + tiles_per_seq, ... (any q length is covered whatever the host's estimate).
+// j takes the sequence's tile groups j, j + tiles_per_seq, ... (any q length is covered whatever the host's
+// estimate).  A group is QT consecutive tiles that share every K/V load: each unit's fragments feed QT tiles' score
+// and P.V products (QT = 2 when a sequence has more than one tile: half the K/V traffic of one tile per workgroup).
 // With splits, phase 1 writes every split of every valid column -- an empty one as m = -1e30, l = 0, O = 0 -- so
 // the combine needs no per-row split count.
-template <int D, int BS, int NW, bool SPLIT>
+template <int D, int BS, int NW, bool SPLIT, int QT>
 __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
     constexpr int KC = D / 32;
     constexpr int VC = D / 16;
@@ -682,19 +684,26 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
     float *sm_l = smem + NW * 16;
     float *sm_o = smem + 2 * NW * 16;
 
-    for (int tile = slot; tile * p.R < qlen; tile += p.tiles_per_seq) {
-        const int i0 = tile * p.R;
-        const int nrows = min(p.R, qlen - i0);
-        const int ncols = nrows * p.G;
-        // column r of this lane: new row i0 + r / G, query head hk * G + r % G
-        const int crow = r / p.G;
-        const bool col_ok = r < ncols;
-        RowLimits lim;
-        lim.lo = 0;
-        lim.first = min(pos + i0, cap - 1);
-        lim.all = min(pos + i0 + nrows - 1, cap - 1);
-        lim.col = col_ok ? min(pos + i0 + crow, cap - 1) : -1;
-        const int nb = (lim.all + 1 + BS - 1) / BS;
+    // Tile group g (QT consecutive tiles) of this slot: g = slot, slot + tiles_per_seq, ...
+    for (int grp = slot; grp * QT * p.R < qlen; grp += p.tiles_per_seq) {
+        // per tile t of the group: rows i0[t] .. i0[t] + nrows[t] - 1 of the sequence's new rows (nrows may be 0)
+        int i0[QT], nrows[QT], crow = r / p.G;
+        bool col_ok[QT];
+        RowLimits lim[QT];
+        int last_all = -1;  // the group's last row any column attends
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+            i0[t] = (grp * QT + t) * p.R;
+            nrows[t] = max(0, min(p.R, qlen - i0[t]));
+            col_ok[t] = r < nrows[t] * p.G;  // column r: new row i0 + r / G, query head hk * G + r % G
+            lim[t].lo = 0;
+            lim[t].first = min(pos + i0[t], cap - 1);
+            lim[t].all = min(pos + i0[t] + nrows[t] - 1, cap - 1);
+            lim[t].col = col_ok[t] ? min(pos + i0[t] + crow, cap - 1) : -1;
+            if (nrows[t] > 0)
+                last_all = max(last_all, lim[t].all);
+        }
+        const int nb = (last_all + 1 + BS - 1) / BS;
         int b0 = 0, b1 = nb;
         if (SPLIT) {
             const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (nb + p.num_splits - 1) / p.num_splits;
@@ -702,25 +711,27 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
             b1 = min(nb, b0 + chunk);
         }
         const int u_begin = b0 * SPB;
-        const int u_end = min(b1 * SPB, (lim.all + 1 + 15) >> 4);
+        const int u_end = min(b1 * SPB, (last_all + 1 + 15) >> 4);
         const int u_first = u_begin + wave;
         const int n_units = u_first < u_end ? (u_end - u_first + NW - 1) / NW : 0;
 
-        f16x8 qf[KC];
-        {
-            const int tok = q0 + i0 + (col_ok ? crow : 0);
-            const int hq = hk * p.G + (col_ok ? r % p.G : 0);
-            const _Float16 *qrow = p.q + ((int64_t)tok * p.Hq + hq) * D + 8 * g4;
+        f16x8 qf[QT][KC];
+        f32x4 o[QT][VC];
+        float m_run[QT], l_run[QT];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+            const int tok = q0 + i0[t] + (col_ok[t] ? crow : 0);
+            const int hq = hk * p.G + (col_ok[t] ? r % p.G : 0);
+            const _Float16 *qrow = p.q + ((int64_t)min(tok, p.T - 1) * p.Hq + hq) * D + 8 * g4;
 #pragma unroll
             for (int c = 0; c < KC; ++c)
-                qf[c] = *reinterpret_cast<const f16x8 *>(qrow + 32 * c);
-        }
-        f32x4 o[VC];
+                qf[t][c] = *reinterpret_cast<const f16x8 *>(qrow + 32 * c);
 #pragma unroll
-        for (int c = 0; c < VC; ++c)
-            o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        float m_run = kNegBig;
-        float l_run = 0.f;
+            for (int c = 0; c < VC; ++c)
+                o[t][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            m_run[t] = kNegBig;
+            l_run[t] = 0.f;
+        }
 
         if (n_units > 0) {
             Frag<D, BS> f[NS];
@@ -748,8 +759,15 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
                     load_unit<D, BS>(f[jn], k_ptr(blk, uu[jn]), v_ptr(blk, uu[jn]), k_lane, v_lane,
                                      k + NS - 1 < n_units && !dead[jn]);
                     raw_q[j] = raw_block(u_first + min(k + 2 * NS - 1, n_units - 1) * NW);
-                    compute_unit<D, BS>(f[j], qf, o, m_run, l_run, uu[j], lim, dead[j], r, g4, p.scale_log2, -1,
-                                        nullptr, nullptr, nullptr, nullptr, k_lane, v_lane);
+                    // Every tile of the group uses this unit's fragments.  Later tiles first: a tile zeroes the V
+                    // rows past its own last row, which every earlier tile leaves unused too.
+#pragma unroll
+                    for (int t = QT - 1; t >= 0; --t) {
+                        if (nrows[t] > 0)  // wave-uniform
+                            compute_unit<D, BS>(f[j], qf[t], o[t], m_run[t], l_run[t], uu[j], lim[t], dead[j], r,
+                                                g4, p.scale_log2, -1, nullptr, nullptr, nullptr, nullptr, k_lane,
+                                                v_lane);
+                    }
                     if (++k >= n_units)
                         goto tile_done;
                 }
@@ -757,55 +775,61 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
         tile_done:;
         }
 
-        l_run = rows_sum(l_run);
-        if (tile != slot)
-            __syncthreads();  // the previous tile's merge has read the LDS
-        // cross-wave merge, as in decode_kernel
-        if (g4 == 0) {
-            sm_m[wave * 16 + r] = m_run;
-            sm_l[wave * 16 + r] = l_run;
-        }
-        __syncthreads();
-        float Mc = kNegBig;
+        // cross-wave merge, as in decode_kernel, one tile of the group after the other through the same LDS
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
-            Mc = fmaxf(Mc, sm_m[w * 16 + r]);
-        float den = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w)
-            den += exp2_fast(sm_m[w * 16 + r] - Mc) * sm_l[w * 16 + r];
-        const int64_t my_row = (int64_t)(q0 + i0 + crow) * p.Hq + hk * p.G + r % p.G;  // token * Hq + hq
-        {
-            const float a = exp2_fast(m_run - Mc);
-            const float f = SPLIT ? a : (den > 0.f ? a / den : 0.f);
-            if (col_ok) {
-                float *dst = sm_o + (wave * 16 + r) * DP + 4 * g4;
-#pragma unroll
-                for (int c = 0; c < VC; ++c) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        dst[16 * c + e] = o[c][e] * f;
-                }
+        for (int t = 0; t < QT; ++t) {
+            if (nrows[t] == 0)
+                break;  // later tiles of the group are empty too
+            const float lt = rows_sum(l_run[t]);
+            if (grp != slot || t > 0)
+                __syncthreads();  // the previous merge has read the LDS
+            if (g4 == 0) {
+                sm_m[wave * 16 + r] = m_run[t];
+                sm_l[wave * 16 + r] = lt;
             }
-            if (SPLIT && wave == 0 && g4 == 0 && col_ok) {
-                // a split without rows (b0 >= b1) leaves M = -1e30 and l = 0: weight 0 in the combine
-                p.part_m[my_row * p.num_splits + split] = Mc * kLn2;
-                p.part_l[my_row * p.num_splits + split] = den;
-            }
-        }
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < ncols * D; idx += NW * 64) {
-            const int c = idx / D;
-            const int d = idx - c * D;
-            float num = 0.f;
+            __syncthreads();
+            float Mc = kNegBig;
 #pragma unroll
             for (int w = 0; w < NW; ++w)
-                num += sm_o[(w * 16 + c) * DP + d];
-            const int64_t row = (int64_t)(q0 + i0 + c / p.G) * p.Hq + hk * p.G + c % p.G;  // token * Hq + hq
-            if (!SPLIT)
-                p.out[row * D + d] = (_Float16)num;
-            else
-                p.part_o[(row * p.num_splits + split) * D + d] = num;
+                Mc = fmaxf(Mc, sm_m[w * 16 + r]);
+            float den = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                den += exp2_fast(sm_m[w * 16 + r] - Mc) * sm_l[w * 16 + r];
+            const int64_t my_row = (int64_t)(q0 + i0[t] + crow) * p.Hq + hk * p.G + r % p.G;  // token * Hq + hq
+            {
+                const float a = exp2_fast(m_run[t] - Mc);
+                const float fs = SPLIT ? a : (den > 0.f ? a / den : 0.f);
+                if (col_ok[t]) {
+                    float *dst = sm_o + (wave * 16 + r) * DP + 4 * g4;
+#pragma unroll
+                    for (int c = 0; c < VC; ++c) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            dst[16 * c + e] = o[t][c][e] * fs;
+                    }
+                }
+                if (SPLIT && wave == 0 && g4 == 0 && col_ok[t]) {
+                    // a split without rows (b0 >= b1) leaves M = -1e30 and l = 0: weight 0 in the combine
+                    p.part_m[my_row * p.num_splits + split] = Mc * kLn2;
+                    p.part_l[my_row * p.num_splits + split] = den;
+                }
+            }
+            __syncthreads();
+            const int ncols = nrows[t] * p.G;
+            for (int idx = threadIdx.x; idx < ncols * D; idx += NW * 64) {
+                const int c = idx / D;
+                const int d = idx - c * D;
+                float num = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+                    num += sm_o[(w * 16 + c) * DP + d];
+                const int64_t row = (int64_t)(q0 + i0[t] + c / p.G) * p.Hq + hk * p.G + c % p.G;  // token * Hq + hq
+                if (!SPLIT)
+                    p.out[row * D + d] = (_Float16)num;
+                else
+                    p.part_o[(row * p.num_splits + split) * D + d] = num;
+            }
         }
     }
 }
@@ -1020,10 +1044,14 @@ static hipError_t launch_varlen_t(const VarlenParams &p, int num_seqs, bool spli
     dim3 grid((unsigned)((int64_t)num_seqs * p.tiles_per_seq * p.Hkv * (split ? p.num_splits : 1)), 1u, 1u);
     dim3 block(NW * 64);
     const size_t lds = varlen_lds_bytes(D, NW);
-    if (split)
-        hipLaunchKernelGGL((varlen_kernel<D, BS, NW, true>), grid, block, lds, stream, p);
+    if (split && p.QT == 2)
+        hipLaunchKernelGGL((varlen_kernel<D, BS, NW, true, 2>), grid, block, lds, stream, p);
+    else if (split)
+        hipLaunchKernelGGL((varlen_kernel<D, BS, NW, true, 1>), grid, block, lds, stream, p);
+    else if (p.QT == 2)
+        hipLaunchKernelGGL((varlen_kernel<D, BS, NW, false, 2>), grid, block, lds, stream, p);
     else
-        hipLaunchKernelGGL((varlen_kernel<D, BS, NW, false>), grid, block, lds, stream, p);
+        hipLaunchKernelGGL((varlen_kernel<D, BS, NW, false, 1>), grid, block, lds, stream, p);
     return hipGetLastError();
 }
 template <int D, int BS>

@@ -404,7 +404,21 @@ def config_v1(rotation: int = 0) -> VarlenCase:
                              extra_blocks=int(math.ceil(0.10 * nblocks)), M=128)
 
 
-VARLEN_CONFIGS = {"v1": config_v1}
+SEEDS["v2"] = 0xC0FFEE12
+
+
+def config_v2(rotation: int = 0) -> VarlenCase:
+    """Speculative verification of 8 draft tokens on the Llama-3-8B-shaped batch: B=32, 32/8 heads, D=128, BS=16,
+    8 new rows per sequence whose final lengths are U{512..2048}, pool = blocks + 10%."""
+    seed = SEEDS["v2"]
+    final = _rng(seed, rotation, "lens").integers(512, 2048, size=32, endpoint=True).astype(np.int32)
+    ql = np.full(32, 8, dtype=np.int32)
+    nblocks = int(sum((int(L) + 15) // 16 for L in final))
+    return build_varlen_case("v2", 32, 32, 8, 128, 16, ql, final - ql, seed, rotation,
+                             extra_blocks=int(math.ceil(0.10 * nblocks)), M=128)
+
+
+VARLEN_CONFIGS = {"v1": config_v1, "v2": config_v2}
 
 
 def algorithmic_bytes_varlen(case: VarlenCase) -> dict:

@@ -11,7 +11,8 @@ from test_gpu_parity import assert_close, say, torch_cuda, _dev  # noqa: F401  (
 
 pytestmark = pytest.mark.gpu
 
-# (Hq, Hkv, D, BS, new rows per sequence, positions of their first new row).  Tiles hold 16 / G new rows, so these
+# (Hq, Hkv, D, BS, new rows per sequence, positions of their first new row).  Tiles hold 16 / G new rows (two tiles
+# per workgroup once a sequence has more than one), so these
 # cover G = 4 (4 rows per tile, ragged tiles, a sequence without new rows, 16 rows = 4 tiles), G = 1 with D = 256
 # (16 rows per tile), G = 16 (one row per tile), G = 3 (5 rows, 15 of 16 columns) and speculative-verify shapes.
 VARLEN_GEOMS = [
@@ -51,13 +52,29 @@ def test_varlen_matches_oracle(torch_cuda, geom, num_splits):
     assert_close(out, _reference(c), "varlen %s S=%d" % (geom, num_splits))
 
 
-def test_varlen_small_grid_estimate_still_covers_every_row(torch_cuda):
-    # max_q_len = 1 sizes the grid for one tile per sequence; the workgroups loop over the remaining tiles
+@pytest.mark.parametrize("max_q_len", [1, 5])
+def test_varlen_small_grid_estimate_still_covers_every_row(torch_cuda, max_q_len):
+    # max_q_len = 1 sizes the grid for one tile per sequence (4 rows at G = 4), 5 for one group of two tiles
+    # (8 rows); the workgroups loop over the remaining tiles or groups
     c = W.build_varlen_case("varlen", 3, 8, 2, 128, 16, (9, 1, 14), (5, 200, 31), 951)
     ref = _reference(c)
     for S in (1, 2):
-        out = _run_case(torch_cuda, c, S, max_q_len=1)
-        assert_close(out, ref, "varlen max_q_len=1 S=%d" % S)
+        out = _run_case(torch_cuda, c, S, max_q_len=max_q_len)
+        assert_close(out, ref, "varlen max_q_len=%d S=%d" % (max_q_len, S))
+
+
+def test_varlen_v2_full_size(torch_cuda):
+    """Speculative verification with 8 new rows per sequence (two tiles of 4 rows sharing each K/V load), the
+    bench workload at full size: 256 sampled (token, head) rows against the oracle."""
+    c = W.config_v2()
+    out = _run_case(torch_cuda, c, 0, max_q_len=8)
+    kp, vp = c.k_pool.copy(), c.v_pool.copy()
+    oracle.paged_kv_append(c.k_new, c.v_new, c.slot_mapping, kp, vp)
+    rng = np.random.default_rng(961)
+    units = np.stack([rng.integers(0, c.T, 256), rng.integers(0, c.Hq, 256)], axis=1).astype(np.int32)
+    units[:3] = [[0, 0], [c.T - 1, c.Hq - 1], [7, 5]]
+    ref = oracle.varlen_attention(c.q, kp, vp, c.block_tables, c.cu_seqlens_q, c.pos_offsets, c.scale, units=units)
+    assert_close(out[units[:, 0], units[:, 1]], ref, "v2 (8 new rows per sequence)")
 
 
 def test_varlen_one_new_row_is_decode_attention(torch_cuda):
