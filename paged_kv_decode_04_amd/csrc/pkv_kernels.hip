@@ -889,19 +889,24 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }
 
 // Paged KV append [kapsl-backends 0.1.1, src/gguf_native.rs: launch_kv_write,
-// launch_batch_kv_write]: one thread per (token, kv head, 8-dim piece).  The K
-// piece is one 16-byte store into the row's panel ([D/8][16][8]); the V piece is
-// 8 two-byte stores into the transposed panel ([D][16]).
+// launch_batch_kv_write]: one thread per (token, kv head, 8-dim piece), tokens
+// fastest, so that neighbouring lanes take neighbouring tokens of the same
+// (head, piece).  The K piece is one 16-byte store into the row's panel
+// ([D/8][16][8]); the V piece is 8 two-byte stores into the transposed panel
+// ([D][16]).  When consecutive tokens have consecutive slots (a sequence's new
+// rows), 16 lanes fill a whole 256-byte run of a K panel and whole 32-byte
+// rows of a V panel.
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int pieces = p.D / 8;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = (int64_t)p.T * p.Hkv * pieces;
     if (gid >= total)
         return;
-    const int c = (int)(gid % pieces);
-    const int64_t th = gid / pieces;  // token * Hkv + head
-    const int h = (int)(th % p.Hkv);
-    const int i = (int)(th / p.Hkv);
+    const int i = (int)(gid % p.T);
+    const int64_t hc = gid / p.T;  // head * pieces + piece
+    const int c = (int)(hc % pieces);
+    const int h = (int)(hc / pieces);
+    const int64_t th = (int64_t)i * p.Hkv + h;  // token * Hkv + head
     const int64_t slot = p.slot_mapping[i];
     if (slot < 0 || slot >= (int64_t)p.N * p.BS)
         return;
