@@ -3,7 +3,9 @@
 A step is one pass of the whole path over one batch: the paged KV append of every sequence's newest row, then
 paged decode attention (single pass, or split-K phase 1 + combine, as the workload's dispatch mode says).  By default
 the step is the library's fused decode step (pkv_paged_decode_step: append and attention in one launch); --unfused
-times the two separate entry points (pkv_paged_kv_append, then pkv_paged_decode_attention).  The r workloads start
+times the two separate entry points (pkv_paged_kv_append, then pkv_paged_decode_attention).  The varlen workloads
+(v1, v2: several new rows per sequence) time the varlen step (pkv_paged_varlen_step, one launch; --unfused:
+pkv_paged_kv_append, then pkv_paged_varlen_attention).  The r workloads start
 one step earlier, from the QKV projection rows: r1 is the decode step from those rows in one launch
 (pkv_paged_decode_step_qkv: q/k RMS norm, RoPE, the new K/V rows written, attention; --unfused: the QKV-to-cache
 kernel, then attention); r2 times the QKV-to-cache kernel alone on a chunked-prefill batch.  Inputs
@@ -66,10 +68,10 @@ QKV_ONLY = {"r2"}  # QKV-step workloads whose step is that kernel alone (a 512-r
 
 
 def step_is_fused(config: str, unfused: bool) -> bool:
-    """Whether bench.py times the workload's step as one fused launch (pkv_paged_decode_step, or
-    pkv_paged_decode_step_qkv for a decode step from QKV rows); varlen, sliding-window and QKV-only workloads launch
-    their kernels one after the other."""
-    return not unfused and config[0] != "v" and config not in WINDOWS and config not in QKV_ONLY
+    """Whether bench.py times the workload's step through the library's step entry point (pkv_paged_decode_step,
+    pkv_paged_varlen_step, or pkv_paged_decode_step_qkv for a decode step from QKV rows), one launch where the grid
+    allows; sliding-window and QKV-only workloads launch their kernels one after the other."""
+    return not unfused and config not in WINDOWS and config not in QKV_ONLY
 
 
 def log(*a):
@@ -78,7 +80,7 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("pkv_kernels.hip", "pkv_qkv.hip", "pkv_api.hip", "pkv_internal.h"):
+    for name in ("pkv_kernels.hip", "pkv_qkv.hip", "pkv_check.hip", "pkv_api.hip", "pkv_internal.h", "pkv_lanes.h"):
         with open(os.path.join(ROOT, "paged_kv_decode_04_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -229,7 +231,7 @@ def main(argv=None) -> int:
                     help="also run a plain copy kernel over this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--unfused", action="store_true",
-                    help="append and attention as two launches instead of the fused decode step")
+                    help="append and attention as two launches instead of the library's step entry point")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph holding 32 consecutive steps instead of eager launches")
     args = ap.parse_args(argv)
@@ -351,6 +353,10 @@ def main(argv=None) -> int:
             else:
                 d["call"] = pkv.prepare_paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
                                                                qc.varlen.scale, d["out"], num_splits=splits)
+        elif fused and varlen:  # one launch: the attention workgroups write the new rows themselves
+            d["call"] = pkv.prepare_paged_varlen_step(d["q"], d["k_new"], d["v_new"], d["k_pool"], d["v_pool"],
+                                                      d["bt"], d["cu"], d["pos"], d["case"].scale,
+                                                      int(d["case"].q_lens.max()), d["out"], num_splits=splits)
         elif fused:
             d["call"] = pkv.prepare_decode_step(d["q"], d["k_new_all"], d["v_new_all"], d["k_pool"], d["v_pool"],
                                                 d["bt"], d["cl"], d["case"].scale, d["out"], num_splits=splits)
@@ -505,6 +511,7 @@ def main(argv=None) -> int:
             "step": ("pkv_split_qkv_norm_rope_into_paged_cache_varlen" if qkv_only else
                      "fused (pkv_paged_decode_step_qkv)" if qkv and fused else
                      "pkv_split_qkv_norm_rope_into_paged_cache_varlen + pkv_paged_decode_attention" if qkv else
+                     "fused (pkv_paged_varlen_step)" if fused and varlen else
                      "fused (pkv_paged_decode_step)" if fused else
                      "pkv_paged_kv_append + pkv_paged_varlen_attention" if varlen else
                      "pkv_paged_kv_append + pkv_paged_decode_attention_window (window %d)" % window if window else

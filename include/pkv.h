@@ -304,6 +304,35 @@ PKV_API int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool
                                int32_t num_splits, int32_t max_q_len, int32_t max_context_hint, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_paged_varlen_step -- the varlen step (append + varlen attention): the
+ *   i-th new token of sequence s (token cu_seqlens_q[s] + i) has its K and V
+ *   rows k_new[token][h][:], v_new[token][h][:] written to row
+ *   p = pos_offsets[s] + i of the sequence (block block_tables[s][p / BS],
+ *   row p % BS, every kv head h), then every new row attends as in
+ *   pkv_paged_varlen_attention over the updated pools.  A row whose table
+ *   entry names no pool block is not written.
+ *   [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs: the q_len > 1 branch
+ *   of paged_decode_attention, whose new rows are already in the cache, and
+ *   split_qkv_norm_rope_into_paged_cache_varlen, which puts them there]
+ *   Launches: one pass with max_q_len <= 32 and no more workgroups than the
+ *   device's CUs gives one launch whose workgroups write the new rows
+ *   themselves (each 16-row panel holding new rows is written back whole,
+ *   its other rows unchanged); otherwise a launch writes the new rows, then
+ *   attention runs.  Results are identical either way.
+ *   k_new, v_new: [total_q_tokens][Hkv][D] fp16, 16-byte aligned.
+ *   max_q_len (required, >= 1): no sequence may have more new rows; it picks
+ *   the launches (a sequence with more leaves its rows past the 32nd
+ *   unspecified in the one-launch form; memory stays safe).  The blocks that
+ *   receive a sequence's new rows must belong to that sequence alone during
+ *   the call.  Other arguments and errors as pkv_paged_varlen_attention.
+ * ------------------------------------------------------------------------- */
+PKV_API int pkv_paged_varlen_step(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                          uint16_t *v_pool, pkv_pool_desc pool, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
+                          int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads, float scale, uint16_t *out,
+                          int32_t num_splits, int32_t max_q_len, int32_t max_context_hint, void *stream);
+
+/* ---------------------------------------------------------------------------
  * pkv_split_qkv_norm_rope_into_paged_cache_varlen -- the step that feeds
  *   paged attention: from the fused QKV projection rows, RMS-normalise the
  *   query and key heads (qk_mode 1), rotate them (RoPE), write the queries to

@@ -519,7 +519,8 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
 int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool, pkv_pool_desc pool,
                 const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q,
                 const int32_t *pos_offsets, int32_t num_seqs, int32_t total_q, int32_t num_q_heads, float scale,
-                uint16_t *out, int32_t num_splits, int32_t max_q_len, int32_t max_context_hint, hipStream_t stream) {
+                uint16_t *out, int32_t num_splits, int32_t max_q_len, int32_t max_context_hint, hipStream_t stream,
+                const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr) {
     int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
     if (rc)
         return rc;
@@ -537,6 +538,15 @@ int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
         return fail(PKV_EINVAL, "q, k_pool, v_pool and out must be 16-byte aligned");
     if (!aligned(block_tables, 4) || !aligned(cu_seqlens_q, 4) || !aligned(pos_offsets, 4))
         return fail(PKV_EINVAL, "block_tables, cu_seqlens_q and pos_offsets must be 4-byte aligned");
+    const bool step = k_new != nullptr || v_new != nullptr;
+    if (step) {
+        if (!k_new || !v_new)
+            return fail(PKV_EINVAL, "null device pointer (k_new=%p v_new=%p)", k_new, v_new);
+        if (!aligned(k_new, 16) || !aligned(v_new, 16))
+            return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+        if (max_q_len < 1)
+            return fail(PKV_EINVAL, "max_q_len must bound every sequence's new rows (>= 1, got %d)", max_q_len);
+    }
     DeviceFacts facts;
     rc = device_facts(&facts);
     if (rc)
@@ -572,13 +582,38 @@ int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     if ((int64_t)num_seqs * tiles_per_seq * pool.num_kv_heads * S > INT32_MAX || S > 65535)
         return fail(PKV_EINVAL, "varlen grid (%d sequences x %lld tiles x %d kv heads x %d splits) is too large",
                     num_seqs, (long long)tiles_per_seq, pool.num_kv_heads, S);
+    // The varlen step in one launch: one pass, at most kStepFusedRows new rows per sequence (the launch keeps
+    // them in LDS), one tile per group at head dim 256 (two would spill), and no more workgroups than one round of
+    // the CUs -- as for the decode step, writes issued from inside a long, read-saturated launch cost more than a
+    // launch of their own.
+    const bool fused = step && S == 1 && max_q_len <= pkv::kStepFusedRows && (QT == 1 || pool.head_dim <= 128) &&
+                       (int64_t)num_seqs * tiles_per_seq * pool.num_kv_heads <= facts.cu_count;
     int waves = pkv::max_waves_per_group(pool.head_dim);
     const size_t limit = facts.lds_per_block > 0 ? (size_t)facts.lds_per_block : (size_t)65536;
-    while (waves > 1 && pkv::varlen_lds_bytes(pool.head_dim, waves) > limit)
+    while (waves > 1 && pkv::varlen_lds_bytes(pool.head_dim, waves, fused) > limit)
         waves >>= 1;
-    if (pkv::varlen_lds_bytes(pool.head_dim, waves) > limit)
+    if (pkv::varlen_lds_bytes(pool.head_dim, waves, fused) > limit)
         return fail(PKV_EUNSUPPORTED, "varlen needs %zu LDS bytes, the device allows %zu",
-                    pkv::varlen_lds_bytes(pool.head_dim, waves), limit);
+                    pkv::varlen_lds_bytes(pool.head_dim, waves, fused), limit);
+    if (step && !fused) {
+        // the new rows' own launch, then attention over the updated pools
+        pkv::AppendParams a;
+        memset(&a, 0, sizeof a);
+        a.k = reinterpret_cast<const _Float16 *>(k_new);
+        a.v = reinterpret_cast<const _Float16 *>(v_new);
+        a.block_tables = block_tables;
+        a.k_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
+        a.v_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
+        a.T = total_q;
+        a.Hkv = pool.num_kv_heads;
+        a.D = pool.head_dim;
+        a.BS = pool.block_size;
+        a.N = pool.num_blocks;
+        a.M = max_blocks_per_seq;
+        hipError_t e = pkv::launch_append_varlen(a, cu_seqlens_q, pos_offsets, num_seqs, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "varlen append kernel launch");
+    }
 
     pkv::VarlenParams p;
     memset(&p, 0, sizeof p);
@@ -601,6 +636,12 @@ int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     p.k_pool = reinterpret_cast<const _Float16 *>(k_pool);
     p.v_pool = reinterpret_cast<const _Float16 *>(v_pool);
     p.out = reinterpret_cast<_Float16 *>(out);
+    if (fused) {
+        p.k_new = reinterpret_cast<const _Float16 *>(k_new);
+        p.v_new = reinterpret_cast<const _Float16 *>(v_new);
+        p.k_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
+        p.v_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
+    }
     if (S == 1) {
         hipError_t e = pkv::launch_varlen(p, num_seqs, pool.head_dim, pool.block_size, waves, false, stream);
         if (e != hipSuccess)
@@ -1102,6 +1143,18 @@ int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool, const 
     return varlen_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, cu_seqlens_q, pos_offsets, num_seqs,
                        total_q_tokens, num_q_heads, scale, out, num_splits, max_q_len, max_context_hint,
                        static_cast<hipStream_t>(stream));
+}
+
+int pkv_paged_varlen_step(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                          uint16_t *v_pool, pkv_pool_desc pool, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
+                          int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads, float scale, uint16_t *out,
+                          int32_t num_splits, int32_t max_q_len, int32_t max_context_hint, void *stream) {
+    if (num_seqs > 0 && total_q_tokens > 0 && (!k_new || !v_new))
+        return fail(PKV_EINVAL, "null device pointer (k_new=%p v_new=%p)", k_new, v_new);
+    return varlen_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, cu_seqlens_q, pos_offsets, num_seqs,
+                       total_q_tokens, num_q_heads, scale, out, num_splits, max_q_len, max_context_hint,
+                       static_cast<hipStream_t>(stream), k_new, v_new);
 }
 
 }  // extern "C"

@@ -63,6 +63,12 @@ struct VarlenParams {
     float *part_o;                // [T][Hq][S][D]             (splits)
     float *part_m;                // [T][Hq][S]
     float *part_l;                // [T][Hq][S]
+    // fused varlen step (k_new non-null, one pass): token t's K/V rows ([T][Hkv][D]) go to row pos[s] + i of its
+    // sequence in k_dst / v_dst (the same pools)
+    const _Float16 *k_new;
+    const _Float16 *v_new;
+    _Float16 *k_dst;
+    _Float16 *v_dst;
 };
 
 struct CombineParams {
@@ -128,11 +134,15 @@ size_t decode_lds_bytes(int head_dim, int G, int waves);
 hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size, int waves,
                          bool split, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int head_dim, hipStream_t stream);
-size_t varlen_lds_bytes(int head_dim, int waves);
+size_t varlen_lds_bytes(int head_dim, int waves, bool fused = false);
+// New rows per sequence the one-launch varlen step holds in LDS.
+constexpr int kStepFusedRows = 32;
 hipError_t launch_varlen(const VarlenParams &p, int num_seqs, int head_dim, int block_size, int waves, bool split,
                          hipStream_t stream);
 hipError_t launch_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream);
+hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
+                                int num_seqs, hipStream_t stream);
 hipError_t launch_qkv_cache(const QkvParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_check(const CheckParams &p, hipStream_t stream);
 

@@ -153,15 +153,41 @@ struct RowLimits {
 // fragment.  The patched fragment -- the unit's 16 rows as loaded, with row prow replaced -- is then written back
 // to the unit's panels (wb_k, wb_v): the pool update is whole cache lines, and no row but prow changes value.
 // A unit whose block id names no pool block (dead) is neither written nor used.
-template <int D, int BS>
+// MULTI (fused varlen step): rows prow .. prow_end-1 of the unit are new, pk / pv point to the LDS copy of row prow
+// (rows D halves apart); every one of them is patched before the write-back.
+template <int D, int BS, bool MULTI = false>
 __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D / 32], f32x4 (&o)[D / 16],
                                              float &m_run, float &l_run, int u, const RowLimits &lim, bool dead,
                                              int r, int g4,
                                              float scale_log2, int prow, const _Float16 *pk, const _Float16 *pv,
-                                             _Float16 *wb_k, _Float16 *wb_v, uint32_t k_lane, uint32_t v_lane) {
+                                             _Float16 *wb_k, _Float16 *wb_v, uint32_t k_lane, uint32_t v_lane,
+                                             int prow_end = 0) {
     constexpr int KC = Frag<D, BS>::KC;
     constexpr int VC = Frag<D, BS>::VC;
-    if (prow >= 0) {  // wave-uniform
+    if (MULTI && prow >= 0) {  // wave-uniform
+        if (r >= prow && r < prow_end) {  // K pieces 4c + g4 of row r
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                f.k[c] = *reinterpret_cast<const f16x8 *>(pk + (r - prow) * D + 32 * c + 8 * g4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // V dims 16c + r of rows 4*g4 + e
+            const int row = 4 * g4 + e;
+            if (row >= prow && row < prow_end) {
+#pragma unroll
+                for (int c = 0; c < VC; ++c)
+                    f.v[c][e] = pv[(row - prow) * D + 16 * c + r];
+            }
+        }
+        if (!dead) {  // the pool update: the patched panel written back whole, before any row is masked
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                *reinterpret_cast<f16x8 *>(reinterpret_cast<char *>(wb_k) + k_lane + 1024 * c) = f.k[c];
+#pragma unroll
+            for (int c = 0; c < VC; ++c)
+                *reinterpret_cast<f16x4 *>(reinterpret_cast<char *>(wb_v) + v_lane + 512 * c) = f.v[c];
+        }
+    } else if (!MULTI && prow >= 0) {  // wave-uniform
         if (r == prow) {  // K pieces 4c + g4
 #pragma unroll
             for (int c = 0; c < KC; ++c)
@@ -616,7 +642,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 // and P.V products (QT = 2 when a sequence has more than one tile: half the K/V traffic of one tile per workgroup).
 // With splits, phase 1 writes every split of every valid column -- an empty one as m = -1e30, l = 0, O = 0 -- so
 // the combine needs no per-row split count.
-template <int D, int BS, int NW, bool SPLIT, int QT>
+// FUSED (the fused varlen step, single pass): the new rows' K/V (k_new / v_new, token-major) are written into the
+// pools by this launch -- each 16-row unit holding new rows is patched from an LDS copy of its new rows whenever it
+// is computed and written back whole, so any interleaving of workgroups leaves the same bytes -- for the first
+// kFusedUnits units of a sequence's new rows: any kStepFusedRows consecutive rows fit.
+constexpr int kFusedUnits = (kStepFusedRows + 2 * 15) / 16;
+
+template <int D, int BS, int NW, bool SPLIT, int QT, bool FUSED = false>
 __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
     constexpr int KC = D / 32;
     constexpr int VC = D / 16;
@@ -668,6 +700,31 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
     const uint32_t v_lane = (uint32_t)(32 * r + 8 * g4);
     const int64_t head_off = (int64_t)hk * (BS * D);
     const int64_t block_stride = (int64_t)p.Hkv * (BS * D);
+
+    // Fused step: units nu0 .. nu0 + n_new_units - 1 hold the new rows pos .. pos + qlen - 1.  The wave that computes
+    // unit u in every tile group (u % NW: with one pass the range starts at unit 0) copies that unit's new rows to
+    // its LDS slot (K then V, 16 rows of D halves each per unit).
+    const int nu0 = pos >> 4;
+    const int n_new_units = FUSED && qlen > 0 ? min(kFusedUnits, ((pos + qlen - 1) >> 4) - nu0 + 1) : 0;
+    _Float16 *sm_new = reinterpret_cast<_Float16 *>(smem + merge_floats(D, 16, NW));
+    if (FUSED) {
+        for (int k = 0; k < n_new_units; ++k) {
+            const int u = nu0 + k;
+            if (u % NW != wave)
+                continue;
+            const int row0 = max(pos, 16 * u), row1 = min(pos + qlen, 16 * u + 16);
+            _Float16 *slot_k = sm_new + k * 32 * D;
+            _Float16 *slot_v = slot_k + 16 * D;
+            // lane-strided 16-byte chunks of the unit's new rows: chunk = row * (D / 8) + piece
+            for (int c = lane; c < (row1 - row0) * (D / 8); c += 64) {
+                const int rr = c / (D / 8), piece = c - rr * (D / 8);
+                const int64_t src = ((int64_t)(q0 + row0 - pos + rr) * p.Hkv + hk) * D + 8 * piece;
+                const int dst = (row0 - 16 * u + rr) * D + 8 * piece;
+                *reinterpret_cast<f16x8 *>(slot_k + dst) = *reinterpret_cast<const f16x8 *>(p.k_new + src);
+                *reinterpret_cast<f16x8 *>(slot_v + dst) = *reinterpret_cast<const f16x8 *>(p.v_new + src);
+            }
+        }
+    }
     auto raw_block = [&](int u) -> int { return uniform_load(bt, min(u, max_units - 1) / SPB); };
     auto resolve = [&](int raw, bool &dead) -> int {
         const int b = __builtin_amdgcn_readfirstlane(raw);
@@ -738,10 +795,12 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
             bool dead[NS];
             int uu[NS];
             int raw_q[NS];
+            int blk_of[NS];  // block of each pipeline slot (the fused step writes its patched units back there)
 #pragma unroll
             for (int j = 0; j < NS - 1; ++j) {
                 uu[j] = u_first + j * NW;
                 const int blk = resolve(start_known ? spec_raw[j] : raw_block(uu[j]), dead[j]);
+                blk_of[j] = blk;
                 load_unit<D, BS>(f[j], k_ptr(blk, uu[j]), v_ptr(blk, uu[j]), k_lane, v_lane,
                                  j < n_units && !dead[j]);
             }
@@ -756,17 +815,37 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
                     const int jn = (j + NS - 1) % NS;
                     uu[jn] = u_first + min(k + NS - 1, n_units - 1) * NW;
                     const int blk = resolve(raw_q[j], dead[jn]);
+                    blk_of[jn] = blk;
                     load_unit<D, BS>(f[jn], k_ptr(blk, uu[jn]), v_ptr(blk, uu[jn]), k_lane, v_lane,
                                      k + NS - 1 < n_units && !dead[jn]);
                     raw_q[j] = raw_block(u_first + min(k + 2 * NS - 1, n_units - 1) * NW);
                     // Every tile of the group uses this unit's fragments.  Later tiles first: a tile zeroes the V
                     // rows past its own last row, which every earlier tile leaves unused too.
+                    // fused step: the unit's new rows (if any) patched in and the unit written back (tile QT-1 only:
+                    // one patch and one write per unit load; the later tiles' calls see the patched fragment)
+                    int prow = -1, prow_end = 0;
+                    const _Float16 *pk = nullptr, *pv = nullptr;
+                    _Float16 *wk = nullptr, *wv = nullptr;
+                    if (FUSED) {
+                        const int kslot = uu[j] - nu0;
+                        if (kslot >= 0 && kslot < n_new_units) {
+                            prow = max(pos, 16 * uu[j]) - 16 * uu[j];
+                            prow_end = min(pos + qlen, 16 * uu[j] + 16) - 16 * uu[j];
+                            pk = sm_new + kslot * 32 * D + prow * D;
+                            pv = pk + 16 * D;
+                            wk = p.k_dst + (k_ptr(blk_of[j], uu[j]) - p.k_pool);
+                            wv = p.v_dst + (v_ptr(blk_of[j], uu[j]) - p.v_pool);
+                        }
+                    }
+                    bool patched = false;
 #pragma unroll
                     for (int t = QT - 1; t >= 0; --t) {
-                        if (nrows[t] > 0)  // wave-uniform
-                            compute_unit<D, BS>(f[j], qf[t], o[t], m_run[t], l_run[t], uu[j], lim[t], dead[j], r,
-                                                g4, p.scale_log2, -1, nullptr, nullptr, nullptr, nullptr, k_lane,
-                                                v_lane);
+                        if (nrows[t] > 0) {  // wave-uniform
+                            compute_unit<D, BS, true>(f[j], qf[t], o[t], m_run[t], l_run[t], uu[j], lim[t], dead[j],
+                                                      r, g4, p.scale_log2, patched ? -1 : prow, pk, pv, wk, wv,
+                                                      k_lane, v_lane, prow_end);
+                            patched = true;
+                        }
                     }
                     if (++k >= n_units)
                         goto tile_done;
@@ -965,6 +1044,49 @@ __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
     }
 }
 
+// The varlen step's append as its own launch: token t of sequence s (tokens cu[s] .. cu[s+1]-1) goes to row
+// pos[s] + (t - cu[s]) of the sequence, through its block table.  One thread per (token, kv head, 8-dim piece),
+// tokens fastest (see append_kernel); the token's sequence by binary search of the prefix sums.  Rows past the
+// table's capacity and table entries outside the pool are skipped.
+__global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, const int32_t *cu, const int32_t *pos,
+                                                            int num_seqs) {
+    const int pieces = p.D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)p.T * p.Hkv * pieces;
+    if (gid >= total)
+        return;
+    const int i = (int)(gid % p.T);
+    const int64_t hc = gid / p.T;
+    const int c = (int)(hc % pieces);
+    const int h = (int)(hc / pieces);
+    int lo = 0, hi = num_seqs - 1;  // the last s with cu[s] <= i
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= i)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int64_t row = (int64_t)pos[lo] + (i - cu[lo]);
+    if (row < 0 || row >= (int64_t)p.M * p.BS || i >= cu[lo + 1])
+        return;
+    const int32_t blk = p.block_tables[(int64_t)lo * p.M + row / p.BS];
+    if (blk < 0 || blk >= p.N)
+        return;
+    const int off = (int)(row % p.BS);
+    const int64_t src = ((int64_t)i * p.Hkv + h) * p.D + 8 * c;
+    const uint4 kv = *reinterpret_cast<const uint4 *>(p.k + src);
+    const uint4 vv = *reinterpret_cast<const uint4 *>(p.v + src);
+    const int64_t panel = ((int64_t)blk * p.Hkv + h) * (int64_t)p.BS * p.D + (int64_t)(off / 16) * 16 * p.D;
+    const int prow = off % 16;
+    *reinterpret_cast<uint4 *>(p.k_pool + panel + ((int64_t)c * 16 + prow) * 8) = kv;
+    const uint16_t *vh = reinterpret_cast<const uint16_t *>(&vv);
+    uint16_t *vdst = reinterpret_cast<uint16_t *>(p.v_pool + panel + (int64_t)(8 * c) * 16 + prow);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        vdst[e * 16] = vh[e];
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 
@@ -1040,16 +1162,26 @@ hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int 
     }
 }
 
-size_t varlen_lds_bytes(int head_dim, int waves) {
-    return sizeof(float) * (size_t)merge_floats(head_dim, 16, waves);
+size_t varlen_lds_bytes(int head_dim, int waves, bool fused) {
+    // the merge area, then (fused step) kFusedUnits units of new K and V rows
+    return sizeof(float) * (size_t)merge_floats(head_dim, 16, waves) +
+           (fused ? sizeof(_Float16) * (size_t)kFusedUnits * 32 * head_dim : 0);
 }
 
 template <int D, int BS, int NW>
 static hipError_t launch_varlen_t(const VarlenParams &p, int num_seqs, bool split, hipStream_t stream) {
     dim3 grid((unsigned)((int64_t)num_seqs * p.tiles_per_seq * p.Hkv * (split ? p.num_splits : 1)), 1u, 1u);
     dim3 block(NW * 64);
-    const size_t lds = varlen_lds_bytes(D, NW);
-    if (split && p.QT == 2)
+    const bool fused = p.k_new != nullptr;
+    const size_t lds = varlen_lds_bytes(D, NW, fused);
+    if (fused && p.QT == 2) {  // the fused step runs as one pass; head dim 256 takes it with one tile per group
+        if constexpr (D <= 128)
+            hipLaunchKernelGGL((varlen_kernel<D, BS, NW, false, 2, true>), grid, block, lds, stream, p);
+        else
+            return hipErrorInvalidValue;
+    } else if (fused)
+        hipLaunchKernelGGL((varlen_kernel<D, BS, NW, false, 1, true>), grid, block, lds, stream, p);
+    else if (split && p.QT == 2)
         hipLaunchKernelGGL((varlen_kernel<D, BS, NW, true, 2>), grid, block, lds, stream, p);
     else if (split)
         hipLaunchKernelGGL((varlen_kernel<D, BS, NW, true, 1>), grid, block, lds, stream, p);
@@ -1110,6 +1242,16 @@ hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream) {
     if (p.T <= 0)
         return hipSuccess;
     hipLaunchKernelGGL(append_newest_kernel, dim3((unsigned)((int64_t)p.T * p.Hkv)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
+                                int num_seqs, hipStream_t stream) {
+    if (p.T <= 0 || num_seqs <= 0)
+        return hipSuccess;
+    const int64_t total = (int64_t)p.T * p.Hkv * (p.D / 8);
+    hipLaunchKernelGGL(append_varlen_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p,
+                       cu_seqlens_q, pos_offsets, num_seqs);
     return hipGetLastError();
 }
 

@@ -43,6 +43,7 @@ EXPORTED = [
     "pkv_paged_decode_step",
     "pkv_paged_decode_step_qkv",
     "pkv_paged_varlen_attention",
+    "pkv_paged_varlen_step",
     "pkv_paged_decode_attention_window",
     "pkv_split_qkv_norm_rope_into_paged_cache_varlen",
     "pkv_split_qkv_norm_rope_into_paged_cache",
@@ -106,6 +107,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.pkv_paged_decode_attention_window.argtypes = attn[:12] + [i32, i32, vp]
         lib.pkv_paged_varlen_attention.argtypes = [vp, vp, vp, PoolDesc, vp, i32, vp, vp, i32, i32, i32, f32, vp, i32,
                                                    i32, i32, vp]
+        lib.pkv_paged_varlen_step.argtypes = [vp, vp, vp, vp, vp, PoolDesc, vp, i32, vp, vp, i32, i32, i32, f32, vp,
+                                              i32, i32, i32, vp]
         qkv = [vp, vp, vp, vp, vp, i32, vp, vp, vp, PoolDesc, vp, i32]
         lib.pkv_split_qkv_norm_rope_into_paged_cache_varlen.argtypes = qkv + [vp, vp, i32, i32, i32, f32, i32, vp]
         lib.pkv_split_qkv_norm_rope_into_paged_cache.argtypes = qkv + [i32, i32, i32, i32, f32, i32, vp]
@@ -408,6 +411,44 @@ def paged_varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_of
     return out
 
 
+def _varlen_step_args(q, k_new, v_new, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets):
+    import torch
+    pool = _pool(k_pool, v_pool)
+    _dev(q, torch.float16, "q", 3)
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1)
+    _dev(pos_offsets, torch.int32, "pos_offsets", 1)
+    T = int(q.shape[0])
+    B = int(pos_offsets.shape[0])
+    if q.shape[2] != pool.head_dim:
+        raise ValueError("q head_dim %d != pool head_dim %d" % (q.shape[2], pool.head_dim))
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, torch.float16, n, 3)
+        if tuple(t.shape) != (T, pool.num_kv_heads, pool.head_dim):
+            raise ValueError("%s must be [T][Hkv][D] = %s" % (n, (T, pool.num_kv_heads, pool.head_dim)))
+    if block_tables.shape[0] != B or cu_seqlens_q.shape[0] != B + 1:
+        raise ValueError("block_tables must have num_seqs = %d rows and cu_seqlens_q num_seqs + 1 entries" % B)
+    return pool, B, T
+
+
+def paged_varlen_step(q, k_new, v_new, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, scale: float,
+                      max_q_len: int, out=None, num_splits: int = 0, max_context_hint: int = 0, stream=None):
+    """The varlen step (pkv_paged_varlen_step): token t's new K/V rows (k_new, v_new: [T][Hkv][D]) go to row
+    pos_offsets[s] + i of its sequence, then every new row attends as in paged_varlen_attention.  max_q_len bounds
+    every sequence's new rows (required)."""
+    import torch
+    pool, B, T = _varlen_step_args(q, k_new, v_new, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, torch.float16, "out", 3)
+    _check(load().pkv_paged_varlen_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), pool,
+                                        _ptr(block_tables), int(block_tables.shape[1]), _ptr(cu_seqlens_q),
+                                        _ptr(pos_offsets), B, T, int(q.shape[1]), float(scale), _ptr(out),
+                                        int(num_splits), int(max_q_len), int(max_context_hint), _stream(stream)))
+    return out
+
+
 def _qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, num_q_heads: int, qk_mode: int):
     import torch
     pool = _pool(k_pool, v_pool)
@@ -611,6 +652,24 @@ def prepare_paged_varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q
             ctypes.c_int32(max_context_hint), ctypes.c_void_p(_stream(stream)))
     return PreparedCall(lib.pkv_paged_varlen_attention, args,
                         (q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, out))
+
+
+def prepare_paged_varlen_step(q, k_new, v_new, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets,
+                              scale: float, max_q_len: int, out, num_splits: int = 0, max_context_hint: int = 0,
+                              stream=None) -> PreparedCall:
+    """pkv_paged_varlen_step with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    pool, B, T = _varlen_step_args(q, k_new, v_new, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets)
+    _dev(out, torch.float16, "out", 3)
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(q)), ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
+            ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool, ctypes.c_void_p(_ptr(block_tables)),
+            ctypes.c_int32(int(block_tables.shape[1])), ctypes.c_void_p(_ptr(cu_seqlens_q)),
+            ctypes.c_void_p(_ptr(pos_offsets)), ctypes.c_int32(B), ctypes.c_int32(T), ctypes.c_int32(int(q.shape[1])),
+            ctypes.c_float(scale), ctypes.c_void_p(_ptr(out)), ctypes.c_int32(num_splits), ctypes.c_int32(max_q_len),
+            ctypes.c_int32(max_context_hint), ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_paged_varlen_step, args,
+                        (q, k_new, v_new, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets, out))
 
 
 def prepare_paged_decode_attention_window(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,

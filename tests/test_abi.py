@@ -143,6 +143,23 @@ def test_entry_points_validate_before_touching_a_device():
                                               None) == pkv.PKV_OK
 
 
+def test_varlen_step_validates_before_touching_a_device():
+    lib = pkv.load()
+    pool = pkv.PoolDesc(8, 128, 16, 100)
+    step = lib.pkv_paged_varlen_step
+    # (q, k_new, v_new, k_pool, v_pool, pool, tables, M, cu, pos, B, T, Hq, scale, out, S, max_q_len, hint, stream)
+    rc = step(16, None, 16, 16, 16, pool, 4, 128, 4, 4, 4, 8, 32, 0.1, 16, 0, 2, 0, None)
+    assert rc == pkv.PKV_EINVAL and "k_new" in pkv.last_error()
+    rc = step(16, 16, 8, 16, 16, pool, 4, 128, 4, 4, 4, 8, 32, 0.1, 16, 0, 2, 0, None)
+    assert rc == pkv.PKV_EINVAL and "aligned" in pkv.last_error()
+    rc = step(16, 16, 16, 16, 16, pool, 4, 128, 4, 4, 4, 8, 32, 0.1, 16, 0, 0, 0, None)  # max_q_len is required
+    assert rc == pkv.PKV_EINVAL and "max_q_len" in pkv.last_error()
+    assert step(None, None, None, None, None, pool, None, 128, None, None, 0, 0, 32, 0.1, None, 0, 0, 0,
+                None) == pkv.PKV_OK  # empty batch
+    assert step(16, 16, 16, 16, 16, pkv.PoolDesc(8, 96, 16, 100), 4, 128, 4, 4, 4, 8, 32, 0.1, 16, 0, 2, 0,
+                None) == pkv.PKV_EUNSUPPORTED
+
+
 def test_qkv_entry_points_validate_before_touching_a_device():
     lib = pkv.load()
     pool = pkv.PoolDesc(8, 128, 16, 100)
