@@ -145,6 +145,43 @@ struct RowLimits {
     int lo;  // first row any column may attend (a sliding window's start; 0 otherwise)
 };
 
+// The fused varlen step's pool update for one loaded 16-row unit: rows prow .. prow_end-1 are new -- their K and V
+// taken from the workgroup's LDS copy of the unit (sk: [16][D] row-major; sv: [D][16], the V panel's own order, so
+// a lane's four rows of one dim are one 8-byte read) -- and the patched fragment is written back whole to the
+// unit's panels (wb_k, wb_v), its other rows with the values just loaded.  A dead unit is patched (its rows are
+// masked anyway) but not written.
+template <int D, int BS>
+__device__ __forceinline__ void patch_unit_rows(Frag<D, BS> &f, int prow, int prow_end, const _Float16 *sk,
+                                                const _Float16 *sv, _Float16 *wb_k, _Float16 *wb_v, bool dead, int r,
+                                                int g4, uint32_t k_lane, uint32_t v_lane) {
+    constexpr int KC = Frag<D, BS>::KC;
+    constexpr int VC = Frag<D, BS>::VC;
+    if (r >= prow && r < prow_end) {  // K pieces 4c + g4 of row r
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            f.k[c] = *reinterpret_cast<const f16x8 *>(sk + r * D + 32 * c + 8 * g4);
+    }
+    bool take[4];  // V dims 16c + r of rows 4*g4 + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        take[e] = 4 * g4 + e >= prow && 4 * g4 + e < prow_end;
+#pragma unroll
+    for (int c = 0; c < VC; ++c) {  // lanes without new rows read unset LDS and keep their own values
+        const f16x4 nv = *reinterpret_cast<const f16x4 *>(sv + (16 * c + r) * 16 + 4 * g4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            f.v[c][e] = take[e] ? nv[e] : f.v[c][e];
+    }
+    if (!dead) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            *reinterpret_cast<f16x8 *>(reinterpret_cast<char *>(wb_k) + k_lane + 1024 * c) = f.k[c];
+#pragma unroll
+        for (int c = 0; c < VC; ++c)
+            *reinterpret_cast<f16x4 *>(reinterpret_cast<char *>(wb_v) + v_lane + 512 * c) = f.v[c];
+    }
+}
+
 // One 16-row unit: scores, online-softmax update, P.V accumulation.  A dead unit (its block id names no pool
 // block) is computed with every row masked, so that the loads of every unit are consumed on every path.
 //
@@ -153,41 +190,15 @@ struct RowLimits {
 // fragment.  The patched fragment -- the unit's 16 rows as loaded, with row prow replaced -- is then written back
 // to the unit's panels (wb_k, wb_v): the pool update is whole cache lines, and no row but prow changes value.
 // A unit whose block id names no pool block (dead) is neither written nor used.
-// MULTI (fused varlen step): rows prow .. prow_end-1 of the unit are new, pk / pv point to the LDS copy of row prow
-// (rows D halves apart); every one of them is patched before the write-back.
-template <int D, int BS, bool MULTI = false>
+template <int D, int BS>
 __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D / 32], f32x4 (&o)[D / 16],
                                              float &m_run, float &l_run, int u, const RowLimits &lim, bool dead,
                                              int r, int g4,
                                              float scale_log2, int prow, const _Float16 *pk, const _Float16 *pv,
-                                             _Float16 *wb_k, _Float16 *wb_v, uint32_t k_lane, uint32_t v_lane,
-                                             int prow_end = 0) {
+                                             _Float16 *wb_k, _Float16 *wb_v, uint32_t k_lane, uint32_t v_lane) {
     constexpr int KC = Frag<D, BS>::KC;
     constexpr int VC = Frag<D, BS>::VC;
-    if (MULTI && prow >= 0) {  // wave-uniform
-        if (r >= prow && r < prow_end) {  // K pieces 4c + g4 of row r
-#pragma unroll
-            for (int c = 0; c < KC; ++c)
-                f.k[c] = *reinterpret_cast<const f16x8 *>(pk + (r - prow) * D + 32 * c + 8 * g4);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {  // V dims 16c + r of rows 4*g4 + e
-            const int row = 4 * g4 + e;
-            if (row >= prow && row < prow_end) {
-#pragma unroll
-                for (int c = 0; c < VC; ++c)
-                    f.v[c][e] = pv[(row - prow) * D + 16 * c + r];
-            }
-        }
-        if (!dead) {  // the pool update: the patched panel written back whole, before any row is masked
-#pragma unroll
-            for (int c = 0; c < KC; ++c)
-                *reinterpret_cast<f16x8 *>(reinterpret_cast<char *>(wb_k) + k_lane + 1024 * c) = f.k[c];
-#pragma unroll
-            for (int c = 0; c < VC; ++c)
-                *reinterpret_cast<f16x4 *>(reinterpret_cast<char *>(wb_v) + v_lane + 512 * c) = f.v[c];
-        }
-    } else if (!MULTI && prow >= 0) {  // wave-uniform
+    if (prow >= 0) {  // wave-uniform
         if (r == prow) {  // K pieces 4c + g4
 #pragma unroll
             for (int c = 0; c < KC; ++c)
@@ -703,7 +714,9 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
 
     // Fused step: units nu0 .. nu0 + n_new_units - 1 hold the new rows pos .. pos + qlen - 1.  The wave that computes
     // unit u in every tile group (u % NW: with one pass the range starts at unit 0) copies that unit's new rows to
-    // its LDS slot (K then V, 16 rows of D halves each per unit).
+    // its LDS slot (K [16][D] row-major, then V [D][16]; rows that are not new stay unset and are never read) before
+    // its first K/V loads.  (Copying after them costs more: the copy's wait then covers the whole first unit, and
+    // direct global-to-LDS loads make the compiler wait for every load in flight before each unit.)
     const int nu0 = pos >> 4;
     const int n_new_units = FUSED && qlen > 0 ? min(kFusedUnits, ((pos + qlen - 1) >> 4) - nu0 + 1) : 0;
     _Float16 *sm_new = reinterpret_cast<_Float16 *>(smem + merge_floats(D, 16, NW));
@@ -719,9 +732,13 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
             for (int c = lane; c < (row1 - row0) * (D / 8); c += 64) {
                 const int rr = c / (D / 8), piece = c - rr * (D / 8);
                 const int64_t src = ((int64_t)(q0 + row0 - pos + rr) * p.Hkv + hk) * D + 8 * piece;
-                const int dst = (row0 - 16 * u + rr) * D + 8 * piece;
-                *reinterpret_cast<f16x8 *>(slot_k + dst) = *reinterpret_cast<const f16x8 *>(p.k_new + src);
-                *reinterpret_cast<f16x8 *>(slot_v + dst) = *reinterpret_cast<const f16x8 *>(p.v_new + src);
+                const int row = row0 - 16 * u + rr;
+                *reinterpret_cast<f16x8 *>(slot_k + row * D + 8 * piece) =
+                    *reinterpret_cast<const f16x8 *>(p.k_new + src);
+                const f16x8 vv = *reinterpret_cast<const f16x8 *>(p.v_new + src);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    slot_v[(8 * piece + e) * 16 + row] = vv[e];
             }
         }
     }
@@ -819,33 +836,25 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
                     load_unit<D, BS>(f[jn], k_ptr(blk, uu[jn]), v_ptr(blk, uu[jn]), k_lane, v_lane,
                                      k + NS - 1 < n_units && !dead[jn]);
                     raw_q[j] = raw_block(u_first + min(k + 2 * NS - 1, n_units - 1) * NW);
-                    // Every tile of the group uses this unit's fragments.  Later tiles first: a tile zeroes the V
-                    // rows past its own last row, which every earlier tile leaves unused too.
-                    // fused step: the unit's new rows (if any) patched in and the unit written back (tile QT-1 only:
-                    // one patch and one write per unit load; the later tiles' calls see the patched fragment)
-                    int prow = -1, prow_end = 0;
-                    const _Float16 *pk = nullptr, *pv = nullptr;
-                    _Float16 *wk = nullptr, *wv = nullptr;
-                    if (FUSED) {
+                    if (FUSED) {  // the unit's new rows (if any) patched in and the unit written back, once per load
                         const int kslot = uu[j] - nu0;
-                        if (kslot >= 0 && kslot < n_new_units) {
-                            prow = max(pos, 16 * uu[j]) - 16 * uu[j];
-                            prow_end = min(pos + qlen, 16 * uu[j] + 16) - 16 * uu[j];
-                            pk = sm_new + kslot * 32 * D + prow * D;
-                            pv = pk + 16 * D;
-                            wk = p.k_dst + (k_ptr(blk_of[j], uu[j]) - p.k_pool);
-                            wv = p.v_dst + (v_ptr(blk_of[j], uu[j]) - p.v_pool);
+                        if (kslot >= 0 && kslot < n_new_units) {  // wave-uniform
+                            const int prow = max(pos, 16 * uu[j]) - 16 * uu[j];
+                            const int prow_end = min(pos + qlen, 16 * uu[j] + 16) - 16 * uu[j];
+                            const _Float16 *sk = sm_new + kslot * 32 * D;
+                            patch_unit_rows<D, BS>(f[j], prow, prow_end, sk, sk + 16 * D,
+                                                   p.k_dst + (k_ptr(blk_of[j], uu[j]) - p.k_pool),
+                                                   p.v_dst + (v_ptr(blk_of[j], uu[j]) - p.v_pool), dead[j], r, g4,
+                                                   k_lane, v_lane);
                         }
                     }
-                    bool patched = false;
+                    // Every tile of the group uses this unit's fragments.  Later tiles first: a tile zeroes the V
+                    // rows past its own last row, which every earlier tile leaves unused too.
 #pragma unroll
                     for (int t = QT - 1; t >= 0; --t) {
-                        if (nrows[t] > 0) {  // wave-uniform
-                            compute_unit<D, BS, true>(f[j], qf[t], o[t], m_run[t], l_run[t], uu[j], lim[t], dead[j],
-                                                      r, g4, p.scale_log2, patched ? -1 : prow, pk, pv, wk, wv,
-                                                      k_lane, v_lane, prow_end);
-                            patched = true;
-                        }
+                        if (nrows[t] > 0)  // wave-uniform
+                            compute_unit<D, BS>(f[j], qf[t], o[t], m_run[t], l_run[t], uu[j], lim[t], dead[j], r, g4,
+                                                p.scale_log2, -1, nullptr, nullptr, nullptr, nullptr, k_lane, v_lane);
                     }
                     if (++k >= n_units)
                         goto tile_done;
