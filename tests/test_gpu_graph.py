@@ -142,6 +142,73 @@ def test_decode_step_qkv_graph_replays_follow_device_state(torch_cuda, B):
     assert_fp16_of(g_state["q"].cpu().numpy(), q64, "graph step_qkv B=%d last q_out" % B)
 
 
+def test_varlen_step_graph_replays_follow_device_state(torch_cuda):
+    """pkv_paged_varlen_step (one launch: 4 sequences x 8 kv heads) captured once and replayed while every sequence
+    verifies 3 new rows per step: positions advance by 3, new q and K/V rows arrive."""
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    B, Hq, Hkv, D, BS, QL = 4, 32, 8, 128, 16, 3
+    pos0 = np.array([40, 15, 77, 0], dtype=np.int32)
+    c = W.build_varlen_case("graph", B, Hq, Hkv, D, BS, np.full(B, QL, np.int32), pos0 + QL * (STEPS - 1), 841,
+                            poison_new=False)  # tables hold the grown sequences
+    rng = np.random.default_rng(842)
+    cu = np.arange(0, B * QL + 1, QL, dtype=np.int32)
+
+    def state():
+        return dict(q=torch.zeros((B * QL, Hq, D), dtype=torch.float16, device="cuda"),
+                    kn=torch.zeros((B * QL, Hkv, D), dtype=torch.float16, device="cuda"),
+                    vn=torch.zeros((B * QL, Hkv, D), dtype=torch.float16, device="cuda"),
+                    kp=_dev(torch, c.k_pool), vp=_dev(torch, c.v_pool), bt=_dev(torch, c.block_tables),
+                    cu=_dev(torch, cu), pos=_dev(torch, pos0 - QL),
+                    out=torch.empty((B * QL, Hq, D), dtype=torch.float16, device="cuda"))
+
+    def step(st):
+        pkv.paged_varlen_step(st["q"], st["kn"], st["vn"], st["kp"], st["vp"], st["bt"], st["cu"], st["pos"], c.scale,
+                              QL, out=st["out"], num_splits=1)
+
+    g_state, e_state = state(), state()
+    stream = torch.cuda.Stream()
+    warm = state()
+    warm["pos"].add_(QL)
+    with torch.cuda.stream(stream):
+        step(warm)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step(g_state)
+    torch.cuda.synchronize()
+    for k in ("kp", "vp", "out"):
+        g_state[k].copy_(e_state[k])
+    kp_o, vp_o = c.k_pool.copy(), c.v_pool.copy()
+    pos = pos0 - QL
+    for i in range(STEPS):
+        q = rng.standard_normal((B * QL, Hq, D)).astype(np.float16)
+        kn = rng.standard_normal((B * QL, Hkv, D)).astype(np.float16)
+        vn = rng.standard_normal((B * QL, Hkv, D)).astype(np.float16)
+        for st in (g_state, e_state):
+            st["pos"].add_(QL)
+            st["q"].copy_(torch.from_numpy(q))
+            st["kn"].copy_(torch.from_numpy(kn))
+            st["vn"].copy_(torch.from_numpy(vn))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e_state)
+        torch.cuda.synchronize()
+        for k in ("out", "kp", "vp"):
+            assert torch.equal(g_state[k].view(torch.int16), e_state[k].view(torch.int16)), "replay %d: %s" % (i, k)
+        say("graph varlen step replay %d: bit-identical to the eager step" % i)
+        pos = pos + QL
+        slots = np.array([int(c.block_tables[s, (int(pos[s]) + j) // BS]) * BS + (int(pos[s]) + j) % BS
+                          for s in range(B) for j in range(QL)], dtype=np.int32)
+        oracle.paged_kv_append(kn, vn, slots, kp_o, vp_o)
+    assert np.array_equal(g_state["pos"].cpu().numpy(), pos)
+    ref = oracle.varlen_attention(q, kp_o, vp_o, c.block_tables, cu, pos, c.scale)
+    assert_close(g_state["out"].cpu().numpy(), ref, "graph varlen step last replay")
+    assert np.array_equal(g_state["kp"].cpu().numpy().view(np.uint16), kp_o.view(np.uint16))
+    assert np.array_equal(g_state["vp"].cpu().numpy().view(np.uint16), vp_o.view(np.uint16))
+
+
 def test_capture_needing_a_new_workspace_fails_cleanly(torch_cuda):
     from paged_kv_decode_04_amd import pkv
     torch = torch_cuda
