@@ -5,7 +5,7 @@ paged decode attention (single pass, or split-K phase 1 + combine, as the worklo
 the step is the library's fused decode step (pkv_paged_decode_step: append and attention in one launch); --unfused
 times the two separate entry points (pkv_paged_kv_append, then pkv_paged_decode_attention).  The varlen workloads
 (v1, v2: several new rows per sequence) time the varlen step (pkv_paged_varlen_step, one launch; --unfused:
-pkv_paged_kv_append, then pkv_paged_varlen_attention).  The r workloads start
+pkv_paged_kv_append, then pkv_paged_varlen_attention), w1 the windowed decode step (pkv_paged_decode_step_window).  The r workloads start
 one step earlier, from the QKV projection rows: r1 is the decode step from those rows in one launch
 (pkv_paged_decode_step_qkv: q/k RMS norm, RoPE, the new K/V rows written, attention; --unfused: the QKV-to-cache
 kernel, then attention); r2 times the QKV-to-cache kernel alone on a chunked-prefill batch.  Inputs
@@ -69,9 +69,9 @@ QKV_ONLY = {"r2"}  # QKV-step workloads whose step is that kernel alone (a 512-r
 
 def step_is_fused(config: str, unfused: bool) -> bool:
     """Whether bench.py times the workload's step through the library's step entry point (pkv_paged_decode_step,
-    pkv_paged_varlen_step, or pkv_paged_decode_step_qkv for a decode step from QKV rows), one launch where the grid
-    allows; sliding-window and QKV-only workloads launch their kernels one after the other."""
-    return not unfused and config not in WINDOWS and config not in QKV_ONLY
+    pkv_paged_decode_step_window, pkv_paged_varlen_step, or pkv_paged_decode_step_qkv for a decode step from QKV
+    rows), one launch where the grid allows; QKV-only workloads time that kernel alone."""
+    return not unfused and config not in QKV_ONLY
 
 
 def log(*a):
@@ -325,7 +325,8 @@ def main(argv=None) -> int:
     if varlen or qkv_only:
         plan = {"num_splits": splits, "note": "varlen: 0 = the library chooses from the grid size"}
     else:
-        plan = pkv.plan_decode(c0.B, c0.Hq, c0.Hkv, c0.D, c0.BS, c0.M, num_splits=splits)
+        plan = pkv.plan_decode(c0.B, c0.Hq, c0.Hkv, c0.D, c0.BS, c0.M, num_splits=splits,
+                               max_context_hint=window)  # a window bounds the rows a sequence attends
     log("plan: %s, %s" % (plan, pkv.version()))
 
     fused = step_is_fused(args.config, args.unfused)  # varlen / window steps: the append, then attention
@@ -357,6 +358,10 @@ def main(argv=None) -> int:
             d["call"] = pkv.prepare_paged_varlen_step(d["q"], d["k_new"], d["v_new"], d["k_pool"], d["v_pool"],
                                                       d["bt"], d["cu"], d["pos"], d["case"].scale,
                                                       int(d["case"].q_lens.max()), d["out"], num_splits=splits)
+        elif fused and window:
+            d["call"] = pkv.prepare_decode_step_window(d["q"], d["k_new_all"], d["v_new_all"], d["k_pool"],
+                                                       d["v_pool"], d["bt"], d["cl"], d["case"].scale, window,
+                                                       d["out"], num_splits=splits)
         elif fused:
             d["call"] = pkv.prepare_decode_step(d["q"], d["k_new_all"], d["v_new_all"], d["k_pool"], d["v_pool"],
                                                 d["bt"], d["cl"], d["case"].scale, d["out"], num_splits=splits)
@@ -512,6 +517,7 @@ def main(argv=None) -> int:
                      "fused (pkv_paged_decode_step_qkv)" if qkv and fused else
                      "pkv_split_qkv_norm_rope_into_paged_cache_varlen + pkv_paged_decode_attention" if qkv else
                      "fused (pkv_paged_varlen_step)" if fused and varlen else
+                     "fused (pkv_paged_decode_step_window, window %d)" % window if fused and window else
                      "fused (pkv_paged_decode_step)" if fused else
                      "pkv_paged_kv_append + pkv_paged_varlen_attention" if varlen else
                      "pkv_paged_kv_append + pkv_paged_decode_attention_window (window %d)" % window if window else

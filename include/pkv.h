@@ -268,6 +268,24 @@ PKV_API int pkv_paged_decode_attention_window(const uint16_t *q, const uint16_t 
                                       int32_t max_context_hint, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_paged_decode_step_window -- the decode step with a sliding window:
+ *   the append of pkv_paged_decode_step (k_new / v_new to row L_s - 1 of each
+ *   sequence), then what pkv_paged_decode_attention_window computes over the
+ *   updated pools.  Launch routing, the single-owner rule for the newest
+ *   block and the results' independence of the route as
+ *   pkv_paged_decode_step; window rules and errors as
+ *   pkv_paged_decode_attention_window (window = 0 is pkv_paged_decode_step).
+ *   [cortiq-engine 0.8.80, src/gpu_cuda.rs: each decode step stores the new
+ *   row, then attends rows stored - window .. stored]
+ * ------------------------------------------------------------------------- */
+PKV_API int pkv_paged_decode_step_window(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                                 uint16_t *k_pool, uint16_t *v_pool, pkv_pool_desc pool,
+                                 const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                                 uint16_t *out, int32_t num_splits, int32_t window, int32_t max_context_hint,
+                                 void *stream);
+
+/* ---------------------------------------------------------------------------
  * pkv_paged_varlen_attention -- attention for several new query rows per
  *   sequence (speculative verification, chunked prefill): sequence s owns the
  *   rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of q and out; its i-th new row

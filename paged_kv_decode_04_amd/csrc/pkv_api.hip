@@ -860,6 +860,20 @@ int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16
                        static_cast<hipStream_t>(stream), k_new, v_new);
 }
 
+int pkv_paged_decode_step_window(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                                 uint16_t *v_pool, pkv_pool_desc pool, const int32_t *block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits, int32_t window,
+                                 int32_t max_context_hint, void *stream) {
+    if (num_seqs > 0 && (!k_new || !v_new))
+        return fail(PKV_EINVAL, "null device pointer (k_new=%p v_new=%p)", k_new, v_new);
+    if (num_seqs > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16)))
+        return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+    return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
+                       static_cast<hipStream_t>(stream), k_new, v_new, window);
+}
+
 int pkv_plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_hint, int32_t num_splits,
                     int32_t cu_count, pkv_decode_plan *plan) {

@@ -45,6 +45,7 @@ EXPORTED = [
     "pkv_paged_varlen_attention",
     "pkv_paged_varlen_step",
     "pkv_paged_decode_attention_window",
+    "pkv_paged_decode_step_window",
     "pkv_split_qkv_norm_rope_into_paged_cache_varlen",
     "pkv_split_qkv_norm_rope_into_paged_cache",
     "pkv_plan_decode",
@@ -105,6 +106,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.pkv_paged_decode_step_qkv.argtypes = [vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, PoolDesc, vp, i32, vp,
                                                   i32, i32, f32, vp, i32, i32, vp]
         lib.pkv_paged_decode_attention_window.argtypes = attn[:12] + [i32, i32, vp]
+        lib.pkv_paged_decode_step_window.argtypes = [vp, vp, vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, vp,
+                                                     i32, i32, i32, vp]
         lib.pkv_paged_varlen_attention.argtypes = [vp, vp, vp, PoolDesc, vp, i32, vp, vp, i32, i32, i32, f32, vp, i32,
                                                    i32, i32, vp]
         lib.pkv_paged_varlen_step.argtypes = [vp, vp, vp, vp, vp, PoolDesc, vp, i32, vp, vp, i32, i32, i32, f32, vp,
@@ -278,6 +281,47 @@ def paged_decode_step(q, k_new, v_new, k_pool, v_pool, block_tables, context_len
                                         _ptr(block_tables), M, _ptr(context_lens), B, Hq, float(scale), _ptr(out),
                                         int(num_splits), int(max_context_hint), _stream(stream)))
     return out
+
+
+def paged_decode_step_window(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale: float, window: int,
+                             out=None, num_splits: int = 0, max_context_hint: int = 0, stream=None):
+    """Decode step with a sliding window (pkv_paged_decode_step_window): write each sequence's new K/V row at
+    position L-1, then attend its last `window` rows."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    _dev(k_new, torch.float16, "k_new", 3)
+    _dev(v_new, torch.float16, "v_new", 3)
+    if tuple(k_new.shape) != (B, pool.num_kv_heads, pool.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must be [B][Hkv][D] = %s" % ((B, pool.num_kv_heads, pool.head_dim),))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.float16, "out", 3)
+    _check(load().pkv_paged_decode_step_window(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), pool,
+                                               _ptr(block_tables), M, _ptr(context_lens), B, Hq, float(scale),
+                                               _ptr(out), int(num_splits), int(window), int(max_context_hint),
+                                               _stream(stream)))
+    return out
+
+
+def prepare_decode_step_window(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale: float,
+                               window: int, out, num_splits: int = 0, max_context_hint: int = 0,
+                               stream=None) -> "PreparedCall":
+    """pkv_paged_decode_step_window with its arguments marshalled once (see PreparedCall)."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, torch.float16, n, 3)
+        if tuple(t.shape) != (B, pool.num_kv_heads, pool.head_dim):
+            raise ValueError("%s must be [B][Hkv][D]" % n)
+    _dev(out, torch.float16, "out", 3)
+    lib = load()
+    args = (ctypes.c_void_p(_ptr(q)), ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
+            ctypes.c_void_p(_ptr(k_pool)), ctypes.c_void_p(_ptr(v_pool)), pool, ctypes.c_void_p(_ptr(block_tables)),
+            ctypes.c_int32(M), ctypes.c_void_p(_ptr(context_lens)), ctypes.c_int32(B), ctypes.c_int32(Hq),
+            ctypes.c_float(scale), ctypes.c_void_p(_ptr(out)), ctypes.c_int32(num_splits), ctypes.c_int32(window),
+            ctypes.c_int32(max_context_hint), ctypes.c_void_p(_stream(stream)))
+    return PreparedCall(lib.pkv_paged_decode_step_window, args, (q, k_new, v_new, k_pool, v_pool, block_tables,
+                                                                 context_lens, out))
 
 
 def _step_qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool, block_tables, context_lens, num_q_heads,

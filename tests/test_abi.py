@@ -160,6 +160,18 @@ def test_varlen_step_validates_before_touching_a_device():
                 None) == pkv.PKV_EUNSUPPORTED
 
 
+def test_window_step_validates_before_touching_a_device():
+    lib = pkv.load()
+    pool = pkv.PoolDesc(8, 128, 16, 100)
+    step = lib.pkv_paged_decode_step_window
+    # (q, k_new, v_new, k_pool, v_pool, pool, tables, M, lens, B, Hq, scale, out, S, window, hint, stream)
+    rc = step(16, None, 16, 16, 16, pool, 4, 128, 4, 4, 32, 0.1, 16, 0, 64, 0, None)
+    assert rc == pkv.PKV_EINVAL and "k_new" in pkv.last_error()
+    rc = step(16, 16, 16, 16, 16, pool, 4, 128, 4, 4, 32, 0.1, 16, 0, -1, 0, None)
+    assert rc == pkv.PKV_EINVAL and "window" in pkv.last_error()
+    assert step(None, None, None, None, None, pool, None, 128, None, 0, 32, 0.1, None, 0, 64, 0, None) == pkv.PKV_OK
+
+
 def test_qkv_entry_points_validate_before_touching_a_device():
     lib = pkv.load()
     pool = pkv.PoolDesc(8, 128, 16, 100)

@@ -72,3 +72,41 @@ def test_window_on_the_llama3_8b_batch(torch_cuda):
         ref = oracle.decode_attention(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
                                       window=window)
         assert_close(_run(torch_cuda, c, window, S), ref, "c2 window %d S=%d" % (window, S))
+
+
+# (B, Hq, Hkv, D, BS, context lengths, window) for the windowed decode step; the last has 40 x 8 = 320 workgroups
+# (the append launch, then attention)
+STEP_WINDOW_GEOMS = WINDOW_GEOMS[:4] + [
+    (3, 8, 2, 64, 16, (37, 16, 5), 1),
+    (40, 16, 8, 128, 16, tuple(1 + (37 * i) % 600 for i in range(40)), 100),
+]
+
+
+@pytest.mark.parametrize("geom", STEP_WINDOW_GEOMS, ids=lambda g: "B%d_Hq%d_Hkv%d_D%d_BS%d_W%d" % (g[:5] + (g[6],)))
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_window_step_matches_append_then_window_attention(torch_cuda, geom, num_splits):
+    """pkv_paged_decode_step_window: pools bit-exact after the oracle's append, output against the oracle's windowed
+    attention, and bit-identical to the append followed by pkv_paged_decode_attention_window."""
+    from paged_kv_decode_04_amd import pkv
+    from test_gpu_parity import full_new_rows
+    torch = torch_cuda
+    B, Hq, Hkv, D, BS, lens, window = geom
+    c = W.small_case(741 + D + BS + window, B, Hq, Hkv, D, BS, lens, poison=True, extra_blocks=4)
+    say("window step %s S=%d" % (geom, num_splits))
+    kn, vn = full_new_rows(c)
+    dk, dv = _dev(torch, c.k_pool), _dev(torch, c.v_pool)
+    out = pkv.paged_decode_step_window(_dev(torch, c.q), _dev(torch, kn), _dev(torch, vn), dk, dv,
+                                       _dev(torch, c.block_tables), _dev(torch, c.context_lens), c.scale, window,
+                                       num_splits=num_splits)
+    torch.cuda.synchronize()
+    kp, vp = c.k_pool.copy(), c.v_pool.copy()
+    oracle.paged_kv_append(c.k_new, c.v_new, c.slot_mapping, kp, vp)
+    assert np.array_equal(dk.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+    assert np.array_equal(dv.cpu().numpy().view(np.uint16), vp.view(np.uint16))
+    ref = oracle.decode_attention(c.q, kp, vp, c.block_tables, c.context_lens, c.scale, window=window)
+    assert_close(out.cpu().numpy(), ref, "window step %s S=%d" % (geom, num_splits))
+    att = pkv.paged_decode_attention_window(_dev(torch, c.q), _dev(torch, kp), _dev(torch, vp),
+                                            _dev(torch, c.block_tables), _dev(torch, c.context_lens), c.scale, window,
+                                            num_splits=num_splits)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), att.cpu().numpy().view(np.uint16))
