@@ -74,6 +74,21 @@ def step_is_fused(config: str, unfused: bool) -> bool:
     return not unfused and config not in QKV_ONLY
 
 
+def step_launch_count(c, plan, splits: int, varlen: bool, cu: int) -> int:
+    """Launches of the library's step entry point for this workload (the routing rule of pkv_paged_decode_step,
+    pkv_paged_decode_step_window, pkv_paged_decode_step_qkv and pkv_paged_varlen_step): 1 when it takes its
+    single-launch form, 2 or more otherwise."""
+    if varlen:
+        G = c.Hq // c.Hkv
+        R = 16 // G
+        qmax = int(c.q_lens.max())
+        QT = 2 if qmax > R else 1
+        grid = c.B * ((qmax + QT * R - 1) // (QT * R)) * c.Hkv
+        one_pass = splits == 1 or (splits == 0 and 2 * grid >= cu)
+        return 1 if one_pass and qmax <= 32 and grid <= cu and (QT == 1 or c.D <= 128) else 2
+    return 1 if plan["num_splits"] == 1 and c.B * c.Hkv <= cu else 2
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -380,6 +395,19 @@ def main(argv=None) -> int:
             d["call"] = pkv.prepare_paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
                                                            d["case"].scale, d["out"], num_splits=splits)
 
+        # attention alone (the dominant launch when a step takes more than one)
+        if varlen:
+            d["attn"] = pkv.prepare_paged_varlen_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cu"],
+                                                           d["pos"], d["case"].scale, d["out"], num_splits=splits,
+                                                           max_q_len=int(d["case"].q_lens.max()))
+        elif window:
+            d["attn"] = pkv.prepare_paged_decode_attention_window(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
+                                                                  d["case"].scale, d["out"], window,
+                                                                  num_splits=splits)
+        elif not qkv_only:
+            d["attn"] = pkv.prepare_paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["bt"], d["cl"],
+                                                           d["case"].scale, d["out"], num_splits=splits)
+
     def step(d):
         if not fused and not qkv_only:
             d["append"]()
@@ -418,7 +446,7 @@ def main(argv=None) -> int:
     # No event inside a timed region: an event pair costs ~7 us of stream time here, more than a kernel's launch gap.
     # The step region gives value; when a step is one launch (the fused single-pass step) that launch's average
     # duration is the same region / K, otherwise a second region of K back-to-back attention calls gives it.
-    one_launch = (fused and plan["num_splits"] == 1) or qkv_only
+    one_launch = qkv_only or (fused and step_launch_count(c0, plan, splits, varlen, pkv.device_cu_count()) == 1)
     if args.graph:
         # 32 consecutive steps over the rotation sets captured once (the capture stream's workspace is sized by an
         # eager step on it first) and replayed; every replay rewrites the same new rows, so the state is stable.
@@ -436,11 +464,11 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         K = (K + G - 1) // G * G
         ms_per_step = timed(lambda i: graph.replay() if i % G == 0 else None)
-        attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["call"]())])
+        attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["attn"]())])
         log("graph of %d steps, %d replays" % (G, K // G))
     else:
         ms_per_step = timed(lambda i: step(sets[i % R]))
-        attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["call"]())])
+        attn_ms = np.array([ms_per_step if one_launch else timed(lambda i: sets[i % R]["attn"]())])
 
     # Per-step spread: REPS regions of C back-to-back steps each (an event pair per region), median and p90 of
     # the per-step times.
@@ -481,13 +509,13 @@ def main(argv=None) -> int:
     # bytes per step, averaged over the rotation sets
     step_bytes = np.mean([d["bytes"]["attention"] + d["bytes"]["append"] for d in sets])
     attn_bytes = np.mean([d["bytes"]["attention"] for d in sets])
-    kernel_bytes = step_bytes if fused or qkv_only else attn_bytes  # algorithmic bytes of one dominant launch
+    kernel_bytes = step_bytes if one_launch else attn_bytes  # algorithmic bytes of one dominant launch
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     attn_avg_ms = float(attn_ms.mean())
     achieved = kernel_bytes / (attn_avg_ms * 1e-3) / 1e9
     calls_per_s = 1e3 / attn_avg_ms
     log("step %.4f ms (%.1f GB/s); %s avg %.4f ms -> %.1f GB/s, %.0f calls/s"
-        % (ms_per_step, value, "fused step kernel" if fused else "attention call", attn_avg_ms, achieved, calls_per_s))
+        % (ms_per_step, value, "step launch" if one_launch else "attention call", attn_avg_ms, achieved, calls_per_s))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -127,18 +127,30 @@ int library_workspace(size_t need, hipStream_t stream, void **ptr) {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Bytes of the library workspace of this (device, stream) now, without growing it.
+size_t library_workspace_bytes(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    std::lock_guard<std::mutex> g(g_ws_mutex);
+    auto it = g_ws.find(std::make_pair(dev, stream));
+    return it == g_ws.end() ? 0 : it->second.bytes;
+}
+
 struct WsLayout {
-    size_t o_off, m_off, l_off, total;
+    size_t o_off, m_off, l_off, order_off, total;
 };
 
-WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t S) {
+// Split-K partials (S > 1), then, with order_seqs > 0, the dispatch order of that many sequences.
+WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t S, int64_t order_seqs = 0) {
     WsLayout L;
-    const size_t o = round256((size_t)(B * Hq * S * D) * sizeof(float));
-    const size_t ml = round256((size_t)(B * Hq * S) * sizeof(float));
+    const size_t o = S > 1 ? round256((size_t)(B * Hq * S * D) * sizeof(float)) : 0;
+    const size_t ml = S > 1 ? round256((size_t)(B * Hq * S) * sizeof(float)) : 0;
     L.o_off = 0;
     L.m_off = o;
     L.l_off = o + ml;
-    L.total = o + 2 * ml;
+    L.order_off = o + 2 * ml;
+    L.total = L.order_off + round256((size_t)order_seqs * sizeof(int32_t));
     return L;
 }
 
@@ -343,7 +355,7 @@ int check_qkv_pointers(const QkvSource &q) {
 int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
              const pkv_pool_desc &pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
-             void *workspace, size_t workspace_bytes, bool library_ws, hipStream_t stream,
+             void *workspace, size_t workspace_bytes, bool library_ws, hipStream_t stream, int cu_count,
              const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr, int32_t window = 0,
              const QkvSource *qsrc = nullptr) {
     pkv::DecodeParams p = decode_params(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
@@ -369,14 +381,29 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
         p.k_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
         p.v_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
     }
-    if (plan.num_splits == 1) {
+    // A grid of more than one round of the CUs runs longest sequences first (a launch of order_kernel fills the
+    // order array in the library workspace): the longest workgroups otherwise tend to start in a late round and
+    // finish alone.  Only with the library workspace, and not where it would have to grow under graph capture.
+    const int64_t grid = (int64_t)num_seqs * pool.num_kv_heads * plan.num_splits;
+    bool order = library_ws && num_seqs > 1 && num_seqs <= pkv::kOrderMaxSeqs && cu_count > 0 && grid > cu_count;
+    WsLayout L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits, order ? num_seqs : 0);
+    if (order && library_workspace_bytes(stream) < L.total) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(stream, &cap);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipStreamIsCapturing");
+        if (cap != hipStreamCaptureStatusNone) {
+            order = false;  // dispatch order is an optimisation: never worth a failed capture
+            L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits);
+        }
+    }
+    if (plan.num_splits == 1 && !order) {
         hipError_t e = pkv::launch_decode(p, num_seqs, pool.head_dim, pool.block_size, plan.waves_per_group, false,
                                           stream);
         if (e != hipSuccess)
             return hip_fail(e, "decode kernel launch");
         return ok();
     }
-    const WsLayout L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits);
     void *ws = workspace;
     if (library_ws) {
         int rc = library_workspace(L.total, stream, &ws);
@@ -390,6 +417,21 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
             return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
     }
     char *base = static_cast<char *>(ws);
+    if (order) {
+        int32_t *ord = reinterpret_cast<int32_t *>(base + L.order_off);
+        hipError_t e = pkv::launch_order(context_lens, num_seqs, max_blocks_per_seq * pool.block_size, window, ord,
+                                         stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "order kernel launch");
+        p.order = ord;
+    }
+    if (plan.num_splits == 1) {
+        hipError_t e = pkv::launch_decode(p, num_seqs, pool.head_dim, pool.block_size, plan.waves_per_group, false,
+                                          stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "decode kernel launch");
+        return ok();
+    }
     p.part_o = reinterpret_cast<float *>(base + L.o_off);
     p.part_m = reinterpret_cast<float *>(base + L.m_off);
     p.part_l = reinterpret_cast<float *>(base + L.l_off);
@@ -511,8 +553,8 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
         k_new = v_new = nullptr;
     }
     return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, k_new, v_new, window,
-                    qsrc);
+                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, facts.cu_count, k_new,
+                    v_new, window, qsrc);
 }
 
 // Paged varlen attention (several new query rows per sequence): plan, checks, launches.

@@ -42,6 +42,8 @@ struct DecodeParams {
     int32_t qk_mode;
     float eps;
     _Float16 *q_out;              // [B][Hq][D]
+    // dispatch order (multi-round grids): workgroup tile t serves sequence order[t / Hkv] (null: sequence t / Hkv)
+    const int32_t *order;         // [B], a permutation
 };
 
 // Arguments of the varlen attention kernel (several new query rows per sequence).
@@ -141,6 +143,12 @@ hipError_t launch_varlen(const VarlenParams &p, int num_seqs, int head_dim, int 
                          hipStream_t stream);
 hipError_t launch_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream);
+// Sequences that a multi-round decode grid can order longest first.
+constexpr int kOrderMaxSeqs = 16384;
+// order[0..B) <- the sequences sorted by the rows they attend (min(clamp(L, 0, cap_rows), window) with window > 0),
+// longest first, ties by index.
+hipError_t launch_order(const int32_t *context_lens, int B, int cap_rows, int window, int32_t *order,
+                        hipStream_t stream);
 hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
                                 int num_seqs, hipStream_t stream);
 hipError_t launch_qkv_cache(const QkvParams &p, int head_dim, hipStream_t stream);

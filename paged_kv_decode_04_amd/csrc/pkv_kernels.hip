@@ -295,8 +295,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     // from unrelated tiles.
     const int tile = SPLIT ? (int)(blockIdx.x / (unsigned)p.num_splits) : (int)blockIdx.x;
     const int split = SPLIT ? (int)(blockIdx.x - (unsigned)tile * p.num_splits) : 0;
-    const int s = tile / p.Hkv;
-    const int hk = tile - s * p.Hkv;
+    const int rank = tile / p.Hkv;
+    const int hk = tile - rank * p.Hkv;
+    // A grid of several rounds runs its sequences longest first (the host's order array): the dispatcher starts
+    // workgroups in id order as CUs free up, so the longest ones no longer start last and finish alone.
+    const int s = p.order ? uniform_load(p.order, rank) : rank;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int r = lane & 15;
@@ -1096,6 +1099,30 @@ __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, cons
         vdst[e * 16] = vh[e];
 }
 
+// Dispatch order for a multi-round decode grid: each thread ranks one sequence against every other by the rows
+// it attends (descending, ties by index), so order[] is a permutation.  Every workgroup holds all B keys in LDS
+// and ranks 256 sequences.
+__global__ __launch_bounds__(256) void order_kernel(const int32_t *lens, int B, int cap_rows, int window,
+                                                    int32_t *order) {
+    extern __shared__ int keys[];
+    for (int i = threadIdx.x; i < B; i += 256) {
+        int L = lens[i];
+        L = L < 0 ? 0 : (L > cap_rows ? cap_rows : L);
+        keys[i] = window > 0 && L > window ? window : L;
+    }
+    __syncthreads();
+    const int s = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (s >= B)
+        return;
+    const int ks = keys[s];
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+        const int kj = keys[j];
+        rank += (kj > ks || (kj == ks && j < s)) ? 1 : 0;
+    }
+    order[rank] = s;
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 
@@ -1261,6 +1288,15 @@ hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens
     const int64_t total = (int64_t)p.T * p.Hkv * (p.D / 8);
     hipLaunchKernelGGL(append_varlen_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p,
                        cu_seqlens_q, pos_offsets, num_seqs);
+    return hipGetLastError();
+}
+
+hipError_t launch_order(const int32_t *context_lens, int B, int cap_rows, int window, int32_t *order,
+                        hipStream_t stream) {
+    if (B <= 0 || B > kOrderMaxSeqs)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(order_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), sizeof(int) * (size_t)B, stream,
+                       context_lens, B, cap_rows, window, order);
     return hipGetLastError();
 }
 

@@ -209,6 +209,28 @@ def test_varlen_step_graph_replays_follow_device_state(torch_cuda):
     assert np.array_equal(g_state["vp"].cpu().numpy().view(np.uint16), vp_o.view(np.uint16))
 
 
+def test_single_pass_capture_of_a_multi_round_grid_needs_no_warm_up(torch_cuda):
+    """A single pass over 40 x 8 workgroups captured on a stream no call has used: the longest-first order would
+    need the library workspace to grow, which capture forbids, so the captured call runs in id order instead of
+    failing; its replay matches the eager result bit for bit."""
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    c = W.small_case(851, 40, 16, 8, 128, 16, tuple(1 + (53 * i) % 500 for i in range(40)))
+    st = _state(torch, c, c.context_lens)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        pkv.paged_decode_attention(st["q"], st["kp"], st["vp"], st["bt"], st["cl"], c.scale, out=st["out"],
+                                   num_splits=1)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        graph.replay()
+        torch.cuda.synchronize()
+    eager = pkv.paged_decode_attention(st["q"], st["kp"], st["vp"], st["bt"], st["cl"], c.scale, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(st["out"].view(torch.int16), eager.view(torch.int16))
+
+
 def test_capture_needing_a_new_workspace_fails_cleanly(torch_cuda):
     from paged_kv_decode_04_amd import pkv
     torch = torch_cuda

@@ -155,6 +155,29 @@ def test_attention_with_caller_workspace(torch_cuda):
     assert e.value.code == pkv.PKV_EWORKSPACE
 
 
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_multi_round_grid_runs_longest_first_with_the_same_results(torch_cuda, num_splits):
+    """80 sequences x 8 kv heads (640 workgroups, more than one round of the CUs) run longest first through the
+    library workspace; every output is bit-identical to the same call with a caller workspace (sequences in id
+    order) and matches the oracle.  Lengths include ties and empty sequences."""
+    torch = torch_cuda
+    from paged_kv_decode_04_amd import pkv
+    rng = np.random.default_rng(141)
+    lens = rng.integers(0, 400, 80)
+    lens[[3, 17, 40]] = 0
+    lens[[5, 6, 70]] = 250  # ties
+    c = W.small_case(142, 80, 32, 8, 128, 16, lens)
+    d = _upload(torch, c)
+    say("multi-round grid S=%d" % num_splits)
+    ordered = _gpu_attention(torch, pkv, c, d, num_splits)
+    plan = pkv.plan_decode(c.B, c.Hq, c.Hkv, c.D, c.BS, c.M, num_splits=num_splits)
+    ws = torch.empty(max(256, plan["workspace_bytes"]), dtype=torch.uint8, device="cuda")
+    plain = _gpu_attention(torch, pkv, c, d, num_splits, workspace=ws)
+    assert np.array_equal(ordered.view(np.uint16), plain.view(np.uint16))
+    ref = oracle.decode_attention(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale)
+    assert_close(ordered, ref, "multi-round grid S=%d" % num_splits)
+
+
 # --------------------------------------------------------------------------------------------------------------
 # split-K phase 1 and the combine, each on its own
 
