@@ -149,12 +149,19 @@ PKV_API int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int3
  *   per (device, stream), allocated on first need (that call synchronises the
  *   stream once before replacing a smaller buffer), never freed before
  *   process exit.  Calls on one stream reuse it in stream order.
+ *   Dispatch order: when the grid (num_seqs * Hkv * splits workgroups) is
+ *   larger than the device's CU count and num_seqs <= 16384, a small launch
+ *   first ranks the sequences by the rows they attend and the attention grid
+ *   runs them longest first (the ranks live in the library workspace; calls
+ *   with a caller workspace keep id order).  Results are identical either way.
  *   Graph capture: every entry point reads lengths, tables and positions on
  *   the device and sizes its launches from host arguments only, so a captured
  *   call replays correctly with new device-resident values.  A workspace that
- *   would have to grow while its stream is being captured is PKV_EWORKSPACE:
- *   make one call with the same shape on that stream before capturing, or
- *   use a _ws variant with a workspace allocated beforehand.
+ *   would have to grow for split-K partials while its stream is being
+ *   captured is PKV_EWORKSPACE: make one call with the same shape on that
+ *   stream before capturing, or use a _ws variant with a workspace allocated
+ *   beforehand.  (Where only the dispatch order would need the growth, the
+ *   captured call keeps id order instead.)
  *   q, k_pool, v_pool, out: 16-byte aligned.  num_seqs == 0 is a no-op.
  *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EHIP.
  * ------------------------------------------------------------------------- */
