@@ -141,8 +141,8 @@ struct WsLayout {
     size_t o_off, m_off, l_off, order_off, total;
 };
 
-// Split-K partials (S > 1), then, with order_seqs > 0, the dispatch order of that many sequences.
-WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t S, int64_t order_seqs = 0) {
+// Split-K partials (S > 1), then order_ints int32 of dispatch-order records.
+WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t S, int64_t order_ints = 0) {
     WsLayout L;
     const size_t o = S > 1 ? round256((size_t)(B * Hq * S * D) * sizeof(float)) : 0;
     const size_t ml = S > 1 ? round256((size_t)(B * Hq * S) * sizeof(float)) : 0;
@@ -150,7 +150,7 @@ WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t S, int64_t order_se
     L.m_off = o;
     L.l_off = o + ml;
     L.order_off = o + 2 * ml;
-    L.total = L.order_off + round256((size_t)order_seqs * sizeof(int32_t));
+    L.total = L.order_off + round256((size_t)order_ints * sizeof(int32_t));
     return L;
 }
 
@@ -386,7 +386,8 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
     // finish alone.  Only with the library workspace, and not where it would have to grow under graph capture.
     const int64_t grid = (int64_t)num_seqs * pool.num_kv_heads * plan.num_splits;
     bool order = library_ws && num_seqs > 1 && num_seqs <= pkv::kOrderMaxSeqs && cu_count > 0 && grid > cu_count;
-    WsLayout L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits, order ? num_seqs : 0);
+    WsLayout L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits,
+                           order ? (int64_t)num_seqs * pkv::kOrderRecord : 0);
     if (order && library_workspace_bytes(stream) < L.total) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         hipError_t e = hipStreamIsCapturing(stream, &cap);
@@ -419,8 +420,8 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
     char *base = static_cast<char *>(ws);
     if (order) {
         int32_t *ord = reinterpret_cast<int32_t *>(base + L.order_off);
-        hipError_t e = pkv::launch_order(context_lens, num_seqs, max_blocks_per_seq * pool.block_size, window, ord,
-                                         stream);
+        hipError_t e = pkv::launch_order(context_lens, block_tables, num_seqs, max_blocks_per_seq,
+                                         max_blocks_per_seq * pool.block_size, window, ord, stream);
         if (e != hipSuccess)
             return hip_fail(e, "order kernel launch");
         p.order = ord;

@@ -42,8 +42,9 @@ struct DecodeParams {
     int32_t qk_mode;
     float eps;
     _Float16 *q_out;              // [B][Hq][D]
-    // dispatch order (multi-round grids): workgroup tile t serves sequence order[t / Hkv] (null: sequence t / Hkv)
-    const int32_t *order;         // [B], a permutation
+    // dispatch order (multi-round grids): workgroup tile t serves the sequence of record order[t / Hkv] (null:
+    // sequence t / Hkv); see kOrderRecord
+    const int32_t *order;         // [B][kOrderRecord]
 };
 
 // Arguments of the varlen attention kernel (several new query rows per sequence).
@@ -145,10 +146,15 @@ hipError_t launch_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream);
 // Sequences that a multi-round decode grid can order longest first.
 constexpr int kOrderMaxSeqs = 16384;
-// order[0..B) <- the sequences sorted by the rows they attend (min(clamp(L, 0, cap_rows), window) with window > 0),
-// longest first, ties by index.
-hipError_t launch_order(const int32_t *context_lens, int B, int cap_rows, int window, int32_t *order,
-                        hipStream_t stream);
+// One record per rank of the dispatch order: the sequence, its length as stored, then its first kOrderRecBlocks
+// block-table entries -- everything a decode workgroup reads before its first K/V loads, in one place.
+constexpr int kOrderRecord = 32;
+constexpr int kOrderRecBlocks = kOrderRecord - 2;
+// Records of the sequences sorted by the rows they attend (min(clamp(L, 0, cap_rows), window) with window > 0),
+// longest first, ties by index: order[rank][0] = sequence, [1] = context_lens[sequence], [2 + i] = its table
+// entry i (i < min(M, kOrderRecBlocks)).
+hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables, int B, int M, int cap_rows,
+                        int window, int32_t *order, hipStream_t stream);
 hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
                                 int num_seqs, hipStream_t stream);
 hipError_t launch_qkv_cache(const QkvParams &p, int head_dim, hipStream_t stream);

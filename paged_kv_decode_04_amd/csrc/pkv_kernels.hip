@@ -83,6 +83,14 @@ __device__ __forceinline__ int uniform_load(const int32_t *p, int64_t i) {
     return ((const_i32_ptr)p)[i];
 }
 
+// p[i] and p[i + 1] in one scalar load (i even, p 8-byte aligned).
+typedef const __attribute__((address_space(4))) int64_t *const_i64_ptr;
+__device__ __forceinline__ void uniform_load_pair(const int32_t *p, int64_t i, int &a, int &b) {
+    const int64_t v = ((const_i64_ptr)p)[i / 2];
+    a = (int)(uint32_t)v;
+    b = (int)(uint32_t)(v >> 32);
+}
+
 // Floats of the decode kernel's cross-wave merge area: per wave, the running max and sum of 16 columns, then the
 // G heads' D-wide partial outputs (rows padded to D + 4).
 __host__ __device__ constexpr int merge_floats(int D, int G, int NW) { return 2 * NW * 16 + NW * G * (D + 4); }
@@ -280,7 +288,7 @@ constexpr int pipeline_stages() {
 // QKV (with FUSED): the decode step from the QKV projection rows -- q and the new K/V rows are taken from p.qkv,
 // the query and key heads RMS-normalised (qk_mode 1) and rotated at position L-1 in the prologue [ferrum-kernels
 // 0.7.7, src/backend/cuda/paged.rs: split_qkv_norm_rope_into_paged_cache_varlen, then paged_decode_attention].
-template <int D, int BS, int NW, bool SPLIT, bool FUSED, bool QKV = false>
+template <int D, int BS, int NW, bool SPLIT, bool FUSED, bool QKV = false, bool ORDERED = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     constexpr int KC = D / 32;
     constexpr int VC = D / 16;
@@ -297,9 +305,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const int split = SPLIT ? (int)(blockIdx.x - (unsigned)tile * p.num_splits) : 0;
     const int rank = tile / p.Hkv;
     const int hk = tile - rank * p.Hkv;
-    // A grid of several rounds runs its sequences longest first (the host's order array): the dispatcher starts
-    // workgroups in id order as CUs free up, so the longest ones no longer start last and finish alone.
-    const int s = p.order ? uniform_load(p.order, rank) : rank;
+    // ORDERED (a grid of several rounds): the sequences run longest first, tile t taking the sequence of order
+    // record t / Hkv -- the dispatcher starts workgroups in id order as CUs free up, so the longest ones no longer
+    // start last and finish alone.  The record also holds the length and the first block ids, so the first K/V
+    // loads still wait for one dependent load.
+    const int32_t *rec = ORDERED ? p.order + (int64_t)rank * kOrderRecord : nullptr;
+    int s_rec = 0, L_rec = 0;  // the record's sequence and length, one load
+    if (ORDERED)
+        uniform_load_pair(rec, 0, s_rec, L_rec);
+    const int s = ORDERED ? s_rec : rank;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int r = lane & 15;
@@ -311,14 +325,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     // them.  When the range start is known from the launch alone (a single pass starts at block 0, a fixed-size
     // split j at j*chunk_blocks), the ids of this wave's first NS units are requested together with the length,
     // so the first K/V loads wait for one dependent load, not two.
-    const bool start_known = (!SPLIT || p.chunk_blocks > 0) && p.window <= 0;
     const int u_known = (SPLIT ? split * p.chunk_blocks : 0) * SPB + wave;
     constexpr int NSPEC = 2 * NS - 1;  // the prologue's NS-1 units and the NS block ids requested ahead
+    const bool start_known = (!SPLIT || p.chunk_blocks > 0) && p.window <= 0 &&
+                             (!ORDERED || (u_known + (NSPEC - 1) * NW) / SPB < kOrderRecBlocks);
     int spec_raw[NSPEC];
 #pragma unroll
-    for (int j = 0; j < NSPEC; ++j)
-        spec_raw[j] = start_known ? uniform_load(bt, min(u_known + j * NW, max_units - 1) / SPB) : -1;
-    int L = uniform_load(p.context_lens, s);
+    for (int j = 0; j < NSPEC; ++j) {
+        const int bi = min(u_known + j * NW, max_units - 1) / SPB;
+        spec_raw[j] = start_known ? (ORDERED ? uniform_load(rec, 2 + bi) : uniform_load(bt, bi)) : -1;
+    }
+    int L = ORDERED ? L_rec : uniform_load(p.context_lens, s);
 
     // Q^T as the B operand: lane (g4, r) holds head r, dims 32c + 8*g4 .. +8.  Columns r >= G (no such head in
     // the group) repeat head 0; every column of the matrix-core tiles is independent and those are never stored.
@@ -1100,10 +1117,11 @@ __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, cons
 }
 
 // Dispatch order for a multi-round decode grid: each thread ranks one sequence against every other by the rows
-// it attends (descending, ties by index), so order[] is a permutation.  Every workgroup holds all B keys in LDS
-// and ranks 256 sequences.
-__global__ __launch_bounds__(256) void order_kernel(const int32_t *lens, int B, int cap_rows, int window,
-                                                    int32_t *order) {
+// it attends (descending, ties by index), so the ranks are a permutation, and writes the sequence's record at its
+// rank.  Every workgroup holds all B keys in LDS and ranks 256 sequences.
+__global__ __launch_bounds__(256) void order_kernel(const int32_t *__restrict__ lens,
+                                                    const int32_t *__restrict__ block_tables, int B, int M,
+                                                    int cap_rows, int window, int32_t *__restrict__ order) {
     extern __shared__ int keys[];
     for (int i = threadIdx.x; i < B; i += 256) {
         int L = lens[i];
@@ -1114,13 +1132,25 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t *lens, int B, 
     const int s = (int)blockIdx.x * 256 + (int)threadIdx.x;
     if (s >= B)
         return;
+    // the record's table entries, all requested before the ranking loop (one memory latency, not one per entry)
+    const int nb = M < kOrderRecBlocks ? M : kOrderRecBlocks;
+    int ids[kOrderRecBlocks];
+#pragma unroll
+    for (int i = 0; i < kOrderRecBlocks; ++i)
+        ids[i] = i < nb ? block_tables[(int64_t)s * M + i] : 0;
     const int ks = keys[s];
     int rank = 0;
     for (int j = 0; j < B; ++j) {
         const int kj = keys[j];
         rank += (kj > ks || (kj == ks && j < s)) ? 1 : 0;
     }
-    order[rank] = s;
+    int32_t *rec = order + (int64_t)rank * kOrderRecord;
+    rec[0] = s;
+    rec[1] = lens[s];
+#pragma unroll
+    for (int i = 0; i < kOrderRecBlocks; ++i)
+        if (i < nb)
+            rec[2 + i] = ids[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -1151,6 +1181,11 @@ static hipError_t launch_decode_t(const DecodeParams &p, int num_seqs, bool spli
             hipLaunchKernelGGL((decode_kernel<D, BS, NW, true, true, true>), grid, block, lds, stream, p);
         else
             hipLaunchKernelGGL((decode_kernel<D, BS, NW, false, true, true>), grid, block, lds, stream, p);
+    } else if (p.order != nullptr && !fused) {  // a multi-round grid in dispatch order (never the one-launch step)
+        if (split)
+            hipLaunchKernelGGL((decode_kernel<D, BS, NW, true, false, false, true>), grid, block, lds, stream, p);
+        else
+            hipLaunchKernelGGL((decode_kernel<D, BS, NW, false, false, false, true>), grid, block, lds, stream, p);
     } else if (split && fused)
         hipLaunchKernelGGL((decode_kernel<D, BS, NW, true, true>), grid, block, lds, stream, p);
     else if (split)
@@ -1291,12 +1326,12 @@ hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens
     return hipGetLastError();
 }
 
-hipError_t launch_order(const int32_t *context_lens, int B, int cap_rows, int window, int32_t *order,
-                        hipStream_t stream) {
+hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables, int B, int M, int cap_rows,
+                        int window, int32_t *order, hipStream_t stream) {
     if (B <= 0 || B > kOrderMaxSeqs)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(order_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), sizeof(int) * (size_t)B, stream,
-                       context_lens, B, cap_rows, window, order);
+                       context_lens, block_tables, B, M, cap_rows, window, order);
     return hipGetLastError();
 }
 
