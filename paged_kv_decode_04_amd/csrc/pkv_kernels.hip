@@ -1116,41 +1116,64 @@ __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, cons
         vdst[e * 16] = vh[e];
 }
 
-// Dispatch order for a multi-round decode grid: each thread ranks one sequence against every other by the rows
-// it attends (descending, ties by index), so the ranks are a permutation, and writes the sequence's record at its
-// rank.  Every workgroup holds all B keys in LDS and ranks 256 sequences.
+// Dispatch order for a multi-round decode grid: each sequence is ranked against every other by the rows it attends
+// (descending, ties by index), so the ranks are a permutation, and its record is written at its rank.  Every
+// workgroup holds all B keys in LDS (padded to a multiple of 4 with -1, which never counts) and ranks 64 sequences,
+// four lanes per sequence, each lane scanning a quarter of the keys 16 bytes at a time; the quad sums its counts.
+constexpr int kOrderSeqsPerGroup = 64;
 __global__ __launch_bounds__(256) void order_kernel(const int32_t *__restrict__ lens,
                                                     const int32_t *__restrict__ block_tables, int B, int M,
                                                     int cap_rows, int window, int32_t *__restrict__ order) {
     extern __shared__ int keys[];
-    for (int i = threadIdx.x; i < B; i += 256) {
-        int L = lens[i];
-        L = L < 0 ? 0 : (L > cap_rows ? cap_rows : L);
-        keys[i] = window > 0 && L > window ? window : L;
+    const int B4 = (B + 3) / 4;
+    for (int i = threadIdx.x; i < 4 * B4; i += 256) {
+        int key = -1;
+        if (i < B) {
+            int L = lens[i];
+            L = L < 0 ? 0 : (L > cap_rows ? cap_rows : L);
+            key = window > 0 && L > window ? window : L;
+        }
+        keys[i] = key;
+    }
+    const int s = (int)blockIdx.x * kOrderSeqsPerGroup + (int)(threadIdx.x >> 2);
+    const int part = (int)(threadIdx.x & 3);
+    // this lane's share of the record's table entries (i = part, part + 4, ...), requested before the scan
+    const int nb = M < kOrderRecBlocks ? M : kOrderRecBlocks;
+    constexpr int kPer = (kOrderRecBlocks + 3) / 4;
+    int ids[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = part + 4 * k;
+        ids[k] = (s < B && i < nb) ? block_tables[(int64_t)s * M + i] : 0;
     }
     __syncthreads();
-    const int s = (int)blockIdx.x * 256 + (int)threadIdx.x;
     if (s >= B)
-        return;
-    // the record's table entries, all requested before the ranking loop (one memory latency, not one per entry)
-    const int nb = M < kOrderRecBlocks ? M : kOrderRecBlocks;
-    int ids[kOrderRecBlocks];
-#pragma unroll
-    for (int i = 0; i < kOrderRecBlocks; ++i)
-        ids[i] = i < nb ? block_tables[(int64_t)s * M + i] : 0;
+        return;  // the whole quad of s leaves together
     const int ks = keys[s];
     int rank = 0;
-    for (int j = 0; j < B; ++j) {
-        const int kj = keys[j];
-        rank += (kj > ks || (kj == ks && j < s)) ? 1 : 0;
+    const int4 *k4 = reinterpret_cast<const int4 *>(keys);
+#pragma unroll 4
+    for (int j4 = part; j4 < B4; j4 += 4) {
+        const int4 kv = k4[j4];
+        const int j = 4 * j4;
+        rank += (kv.x > ks || (kv.x == ks && j < s)) ? 1 : 0;
+        rank += (kv.y > ks || (kv.y == ks && j + 1 < s)) ? 1 : 0;
+        rank += (kv.z > ks || (kv.z == ks && j + 2 < s)) ? 1 : 0;
+        rank += (kv.w > ks || (kv.w == ks && j + 3 < s)) ? 1 : 0;
     }
+    rank += __shfl_xor(rank, 1);
+    rank += __shfl_xor(rank, 2);
     int32_t *rec = order + (int64_t)rank * kOrderRecord;
-    rec[0] = s;
-    rec[1] = lens[s];
+    if (part == 0) {
+        rec[0] = s;
+        rec[1] = lens[s];
+    }
 #pragma unroll
-    for (int i = 0; i < kOrderRecBlocks; ++i)
+    for (int k = 0; k < kPer; ++k) {
+        const int i = part + 4 * k;
         if (i < nb)
-            rec[2 + i] = ids[i];
+            rec[2 + i] = ids[k];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1330,8 +1353,9 @@ hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables
                         int window, int32_t *order, hipStream_t stream) {
     if (B <= 0 || B > kOrderMaxSeqs)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(order_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), sizeof(int) * (size_t)B, stream,
-                       context_lens, block_tables, B, M, cap_rows, window, order);
+    hipLaunchKernelGGL(order_kernel, dim3((unsigned)((B + kOrderSeqsPerGroup - 1) / kOrderSeqsPerGroup)), dim3(256),
+                       sizeof(int) * (size_t)((B + 3) / 4 * 4), stream, context_lens, block_tables, B, M, cap_rows,
+                       window, order);
     return hipGetLastError();
 }
 
