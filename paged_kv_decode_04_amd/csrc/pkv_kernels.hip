@@ -944,15 +944,37 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
 
 // Split-K phase 2: one wavefront per (sequence, query head), lanes over dims.
 // out = sum_j e^(m_j - M) O_j / sum_j e^(m_j - M) l_j over the non-empty splits.
+// Up to 64 splits (lane j holds m_j, l_j), every load the row needs is issued before its length arrives -- the
+// partials of splits past the last non-empty one are read but never used -- so the kernel waits on memory once;
+// the weights reach the dim lanes by lane broadcast.  More splits take the general loop.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     constexpr int PER = (D + 63) / 64;
+    constexpr int CH = 8;  // splits whose outputs are requested together
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // s * Hq + hq
     if (row >= p.B * p.Hq)
         return;
     const int s = row / p.Hq;
-    int nvalid = p.num_splits;  // no lengths: every split was written (varlen phase 1)
+    const int S = p.num_splits;
+    const int64_t base = (int64_t)row * S;
+    const bool fast = S <= 64;
+    float mj = kNegBig, lj = 0.f, o0[CH][PER];
+    if (fast) {
+        if (lane < S) {
+            mj = p.part_m[base + lane];
+            lj = p.part_l[base + lane];
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int d = lane + 64 * k;
+                o0[c][k] = (c < S && d < D) ? p.part_o[(base + c) * D + d] : 0.f;
+            }
+        }
+    }
+    int nvalid = S;  // no lengths: every split was written (varlen phase 1)
     if (p.context_lens != nullptr) {
         int L = p.context_lens[s];
         L = L < 0 ? 0 : (L > p.M * p.BS ? p.M * p.BS : L);
@@ -961,31 +983,64 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
         nvalid = 0;
         if (nb > b_lo) {
             const int n = nb - b_lo;
-            const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (n + p.num_splits - 1) / p.num_splits;
-            nvalid = min(p.num_splits, (n + chunk - 1) / chunk);
+            const int chunk = p.chunk_blocks > 0 ? p.chunk_blocks : (n + S - 1) / S;
+            nvalid = min(S, (n + chunk - 1) / chunk);
         }
     }
-    const int64_t base = (int64_t)row * p.num_splits;
-    float M = kNegBig;
-    for (int j = lane; j < nvalid; j += 64)
-        M = fmaxf(M, p.part_m[base + j]);
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1)
-        M = fmaxf(M, xor_lane(M, mask));
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k)
         acc[k] = 0.f;
     float den = 0.f;
-    for (int j = 0; j < nvalid; ++j) {
-        const float a = expf(p.part_m[base + j] - M);
-        den += a * p.part_l[base + j];
-        const float *oj = p.part_o + (base + j) * D;
+    if (fast) {
+        float M = lane < nvalid ? mj : kNegBig;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int d = lane + 64 * k;
-            if (d < D)
-                acc[k] += a * oj[d];
+        for (int mask = 32; mask >= 1; mask >>= 1)
+            M = fmaxf(M, xor_lane(M, mask));
+        const float a_lane = lane < nvalid ? expf(mj - M) : 0.f;
+        den = lane < nvalid ? a_lane * lj : 0.f;
+#pragma unroll
+        for (int mask = 32; mask >= 1; mask >>= 1)
+            den += xor_lane(den, mask);
+        for (int j0 = 0; j0 < nvalid; j0 += CH) {
+            float o[CH][PER];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+#pragma unroll
+                for (int k = 0; k < PER; ++k) {
+                    const int d = lane + 64 * k;
+                    o[c][k] = j0 == 0 ? o0[c][k]
+                                      : ((j0 + c < S && d < D) ? p.part_o[(base + j0 + c) * D + d] : 0.f);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int j = j0 + c;
+                const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a_lane), j < 64 ? j : 63));
+                if (j < nvalid) {
+#pragma unroll
+                    for (int k = 0; k < PER; ++k)
+                        acc[k] += a * o[c][k];
+                }
+            }
+        }
+    } else {
+        float M = kNegBig;
+        for (int j = lane; j < nvalid; j += 64)
+            M = fmaxf(M, p.part_m[base + j]);
+#pragma unroll
+        for (int mask = 32; mask >= 1; mask >>= 1)
+            M = fmaxf(M, xor_lane(M, mask));
+        for (int j = 0; j < nvalid; ++j) {
+            const float a = expf(p.part_m[base + j] - M);
+            den += a * p.part_l[base + j];
+            const float *oj = p.part_o + (base + j) * D;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int d = lane + 64 * k;
+                if (d < D)
+                    acc[k] += a * oj[d];
+            }
         }
     }
 #pragma unroll
