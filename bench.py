@@ -133,12 +133,32 @@ def _pmc_per_dispatch(path: str, counter: str) -> dict:
     return rows
 
 
-def dominant(config: str, kernel: str) -> bool:
-    """Whether a pkv kernel is part of the workload's dominant kernel (the one `roofline` reports): the QKV kernel
-    for QKV-only workloads, the attention kernels otherwise."""
+def _kernel_kind(short: str):
+    """(base name, fused, split) of a pkv kernel name as the profiler prints it, e.g.
+    'pkv::decode_kernel<128, 16, 8, false, true, false, false>' (template arguments D, BS, NW, SPLIT, FUSED, ...;
+    varlen_kernel: D, BS, NW, SPLIT, QT[, FUSED])."""
+    base, _, rest = short.partition("<")
+    args = [a.strip() for a in rest.rstrip(">").split(",")] if rest else []
+    base = base.split("::")[-1]
+    if base == "decode_kernel" and len(args) >= 5:
+        return base, args[4] == "true", args[3] == "true"
+    if base == "varlen_kernel" and len(args) >= 5:
+        return base, len(args) >= 6 and args[5] == "true", args[3] == "true"
+    return base, False, False
+
+
+def dominant_kernels(config: str, names) -> list:
+    """The kernels of the launch (or call) `roofline` reports: the QKV kernel for QKV-only workloads; the step
+    kernel when the step is one launch (a fused single-pass kernel); otherwise the attention call's kernels
+    (unfused attention, the dispatch order, the combine)."""
     if config in QKV_ONLY:
-        return "qkv" in kernel
-    return "append" not in kernel and "qkv" not in kernel
+        return [n for n in names if "qkv" in n]
+    kinds = {n: _kernel_kind(n) for n in names}
+    step = [n for n, (_, fused, split) in kinds.items() if fused and not split]
+    if step:
+        return step
+    return [n for n, (base, fused, _) in kinds.items()
+            if (base in ("decode_kernel", "varlen_kernel") and not fused) or base in ("combine_kernel", "order_kernel")]
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy_mib: float) -> dict:
@@ -160,21 +180,23 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy
                 per_kernel.setdefault(short, {}).setdefault(counter, []).append(v)
     step_bytes = 0.0
     kern = {}
+    dom = dominant_kernels(config, list(per_kernel))
     for short, cnt in per_kernel.items():
         f = sum(cnt.get("FETCH_SIZE", [0])) / max(1, len(cnt.get("FETCH_SIZE", [0])))
         w = sum(cnt.get("WRITE_SIZE", [0])) / max(1, len(cnt.get("WRITE_SIZE", [0])))
         fb = f * 1024 * factors["FETCH_SIZE"]
         wb = w * 1024 * factors["WRITE_SIZE"]
         kern[short] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": len(cnt.get("FETCH_SIZE", []))}
-        if dominant(config, short):
+        if short in dom:
             step_bytes += fb + wb
     out.update({"copy_calibration_mib": copy_mib, "scale_factors": factors, "kernels": kern,
+                "dominant_kernels": dom,
                 "hbm_bytes_per_step": round(step_bytes),
                 "note": "Counters are KiB per dispatch; each is scaled by its reading for the calibration copy kernel "
-                        "(torch.neg over %g MiB, which reads and writes %g MiB). hbm_bytes_per_step sums the "
-                        "dominant kernels of one step (%s)."
-                        % (copy_mib, copy_mib, "the QKV-to-cache kernel" if config in QKV_ONLY else
-                           "attention; a separate append or QKV launch, if any, excluded")})
+                        "(torch.neg over %g MiB, which reads and writes %g MiB). hbm_bytes_per_step sums, per "
+                        "dispatch, the kernels of the launch or call that roofline reports (dominant_kernels: the "
+                        "step kernel when a step is one launch, else the attention call's kernels; a separate append "
+                        "or QKV launch excluded)." % (copy_mib, copy_mib)})
     return out
 
 
