@@ -357,7 +357,7 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
              void *workspace, size_t workspace_bytes, bool library_ws, hipStream_t stream, int cu_count,
              const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr, int32_t window = 0,
-             const QkvSource *qsrc = nullptr) {
+             const QkvSource *qsrc = nullptr, const pkv::AppendParams *pre_append = nullptr) {
     pkv::DecodeParams p = decode_params(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
                                         num_q_heads, scale);
     p.window = window;
@@ -399,6 +399,11 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
         }
     }
     if (plan.num_splits == 1 && !order) {
+        if (pre_append) {
+            hipError_t e = pkv::launch_append_newest(*pre_append, stream);
+            if (e != hipSuccess)
+                return hip_fail(e, "append kernel launch");
+        }
         hipError_t e = pkv::launch_decode(p, num_seqs, pool.head_dim, pool.block_size, plan.waves_per_group, false,
                                           stream);
         if (e != hipSuccess)
@@ -418,14 +423,22 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
             return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
     }
     char *base = static_cast<char *>(ws);
-    if (order) {
-        int32_t *ord = reinterpret_cast<int32_t *>(base + L.order_off);
+    int32_t *ord = order ? reinterpret_cast<int32_t *>(base + L.order_off) : nullptr;
+    if (pre_append) {  // the decode step's append launch, which also writes the order records
+        pkv::AppendParams a = *pre_append;
+        a.order = ord;
+        a.order_cap = max_blocks_per_seq * pool.block_size;
+        a.order_window = window;
+        hipError_t e = pkv::launch_append_newest(a, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "append kernel launch");
+    } else if (ord) {
         hipError_t e = pkv::launch_order(context_lens, block_tables, num_seqs, max_blocks_per_seq,
                                          max_blocks_per_seq * pool.block_size, window, ord, stream);
         if (e != hipSuccess)
             return hip_fail(e, "order kernel launch");
-        p.order = ord;
     }
+    p.order = ord;
     if (plan.num_splits == 1) {
         hipError_t e = pkv::launch_decode(p, num_seqs, pool.head_dim, pool.block_size, plan.waves_per_group, false,
                                           stream);
@@ -548,10 +561,11 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
         a.BS = pool.block_size;
         a.N = pool.num_blocks;
         a.M = max_blocks_per_seq;
-        hipError_t e = pkv::launch_append_newest(a, stream);
-        if (e != hipSuccess)
-            return hip_fail(e, "append kernel launch");
         k_new = v_new = nullptr;
+        // run_plan launches it first, with the dispatch-order records folded in when the grid is ordered
+        return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                        num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, facts.cu_count,
+                        nullptr, nullptr, window, qsrc, &a);
     }
     return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                     num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, facts.cu_count, k_new,

@@ -94,6 +94,10 @@ struct AppendParams {
     _Float16 *k_pool;
     _Float16 *v_pool;
     int32_t T, Hkv, D, BS, N, M;
+    // launch_append_newest only: when order is non-null, extra workgroups also write the dispatch-order records of
+    // the T sequences (as launch_order, rows capped at order_cap, window order_window)
+    int32_t *order;
+    int32_t order_cap, order_window;
 };
 
 // Arguments of the QKV-to-cache kernel (split QKV, q/k RMSNorm, RoPE, paged-cache write).

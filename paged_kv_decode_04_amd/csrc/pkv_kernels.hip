@@ -1094,7 +1094,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // panels holding the row whole -- each thread one 16-byte chunk: read, replace the row's part, write back -- so the
 // pools see only full-line writes (scattered 2- and 16-byte row stores cost far more at the memory than their
 // bytes).  Valid only because the block holding a sequence's newest row belongs to that sequence alone.
+__device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ lens,
+                                                  const int32_t *__restrict__ block_tables, int B, int M, int cap_rows,
+                                                  int window, int32_t *__restrict__ order, int group, int *keys);
+
+// With p.order set, the workgroups past the T * Hkv appends write the dispatch-order records instead (the ranking
+// of launch_order, in the same launch as the append).
 __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
+    if (p.order != nullptr && blockIdx.x >= (unsigned)(p.T * p.Hkv)) {
+        extern __shared__ int keys[];
+        rank_into_records(p.context_lens, p.block_tables, p.T, p.M, p.order_cap, p.order_window, p.order,
+                          (int)(blockIdx.x - (unsigned)(p.T * p.Hkv)), keys);
+        return;
+    }
     const int s = (int)(blockIdx.x / (unsigned)p.Hkv);
     const int h = (int)(blockIdx.x - (unsigned)s * p.Hkv);
     int L = p.context_lens[s];
@@ -1176,10 +1188,10 @@ __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, cons
 // workgroup holds all B keys in LDS (padded to a multiple of 4 with -1, which never counts) and ranks 64 sequences,
 // four lanes per sequence, each lane scanning a quarter of the keys 16 bytes at a time; the quad sums its counts.
 constexpr int kOrderSeqsPerGroup = 64;
-__global__ __launch_bounds__(256) void order_kernel(const int32_t *__restrict__ lens,
-                                                    const int32_t *__restrict__ block_tables, int B, int M,
-                                                    int cap_rows, int window, int32_t *__restrict__ order) {
-    extern __shared__ int keys[];
+// One workgroup's share (sequences group * 64 ..) of the ranking; keys: LDS for all B keys, rounded up to 4.
+__device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ lens,
+                                                  const int32_t *__restrict__ block_tables, int B, int M, int cap_rows,
+                                                  int window, int32_t *__restrict__ order, int group, int *keys) {
     const int B4 = (B + 3) / 4;
     for (int i = threadIdx.x; i < 4 * B4; i += 256) {
         int key = -1;
@@ -1190,7 +1202,7 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t *__restrict__ 
         }
         keys[i] = key;
     }
-    const int s = (int)blockIdx.x * kOrderSeqsPerGroup + (int)(threadIdx.x >> 2);
+    const int s = group * kOrderSeqsPerGroup + (int)(threadIdx.x >> 2);
     const int part = (int)(threadIdx.x & 3);
     // this lane's share of the record's table entries (i = part, part + 4, ...), requested before the scan
     const int nb = M < kOrderRecBlocks ? M : kOrderRecBlocks;
@@ -1229,6 +1241,13 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t *__restrict__ 
         if (i < nb)
             rec[2 + i] = ids[k];
     }
+}
+
+__global__ __launch_bounds__(256) void order_kernel(const int32_t *__restrict__ lens,
+                                                    const int32_t *__restrict__ block_tables, int B, int M,
+                                                    int cap_rows, int window, int32_t *__restrict__ order) {
+    extern __shared__ int keys[];
+    rank_into_records(lens, block_tables, B, M, cap_rows, window, order, (int)blockIdx.x, keys);
 }
 
 // ---------------------------------------------------------------------------
@@ -1390,7 +1409,12 @@ hipError_t launch_combine(const CombineParams &p, int head_dim, hipStream_t stre
 hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream) {
     if (p.T <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL(append_newest_kernel, dim3((unsigned)((int64_t)p.T * p.Hkv)), dim3(256), 0, stream, p);
+    if (p.order != nullptr && p.T > kOrderMaxSeqs)
+        return hipErrorInvalidValue;
+    const unsigned order_groups = p.order ? (unsigned)((p.T + kOrderSeqsPerGroup - 1) / kOrderSeqsPerGroup) : 0u;
+    const size_t lds = p.order ? sizeof(int) * (size_t)((p.T + 3) / 4 * 4) : 0;
+    hipLaunchKernelGGL(append_newest_kernel, dim3((unsigned)((int64_t)p.T * p.Hkv) + order_groups), dim3(256), lds,
+                       stream, p);
     return hipGetLastError();
 }
 
