@@ -178,6 +178,32 @@ def test_multi_round_grid_runs_longest_first_with_the_same_results(torch_cuda, n
     assert_close(ordered, ref, "multi-round grid S=%d" % num_splits)
 
 
+@pytest.mark.parametrize("B", [4, 80])
+@pytest.mark.parametrize("plan", [dict(num_splits=1, chunk_blocks=0, waves_per_group=8),
+                                  dict(num_splits=1, chunk_blocks=0, waves_per_group=2),
+                                  dict(num_splits=3, chunk_blocks=0, waves_per_group=4),
+                                  dict(num_splits=10, chunk_blocks=4, waves_per_group=8),
+                                  dict(num_splits=20, chunk_blocks=2, waves_per_group=1)],
+                         ids=lambda p: "S%d_chunk%d_w%d" % (p["num_splits"], p["chunk_blocks"], p["waves_per_group"]))
+def test_planned_calls_match_oracle(torch_cuda, B, plan):
+    """pkv_paged_decode_attention_planned with explicit split counts, fixed block chunks and wave counts, on a
+    batch of one round (4 x 8 kv heads) and of several (80 x 8: longest first through the library workspace, where
+    fixed chunks start past the order record's block ids)."""
+    torch = torch_cuda
+    from paged_kv_decode_04_amd import pkv
+    rng = np.random.default_rng(150 + B)
+    lens = rng.integers(1, 600, B)
+    lens[0] = 600
+    c = W.small_case(151 + B, B, 32, 8, 128, 16, lens)
+    d = _upload(torch, c)
+    say("planned %s B=%d" % (plan, B))
+    out = pkv.paged_decode_attention_planned(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                                             c.scale, plan)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale)
+    assert_close(out.cpu().numpy(), ref, "planned %s B=%d" % (plan, B))
+
+
 # --------------------------------------------------------------------------------------------------------------
 # split-K phase 1 and the combine, each on its own
 
