@@ -278,15 +278,16 @@ def main(argv=None) -> int:
         rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config, splits,
                             args.copy_calibration_mib or 512.0)
         extra = " --unfused" if args.unfused and step_is_fused(args.config, False) else ""
+        # the commands that produced the two counter files (their directories as given here)
+        fetch_csv, write_csv = args.summarize_pmc
         rec["commands"] = [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o %s -- python3 bench.py --config %s "
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o %s -- python3 bench.py --config %s "
             "--steps 50 --warmup 10 --no-cpu-baseline --copy-calibration-mib %g%s"
-            % (args.config, args.config, rec["copy_calibration_mib"], extra),
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o %s -- python3 bench.py --config %s "
+            % (os.path.dirname(fetch_csv), args.config, args.config, rec["copy_calibration_mib"], extra),
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o %s -- python3 bench.py --config %s "
             "--steps 50 --warmup 10 --no-cpu-baseline --copy-calibration-mib %g%s"
-            % (args.config, args.config, rec["copy_calibration_mib"], extra),
-            "python bench.py --summarize-pmc gpurun_out/pmc_fetch/%s_counter_collection.csv "
-            "gpurun_out/pmc_write/%s_counter_collection.csv --config %s%s" % (args.config, args.config, args.config, extra),
+            % (os.path.dirname(write_csv), args.config, args.config, rec["copy_calibration_mib"], extra),
+            "python bench.py --summarize-pmc %s %s --config %s%s" % (fetch_csv, write_csv, args.config, extra),
         ]
         path = traffic_path(args.config, splits, step_is_fused(args.config, args.unfused))
         with open(path, "w") as f:
