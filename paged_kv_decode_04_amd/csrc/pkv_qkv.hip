@@ -53,7 +53,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kBatch = 1;  // passes whose qkv pieces are loaded together (more measured no faster)
+constexpr int kBatch = 2;  // passes whose qkv pieces are loaded together (1 and 4 measured slower)
 
 // Sequence s's unit slots are [V_s / 16, V_{s+1} / 16) with V_s = cu[s] + 32 s: at least floor(n_s / 16) + 2 slots
 // for its n_s new rows, enough for the 16-row cache units they touch wherever the first one starts.  The slot
