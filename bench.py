@@ -200,6 +200,20 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy
     return out
 
 
+def _host_cpu() -> dict:
+    """The host's logical CPU count and model name (from /proc/cpuinfo, where readable)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cpus": os.cpu_count(), "cpu_model": model}
+
+
 def cpu_baseline_qkv(case, seconds: float, with_attention: bool):
     """The oracle's QKV step (and, for a decode step, its decode attention on the step's outputs) on the host."""
     import oracle
@@ -225,6 +239,7 @@ def cpu_baseline_qkv(case, seconds: float, with_attention: bool):
         if el >= seconds:
             break
     return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            **_host_cpu(),
             "sample": "%d full step(s) of the workload (QKV step of %d tokens%s, f64) in %.1f s; %.3f steps/s; the "
                       "QKV step is single-threaded" % (reps, vc.T, ", then decode attention of all %d sequences x %d "
                       "heads" % (vc.B, vc.Hq) if with_attention else "", el, reps / el)}
@@ -249,6 +264,7 @@ def cpu_baseline(case, seconds: float, window: int = 0):
         if el >= seconds:
             break
     return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            **_host_cpu(),
             "sample": "%d full %s call(s) of the workload (all %d sequences x %d heads, f64) in %.1f s; "
                       "%.3f calls/s" % (reps, "varlen-attention" if varlen else "decode-attention", case.B, case.Hq,
                                         el, reps / el)}
