@@ -103,16 +103,18 @@ def test_varlen_step_rows_of_a_missing_block_are_not_written(torch_cuda):
     assert_close(out[:4], ref0, "missing block: the intact sequence")
 
 
-def test_varlen_step_v2_full_size(torch_cuda):
-    """The step on the bench's v2 workload (32 sequences, 8 new rows each, one launch): pools bit-exact and 256
-    sampled (token, head) rows against the oracle."""
-    c = W.config_v2()
-    out, kp, vp = _step(torch_cuda, c, 0, 8)
+@pytest.mark.parametrize("name", ["v1", "v2"])
+def test_varlen_step_full_size(torch_cuda, name):
+    """The step on the bench's v1 / v2 workloads (32 sequences, 4 or 8 new rows each, one launch): pools bit-exact
+    and 256 sampled (token, head) rows against the oracle."""
+    c = W.VARLEN_CONFIGS[name]()
+    say("varlen step %s full size" % name)
+    out, kp, vp = _step(torch_cuda, c, 0, int(c.q_lens.max()))
     rk, rv = c.k_pool.copy(), c.v_pool.copy()
     oracle.paged_kv_append(c.k_new, c.v_new, c.slot_mapping, rk, rv)
-    _assert_pools(kp, vp, rk, rv, "v2 step")
+    _assert_pools(kp, vp, rk, rv, "%s step" % name)
     rng = np.random.default_rng(1371)
     units = np.stack([rng.integers(0, c.T, 256), rng.integers(0, c.Hq, 256)], axis=1).astype(np.int32)
     units[:3] = [[0, 0], [c.T - 1, c.Hq - 1], [7, 5]]
     ref = oracle.varlen_attention(c.q, rk, rv, c.block_tables, c.cu_seqlens_q, c.pos_offsets, c.scale, units=units)
-    assert_close(out[units[:, 0], units[:, 1]], ref, "v2 step")
+    assert_close(out[units[:, 0], units[:, 1]], ref, "%s step" % name)

@@ -110,3 +110,24 @@ def test_window_step_matches_append_then_window_attention(torch_cuda, geom, num_
                                             num_splits=num_splits)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint16), att.cpu().numpy().view(np.uint16))
+
+
+def test_window_step_on_the_llama3_8b_batch(torch_cuda):
+    """The w1 workload bench.py times: pkv_paged_decode_step_window on the c2 batch at window 512 (one launch), its
+    newest rows poisoned beforehand; pools bit-exact on every written block and every output against the oracle."""
+    from paged_kv_decode_04_amd import pkv
+    from test_gpu_parity import full_new_rows
+    torch = torch_cuda
+    c = W.config_c2()
+    kn, vn = full_new_rows(c)
+    dk, dv = _dev(torch, c.k_pool), _dev(torch, c.v_pool)
+    out = pkv.paged_decode_step_window(_dev(torch, c.q), _dev(torch, kn), _dev(torch, vn), dk, dv,
+                                       _dev(torch, c.block_tables), _dev(torch, c.context_lens), c.scale, 512)
+    torch.cuda.synchronize()
+    kp, vp = c.k_pool.copy(), c.v_pool.copy()
+    oracle.paged_kv_append(c.k_new, c.v_new, c.slot_mapping, kp, vp)
+    blocks = c.slot_mapping // c.BS
+    assert np.array_equal(dk.cpu().numpy()[blocks].view(np.uint16), kp[blocks].view(np.uint16))
+    assert np.array_equal(dv.cpu().numpy()[blocks].view(np.uint16), vp[blocks].view(np.uint16))
+    ref = oracle.decode_attention(c.q, kp, vp, c.block_tables, c.context_lens, c.scale, window=512)
+    assert_close(out.cpu().numpy(), ref, "w1 window step")
