@@ -23,12 +23,17 @@ def _state(torch, c, lens0):
                 cl=_dev(torch, lens0), out=torch.empty((c.B, c.Hq, c.D), dtype=torch.float16, device="cuda"))
 
 
+@pytest.mark.parametrize("B", [4, 40])
 @pytest.mark.parametrize("num_splits", [1, 3])
-def test_decode_step_graph_replays_follow_device_state(torch_cuda, num_splits):
+def test_decode_step_graph_replays_follow_device_state(torch_cuda, num_splits, B):
+    """B = 4: one launch per step; B = 40 (320 workgroups, more than one round of the CUs): the append launch,
+    which also ranks the sequences longest first, then the ordered attention -- the order recomputed from the
+    device-resident lengths on every replay."""
     from paged_kv_decode_04_amd import pkv
     torch = torch_cuda
-    lens0 = np.array([100, 31, 47, 16], dtype=np.int32)
-    c = W.small_case(811 + num_splits, 4, 32, 8, 128, 16, lens0 + STEPS)  # tables hold the grown sequences
+    lens0 = (np.array([100, 31, 47, 16], dtype=np.int32) if B == 4 else
+             np.random.default_rng(810).integers(1, 300, B).astype(np.int32))
+    c = W.small_case(811 + num_splits + B, B, 32, 8, 128, 16, lens0 + STEPS)  # tables hold the grown sequences
     rng = np.random.default_rng(812)
     g_state, e_state = _state(torch, c, lens0), _state(torch, c, lens0)
 
@@ -66,13 +71,13 @@ def test_decode_step_graph_replays_follow_device_state(torch_cuda, num_splits):
         torch.cuda.synchronize()
         for k in ("out", "kp", "vp"):
             assert torch.equal(g_state[k].view(torch.int16), e_state[k].view(torch.int16)), "replay %d: %s" % (i, k)
-        say("graph S=%d replay %d: bit-identical to the eager step" % (num_splits, i))
+        say("graph B=%d S=%d replay %d: bit-identical to the eager step" % (B, num_splits, i))
         lens += 1
         oracle.paged_kv_append(kn, vn, W.newest_row_slots(lens, c.block_tables, c.BS), kp_o, vp_o)
     # the last replay against the oracle on the state it advanced itself
     assert np.array_equal(g_state["cl"].cpu().numpy(), lens)
     ref = oracle.decode_attention(q, kp_o, vp_o, c.block_tables, lens, c.scale)
-    assert_close(g_state["out"].cpu().numpy(), ref, "graph S=%d last replay" % num_splits)
+    assert_close(g_state["out"].cpu().numpy(), ref, "graph B=%d S=%d last replay" % (B, num_splits))
     assert np.array_equal(g_state["kp"].cpu().numpy().view(np.uint16), kp_o.view(np.uint16))
     assert np.array_equal(g_state["vp"].cpu().numpy().view(np.uint16), vp_o.view(np.uint16))
 
