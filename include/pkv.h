@@ -196,7 +196,9 @@ PKV_API int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_p
  *   fits one round of the device's CUs, a single fused launch whose workgroups
  *   write the new rows themselves (the 16-row panel holding a new row is
  *   written back whole, its other rows unchanged); otherwise the append kernel
- *   then attention, in stream order.  Results are identical either way.
+ *   (which also ranks the sequences for the dispatch order described under
+ *   pkv_paged_decode_attention) then attention, in stream order.  Results are
+ *   identical either way.
  *   k_new, v_new: [num_seqs][Hkv][D] fp16, 16-byte aligned.  The block
  *   holding each sequence's newest row must belong to that sequence alone (no
  *   other sequence of the batch may read or write it).  Other arguments,
