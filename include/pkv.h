@@ -321,6 +321,9 @@ PKV_API int pkv_paged_decode_step_window(const uint16_t *q, const uint16_t *k_ne
  *   max_q_len: host upper bound of the new rows of any sequence, used only to
  *     size the grid (0 = total_q_tokens); a smaller value stays correct, the
  *     workgroups then loop.  max_context_hint: as pkv_paged_decode_attention.
+ *   A grid of more workgroups than the device has CUs runs its sequences
+ *   longest first (pos_offsets[s] + new rows), as pkv_paged_decode_attention
+ *   does; results are identical either way.
  *   num_seqs == 0 or total_q_tokens == 0 is a no-op.
  *   Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EHIP.
  * ------------------------------------------------------------------------- */

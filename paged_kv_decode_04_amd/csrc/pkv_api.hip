@@ -699,18 +699,42 @@ int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
         p.k_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
         p.v_dst = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
     }
+    // A grid of more than one round runs its sequences longest first, as in decode (the records live in the
+    // library workspace; skipped where the workspace would have to grow under graph capture).
+    const int64_t grid = (int64_t)num_seqs * tiles_per_seq * pool.num_kv_heads * S;
+    bool order = !fused && num_seqs > 1 && num_seqs <= pkv::kOrderMaxSeqs && grid > facts.cu_count;
+    WsLayout L = ws_layout(total_q, num_q_heads, pool.head_dim, S, order ? (int64_t)num_seqs * pkv::kOrderRecord : 0);
+    if (order && library_workspace_bytes(stream) < L.total) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(stream, &cap);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipStreamIsCapturing");
+        if (cap != hipStreamCaptureStatusNone) {
+            order = false;
+            L = ws_layout(total_q, num_q_heads, pool.head_dim, S);
+        }
+    }
+    void *ws = nullptr;
+    if (S > 1 || order) {
+        rc = library_workspace(L.total, stream, &ws);
+        if (rc)
+            return rc;
+    }
+    char *base = static_cast<char *>(ws);
+    if (order) {
+        int32_t *ord = reinterpret_cast<int32_t *>(base + L.order_off);
+        hipError_t e = pkv::launch_order_varlen(cu_seqlens_q, pos_offsets, block_tables, num_seqs, max_blocks_per_seq,
+                                                max_blocks_per_seq * pool.block_size, ord, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "varlen order kernel launch");
+        p.order = ord;
+    }
     if (S == 1) {
         hipError_t e = pkv::launch_varlen(p, num_seqs, pool.head_dim, pool.block_size, waves, false, stream);
         if (e != hipSuccess)
             return hip_fail(e, "varlen kernel launch");
         return ok();
     }
-    const WsLayout L = ws_layout(total_q, num_q_heads, pool.head_dim, S);
-    void *ws = nullptr;
-    rc = library_workspace(L.total, stream, &ws);
-    if (rc)
-        return rc;
-    char *base = static_cast<char *>(ws);
     p.part_o = reinterpret_cast<float *>(base + L.o_off);
     p.part_m = reinterpret_cast<float *>(base + L.m_off);
     p.part_l = reinterpret_cast<float *>(base + L.l_off);

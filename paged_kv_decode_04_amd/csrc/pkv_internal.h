@@ -72,6 +72,9 @@ struct VarlenParams {
     const _Float16 *v_new;
     _Float16 *k_dst;
     _Float16 *v_dst;
+    // dispatch order (multi-round grids, not with k_new): the sequence of workgroup group t / tiles_per_seq is that
+    // of varlen record order[t / tiles_per_seq] (see launch_order_varlen); null: sequence t / tiles_per_seq
+    const int32_t *order;
 };
 
 struct CombineParams {
@@ -159,6 +162,12 @@ constexpr int kOrderRecBlocks = kOrderRecord - 2;
 // entry i (i < min(M, kOrderRecBlocks)).
 hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables, int B, int M, int cap_rows,
                         int window, int32_t *order, hipStream_t stream);
+// Varlen records: order[rank][0] = sequence, [1] = cu_seqlens_q[s], [2] = cu_seqlens_q[s + 1], [3] = pos_offsets[s],
+// [4 + i] = its table entry i (i < min(M, kVarlenRecBlocks)); ranked by min(pos + new rows, cap_rows), longest
+// first, ties by index.
+constexpr int kVarlenRecBlocks = kOrderRecord - 4;
+hipError_t launch_order_varlen(const int32_t *cu_seqlens_q, const int32_t *pos_offsets, const int32_t *block_tables,
+                               int B, int M, int cap_rows, int32_t *order, hipStream_t stream);
 hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
                                 int num_seqs, hipStream_t stream);
 hipError_t launch_qkv_cache(const QkvParams &p, int head_dim, hipStream_t stream);

@@ -679,7 +679,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 // kFusedUnits units of a sequence's new rows: any kStepFusedRows consecutive rows fit.
 constexpr int kFusedUnits = (kStepFusedRows + 2 * 15) / 16;
 
-template <int D, int BS, int NW, bool SPLIT, int QT, bool FUSED = false>
+template <int D, int BS, int NW, bool SPLIT, int QT, bool FUSED = false, bool ORDERED = false>
 __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
     constexpr int KC = D / 32;
     constexpr int VC = D / 16;
@@ -695,7 +695,16 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
     const int hk = (int)(id % (unsigned)p.Hkv);
     id /= (unsigned)p.Hkv;
     const int slot = (int)(id % (unsigned)p.tiles_per_seq);
-    const int s = (int)(id / (unsigned)p.tiles_per_seq);
+    const int rank = (int)(id / (unsigned)p.tiles_per_seq);
+    // ORDERED (a grid of several rounds): the sequences run longest first, their prefix sums, position and first
+    // block ids read from the order record (see the decode kernel)
+    const int32_t *rec = ORDERED ? p.order + (int64_t)rank * kOrderRecord : nullptr;
+    int s_rec = 0, q0_rec = 0, q1_rec = 0, pos_rec = 0;
+    if (ORDERED) {
+        uniform_load_pair(rec, 0, s_rec, q0_rec);
+        uniform_load_pair(rec, 2, q1_rec, pos_rec);
+    }
+    const int s = ORDERED ? s_rec : rank;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int r = lane & 15;
@@ -706,16 +715,19 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
     const int cap = p.M * BS;  // rows the table can name
     // Every tile's key range starts at row 0 (in split mode with fixed chunks, at split * chunk_blocks), so the
     // block ids of this wave's first units are requested together with the prefix sums and the position.
-    const bool start_known = !SPLIT || p.chunk_blocks > 0;
     const int u_known = (SPLIT ? split * p.chunk_blocks : 0) * SPB + wave;
     constexpr int NSPEC = 2 * NS - 1;
+    const bool start_known = (!SPLIT || p.chunk_blocks > 0) &&
+                             (!ORDERED || (u_known + (NSPEC - 1) * NW) / SPB < kVarlenRecBlocks);
     int spec_raw[NSPEC];
 #pragma unroll
-    for (int j = 0; j < NSPEC; ++j)
-        spec_raw[j] = start_known ? uniform_load(bt, min(u_known + j * NW, max_units - 1) / SPB) : -1;
-    int q0 = uniform_load(p.cu_seqlens_q, s);
-    int q1 = uniform_load(p.cu_seqlens_q, s + 1);
-    int pos = uniform_load(p.pos_offsets, s);
+    for (int j = 0; j < NSPEC; ++j) {
+        const int bi = min(u_known + j * NW, max_units - 1) / SPB;
+        spec_raw[j] = start_known ? (ORDERED ? uniform_load(rec, 4 + bi) : uniform_load(bt, bi)) : -1;
+    }
+    int q0 = ORDERED ? q0_rec : uniform_load(p.cu_seqlens_q, s);
+    int q1 = ORDERED ? q1_rec : uniform_load(p.cu_seqlens_q, s + 1);
+    int pos = ORDERED ? pos_rec : uniform_load(p.pos_offsets, s);
     static_assert(NSPEC <= 3, "the barrier below names at most three block ids");
     asm volatile("" ::"s"(q0), "s"(q1), "s"(pos), "s"(spec_raw[0]), "s"(spec_raw[NSPEC > 1 ? 1 : 0]),
                  "s"(spec_raw[NSPEC > 2 ? 2 : 0])
@@ -1094,7 +1106,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // panels holding the row whole -- each thread one 16-byte chunk: read, replace the row's part, write back -- so the
 // pools see only full-line writes (scattered 2- and 16-byte row stores cost far more at the memory than their
 // bytes).  Valid only because the block holding a sequence's newest row belongs to that sequence alone.
-__device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ lens,
+template <bool VARLEN>
+__device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ lens, const int32_t *__restrict__ cu,
+                                                  const int32_t *__restrict__ pos,
                                                   const int32_t *__restrict__ block_tables, int B, int M, int cap_rows,
                                                   int window, int32_t *__restrict__ order, int group, int *keys);
 
@@ -1103,8 +1117,8 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
 __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
     if (p.order != nullptr && blockIdx.x >= (unsigned)(p.T * p.Hkv)) {
         extern __shared__ int keys[];
-        rank_into_records(p.context_lens, p.block_tables, p.T, p.M, p.order_cap, p.order_window, p.order,
-                          (int)(blockIdx.x - (unsigned)(p.T * p.Hkv)), keys);
+        rank_into_records<false>(p.context_lens, nullptr, nullptr, p.block_tables, p.T, p.M, p.order_cap,
+                                 p.order_window, p.order, (int)(blockIdx.x - (unsigned)(p.T * p.Hkv)), keys);
         return;
     }
     const int s = (int)(blockIdx.x / (unsigned)p.Hkv);
@@ -1189,24 +1203,38 @@ __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, cons
 // four lanes per sequence, each lane scanning a quarter of the keys 16 bytes at a time; the quad sums its counts.
 constexpr int kOrderSeqsPerGroup = 64;
 // One workgroup's share (sequences group * 64 ..) of the ranking; keys: LDS for all B keys, rounded up to 4.
-__device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ lens,
+// Decode (VARLEN false): key = rows attended, min(clamp(L, 0, cap_rows), window) with window > 0; record = sequence,
+// context_lens[s], then its first kOrderRecBlocks table entries.  Varlen: key = clamp(pos[s] + new rows, 0,
+// cap_rows), the rows its last new row attends; record = sequence, cu[s], cu[s + 1], pos[s], then its first
+// kVarlenRecBlocks table entries.
+template <bool VARLEN>
+__device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ lens, const int32_t *__restrict__ cu,
+                                                  const int32_t *__restrict__ pos,
                                                   const int32_t *__restrict__ block_tables, int B, int M, int cap_rows,
                                                   int window, int32_t *__restrict__ order, int group, int *keys) {
+    constexpr int kHead = VARLEN ? 4 : 2;
+    constexpr int kBlocks = kOrderRecord - kHead;
     const int B4 = (B + 3) / 4;
     for (int i = threadIdx.x; i < 4 * B4; i += 256) {
         int key = -1;
         if (i < B) {
-            int L = lens[i];
-            L = L < 0 ? 0 : (L > cap_rows ? cap_rows : L);
-            key = window > 0 && L > window ? window : L;
+            if (VARLEN) {
+                const int64_t n = (int64_t)cu[i + 1] - cu[i];
+                const int64_t rows = (int64_t)pos[i] + (n > 0 ? n : 0);
+                key = rows < 0 ? 0 : (rows > cap_rows ? cap_rows : (int)rows);
+            } else {
+                int L = lens[i];
+                L = L < 0 ? 0 : (L > cap_rows ? cap_rows : L);
+                key = window > 0 && L > window ? window : L;
+            }
         }
         keys[i] = key;
     }
     const int s = group * kOrderSeqsPerGroup + (int)(threadIdx.x >> 2);
     const int part = (int)(threadIdx.x & 3);
     // this lane's share of the record's table entries (i = part, part + 4, ...), requested before the scan
-    const int nb = M < kOrderRecBlocks ? M : kOrderRecBlocks;
-    constexpr int kPer = (kOrderRecBlocks + 3) / 4;
+    const int nb = M < kBlocks ? M : kBlocks;
+    constexpr int kPer = (kBlocks + 3) / 4;
     int ids[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -1233,13 +1261,19 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
     int32_t *rec = order + (int64_t)rank * kOrderRecord;
     if (part == 0) {
         rec[0] = s;
-        rec[1] = lens[s];
+        if (VARLEN) {
+            rec[1] = cu[s];
+            rec[2] = cu[s + 1];
+            rec[3] = pos[s];
+        } else {
+            rec[1] = lens[s];
+        }
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int i = part + 4 * k;
         if (i < nb)
-            rec[2 + i] = ids[k];
+            rec[kHead + i] = ids[k];
     }
 }
 
@@ -1247,7 +1281,16 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t *__restrict__ 
                                                     const int32_t *__restrict__ block_tables, int B, int M,
                                                     int cap_rows, int window, int32_t *__restrict__ order) {
     extern __shared__ int keys[];
-    rank_into_records(lens, block_tables, B, M, cap_rows, window, order, (int)blockIdx.x, keys);
+    rank_into_records<false>(lens, nullptr, nullptr, block_tables, B, M, cap_rows, window, order, (int)blockIdx.x,
+                             keys);
+}
+
+__global__ __launch_bounds__(256) void order_varlen_kernel(const int32_t *__restrict__ cu,
+                                                           const int32_t *__restrict__ pos,
+                                                           const int32_t *__restrict__ block_tables, int B, int M,
+                                                           int cap_rows, int32_t *__restrict__ order) {
+    extern __shared__ int keys[];
+    rank_into_records<true>(nullptr, cu, pos, block_tables, B, M, cap_rows, 0, order, (int)blockIdx.x, keys);
 }
 
 // ---------------------------------------------------------------------------
@@ -1349,6 +1392,16 @@ static hipError_t launch_varlen_t(const VarlenParams &p, int num_seqs, bool spli
             return hipErrorInvalidValue;
     } else if (fused)
         hipLaunchKernelGGL((varlen_kernel<D, BS, NW, false, 1, true>), grid, block, lds, stream, p);
+    else if (p.order != nullptr) {  // a multi-round grid in dispatch order
+        if (split && p.QT == 2)
+            hipLaunchKernelGGL((varlen_kernel<D, BS, NW, true, 2, false, true>), grid, block, lds, stream, p);
+        else if (split)
+            hipLaunchKernelGGL((varlen_kernel<D, BS, NW, true, 1, false, true>), grid, block, lds, stream, p);
+        else if (p.QT == 2)
+            hipLaunchKernelGGL((varlen_kernel<D, BS, NW, false, 2, false, true>), grid, block, lds, stream, p);
+        else
+            hipLaunchKernelGGL((varlen_kernel<D, BS, NW, false, 1, false, true>), grid, block, lds, stream, p);
+    }
     else if (split && p.QT == 2)
         hipLaunchKernelGGL((varlen_kernel<D, BS, NW, true, 2>), grid, block, lds, stream, p);
     else if (split)
@@ -1435,6 +1488,16 @@ hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables
     hipLaunchKernelGGL(order_kernel, dim3((unsigned)((B + kOrderSeqsPerGroup - 1) / kOrderSeqsPerGroup)), dim3(256),
                        sizeof(int) * (size_t)((B + 3) / 4 * 4), stream, context_lens, block_tables, B, M, cap_rows,
                        window, order);
+    return hipGetLastError();
+}
+
+hipError_t launch_order_varlen(const int32_t *cu_seqlens_q, const int32_t *pos_offsets, const int32_t *block_tables,
+                               int B, int M, int cap_rows, int32_t *order, hipStream_t stream) {
+    if (B <= 0 || B > kOrderMaxSeqs)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(order_varlen_kernel, dim3((unsigned)((B + kOrderSeqsPerGroup - 1) / kOrderSeqsPerGroup)),
+                       dim3(256), sizeof(int) * (size_t)((B + 3) / 4 * 4), stream, cu_seqlens_q, pos_offsets,
+                       block_tables, B, M, cap_rows, order);
     return hipGetLastError();
 }
 
