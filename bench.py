@@ -53,6 +53,8 @@ WORKLOADS = {
            "per sequence, final L~U[512,2048]", 0, 4),
     "v2": ("speculative verification of 8 draft tokens, varlen (Llama-3-8B-shaped batch): B=32, Hq=32, Hkv=8, D=128, "
            "BS=16, 8 new rows per sequence, final L~U[512,2048]", 0, 4),
+    "v3": ("speculative verification on the mixed serving batch: B=256, Hq=64, Hkv=8, D=128, BS=16, 4 new rows per "
+           "sequence, final L lognormal (median 1024, sigma 1) clipped to [4,16384]", 0, 1),
     "w1": ("sliding-window decode on the Llama-3-8B-shaped batch: B=32, Hq=32, Hkv=8, D=128, BS=16, L~U[512,2048], "
            "window 512", 0, 8),
     "r1": ("Qwen3-8B-shaped decode step from the QKV projection: split QKV + q/k RMSNorm + RoPE + paged-cache write, "
@@ -158,7 +160,7 @@ def dominant_kernels(config: str, names) -> list:
     if step:
         return step
     return [n for n, (base, fused, _) in kinds.items()
-            if (base in ("decode_kernel", "varlen_kernel") and not fused) or base in ("combine_kernel", "order_kernel")]
+            if (base in ("decode_kernel", "varlen_kernel") and not fused) or base in ("combine_kernel", "order_kernel", "order_varlen_kernel")]
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy_mib: float) -> dict:

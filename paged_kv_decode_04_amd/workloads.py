@@ -418,7 +418,23 @@ def config_v2(rotation: int = 0) -> VarlenCase:
                              extra_blocks=int(math.ceil(0.10 * nblocks)), M=128)
 
 
-VARLEN_CONFIGS = {"v1": config_v1, "v2": config_v2}
+SEEDS["v3"] = 0xC0FFEE13
+
+
+def config_v3(rotation: int = 0) -> VarlenCase:
+    """Speculative verification on the mixed serving batch: B=256, 64/8 heads, D=128, BS=16, 4 new rows per
+    sequence whose final lengths are drawn as c4's (lognormal, median 1024, sigma 1, clipped to [4, 16384]), pool =
+    blocks + 10% (2048 workgroups: several rounds of the CUs)."""
+    seed = SEEDS["v3"]
+    raw = _rng(seed, rotation, "lens").lognormal(mean=math.log(1024.0), sigma=1.0, size=256)
+    final = np.clip(np.rint(raw), 4, 16384).astype(np.int32)
+    ql = np.full(256, 4, dtype=np.int32)
+    nblocks = int(sum((int(L) + 15) // 16 for L in final))
+    return build_varlen_case("v3", 256, 64, 8, 128, 16, ql, final - ql, seed, rotation,
+                             extra_blocks=int(math.ceil(0.10 * nblocks)))
+
+
+VARLEN_CONFIGS = {"v1": config_v1, "v2": config_v2, "v3": config_v3}
 
 
 def algorithmic_bytes_varlen(case: VarlenCase) -> dict:

@@ -43,6 +43,9 @@ def test_dominant_kernels_follow_the_step_shape():
     rounds = ["pkv::append_newest_kernel", "pkv::order_kernel",
               "pkv::decode_kernel<128, 16, 8, false, false, false, true>", "pkv::append_kernel"]
     assert sorted(bench.dominant_kernels("c4", rounds)) == sorted(rounds[1:3])
+    varlen = ["pkv::append_varlen_kernel", "pkv::order_varlen_kernel",
+              "pkv::varlen_kernel<128, 16, 8, false, 2, false, true>", "pkv::append_kernel"]
+    assert sorted(bench.dominant_kernels("v3", varlen)) == sorted(varlen[1:3])
     assert bench.dominant_kernels("r2", ["pkv::qkv_cache_kernel<128>"]) == ["pkv::qkv_cache_kernel<128>"]
 
 

@@ -103,10 +103,11 @@ def test_varlen_step_rows_of_a_missing_block_are_not_written(torch_cuda):
     assert_close(out[:4], ref0, "missing block: the intact sequence")
 
 
-@pytest.mark.parametrize("name", ["v1", "v2"])
+@pytest.mark.parametrize("name", ["v1", "v2", "v3"])
 def test_varlen_step_full_size(torch_cuda, name):
-    """The step on the bench's v1 / v2 workloads (32 sequences, 4 or 8 new rows each, one launch): pools bit-exact
-    and 256 sampled (token, head) rows against the oracle."""
+    """The step on the bench's v1 / v2 workloads (32 sequences, 4 or 8 new rows each, one launch) and v3 (256
+    sequences of mixed lengths, 2048 workgroups: the append launch, the dispatch order, then attention longest first):
+    pools bit-exact and 256 sampled (token, head) rows against the oracle."""
     c = W.VARLEN_CONFIGS[name]()
     say("varlen step %s full size" % name)
     out, kp, vp = _step(torch_cuda, c, 0, int(c.q_lens.max()))
