@@ -285,6 +285,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration-mib", type=float, default=0.0,
                     help="also run a plain copy kernel over this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--pmc-steps", type=int, nargs=2, default=(50, 10), metavar=("STEPS", "WARMUP"),
+                    help="with --summarize-pmc: the --steps/--warmup of the counter runs, for the recorded commands")
     ap.add_argument("--unfused", action="store_true",
                     help="append and attention as two launches instead of the library's step entry point")
     ap.add_argument("--graph", action="store_true",
@@ -300,11 +302,13 @@ def main(argv=None) -> int:
         fetch_csv, write_csv = args.summarize_pmc
         rec["commands"] = [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o %s -- python3 bench.py --config %s "
-            "--steps 50 --warmup 10 --no-cpu-baseline --copy-calibration-mib %g%s"
-            % (os.path.dirname(fetch_csv), args.config, args.config, rec["copy_calibration_mib"], extra),
+            "--steps %d --warmup %d --no-cpu-baseline --copy-calibration-mib %g%s"
+            % (os.path.dirname(fetch_csv), args.config, args.config, args.pmc_steps[0], args.pmc_steps[1],
+               rec["copy_calibration_mib"], extra),
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o %s -- python3 bench.py --config %s "
-            "--steps 50 --warmup 10 --no-cpu-baseline --copy-calibration-mib %g%s"
-            % (os.path.dirname(write_csv), args.config, args.config, rec["copy_calibration_mib"], extra),
+            "--steps %d --warmup %d --no-cpu-baseline --copy-calibration-mib %g%s"
+            % (os.path.dirname(write_csv), args.config, args.config, args.pmc_steps[0], args.pmc_steps[1],
+               rec["copy_calibration_mib"], extra),
             "python bench.py --summarize-pmc %s %s --config %s%s" % (fetch_csv, write_csv, args.config, extra),
         ]
         path = traffic_path(args.config, splits, step_is_fused(args.config, args.unfused))

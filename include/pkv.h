@@ -347,12 +347,14 @@ PKV_API int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool
  *   Launches: one pass with max_q_len <= 32 and no more workgroups than the
  *   device's CUs gives one launch whose workgroups write the new rows
  *   themselves (each 16-row panel holding new rows is written back whole,
- *   its other rows unchanged); otherwise a launch writes the new rows, then
- *   attention runs.  Results are identical either way.
+ *   its other rows unchanged); otherwise a launch writes the new rows (also
+ *   as whole panels, and with a grid of more workgroups than CUs it ranks
+ *   the sequences for the attention launch's dispatch order), then attention
+ *   runs.  Results are identical either way.
  *   k_new, v_new: [total_q_tokens][Hkv][D] fp16, 16-byte aligned.
  *   max_q_len (required, >= 1): no sequence may have more new rows; it picks
- *   the launches (a sequence with more leaves its rows past the 32nd
- *   unspecified in the one-launch form; memory stays safe).  The blocks that
+ *   the launches and sizes the append (a sequence with more leaves its rows
+ *   past the first max_q_len unspecified; memory stays safe).  The blocks that
  *   receive a sequence's new rows must belong to that sequence alone during
  *   the call.  Other arguments and errors as pkv_paged_varlen_attention.
  * ------------------------------------------------------------------------- */

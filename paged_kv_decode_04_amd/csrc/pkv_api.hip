@@ -652,26 +652,6 @@ int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     if (pkv::varlen_lds_bytes(pool.head_dim, waves, fused) > limit)
         return fail(PKV_EUNSUPPORTED, "varlen needs %zu LDS bytes, the device allows %zu",
                     pkv::varlen_lds_bytes(pool.head_dim, waves, fused), limit);
-    if (step && !fused) {
-        // the new rows' own launch, then attention over the updated pools
-        pkv::AppendParams a;
-        memset(&a, 0, sizeof a);
-        a.k = reinterpret_cast<const _Float16 *>(k_new);
-        a.v = reinterpret_cast<const _Float16 *>(v_new);
-        a.block_tables = block_tables;
-        a.k_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
-        a.v_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
-        a.T = total_q;
-        a.Hkv = pool.num_kv_heads;
-        a.D = pool.head_dim;
-        a.BS = pool.block_size;
-        a.N = pool.num_blocks;
-        a.M = max_blocks_per_seq;
-        hipError_t e = pkv::launch_append_varlen(a, cu_seqlens_q, pos_offsets, num_seqs, stream);
-        if (e != hipSuccess)
-            return hip_fail(e, "varlen append kernel launch");
-    }
-
     pkv::VarlenParams p;
     memset(&p, 0, sizeof p);
     p.q = reinterpret_cast<const _Float16 *>(q);
@@ -721,14 +701,34 @@ int varlen_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
             return rc;
     }
     char *base = static_cast<char *>(ws);
-    if (order) {
-        int32_t *ord = reinterpret_cast<int32_t *>(base + L.order_off);
+    int32_t *ord = order ? reinterpret_cast<int32_t *>(base + L.order_off) : nullptr;
+    if (step && !fused) {
+        // the new rows' own launch (which also writes the order records), then attention over the updated pools
+        pkv::AppendParams a;
+        memset(&a, 0, sizeof a);
+        a.k = reinterpret_cast<const _Float16 *>(k_new);
+        a.v = reinterpret_cast<const _Float16 *>(v_new);
+        a.block_tables = block_tables;
+        a.k_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(k_pool));
+        a.v_pool = reinterpret_cast<_Float16 *>(const_cast<uint16_t *>(v_pool));
+        a.T = total_q;
+        a.Hkv = pool.num_kv_heads;
+        a.D = pool.head_dim;
+        a.BS = pool.block_size;
+        a.N = pool.num_blocks;
+        a.M = max_blocks_per_seq;
+        a.order = ord;
+        a.order_cap = max_blocks_per_seq * pool.block_size;
+        hipError_t e = pkv::launch_append_varlen(a, cu_seqlens_q, pos_offsets, num_seqs, (int)qmax, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "varlen append kernel launch");
+    } else if (order) {
         hipError_t e = pkv::launch_order_varlen(cu_seqlens_q, pos_offsets, block_tables, num_seqs, max_blocks_per_seq,
                                                 max_blocks_per_seq * pool.block_size, ord, stream);
         if (e != hipSuccess)
             return hip_fail(e, "varlen order kernel launch");
-        p.order = ord;
     }
+    p.order = ord;
     if (S == 1) {
         hipError_t e = pkv::launch_varlen(p, num_seqs, pool.head_dim, pool.block_size, waves, false, stream);
         if (e != hipSuccess)

@@ -97,8 +97,9 @@ struct AppendParams {
     _Float16 *k_pool;
     _Float16 *v_pool;
     int32_t T, Hkv, D, BS, N, M;
-    // launch_append_newest only: when order is non-null, extra workgroups also write the dispatch-order records of
-    // the T sequences (as launch_order, rows capped at order_cap, window order_window)
+    // launch_append_newest and launch_append_varlen: when order is non-null, the launch also writes the
+    // dispatch-order records of the sequences (as launch_order / launch_order_varlen, rows capped at order_cap,
+    // window order_window for decode)
     int32_t *order;
     int32_t order_cap, order_window;
 };
@@ -153,6 +154,8 @@ hipError_t launch_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream);
 // Sequences that a multi-round decode grid can order longest first.
 constexpr int kOrderMaxSeqs = 16384;
+// Largest one-dimensional grid of 256-thread workgroups (a launch's threads along x must fit in 32 bits).
+constexpr int64_t kMaxGroups = 0xFFFFFFFFll / 256;
 // One record per rank of the dispatch order: the sequence, its length as stored, then its first kOrderRecBlocks
 // block-table entries -- everything a decode workgroup reads before its first K/V loads, in one place.
 constexpr int kOrderRecord = 32;
@@ -168,8 +171,12 @@ hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables
 constexpr int kVarlenRecBlocks = kOrderRecord - 4;
 hipError_t launch_order_varlen(const int32_t *cu_seqlens_q, const int32_t *pos_offsets, const int32_t *block_tables,
                                int B, int M, int cap_rows, int32_t *order, hipStream_t stream);
+// The varlen step's new rows (token t of sequence s to row pos[s] + t - cu[s]): whole-panel rewrites, one workgroup
+// per (sequence, kv head, 16-row unit the sequence's first max_q_len new rows can touch); a grid past kMaxGroups
+// takes the per-row form.  With p.order set (order_cap = M * BS) the same call also writes the varlen dispatch-order
+// records (see launch_order_varlen): in extra workgroups of the panel launch, else in an order launch of its own.
 hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
-                                int num_seqs, hipStream_t stream);
+                                int num_seqs, int max_q_len, hipStream_t stream);
 hipError_t launch_qkv_cache(const QkvParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_check(const CheckParams &p, hipStream_t stream);
 

@@ -1101,17 +1101,18 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         vdst[e * 16] = vh[e];
 }
 
-// The decode step's append as its own launch: the new row of sequence s (block bt[s][(L-1)/BS], row (L-1)%BS, as
-// the fused step places it) for every kv head.  One workgroup per (sequence, kv head) rewrites the two 16-row
-// panels holding the row whole -- each thread one 16-byte chunk: read, replace the row's part, write back -- so the
-// pools see only full-line writes (scattered 2- and 16-byte row stores cost far more at the memory than their
-// bytes).  Valid only because the block holding a sequence's newest row belongs to that sequence alone.
+constexpr int kOrderSeqsPerGroup = 64;  // sequences one order workgroup ranks
 template <bool VARLEN>
 __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ lens, const int32_t *__restrict__ cu,
                                                   const int32_t *__restrict__ pos,
                                                   const int32_t *__restrict__ block_tables, int B, int M, int cap_rows,
                                                   int window, int32_t *__restrict__ order, int group, int *keys);
 
+// The decode step's append as its own launch: the new row of sequence s (block bt[s][(L-1)/BS], row (L-1)%BS, as
+// the fused step places it) for every kv head.  One workgroup per (sequence, kv head) rewrites the two 16-row
+// panels holding the row whole -- each thread one 16-byte chunk: read, replace the row's part, write back -- so the
+// pools see only full-line writes (scattered 2- and 16-byte row stores cost far more at the memory than their
+// bytes).  Valid only because the block holding a sequence's newest row belongs to that sequence alone.
 // With p.order set, the workgroups past the T * Hkv appends write the dispatch-order records instead (the ranking
 // of launch_order, in the same launch as the append).
 __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
@@ -1197,11 +1198,95 @@ __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, cons
         vdst[e * 16] = vh[e];
 }
 
+// The varlen step's append in whole panels: workgroup (s, h, j) takes the j-th 16-row unit that sequence s's new
+// rows touch (rows pos[s] .. pos[s] + n - 1, n = cu[s+1] - cu[s], clipped to 0 .. M*BS - 1), stages those rows of kv
+// head h in LDS and rewrites the unit's K and V panels whole, new rows from LDS and the others as read, so the pools
+// see full-line writes only (as append_newest_kernel; the per-row form above scatters 2-byte V stores).  Valid only
+// because the blocks receiving a sequence's new rows belong to that sequence alone.  units: unit slots per sequence,
+// enough for max_q_len rows from any offset in a unit; rows past them are not written.  With p.order set, the
+// workgroups past num_seqs * Hkv * units write the varlen dispatch-order records instead (as order_varlen_kernel;
+// placed first in the grid, they made the attention launch that follows slower, c4-shaped decode by 13 us).  Head
+// dim at most 256 (two 16-byte chunks of each panel per thread).  Dynamic LDS: max(2 * 16 * D halves, the keys).
+__global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams p, const int32_t *cu,
+                                                                   const int32_t *pos, int num_seqs, int units) {
+    extern __shared__ __align__(16) unsigned char panel_lds[];
+    const unsigned per_seq = (unsigned)p.Hkv * (unsigned)units;
+    const unsigned appends = (unsigned)num_seqs * per_seq;
+    if (blockIdx.x >= appends) {
+        rank_into_records<true>(nullptr, cu, pos, p.block_tables, num_seqs, p.M, p.order_cap, 0, p.order,
+                                (int)(blockIdx.x - appends), reinterpret_cast<int *>(panel_lds));
+        return;
+    }
+    const int s = (int)(blockIdx.x / per_seq);
+    const int rem = (int)(blockIdx.x - (unsigned)s * per_seq);
+    const int h = rem / units;
+    const int j = rem - h * units;
+    const int64_t first = pos[s];
+    const int64_t cap = (int64_t)p.M * p.BS;
+    const int64_t lo = first < 0 ? 0 : first;
+    int64_t hi = first + ((int64_t)cu[s + 1] - cu[s]);
+    hi = hi > cap ? cap : hi;
+    const int64_t r0 = (lo / 16 + j) * 16;  // this workgroup's unit: rows r0 .. r0 + 15 of the sequence
+    if (lo >= hi || r0 >= hi)
+        return;
+    const int b = p.block_tables[(int64_t)s * p.M + r0 / p.BS];
+    if (b < 0 || b >= p.N)
+        return;
+    const int a = (int)((lo > r0 ? lo : r0) - r0);         // new rows of the unit: a .. e - 1
+    const int e = (int)((hi < r0 + 16 ? hi : r0 + 16) - r0);
+    const int64_t panel = ((int64_t)b * p.Hkv + h) * p.BS * p.D + (r0 % p.BS) * p.D;
+    // The panels' chunks that keep old rows, read before the staging so both sets of loads are in flight together.
+    // K panel [D/8][16][8]: chunk q is piece q/16 of row q%16.  V panel [D][16]: chunk q is dim q/2, rows 8*(q%2)..+8.
+    f16x8 kc[2] = {}, vc[2] = {};
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int q = (int)threadIdx.x + 256 * it;
+        if (q < 2 * p.D) {
+            const int kr = q % 16;
+            if (kr < a || kr >= e)
+                kc[it] = *reinterpret_cast<const f16x8 *>(p.k_pool + panel + 8 * q);
+            const int vr = 8 * (q & 1);
+            if (vr < a || vr + 8 > e)
+                vc[it] = *reinterpret_cast<const f16x8 *>(p.v_pool + panel + 8 * q);
+        }
+    }
+    const int pieces = p.D / 8;
+    f16x8 *kst = reinterpret_cast<f16x8 *>(panel_lds);  // [16][D/8]
+    f16x8 *vst = kst + 16 * pieces;                      // [16][D/8]
+    const int64_t t0 = (int64_t)cu[s] + (r0 - first);  // token of unit row r (used for a <= r < e only)
+    for (int i = threadIdx.x; i < 16 * pieces; i += 256) {
+        const int r = i / pieces;
+        if (r >= a && r < e && t0 + r < p.T) {  // (t0 + r >= cu[s] >= 0; the bound holds for valid prefix sums)
+            const int64_t src = ((t0 + r) * p.Hkv + h) * p.D + 8 * (i - r * pieces);
+            kst[i] = *reinterpret_cast<const f16x8 *>(p.k + src);
+            vst[i] = *reinterpret_cast<const f16x8 *>(p.v + src);
+        }
+    }
+    __syncthreads();
+    const _Float16 *vsh = reinterpret_cast<const _Float16 *>(vst);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int q = (int)threadIdx.x + 256 * it;
+        if (q < 2 * p.D) {
+            const int kr = q % 16;
+            if (kr >= a && kr < e)
+                kc[it] = kst[kr * pieces + q / 16];
+            *reinterpret_cast<f16x8 *>(p.k_pool + panel + 8 * q) = kc[it];
+            const int vr = 8 * (q & 1);
+            const int dim = q / 2;
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+                if (vr + x >= a && vr + x < e)
+                    vc[it][x] = vsh[(vr + x) * p.D + dim];
+            *reinterpret_cast<f16x8 *>(p.v_pool + panel + 8 * q) = vc[it];
+        }
+    }
+}
+
 // Dispatch order for a multi-round decode grid: each sequence is ranked against every other by the rows it attends
 // (descending, ties by index), so the ranks are a permutation, and its record is written at its rank.  Every
 // workgroup holds all B keys in LDS (padded to a multiple of 4 with -1, which never counts) and ranks 64 sequences,
 // four lanes per sequence, each lane scanning a quarter of the keys 16 bytes at a time; the quad sums its counts.
-constexpr int kOrderSeqsPerGroup = 64;
 // One workgroup's share (sequences group * 64 ..) of the ranking; keys: LDS for all B keys, rounded up to 4.
 // Decode (VARLEN false): key = rows attended, min(clamp(L, 0, cap_rows), window) with window > 0; record = sequence,
 // context_lens[s], then its first kOrderRecBlocks table entries.  Varlen: key = clamp(pos[s] + new rows, 0,
@@ -1472,13 +1557,35 @@ hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens_q, const int32_t *pos_offsets,
-                                int num_seqs, hipStream_t stream) {
-    if (p.T <= 0 || num_seqs <= 0)
+                                int num_seqs, int max_q_len, hipStream_t stream) {
+    if (num_seqs <= 0)
         return hipSuccess;
-    const int64_t total = (int64_t)p.T * p.Hkv * (p.D / 8);
-    hipLaunchKernelGGL(append_varlen_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p,
-                       cu_seqlens_q, pos_offsets, num_seqs);
-    return hipGetLastError();
+    if (p.order != nullptr && num_seqs > kOrderMaxSeqs)
+        return hipErrorInvalidValue;
+    const unsigned order_groups =
+        p.order ? (unsigned)((num_seqs + kOrderSeqsPerGroup - 1) / kOrderSeqsPerGroup) : 0u;
+    // unit slots for max_q_len rows starting anywhere in a 16-row unit
+    const int64_t units = max_q_len > 0 ? ((int64_t)max_q_len + 14) / 16 + 1 : 0;
+    const int64_t panels = (int64_t)num_seqs * p.Hkv * units;
+    if (units > 0 && p.T > 0 && p.D <= 256 && panels + order_groups <= kMaxGroups) {
+        const size_t stage = sizeof(_Float16) * 2 * 16 * (size_t)p.D;
+        const size_t keys = p.order ? sizeof(int) * (size_t)((num_seqs + 3) / 4 * 4) : 0;
+        hipLaunchKernelGGL(append_varlen_panels_kernel, dim3((unsigned)panels + order_groups), dim3(256),
+                           stage > keys ? stage : keys, stream, p, cu_seqlens_q, pos_offsets, num_seqs, (int)units);
+        return hipGetLastError();
+    }
+    if (p.T > 0) {
+        const int64_t total = (int64_t)p.T * p.Hkv * (p.D / 8);
+        hipLaunchKernelGGL(append_varlen_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p,
+                           cu_seqlens_q, pos_offsets, num_seqs);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    if (p.order == nullptr)
+        return hipSuccess;
+    return launch_order_varlen(cu_seqlens_q, pos_offsets, p.block_tables, num_seqs, p.M, p.order_cap, p.order,
+                               stream);
 }
 
 hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables, int B, int M, int cap_rows,

@@ -119,3 +119,16 @@ def test_varlen_step_full_size(torch_cuda, name):
     units[:3] = [[0, 0], [c.T - 1, c.Hq - 1], [7, 5]]
     ref = oracle.varlen_attention(c.q, rk, rv, c.block_tables, c.cu_seqlens_q, c.pos_offsets, c.scale, units=units)
     assert_close(out[units[:, 0], units[:, 1]], ref, "%s step" % name)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2])
+def test_varlen_step_with_a_loose_max_q_len(torch_cuda, num_splits):
+    """max_q_len far above every sequence's new rows (40 against at most 5, the append launch then has idle unit
+    slots; rows spanning two 16-row units and a block boundary): pools bit-exact, output against the oracle."""
+    c = W.build_varlen_case("step", 5, 16, 4, 64, 32, (5, 0, 3, 4, 1), (14, 9, 30, 0, 63), 1381)
+    what = "loose max_q_len S=%d" % num_splits
+    say(what)
+    out, kp, vp = _step(torch_cuda, c, num_splits, 40)
+    rk, rv, ref = _reference(c)
+    _assert_pools(kp, vp, rk, rv, what)
+    assert_close(out, ref, what)
