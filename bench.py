@@ -319,7 +319,7 @@ def main(argv=None) -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the decode-attention hot path has no cross-GPU "
+        print("bench.py measures one GPU only (the decode-attention hot path has no cross-GPU "
               "exchange); run with --gpus 1", file=sys.stderr)
         return 2
 
