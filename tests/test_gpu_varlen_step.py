@@ -75,16 +75,26 @@ def test_varlen_step_matches_oracle(torch_cuda, geom, num_splits):
     assert np.array_equal(out.view(np.uint16), two.view(np.uint16)), "%s: differs from append + attention" % what
 
 
-def test_varlen_step_grid_past_the_cus_takes_two_launches(torch_cuda):
-    # 40 sequences x 8 kv heads = 320 workgroups: the append launch, then attention
-    rng = np.random.default_rng(1351)
-    ql = rng.integers(0, 6, 40)
-    po = rng.integers(0, 300, 40)
-    c = W.build_varlen_case("step", 40, 32, 8, 128, 16, ql, po, 1352)
+@pytest.mark.parametrize("geom", [(40, 32, 8, 128, 16, 6), (40, 16, 16, 256, 32, 3), (160, 8, 2, 64, 64, 21)],
+                         ids=lambda g: "B%d_Hq%d_Hkv%d_D%d_BS%d_q%d" % g)
+def test_varlen_step_grid_past_the_cus_takes_two_launches(torch_cuda, geom):
+    """More workgroups than CUs: the append launch (whole panels, its extra workgroups writing the dispatch-order
+    records), then attention longest first.  Pools bit-exact, output against the oracle and bit-identical to the
+    slot-mapping append followed by varlen attention (whose order comes from a launch of its own)."""
+    B, Hq, Hkv, D, BS, qmax = geom
+    rng = np.random.default_rng(1351 + B + D)
+    ql = rng.integers(0, qmax, B)
+    ql[0] = qmax - 1
+    po = rng.integers(0, 300, B)
+    c = W.build_varlen_case("step", B, Hq, Hkv, D, BS, ql, po, 1352 + D)
+    what = "step %s" % (geom,)
+    say(what)
     out, kp, vp = _step(torch_cuda, c, 0, int(ql.max()))
     rk, rv, ref = _reference(c)
-    _assert_pools(kp, vp, rk, rv, "step B=40")
-    assert_close(out, ref, "step B=40")
+    _assert_pools(kp, vp, rk, rv, what)
+    assert_close(out, ref, what)
+    two = _two_calls(torch_cuda, c, 0, int(ql.max()))
+    assert np.array_equal(out.view(np.uint16), two.view(np.uint16)), "%s: differs from append + attention" % what
 
 
 def test_varlen_step_rows_of_a_missing_block_are_not_written(torch_cuda):
