@@ -8,7 +8,8 @@ it does not know the feature, which is harmless.  After linking, the gfx950
 assembly of the kernels is generated once more and searched for packed-FP32
 arithmetic (v_pk_add_f32 / v_pk_mul_f32 / v_pk_fma_f32), and the kernel
 metadata for private (scratch) segments: the build fails if packed-FP32
-arithmetic appears or if any kernel spills registers to scratch memory.
+arithmetic appears or if any kernel spills registers to scratch memory.  The
+objects and the assembly are compiled concurrently, then the objects linked.
 """
 from __future__ import annotations
 
@@ -17,6 +18,7 @@ import re
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -43,37 +45,60 @@ def _run(cmd):
     return out
 
 
+def _check_asm(src: str, tmp: str) -> None:
+    """Compile one source to gfx950 assembly and fail on packed-FP32 arithmetic or scratch use."""
+    asm = os.path.join(tmp, src + ".s")
+    _run([HIPCC] + COMMON + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
+    with open(asm) as f:
+        text = f.read()
+    hits = sorted(set(m.group(0) for m in _PACKED_F32.finditer(text)))
+    if hits:
+        raise RuntimeError("packed-FP32 instructions in %s: %s" % (src, ", ".join(hits)))
+    spills, name = [], None
+    for m in _KERNEL_META.finditer(text):  # each kernel's .name precedes its segment size
+        if m.group(1) is not None:
+            name = m.group(1)
+        elif name is not None:
+            if int(m.group(2)):
+                spills.append("%s (%s B)" % (name, m.group(2)))
+            name = None
+    if spills:
+        raise RuntimeError("kernels using scratch memory in %s: %s" % (src, ", ".join(spills)))
+
+
+def _jobs() -> int:
+    try:
+        n = int(os.environ.get("MAX_JOBS", "0"))
+    except ValueError:
+        n = 0
+    return max(1, min(n or (os.cpu_count() or 1), 2 * len(SOURCES)))
+
+
 def check_no_packed_fp32() -> None:
-    with tempfile.TemporaryDirectory() as tmp:
-        for src in SOURCES:
-            asm = os.path.join(tmp, src + ".s")
-            _run([HIPCC] + COMMON + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
-            with open(asm) as f:
-                text = f.read()
-            hits = sorted(set(m.group(0) for m in _PACKED_F32.finditer(text)))
-            if hits:
-                raise RuntimeError("packed-FP32 instructions in %s: %s" % (src, ", ".join(hits)))
-            spills, name = [], None
-            for m in _KERNEL_META.finditer(text):  # each kernel's .name precedes its segment size
-                if m.group(1) is not None:
-                    name = m.group(1)
-                elif name is not None:
-                    if int(m.group(2)):
-                        spills.append("%s (%s B)" % (name, m.group(2)))
-                    name = None
-            if spills:
-                raise RuntimeError("kernels using scratch memory in %s: %s" % (src, ", ".join(spills)))
+    with tempfile.TemporaryDirectory() as tmp, ThreadPoolExecutor(_jobs()) as pool:
+        for fut in [pool.submit(_check_asm, src, tmp) for src in SOURCES]:
+            fut.result()
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the HIP sources into libpkv.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + COMMON + ["-shared", "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
-    out = _run(cmd)
+    """Compile the HIP sources into libpkv.so (always recompiles).
+
+    Each source is compiled to an object, and to assembly for the checks above, in concurrent hipcc processes
+    (at most MAX_JOBS, else the CPU count); the objects are then linked into the library.
+    """
+    with tempfile.TemporaryDirectory() as tmp, ThreadPoolExecutor(_jobs()) as pool:
+        objs = [os.path.join(tmp, src + ".o") for src in SOURCES]
+        compiles = [pool.submit(_run, [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj])
+                    for src, obj in zip(SOURCES, objs)]
+        checks = [pool.submit(_check_asm, src, tmp) for src in SOURCES]
+        out = "\n".join(f.result() for f in compiles)
+        lib_tmp = LIB + ".tmp%d" % os.getpid()
+        out += _run([HIPCC, "--offload-arch=" + ARCH, "-fPIC", "-shared", "-o", lib_tmp] + objs)
+        for f in checks:
+            f.result()
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    check_no_packed_fp32()
+    os.replace(lib_tmp, LIB)
     return LIB
 
 
