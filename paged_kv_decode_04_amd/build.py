@@ -34,7 +34,8 @@ COMMON = ["-std=c++17", "-O3", "--offload-arch=" + ARCH, "-fPIC", "-fvisibility=
           "-I", INCLUDE, "-I", CSRC]
 
 _PACKED_F32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
-_KERNEL_META = re.compile(r"^\s+\.name:\s+(\S+)\s*$|^\s+\.private_segment_fixed_size:\s+(\d+)", re.M)
+_KERNEL_META = re.compile(r"^\s+(?:-\s+)?\.name:\s+(\S+)\s*$|^\s+(?:-\s+)?\.private_segment_fixed_size:\s+(\d+)",
+                          re.M)
 
 
 def _run(cmd):
@@ -50,7 +51,11 @@ def _check_asm(src: str, tmp: str) -> None:
     asm = os.path.join(tmp, src + ".s")
     _run([HIPCC] + COMMON + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
     with open(asm) as f:
-        text = f.read()
+        scan_asm(src, f.read())
+
+
+def scan_asm(src: str, text: str) -> None:
+    """Raise if gfx950 assembly text holds packed-FP32 arithmetic or a kernel with a private (scratch) segment."""
     hits = sorted(set(m.group(0) for m in _PACKED_F32.finditer(text)))
     if hits:
         raise RuntimeError("packed-FP32 instructions in %s: %s" % (src, ", ".join(hits)))
