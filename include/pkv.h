@@ -146,9 +146,12 @@ PKV_API int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int3
  *     dispatcher; 0 = block_size * max_blocks_per_seq (the table capacity, as
  *     the pages do).
  *   Split-K partials go to a workspace the library owns: one grow-only buffer
- *   per (device, stream), allocated on first need (that call synchronises the
- *   stream once before replacing a smaller buffer), never freed before
- *   process exit.  Calls on one stream reuse it in stream order.
+ *   per (device, stream), allocated on first need and replaced by a larger one
+ *   when a call needs more.  No workspace buffer is freed before process exit,
+ *   the replaced ones included, so a graph captured against a smaller buffer
+ *   stays valid after a later, larger call on the same stream grows it (the
+ *   growth does not synchronise).  Calls on one stream reuse it in stream
+ *   order.
  *   Dispatch order: when the grid (num_seqs * Hkv * splits workgroups) is
  *   larger than the device's CU count and num_seqs <= 16384, a small launch
  *   first ranks the sequences by the rows they attend and the attention grid

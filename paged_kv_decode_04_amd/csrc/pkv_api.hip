@@ -12,6 +12,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "pkv.h"
 #include "pkv_internal.h"
@@ -83,6 +84,9 @@ struct Workspace {
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Buffers replaced by growth.  They stay allocated until the process exits: a HIP graph captured while one of them
+// was current holds its address in its kernel arguments and may be replayed after the growth.
+std::vector<void *> g_ws_retired;
 
 int library_workspace(size_t need, hipStream_t stream, void **ptr) {
     int dev = 0;
@@ -92,7 +96,7 @@ int library_workspace(size_t need, hipStream_t stream, void **ptr) {
     std::lock_guard<std::mutex> g(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
     if (w.bytes < need) {
-        // Growing allocates and synchronises, which a stream under graph capture must not do: the caller warms the
+        // Growing allocates (hipMalloc), which a stream under graph capture must not do: the caller warms the
         // workspace up with one call on this stream before capturing, or passes its own (the _ws variants).
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         e = hipStreamIsCapturing(stream, &cap);
@@ -102,23 +106,15 @@ int library_workspace(size_t need, hipStream_t stream, void **ptr) {
             return fail(PKV_EWORKSPACE, "the library workspace of this stream holds %zu bytes, the call needs %zu, and "
                         "the stream is being captured: make one call on this stream before capture, or pass a "
                         "workspace", w.bytes, need);
-        if (w.ptr) {
-            // queued kernels on this stream may still read the old buffer
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess)
-                return hip_fail(e, "hipStreamSynchronize (workspace growth)");
-            e = hipFree(w.ptr);
-            if (e != hipSuccess)
-                return hip_fail(e, "hipFree (workspace growth)");
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
+        // The old buffer is retired, not freed: queued kernels and captured graphs may still use it.
         size_t grown = need + need / 4;  // slack so that small growth does not reallocate every call
-        e = hipMalloc(&w.ptr, grown);
-        if (e != hipSuccess) {
-            w.ptr = nullptr;
+        void *fresh = nullptr;
+        e = hipMalloc(&fresh, grown);
+        if (e != hipSuccess)
             return fail(PKV_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", grown, hipGetErrorString(e));
-        }
+        if (w.ptr)
+            g_ws_retired.push_back(w.ptr);
+        w.ptr = fresh;
         w.bytes = grown;
     }
     *ptr = w.ptr;

@@ -249,3 +249,42 @@ def test_capture_needing_a_new_workspace_fails_cleanly(torch_cuda):
                                        num_splits=4)
     assert e.value.code == pkv.PKV_EWORKSPACE
     torch.cuda.synchronize()
+
+
+def test_replay_after_the_workspace_grew_uses_a_live_buffer(torch_cuda):
+    """A split-K call captured against the stream's library workspace, then a larger eager call on the same stream
+    that makes the workspace grow: the captured graph still names the old buffer, which the library keeps alive, so
+    replays (with fresh allocations made after the growth in between) stay correct against the oracle and leave
+    those allocations untouched."""
+    from paged_kv_decode_04_amd import pkv
+    torch = torch_cuda
+    small = W.small_case(861, 4, 32, 8, 128, 16, (700, 90, 333, 1024))
+    big = W.small_case(862, 48, 32, 8, 128, 16, tuple(200 + (97 * i) % 1800 for i in range(48)))
+    st = _state(torch, small, small.context_lens)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):  # sizes this stream's workspace for the small shape
+        pkv.paged_decode_attention(st["q"], st["kp"], st["vp"], st["bt"], st["cl"], small.scale, out=st["out"],
+                                   num_splits=3)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        pkv.paged_decode_attention(st["q"], st["kp"], st["vp"], st["bt"], st["cl"], small.scale, out=st["out"],
+                                   num_splits=3)
+    torch.cuda.synchronize()
+    bst = _state(torch, big, big.context_lens)
+    with torch.cuda.stream(stream):  # needs far more split partials: the workspace grows
+        big_out = pkv.paged_decode_attention(bst["q"], bst["kp"], bst["vp"], bst["bt"], bst["cl"], big.scale,
+                                             num_splits=8)
+    stream.synchronize()
+    canary = torch.full((1 << 20,), 0x5A5A, dtype=torch.int32, device="cuda")  # allocated after the growth
+    ref_small = oracle.decode_attention(small.q, small.k_pool, small.v_pool, small.block_tables, small.context_lens,
+                                        small.scale)
+    for i in range(3):
+        st["out"].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_close(st["out"].cpu().numpy(), ref_small, "replay %d after the workspace grew" % i)
+    assert bool((canary == 0x5A5A).all())
+    ref_big = oracle.decode_attention(big.q, big.k_pool, big.v_pool, big.block_tables, big.context_lens, big.scale)
+    assert_close(big_out.cpu().numpy(), ref_big, "the call that grew the workspace")
