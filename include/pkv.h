@@ -187,6 +187,35 @@ PKV_API int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_p
                                   size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_paged_decode_attention_noalloc -- for callers that cannot allocate
+ *   device memory: code under HIP graph capture on a stream no call has
+ *   warmed up, serving loops that must not call hipMalloc, harnesses that
+ *   forbid allocation.  Same operation, arguments, dispatcher, results and
+ *   errors as pkv_paged_decode_attention, but the split-K partials and the
+ *   dispatch-order records live in a fixed device array of
+ *   PKV_NOALLOC_SCRATCH_BYTES bytes that the library defines; each device
+ *   holds its own copy from the first call on it until the process exits.
+ *   The call never allocates or frees device memory (no hipMalloc, no
+ *   hipFree, no allocating library routine); its first call on a device
+ *   looks the array's device address up once (hipGetSymbolAddress).
+ *   Limit: a plan whose partials need more than PKV_NOALLOC_SCRATCH_BYTES
+ *   fails with PKV_EWORKSPACE before anything is enqueued (the partials take
+ *   num_seqs * num_q_heads * splits * (head_dim + 2) * 4 bytes, rounded up;
+ *   a single pass takes none); when the dispatch-order records would not fit
+ *   beside them the grid runs in id order instead (same results).
+ *   Every call on one device shares that device's array, which keeps what
+ *   the last call left there: calls whose kernels may overlap on one device
+ *   (several host threads, or streams not ordered against each other) race
+ *   and give unspecified results.  Calls in one stream's order are safe.
+ * ------------------------------------------------------------------------- */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+PKV_API int pkv_paged_decode_attention_noalloc(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                       pkv_pool_desc pool, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                       int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
+                                       int32_t num_splits, int32_t max_context_hint, void *stream);
+
+/* ---------------------------------------------------------------------------
  * pkv_paged_decode_step -- the decode step (append + attention): for every
  *   sequence s with L_s = context_lens[s] > 0, first writes k_new[s][h][:] and
  *   v_new[s][h][:] (every kv head h) to row L_s - 1 of the sequence -- block

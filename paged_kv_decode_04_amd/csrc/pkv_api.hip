@@ -150,6 +150,46 @@ WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t S, int64_t order_in
     return L;
 }
 
+// Where a call's split-K partials and dispatch-order records live.
+enum WsKind {
+    kCallerWs = 0,   // a workspace the caller passes (the _ws / _planned variants)
+    kLibraryWs = 1,  // the library-owned, grow-only buffer of the (device, stream)
+    kFixedWs = 2,    // the fixed device array below (pkv_paged_decode_attention_noalloc)
+};
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch for callers that cannot allocate (pkv_paged_decode_attention_noalloc).  Each device that
+// loads the library holds its own copy of the array until the process exits.  In host code `scratch` names a host
+// stand-in, not device memory: kernels get the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.
+
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+std::map<int, void *> g_scratch_ptr;  // device ordinal -> that device's address of `scratch`
+
+int scratch_address(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> g(g_scratch_mutex);
+    auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end()) {
+        *ptr = it->second;
+        return PKV_OK;
+    }
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256))
+        return fail(PKV_EHIP, "hipGetSymbolAddress(scratch) returned %p, not a 256-byte aligned device address", p);
+    g_scratch_ptr[dev] = p;
+    *ptr = p;
+    return PKV_OK;
+}
+
 // ---------------------------------------------------------------------------
 // checks shared by the attention entry points
 
@@ -351,7 +391,7 @@ int check_qkv_pointers(const QkvSource &q) {
 int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
              const pkv_pool_desc &pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out,
-             void *workspace, size_t workspace_bytes, bool library_ws, hipStream_t stream, int cu_count,
+             void *workspace, size_t workspace_bytes, WsKind ws_kind, hipStream_t stream, int cu_count,
              const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr, int32_t window = 0,
              const QkvSource *qsrc = nullptr, const pkv::AppendParams *pre_append = nullptr) {
     pkv::DecodeParams p = decode_params(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
@@ -381,10 +421,15 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
     // order array in the library workspace): the longest workgroups otherwise tend to start in a late round and
     // finish alone.  Only with the library workspace, and not where it would have to grow under graph capture.
     const int64_t grid = (int64_t)num_seqs * pool.num_kv_heads * plan.num_splits;
-    bool order = library_ws && num_seqs > 1 && num_seqs <= pkv::kOrderMaxSeqs && cu_count > 0 && grid > cu_count;
+    bool order = ws_kind != kCallerWs && num_seqs > 1 && num_seqs <= pkv::kOrderMaxSeqs && cu_count > 0 &&
+                 grid > cu_count;
     WsLayout L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits,
                            order ? (int64_t)num_seqs * pkv::kOrderRecord : 0);
-    if (order && library_workspace_bytes(stream) < L.total) {
+    if (order && ws_kind == kFixedWs && L.total > workspace_bytes) {
+        order = false;  // the records do not fit beside the partials: id order
+        L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits);
+    }
+    if (order && ws_kind == kLibraryWs && library_workspace_bytes(stream) < L.total) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         hipError_t e = hipStreamIsCapturing(stream, &cap);
         if (e != hipSuccess)
@@ -407,10 +452,15 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
         return ok();
     }
     void *ws = workspace;
-    if (library_ws) {
+    if (ws_kind == kLibraryWs) {
         int rc = library_workspace(L.total, stream, &ws);
         if (rc)
             return rc;
+    } else if (ws_kind == kFixedWs) {
+        if (L.total > workspace_bytes)
+            return fail(PKV_EWORKSPACE, "the plan (%d splits, %d sequences) needs %zu bytes of split-K partials; the "
+                        "fixed scratch of the no-allocation entry point holds %zu", plan.num_splits, num_seqs,
+                        L.total, workspace_bytes);
     } else {
         if (!ws || workspace_bytes < L.total)
             return fail(PKV_EWORKSPACE, "workspace of %zu bytes at %p; the plan (%d splits) needs %zu",
@@ -474,7 +524,7 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
                 const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
                 int32_t num_seqs, int32_t num_q_heads, float scale, uint16_t *out, int32_t num_splits,
                 int32_t max_context_hint, const pkv_decode_plan *given, void *workspace, size_t workspace_bytes,
-                bool library_ws, hipStream_t stream, const uint16_t *k_new = nullptr,
+                WsKind ws_kind, hipStream_t stream, const uint16_t *k_new = nullptr,
                 const uint16_t *v_new = nullptr, int32_t window = 0, const QkvSource *qsrc = nullptr) {
     int rc = check_decode_geometry(num_seqs, num_q_heads, pool, max_blocks_per_seq);
     if (rc)
@@ -560,11 +610,11 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
         k_new = v_new = nullptr;
         // run_plan launches it first, with the dispatch-order records folded in when the grid is ordered
         return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                        num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, facts.cu_count,
+                        num_q_heads, scale, out, workspace, workspace_bytes, ws_kind, stream, facts.cu_count,
                         nullptr, nullptr, window, qsrc, &a);
     }
     return run_plan(plan, q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                    num_q_heads, scale, out, workspace, workspace_bytes, library_ws, stream, facts.cu_count, k_new,
+                    num_q_heads, scale, out, workspace, workspace_bytes, ws_kind, stream, facts.cu_count, k_new,
                     v_new, window, qsrc);
 }
 
@@ -897,7 +947,7 @@ int pkv_paged_decode_attention(const uint16_t *q, const uint16_t *k_pool, const 
                                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                                uint16_t *out, int32_t num_splits, int32_t max_context_hint, void *stream) {
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, kLibraryWs,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -908,7 +958,21 @@ int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_pool, con
                                   size_t workspace_bytes, void *stream) {
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                        num_q_heads, scale, out, num_splits, max_context_hint, nullptr, workspace, workspace_bytes,
-                       false, static_cast<hipStream_t>(stream));
+                       kCallerWs, static_cast<hipStream_t>(stream));
+}
+
+int pkv_paged_decode_attention_noalloc(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                       pkv_pool_desc pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                       float scale, uint16_t *out, int32_t num_splits, int32_t max_context_hint,
+                                       void *stream) {
+    void *ws = nullptr;
+    int rc = scratch_address(&ws);  // once per device: the address of that device's copy of `scratch`
+    if (rc)
+        return rc;
+    return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, ws,
+                       (size_t)PKV_NOALLOC_SCRATCH_BYTES, kFixedWs, static_cast<hipStream_t>(stream));
 }
 
 int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
@@ -919,7 +983,8 @@ int pkv_paged_decode_attention_planned(const uint16_t *q, const uint16_t *k_pool
     if (!plan)
         return fail(PKV_EINVAL, "plan is null");
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_q_heads, scale, out, 0, 0, plan, workspace, workspace_bytes, workspace == nullptr,
+                       num_q_heads, scale, out, 0, 0, plan, workspace, workspace_bytes,
+                       workspace == nullptr ? kLibraryWs : kCallerWs,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -933,7 +998,7 @@ int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, const uint16
     if (num_seqs > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16)))
         return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, kLibraryWs,
                        static_cast<hipStream_t>(stream), k_new, v_new);
 }
 
@@ -947,7 +1012,7 @@ int pkv_paged_decode_step_window(const uint16_t *q, const uint16_t *k_new, const
     if (num_seqs > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16)))
         return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, kLibraryWs,
                        static_cast<hipStream_t>(stream), k_new, v_new, window);
 }
 
@@ -1105,7 +1170,7 @@ int pkv_paged_decode_step_qkv(const uint16_t *qkv, const uint16_t *q_norm_w, con
             return rc;
     }
     return decode_impl(q_out, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, kLibraryWs,
                        static_cast<hipStream_t>(stream), nullptr, nullptr, 0, &src);
 }
 
@@ -1222,7 +1287,7 @@ int pkv_paged_decode_attention_window(const uint16_t *q, const uint16_t *k_pool,
                                       float scale, uint16_t *out, int32_t num_splits, int32_t window,
                                       int32_t max_context_hint, void *stream) {
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, true,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr, 0, kLibraryWs,
                        static_cast<hipStream_t>(stream), nullptr, nullptr, window);
 }
 

@@ -39,6 +39,7 @@ EXPORTED = [
     "pkv_paged_kv_append",
     "pkv_paged_decode_attention",
     "pkv_paged_decode_attention_ws",
+    "pkv_paged_decode_attention_noalloc",
     "pkv_paged_decode_attention_planned",
     "pkv_paged_decode_step",
     "pkv_paged_decode_step_qkv",
@@ -100,6 +101,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         attn = [vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, vp, i32, i32]
         lib.pkv_paged_decode_attention.argtypes = attn + [vp]
         lib.pkv_paged_decode_attention_ws.argtypes = attn + [vp, sz, vp]
+        lib.pkv_paged_decode_attention_noalloc.argtypes = attn + [vp]
         lib.pkv_paged_decode_attention_planned.argtypes = attn[:11] + [ctypes.POINTER(DecodePlan), vp, sz, vp]
         lib.pkv_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, PoolDesc, vp, i32, vp, i32, i32, f32, vp, i32, i32,
                                               vp]
@@ -246,6 +248,25 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale:
         nbytes = workspace.numel() * workspace.element_size()
         _check(lib.pkv_paged_decode_attention_ws(*args, _ptr(workspace), nbytes, _stream(stream)))
     return out
+
+
+def paged_decode_attention_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,
+                                   num_splits: int = 0, max_context_hint: int = 0, stream=None):
+    """pkv_paged_decode_attention_noalloc: decode attention whose split-K partials and dispatch-order records use the
+    library's fixed device scratch (PKV_NOALLOC_SCRATCH_BYTES per device) -- the call allocates nothing, so ``out``
+    must be given.  Calls on one device share that scratch: calls that may overlap in time race."""
+    import torch
+    pool, B, Hq, M = _attn_args(q, k_pool, v_pool, block_tables, context_lens)
+    _dev(out, torch.float16, "out", 3)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check(load().pkv_paged_decode_attention_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), pool, _ptr(block_tables),
+                                                     M, _ptr(context_lens), B, Hq, float(scale), _ptr(out),
+                                                     int(num_splits), int(max_context_hint), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # PKV_NOALLOC_SCRATCH_BYTES in include/pkv.h
 
 
 def paged_decode_attention_planned(q, k_pool, v_pool, block_tables, context_lens, scale: float, plan: dict,
