@@ -483,7 +483,11 @@ PKV_API int pkv_plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
 
 /* Bytes of f32 split-K partials for a grid of num_splits splits:
  * partial_out [B][Hq][S][D] then partial_m and partial_l [B][Hq][S], each
- * array starting on a 256-byte boundary.  0 when num_splits <= 1. */
+ * array starting on a 256-byte boundary.  0 when num_splits <= 1.
+ * [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs: SplitKScratch, whose three
+ * f32 buffers hold rows * q heads * splits * head_dim (partial_out) and
+ * rows * q heads * splits (partial_m, partial_l); one workspace here packs the
+ * three.]  Pure host function. */
 PKV_API size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t num_splits);
 
@@ -568,13 +572,19 @@ PKV_API int pkv_check_varlen_inputs(const int32_t *block_tables, int32_t max_blo
 PKV_API int pkv_check_slot_mapping(const int32_t *slot_mapping, int32_t num_tokens, pkv_pool_desc pool, int32_t *report,
                            void *stream);
 
-/* Number of compute units of the current device (hipDeviceProp_t::multiProcessorCount). */
+/* Number of compute units of the current device (hipDeviceProp_t::multiProcessorCount): the count the
+ * dispatcher sizes grids against, where the pages assume a fixed 128 SMs
+ * [ferrum-kernels 0.7.7, src/backend/cuda/paged.rs: paged_varlen_split_k_dispatch,
+ * "total blocks >= 2 x SM count"].  Errors: PKV_EINVAL (NULL), PKV_EHIP. */
 PKV_API int pkv_device_cu_count(int32_t *cu_count);
 
-/* Thread-local message for the last non-zero return on this thread ("" if none). */
+/* Thread-local message for the last non-zero return on this thread ("" if none): the C form of the
+ * error values the pages' backend calls return with a message [ferrum-kernels 0.7.1,
+ * src/backend/cuda.rs: Result with a FerrumError, e.g. from end_graph_capture].  The
+ * string stays valid until the thread's next failing call. */
 PKV_API const char *pkv_last_error(void);
 
-/* Library version string. */
+/* Library version string (static storage).  A library utility with no counterpart on the pages. */
 PKV_API const char *pkv_version(void);
 
 #ifdef __cplusplus

@@ -25,7 +25,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["pkv_kernels.hip", "pkv_qkv.hip", "pkv_check.hip", "pkv_api.hip"]
+SOURCES = ["pkv_kernels.hip", "pkv_qkv.hip", "pkv_check.hip", "pkv_geometry.hip", "pkv_api.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -344,6 +344,8 @@ int check_plan(const pkv_decode_plan &plan, int32_t num_seqs, int32_t num_q_head
     if (w > pkv::max_waves_per_group(pool.head_dim))
         return fail(PKV_EUNSUPPORTED, "plan.waves_per_group %d exceeds the %d compiled for head_dim %d", w,
                     pkv::max_waves_per_group(pool.head_dim), pool.head_dim);
+    if (lds_limit < 0)
+        return PKV_OK;  // the device-free checks only (the LDS limit is the device's)
     const size_t need = pkv::decode_lds_bytes(pool.head_dim, num_q_heads / pool.num_kv_heads, w);
     const size_t limit = lds_limit > 0 ? (size_t)lds_limit : (size_t)65536;
     if (need > limit)
@@ -542,10 +544,17 @@ int decode_impl(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_poo
     rc = check_decode_pointers(q, k_pool, v_pool, block_tables, context_lens, out);
     if (rc)
         return rc;
+    if (given && (rc = check_plan(*given, num_seqs, num_q_heads, pool, max_blocks_per_seq, -1)) != 0)
+        return rc;  // every argument error is reported before the first device query
     DeviceFacts facts;
     rc = device_facts(&facts);
     if (rc)
         return rc;
+    if (ws_kind == kFixedWs && workspace == nullptr) {
+        rc = scratch_address(&workspace);  // once per device: the address of that device's copy of `scratch`
+        if (rc)
+            return rc;
+    }
     pkv_decode_plan plan;
     if (given) {
         plan = *given;
@@ -966,12 +975,9 @@ int pkv_paged_decode_attention_noalloc(const uint16_t *q, const uint16_t *k_pool
                                        const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
                                        float scale, uint16_t *out, int32_t num_splits, int32_t max_context_hint,
                                        void *stream) {
-    void *ws = nullptr;
-    int rc = scratch_address(&ws);  // once per device: the address of that device's copy of `scratch`
-    if (rc)
-        return rc;
+    // the fixed array's address is looked up inside, once the arguments have passed their checks
     return decode_impl(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, ws,
+                       num_q_heads, scale, out, num_splits, max_context_hint, nullptr, nullptr,
                        (size_t)PKV_NOALLOC_SCRATCH_BYTES, kFixedWs, static_cast<hipStream_t>(stream));
 }
 

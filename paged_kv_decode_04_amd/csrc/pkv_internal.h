@@ -148,6 +148,8 @@ hipError_t launch_combine(const CombineParams &p, int head_dim, hipStream_t stre
 size_t varlen_lds_bytes(int head_dim, int waves, bool fused = false);
 // New rows per sequence the one-launch varlen step holds in LDS.
 constexpr int kStepFusedRows = 32;
+// 16-row units of new rows the fused varlen step's workgroup stages: any kStepFusedRows consecutive rows fit.
+constexpr int kFusedUnits = (kStepFusedRows + 2 * 15) / 16;
 hipError_t launch_varlen(const VarlenParams &p, int num_seqs, int head_dim, int block_size, int waves, bool split,
                          hipStream_t stream);
 hipError_t launch_append(const AppendParams &p, hipStream_t stream);

@@ -440,7 +440,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 // pools by this launch -- each 16-row unit holding new rows is patched from an LDS copy of its new rows whenever it
 // is computed and written back whole, so any interleaving of workgroups leaves the same bytes -- for the first
 // kFusedUnits units of a sequence's new rows: any kStepFusedRows consecutive rows fit.
-constexpr int kFusedUnits = (kStepFusedRows + 2 * 15) / 16;
 
 template <int D, int BS, int NW, bool SPLIT, int QT, bool FUSED = false, bool ORDERED = false>
 __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
@@ -1144,20 +1143,6 @@ __global__ __launch_bounds__(256) void order_varlen_kernel(const int32_t *__rest
 // ---------------------------------------------------------------------------
 // launchers
 
-size_t decode_lds_bytes(int head_dim, int G, int waves) {
-    // the merge area, then the fused step's copy of the new row (K and V, head_dim halves each)
-    return sizeof(float) * merge_floats(head_dim, G, waves) + 4 * (size_t)head_dim;
-}
-
-bool decode_geometry_supported(int head_dim, int block_size) {
-    return (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
-           (block_size == 16 || block_size == 32 || block_size == 64);
-}
-
-// Two K/V fragment sets of head dim 256 need more registers than a wave of an 8-wave group has, so that variant
-// would spill and is not compiled.
-int max_waves_per_group(int head_dim) { return head_dim >= 256 ? 4 : kMaxWaves; }
-
 template <int D, int BS, int NW>
 static hipError_t launch_decode_t(const DecodeParams &p, int num_seqs, bool split, hipStream_t stream) {
     dim3 grid((unsigned)((int64_t)num_seqs * p.Hkv * (split ? p.num_splits : 1)), 1u, 1u);
@@ -1219,12 +1204,6 @@ hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int 
     case 256: return launch_decode_d<256>(p, num_seqs, block_size, waves, split, stream);
     default: return hipErrorInvalidValue;
     }
-}
-
-size_t varlen_lds_bytes(int head_dim, int waves, bool fused) {
-    // the merge area, then (fused step) kFusedUnits units of new K and V rows
-    return sizeof(float) * (size_t)merge_floats(head_dim, 16, waves) +
-           (fused ? sizeof(_Float16) * (size_t)kFusedUnits * 32 * head_dim : 0);
 }
 
 template <int D, int BS, int NW>
