@@ -96,10 +96,14 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of every source of the library (any change retires the traffic summaries taken before it)."""
     h = hashlib.sha256()
-    for name in ("pkv_kernels.hip", "pkv_qkv.hip", "pkv_check.hip", "pkv_api.hip", "pkv_internal.h", "pkv_lanes.h"):
-        with open(os.path.join(ROOT, "paged_kv_decode_04_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "paged_kv_decode_04_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 

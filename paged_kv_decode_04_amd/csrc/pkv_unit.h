@@ -228,14 +228,22 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
         pe[e] = exp2_fast(y[e] - m_new);
     l_run = l_run * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
     m_run = m_new;
-    f16x4 pf;
+    // The weights enter the f16 matrix-core product as two halves, p = hi + lo with hi = fp16(p) and
+    // lo = fp16(p - hi) (the difference is exact in f32): one fp16 rounding alone moves a weight by up to 2^-11 of
+    // itself, and weights sitting just off rounding midpoints with V signs that follow the rounding direction add
+    // up to 2^-11 * max|v| of error in the output; with the low half the weights are good to about 2^-22.  The
+    // second product costs matrix-core cycles only, which this memory-bound loop has to spare.
+    f16x4 ph, pl;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        pf[e] = (_Float16)pe[e];
+    for (int e = 0; e < 4; ++e) {
+        ph[e] = (_Float16)pe[e];
+        pl[e] = (_Float16)(pe[e] - (float)ph[e]);
+    }
 #pragma unroll
     for (int c = 0; c < VC; ++c) {
         o[c] *= alpha;
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(f.v[c], pf, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(f.v[c], ph, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(f.v[c], pl, o[c], 0, 0, 0);
     }
 }
 

@@ -1,15 +1,20 @@
-"""The worst case of the fp16 P in the P.V product, built on purpose.
+"""The worst case of fp16 softmax weights in the P.V product, built on purpose.
 
-The kernels round the softmax weights p = 2^(s' - m) to fp16 for the matrix-core P.V product, while the running sum l
-keeps the f32 p.  A normal fp16 rounding moves p by at most 2^-11 of itself (the most just above a power of two), so
-the output moves by at most 2^-11 * sum_j p_j |v_j| / sum_j p_j <= 2^-11 * max|v|; the errors cancel unless every
-weight sits just off a rounding midpoint and V's sign follows the direction each weight rounds.  These cases put them
-there: with scale = ln 2 (in f32) the kernels' log2-domain scale is exactly 1, q = e0 + e1 and a key (-1, b) has the
-score s' = b - 1 exactly (fp16 b, exact f32 sum), so p = 2^(b - 1) lands 1e-6 below or above the midpoint
-0.5 + 2^-12 between the fp16 values 0.5 and 0.5 + 2^-11; the keys below round down and carry v = -4, those above round
-up and carry v = +4.  One key with score 0 (and v = 0) in the first unit each wave reads keeps every wave's running
-max at 0, so every weight is rounded where it was placed.  The bound is then 2^-11 * 4 = 1.95e-3, under the 2e-3
-attention bar; the reference output is about 0, so only the absolute bar applies.
+The matrix-core P.V product takes the weights p = 2^(s' - m) in fp16, while the running sum l keeps the f32 p.  Had
+the kernels rounded each weight once, a normal fp16 rounding would move p by up to 2^-11 of itself (the most just
+above a power of two), and the output by up to 2^-11 * sum_j p_j |v_j| / sum_j p_j <= 2^-11 * max|v|: the errors
+cancel unless every weight sits just off a rounding midpoint and V's sign follows the direction each weight rounds.
+Measured with one rounding, the case below gave 1.930e-3 against a model of 1.929e-3 and a bound of 1.953e-3 (at
+|v| = 4; just under the 2e-3 attention bar, and past it for |v| > 4.1).  The kernels now split each weight into
+hi = fp16(p) and lo = fp16(p - hi) and run the product on both, so the weights are good to about 2^-22 and the
+output error is the fp16 output rounding; the test holds the case to 5% of the single-rounding model.
+
+These cases put the weights there: with scale = ln 2 (in f32) the kernels' log2-domain scale is exactly 1,
+q = e0 + e1 and a key (-1, b) has the score s' = b - 1 exactly (fp16 b, exact f32 sum), so p = 2^(b - 1) lands 1e-6
+below or above the midpoint 0.5 + 2^-12 between the fp16 values 0.5 and 0.5 + 2^-11; the keys below round down and
+carry v = -4, those above round up and carry v = +4.  One key with score 0 (and v = 0) in the first unit each wave reads keeps every wave's running
+max at 0, so every weight is rounded where it was placed.  The reference output is small (1.6e-2 and 0.24), so the
+bars are absolute.
 """
 import math
 
@@ -97,7 +102,7 @@ def test_the_case_rounds_every_weight_the_way_its_value_points():
     ("first unit of every wave", 2048, set(range(0, 128, 16)), (1,)),
     ("every unit", 2048, set(range(0, 2048, 16)), (1, 0, 4)),
 ])
-def test_fp16_weights_aligned_worst_case_within_the_bar(what, L, max_rows, splits):
+def test_fp16_weights_aligned_worst_case(what, L, max_rows, splits):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -114,4 +119,4 @@ def test_fp16_weights_aligned_worst_case_within_the_bar(what, L, max_rows, split
         print("[precision] %s, num_splits=%d: max|err| %.3e (f16-weight model %.3e, bound %.3e), max|ref| %.1e"
               % (what, S, err, abs(model), 2.0 ** -11 * 4, float(np.abs(ref).max())), flush=True)
         assert np.all(np.isfinite(out))
-        assert err <= BAR
+        assert err <= BAR and err <= 0.05 * abs(model)
