@@ -43,7 +43,7 @@
  * -------
  *    q, out        [num_seqs][num_q_heads][head_dim]            fp16
  *    k_pool        [num_blocks][num_kv_heads][block_size/16][head_dim/8][16][8]  fp16
- *    v_pool        [num_blocks][num_kv_heads][block_size/16][head_dim][16]       fp16
+ *    v_pool        [num_blocks][num_kv_heads][block_size/16][4][head_dim][4]     fp16
  *    block_tables  [num_seqs][max_blocks_per_seq]                int32
  *    context_lens  [num_seqs]                                    int32
  *    k, v (append) [num_tokens][num_kv_heads][head_dim]          fp16
@@ -51,11 +51,13 @@
  *  The pages fix no pool layout.  Each (block, kv head) tile is one contiguous
  *  run of block_size*head_dim values, stored as block_size/16 panels of 16
  *  rows.  A K panel holds the 16 rows' dims in 8-wide pieces, piece-major
- *  (element (row r, dim d) at ((d/8)*16 + r)*8 + d%8); a V panel holds V
- *  transposed (element (r, d) at d*16 + r).  With this layout every operand
- *  the decode kernel feeds to the matrix cores is a contiguous run in memory
- *  (1 KB per K load, 512 B per V load of a wavefront).  K/V row t of a tile
- *  is in panel t/16, row t%16.
+ *  (element (row r, dim d) at ((d/8)*16 + r)*8 + d%8); a V panel holds four
+ *  quads of 4 rows, and in a quad each dim's 4 rows side by side (element
+ *  (r, d) at ((r/4)*head_dim + d)*4 + r%4).  With this layout every operand
+ *  the decode kernel feeds to the matrix cores is whole cache lines (one 1 KB
+ *  run per K load, four 128-byte runs per V load of a wavefront), and a new
+ *  row written into a panel touches head_dim/4 of its 32-byte V sectors.
+ *  K/V row t of a tile is in panel t/16, row t%16.
  *
  *  context_lens[s] counts the rows of sequence s including the token being
  *  decoded (the length after the append) [kapsl-backends 0.1.1,

@@ -112,7 +112,7 @@ def k_index(num_kv_heads, block_size, head_dim, block, head, offset, dim) -> int
 
 
 def v_index(num_kv_heads, block_size, head_dim, block, head, offset, dim) -> int:
-    """Flat index of V element (block, kv head, row offset, dim) in v_pool[N][Hkv][BS/16][D][16]."""
+    """Flat index of V element (block, kv head, row offset, dim) in v_pool[N][Hkv][BS/16][4][D][4]."""
     return _load().oracle_v_index(num_kv_heads, block_size, head_dim, block, head, offset, dim)
 
 
@@ -120,7 +120,7 @@ def _geometry(q, k_pool, v_pool, block_tables, context_lens):
     B, Hq, D = q.shape
     N, Hkv, NP, D8, sixteen, eight = k_pool.shape
     BS = NP * 16
-    if (sixteen, eight) != (16, 8) or D8 * 8 != D or v_pool.shape != (N, Hkv, NP, D, 16):
+    if (sixteen, eight) != (16, 8) or D8 * 8 != D or v_pool.shape != (N, Hkv, NP, 4, D, 4):
         raise ValueError("pool shapes %s / %s do not match q %s" % (k_pool.shape, v_pool.shape, q.shape))
     bt = _i32(block_tables)
     if bt.ndim != 2 or bt.shape[0] != B:
@@ -134,7 +134,7 @@ def _geometry(q, k_pool, v_pool, block_tables, context_lens):
 def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale, units=None, threads=None, window=0):
     """out[B][Hq][D] (or out[len(units)][D] for a list of (s, hq) units) in float64.
 
-    q: [B][Hq][D] fp16; k_pool: [N][Hkv][BS/16][D/8][16][8] fp16; v_pool: [N][Hkv][BS/16][D][16] fp16;
+    q: [B][Hq][D] fp16; k_pool: [N][Hkv][BS/16][D/8][16][8] fp16; v_pool: [N][Hkv][BS/16][4][D][4] fp16;
     block_tables: [B][M] int32; context_lens: [B] int32 (rows including the newest token).
     window > 0: each new row attends only its sequence's last `window` rows (sliding-window decode).
     """
@@ -216,7 +216,7 @@ def paged_kv_append(k, v, slot_mapping, k_pool, v_pool) -> int:
     T, Hkv, D = kb.shape
     N, Hkv2, NP, D8, sixteen, eight = k_pool.shape
     BS = NP * 16
-    if (Hkv2, D8 * 8, sixteen, eight) != (Hkv, D, 16, 8) or v_pool.shape != (N, Hkv, NP, D, 16):
+    if (Hkv2, D8 * 8, sixteen, eight) != (Hkv, D, 16, 8) or v_pool.shape != (N, Hkv, NP, 4, D, 4):
         raise ValueError("pool shapes do not match k/v")
     if not (k_pool.flags.c_contiguous and v_pool.flags.c_contiguous):
         raise ValueError("pools must be C-contiguous (updated in place)")
@@ -240,7 +240,7 @@ def varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets,
     T, Hq, D = q.shape
     N, Hkv, NP, D8, sixteen, eight = k_pool.shape
     BS = NP * 16
-    if (sixteen, eight) != (16, 8) or D8 * 8 != D or v_pool.shape != (N, Hkv, NP, D, 16):
+    if (sixteen, eight) != (16, 8) or D8 * 8 != D or v_pool.shape != (N, Hkv, NP, 4, D, 4):
         raise ValueError("pool shapes %s / %s do not match q %s" % (k_pool.shape, v_pool.shape, q.shape))
     bt = _i32(block_tables)
     cu = _i32(cu_seqlens_q)
@@ -282,7 +282,7 @@ def qkv_norm_rope_paged(qkv, q_norm_w, k_norm_w, cos, sin, cu_seqlens_q, rope_po
     T, width = qb.shape
     N, Hkv, NP, D8, sixteen, eight = k_pool.shape
     BS, D = NP * 16, D8 * 8
-    if (sixteen, eight) != (16, 8) or v_pool.shape != (N, Hkv, NP, D, 16) or width % D:
+    if (sixteen, eight) != (16, 8) or v_pool.shape != (N, Hkv, NP, 4, D, 4) or width % D:
         raise ValueError("pool shapes %s / %s do not match qkv %s" % (k_pool.shape, v_pool.shape, qb.shape))
     Hq = width // D - 2 * Hkv
     if Hq <= 0:

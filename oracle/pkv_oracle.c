@@ -48,8 +48,10 @@
  *    k_pool[num_blocks][num_kv_heads][block_size/16][head_dim/8][16][8]
  *           (a panel holds each row's dims in 8-wide pieces: piece 0 of the
  *           16 rows, then piece 1, ...)
- *    v_pool[num_blocks][num_kv_heads][block_size/16][head_dim][16]
- *           (a panel holds V transposed: dim-major, 16 rows per dim)
+ *    v_pool[num_blocks][num_kv_heads][block_size/16][4][head_dim][4]
+ *           (a panel holds V in four quads of 4 rows; in a quad each
+ *           dim's 4 rows are adjacent: dim 0 of rows 4i..4i+3, then dim 1,
+ *           ...)
  * head_dim must be a multiple of 8 and block_size a multiple of 16.
  *
  * All arithmetic is IEEE binary64; fp16 inputs are decoded exactly.  No
@@ -94,7 +96,7 @@ void oracle_f16_array_to_f64(const uint16_t *src, int64_t n, double *dst)
 typedef struct {
     const uint16_t *q;            /* [B][Hq][D] fp16 bits */
     const uint16_t *k_pool;       /* [N][Hkv][BS/16][D/8][16][8] fp16 bits */
-    const uint16_t *v_pool;       /* [N][Hkv][BS/16][D][16] fp16 bits */
+    const uint16_t *v_pool;       /* [N][Hkv][BS/16][4][D][4] fp16 bits */
     const int32_t *block_tables;  /* [B][M] */
     const int32_t *context_lens;  /* [B] */
     int32_t B, Hq, Hkv, D, BS, N, M;
@@ -109,11 +111,11 @@ static int64_t k_index(const oracle_problem *P, int64_t b, int h, int o, int d)
     return ((panel * (P->D / 8) + d / 8) * 16 + o % 16) * 8 + d % 8;
 }
 
-/* v_pool element (block b, kv head h, row offset o, dim d): panel o / 16, dim d, row o % 16 */
+/* v_pool element (block b, kv head h, row offset o, dim d): panel o / 16, quad (o % 16) / 4, dim d, row o % 4 */
 static int64_t v_index(const oracle_problem *P, int64_t b, int h, int o, int d)
 {
     int64_t panel = (b * P->Hkv + h) * (P->BS / 16) + o / 16;
-    return (panel * P->D + d) * 16 + o % 16;
+    return ((panel * 4 + (o % 16) / 4) * P->D + d) * 4 + o % 4;
 }
 
 int64_t oracle_k_index(int32_t Hkv, int32_t BS, int32_t D, int64_t b, int h, int o, int d)

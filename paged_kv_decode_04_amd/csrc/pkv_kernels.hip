@@ -164,7 +164,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     float l_run = 0.f;
 
     const uint32_t k_lane = (uint32_t)(16 * lane);            // bytes into a K panel
-    const uint32_t v_lane = (uint32_t)(32 * r + 8 * g4);      // bytes into a V panel
+    const uint32_t v_lane = v_lane_offset(D, r, g4);          // bytes into a V panel
     const int64_t head_off = (int64_t)hk * (BS * D);
     const int64_t block_stride = (int64_t)p.Hkv * (BS * D);
 
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
     const int qlen = q1 - q0;
 
     const uint32_t k_lane = (uint32_t)(16 * lane);
-    const uint32_t v_lane = (uint32_t)(32 * r + 8 * g4);
+    const uint32_t v_lane = v_lane_offset(D, r, g4);
     const int64_t head_off = (int64_t)hk * (BS * D);
     const int64_t block_stride = (int64_t)p.Hkv * (BS * D);
 
@@ -829,10 +829,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 // launch_batch_kv_write]: one thread per (token, kv head, 8-dim piece), tokens
 // fastest, so that neighbouring lanes take neighbouring tokens of the same
 // (head, piece).  The K piece is one 16-byte store into the row's panel
-// ([D/8][16][8]); the V piece is 8 two-byte stores into the transposed panel
-// ([D][16]).  When consecutive tokens have consecutive slots (a sequence's new
-// rows), 16 lanes fill a whole 256-byte run of a K panel and whole 32-byte
-// rows of a V panel.
+// ([D/8][16][8]); the V piece is 8 two-byte stores 8 bytes apart into the row's
+// quad of the V panel ([4][D][4]), two 32-byte sectors.  When consecutive tokens
+// have consecutive slots (a sequence's new rows), 16 lanes fill a whole 256-byte
+// run of a K panel and every 4 lanes whole 64-byte runs of a V quad.
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int pieces = p.D / 8;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -857,10 +857,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int row = off % 16;
     *reinterpret_cast<uint4 *>(p.k_pool + panel + ((int64_t)c * 16 + row) * 8) = kv;  // K panel [D/8][16][8]
     const uint16_t *vh = reinterpret_cast<const uint16_t *>(&vv);
-    uint16_t *vdst = reinterpret_cast<uint16_t *>(p.v_pool + panel + (int64_t)(8 * c) * 16 + row);  // [D][16]
+    uint16_t *vdst = reinterpret_cast<uint16_t *>(p.v_pool + panel + (int64_t)(row >> 2) * 4 * p.D + 32 * c +
+                                                  (row & 3));  // V panel [4][D][4]: dims 8c .. 8c+7 of the row
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        vdst[e * 16] = vh[e];
+        vdst[e * 4] = vh[e];
 }
 
 constexpr int kOrderSeqsPerGroup = 64;  // sequences one order workgroup ranks
@@ -871,10 +872,11 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
                                                   int window, int32_t *__restrict__ order, int group, int *keys);
 
 // The decode step's append as its own launch: the new row of sequence s (block bt[s][(L-1)/BS], row (L-1)%BS, as
-// the fused step places it) for every kv head.  One workgroup per (sequence, kv head) rewrites the two 16-row
-// panels holding the row whole -- each thread one 16-byte chunk: read, replace the row's part, write back -- so the
-// pools see only full-line writes (scattered 2- and 16-byte row stores cost far more at the memory than their
-// bytes).  Valid only because the block holding a sequence's newest row belongs to that sequence alone.
+// the fused step places it) for every kv head.  One workgroup per (sequence, kv head) rewrites the 128-byte lines
+// that hold the row whole -- each thread one 16-byte chunk: read, replace the row's part, write back -- so the pools
+// see only full-line writes: in the K panel the D/8 lines of the row's 8-row half (one 8-dim piece each), in the V
+// panel the D/16 lines of the row's quad.  Valid only because the block holding a sequence's newest row belongs to
+// that sequence alone.
 // With p.order set, the workgroups past the T * Hkv appends write the dispatch-order records instead (the ranking
 // of launch_order, in the same launch as the append).
 __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
@@ -898,22 +900,24 @@ __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
     const int64_t panel = ((int64_t)b * p.Hkv + h) * p.BS * p.D + (int64_t)(off / 16) * 16 * p.D;
     const _Float16 *kn = p.k + ((int64_t)s * p.Hkv + h) * p.D;
     const _Float16 *vn = p.v + ((int64_t)s * p.Hkv + h) * p.D;
-    const int chunks = 2 * p.D;  // 16-byte chunks of one 16-row panel (16 * D halves)
-    for (int q = threadIdx.x; q < chunks; q += 256) {
-        // K panel [D/8][16][8]: chunk q is piece q/16 of row q%16
-        f16x8 kc = *reinterpret_cast<const f16x8 *>(p.k_pool + panel + 8 * q);
-        if (q % 16 == row)
-            kc = *reinterpret_cast<const f16x8 *>(kn + 8 * (q / 16));
-        *reinterpret_cast<f16x8 *>(p.k_pool + panel + 8 * q) = kc;
-        // V panel [D][16]: chunk q is dim q/2, rows 8*(q%2) .. +8
-        f16x8 vc = *reinterpret_cast<const f16x8 *>(p.v_pool + panel + 8 * q);
-        if ((q & 1) == row / 8) {
-            const _Float16 x = vn[q / 2];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                vc[e] = (e == row % 8) ? x : vc[e];
-        }
-        *reinterpret_cast<f16x8 *>(p.v_pool + panel + 8 * q) = vc;
+    // One 16-byte chunk per thread (head_dim <= 256, so D K chunks and D/2 V chunks fit the 256 threads).
+    const int q = (int)threadIdx.x;
+    if (q < p.D) {
+        // K panel [D/8][16][8]: the D/8 lines of the row's 8-row half; chunk (c, j) is piece c of row (row & 8) + j
+        const int c = q >> 3, j = q & 7;
+        f16x8 *dst = reinterpret_cast<f16x8 *>(p.k_pool + panel + ((row & 8) + c * 16 + j) * 8);
+        *dst = (j == (row & 7)) ? *reinterpret_cast<const f16x8 *>(kn + 8 * c) : *dst;
+    }
+    if (q < p.D / 2) {
+        // V panel [4][D][4]: the row's quad; chunk q holds dims 2q (its first 8 bytes) and 2q + 1 (its last 8), four
+        // rows each, so the row is 16-bit field row % 4 of both halves
+        uint64_t *dst = reinterpret_cast<uint64_t *>(p.v_pool + panel + (row >> 2) * 4 * p.D + 8 * q);
+        const int sh = 16 * (row & 3);
+        const uint64_t keep = ~(0xFFFFull << sh);
+        const uint16_t *vbits = reinterpret_cast<const uint16_t *>(vn);
+        const uint64_t a = dst[0], b = dst[1];
+        dst[0] = (a & keep) | ((uint64_t)vbits[2 * q] << sh);
+        dst[1] = (b & keep) | ((uint64_t)vbits[2 * q + 1] << sh);
     }
 }
 
@@ -954,10 +958,11 @@ __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, cons
     const int prow = off % 16;
     *reinterpret_cast<uint4 *>(p.k_pool + panel + ((int64_t)c * 16 + prow) * 8) = kv;
     const uint16_t *vh = reinterpret_cast<const uint16_t *>(&vv);
-    uint16_t *vdst = reinterpret_cast<uint16_t *>(p.v_pool + panel + (int64_t)(8 * c) * 16 + prow);
+    uint16_t *vdst = reinterpret_cast<uint16_t *>(p.v_pool + panel + (int64_t)(prow >> 2) * 4 * p.D + 32 * c +
+                                                  (prow & 3));
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        vdst[e * 16] = vh[e];
+        vdst[e * 4] = vh[e];
 }
 
 // The varlen step's append in whole panels: workgroup (s, h, j) takes the j-th 16-row unit that sequence s's new
@@ -998,7 +1003,9 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
     const int e = (int)((hi < r0 + 16 ? hi : r0 + 16) - r0);
     const int64_t panel = ((int64_t)b * p.Hkv + h) * p.BS * p.D + (r0 % p.BS) * p.D;
     // The panels' chunks that keep old rows, read before the staging so both sets of loads are in flight together.
-    // K panel [D/8][16][8]: chunk q is piece q/16 of row q%16.  V panel [D][16]: chunk q is dim q/2, rows 8*(q%2)..+8.
+    // K panel [D/8][16][8]: chunk q is piece q/16 of row q%16.  V panel [4][D][4]: chunk q is dims 2*(q % (D/2))
+    // and the next of quad q / (D/2), i.e. of rows 4*(q / (D/2)) .. +4.
+    const int qpd = p.D / 2;  // V chunks per quad
     f16x8 kc[2] = {}, vc[2] = {};
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -1007,8 +1014,8 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
             const int kr = q % 16;
             if (kr < a || kr >= e)
                 kc[it] = *reinterpret_cast<const f16x8 *>(p.k_pool + panel + 8 * q);
-            const int vr = 8 * (q & 1);
-            if (vr < a || vr + 8 > e)
+            const int vr = 4 * (q / qpd);
+            if (vr < a || vr + 4 > e)
                 vc[it] = *reinterpret_cast<const f16x8 *>(p.v_pool + panel + 8 * q);
         }
     }
@@ -1034,12 +1041,13 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
             if (kr >= a && kr < e)
                 kc[it] = kst[kr * pieces + q / 16];
             *reinterpret_cast<f16x8 *>(p.k_pool + panel + 8 * q) = kc[it];
-            const int vr = 8 * (q & 1);
-            const int dim = q / 2;
+            const int vq = q / qpd, d0 = 2 * (q - vq * qpd);
 #pragma unroll
-            for (int x = 0; x < 8; ++x)
-                if (vr + x >= a && vr + x < e)
-                    vc[it][x] = vsh[(vr + x) * p.D + dim];
+            for (int x = 0; x < 8; ++x) {  // element x: dim d0 + x / 4 of row 4 * vq + x % 4
+                const int vr = 4 * vq + (x & 3);
+                if (vr >= a && vr < e)
+                    vc[it][x] = vsh[vr * p.D + d0 + (x >> 2)];
+            }
             *reinterpret_cast<f16x8 *>(p.v_pool + panel + 8 * q) = vc[it];
         }
     }
@@ -1083,10 +1091,12 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
     const int nb = M < kBlocks ? M : kBlocks;
     constexpr int kPer = (kBlocks + 3) / 4;
     int ids[kPer];
+    // clamped into the table, so every load is unconditional (entries past nb and rows past B are never stored)
+    const int32_t *trow = block_tables + (int64_t)(s < B ? s : B - 1) * M;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int i = part + 4 * k;
-        ids[k] = (s < B && i < nb) ? block_tables[(int64_t)s * M + i] : 0;
+        ids[k] = nb > 0 ? trow[i < nb ? i : nb - 1] : 0;
     }
     __syncthreads();
     if (s >= B)

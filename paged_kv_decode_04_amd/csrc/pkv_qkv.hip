@@ -26,10 +26,10 @@
 //     and a v_permlane16_swap for 32-lane groups);
 //   * q goes straight to q_out (8-byte stores, coalesced per half head row).  The unit's new K rows are staged in
 //     LDS in the pool's panel layout (rows XOR-swizzled per piece), its V rows row-major (padded rows); each
-//     thread then writes 16-byte chunks of the two panels (V transposed on the way), taking rows outside the new
-//     range from the old panel, which it loaded at the start (so that load overlaps everything else).  The pools
-//     thus see only whole 16-byte chunks of whole panels -- scattered 2-byte V stores and 16-byte K row pieces
-//     cost far more at the memory than their bytes;
+//     thread then writes 16-byte chunks of the two panels (V put in its quad order on the way), taking rows
+//     outside the new range from the old panel, which it loaded at the start (so that load overlaps everything
+//     else).  The pools thus see only whole 16-byte chunks of whole panels -- scattered 2-byte V stores and
+//     16-byte K row pieces cost far more at the memory than their bytes;
 //   * decode mode (decode_lens set): slot g is sequence g, whose one new token sits at row decode_lens[g] - 1 --
 //     the QKV half of the decode step from QKV rows when it runs as two launches.
 //
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
             source(idx, rr, hs, piece);
             const int rin = r0 + rr;
             if (hs > p.G) {
-                // value head: staged row-major, transposed into the panel layout on the way out
+                // value head: staged row-major, put into the panel's quad order on the way out
                 const h8 v = raw[b];
                 *reinterpret_cast<h4 *>(sv + rin * VS + 4 * piece) = h4{v[0], v[1], v[2], v[3]};
                 *reinterpret_cast<h4 *>(sv + rin * VS + HALF + 4 * piece) = h4{v[4], v[5], v[6], v[7]};
@@ -307,16 +307,19 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
             *reinterpret_cast<h8 *>(p.k_pool + panel + 8 * q) = knew ? kn : ok[c];
         }
         if (has_v) {
-            // V chunk q: dim q / 2, rows 8 * (q % 2) .. + 8
-            const int vd = q >> 1, vr = 8 * (q & 1);
+            // V panel [4][D][4], chunk q: dims d0 = 2 * (q % (D/2)) and d0 + 1 of quad q / (D/2); element x is dim
+            // d0 + x / 4 of row 4 * (q / (D/2)) + x % 4
+            const int vq = q / (D / 2), d0 = 2 * (q % (D / 2));
             h8 vn;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                vn[e] = sv[(vr + e) * VS + vd];
+            for (int x = 0; x < 8; ++x)
+                vn[x] = sv[(4 * vq + (x & 3)) * VS + d0 + (x >> 2)];
             if (!whole) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    vn[e] = (vr + e >= r0 && vr + e < r0 + rows) ? vn[e] : ov[c][e];
+                for (int x = 0; x < 8; ++x) {
+                    const int vr = 4 * vq + (x & 3);
+                    vn[x] = (vr >= r0 && vr < r0 + rows) ? vn[x] : ov[c][x];
+                }
             }
             *reinterpret_cast<h8 *>(p.v_pool + panel + 8 * q) = vn;
         }

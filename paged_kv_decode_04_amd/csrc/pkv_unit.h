@@ -76,13 +76,18 @@ struct Frag {
 //     4c + g4 -- sits at byte 1024*c + 16*(16*g4 + r) = 1024*c + 16*lane: each wave load is one contiguous 1 KB
 //     run of whole cache lines (a row-major tile would touch sixteen half lines per load, which caps one CU at
 //     about a third of the rate it reaches on whole lines);
-//   V panel [D][16] (V transposed): lane (g4, r) reads dims 16c + r, rows 4*g4 .. +3 at byte
-//     512*c + 32*r + 8*g4: each wave load is one contiguous 512-byte run.
+//   V panel [4][D][4] (four quads of 4 rows; in a quad each dim's 4 rows are adjacent): lane (g4, r) reads dims
+//     16c + r, rows 4*g4 .. +3 -- quad g4 -- at byte 8*(g4*D + r) + 128*c: each wave load is four whole 128-byte
+//     lines, one per quad.  A new row then touches D/4 of the panel's 32-byte sectors (4 dims in each), where a
+//     dim-major [D][16] panel, equally good to load, would put each of its D values in a sector of its own;
+//   v_lane_offset() below gives the lane's byte offset.
 // kb / vb are wave-uniform pointers to the panel; each becomes a buffer resource built on the scalar unit, and the
 // lane's loop-invariant byte offsets (k_lane, v_lane) are the only VGPR operands, so no per-unit address arithmetic
 // lands in vector registers that loads in flight still own.  The resource's record count is the panel's size: an
 // offset past it reads 0.
 constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, no swizzle (gfx9 family)
+constexpr int kVGroupBytes = 128;       // V bytes of 16 dims of one quad: the step between a lane's V loads
+__host__ __device__ constexpr uint32_t v_lane_offset(int D, int r, int g4) { return (uint32_t)(8 * (g4 * D + r)); }
 // Cache-policy bits of the streamed K/V loads: nt (non-temporal).  K and V are read once per step, and the hint
 // keeps them from displacing lines that are reused (measured on MI355X: 17% faster on the Llama-3-8B-shaped batch,
 // 11% on the long-context split; the coherence-scope bits change nothing once it is set).
@@ -106,7 +111,7 @@ __device__ __forceinline__ void load_unit(Frag<D, BS> &f, const _Float16 *kb, co
                                                                                  kKvLoadPolicy));
 #pragma unroll
     for (int c = 0; c < Frag<D, BS>::VC; ++c)
-        f.v[c] = __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(vr, v_lane, 512 * c,
+        f.v[c] = __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(vr, v_lane, kVGroupBytes * c,
                                                                                 kKvLoadPolicy));
 }
 
@@ -122,8 +127,8 @@ struct RowLimits {
 };
 
 // The fused varlen step's pool update for one loaded 16-row unit: rows prow .. prow_end-1 are new -- their K and V
-// taken from the workgroup's LDS copy of the unit (sk: [16][D] row-major; sv: [D][16], the V panel's own order, so
-// a lane's four rows of one dim are one 8-byte read) -- and the patched fragment is written back whole to the
+// taken from the workgroup's LDS copy of the unit (sk: [16][D] row-major; sv: [D][16] dim-major, so a lane's four
+// rows of one dim are one 8-byte read) -- and the patched fragment is written back whole to the
 // unit's panels (wb_k, wb_v), its other rows with the values just loaded.  A dead unit is patched (its rows are
 // masked anyway) but not written.
 template <int D, int BS>
@@ -154,7 +159,7 @@ __device__ __forceinline__ void patch_unit_rows(Frag<D, BS> &f, int prow, int pr
             *reinterpret_cast<f16x8 *>(reinterpret_cast<char *>(wb_k) + k_lane + 1024 * c) = f.k[c];
 #pragma unroll
         for (int c = 0; c < VC; ++c)
-            *reinterpret_cast<f16x4 *>(reinterpret_cast<char *>(wb_v) + v_lane + 512 * c) = f.v[c];
+            *reinterpret_cast<f16x4 *>(reinterpret_cast<char *>(wb_v) + v_lane + kVGroupBytes * c) = f.v[c];
     }
 }
 
@@ -196,7 +201,7 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
                 *reinterpret_cast<f16x8 *>(reinterpret_cast<char *>(wb_k) + k_lane + 1024 * c) = f.k[c];
 #pragma unroll
             for (int c = 0; c < VC; ++c)
-                *reinterpret_cast<f16x4 *>(reinterpret_cast<char *>(wb_v) + v_lane + 512 * c) = f.v[c];
+                *reinterpret_cast<f16x4 *>(reinterpret_cast<char *>(wb_v) + v_lane + kVGroupBytes * c) = f.v[c];
         }
     }
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};

@@ -170,14 +170,14 @@ def _dev(t, dtype, name: str, ndim: Optional[int] = None):
 def _pool(k_pool, v_pool) -> PoolDesc:
     import torch
     _dev(k_pool, torch.float16, "k_pool", 6)
-    _dev(v_pool, torch.float16, "v_pool", 5)
+    _dev(v_pool, torch.float16, "v_pool", 6)
     N, Hkv, NP, D8, sixteen, eight = k_pool.shape
     D, BS = D8 * 8, NP * 16
     if (sixteen, eight) != (16, 8):
         raise ValueError("k_pool must be [N][Hkv][BS/16][D/8][16][8], got %s" % (tuple(k_pool.shape),))
-    if tuple(v_pool.shape) != (N, Hkv, NP, D, 16):
-        raise ValueError("v_pool must be [N][Hkv][BS/16][D][16] = %s, got %s"
-                         % ((N, Hkv, NP, D, 16), tuple(v_pool.shape)))
+    if tuple(v_pool.shape) != (N, Hkv, NP, 4, D, 4):
+        raise ValueError("v_pool must be [N][Hkv][BS/16][4][D][4] = %s, got %s"
+                         % ((N, Hkv, NP, 4, D, 4), tuple(v_pool.shape)))
     return PoolDesc(Hkv, D, BS, N)
 
 

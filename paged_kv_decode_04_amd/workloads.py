@@ -6,7 +6,7 @@ tables, slot mappings); it holds none of the attention arithmetic and imports ne
 
 Pool layouts, fixed by the library's header (each block is BS/16 panels of 16 rows):
     k_pool[N][Hkv][BS/16][D/8][16][8] fp16  (a panel holds each row's dims in 8-wide pieces, piece-major)
-    v_pool[N][Hkv][BS/16][D][16] fp16       (a panel holds V transposed, dim-major)
+    v_pool[N][Hkv][BS/16][4][D][4] fp16     (a panel holds four quads of 4 rows, each dim's 4 rows adjacent)
 Use k_row / v_row / set_k_row / set_v_row to address one token row.
 
 Randomness: numpy PCG64 streams keyed by ``SeedSequence([seed, rotation, tag])``; large arrays are filled in fixed
@@ -97,7 +97,7 @@ class DecodeCase:
     block_tables: np.ndarray           # [B][M] int32
     q: Optional[np.ndarray] = None      # [B][Hq][D] fp16
     k_pool: Optional[np.ndarray] = None  # [N][Hkv][BS/16][D/8][16][8] fp16
-    v_pool: Optional[np.ndarray] = None  # [N][Hkv][BS/16][D][16] fp16
+    v_pool: Optional[np.ndarray] = None  # [N][Hkv][BS/16][4][D][4] fp16
     k_new: Optional[np.ndarray] = None   # [T][Hkv][D] fp16, the rows appended this step
     v_new: Optional[np.ndarray] = None   # [T][Hkv][D] fp16
     slot_mapping: Optional[np.ndarray] = None  # [T] int32
@@ -147,14 +147,22 @@ def poison_rows(k_pool: np.ndarray, v_pool: np.ndarray, slots: np.ndarray, BS: i
             continue
         b, o = int(slot) // BS, int(slot) % BS
         k_pool[b, :, o // 16, :, o % 16, :] = POISON
-        v_pool[b, :, o // 16, :, o % 16] = POISON
+        v_pool[b, :, o // 16, (o % 16) // 4, :, o % 4] = POISON
+
+
+def k_pool_shape(N: int, Hkv: int, BS: int, D: int) -> tuple:
+    return (N, Hkv, BS // 16, D // 8, 16, 8)
+
+
+def v_pool_shape(N: int, Hkv: int, BS: int, D: int) -> tuple:
+    return (N, Hkv, BS // 16, 4, D, 4)
 
 
 def _alloc_pools(N, Hkv, BS, D):
     if BS % 16 or D % 8:
         raise ValueError("block_size must be a multiple of 16 and head_dim a multiple of 8")
-    return (np.empty((N, Hkv, BS // 16, D // 8, 16, 8), dtype=np.float16),
-            np.empty((N, Hkv, BS // 16, D, 16), dtype=np.float16))
+    return (np.empty(k_pool_shape(N, Hkv, BS, D), dtype=np.float16),
+            np.empty(v_pool_shape(N, Hkv, BS, D), dtype=np.float16))
 
 
 def k_row(k_pool: np.ndarray, block: int, head: int, offset: int) -> np.ndarray:
@@ -163,7 +171,7 @@ def k_row(k_pool: np.ndarray, block: int, head: int, offset: int) -> np.ndarray:
 
 
 def v_row(v_pool: np.ndarray, block: int, head: int, offset: int) -> np.ndarray:
-    return v_pool[block, head, offset // 16, :, offset % 16]
+    return v_pool[block, head, offset // 16, (offset % 16) // 4, :, offset % 4]
 
 
 def set_k_row(k_pool: np.ndarray, block: int, head, offset: int, row) -> None:
@@ -173,7 +181,7 @@ def set_k_row(k_pool: np.ndarray, block: int, head, offset: int, row) -> None:
 
 
 def set_v_row(v_pool: np.ndarray, block: int, head, offset: int, row) -> None:
-    v_pool[block, head, offset // 16, :, offset % 16] = np.asarray(row, dtype=np.float16)
+    v_pool[block, head, offset // 16, (offset % 16) // 4, :, offset % 4] = np.asarray(row, dtype=np.float16)
 
 
 def build_case(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int, context_lens, N: int, M: int, scale: float,

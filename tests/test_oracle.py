@@ -42,7 +42,7 @@ def _pad8(x, D):
 
 def _zero_pools(N, Hkv, BS, D):
     return (np.zeros((N, Hkv, BS // 16, D // 8, 16, 8), dtype=np.float16),
-            np.zeros((N, Hkv, BS // 16, D, 16), dtype=np.float16))
+            np.zeros(W.v_pool_shape(N, Hkv, BS, D), dtype=np.float16))
 
 
 def _pools_from_rows(case):
@@ -73,11 +73,12 @@ def test_pool_index_functions_match_numpy_strides():
     rng = np.random.default_rng(7)
     for (N, Hkv, BS, D) in [(5, 3, 16, 64), (2, 1, 32, 256), (7, 8, 16, 128), (3, 2, 64, 8)]:
         k = np.empty((N, Hkv, BS // 16, D // 8, 16, 8), dtype=np.float16)
-        v = np.empty((N, Hkv, BS // 16, D, 16), dtype=np.float16)
+        v = np.empty(W.v_pool_shape(N, Hkv, BS, D), dtype=np.float16)
         for _ in range(50):
             b, h, o, d = (int(rng.integers(N)), int(rng.integers(Hkv)), int(rng.integers(BS)), int(rng.integers(D)))
             assert oracle.k_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(k.strides, (b, h, o // 16, d // 8, o % 16, d % 8))
-            assert oracle.v_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(v.strides, (b, h, o // 16, d, o % 16))
+            assert oracle.v_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(v.strides,
+                                                                        (b, h, o // 16, (o % 16) // 4, d, o % 4))
 
 
 def test_row_helpers_round_trip():
@@ -278,7 +279,7 @@ def _contiguous_problem(seed, B, Hq, Hkv, D, BS, lens, scale):
     perm = rng.permutation(N).astype(np.int32)
     bt = np.full((B, M), -1, np.int32)
     k_pool = rng.standard_normal((N, Hkv, BS // 16, D // 8, 16, 8)).astype(np.float16)
-    v_pool = rng.standard_normal((N, Hkv, BS // 16, D, 16)).astype(np.float16)
+    v_pool = rng.standard_normal(W.v_pool_shape(N, Hkv, BS, D)).astype(np.float16)
     q = rng.standard_normal((B, Hq, D)).astype(np.float16)
     Kc, Vc = [], []
     pos = 0
@@ -392,7 +393,7 @@ def test_append_writes_rows_and_leaves_everything_else():
     rng = np.random.default_rng(31)
     N, Hkv, BS, D, T = 9, 3, 32, 64, 20
     k_pool = rng.standard_normal((N, Hkv, BS // 16, D // 8, 16, 8)).astype(np.float16)
-    v_pool = rng.standard_normal((N, Hkv, BS // 16, D, 16)).astype(np.float16)
+    v_pool = rng.standard_normal(W.v_pool_shape(N, Hkv, BS, D)).astype(np.float16)
     k0, v0 = k_pool.copy(), v_pool.copy()
     slots = rng.choice(N * BS, size=T, replace=False).astype(np.int32)
     slots[3] = -1
