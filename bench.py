@@ -15,6 +15,7 @@ Infinity Cache cannot hold a step's working set (R=4 for c2).
     python bench.py [--steps K] [--warmup W] [--config c2] [--splits S] [--rotations R] [--no-cpu-baseline]
     python bench.py --copy-calibration-mib 512 ...     also runs a plain copy kernel (torch.neg, out=) of known size
     python bench.py --summarize-pmc FETCH.csv WRITE.csv --config c2   writes profiles/traffic_<config>_s<S>.json
+    python bench.py --summarize-counters COUNTERS.csv                  mean per dispatch of each counter, per kernel
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value        algorithmic HBM bytes of a step / measured step time, in GB/s (whole job, one GPU)
@@ -206,6 +207,23 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str, splits: int, copy
     return out
 
 
+def summarize_counters(path: str) -> dict:
+    """Mean value per dispatch of every counter in a rocprofv3 --pmc CSV, per kernel (pkv kernels by their short
+    name, others by the start of theirs), with the dispatch count."""
+    import csv
+    with open(path) as f:
+        counters = sorted({r["Counter_Name"] for r in csv.DictReader(f)})
+    out = {}
+    for counter in counters:
+        for name, val in _pmc_per_dispatch(path, counter).values():
+            short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+            short = short if "pkv::" in short else short[:60]
+            rec = out.setdefault(short, {})
+            rec.setdefault(counter, []).append(val)
+    return {k: dict({c: sum(v) / len(v) for c, v in cs.items()}, dispatches=max(len(v) for v in cs.values()))
+            for k, cs in out.items()}
+
+
 def _host_cpu() -> dict:
     """The host's logical CPU count and model name (from /proc/cpuinfo, where readable)."""
     model = None
@@ -289,6 +307,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration-mib", type=float, default=0.0,
                     help="also run a plain copy kernel over this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="print the mean per dispatch of every counter in a rocprofv3 --pmc CSV, per kernel")
     ap.add_argument("--pmc-steps", type=int, nargs=2, default=(50, 10), metavar=("STEPS", "WARMUP"),
                     help="with --summarize-pmc: the --steps/--warmup of the counter runs, for the recorded commands")
     ap.add_argument("--unfused", action="store_true",
@@ -296,6 +316,10 @@ def main(argv=None) -> int:
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph holding 32 consecutive steps instead of eager launches")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return 0
 
     if args.summarize_pmc:
         splits = WORKLOADS[args.config][1] if args.splits is None else args.splits
