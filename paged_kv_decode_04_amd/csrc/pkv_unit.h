@@ -233,22 +233,19 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
         pe[e] = exp2_fast(y[e] - m_new);
     l_run = l_run * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
     m_run = m_new;
-    // The weights enter the f16 matrix-core product as two halves, p = hi + lo with hi = fp16(p) and
-    // lo = fp16(p - hi) (the difference is exact in f32): one fp16 rounding alone moves a weight by up to 2^-11 of
-    // itself, and weights sitting just off rounding midpoints with V signs that follow the rounding direction add
-    // up to 2^-11 * max|v| of error in the output; with the low half the weights are good to about 2^-22.  The
-    // second product costs matrix-core cycles only, which this memory-bound loop has to spare.
-    f16x4 ph, pl;
+    // The weights enter the f16 matrix-core product rounded once to fp16 (l keeps the f32 sum): a weight moves by up
+    // to 2^-11 of itself, the output by at most 2^-11 * max|v| when every weight sits just off a rounding midpoint
+    // and V's signs follow the rounding directions, and far less otherwise -- the size of the fp16 output's own
+    // rounding.  Carrying the rounding residue as a second fp16 product removed it but cost 0.6% on the
+    // Llama-3-8B-shaped step and 4.7% on the two-tile varlen step.
+    f16x4 pf;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        ph[e] = (_Float16)pe[e];
-        pl[e] = (_Float16)(pe[e] - (float)ph[e]);
-    }
+    for (int e = 0; e < 4; ++e)
+        pf[e] = (_Float16)pe[e];
 #pragma unroll
     for (int c = 0; c < VC; ++c) {
         o[c] *= alpha;
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(f.v[c], ph, o[c], 0, 0, 0);
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(f.v[c], pl, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(f.v[c], pf, o[c], 0, 0, 0);
     }
 }
 
