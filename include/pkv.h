@@ -42,7 +42,7 @@
  * Layouts
  * -------
  *    q, out        [num_seqs][num_q_heads][head_dim]            fp16
- *    k_pool        [num_blocks][num_kv_heads][block_size/16][head_dim/8][16][8]  fp16
+ *    k_pool        [num_blocks][num_kv_heads][block_size/16][head_dim/32][16][32]  fp16
  *    v_pool        [num_blocks][num_kv_heads][block_size/16][4][head_dim][4]     fp16
  *    block_tables  [num_seqs][max_blocks_per_seq]                int32
  *    context_lens  [num_seqs]                                    int32
@@ -50,13 +50,14 @@
  *    slot_mapping  [num_tokens]                                  int32
  *  The pages fix no pool layout.  Each (block, kv head) tile is one contiguous
  *  run of block_size*head_dim values, stored as block_size/16 panels of 16
- *  rows.  A K panel holds the 16 rows' dims in 8-wide pieces, piece-major
- *  (element (row r, dim d) at ((d/8)*16 + r)*8 + d%8); a V panel holds four
+ *  rows.  A K panel holds the 16 rows' dims in 32-wide pieces, piece-major
+ *  (element (row r, dim d) at ((d/32)*16 + r)*32 + d%32); a V panel holds four
  *  quads of 4 rows, and in a quad each dim's 4 rows side by side (element
  *  (r, d) at ((r/4)*head_dim + d)*4 + r%4).  With this layout every operand
  *  the decode kernel feeds to the matrix cores is whole cache lines (one 1 KB
  *  run per K load, four 128-byte runs per V load of a wavefront), and a new
- *  row written into a panel touches head_dim/4 of its 32-byte V sectors.
+ *  row written into a panel is head_dim/32 runs of 64 bytes in K and touches
+ *  head_dim/16 lines (head_dim/4 32-byte sectors) in V.
  *  K/V row t of a tile is in panel t/16, row t%16.
  *
  *  context_lens[s] counts the rows of sequence s including the token being
@@ -71,7 +72,7 @@
  *
  * Compiled geometries: head_dim in {64, 128, 256}, block_size in {16, 32, 64},
  * group size G = num_q_heads / num_kv_heads in 1..16.  The append needs
- * head_dim % 8 == 0 and block_size % 16 == 0.
+ * head_dim % 32 == 0 and block_size % 16 == 0 (the K panel's 32-dim pieces).
  */
 #ifndef PKV_H
 #define PKV_H
@@ -124,8 +125,8 @@ typedef struct {
  *   and offsets); the slot = physical_block * block_size + pos_in_block form
  *   folds the two per-token arrays into one]
  *   k, v: [num_tokens][Hkv][D] fp16, 16-byte aligned.  num_tokens == 0 is a
- *   no-op.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED (D not a multiple of 8 or BS not a
- *   multiple of 16),
+ *   no-op.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED (D not a multiple of 32 or BS
+ *   not a multiple of 16),
  *   PKV_EHIP.
  * ------------------------------------------------------------------------- */
 PKV_API int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping,

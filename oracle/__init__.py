@@ -107,7 +107,7 @@ def f16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def k_index(num_kv_heads, block_size, head_dim, block, head, offset, dim) -> int:
-    """Flat index of K element (block, kv head, row offset, dim) in k_pool[N][Hkv][BS/16][D/8][16][8]."""
+    """Flat index of K element (block, kv head, row offset, dim) in k_pool[N][Hkv][BS/16][D/32][16][32]."""
     return _load().oracle_k_index(num_kv_heads, block_size, head_dim, block, head, offset, dim)
 
 
@@ -118,9 +118,9 @@ def v_index(num_kv_heads, block_size, head_dim, block, head, offset, dim) -> int
 
 def _geometry(q, k_pool, v_pool, block_tables, context_lens):
     B, Hq, D = q.shape
-    N, Hkv, NP, D8, sixteen, eight = k_pool.shape
+    N, Hkv, NP, D32, sixteen, w32 = k_pool.shape
     BS = NP * 16
-    if (sixteen, eight) != (16, 8) or D8 * 8 != D or v_pool.shape != (N, Hkv, NP, 4, D, 4):
+    if (sixteen, w32) != (16, 32) or D32 * 32 != D or v_pool.shape != (N, Hkv, NP, 4, D, 4):
         raise ValueError("pool shapes %s / %s do not match q %s" % (k_pool.shape, v_pool.shape, q.shape))
     bt = _i32(block_tables)
     if bt.ndim != 2 or bt.shape[0] != B:
@@ -134,7 +134,7 @@ def _geometry(q, k_pool, v_pool, block_tables, context_lens):
 def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale, units=None, threads=None, window=0):
     """out[B][Hq][D] (or out[len(units)][D] for a list of (s, hq) units) in float64.
 
-    q: [B][Hq][D] fp16; k_pool: [N][Hkv][BS/16][D/8][16][8] fp16; v_pool: [N][Hkv][BS/16][4][D][4] fp16;
+    q: [B][Hq][D] fp16; k_pool: [N][Hkv][BS/16][D/32][16][32] fp16; v_pool: [N][Hkv][BS/16][4][D][4] fp16;
     block_tables: [B][M] int32; context_lens: [B] int32 (rows including the newest token).
     window > 0: each new row attends only its sequence's last `window` rows (sliding-window decode).
     """
@@ -214,9 +214,9 @@ def paged_kv_append(k, v, slot_mapping, k_pool, v_pool) -> int:
     """In-place append of k, v ([T][Hkv][D] fp16) into the pools; returns the number of skipped slots."""
     kb, vb = _bits(k), _bits(v)
     T, Hkv, D = kb.shape
-    N, Hkv2, NP, D8, sixteen, eight = k_pool.shape
+    N, Hkv2, NP, D32, sixteen, w32 = k_pool.shape
     BS = NP * 16
-    if (Hkv2, D8 * 8, sixteen, eight) != (Hkv, D, 16, 8) or v_pool.shape != (N, Hkv, NP, 4, D, 4):
+    if (Hkv2, D32 * 32, sixteen, w32) != (Hkv, D, 16, 32) or v_pool.shape != (N, Hkv, NP, 4, D, 4):
         raise ValueError("pool shapes do not match k/v")
     if not (k_pool.flags.c_contiguous and v_pool.flags.c_contiguous):
         raise ValueError("pools must be C-contiguous (updated in place)")
@@ -238,9 +238,9 @@ def varlen_attention(q, k_pool, v_pool, block_tables, cu_seqlens_q, pos_offsets,
     at position pos_offsets[s] + i attends rows 0 .. pos_offsets[s] + i.  Pools and block_tables as decode_attention.
     """
     T, Hq, D = q.shape
-    N, Hkv, NP, D8, sixteen, eight = k_pool.shape
+    N, Hkv, NP, D32, sixteen, w32 = k_pool.shape
     BS = NP * 16
-    if (sixteen, eight) != (16, 8) or D8 * 8 != D or v_pool.shape != (N, Hkv, NP, 4, D, 4):
+    if (sixteen, w32) != (16, 32) or D32 * 32 != D or v_pool.shape != (N, Hkv, NP, 4, D, 4):
         raise ValueError("pool shapes %s / %s do not match q %s" % (k_pool.shape, v_pool.shape, q.shape))
     bt = _i32(block_tables)
     cu = _i32(cu_seqlens_q)
@@ -274,15 +274,15 @@ def qkv_norm_rope_paged(qkv, q_norm_w, k_norm_w, cos, sin, cu_seqlens_q, rope_po
     qkv: [T][(Hq + 2*Hkv)*D] fp16; q_norm_w, k_norm_w: [D] fp16 (ignored when qk_mode == 0, may be None);
     cos, sin: [P][D/2] float32 tables; sequence s owns tokens cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1, its i-th at
     RoPE position rope_pos[s] + i and cache row cache_pos[s] + i; eps is taken as a float32 (as the step receives
-    it).  k_pool gives the geometry only; v_pool
+    it).  k_pool gives the geometry only (its piece axis is D // 32, empty for D < 32); v_pool
     (C-contiguous fp16) receives the value rows in place.  Returns (q_out [T][Hq][D] f64, k_rows [T][Hkv][D] f64,
     slots [T] int64 = block * BS + offset of each token's cache row).
     """
     qb = _bits(qkv)
     T, width = qb.shape
-    N, Hkv, NP, D8, sixteen, eight = k_pool.shape
-    BS, D = NP * 16, D8 * 8
-    if (sixteen, eight) != (16, 8) or v_pool.shape != (N, Hkv, NP, 4, D, 4) or width % D:
+    N, Hkv, NP, four, D, four2 = v_pool.shape
+    BS = NP * 16
+    if (four, four2) != (4, 4) or k_pool.shape != (N, Hkv, NP, D // 32, 16, 32) or width % D:
         raise ValueError("pool shapes %s / %s do not match qkv %s" % (k_pool.shape, v_pool.shape, qb.shape))
     Hq = width // D - 2 * Hkv
     if Hq <= 0:

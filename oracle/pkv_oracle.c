@@ -45,14 +45,14 @@
  * Pool layouts (the pages do not fix one; this library and the HIP library
  * both document the same two).  Each block of block_size rows is stored as
  * block_size/16 panels of 16 rows:
- *    k_pool[num_blocks][num_kv_heads][block_size/16][head_dim/8][16][8]
- *           (a panel holds each row's dims in 8-wide pieces: piece 0 of the
- *           16 rows, then piece 1, ...)
+ *    k_pool[num_blocks][num_kv_heads][block_size/16][head_dim/32][16][32]
+ *           (a panel holds each row's dims in 32-wide pieces: dims 0..31
+ *           of the 16 rows, then dims 32..63, ...)
  *    v_pool[num_blocks][num_kv_heads][block_size/16][4][head_dim][4]
  *           (a panel holds V in four quads of 4 rows; in a quad each
  *           dim's 4 rows are adjacent: dim 0 of rows 4i..4i+3, then dim 1,
  *           ...)
- * head_dim must be a multiple of 8 and block_size a multiple of 16.
+ * head_dim must be a multiple of 32 and block_size a multiple of 16.
  *
  * All arithmetic is IEEE binary64; fp16 inputs are decoded exactly.  No
  * blocking, fusion or reordering beyond the definitions above.
@@ -95,7 +95,7 @@ void oracle_f16_array_to_f64(const uint16_t *src, int64_t n, double *dst)
 
 typedef struct {
     const uint16_t *q;            /* [B][Hq][D] fp16 bits */
-    const uint16_t *k_pool;       /* [N][Hkv][BS/16][D/8][16][8] fp16 bits */
+    const uint16_t *k_pool;       /* [N][Hkv][BS/16][D/32][16][32] fp16 bits */
     const uint16_t *v_pool;       /* [N][Hkv][BS/16][4][D][4] fp16 bits */
     const int32_t *block_tables;  /* [B][M] */
     const int32_t *context_lens;  /* [B] */
@@ -104,11 +104,11 @@ typedef struct {
     int32_t window;               /* sliding window: > 0 attends only the last `window` rows; 0 = all rows */
 } oracle_problem;
 
-/* k_pool element (block b, kv head h, row offset o, dim d): panel o / 16, piece d / 8, row o % 16, lane d % 8 */
+/* k_pool element (block b, kv head h, row offset o, dim d): panel o / 16, piece d / 32, row o % 16, dim d % 32 */
 static int64_t k_index(const oracle_problem *P, int64_t b, int h, int o, int d)
 {
     int64_t panel = (b * P->Hkv + h) * (P->BS / 16) + o / 16;
-    return ((panel * (P->D / 8) + d / 8) * 16 + o % 16) * 8 + d % 8;
+    return ((panel * (P->D / 32) + d / 32) * 16 + o % 16) * 32 + d % 32;
 }
 
 /* v_pool element (block b, kv head h, row offset o, dim d): panel o / 16, quad (o % 16) / 4, dim d, row o % 4 */
@@ -279,7 +279,7 @@ static int check_geometry(const oracle_problem *P)
 {
     if (P->B < 0 || P->Hq <= 0 || P->Hkv <= 0 || P->D <= 0 || P->BS <= 0 || P->N < 0 || P->M < 0)
         return -1;
-    if (P->Hq % P->Hkv || P->D % 8 || P->BS % 16)
+    if (P->Hq % P->Hkv || P->D % 32 || P->BS % 16)
         return -1;
     return 0;
 }
@@ -476,7 +476,7 @@ int64_t oracle_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32
                                int32_t T, int32_t Hkv, int32_t D, int32_t BS, int32_t N,
                                uint16_t *k_pool, uint16_t *v_pool)
 {
-    if (T < 0 || Hkv <= 0 || D <= 0 || D % 8 || BS <= 0 || BS % 16 || N < 0)
+    if (T < 0 || Hkv <= 0 || D <= 0 || D % 32 || BS <= 0 || BS % 16 || N < 0)
         return -1;
     oracle_problem P;
     memset(&P, 0, sizeof P);

@@ -920,8 +920,8 @@ int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slo
         return rc;
     if (num_tokens < 0)
         return fail(PKV_EINVAL, "num_tokens must be >= 0 (got %d)", num_tokens);
-    if (pool.head_dim % 8 != 0 || pool.block_size % 16 != 0)
-        return fail(PKV_EUNSUPPORTED, "head_dim %d must be a multiple of 8 and block_size %d a multiple of 16",
+    if (pool.head_dim % 32 != 0 || pool.block_size % 16 != 0)
+        return fail(PKV_EUNSUPPORTED, "head_dim %d must be a multiple of 32 and block_size %d a multiple of 16",
                     pool.head_dim, pool.block_size);
     if (num_tokens == 0)
         return ok();

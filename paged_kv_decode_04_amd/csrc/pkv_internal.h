@@ -26,7 +26,7 @@ struct DecodeParams {
     int32_t chunk_blocks;         // > 0 fixed blocks per split, 0 = ceil(blocks in range / S) per sequence
     float scale_log2;             // scale * log2(e)
     int32_t window;               // > 0: attend only the last `window` rows of each sequence; 0 = all rows
-    const _Float16 *k_pool;       // [N][Hkv][BS/16][D/8][16][8]
+    const _Float16 *k_pool;       // [N][Hkv][BS/16][D/32][16][32]
     const _Float16 *v_pool;       // [N][Hkv][BS/16][4][D][4]
     _Float16 *out;                // [B][Hq][D]            (single pass)
     float *part_o;                // [B][Hq][S][D]         (split-K)

@@ -22,9 +22,10 @@
 //     probabilities never leave registers.  Query heads beyond G are zero
 //     columns.  The reduction dimension of the first product is permuted the
 //     same way in both operands (lane group g owns dims 32c + 8g .. +8), which
-//     lets every lane load a 16-byte piece of a K row straight from HBM; V is
-//     stored transposed per tile, so a lane's 4 consecutive rows of one dim are
-//     8 contiguous bytes and each V load of the wave is one 512-byte run.
+//     lets every lane load a 16-byte piece of a K row straight from HBM, each
+//     K load of the wave one 1 KB run; V is stored in quads of 4 rows, so a
+//     lane's 4 consecutive rows of one dim are 8 contiguous bytes and each V
+//     load of the wave is four whole 128-byte lines.
 //   * online softmax in f32, in the log2 domain (scores pre-multiplied by
 //     scale*log2(e)); the running max starts at a finite -1e30 so that an
 //     all-masked unit never forms inf - inf.
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     float m_run = kNegBig;
     float l_run = 0.f;
 
-    const uint32_t k_lane = (uint32_t)(16 * lane);            // bytes into a K panel
+    const uint32_t k_lane = k_lane_offset(r, g4);             // bytes into a K panel
     const uint32_t v_lane = v_lane_offset(D, r, g4);          // bytes into a V panel
     const int64_t head_off = (int64_t)hk * (BS * D);
     const int64_t block_stride = (int64_t)p.Hkv * (BS * D);
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
         q1 = q0;  // an empty pool holds no rows
     const int qlen = q1 - q0;
 
-    const uint32_t k_lane = (uint32_t)(16 * lane);
+    const uint32_t k_lane = k_lane_offset(r, g4);
     const uint32_t v_lane = v_lane_offset(D, r, g4);
     const int64_t head_off = (int64_t)hk * (BS * D);
     const int64_t block_stride = (int64_t)p.Hkv * (BS * D);
@@ -825,24 +826,44 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
 }
 
+// The appends' thread order: one thread per (token, kv head, 8-dim piece), in groups of four tokens -- thread
+// ((t/4 * Hkv + h) * D/8 + c) * 4 + t%4 -- so that a wavefront reads whole rows of the [T][Hkv][D] input (four
+// tokens' rows of one head; a tokens-fastest order read each 128-byte line for one 16-byte piece, 8x the input
+// bytes), four neighbouring lanes write a row's 64-byte K run ([D/32][16][32] panel), and the lanes of one piece
+// write four consecutive tokens' values side by side in a V quad ([4][D][4]), whole 64-byte runs when the tokens'
+// rows are consecutive (a sequence's new rows).
+struct AppendThread {
+    int i;  // token (>= T for the padding of the last group)
+    int h;  // kv head
+    int c;  // 8-dim piece
+};
+__device__ __forceinline__ AppendThread append_thread(int64_t gid, int Hkv, int pieces) {
+    AppendThread a;
+    const int64_t g = gid >> 2;  // (t/4 * Hkv + h) * pieces + c
+    a.c = (int)(g % pieces);
+    const int64_t th = g / pieces;
+    a.h = (int)(th % Hkv);
+    a.i = (int)((th / Hkv) * 4 + (gid & 3));
+    return a;
+}
+__host__ __device__ constexpr int64_t append_threads(int64_t T, int Hkv, int D) {
+    return (T + 3) / 4 * 4 * Hkv * (D / 8);
+}
+
 // Paged KV append [kapsl-backends 0.1.1, src/gguf_native.rs: launch_kv_write,
-// launch_batch_kv_write]: one thread per (token, kv head, 8-dim piece), tokens
-// fastest, so that neighbouring lanes take neighbouring tokens of the same
-// (head, piece).  The K piece is one 16-byte store into the row's panel
-// ([D/8][16][8]); the V piece is 8 two-byte stores 8 bytes apart into the row's
-// quad of the V panel ([4][D][4]), two 32-byte sectors.  When consecutive tokens
-// have consecutive slots (a sequence's new rows), 16 lanes fill a whole 256-byte
-// run of a K panel and every 4 lanes whole 64-byte runs of a V quad.
+// launch_batch_kv_write]: each thread (order above) copies one 8-dim piece of a
+// token's K and V rows: one 16-byte K store into the row's 64-byte run of its
+// 32-dim group in the panel (a row touches D/32 lines), and 8 two-byte V stores
+// 8 bytes apart into the row's quad of the V panel, two 32-byte sectors.
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int pieces = p.D / 8;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)p.T * p.Hkv * pieces;
-    if (gid >= total)
+    if (gid >= append_threads(p.T, p.Hkv, p.D))
         return;
-    const int i = (int)(gid % p.T);
-    const int64_t hc = gid / p.T;  // head * pieces + piece
-    const int c = (int)(hc % pieces);
-    const int h = (int)(hc / pieces);
+    const AppendThread a = append_thread(gid, p.Hkv, pieces);
+    const int i = a.i, h = a.h, c = a.c;
+    if (i >= p.T)
+        return;
     const int64_t th = (int64_t)i * p.Hkv + h;  // token * Hkv + head
     const int64_t slot = p.slot_mapping[i];
     if (slot < 0 || slot >= (int64_t)p.N * p.BS)
@@ -855,7 +876,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     // the row's 16-row panel inside the (block, kv head) tile
     const int64_t panel = (blk * p.Hkv + h) * (int64_t)p.BS * p.D + (int64_t)(off / 16) * 16 * p.D;
     const int row = off % 16;
-    *reinterpret_cast<uint4 *>(p.k_pool + panel + ((int64_t)c * 16 + row) * 8) = kv;  // K panel [D/8][16][8]
+    *reinterpret_cast<uint4 *>(p.k_pool + panel + ((int64_t)(c >> 2) * 16 + row) * 32 + 8 * (c & 3)) = kv;  // [D/32][16][32]
     const uint16_t *vh = reinterpret_cast<const uint16_t *>(&vv);
     uint16_t *vdst = reinterpret_cast<uint16_t *>(p.v_pool + panel + (int64_t)(row >> 2) * 4 * p.D + 32 * c +
                                                   (row & 3));  // V panel [4][D][4]: dims 8c .. 8c+7 of the row
@@ -872,11 +893,11 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
                                                   int window, int32_t *__restrict__ order, int group, int *keys);
 
 // The decode step's append as its own launch: the new row of sequence s (block bt[s][(L-1)/BS], row (L-1)%BS, as
-// the fused step places it) for every kv head.  One workgroup per (sequence, kv head) rewrites the 128-byte lines
-// that hold the row whole -- each thread one 16-byte chunk: read, replace the row's part, write back -- so the pools
-// see only full-line writes: in the K panel the D/8 lines of the row's 8-row half (one 8-dim piece each), in the V
-// panel the D/16 lines of the row's quad.  Valid only because the block holding a sequence's newest row belongs to
-// that sequence alone.
+// the fused step places it) for every kv head.  One workgroup per (sequence, kv head), each thread one 16-byte
+// chunk.  In the K panel the row is D/32 runs of 64 bytes (whole 32-byte sectors, half a line each), written as they
+// are; in the V panel its values are 2-byte fields spread over the D/16 lines of its quad, and those lines are
+// rewritten whole (read, replace the row's fields, write back), so no partial sector is ever written.  Valid only
+// because the block holding a sequence's newest row belongs to that sequence alone.
 // With p.order set, the workgroups past the T * Hkv appends write the dispatch-order records instead (the ranking
 // of launch_order, in the same launch as the append).
 __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
@@ -900,13 +921,12 @@ __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
     const int64_t panel = ((int64_t)b * p.Hkv + h) * p.BS * p.D + (int64_t)(off / 16) * 16 * p.D;
     const _Float16 *kn = p.k + ((int64_t)s * p.Hkv + h) * p.D;
     const _Float16 *vn = p.v + ((int64_t)s * p.Hkv + h) * p.D;
-    // One 16-byte chunk per thread (head_dim <= 256, so D K chunks and D/2 V chunks fit the 256 threads).
+    // One 16-byte chunk per thread (head_dim <= 256, so D/8 K chunks and D/2 V chunks fit the 256 threads).
     const int q = (int)threadIdx.x;
-    if (q < p.D) {
-        // K panel [D/8][16][8]: the D/8 lines of the row's 8-row half; chunk (c, j) is piece c of row (row & 8) + j
-        const int c = q >> 3, j = q & 7;
-        f16x8 *dst = reinterpret_cast<f16x8 *>(p.k_pool + panel + ((row & 8) + c * 16 + j) * 8);
-        *dst = (j == (row & 7)) ? *reinterpret_cast<const f16x8 *>(kn + 8 * c) : *dst;
+    if (q < p.D / 8) {
+        // K panel [D/32][16][32]: dims 8q .. 8q+7 of the row, in the 64-byte run of its 32-dim group q / 4
+        *reinterpret_cast<f16x8 *>(p.k_pool + panel + ((q >> 2) * 16 + row) * 32 + 8 * (q & 3)) =
+            *reinterpret_cast<const f16x8 *>(kn + 8 * q);
     }
     if (q < p.D / 2) {
         // V panel [4][D][4]: the row's quad; chunk q holds dims 2q (its first 8 bytes) and 2q + 1 (its last 8), four
@@ -922,20 +942,19 @@ __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
 }
 
 // The varlen step's append as its own launch: token t of sequence s (tokens cu[s] .. cu[s+1]-1) goes to row
-// pos[s] + (t - cu[s]) of the sequence, through its block table.  One thread per (token, kv head, 8-dim piece),
-// tokens fastest (see append_kernel); the token's sequence by binary search of the prefix sums.  Rows past the
-// table's capacity and table entries outside the pool are skipped.
+// pos[s] + (t - cu[s]) of the sequence, through its block table.  One thread per (token, kv head, 8-dim piece), in
+// the order of append_kernel; the token's sequence by binary search of the prefix sums.  Rows past the table's
+// capacity and table entries outside the pool are skipped.
 __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, const int32_t *cu, const int32_t *pos,
                                                             int num_seqs) {
     const int pieces = p.D / 8;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)p.T * p.Hkv * pieces;
-    if (gid >= total)
+    if (gid >= append_threads(p.T, p.Hkv, p.D))
         return;
-    const int i = (int)(gid % p.T);
-    const int64_t hc = gid / p.T;
-    const int c = (int)(hc % pieces);
-    const int h = (int)(hc / pieces);
+    const AppendThread a = append_thread(gid, p.Hkv, pieces);
+    const int i = a.i, h = a.h, c = a.c;
+    if (i >= p.T)
+        return;
     int lo = 0, hi = num_seqs - 1;  // the last s with cu[s] <= i
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -956,7 +975,7 @@ __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, cons
     const uint4 vv = *reinterpret_cast<const uint4 *>(p.v + src);
     const int64_t panel = ((int64_t)blk * p.Hkv + h) * (int64_t)p.BS * p.D + (int64_t)(off / 16) * 16 * p.D;
     const int prow = off % 16;
-    *reinterpret_cast<uint4 *>(p.k_pool + panel + ((int64_t)c * 16 + prow) * 8) = kv;
+    *reinterpret_cast<uint4 *>(p.k_pool + panel + ((int64_t)(c >> 2) * 16 + prow) * 32 + 8 * (c & 3)) = kv;
     const uint16_t *vh = reinterpret_cast<const uint16_t *>(&vv);
     uint16_t *vdst = reinterpret_cast<uint16_t *>(p.v_pool + panel + (int64_t)(prow >> 2) * 4 * p.D + 32 * c +
                                                   (prow & 3));
@@ -1003,15 +1022,15 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
     const int e = (int)((hi < r0 + 16 ? hi : r0 + 16) - r0);
     const int64_t panel = ((int64_t)b * p.Hkv + h) * p.BS * p.D + (r0 % p.BS) * p.D;
     // The panels' chunks that keep old rows, read before the staging so both sets of loads are in flight together.
-    // K panel [D/8][16][8]: chunk q is piece q/16 of row q%16.  V panel [4][D][4]: chunk q is dims 2*(q % (D/2))
-    // and the next of quad q / (D/2), i.e. of rows 4*(q / (D/2)) .. +4.
+    // K panel [D/32][16][32]: chunk q is dims 8 * (4 * (q / 64) + q % 4) .. +8 of row (q / 4) % 16.  V panel
+    // [4][D][4]: chunk q is dims 2*(q % (D/2)) and the next of quad q / (D/2), i.e. of rows 4*(q / (D/2)) .. +4.
     const int qpd = p.D / 2;  // V chunks per quad
     f16x8 kc[2] = {}, vc[2] = {};
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int q = (int)threadIdx.x + 256 * it;
         if (q < 2 * p.D) {
-            const int kr = q % 16;
+            const int kr = (q >> 2) & 15;
             if (kr < a || kr >= e)
                 kc[it] = *reinterpret_cast<const f16x8 *>(p.k_pool + panel + 8 * q);
             const int vr = 4 * (q / qpd);
@@ -1037,9 +1056,9 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
     for (int it = 0; it < 2; ++it) {
         const int q = (int)threadIdx.x + 256 * it;
         if (q < 2 * p.D) {
-            const int kr = q % 16;
+            const int kr = (q >> 2) & 15;
             if (kr >= a && kr < e)
-                kc[it] = kst[kr * pieces + q / 16];
+                kc[it] = kst[kr * pieces + 4 * (q >> 6) + (q & 3)];
             *reinterpret_cast<f16x8 *>(p.k_pool + panel + 8 * q) = kc[it];
             const int vq = q / qpd, d0 = 2 * (q - vq * qpd);
 #pragma unroll
@@ -1327,7 +1346,7 @@ hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens
         return hipGetLastError();
     }
     if (p.T > 0) {
-        const int64_t total = (int64_t)p.T * p.Hkv * (p.D / 8);
+        const int64_t total = append_threads(p.T, p.Hkv, p.D);
         hipLaunchKernelGGL(append_varlen_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p,
                            cu_seqlens_q, pos_offsets, num_seqs);
         hipError_t e = hipGetLastError();
@@ -1361,7 +1380,7 @@ hipError_t launch_order_varlen(const int32_t *cu_seqlens_q, const int32_t *pos_o
 }
 
 hipError_t launch_append(const AppendParams &p, hipStream_t stream) {
-    const int64_t total = (int64_t)p.T * p.Hkv * (p.D / 8);
+    const int64_t total = append_threads(p.T, p.Hkv, p.D);
     dim3 grid((unsigned)((total + 255) / 256));
     dim3 block(256);
     hipLaunchKernelGGL(append_kernel, grid, block, 0, stream, p);

@@ -24,9 +24,9 @@
 //   * a head row is D/8 lanes; lane l holds dims 4l .. 4l+3 and D/2 + 4l .. +3, so each RoPE pair (j, j + D/2)
 //     lives in one lane.  The sum of squares is reduced across the group's lanes on the VALU (DPP row rotations,
 //     and a v_permlane16_swap for 32-lane groups);
-//   * q goes straight to q_out (8-byte stores, coalesced per half head row).  The unit's new K rows are staged in
-//     LDS in the pool's panel layout (rows XOR-swizzled per piece), its V rows row-major (padded rows); each
-//     thread then writes 16-byte chunks of the two panels (V put in its quad order on the way), taking rows
+//   * q goes straight to q_out (8-byte stores, coalesced per half head row).  The unit's new K and V rows are
+//     staged in LDS row-major (padded rows); each thread then writes 16-byte chunks of the two panels (each put in
+//     its panel order on the way), taking rows
 //     outside the new range from the old panel, which it loaded at the start (so that load overlaps everything
 //     else).  The pools thus see only whole 16-byte chunks of whole panels -- scattered 2-byte V stores and
 //     16-byte K row pieces cost far more at the memory than their bytes;
@@ -111,9 +111,8 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
     constexpr int CPT = (CHUNKS + kThreads - 1) / kThreads;
     constexpr int TAB = 16 * HALF / 4;  // float4 chunks of 16 rows of one table
     constexpr int VS = D + 4;  // row stride of the V staging (the pad spreads a dim's 16 rows over distinct banks)
-    // new K rows in the panel layout [D/8][16][8], row r of piece c kept in slot r ^ (c % 16) so that one row's
-    // pieces (written by one head row's lanes) and one piece's rows (read back per 16-byte chunk) hit distinct banks
-    __shared__ __attribute__((aligned(16))) _Float16 sk[16 * D];
+    constexpr int KS = D + 8;  // row stride of the K staging (16-byte chunks of 16 rows read back together)
+    __shared__ __attribute__((aligned(16))) _Float16 sk[16 * KS];  // new K rows, row-major [16][D + 8]
     __shared__ __attribute__((aligned(16))) _Float16 sv[16 * VS];  // new V rows, row-major [16][D + 4]
     __shared__ __attribute__((aligned(16))) float scos[16 * HALF];  // the unit's rows of the tables
     __shared__ __attribute__((aligned(16))) float ssin[16 * HALF];
@@ -284,10 +283,8 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
                 *reinterpret_cast<h4 *>(dst) = ya;
                 *reinterpret_cast<h4 *>(dst + HALF) = yb;
             } else {
-                // K panel [D/8][16][8]: dims 4 piece .. +4 are half of 8-wide piece (4 piece) / 8
-                const int ca = (4 * piece) / 8, cb = (HALF + 4 * piece) / 8;
-                *reinterpret_cast<h4 *>(sk + (ca * 16 + (rin ^ (ca & 15))) * 8 + (4 * piece) % 8) = ya;
-                *reinterpret_cast<h4 *>(sk + (cb * 16 + (rin ^ (cb & 15))) * 8 + (4 * piece) % 8) = yb;
+                *reinterpret_cast<h4 *>(sk + rin * KS + 4 * piece) = ya;
+                *reinterpret_cast<h4 *>(sk + rin * KS + HALF + 4 * piece) = yb;
             }
         }
     }
@@ -300,9 +297,9 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
         if (q >= CHUNKS)
             break;
         if (has_k) {
-            // K chunk q: piece q / 16 of row q % 16
-            const int kr = q & 15, kc = q >> 4;
-            const h8 kn = *reinterpret_cast<const h8 *>(sk + (kc * 16 + (kr ^ (kc & 15))) * 8);
+            // K panel [D/32][16][32], chunk q: dims 8 * (4 * (q / 64) + q % 4) .. +8 of row (q / 4) % 16
+            const int kr = (q >> 2) & 15;
+            const h8 kn = *reinterpret_cast<const h8 *>(sk + kr * KS + 8 * (4 * (q >> 6) + (q & 3)));
             const bool knew = whole || (kr >= r0 && kr < r0 + rows);
             *reinterpret_cast<h8 *>(p.k_pool + panel + 8 * q) = knew ? kn : ok[c];
         }

@@ -72,21 +72,23 @@ struct Frag {
 };
 
 // Loads one 16-row unit with buffer loads.  Every block is stored as panels of 16 rows; a unit is one panel:
-//   K panel [D/8][16][8]: the A-operand fragment of lane (g4, r) -- row r, dims 32c + 8*g4 .. +8, i.e. piece
-//     4c + g4 -- sits at byte 1024*c + 16*(16*g4 + r) = 1024*c + 16*lane: each wave load is one contiguous 1 KB
-//     run of whole cache lines (a row-major tile would touch sixteen half lines per load, which caps one CU at
-//     about a third of the rate it reaches on whole lines);
+//   K panel [D/32][16][32] (each row's dims in 32-wide pieces, piece-major): the A-operand fragment of lane
+//     (g4, r) -- row r, dims 32c + 8*g4 .. +8 -- sits at byte 1024*c + 64*r + 16*g4: each wave load is one
+//     contiguous 1 KB run of whole cache lines (a row-major tile would touch sixteen half lines per load, which
+//     caps one CU at about a third of the rate it reaches on whole lines), and a new row is D/32 runs of 64 bytes
+//     (an [D/8][16][8] panel, which loads at the same rate, spreads it over D/8 lines in 16-byte pieces);
 //   V panel [4][D][4] (four quads of 4 rows; in a quad each dim's 4 rows are adjacent): lane (g4, r) reads dims
 //     16c + r, rows 4*g4 .. +3 -- quad g4 -- at byte 8*(g4*D + r) + 128*c: each wave load is four whole 128-byte
 //     lines, one per quad.  A new row then touches D/4 of the panel's 32-byte sectors (4 dims in each), where a
 //     dim-major [D][16] panel, equally good to load, would put each of its D values in a sector of its own;
-//   v_lane_offset() below gives the lane's byte offset.
+//   k_lane_offset() and v_lane_offset() below give the lane's byte offsets.
 // kb / vb are wave-uniform pointers to the panel; each becomes a buffer resource built on the scalar unit, and the
 // lane's loop-invariant byte offsets (k_lane, v_lane) are the only VGPR operands, so no per-unit address arithmetic
 // lands in vector registers that loads in flight still own.  The resource's record count is the panel's size: an
 // offset past it reads 0.
 constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, no swizzle (gfx9 family)
 constexpr int kVGroupBytes = 128;       // V bytes of 16 dims of one quad: the step between a lane's V loads
+__host__ __device__ constexpr uint32_t k_lane_offset(int r, int g4) { return (uint32_t)(64 * r + 16 * g4); }
 __host__ __device__ constexpr uint32_t v_lane_offset(int D, int r, int g4) { return (uint32_t)(8 * (g4 * D + r)); }
 // Cache-policy bits of the streamed K/V loads: nt (non-temporal).  K and V are read once per step, and the hint
 // keeps them from displacing lines that are reused (measured on MI355X: 17% faster on the Llama-3-8B-shaped batch,
@@ -137,7 +139,7 @@ __device__ __forceinline__ void patch_unit_rows(Frag<D, BS> &f, int prow, int pr
                                                 int g4, uint32_t k_lane, uint32_t v_lane) {
     constexpr int KC = Frag<D, BS>::KC;
     constexpr int VC = Frag<D, BS>::VC;
-    if (r >= prow && r < prow_end) {  // K pieces 4c + g4 of row r
+    if (r >= prow && r < prow_end) {  // K dims 32c + 8*g4 .. +8 of row r
 #pragma unroll
         for (int c = 0; c < KC; ++c)
             f.k[c] = *reinterpret_cast<const f16x8 *>(sk + r * D + 32 * c + 8 * g4);
@@ -180,7 +182,7 @@ __device__ __forceinline__ void compute_unit(Frag<D, BS> &f, const f16x8 (&qf)[D
     constexpr int KC = Frag<D, BS>::KC;
     constexpr int VC = Frag<D, BS>::VC;
     if (prow >= 0) {  // wave-uniform
-        if (r == prow) {  // K pieces 4c + g4
+        if (r == prow) {  // K dims 32c + 8*g4 .. +8
 #pragma unroll
             for (int c = 0; c < KC; ++c)
                 f.k[c] = *reinterpret_cast<const f16x8 *>(pk + 32 * c + 8 * g4);

@@ -7,8 +7,8 @@ call raises.
 
 Tensor layouts (all C-contiguous, on the GPU):
     q, out        [num_seqs][num_q_heads][head_dim]                 float16
-    k_pool        [num_blocks][num_kv_heads][block_size/16][head_dim/8][16][8]  float16
-    v_pool        [num_blocks][num_kv_heads][block_size/16][head_dim][16]       float16
+    k_pool        [num_blocks][num_kv_heads][block_size/16][head_dim/32][16][32]  float16
+    v_pool        [num_blocks][num_kv_heads][block_size/16][4][head_dim][4]       float16
     block_tables  [num_seqs][max_blocks_per_seq]                    int32
     context_lens  [num_seqs]                                        int32
     k, v          [num_tokens][num_kv_heads][head_dim]              float16
@@ -171,10 +171,10 @@ def _pool(k_pool, v_pool) -> PoolDesc:
     import torch
     _dev(k_pool, torch.float16, "k_pool", 6)
     _dev(v_pool, torch.float16, "v_pool", 6)
-    N, Hkv, NP, D8, sixteen, eight = k_pool.shape
-    D, BS = D8 * 8, NP * 16
-    if (sixteen, eight) != (16, 8):
-        raise ValueError("k_pool must be [N][Hkv][BS/16][D/8][16][8], got %s" % (tuple(k_pool.shape),))
+    N, Hkv, NP, D32, sixteen, w32 = k_pool.shape
+    D, BS = D32 * 32, NP * 16
+    if (sixteen, w32) != (16, 32):
+        raise ValueError("k_pool must be [N][Hkv][BS/16][D/32][16][32], got %s" % (tuple(k_pool.shape),))
     if tuple(v_pool.shape) != (N, Hkv, NP, 4, D, 4):
         raise ValueError("v_pool must be [N][Hkv][BS/16][4][D][4] = %s, got %s"
                          % ((N, Hkv, NP, 4, D, 4), tuple(v_pool.shape)))
@@ -364,7 +364,7 @@ def paged_decode_step_qkv(qkv, q_norm_w, k_norm_w, cos, sin, k_pool, v_pool, blo
     sequence's new token at position L-1, its K/V rows written to row L-1, then decode attention.  Returns
     (out, q_out)."""
     import torch
-    B, D = int(context_lens.shape[0]), k_pool.shape[3] * 8
+    B, D = int(context_lens.shape[0]), v_pool.shape[4]
     if q_out is None:
         q_out = torch.empty((B, int(num_q_heads), D), dtype=torch.float16, device=qkv.device)
     if out is None:
@@ -547,7 +547,7 @@ def split_qkv_norm_rope_into_paged_cache_varlen(qkv, q_norm_w, k_norm_w, cos, si
     into the pools at row pos_offsets[s] + i of its sequence.  Returns q_out."""
     import torch
     if q_out is None:
-        q_out = torch.empty((qkv.shape[0], int(num_q_heads), k_pool.shape[3] * 8), dtype=torch.float16,
+        q_out = torch.empty((qkv.shape[0], int(num_q_heads), v_pool.shape[4]), dtype=torch.float16,
                             device=qkv.device)
     pool, T, P = _qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, num_q_heads, qk_mode)
     _dev(block_tables, torch.int32, "block_tables", 2)
@@ -570,7 +570,7 @@ def split_qkv_norm_rope_into_paged_cache(qkv, q_norm_w, k_norm_w, cos, sin, k_po
     cache row cache_len + i of the sequence whose table is block_table [M].  Returns q_out."""
     import torch
     if q_out is None:
-        q_out = torch.empty((qkv.shape[0], int(num_q_heads), k_pool.shape[3] * 8), dtype=torch.float16,
+        q_out = torch.empty((qkv.shape[0], int(num_q_heads), v_pool.shape[4]), dtype=torch.float16,
                             device=qkv.device)
     pool, T, P = _qkv_args(qkv, q_norm_w, k_norm_w, cos, sin, q_out, k_pool, v_pool, num_q_heads, qk_mode)
     _dev(block_table, torch.int32, "block_table", 1)

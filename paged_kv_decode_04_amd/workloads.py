@@ -5,7 +5,7 @@ library and the CPU oracle.  This module draws random numbers and builds index s
 tables, slot mappings); it holds none of the attention arithmetic and imports neither the oracle nor the HIP binding.
 
 Pool layouts, fixed by the library's header (each block is BS/16 panels of 16 rows):
-    k_pool[N][Hkv][BS/16][D/8][16][8] fp16  (a panel holds each row's dims in 8-wide pieces, piece-major)
+    k_pool[N][Hkv][BS/16][D/32][16][32] fp16  (a panel holds each row's dims in 32-wide pieces, piece-major)
     v_pool[N][Hkv][BS/16][4][D][4] fp16     (a panel holds four quads of 4 rows, each dim's 4 rows adjacent)
 Use k_row / v_row / set_k_row / set_v_row to address one token row.
 
@@ -96,7 +96,7 @@ class DecodeCase:
     context_lens: np.ndarray           # [B] int32, rows including the newest token
     block_tables: np.ndarray           # [B][M] int32
     q: Optional[np.ndarray] = None      # [B][Hq][D] fp16
-    k_pool: Optional[np.ndarray] = None  # [N][Hkv][BS/16][D/8][16][8] fp16
+    k_pool: Optional[np.ndarray] = None  # [N][Hkv][BS/16][D/32][16][32] fp16
     v_pool: Optional[np.ndarray] = None  # [N][Hkv][BS/16][4][D][4] fp16
     k_new: Optional[np.ndarray] = None   # [T][Hkv][D] fp16, the rows appended this step
     v_new: Optional[np.ndarray] = None   # [T][Hkv][D] fp16
@@ -151,7 +151,7 @@ def poison_rows(k_pool: np.ndarray, v_pool: np.ndarray, slots: np.ndarray, BS: i
 
 
 def k_pool_shape(N: int, Hkv: int, BS: int, D: int) -> tuple:
-    return (N, Hkv, BS // 16, D // 8, 16, 8)
+    return (N, Hkv, BS // 16, D // 32, 16, 32)
 
 
 def v_pool_shape(N: int, Hkv: int, BS: int, D: int) -> tuple:
@@ -159,8 +159,8 @@ def v_pool_shape(N: int, Hkv: int, BS: int, D: int) -> tuple:
 
 
 def _alloc_pools(N, Hkv, BS, D):
-    if BS % 16 or D % 8:
-        raise ValueError("block_size must be a multiple of 16 and head_dim a multiple of 8")
+    if BS % 16 or D % 32:
+        raise ValueError("block_size must be a multiple of 16 and head_dim a multiple of 32")
     return (np.empty(k_pool_shape(N, Hkv, BS, D), dtype=np.float16),
             np.empty(v_pool_shape(N, Hkv, BS, D), dtype=np.float16))
 
@@ -177,7 +177,7 @@ def v_row(v_pool: np.ndarray, block: int, head: int, offset: int) -> np.ndarray:
 def set_k_row(k_pool: np.ndarray, block: int, head, offset: int, row) -> None:
     """Write K row(s) of D values at (block, head(s), offset)."""
     r = np.asarray(row, dtype=np.float16)
-    k_pool[block, head, offset // 16, :, offset % 16, :] = r.reshape(r.shape[:-1] + (-1, 8))
+    k_pool[block, head, offset // 16, :, offset % 16, :] = r.reshape(r.shape[:-1] + (-1, 32))
 
 
 def set_v_row(v_pool: np.ndarray, block: int, head, offset: int, row) -> None:

@@ -76,11 +76,13 @@ int main(void) {
     check(pkv_plan_decode(32, 32, 8, 128, 16, -4, 0, 0, 256, &plan) == PKV_EINVAL, "plan: negative table width");
 
     pkv_pool_desc pool = {8, 128, 16, 64}, odd = {8, 100, 16, 64}, wide = {8, 512, 16, 64}, bs8 = {8, 128, 8, 64};
+    pkv_pool_desc d40 = {8, 40, 16, 64};
     /* append */
     check(pkv_paged_kv_append(h16, h16, h32, -1, h16, h16, pool, NULL) == PKV_EINVAL, "append: negative tokens");
     check(pkv_paged_kv_append(h16, h16, h32, 0, h16, h16, pool, NULL) == PKV_OK, "append: zero tokens is a no-op");
     check(pkv_paged_kv_append(NULL, h16, h32, 4, h16, h16, pool, NULL) == PKV_EINVAL, "append: NULL k");
     check(pkv_paged_kv_append(h16, h16, h32, 4, h16, h16, odd, NULL) == PKV_EUNSUPPORTED, "append: head_dim 100");
+    check(pkv_paged_kv_append(h16, h16, h32, 4, h16, h16, d40, NULL) == PKV_EUNSUPPORTED, "append: head_dim 40");
     check(pkv_paged_kv_append(h16, h16, h32, 4, h16, h16, bs8, NULL) == PKV_EUNSUPPORTED, "append: block_size 8");
     check(pkv_paged_kv_append(h16 + 1, h16, h32, 4, h16, h16, pool, NULL) == PKV_EINVAL, "append: misaligned k");
     /* attention and its variants */

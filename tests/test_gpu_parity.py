@@ -74,7 +74,7 @@ def test_append_bit_exact_small(torch_cuda):
     rng = np.random.default_rng(5)
     for (N, Hkv, BS, D, T) in [(9, 3, 16, 64, 20), (40, 8, 16, 128, 64), (5, 16, 32, 256, 7), (4, 2, 64, 128, 30)]:
         say("append N=%d Hkv=%d BS=%d D=%d T=%d" % (N, Hkv, BS, D, T))
-        k_pool = rng.standard_normal((N, Hkv, BS // 16, D // 8, 16, 8)).astype(np.float16)
+        k_pool = rng.standard_normal(W.k_pool_shape(N, Hkv, BS, D)).astype(np.float16)
         v_pool = rng.standard_normal(W.v_pool_shape(N, Hkv, BS, D)).astype(np.float16)
         slots = rng.choice(N * BS, size=T, replace=False).astype(np.int32)
         slots[1] = -1

@@ -270,9 +270,13 @@ STEP_GEOMS = [
 
 
 def _step_case(B, Hq, Hkv, D, BS, lens, seed, qk_mode):
+    """qkv ~ 2 N(0,1) with the value heads halved (exact in fp16): the new V rows are then N(0,1) like the pool's,
+    so the outputs stay below ~5, where fp16 resolves the 2e-3 bar (at |out| >= 8 its half-ulp alone is 3.9e-3)."""
     lens = np.asarray(lens, dtype=np.int32)
-    return W.build_qkv_case("step", B, Hq, Hkv, D, BS, np.ones(B, np.int32), lens - 1, seed, qk_mode=qk_mode,
-                            qkv_scale=2.0, eps=1e-5)
+    c = W.build_qkv_case("step", B, Hq, Hkv, D, BS, np.ones(B, np.int32), lens - 1, seed, qk_mode=qk_mode,
+                         qkv_scale=2.0, eps=1e-5)
+    c.qkv[:, (Hq + Hkv) * D:] *= np.float16(0.5)
+    return c
 
 
 def _run_step(torch, c, num_splits, lens=None):

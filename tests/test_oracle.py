@@ -31,27 +31,27 @@ def _nums(a):
     return _num(a)
 
 
-def _pad8(x, D):
-    """Zero-pad the last axis from D to the next multiple of 8 (the K layout needs D % 8 == 0); zero dims change
+def _pad32(x, D):
+    """Zero-pad the last axis from D to the next multiple of 32 (the K layout needs D % 32 == 0); zero dims change
     no dot product, and the outputs on them are sums of zeros."""
     x = np.asarray(x, dtype=np.float64)
-    Dp = (D + 7) // 8 * 8
+    Dp = (D + 31) // 32 * 32
     pad = [(0, 0)] * (x.ndim - 1) + [(0, Dp - D)]
     return np.pad(x, pad)
 
 
 def _zero_pools(N, Hkv, BS, D):
-    return (np.zeros((N, Hkv, BS // 16, D // 8, 16, 8), dtype=np.float16),
+    return (np.zeros(W.k_pool_shape(N, Hkv, BS, D), dtype=np.float16),
             np.zeros(W.v_pool_shape(N, Hkv, BS, D), dtype=np.float16))
 
 
 def _pools_from_rows(case):
     N, Hkv, BS, D = case["N"], case["Hkv"], case["BS"], case["D"]
-    Dp = (D + 7) // 8 * 8
+    Dp = (D + 31) // 32 * 32
     k_pool, v_pool = _zero_pools(N, Hkv, BS, Dp)
     for r in case["rows"]:
-        W.set_k_row(k_pool, r["block"], r["head"], r["offset"], _pad8(r["k"], D))
-        W.set_v_row(v_pool, r["block"], r["head"], r["offset"], _pad8(r["v"], D))
+        W.set_k_row(k_pool, r["block"], r["head"], r["offset"], _pad32(r["k"], D))
+        W.set_v_row(v_pool, r["block"], r["head"], r["offset"], _pad32(r["v"], D))
     return k_pool, v_pool
 
 
@@ -71,12 +71,12 @@ def test_f16_decode_matches_numpy_on_every_bit_pattern():
 
 def test_pool_index_functions_match_numpy_strides():
     rng = np.random.default_rng(7)
-    for (N, Hkv, BS, D) in [(5, 3, 16, 64), (2, 1, 32, 256), (7, 8, 16, 128), (3, 2, 64, 8)]:
-        k = np.empty((N, Hkv, BS // 16, D // 8, 16, 8), dtype=np.float16)
+    for (N, Hkv, BS, D) in [(5, 3, 16, 64), (2, 1, 32, 256), (7, 8, 16, 128), (3, 2, 64, 32)]:
+        k = np.empty(W.k_pool_shape(N, Hkv, BS, D), dtype=np.float16)
         v = np.empty(W.v_pool_shape(N, Hkv, BS, D), dtype=np.float16)
         for _ in range(50):
             b, h, o, d = (int(rng.integers(N)), int(rng.integers(Hkv)), int(rng.integers(BS)), int(rng.integers(D)))
-            assert oracle.k_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(k.strides, (b, h, o // 16, d // 8, o % 16, d % 8))
+            assert oracle.k_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(k.strides, (b, h, o // 16, d // 32, o % 16, d % 32))
             assert oracle.v_index(Hkv, BS, D, b, h, o, d) * 2 == np.dot(v.strides,
                                                                         (b, h, o // 16, (o % 16) // 4, d, o % 4))
 
@@ -106,12 +106,12 @@ def _golden_attention_cases():
 @pytest.mark.parametrize("case", _golden_attention_cases(), ids=lambda c: c["name"])
 def test_golden_attention(case):
     k_pool, v_pool = _pools_from_rows(case)
-    q = _pad8(case["q"], case["D"]).astype(np.float16)
+    q = _pad32(case["q"], case["D"]).astype(np.float16)
     bt = np.array(case["block_tables"], dtype=np.int32)
     cl = np.array(case["context_lens"], dtype=np.int32)
     scale = _num(case["scale"])
     out = oracle.decode_attention(q, k_pool, v_pool, bt, cl, scale, threads=2)
-    np.testing.assert_allclose(out, _pad8(case["expected"], case["D"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(out, _pad32(case["expected"], case["D"]), rtol=1e-14, atol=1e-14)
     if "weights" in case:
         for s, wexp in enumerate(case["weights"]):
             _, w = oracle.attention_weights(q, k_pool, v_pool, bt, cl, scale, s, 0)
@@ -142,15 +142,15 @@ def test_golden_append():
         cases = json.load(f)["cases"]
     for c in cases:
         N, Hkv, BS, D = c["N"], c["Hkv"], c["BS"], c["D"]
-        k_pool, v_pool = _zero_pools(N, Hkv, BS, D)
-        skipped = oracle.paged_kv_append(np.array(c["k"], np.float16), np.array(c["v"], np.float16),
+        k_pool, v_pool = _zero_pools(N, Hkv, BS, (D + 31) // 32 * 32)
+        skipped = oracle.paged_kv_append(_pad32(c["k"], D).astype(np.float16), _pad32(c["v"], D).astype(np.float16),
                                          c["slot_mapping"], k_pool, v_pool)
         assert skipped == c["expected_skipped"]
         k_exp = np.zeros_like(k_pool)
         v_exp = np.zeros_like(v_pool)
         for r in c["expected_rows"]:
-            W.set_k_row(k_exp, r["block"], r["head"], r["offset"], r["k"])
-            W.set_v_row(v_exp, r["block"], r["head"], r["offset"], r["v"])
+            W.set_k_row(k_exp, r["block"], r["head"], r["offset"], _pad32(r["k"], D))
+            W.set_v_row(v_exp, r["block"], r["head"], r["offset"], _pad32(r["v"], D))
         assert np.array_equal(k_pool, k_exp)
         assert np.array_equal(v_pool, v_exp)
 
@@ -278,7 +278,7 @@ def _contiguous_problem(seed, B, Hq, Hkv, D, BS, lens, scale):
     M = max(nbs)
     perm = rng.permutation(N).astype(np.int32)
     bt = np.full((B, M), -1, np.int32)
-    k_pool = rng.standard_normal((N, Hkv, BS // 16, D // 8, 16, 8)).astype(np.float16)
+    k_pool = rng.standard_normal(W.k_pool_shape(N, Hkv, BS, D)).astype(np.float16)
     v_pool = rng.standard_normal(W.v_pool_shape(N, Hkv, BS, D)).astype(np.float16)
     q = rng.standard_normal((B, Hq, D)).astype(np.float16)
     Kc, Vc = [], []
@@ -392,7 +392,7 @@ def test_combine_never_reads_past_the_valid_splits():
 def test_append_writes_rows_and_leaves_everything_else():
     rng = np.random.default_rng(31)
     N, Hkv, BS, D, T = 9, 3, 32, 64, 20
-    k_pool = rng.standard_normal((N, Hkv, BS // 16, D // 8, 16, 8)).astype(np.float16)
+    k_pool = rng.standard_normal(W.k_pool_shape(N, Hkv, BS, D)).astype(np.float16)
     v_pool = rng.standard_normal(W.v_pool_shape(N, Hkv, BS, D)).astype(np.float16)
     k0, v0 = k_pool.copy(), v_pool.copy()
     slots = rng.choice(N * BS, size=T, replace=False).astype(np.int32)
@@ -442,10 +442,10 @@ def _golden_varlen_cases():
 @pytest.mark.parametrize("case", _golden_varlen_cases(), ids=lambda c: c["name"])
 def test_golden_varlen(case):
     k_pool, v_pool = _pools_from_rows(case)
-    q = _pad8(case["q"], case["D"]).astype(np.float16)
+    q = _pad32(case["q"], case["D"]).astype(np.float16)
     out = oracle.varlen_attention(q, k_pool, v_pool, case["block_tables"], case["cu_seqlens_q"],
                                   case["pos_offsets"], _num(case["scale"]), threads=2)
-    np.testing.assert_allclose(out, _pad8(case["expected"], case["D"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(out, _pad32(case["expected"], case["D"]), rtol=1e-14, atol=1e-14)
 
 
 def _varlen(c, threads=4, units=None, k_pool=None, v_pool=None):
@@ -537,10 +537,10 @@ def _golden_window_cases():
 @pytest.mark.parametrize("case", _golden_window_cases(), ids=lambda c: c["name"])
 def test_golden_window(case):
     k_pool, v_pool = _pools_from_rows(case)
-    q = _pad8(case["q"], case["D"]).astype(np.float16)
+    q = _pad32(case["q"], case["D"]).astype(np.float16)
     out = oracle.decode_attention(q, k_pool, v_pool, case["block_tables"], case["context_lens"], _num(case["scale"]),
                                   threads=2, window=case["window"])
-    np.testing.assert_allclose(out, _pad8(case["expected"], case["D"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(out, _pad32(case["expected"], case["D"]), rtol=1e-14, atol=1e-14)
 
 
 def test_window_at_least_the_context_is_plain_decode_and_one_row_returns_v():
@@ -650,7 +650,7 @@ def _heads(c):
     return oracle.f16_to_f64(c.qkv).reshape(vc.T, vc.Hq + 2 * vc.Hkv, vc.D)
 
 
-@pytest.mark.parametrize("D", [8, 64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_qkv_rope_is_a_complex_rotation(D):
     """Without the norm, each head's dims j and j + D/2 form the complex number a + ib, which RoPE multiplies by
     cos + i sin of the token's table row (numpy complex arithmetic as the independent second opinion)."""

@@ -109,7 +109,7 @@ def test_a_plan_beyond_the_scratch_is_refused(torch_cuda):
     torch = torch_cuda
     B, Hq, Hkv, D, BS = 512, 64, 8, 128, 16
     q = torch.zeros((B, Hq, D), dtype=torch.float16, device="cuda")
-    kp = torch.zeros((1, Hkv, BS // 16, D // 8, 16, 8), dtype=torch.float16, device="cuda")
+    kp = torch.zeros(W.k_pool_shape(1, Hkv, BS, D), dtype=torch.float16, device="cuda")
     vp = torch.zeros(W.v_pool_shape(1, Hkv, BS, D), dtype=torch.float16, device="cuda")
     bt = torch.zeros((B, 4), dtype=torch.int32, device="cuda")
     cl = torch.zeros((B,), dtype=torch.int32, device="cuda")
