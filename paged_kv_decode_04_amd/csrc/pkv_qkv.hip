@@ -18,17 +18,17 @@
 //     first starts); a slot finds its sequence by a wave-wide search of the prefix sums, and slots past a
 //     sequence's last unit return at once.  The unit's head slots of kv head h (its G query heads, key head h,
 //     value head h) are split over `parts` workgroups of `hpp` slots each (the host picks them: one part when
-//     units hold a row or two, as in decode; a few, about four passes of 256 threads each, when units are full);
-//     items are (new row, head slot) pairs.  The first loads are issued at once (the old panels, the unit's rows
-//     of the cos/sin tables and the norm weights into LDS, each thread's qkv pieces of the first pass);
+//     units hold a row or two, as in decode; parts of two passes of 256 threads each when units are full), the
+//     part holding K and V dispatched first; items are (new row, head slot) pairs.  Every load of the unit is
+//     issued before the first wait (the norm weights, the unit's rows of the cos/sin tables, each thread's qkv
+//     pieces of the first two passes, the old panels of a partly written unit);
 //   * a head row is D/8 lanes; lane l holds dims 4l .. 4l+3 and D/2 + 4l .. +3, so each RoPE pair (j, j + D/2)
 //     lives in one lane.  The sum of squares is reduced across the group's lanes on the VALU (DPP row rotations,
 //     and a v_permlane16_swap for 32-lane groups);
 //   * q goes straight to q_out (8-byte stores, coalesced per half head row).  The unit's new K and V rows are
 //     staged in LDS row-major (padded rows); each thread then writes 16-byte chunks of the two panels (each put in
-//     its panel order on the way), taking rows
-//     outside the new range from the old panel, which it loaded at the start (so that load overlaps everything
-//     else).  The pools thus see only whole 16-byte chunks of whole panels -- scattered 2-byte V stores and
+//     its panel order on the way), taking rows outside the new range from the old panel, which it loaded at the
+//     start (so that load overlaps everything else).  The pools thus see only whole 16-byte chunks of whole panels -- scattered 2-byte V stores and
 //     16-byte K row pieces cost far more at the memory than their bytes;
 //   * decode mode (decode_lens set): slot g is sequence g, whose one new token sits at row decode_lens[g] - 1 --
 //     the QKV half of the decode step from QKV rows when it runs as two launches.
@@ -44,6 +44,7 @@
 
 #include "pkv_internal.h"
 #include "pkv_lanes.h"
+#include "pkv_unit.h"
 
 namespace pkv {
 
@@ -62,29 +63,37 @@ __device__ __forceinline__ int slot_key(const int32_t *cu, int s) { return cu[s]
 
 // The sequence of unit slot g -- the last s in [0, B] with slot_key(s) <= 16 g + 15 -- with its first token, new
 // token count and first position.  The 64 lanes of the wave test 64 evenly spaced candidates per round; with
-// B < 64 one round loads every candidate and its position at once, and the answer's neighbours come from lane
-// exchanges.  Keys increase, so the lanes that pass are a prefix; with malformed prefix sums s still lies in
-// [0, B].
+// B < 64 one round holds every candidate (SlotKeys) and the answer's neighbours come from lane exchanges.  Keys increase, so the lanes that pass are a prefix; with malformed prefix
+// sums s still lies in [0, B].
 struct SeqOfSlot {
     int s, first, n, pos;
 };
 
-__device__ __forceinline__ SeqOfSlot find_sequence(const int32_t *cu, const int32_t *pos, int B, int g) {
+struct SlotKeys {
+    int c, q;  // lane l: cu[l] (l <= B) and pos[l]
+};
+
+__device__ __forceinline__ SlotKeys load_slot_keys(const int32_t *cu, const int32_t *pos, int B) {
+    const int lane = threadIdx.x & 63;
+    return SlotKeys{cu[lane <= B ? lane : B], pos[lane < B ? lane : B - 1]};
+}
+
+__device__ __forceinline__ SeqOfSlot lookup_slot(const SlotKeys &key, int B, int g) {  // B < 64
+    const int lane = threadIdx.x & 63;
+    const bool pass = lane <= B && key.c + 32 * lane <= 16 * g + 15;
+    int k = __popcll(__ballot(pass)) - 1;
+    k = k > 0 ? k : 0;
+    SeqOfSlot r;
+    r.s = k;
+    r.first = __shfl(key.c, k, 64);
+    r.n = __shfl(key.c, k + 1 <= B ? k + 1 : B, 64) - r.first;
+    r.pos = __shfl(key.q, k < B ? k : B - 1, 64);
+    return r;
+}
+
+__device__ __forceinline__ SeqOfSlot search_slot(const int32_t *cu, const int32_t *pos, int B, int g) {  // any B
     const int lane = threadIdx.x & 63;
     const int target = 16 * g + 15;
-    SeqOfSlot r;
-    if (B < 64) {
-        const int c = cu[lane <= B ? lane : B];
-        const int q = pos[lane < B ? lane : B - 1];
-        const bool pass = lane <= B && c + 32 * lane <= target;
-        int k = __popcll(__ballot(pass)) - 1;
-        k = k > 0 ? k : 0;
-        r.s = k;
-        r.first = __shfl(c, k, 64);
-        r.n = __shfl(c, k + 1 <= B ? k + 1 : B, 64) - r.first;
-        r.pos = __shfl(q, k < B ? k : B - 1, 64);
-        return r;
-    }
     int lo = 0, hi = B;
     while (lo < hi) {
         const int stride = (hi - lo + 64) / 64;
@@ -94,13 +103,57 @@ __device__ __forceinline__ SeqOfSlot find_sequence(const int32_t *cu, const int3
         lo += (k > 0 ? k : 0) * stride;
         hi = min(hi, lo + stride - 1);
     }
-    r.s = lo;
+    SeqOfSlot r{lo, 0, 0, 0};
     if (lo < B) {
         r.first = cu[lo];
         r.n = cu[lo + 1] - r.first;
         r.pos = pos[lo];
     }
     return r;
+}
+
+// One 16-row cache unit of a workgroup: new rows r0 .. r0 + rows - 1 (rows == 0: the slot has nothing to write),
+// of sequence s, token m0 first; lo is the cache row of row r0 in the sequence and rp0 its RoPE position.
+struct Unit {
+    int s, r0, rows, m0;
+    int64_t lo, rp0;
+};
+
+// The j-th unit slot of sequence s (first token `first`, n new tokens, the first of them at RoPE position rope0 and
+// cache row cache0): its unit and the new rows in it, or rows == 0 when the slot lies past the sequence's units or
+// its tokens or positions fall outside the arrays (malformed prefix sums, positions outside the tables: those
+// tokens are not written).
+__device__ __forceinline__ Unit unit_of_slot(const QkvParams &p, int s, int first, int n, int rope0, int cache0,
+                                             int j) {
+    Unit un{s, 0, 0, 0, 0, 0};
+    const int64_t u = (int64_t)(cache0 >> 4) + j;
+    const int64_t lo = max((int64_t)cache0, 16 * u);
+    const int64_t hi = min((int64_t)cache0 + n, 16 * u + 16);
+    if (j < 0 || lo >= hi)
+        return un;
+    const int i0 = (int)(lo - cache0);  // index of row r0 among the sequence's new tokens
+    const int m0 = first + i0;
+    int rows = (int)(hi - lo);
+    rows = rows < p.T - m0 ? rows : p.T - m0;
+    const int64_t rp0 = (int64_t)rope0 + i0;
+    if (m0 < 0 || rows <= 0 || rp0 < 0 || rp0 + rows > p.P)
+        return un;
+    un.r0 = (int)(lo - 16 * u);
+    un.rows = rows;
+    un.m0 = m0;
+    un.lo = lo;
+    un.rp0 = rp0;
+    return un;
+}
+
+// The same values in every lane (they come from wave-wide searches), made scalar so that the buffer resources
+// built from them stay in scalar registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni(int64_t x) {
+    return (int64_t)(((uint64_t)(uint32_t)uni((int)(x >> 32)) << 32) | (uint32_t)uni((int)x));
+}
+__device__ __forceinline__ Unit uniform(const Unit &u) {
+    return Unit{uni(u.s), uni(u.r0), uni(u.rows), uni(u.m0), uni(u.lo), uni(u.rp0)};
 }
 
 template <int D>
@@ -110,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
     constexpr int CHUNKS = 2 * D;    // 16-byte chunks of one 16-row panel (16 * D halves)
     constexpr int CPT = (CHUNKS + kThreads - 1) / kThreads;
     constexpr int TAB = 16 * HALF / 4;  // float4 chunks of 16 rows of one table
+    constexpr int TPT = (TAB + kThreads - 1) / kThreads;  // chunks of each table per thread
     constexpr int VS = D + 4;  // row stride of the V staging (the pad spreads a dim's 16 rows over distinct banks)
     constexpr int KS = D + 8;  // row stride of the K staging (16-byte chunks of 16 rows read back together)
     __shared__ __attribute__((aligned(16))) _Float16 sk[16 * KS];  // new K rows, row-major [16][D + 8]
@@ -117,65 +171,82 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
     __shared__ __attribute__((aligned(16))) float scos[16 * HALF];  // the unit's rows of the tables
     __shared__ __attribute__((aligned(16))) float ssin[16 * HALF];
     __shared__ __attribute__((aligned(16))) _Float16 sw[2 * D];     // q_norm_w, k_norm_w
+    typedef float f4 __attribute__((ext_vector_type(4)));
 
-    const int g = (int)blockIdx.x;                  // unit slot
-    const int h = (int)blockIdx.y / p.parts;        // kv head
-    const int part = (int)blockIdx.y - h * p.parts;  // which of its head slots (G query heads, K, V) this group does
-    int s = 0, first = 0, n = p.T, rope0 = p.rope_base, cache0 = p.cache_base;
-    int j;  // index of this slot's cache unit among the sequence's units
-    if (p.decode_lens) {
-        // one new token per sequence: slot g is sequence g, its row at position L - 1
-        s = first = g;
-        const int L = p.decode_lens[s];
-        n = L > 0 ? 1 : 0;
-        rope0 = cache0 = L - 1;
-        j = 0;
-    } else {
-        if (p.cu_seqlens_q) {
-            const SeqOfSlot q = find_sequence(p.cu_seqlens_q, p.pos_offsets, p.B, g);
-            if (q.s >= p.B)
-                return;
-            s = q.s;
-            first = q.first;
-            n = q.n;
-            rope0 = cache0 = q.pos;
-        }
-        j = g - ((first + 32 * s) >> 4);
-    }
-    // this slot's 16-row cache unit and the new rows in it
-    const int64_t u = (int64_t)(cache0 >> 4) + j;
-    const int64_t lo = max((int64_t)cache0, 16 * u);
-    const int64_t hi = min((int64_t)cache0 + n, 16 * u + 16);
-    if (j < 0 || lo >= hi)
-        return;
-    const int r0 = (int)(lo - 16 * u);  // first new row inside the unit
-    int rows = (int)(hi - lo);
-    const int i0 = (int)(lo - cache0);  // its index among the sequence's new tokens
-    const int m0 = first + i0;          // its token
-    rows = rows < p.T - m0 ? rows : p.T - m0;
-    const int64_t rp0 = (int64_t)rope0 + i0;
-    if (m0 < 0 || rows <= 0 || rp0 < 0 || rp0 + rows > p.P)
-        return;  // positions outside the tables (or malformed prefix sums): the unit's tokens are not written
-
+    // (kv head, part): the part holding K and V, the heaviest, is dispatched first, so that the workgroups that
+    // wait for a free slot are light ones
+    const int yy = (int)gridDim.y - 1 - (int)blockIdx.y;
+    const int part = yy / p.Hkv;  // which of the kv head's head slots (G query heads, K, V) this group does
+    const int h = yy - part * p.Hkv;
     // head slots [hs0, hs1) of kv head h: < G query heads, G the key head, G + 1 the value head
     const int hs0 = part * p.hpp;
     const int hs1 = min(hs0 + p.hpp, p.G + 2);
     const int nh = hs1 - hs0;
     const bool has_k = hs0 <= p.G && p.G < hs1;
     const bool has_v = hs1 == p.G + 2;
-    int64_t panel = -1;  // the unit's panel (element offset of its first half) in both pools
-    if ((has_k || has_v) && lo >= 0 && lo < (int64_t)p.M * p.BS) {
-        const int row = (int)lo;
-        const int blk = p.block_tables[(int64_t)s * p.M + row / p.BS];
-        if (blk >= 0 && blk < p.N)
-            panel = (((int64_t)blk * p.Hkv + h) * p.BS + (row % p.BS - r0)) * D;
-    }
-    const bool whole = r0 == 0 && rows == 16;
+    const bool rotates = hs0 <= p.G;  // the group holds a query or key head
     const int tid = threadIdx.x;
     const int width = (p.Hq + 2 * p.Hkv) * D;
-    const int lanes = rows * nh * LPR;
-    const bool rotates = hs0 <= p.G;  // the group holds a query or key head
 
+    // Every load is a buffer load whose resource bounds the bytes it may touch: a lane with nothing to load passes
+    // an offset past the bound and gets zeros without a memory access, so no load sits under a branch and all of
+    // them are in flight before the first wait.  (With per-lane branches the compiler waited for each load where
+    // its value left the branch: the block id, then each table chunk, then each qkv piece, a chain of round trips
+    // before the unit's data was all requested.)
+    constexpr uint32_t kPast = 0x7ffffff0u;  // an offset past every bound below
+    auto rsrc = [](const void *base, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kRsrcWord3);
+    };
+    // the norm weights first: they depend on nothing
+    const int w_bytes = rotates && p.qk_mode == 1 ? 2 * D : 0;
+    const h8 wq = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rsrc(p.q_norm_w, w_bytes), tid < LPR ? (uint32_t)(16 * tid) : kPast, 0, 0));
+    const h8 wk = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rsrc(p.k_norm_w, w_bytes),
+                                             tid >= LPR && tid < 2 * LPR ? (uint32_t)(16 * (tid - LPR)) : kPast, 0, 0));
+
+    // this slot's unit
+    const int g = (int)blockIdx.x;
+    Unit w;
+    if (p.decode_lens) {
+        // one new token per sequence: slot g is sequence g, its row at position L - 1
+        const int L = p.decode_lens[g];
+        w = unit_of_slot(p, g, g, L > 0 ? 1 : 0, L - 1, L - 1, 0);
+    } else {
+        SeqOfSlot q{0, 0, p.T, p.rope_base};
+        int cache0 = p.cache_base;
+        if (p.cu_seqlens_q) {
+            q = p.B < 64 ? lookup_slot(load_slot_keys(p.cu_seqlens_q, p.pos_offsets, p.B), p.B, g)
+                         : search_slot(p.cu_seqlens_q, p.pos_offsets, p.B, g);
+            cache0 = q.pos;
+            q.n = q.s < p.B ? q.n : 0;
+        }
+        w = unit_of_slot(p, q.s, q.first, q.n, q.pos, cache0, g - ((q.first + 32 * q.s) >> 4));
+    }
+    w = uniform(w);
+    if (w.rows <= 0)
+        return;  // (wave-uniform, and the same in every wave of the group)
+    const bool whole = w.r0 == 0 && w.rows == 16;
+    const int lanes = w.rows * nh * LPR;
+
+    // the unit's block id: a scalar load (its wait never holds back the vector loads), used once they are in flight
+    const bool in_table = (has_k || has_v) && w.lo >= 0 && w.lo < (int64_t)p.M * p.BS;
+    const int blk = in_table ? uniform_load(p.block_tables, (int64_t)w.s * p.M + w.lo / p.BS) : -1;
+    // the unit's rows of the cos/sin tables (LDS copies below), before its qkv pieces, so that the copies and the
+    // barrier after them wait for the older loads only
+    const int tab_bytes = rotates ? w.rows * HALF * 4 : 0;
+    const __amdgpu_buffer_rsrc_t cos_r = rsrc(p.cos_t + w.rp0 * HALF, tab_bytes);
+    const __amdgpu_buffer_rsrc_t sin_r = rsrc(p.sin_t + w.rp0 * HALF, tab_bytes);
+    f4 cv[TPT], sv4[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+        const int t = tid + kThreads * i;  // float4 t of the unit's 16 table rows
+        const uint32_t off = t < TAB ? (uint32_t)(16 * t) : kPast;
+        cv[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(cos_r, off, 0, 0));
+        sv4[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(sin_r, off, 0, 0));
+    }
+    // this thread's qkv pieces: rows m0 .. m0 + rows - 1 of qkv
+    const __amdgpu_buffer_rsrc_t qkv_r = rsrc(p.qkv + (int64_t)w.m0 * width, w.rows * width * 2);
     auto source = [&](int idx, int &rr, int &hs, int &piece) {
         const int item = idx / LPR;
         piece = idx - item * LPR;
@@ -187,43 +258,40 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
         int rr, hs, piece;
         source(idx, rr, hs, piece);
         const int head = hs < p.G ? h * p.G + hs : (hs == p.G ? p.Hq + h : p.Hq + p.Hkv + h);
-        const _Float16 *src = p.qkv + (int64_t)(m0 + rr) * width + (int64_t)head * D + 4 * piece;
-        const h4 a = *reinterpret_cast<const h4 *>(src);
-        const h4 b = *reinterpret_cast<const h4 *>(src + HALF);
+        const uint32_t off = idx < lanes ? (uint32_t)(2 * (rr * width + head * D + 4 * piece)) : kPast;
+        const h4 a = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(qkv_r, off, 0, 0));
+        const h4 b = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(qkv_r, off, 2 * HALF, 0));
         return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     };
-
-    // The first batch of global loads at once: the old panels (rows outside [r0, r0 + rows) are written back
-    // unchanged), the unit's rows of the cos/sin tables and the norm weights (to LDS), this thread's qkv pieces.
+    h8 raw[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+        raw[b] = fetch(b * kThreads + tid);
+    // the old panels, once the block id is in (rows outside [r0, r0 + rows) are written back unchanged)
+    int64_t panel = -1;  // the unit's panel (element offset of its first half) in both pools
+    if (in_table && blk >= 0 && blk < p.N)
+        panel = (((int64_t)blk * p.Hkv + h) * p.BS + ((int)w.lo % p.BS - w.r0)) * D;
+    const bool keep_old = panel >= 0 && !whole;
+    const __amdgpu_buffer_rsrc_t ok_r = rsrc(keep_old ? p.k_pool + panel : p.k_pool, keep_old && has_k ? 32 * D : 0);
+    const __amdgpu_buffer_rsrc_t ov_r = rsrc(keep_old ? p.v_pool + panel : p.v_pool, keep_old && has_v ? 32 * D : 0);
     h8 ok[CPT], ov[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const int q = tid + kThreads * c;
-        if (panel >= 0 && !whole && q < CHUNKS) {
-            if (has_k)
-                ok[c] = *reinterpret_cast<const h8 *>(p.k_pool + panel + 8 * q);
-            if (has_v)
-                ov[c] = *reinterpret_cast<const h8 *>(p.v_pool + panel + 8 * q);
-        }
+        const uint32_t off = q < CHUNKS ? (uint32_t)(16 * q) : kPast;
+        ok[c] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(ok_r, off, 0, 0));
+        ov[c] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(ov_r, off, 0, 0));
     }
-    if (rotates) {
-        for (int c = tid; c < 2 * TAB; c += kThreads) {
-            const int t = c < TAB ? c : c - TAB;  // float4 t of the unit's 16 table rows
-            if (t < rows * (HALF / 4)) {
-                const float *src = (c < TAB ? p.cos_t : p.sin_t) + rp0 * HALF + 4 * t;
-                *reinterpret_cast<float4 *>((c < TAB ? scos : ssin) + 4 * t) =
-                    *reinterpret_cast<const float4 *>(src);
-            }
-        }
-        if (p.qk_mode == 1 && tid < 2 * LPR)
-            *reinterpret_cast<h8 *>(sw + 8 * tid) =
-                *reinterpret_cast<const h8 *>((tid < LPR ? p.q_norm_w : p.k_norm_w) + 8 * (tid % LPR));
-    }
-    h8 raw[kBatch];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b)
-        if (b * kThreads + tid < lanes)
-            raw[b] = fetch(b * kThreads + tid);
+    for (int i = 0; i < TPT; ++i) {
+        const int t = tid + kThreads * i;
+        if (rotates && t < TAB) {
+            *reinterpret_cast<f4 *>(scos + 4 * t) = cv[i];
+            *reinterpret_cast<f4 *>(ssin + 4 * t) = sv4[i];
+        }
+    }
+    if (rotates && p.qk_mode == 1 && tid < 2 * LPR)
+        *reinterpret_cast<h8 *>(sw + 8 * tid) = tid < LPR ? wq : wk;
     __syncthreads();
 
     const float inv_d = 1.0f / (float)D;
@@ -231,8 +299,7 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
         if (base > 0) {
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
-                if (base + b * kThreads + tid < lanes)
-                    raw[b] = fetch(base + b * kThreads + tid);
+                raw[b] = fetch(base + b * kThreads + tid);
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
@@ -241,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
                 break;  // lanes below `lanes` form whole head-row groups, so every group sum has all its lanes
             int rr, hs, piece;
             source(idx, rr, hs, piece);
-            const int rin = r0 + rr;
+            const int rin = w.r0 + rr;
             if (hs > p.G) {
                 // value head: staged row-major, put into the panel's quad order on the way out
                 const h8 v = raw[b];
@@ -268,18 +335,16 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
                     x[4 + e] = x[4 + e] * r * (float)wb[e];
                 }
             }
-            const float4 c = *reinterpret_cast<const float4 *>(scos + rr * HALF + 4 * piece);
-            const float4 sn = *reinterpret_cast<const float4 *>(ssin + rr * HALF + 4 * piece);
-            const float cs[4] = {c.x, c.y, c.z, c.w};
-            const float ss4[4] = {sn.x, sn.y, sn.z, sn.w};
+            const f4 c = *reinterpret_cast<const f4 *>(scos + rr * HALF + 4 * piece);
+            const f4 sn = *reinterpret_cast<const f4 *>(ssin + rr * HALF + 4 * piece);
             h4 ya, yb;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ya[e] = (_Float16)(x[e] * cs[e] - x[4 + e] * ss4[e]);
-                yb[e] = (_Float16)(x[4 + e] * cs[e] + x[e] * ss4[e]);
+                ya[e] = (_Float16)(x[e] * c[e] - x[4 + e] * sn[e]);
+                yb[e] = (_Float16)(x[4 + e] * c[e] + x[e] * sn[e]);
             }
             if (hs < p.G) {
-                _Float16 *dst = p.q_out + ((int64_t)(m0 + rr) * p.Hq + h * p.G + hs) * D + 4 * piece;
+                _Float16 *dst = p.q_out + ((int64_t)(w.m0 + rr) * p.Hq + h * p.G + hs) * D + 4 * piece;
                 *reinterpret_cast<h4 *>(dst) = ya;
                 *reinterpret_cast<h4 *>(dst + HALF) = yb;
             } else {
@@ -300,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
             // K panel [D/32][16][32], chunk q: dims 8 * (4 * (q / 64) + q % 4) .. +8 of row (q / 4) % 16
             const int kr = (q >> 2) & 15;
             const h8 kn = *reinterpret_cast<const h8 *>(sk + kr * KS + 8 * (4 * (q >> 6) + (q & 3)));
-            const bool knew = whole || (kr >= r0 && kr < r0 + rows);
+            const bool knew = whole || (kr >= w.r0 && kr < w.r0 + w.rows);
             *reinterpret_cast<h8 *>(p.k_pool + panel + 8 * q) = knew ? kn : ok[c];
         }
         if (has_v) {
@@ -315,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const int vr = 4 * vq + (x & 3);
-                    vn[x] = (vr >= r0 && vr < r0 + rows) ? vn[x] : ov[c][x];
+                    vn[x] = (vr >= w.r0 && vr < w.r0 + w.rows) ? vn[x] : ov[c][x];
                 }
             }
             *reinterpret_cast<h8 *>(p.v_pool + panel + 8 * q) = vn;
