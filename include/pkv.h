@@ -159,7 +159,17 @@ PKV_API int pkv_paged_kv_append(const uint16_t *k, const uint16_t *v, const int3
  *   larger than the device's CU count and num_seqs <= 16384, a small launch
  *   first ranks the sequences by the rows they attend and the attention grid
  *   runs them longest first (the ranks live in the library workspace; calls
- *   with a caller workspace keep id order).  Results are identical either way.
+ *   with a caller workspace keep id order).  A single pass without a window
+ *   also splits each sequence longer than a CU's fair share of the launch
+ *   (all rows * Hkv / CUs, at least 1024 rows) into pieces run by separate
+ *   workgroups; the last piece of each (sequence, kv head) to finish merges
+ *   the pieces' partials in piece order in the same launch [ferrum-kernels
+ *   0.7.7, src/backend/cuda/paged.rs: paged_batched_flash_dispatch, splits
+ *   even for grids past the CU count].  The library workspace then holds
+ *   (num_seqs + CUs/Hkv) * (num_q_heads * (head_dim + 2) * 4 + 128) bytes
+ *   plus 4 * num_seqs * Hkv, rounded up.  Results are the same bits on every
+ *   call with the same inputs; a split sequence's outputs differ from a
+ *   whole-sequence pass (a caller workspace) by rounding only.
  *   Graph capture: every entry point reads lengths, tables and positions on
  *   the device and sizes its launches from host arguments only, so a captured
  *   call replays correctly with new device-resident values.  A workspace that
@@ -204,8 +214,9 @@ PKV_API int pkv_paged_decode_attention_ws(const uint16_t *q, const uint16_t *k_p
  *   Limit: a plan whose partials need more than PKV_NOALLOC_SCRATCH_BYTES
  *   fails with PKV_EWORKSPACE before anything is enqueued (the partials take
  *   num_seqs * num_q_heads * splits * (head_dim + 2) * 4 bytes, rounded up;
- *   a single pass takes none); when the dispatch-order records would not fit
- *   beside them the grid runs in id order instead (same results).
+ *   a single pass takes none); when the pieces of the dispatch order would
+ *   not fit the grid runs whole sequences in order, and when the records
+ *   would not fit beside the partials it runs in id order.
  *   Every call on one device shares that device's array, which keeps what
  *   the last call left there: calls whose kernels may overlap on one device
  *   (several host threads, or streams not ordered against each other) race

@@ -134,7 +134,7 @@ size_t library_workspace_bytes(hipStream_t stream) {
 }
 
 struct WsLayout {
-    size_t o_off, m_off, l_off, order_off, total;
+    size_t o_off, m_off, l_off, order_off, count_off, total;
 };
 
 // Split-K partials (S > 1), then order_ints int32 of dispatch-order records.
@@ -146,7 +146,23 @@ WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t S, int64_t order_in
     L.m_off = o;
     L.l_off = o + ml;
     L.order_off = o + 2 * ml;
+    L.count_off = 0;
     L.total = L.order_off + round256((size_t)order_ints * sizeof(int32_t));
+    return L;
+}
+
+// An ordered single pass with pieces (see pkv::PieceRule): the pieces' partials ([records][Hq][D] outputs, then
+// [records][Hq] maxima and sums), the records, then the [B][Hkv] piece counters.
+WsLayout ws_layout_pieces(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t records) {
+    WsLayout L;
+    const size_t o = round256((size_t)(records * Hq * D) * sizeof(float));
+    const size_t ml = round256((size_t)(records * Hq) * sizeof(float));
+    L.o_off = 0;
+    L.m_off = o;
+    L.l_off = o + ml;
+    L.order_off = o + 2 * ml;
+    L.count_off = L.order_off + round256((size_t)(records * pkv::kOrderRecord) * sizeof(int32_t));
+    L.total = L.count_off + round256((size_t)(B * Hkv) * sizeof(int32_t));
     return L;
 }
 
@@ -425,11 +441,24 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
     const int64_t grid = (int64_t)num_seqs * pool.num_kv_heads * plan.num_splits;
     bool order = ws_kind != kCallerWs && num_seqs > 1 && num_seqs <= pkv::kOrderMaxSeqs && cu_count > 0 &&
                  grid > cu_count;
-    WsLayout L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits,
-                           order ? (int64_t)num_seqs * pkv::kOrderRecord : 0);
+    // An ordered single pass also splits the longest sequences into pieces (pkv::PieceRule): fewer than
+    // cu_count / Hkv extra records.
+    bool pieces = order && plan.num_splits == 1 && window <= 0;
+    const int64_t records = num_seqs + (cu_count + pool.num_kv_heads - 1) / pool.num_kv_heads;
+    auto layout = [&]() {
+        if (pieces)
+            return ws_layout_pieces(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, records);
+        return ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits,
+                         order ? (int64_t)num_seqs * pkv::kOrderRecord : 0);
+    };
+    WsLayout L = layout();
+    if (pieces && ws_kind == kFixedWs && L.total > workspace_bytes) {
+        pieces = false;  // the pieces' partials do not fit: whole sequences in order
+        L = layout();
+    }
     if (order && ws_kind == kFixedWs && L.total > workspace_bytes) {
         order = false;  // the records do not fit beside the partials: id order
-        L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits);
+        L = layout();
     }
     if (order && ws_kind == kLibraryWs && library_workspace_bytes(stream) < L.total) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -437,8 +466,8 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
         if (e != hipSuccess)
             return hip_fail(e, "hipStreamIsCapturing");
         if (cap != hipStreamCaptureStatusNone) {
-            order = false;  // dispatch order is an optimisation: never worth a failed capture
-            L = ws_layout(num_seqs, num_q_heads, pool.head_dim, plan.num_splits);
+            order = pieces = false;  // dispatch order is an optimisation: never worth a failed capture
+            L = layout();
         }
     }
     if (plan.num_splits == 1 && !order) {
@@ -472,17 +501,31 @@ int run_plan(const pkv_decode_plan &plan, const uint16_t *q, const uint16_t *k_p
     }
     char *base = static_cast<char *>(ws);
     int32_t *ord = order ? reinterpret_cast<int32_t *>(base + L.order_off) : nullptr;
+    pkv::PieceRule rule{};
+    if (pieces) {
+        rule.records = (int32_t)records;
+        rule.cus = cu_count;
+        rule.hkv = pool.num_kv_heads;
+        rule.block_size = pool.block_size;
+        rule.counters = reinterpret_cast<int32_t *>(base + L.count_off);
+        p.order_records = rule.records;
+        p.piece_count = rule.counters;
+        p.part_o = reinterpret_cast<float *>(base + L.o_off);
+        p.part_m = reinterpret_cast<float *>(base + L.m_off);
+        p.part_l = reinterpret_cast<float *>(base + L.l_off);
+    }
     if (pre_append) {  // the decode step's append launch, which also writes the order records
         pkv::AppendParams a = *pre_append;
         a.order = ord;
         a.order_cap = max_blocks_per_seq * pool.block_size;
         a.order_window = window;
+        a.pieces = rule;
         hipError_t e = pkv::launch_append_newest(a, stream);
         if (e != hipSuccess)
             return hip_fail(e, "append kernel launch");
     } else if (ord) {
         hipError_t e = pkv::launch_order(context_lens, block_tables, num_seqs, max_blocks_per_seq,
-                                         max_blocks_per_seq * pool.block_size, window, ord, stream);
+                                         max_blocks_per_seq * pool.block_size, window, ord, rule, stream);
         if (e != hipSuccess)
             return hip_fail(e, "order kernel launch");
     }

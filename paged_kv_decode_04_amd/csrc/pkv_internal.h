@@ -29,9 +29,9 @@ struct DecodeParams {
     const _Float16 *k_pool;       // [N][Hkv][BS/16][D/32][16][32]
     const _Float16 *v_pool;       // [N][Hkv][BS/16][4][D][4]
     _Float16 *out;                // [B][Hq][D]            (single pass)
-    float *part_o;                // [B][Hq][S][D]         (split-K)
-    float *part_m;                // [B][Hq][S]
-    float *part_l;                // [B][Hq][S]
+    float *part_o;                // [B][Hq][S][D]         (split-K; ordered pieces: [records][Hq][D])
+    float *part_m;                // [B][Hq][S]            (ordered pieces: [records][Hq], log2 units)
+    float *part_l;                // [B][Hq][S]            (ordered pieces: [records][Hq])
     _Float16 *k_dst;
     _Float16 *v_dst;
     const _Float16 *q_norm_w;     // [D]
@@ -42,9 +42,11 @@ struct DecodeParams {
     int32_t qk_mode;
     float eps;
     _Float16 *q_out;              // [B][Hq][D]
-    // dispatch order (multi-round grids): workgroup tile t serves the sequence of record order[t / Hkv] (null:
-    // sequence t / Hkv); see kOrderRecord
-    const int32_t *order;         // [B][kOrderRecord]
+    // dispatch order (multi-round grids): workgroup tile t serves the sequence (or piece of one) of record
+    // order[t / Hkv] (null: sequence t / Hkv); see kOrderRecord
+    const int32_t *order;         // [order_records][kOrderRecord]
+    int32_t order_records;        // records in order (a single pass: B plus room for pieces); 0: B
+    int32_t *piece_count;         // [B][Hkv] pieces of a split tile done so far (zeroed by the ordering launch)
 };
 
 // Arguments of the varlen attention kernel (several new query rows per sequence).
@@ -88,6 +90,21 @@ struct CombineParams {
     int32_t window;               // as DecodeParams::window (the split ranges start at the window's block)
 };
 
+// The pieces of a single-pass decode dispatch order.  A grid of several rounds still ends on its longest tile when
+// that tile alone needs more rows than a CU's fair share of the launch (all rows times Hkv over the CUs): its CU
+// streams alone at the end.  The ordering launch splits each sequence longer than
+// C = max(kMinPieceRows, fair share rounded up to 64 rows) into ceil(rows / C) pieces of equal rows (rounded up to
+// 64, so every piece starts on a block), one record each; the attention launch computes each piece as a tile and
+// the last piece of a (sequence, kv head) to finish merges them.  The extra records number less than cus / hkv.
+struct PieceRule {
+    int32_t records;              // records the order array holds (B + ceil(cus / hkv)); 0: one per sequence
+    int32_t cus;                  // CUs the launch spreads over
+    int32_t hkv;                  // kv heads: tiles per record
+    int32_t block_size;
+    int32_t *counters;            // [B][hkv]: zeroed by the ordering launch, counted up by the pieces
+};
+constexpr int kMinPieceRows = 1024;
+
 struct AppendParams {
     const _Float16 *k;            // [T][Hkv][D]
     const _Float16 *v;
@@ -102,6 +119,7 @@ struct AppendParams {
     // window order_window for decode)
     int32_t *order;
     int32_t order_cap, order_window;
+    PieceRule pieces;             // decode order: the longest sequences' pieces (records == 0: none)
 };
 
 // Arguments of the QKV-to-cache kernel (split QKV, q/k RMSNorm, RoPE, paged-cache write).
@@ -158,15 +176,19 @@ hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream);
 constexpr int kOrderMaxSeqs = 16384;
 // Largest one-dimensional grid of 256-thread workgroups (a launch's threads along x must fit in 32 bits).
 constexpr int64_t kMaxGroups = 0xFFFFFFFFll / 256;
-// One record per rank of the dispatch order: the sequence, its length as stored, then its first kOrderRecBlocks
-// block-table entries -- everything a decode workgroup reads before its first K/V loads, in one place.
+// One record per rank of the dispatch order (per piece of a split sequence): the sequence, its length as stored,
+// the piece's unit range and place, then the table entries of its first kOrderRecBlocks blocks -- everything a
+// decode workgroup reads before its first K/V loads, in one place.
 constexpr int kOrderRecord = 32;
-constexpr int kOrderRecBlocks = kOrderRecord - 2;
+constexpr int kOrderRecHead = 6;
+constexpr int kOrderRecBlocks = kOrderRecord - kOrderRecHead;
 // Records of the sequences sorted by the rows they attend (min(clamp(L, 0, cap_rows), window) with window > 0),
-// longest first, ties by index: order[rank][0] = sequence, [1] = context_lens[sequence], [2 + i] = its table
-// entry i (i < min(M, kOrderRecBlocks)).
+// longest first, ties by index; a sequence split into n pieces (see PieceRule) takes n consecutive records.
+// order[r][0] = sequence (-1: an unused record), [1] = context_lens[sequence], [2] = the piece's first 16-row unit,
+// [3] = its end unit (INT32_MAX: the sequence's end), [4] = piece index | n << 16, [5] = the record of piece 0,
+// [6 + i] = table entry (first unit / units per block) + i, i < kOrderRecBlocks.
 hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables, int B, int M, int cap_rows,
-                        int window, int32_t *order, hipStream_t stream);
+                        int window, int32_t *order, const PieceRule &pieces, hipStream_t stream);
 // Varlen records: order[rank][0] = sequence, [1] = cu_seqlens_q[s], [2] = cu_seqlens_q[s + 1], [3] = pos_offsets[s],
 // [4 + i] = its table entry i (i < min(M, kVarlenRecBlocks)); ranked by min(pos + new rows, cap_rows), longest
 // first, ties by index.

@@ -72,12 +72,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     // ORDERED (a grid of several rounds): the sequences run longest first, tile t taking the sequence of order
     // record t / Hkv -- the dispatcher starts workgroups in id order as CUs free up, so the longest ones no longer
     // start last and finish alone.  The record also holds the length and the first block ids, so the first K/V
-    // loads still wait for one dependent load.
+    // loads still wait for one dependent load.  A record may be one piece of a sequence (a range of its units, see
+    // PieceRule): the pieces' partials are merged by the last of them to finish (the epilogue below).
     const int32_t *rec = ORDERED ? p.order + (int64_t)rank * kOrderRecord : nullptr;
-    int s_rec = 0, L_rec = 0;  // the record's sequence and length, one load
-    if (ORDERED)
+    int s_rec = 0, L_rec = 0;          // the record's sequence and length
+    int u0_rec = 0, u1_rec = 0;        // its unit range
+    int pc_rec = 1 << 16, base_rec = 0;  // piece index | pieces << 16; the record of piece 0
+    if (ORDERED) {
         uniform_load_pair(rec, 0, s_rec, L_rec);
-    const int s = ORDERED ? s_rec : rank;
+        uniform_load_pair(rec, 2, u0_rec, u1_rec);
+        uniform_load_pair(rec, 4, pc_rec, base_rec);
+    }
+    const bool unused_rec = ORDERED && s_rec < 0;  // a record past the last piece (wave-uniform)
+    const int s = ORDERED ? (unused_rec ? 0 : s_rec) : rank;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int r = lane & 15;
@@ -97,7 +104,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int j = 0; j < NSPEC; ++j) {
         const int bi = min(u_known + j * NW, max_units - 1) / SPB;
-        spec_raw[j] = start_known ? (ORDERED ? uniform_load(rec, 2 + bi) : uniform_load(bt, bi)) : -1;
+        spec_raw[j] = start_known ? (ORDERED ? uniform_load(rec, kOrderRecHead + bi) : uniform_load(bt, bi)) : -1;
     }
     int L = ORDERED ? L_rec : uniform_load(p.context_lens, s);
 
@@ -127,6 +134,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
                  "s"(spec_raw[NSPEC > 3 ? 3 : 0]), "s"(spec_raw[NSPEC > 4 ? 4 : 0])
                  : "memory");
 
+    if (unused_rec)
+        return;
     L = L < 0 ? 0 : (L > p.M * BS ? p.M * BS : L);
     if (p.N <= 0)
         L = 0;  // an empty pool holds no rows
@@ -143,8 +152,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         if (b0 >= b1)
             return;  // empty split: the combine never reads it
     }
-    const int u_begin = max(b0 * SPB, lo >> 4);  // units wholly before the window are skipped
-    const int u_end = min(b1 * SPB, (L + 15) >> 4);
+    // units wholly before the window are skipped; an ordered piece reads its own range of units
+    const int u_begin = max(max(b0 * SPB, lo >> 4), ORDERED && !SPLIT ? u0_rec : 0);
+    const int u_end = min(min(b1 * SPB, (L + 15) >> 4), ORDERED && !SPLIT ? u1_rec : INT32_MAX);
+    const int npieces = ORDERED && !SPLIT ? (pc_rec >> 16) : 1;
+    const bool piece = npieces > 1;  // this tile is one piece of a split sequence: it writes a partial
     const RowLimits lim = {L - 1, L - 1, L - 1, lo};
     const int u_first = u_begin + wave;  // wave w takes units u_begin + w, + w + NW, ...
     const int n_units = u_first < u_end ? (u_end - u_first + NW - 1) / NW : 0;
@@ -392,7 +404,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         den += exp2_fast(sm_m[w * 16 + r] - Mc) * sm_l[w * 16 + r];
     {
         const float a = exp2_fast(m_run - Mc);
-        const float f = SPLIT ? a : (den > 0.f ? a / den : 0.f);
+        const float f = SPLIT || piece ? a : (den > 0.f ? a / den : 0.f);
         if (r < p.G) {
             float *dst = sm_o + (wave * p.G + r) * DP + 4 * g4;
 #pragma unroll
@@ -407,6 +419,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
             p.part_m[base] = Mc * kLn2;
             p.part_l[base] = den;
         }
+        if (piece && wave == 0 && g4 == 0 && r < p.G) {  // the piece's (max in log2 units, sum) per query head
+            const int64_t slot = (int64_t)rank * p.Hq + hk * p.G + r;
+            store_agent(p.part_m + slot, Mc);
+            store_agent(p.part_l + slot, den);
+        }
     }
     __syncthreads();
 
@@ -419,10 +436,50 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         for (int w = 0; w < NW; ++w)
             num += sm_o[(w * p.G + h) * DP + d];
         const int64_t row = (int64_t)s * p.Hq + hk * p.G + h;
-        if (!SPLIT)
-            p.out[row * D + d] = (_Float16)num;
-        else
+        if (SPLIT)
             p.part_o[(row * p.num_splits + split) * D + d] = num;
+        else if (piece)
+            store_agent(p.part_o + ((int64_t)rank * p.Hq + hk * p.G + h) * D + d, num);
+        else
+            p.out[row * D + d] = (_Float16)num;
+    }
+    if (piece) {
+        // The pieces of a (sequence, kv head) meet at their ends only: each stores its partial with agent-coherent
+        // stores (coherent across the XCDs' L2 caches), waits until they are complete, then counts itself in; the
+        // piece that counts in last reads every piece's partial and merges them in piece order, whoever it is,
+        // so the output does not depend on which piece ends last.  No workgroup waits for another, and no
+        // cache-wide write-back is needed.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        int *seen = reinterpret_cast<int *>(smem);
+        if (threadIdx.x == 0)
+            seen[0] = __hip_atomic_fetch_add(p.piece_count + (int64_t)s * p.Hkv + hk, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (seen[0] == npieces - 1) {
+            for (int idx = threadIdx.x; idx < total; idx += NW * 64) {
+                const int h = idx / D;
+                const int d = idx - h * D;
+                const int64_t hq = (int64_t)hk * p.G + h;
+                float Mx = kNegBig;
+                for (int pc = 0; pc < npieces; ++pc) {
+                    const int64_t slot = (int64_t)(base_rec + pc) * p.Hq + hq;
+                    if (load_agent(p.part_l + slot) > 0.f)
+                        Mx = fmaxf(Mx, load_agent(p.part_m + slot));
+                }
+                float num = 0.f, dsum = 0.f;
+                for (int pc = 0; pc < npieces; ++pc) {
+                    const int64_t slot = (int64_t)(base_rec + pc) * p.Hq + hq;
+                    const float l = load_agent(p.part_l + slot);
+                    if (l > 0.f) {
+                        const float a = exp2_fast(load_agent(p.part_m + slot) - Mx);
+                        num += a * load_agent(p.part_o + slot * D + d);
+                        dsum += a * l;
+                    }
+                }
+                p.out[((int64_t)s * p.Hq + hq) * D + d] = (_Float16)(dsum > 0.f ? num / dsum : 0.f);
+            }
+        }
     }
 }
 
@@ -886,11 +943,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 }
 
 constexpr int kOrderSeqsPerGroup = 64;  // sequences one order workgroup ranks
+// LDS of a ranking workgroup: all B keys rounded up to 4, and four 8-byte partial sums
+__host__ __device__ constexpr size_t order_lds_bytes(int B) { return sizeof(int) * ((size_t)(B + 3) / 4 * 4 + 8); }
 template <bool VARLEN>
 __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ lens, const int32_t *__restrict__ cu,
                                                   const int32_t *__restrict__ pos,
                                                   const int32_t *__restrict__ block_tables, int B, int M, int cap_rows,
-                                                  int window, int32_t *__restrict__ order, int group, int *keys);
+                                                  int window, int32_t *__restrict__ order, int group, int *keys,
+                                                  const PieceRule &pieces);
 
 // The decode step's append as its own launch: the new row of sequence s (block bt[s][(L-1)/BS], row (L-1)%BS, as
 // the fused step places it) for every kv head.  One workgroup per (sequence, kv head), each thread one 16-byte
@@ -904,7 +964,8 @@ __global__ __launch_bounds__(256) void append_newest_kernel(AppendParams p) {
     if (p.order != nullptr && blockIdx.x >= (unsigned)(p.T * p.Hkv)) {
         extern __shared__ int keys[];
         rank_into_records<false>(p.context_lens, nullptr, nullptr, p.block_tables, p.T, p.M, p.order_cap,
-                                 p.order_window, p.order, (int)(blockIdx.x - (unsigned)(p.T * p.Hkv)), keys);
+                                 p.order_window, p.order, (int)(blockIdx.x - (unsigned)(p.T * p.Hkv)), keys,
+                                 p.pieces);
         return;
     }
     const int s = (int)(blockIdx.x / (unsigned)p.Hkv);
@@ -1000,7 +1061,7 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
     const unsigned appends = (unsigned)num_seqs * per_seq;
     if (blockIdx.x >= appends) {
         rank_into_records<true>(nullptr, cu, pos, p.block_tables, num_seqs, p.M, p.order_cap, 0, p.order,
-                                (int)(blockIdx.x - appends), reinterpret_cast<int *>(panel_lds));
+                                (int)(blockIdx.x - appends), reinterpret_cast<int *>(panel_lds), PieceRule{});
         return;
     }
     const int s = (int)(blockIdx.x / per_seq);
@@ -1077,18 +1138,21 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
 // workgroup holds all B keys in LDS (padded to a multiple of 4 with -1, which never counts) and ranks 64 sequences,
 // four lanes per sequence, each lane scanning a quarter of the keys 16 bytes at a time; the quad sums its counts.
 // One workgroup's share (sequences group * 64 ..) of the ranking; keys: LDS for all B keys, rounded up to 4.
-// Decode (VARLEN false): key = rows attended, min(clamp(L, 0, cap_rows), window) with window > 0; record = sequence,
-// context_lens[s], then its first kOrderRecBlocks table entries.  Varlen: key = clamp(pos[s] + new rows, 0,
-// cap_rows), the rows its last new row attends; record = sequence, cu[s], cu[s + 1], pos[s], then its first
-// kVarlenRecBlocks table entries.
+// Decode (VARLEN false): key = rows attended, min(clamp(L, 0, cap_rows), window) with window > 0; records as
+// launch_order describes them (pieces.records > 0 and no window: the longest sequences split into pieces, see
+// PieceRule).  Varlen: key = clamp(pos[s] + new rows, 0, cap_rows), the rows its last new row attends; record =
+// sequence, cu[s], cu[s + 1], pos[s], then its first kVarlenRecBlocks table entries.
+// keys: LDS for all B keys rounded up to 4, plus 8 ints.
 template <bool VARLEN>
 __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ lens, const int32_t *__restrict__ cu,
                                                   const int32_t *__restrict__ pos,
                                                   const int32_t *__restrict__ block_tables, int B, int M, int cap_rows,
-                                                  int window, int32_t *__restrict__ order, int group, int *keys) {
-    constexpr int kHead = VARLEN ? 4 : 2;
+                                                  int window, int32_t *__restrict__ order, int group, int *keys,
+                                                  const PieceRule &pieces) {
+    constexpr int kHead = VARLEN ? 4 : kOrderRecHead;
     constexpr int kBlocks = kOrderRecord - kHead;
     const int B4 = (B + 3) / 4;
+    int64_t my_sum = 0;  // this thread's share of the rows of all sequences (the piece rule's fair share)
     for (int i = threadIdx.x; i < 4 * B4; i += 256) {
         int key = -1;
         if (i < B) {
@@ -1101,8 +1165,18 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
                 L = L < 0 ? 0 : (L > cap_rows ? cap_rows : L);
                 key = window > 0 && L > window ? window : L;
             }
+            my_sum += key;
         }
         keys[i] = key;
+    }
+    const bool split = !VARLEN && pieces.records > 0 && window <= 0;  // (uniform)
+    int64_t *sums = reinterpret_cast<int64_t *>(keys + 4 * B4);
+    if (split) {
+        // the sum of all keys: wave sums, then the four waves' through LDS (8-byte aligned: 4 * B4 ints is even)
+        for (int m = 32; m >= 1; m >>= 1)
+            my_sum += __shfl_xor(my_sum, m);
+        if ((threadIdx.x & 63) == 0)
+            sums[threadIdx.x >> 6] = my_sum;
     }
     const int s = group * kOrderSeqsPerGroup + (int)(threadIdx.x >> 2);
     const int part = (int)(threadIdx.x & 3);
@@ -1120,45 +1194,100 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
     __syncthreads();
     if (s >= B)
         return;  // the whole quad of s leaves together
+    // piece rows C and the piece count of a key (a function of the key alone, so every thread agrees)
+    int64_t C = INT64_MAX;
+    if (split) {
+        const int64_t total = sums[0] + sums[1] + sums[2] + sums[3];
+        const int64_t fair = (total * pieces.hkv + pieces.cus - 1) / (pieces.cus > 0 ? pieces.cus : 1);
+        C = (fair + 63) / 64 * 64;
+        C = C < kMinPieceRows ? kMinPieceRows : C;
+    }
+    auto piece_rows = [&](int key) -> int {  // rows of each piece but the last
+        if (key <= C)
+            return key;
+        const int64_t n = (key + C - 1) / C;
+        return (int)(((key + n - 1) / n + 63) / 64 * 64);
+    };
+    auto piece_count = [&](int key) -> int {
+        if (key <= C)
+            return 1;
+        const int pr = piece_rows(key);
+        return (key + pr - 1) / pr;
+    };
     const int ks = keys[s];
-    int rank = 0;
+    int rank = 0, start = 0;
     const int4 *k4 = reinterpret_cast<const int4 *>(keys);
 #pragma unroll 4
     for (int j4 = part; j4 < B4; j4 += 4) {
         const int4 kv = k4[j4];
         const int j = 4 * j4;
-        rank += (kv.x > ks || (kv.x == ks && j < s)) ? 1 : 0;
-        rank += (kv.y > ks || (kv.y == ks && j + 1 < s)) ? 1 : 0;
-        rank += (kv.z > ks || (kv.z == ks && j + 2 < s)) ? 1 : 0;
-        rank += (kv.w > ks || (kv.w == ks && j + 3 < s)) ? 1 : 0;
+        const bool bx = kv.x > ks || (kv.x == ks && j < s);
+        const bool by = kv.y > ks || (kv.y == ks && j + 1 < s);
+        const bool bz = kv.z > ks || (kv.z == ks && j + 2 < s);
+        const bool bw = kv.w > ks || (kv.w == ks && j + 3 < s);
+        rank += (bx ? 1 : 0) + (by ? 1 : 0) + (bz ? 1 : 0) + (bw ? 1 : 0);
+        if (split)
+            start += (bx ? piece_count(kv.x) : 0) + (by ? piece_count(kv.y) : 0) + (bz ? piece_count(kv.z) : 0) +
+                     (bw ? piece_count(kv.w) : 0);
     }
     rank += __shfl_xor(rank, 1);
     rank += __shfl_xor(rank, 2);
-    int32_t *rec = order + (int64_t)rank * kOrderRecord;
-    if (part == 0) {
-        rec[0] = s;
-        if (VARLEN) {
-            rec[1] = cu[s];
-            rec[2] = cu[s + 1];
-            rec[3] = pos[s];
-        } else {
-            rec[1] = lens[s];
-        }
+    start += __shfl_xor(start, 1);
+    start += __shfl_xor(start, 2);
+    if (!split)
+        start = rank;
+    const int n = split ? piece_count(ks) : 1;
+    const int pr = split ? piece_rows(ks) : 0;
+    if (split) {
+        // this launch's piece counters start at zero
+        for (int h = part; h < pieces.hkv; h += 4)
+            pieces.counters[(int64_t)s * pieces.hkv + h] = 0;
+        // the last sequence in the order marks the records past the last piece unused
+        if (rank == B - 1)
+            for (int r = start + n + part; r < pieces.records; r += 4)
+                order[(int64_t)r * kOrderRecord] = -1;
     }
+    for (int pc = 0; pc < n; ++pc) {
+        if (split && start + pc >= pieces.records)
+            break;  // (never: the extra records number less than cus / hkv)
+        int32_t *rec = order + (int64_t)(start + pc) * kOrderRecord;
+        const int u0 = pc * (pr / 16);
+        if (part == 0) {
+            rec[0] = s;
+            if (VARLEN) {
+                rec[1] = cu[s];
+                rec[2] = cu[s + 1];
+                rec[3] = pos[s];
+            } else {
+                rec[1] = lens[s];
+                rec[2] = u0;
+                rec[3] = pc + 1 < n ? u0 + pr / 16 : INT32_MAX;
+                rec[4] = pc | (n << 16);
+                rec[5] = start;
+            }
+        }
+        if (pc == 0) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int i = part + 4 * k;
-        if (i < nb)
-            rec[kHead + i] = ids[k];
+            for (int k = 0; k < kPer; ++k) {
+                const int i = part + 4 * k;
+                if (i < nb)
+                    rec[kHead + i] = ids[k];
+            }
+        } else {  // a later piece: the entries from its first block (pieces start on a block)
+            const int b0 = u0 * 16 / pieces.block_size;
+            for (int i = part; i < kBlocks && b0 + i < M; i += 4)
+                rec[kHead + i] = trow[b0 + i];
+        }
     }
 }
 
 __global__ __launch_bounds__(256) void order_kernel(const int32_t *__restrict__ lens,
                                                     const int32_t *__restrict__ block_tables, int B, int M,
-                                                    int cap_rows, int window, int32_t *__restrict__ order) {
+                                                    int cap_rows, int window, int32_t *__restrict__ order,
+                                                    PieceRule pieces) {
     extern __shared__ int keys[];
     rank_into_records<false>(lens, nullptr, nullptr, block_tables, B, M, cap_rows, window, order, (int)blockIdx.x,
-                             keys);
+                             keys, pieces);
 }
 
 __global__ __launch_bounds__(256) void order_varlen_kernel(const int32_t *__restrict__ cu,
@@ -1166,7 +1295,8 @@ __global__ __launch_bounds__(256) void order_varlen_kernel(const int32_t *__rest
                                                            const int32_t *__restrict__ block_tables, int B, int M,
                                                            int cap_rows, int32_t *__restrict__ order) {
     extern __shared__ int keys[];
-    rank_into_records<true>(nullptr, cu, pos, block_tables, B, M, cap_rows, 0, order, (int)blockIdx.x, keys);
+    rank_into_records<true>(nullptr, cu, pos, block_tables, B, M, cap_rows, 0, order, (int)blockIdx.x, keys,
+                            PieceRule{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1174,7 +1304,9 @@ __global__ __launch_bounds__(256) void order_varlen_kernel(const int32_t *__rest
 
 template <int D, int BS, int NW>
 static hipError_t launch_decode_t(const DecodeParams &p, int num_seqs, bool split, hipStream_t stream) {
-    dim3 grid((unsigned)((int64_t)num_seqs * p.Hkv * (split ? p.num_splits : 1)), 1u, 1u);
+    // an ordered single pass has a workgroup per (record, kv head); a record may be a piece of a sequence
+    const int64_t rows = p.order != nullptr && !split && p.order_records > 0 ? p.order_records : num_seqs;
+    dim3 grid((unsigned)(rows * p.Hkv * (split ? p.num_splits : 1)), 1u, 1u);
     dim3 block(NW * 64);
     const size_t lds = decode_lds_bytes(D, p.G, NW);
     const bool fused = p.k_new != nullptr;
@@ -1321,7 +1453,7 @@ hipError_t launch_append_newest(const AppendParams &p, hipStream_t stream) {
     if (p.order != nullptr && p.T > kOrderMaxSeqs)
         return hipErrorInvalidValue;
     const unsigned order_groups = p.order ? (unsigned)((p.T + kOrderSeqsPerGroup - 1) / kOrderSeqsPerGroup) : 0u;
-    const size_t lds = p.order ? sizeof(int) * (size_t)((p.T + 3) / 4 * 4) : 0;
+    const size_t lds = p.order ? order_lds_bytes(p.T) : 0;
     hipLaunchKernelGGL(append_newest_kernel, dim3((unsigned)((int64_t)p.T * p.Hkv) + order_groups), dim3(256), lds,
                        stream, p);
     return hipGetLastError();
@@ -1340,7 +1472,7 @@ hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens
     const int64_t panels = (int64_t)num_seqs * p.Hkv * units;
     if (units > 0 && p.T > 0 && p.D <= 256 && panels + order_groups <= kMaxGroups) {
         const size_t stage = sizeof(_Float16) * 2 * 16 * (size_t)p.D;
-        const size_t keys = p.order ? sizeof(int) * (size_t)((num_seqs + 3) / 4 * 4) : 0;
+        const size_t keys = p.order ? order_lds_bytes(num_seqs) : 0;
         hipLaunchKernelGGL(append_varlen_panels_kernel, dim3((unsigned)panels + order_groups), dim3(256),
                            stage > keys ? stage : keys, stream, p, cu_seqlens_q, pos_offsets, num_seqs, (int)units);
         return hipGetLastError();
@@ -1360,12 +1492,11 @@ hipError_t launch_append_varlen(const AppendParams &p, const int32_t *cu_seqlens
 }
 
 hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables, int B, int M, int cap_rows,
-                        int window, int32_t *order, hipStream_t stream) {
+                        int window, int32_t *order, const PieceRule &pieces, hipStream_t stream) {
     if (B <= 0 || B > kOrderMaxSeqs)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(order_kernel, dim3((unsigned)((B + kOrderSeqsPerGroup - 1) / kOrderSeqsPerGroup)), dim3(256),
-                       sizeof(int) * (size_t)((B + 3) / 4 * 4), stream, context_lens, block_tables, B, M, cap_rows,
-                       window, order);
+                       order_lds_bytes(B), stream, context_lens, block_tables, B, M, cap_rows, window, order, pieces);
     return hipGetLastError();
 }
 
@@ -1374,7 +1505,7 @@ hipError_t launch_order_varlen(const int32_t *cu_seqlens_q, const int32_t *pos_o
     if (B <= 0 || B > kOrderMaxSeqs)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(order_varlen_kernel, dim3((unsigned)((B + kOrderSeqsPerGroup - 1) / kOrderSeqsPerGroup)),
-                       dim3(256), sizeof(int) * (size_t)((B + 3) / 4 * 4), stream, cu_seqlens_q, pos_offsets,
+                       dim3(256), order_lds_bytes(B), stream, cu_seqlens_q, pos_offsets,
                        block_tables, B, M, cap_rows, order);
     return hipGetLastError();
 }

@@ -24,6 +24,15 @@ constexpr int kMaxWaves = 8;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Relaxed agent-scope vector stores and loads: they reach the memory side, coherent across the XCDs' L2 caches,
+// without a cache-wide write-back or invalidate.
+__device__ __forceinline__ void store_agent(float *p, float x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
 // Reductions over the four 16-lane rows that hold the same MFMA column (lanes r, r+16, r+32, r+48), on the VALU

@@ -24,7 +24,7 @@ hipError_t launch_combine(const CombineParams &, int, hipStream_t) { return stub
 hipError_t launch_varlen(const VarlenParams &, int, int, int, int, bool, hipStream_t) { return stub("varlen"); }
 hipError_t launch_append(const AppendParams &, hipStream_t) { return stub("append"); }
 hipError_t launch_append_newest(const AppendParams &, hipStream_t) { return stub("append_newest"); }
-hipError_t launch_order(const int32_t *, const int32_t *, int, int, int, int, int32_t *, hipStream_t) {
+hipError_t launch_order(const int32_t *, const int32_t *, int, int, int, int, int32_t *, const PieceRule &, hipStream_t) {
     return stub("order");
 }
 hipError_t launch_order_varlen(const int32_t *, const int32_t *, const int32_t *, int, int, int, int32_t *,
