@@ -186,7 +186,8 @@ constexpr int kOrderRecBlocks = kOrderRecord - kOrderRecHead;
 // longest first, ties by index; a sequence split into n pieces (see PieceRule) takes n consecutive records.
 // order[r][0] = sequence (-1: an unused record), [1] = context_lens[sequence], [2] = the piece's first 16-row unit,
 // [3] = its end unit (INT32_MAX: the sequence's end), [4] = piece index | n << 16, [5] = the record of piece 0,
-// [6 + i] = table entry (first unit / units per block) + i, i < kOrderRecBlocks.
+// [6 + i] = table entry i, i < kOrderRecBlocks (piece 0 and whole sequences only: a later piece's workgroups read
+// their first entries from the table).
 hipError_t launch_order(const int32_t *context_lens, const int32_t *block_tables, int B, int M, int cap_rows,
                         int window, int32_t *order, const PieceRule &pieces, hipStream_t stream);
 // Varlen records: order[rank][0] = sequence, [1] = cu_seqlens_q[s], [2] = cu_seqlens_q[s + 1], [3] = pos_offsets[s],

@@ -136,6 +136,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 
     if (unused_rec)
         return;
+    if (ORDERED && !SPLIT && start_known && (pc_rec & 0xffff) != 0) {
+        // a later piece's record holds no block ids: its first ones come from the table (one more dependent load,
+        // for the few workgroups of the pieces past the first)
+#pragma unroll
+        for (int j = 0; j < NSPEC; ++j)
+            spec_raw[j] = uniform_load(bt, min(u0_rec + u_known + j * NW, max_units - 1) / SPB);
+    }
     L = L < 0 ? 0 : (L > p.M * BS ? p.M * BS : L);
     if (p.N <= 0)
         L = 0;  // an empty pool holds no rows
@@ -1138,6 +1145,15 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
 // workgroup holds all B keys in LDS (padded to a multiple of 4 with -1, which never counts) and ranks 64 sequences,
 // four lanes per sequence, each lane scanning a quarter of the keys 16 bytes at a time; the quad sums its counts.
 // One workgroup's share (sequences group * 64 ..) of the ranking; keys: LDS for all B keys, rounded up to 4.
+// A key (rows) longer than the piece rows C in pieces: ceil(key / C) pieces of equal rows rounded up to 64 (so each
+// starts on a block), and the count of those pieces that the key fills: (rows of each but the last, pieces).  Out of
+// line: the ranking calls it only for the rare keys past C.
+__device__ __noinline__ int2 piece_split(int key, int C) {
+    const int64_t n = ((int64_t)key + C - 1) / C;
+    const int64_t pr = (((int64_t)key + n - 1) / n + 63) / 64 * 64;
+    return make_int2((int)pr, (int)(((int64_t)key + pr - 1) / pr));
+}
+
 // Decode (VARLEN false): key = rows attended, min(clamp(L, 0, cap_rows), window) with window > 0; records as
 // launch_order describes them (pieces.records > 0 and no window: the longest sequences split into pieces, see
 // PieceRule).  Varlen: key = clamp(pos[s] + new rows, 0, cap_rows), the rows its last new row attends; record =
@@ -1194,28 +1210,17 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
     __syncthreads();
     if (s >= B)
         return;  // the whole quad of s leaves together
-    // piece rows C and the piece count of a key (a function of the key alone, so every thread agrees)
-    int64_t C = INT64_MAX;
+    // piece rows C (a key longer than C is split): INT32_MAX when nothing is split, so that every key compares
+    // below it
+    int C = INT32_MAX;
     if (split) {
         const int64_t total = sums[0] + sums[1] + sums[2] + sums[3];
         const int64_t fair = (total * pieces.hkv + pieces.cus - 1) / (pieces.cus > 0 ? pieces.cus : 1);
-        C = (fair + 63) / 64 * 64;
-        C = C < kMinPieceRows ? kMinPieceRows : C;
+        const int64_t c = (fair + 63) / 64 * 64;
+        C = c < kMinPieceRows ? kMinPieceRows : (c > INT32_MAX ? INT32_MAX : (int)c);
     }
-    auto piece_rows = [&](int key) -> int {  // rows of each piece but the last
-        if (key <= C)
-            return key;
-        const int64_t n = (key + C - 1) / C;
-        return (int)(((key + n - 1) / n + 63) / 64 * 64);
-    };
-    auto piece_count = [&](int key) -> int {
-        if (key <= C)
-            return 1;
-        const int pr = piece_rows(key);
-        return (key + pr - 1) / pr;
-    };
     const int ks = keys[s];
-    int rank = 0, start = 0;
+    int rank = 0, extra = 0;  // extra: the pieces past the first of the sequences ranked before s
     const int4 *k4 = reinterpret_cast<const int4 *>(keys);
 #pragma unroll 4
     for (int j4 = part; j4 < B4; j4 += 4) {
@@ -1226,18 +1231,23 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
         const bool bz = kv.z > ks || (kv.z == ks && j + 2 < s);
         const bool bw = kv.w > ks || (kv.w == ks && j + 3 < s);
         rank += (bx ? 1 : 0) + (by ? 1 : 0) + (bz ? 1 : 0) + (bw ? 1 : 0);
-        if (split)
-            start += (bx ? piece_count(kv.x) : 0) + (by ? piece_count(kv.y) : 0) + (bz ? piece_count(kv.z) : 0) +
-                     (bw ? piece_count(kv.w) : 0);
+        if (bx && kv.x > C)  // (rare: only keys past a CU's fair share)
+            extra += piece_split(kv.x, C).y - 1;
+        if (by && kv.y > C)
+            extra += piece_split(kv.y, C).y - 1;
+        if (bz && kv.z > C)
+            extra += piece_split(kv.z, C).y - 1;
+        if (bw && kv.w > C)
+            extra += piece_split(kv.w, C).y - 1;
     }
     rank += __shfl_xor(rank, 1);
     rank += __shfl_xor(rank, 2);
-    start += __shfl_xor(start, 1);
-    start += __shfl_xor(start, 2);
-    if (!split)
-        start = rank;
-    const int n = split ? piece_count(ks) : 1;
-    const int pr = split ? piece_rows(ks) : 0;
+    extra += __shfl_xor(extra, 1);
+    extra += __shfl_xor(extra, 2);
+    const int start = rank + extra;
+    const int2 split_s = ks > C ? piece_split(ks, C) : make_int2(ks, 1);
+    const int pr = split_s.x;
+    const int n = split_s.y;
     if (split) {
         // this launch's piece counters start at zero
         for (int h = part; h < pieces.hkv; h += 4)
@@ -1266,17 +1276,13 @@ __device__ __forceinline__ void rank_into_records(const int32_t *__restrict__ le
                 rec[5] = start;
             }
         }
-        if (pc == 0) {
+        if (pc == 0) {  // (a later piece's workgroups read their first block ids from the table themselves)
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 const int i = part + 4 * k;
                 if (i < nb)
                     rec[kHead + i] = ids[k];
             }
-        } else {  // a later piece: the entries from its first block (pieces start on a block)
-            const int b0 = u0 * 16 / pieces.block_size;
-            for (int i = part; i < kBlocks && b0 + i < M; i += 4)
-                rec[kHead + i] = trow[b0 + i];
         }
     }
 }
