@@ -412,14 +412,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     {
         const float a = exp2_fast(m_run - Mc);
         const float f = SPLIT || piece ? a : (den > 0.f ? a / den : 0.f);
-        if (r < p.G) {
+        if (r < p.G) {  // 16-byte writes: with DP = D + 4 the eight lanes of a pass hit distinct banks
             float *dst = sm_o + (wave * p.G + r) * DP + 4 * g4;
 #pragma unroll
-            for (int c = 0; c < VC; ++c) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dst[16 * c + e] = o[c][e] * f;
-            }
+            for (int c = 0; c < VC; ++c)
+                *reinterpret_cast<f32x4 *>(dst + 16 * c) = o[c] * f;
         }
         if (SPLIT && wave == 0 && g4 == 0 && r < p.G) {
             const int64_t base = ((int64_t)s * p.Hq + hk * p.G + r) * p.num_splits + split;
@@ -434,21 +431,29 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     }
     __syncthreads();
 
-    const int total = p.G * D;
-    for (int idx = threadIdx.x; idx < total; idx += NW * 64) {
-        const int h = idx / D;
-        const int d = idx - h * D;
-        float num = 0.f;
+    // Four dims per thread: 16-byte LDS reads, the waves summed in order from 0 (the same sums as one dim at a time)
+    const int total4 = p.G * (D / 4);
+    for (int idx = threadIdx.x; idx < total4; idx += NW * 64) {
+        const int h = idx / (D / 4);
+        const int d = 4 * (idx - h * (D / 4));
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < NW; ++w)
-            num += sm_o[(w * p.G + h) * DP + d];
+            num += *reinterpret_cast<const f32x4 *>(sm_o + (w * p.G + h) * DP + d);
         const int64_t row = (int64_t)s * p.Hq + hk * p.G + h;
-        if (SPLIT)
-            p.part_o[(row * p.num_splits + split) * D + d] = num;
-        else if (piece)
-            store_agent(p.part_o + ((int64_t)rank * p.Hq + hk * p.G + h) * D + d, num);
-        else
-            p.out[row * D + d] = (_Float16)num;
+        if (SPLIT) {
+            *reinterpret_cast<f32x4 *>(p.part_o + (row * p.num_splits + split) * D + d) = num;
+        } else if (piece) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                store_agent(p.part_o + ((int64_t)rank * p.Hq + hk * p.G + h) * D + d + e, num[e]);
+        } else {
+            f16x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                y[e] = (_Float16)num[e];
+            *reinterpret_cast<f16x4 *>(p.out + row * D + d) = y;
+        }
     }
     if (piece) {
         // The pieces of a (sequence, kv head) meet at their ends only: each stores its partial with agent-coherent
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
                                              __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (seen[0] == npieces - 1) {
-            for (int idx = threadIdx.x; idx < total; idx += NW * 64) {
+            for (int idx = threadIdx.x; idx < p.G * D; idx += NW * 64) {
                 const int h = idx / D;
                 const int d = idx - h * D;
                 const int64_t hq = (int64_t)hk * p.G + h;
@@ -573,34 +578,67 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
 
     // Fused step: units nu0 .. nu0 + n_new_units - 1 hold the new rows pos .. pos + qlen - 1.  The wave that computes
     // unit u in every tile group (u % NW: with one pass the range starts at unit 0) copies that unit's new rows to
-    // its LDS slot (K [16][D] row-major, then V [D][16]; rows that are not new stay unset and are never read) before
-    // its first K/V loads.  (Copying after them costs more: the copy's wait then covers the whole first unit, and
-    // direct global-to-LDS loads make the compiler wait for every load in flight before each unit.)
+    // its LDS slot (K [16][D] row-major, then V [D][16]; rows that are not new stay unset and are never read).  Its
+    // first kPreChunks 16-byte chunks per lane of K and of V are loaded into registers before any K/V load and
+    // written to LDS once the first units' loads are in flight, so that the wait for them covers only these older
+    // loads (a wave's loads retire in order: copying through LDS before the first K/V loads held the owner wave's
+    // stream back by a round trip, and loading the rows after them made the wait cover the whole first unit).
+    // Chunks past those (more new rows in the unit than the registers hold), and the units of a wave that owns more
+    // than one, are copied at once, the slow way.
     const int nu0 = pos >> 4;
     const int n_new_units = FUSED && qlen > 0 ? min(kFusedUnits, ((pos + qlen - 1) >> 4) - nu0 + 1) : 0;
     _Float16 *sm_new = reinterpret_cast<_Float16 *>(smem + merge_floats(D, 16, NW));
-    if (FUSED) {
-        for (int k = 0; k < n_new_units; ++k) {
-            const int u = nu0 + k;
-            if (u % NW != wave)
-                continue;
-            const int row0 = max(pos, 16 * u), row1 = min(pos + qlen, 16 * u + 16);
-            _Float16 *slot_k = sm_new + k * 32 * D;
-            _Float16 *slot_v = slot_k + 16 * D;
-            // lane-strided 16-byte chunks of the unit's new rows: chunk = row * (D / 8) + piece
-            for (int c = lane; c < (row1 - row0) * (D / 8); c += 64) {
-                const int rr = c / (D / 8), piece = c - rr * (D / 8);
-                const int64_t src = ((int64_t)(q0 + row0 - pos + rr) * p.Hkv + hk) * D + 8 * piece;
-                const int row = row0 - 16 * u + rr;
-                *reinterpret_cast<f16x8 *>(slot_k + row * D + 8 * piece) =
-                    *reinterpret_cast<const f16x8 *>(p.k_new + src);
-                const f16x8 vv = *reinterpret_cast<const f16x8 *>(p.v_new + src);
+    constexpr int kPreChunks = 2;
+    // new unit k (of n_new_units): its new rows start at unit row row0_of(k); chunk c = row * (D / 8) + piece
+    auto row0_of = [&](int k) { return max(pos, 16 * (nu0 + k)) - 16 * (nu0 + k); };
+    auto rows_of = [&](int k) { return min(pos + qlen, 16 * (nu0 + k) + 16) - 16 * (nu0 + k) - row0_of(k); };
+    auto chunk_src = [&](int k, int c) {  // offset of chunk c of unit k in k_new / v_new
+        const int rr = c / (D / 8), piece = c - rr * (D / 8);
+        return ((int64_t)(q0 + 16 * (nu0 + k) + row0_of(k) - pos + rr) * p.Hkv + hk) * D + 8 * piece;
+    };
+    auto chunk_to_lds = [&](int k, int c, const f16x8 &kk, const f16x8 &vv) {
+        const int rr = c / (D / 8), piece = c - rr * (D / 8);
+        const int row = row0_of(k) + rr;
+        _Float16 *slot_k = sm_new + k * 32 * D;
+        _Float16 *slot_v = slot_k + 16 * D;
+        *reinterpret_cast<f16x8 *>(slot_k + row * D + 8 * piece) = kk;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    slot_v[(8 * piece + e) * 16 + row] = vv[e];
+        for (int e = 0; e < 8; ++e)
+            slot_v[(8 * piece + e) * 16 + row] = vv[e];
+    };
+    auto copy_now = [&](int k, int c0) {  // chunks c0, c0 + 64, ... of unit k, lane-strided, waited for at once
+        for (int c = c0 + lane; c < rows_of(k) * (D / 8); c += 64)
+            chunk_to_lds(k, c, *reinterpret_cast<const f16x8 *>(p.k_new + chunk_src(k, c)),
+                         *reinterpret_cast<const f16x8 *>(p.v_new + chunk_src(k, c)));
+    };
+    const int own = (wave - nu0 % NW + NW) % NW;  // the wave's first unit among the new ones, if < n_new_units
+    const bool owner = FUSED && own < n_new_units;  // (wave-uniform)
+    f16x8 pre_k[kPreChunks], pre_v[kPreChunks];
+    if (owner) {
+#pragma unroll
+        for (int i = 0; i < kPreChunks; ++i) {
+            const int c = lane + 64 * i;
+            if (c < rows_of(own) * (D / 8)) {
+                pre_k[i] = *reinterpret_cast<const f16x8 *>(p.k_new + chunk_src(own, c));
+                pre_v[i] = *reinterpret_cast<const f16x8 *>(p.v_new + chunk_src(own, c));
             }
         }
+        copy_now(own, 64 * kPreChunks);
+        for (int k = own + NW; k < n_new_units; k += NW)  // fewer waves than new units: the wave's other units
+            copy_now(k, 0);
     }
+    bool pre_pending = owner;  // the register chunks still wait to be written to LDS (before the owned unit's patch)
+    auto flush_pre = [&]() {
+        if (pre_pending) {
+#pragma unroll
+            for (int i = 0; i < kPreChunks; ++i) {
+                const int c = lane + 64 * i;
+                if (c < rows_of(own) * (D / 8))
+                    chunk_to_lds(own, c, pre_k[i], pre_v[i]);
+            }
+            pre_pending = false;
+        }
+    };
     auto raw_block = [&](int u) -> int { return uniform_load(bt, min(u, max_units - 1) / SPB); };
     auto resolve = [&](int raw, bool &dead) -> int {
         const int b = __builtin_amdgcn_readfirstlane(raw);
@@ -684,6 +722,8 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
             for (int j = 0; j < NS; ++j)
                 raw_q[j] = start_known ? spec_raw[NS - 1 + j]
                                        : raw_block(u_first + min(NS - 1 + j, n_units - 1) * NW);
+            if (FUSED)
+                flush_pre();
             int k = 0;
             for (;;) {
 #pragma unroll
@@ -747,14 +787,11 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
             {
                 const float a = exp2_fast(m_run[t] - Mc);
                 const float fs = SPLIT ? a : (den > 0.f ? a / den : 0.f);
-                if (col_ok[t]) {
+                if (col_ok[t]) {  // 16-byte writes: with DP = D + 4 the eight lanes of a pass hit distinct banks
                     float *dst = sm_o + (wave * 16 + r) * DP + 4 * g4;
 #pragma unroll
-                    for (int c = 0; c < VC; ++c) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            dst[16 * c + e] = o[t][c][e] * fs;
-                    }
+                    for (int c = 0; c < VC; ++c)
+                        *reinterpret_cast<f32x4 *>(dst + 16 * c) = o[t][c] * fs;
                 }
                 if (SPLIT && wave == 0 && g4 == 0 && col_ok[t]) {
                     // a split without rows (b0 >= b1) leaves M = -1e30 and l = 0: weight 0 in the combine
@@ -763,19 +800,25 @@ __global__ __launch_bounds__(NW * 64) void varlen_kernel(VarlenParams p) {
                 }
             }
             __syncthreads();
+            // four dims per thread, as in decode_kernel
             const int ncols = nrows[t] * p.G;
-            for (int idx = threadIdx.x; idx < ncols * D; idx += NW * 64) {
-                const int c = idx / D;
-                const int d = idx - c * D;
-                float num = 0.f;
+            for (int idx = threadIdx.x; idx < ncols * (D / 4); idx += NW * 64) {
+                const int c = idx / (D / 4);
+                const int d = 4 * (idx - c * (D / 4));
+                f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int w = 0; w < NW; ++w)
-                    num += sm_o[(w * 16 + c) * DP + d];
+                    num += *reinterpret_cast<const f32x4 *>(sm_o + (w * 16 + c) * DP + d);
                 const int64_t row = (int64_t)(q0 + i0[t] + c / p.G) * p.Hq + hk * p.G + c % p.G;  // token * Hq + hq
-                if (!SPLIT)
-                    p.out[row * D + d] = (_Float16)num;
-                else
-                    p.part_o[(row * p.num_splits + split) * D + d] = num;
+                if (!SPLIT) {
+                    f16x4 y;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        y[e] = (_Float16)num[e];
+                    *reinterpret_cast<f16x4 *>(p.out + row * D + d) = y;
+                } else {
+                    *reinterpret_cast<f32x4 *>(p.part_o + (row * p.num_splits + split) * D + d) = num;
+                }
             }
         }
     }
