@@ -240,8 +240,8 @@ PKV_API int pkv_paged_decode_attention_noalloc(const uint16_t *q, const uint16_t
  *   table entry names no pool block is not written.
  *   Launches: when the attention grid (num_seqs * Hkv * splits workgroups)
  *   fits one round of the device's CUs, a single fused launch whose workgroups
- *   write the new rows themselves (the 16-row panel holding a new row is
- *   written back whole, its other rows unchanged); otherwise the append kernel
+ *   write the new rows themselves (the row's K runs and the 128-byte V lines
+ *   of its quad of rows, the quad's other rows unchanged); otherwise the append kernel
  *   (which also ranks the sequences for the dispatch order described under
  *   pkv_paged_decode_attention) then attention, in stream order.  Results are
  *   identical either way.
@@ -275,8 +275,8 @@ PKV_API int pkv_paged_decode_step(const uint16_t *q, const uint16_t *k_new, cons
  *   max_positions gives unspecified results (never an access outside the
  *   tables).
  *   Launches: when the attention grid fits one round of the device's CUs, one
- *   launch forms q and the new K/V rows in its prologue (the 16-row panel
- *   holding each new row is written back whole, as in pkv_paged_decode_step);
+ *   launch forms q and the new K/V rows in its prologue (and writes them as
+ *   pkv_paged_decode_step does);
  *   otherwise the QKV kernel, then attention.  The two routes agree to within
  *   f32 summation order (the RMS sums are reduced in different orders), not
  *   bit for bit.  The block holding each sequence's newest row must belong to
@@ -392,9 +392,9 @@ PKV_API int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool
  *   split_qkv_norm_rope_into_paged_cache_varlen, which puts them there]
  *   Launches: one pass with max_q_len <= 32 and no more workgroups than the
  *   device's CUs gives one launch whose workgroups write the new rows
- *   themselves (each 16-row panel holding new rows is written back whole,
- *   its other rows unchanged); otherwise a launch writes the new rows (also
- *   as whole panels, and with a grid of more workgroups than CUs it ranks
+ *   themselves (the new rows' K runs and the V lines of their quads of rows,
+ *   other rows unchanged); otherwise a launch writes the new rows (as whole
+ *   panels, and with a grid of more workgroups than CUs it ranks
  *   the sequences for the attention launch's dispatch order), then attention
  *   runs.  Results are identical either way.
  *   k_new, v_new: [total_q_tokens][Hkv][D] fp16, 16-byte aligned.

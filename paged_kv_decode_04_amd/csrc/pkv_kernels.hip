@@ -169,8 +169,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const int n_units = u_first < u_end ? (u_end - u_first + NW - 1) / NW : 0;
     // Fused decode step: the workgroup whose range holds row L-1 writes the sequence's new K/V row there (the slot
     // the callers form from the table: block bt[(L-1)/BS], row (L-1)%BS).  The wave that computes the unit holding
-    // row L-1 loads the row, keeps a copy in LDS and, when it computes that unit, writes the unit's panels back
-    // with the row in place (see compute_unit).
+    // row L-1 loads the row, keeps a copy in LDS and, when it computes that unit, patches it into the fragments and
+    // writes its K runs and V quad back (see compute_unit).
     const bool appending = FUSED && L > 0 && (L - 1) / BS >= b0 && (L - 1) / BS < b1;
     const int patch_unit = appending ? (L - 1) >> 4 : -1;
     const int prow_row = (L - 1) & 15;
@@ -508,7 +508,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 // the combine needs no per-row split count.
 // FUSED (the fused varlen step, single pass): the new rows' K/V (k_new / v_new, token-major) are written into the
 // pools by this launch -- each 16-row unit holding new rows is patched from an LDS copy of its new rows whenever it
-// is computed and written back whole, so any interleaving of workgroups leaves the same bytes -- for the first
+// is computed, and the new rows' K runs and V quads are written back, so any interleaving of workgroups leaves the
+// same bytes -- for the first
 // kFusedUnits units of a sequence's new rows: any kStepFusedRows consecutive rows fit.
 
 template <int D, int BS, int NW, bool SPLIT, int QT, bool FUSED = false, bool ORDERED = false>
