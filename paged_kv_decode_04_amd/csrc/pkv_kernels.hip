@@ -1096,10 +1096,11 @@ __global__ __launch_bounds__(256) void append_varlen_kernel(AppendParams p, cons
         vdst[e * 4] = vh[e];
 }
 
-// The varlen step's append in whole panels: workgroup (s, h, j) takes the j-th 16-row unit that sequence s's new
-// rows touch (rows pos[s] .. pos[s] + n - 1, n = cu[s+1] - cu[s], clipped to 0 .. M*BS - 1), stages those rows of kv
-// head h in LDS and rewrites the unit's K and V panels whole, new rows from LDS and the others as read, so the pools
-// see full-line writes only (as append_newest_kernel; the per-row form above scatters 2-byte V stores).  Valid only
+// The varlen step's append by panel: workgroup (s, h, j) takes the j-th 16-row unit that sequence s's new rows touch
+// (rows pos[s] .. pos[s] + n - 1, n = cu[s+1] - cu[s], clipped to 0 .. M*BS - 1), stages those rows of kv head h in
+// LDS and writes their K runs and the V quads that hold them, the quads' old rows as read, so the pools see
+// whole-sector and whole-line writes only (as append_newest_kernel; the per-row form above scatters 2-byte V stores;
+// rewriting both panels whole moved 5x the new rows' bytes).  Valid only
 // because the blocks receiving a sequence's new rows belong to that sequence alone.  units: unit slots per sequence,
 // enough for max_q_len rows from any offset in a unit; rows past them are not written.  With p.order set, the
 // workgroups past num_seqs * Hkv * units write the varlen dispatch-order records instead (as order_varlen_kernel;
@@ -1133,20 +1134,19 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
     const int a = (int)((lo > r0 ? lo : r0) - r0);         // new rows of the unit: a .. e - 1
     const int e = (int)((hi < r0 + 16 ? hi : r0 + 16) - r0);
     const int64_t panel = ((int64_t)b * p.Hkv + h) * p.BS * p.D + (r0 % p.BS) * p.D;
-    // The panels' chunks that keep old rows, read before the staging so both sets of loads are in flight together.
-    // K panel [D/32][16][32]: chunk q is dims 8 * (4 * (q / 64) + q % 4) .. +8 of row (q / 4) % 16.  V panel
-    // [4][D][4]: chunk q is dims 2*(q % (D/2)) and the next of quad q / (D/2), i.e. of rows 4*(q / (D/2)) .. +4.
+    // Only what holds new rows is written: in the K panel [D/32][16][32] (chunk q: dims 8 * (4 * (q / 64) + q % 4)
+    // .. +8 of row (q / 4) % 16) a new row's own 64-byte runs, which need no read; in the V panel [4][D][4] (chunk q:
+    // dims 2*(q % (D/2)) and the next of quad q / (D/2), i.e. of rows 4*(q / (D/2)) .. +4) the quads that hold new
+    // rows, whole 128-byte lines -- a quad that also holds old rows is read first (before the staging, so both sets
+    // of loads are in flight together) and written back with them unchanged.
     const int qpd = p.D / 2;  // V chunks per quad
-    f16x8 kc[2] = {}, vc[2] = {};
+    f16x8 vc[2] = {};
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int q = (int)threadIdx.x + 256 * it;
         if (q < 2 * p.D) {
-            const int kr = (q >> 2) & 15;
-            if (kr < a || kr >= e)
-                kc[it] = *reinterpret_cast<const f16x8 *>(p.k_pool + panel + 8 * q);
             const int vr = 4 * (q / qpd);
-            if (vr < a || vr + 4 > e)
+            if (vr + 3 >= a && vr < e && (vr < a || vr + 4 > e))
                 vc[it] = *reinterpret_cast<const f16x8 *>(p.v_pool + panel + 8 * q);
         }
     }
@@ -1170,16 +1170,17 @@ __global__ __launch_bounds__(256) void append_varlen_panels_kernel(AppendParams 
         if (q < 2 * p.D) {
             const int kr = (q >> 2) & 15;
             if (kr >= a && kr < e)
-                kc[it] = kst[kr * pieces + 4 * (q >> 6) + (q & 3)];
-            *reinterpret_cast<f16x8 *>(p.k_pool + panel + 8 * q) = kc[it];
+                *reinterpret_cast<f16x8 *>(p.k_pool + panel + 8 * q) = kst[kr * pieces + 4 * (q >> 6) + (q & 3)];
             const int vq = q / qpd, d0 = 2 * (q - vq * qpd);
+            if (4 * vq + 3 >= a && 4 * vq < e) {
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {  // element x: dim d0 + x / 4 of row 4 * vq + x % 4
-                const int vr = 4 * vq + (x & 3);
-                if (vr >= a && vr < e)
-                    vc[it][x] = vsh[vr * p.D + d0 + (x >> 2)];
+                for (int x = 0; x < 8; ++x) {  // element x: dim d0 + x / 4 of row 4 * vq + x % 4
+                    const int vr = 4 * vq + (x & 3);
+                    if (vr >= a && vr < e)
+                        vc[it][x] = vsh[vr * p.D + d0 + (x >> 2)];
+                }
+                *reinterpret_cast<f16x8 *>(p.v_pool + panel + 8 * q) = vc[it];
             }
-            *reinterpret_cast<f16x8 *>(p.v_pool + panel + 8 * q) = vc[it];
         }
     }
 }
