@@ -26,15 +26,16 @@
 //     lives in one lane.  The sum of squares is reduced across the group's lanes on the VALU (DPP row rotations,
 //     and a v_permlane16_swap for 32-lane groups);
 //   * q goes straight to q_out (8-byte stores, coalesced per half head row).  The unit's new K and V rows are
-//     staged in LDS row-major (padded rows); each thread then writes 16-byte chunks of the two panels (each put in
-//     its panel order on the way), taking rows outside the new range from the old panel, which it loaded at the
-//     start (so that load overlaps everything else).  The pools thus see only whole 16-byte chunks of whole panels -- scattered 2-byte V stores and
-//     16-byte K row pieces cost far more at the memory than their bytes;
+//     staged in LDS row-major (padded rows); each thread then writes 16-byte chunks of the panels (each put in its
+//     panel order on the way): the new rows' K runs (64 bytes per row and 32-dim piece), and the V quads of 4 rows
+//     that hold new rows, whole 128-byte lines whose old rows come from the quad as loaded at the start (so that
+//     load overlaps everything else).  The pools thus see whole sectors and lines only -- scattered 2-byte V stores
+//     cost far more at the memory than their bytes -- and nothing that holds no new row is rewritten;
 //   * decode mode (decode_lens set): slot g is sequence g, whose one new token sits at row decode_lens[g] - 1 --
 //     the QKV half of the decode step from QKV rows when it runs as two launches.
 //
-// A unit's other rows are rewritten with their own values: no other work may write the panel meanwhile (the
-// block holding a sequence's new rows belongs to that sequence alone).
+// The other rows of a quad that holds new rows are rewritten with their own values: no other work may write the
+// panel meanwhile (the block holding a sequence's new rows belongs to that sequence alone).
 //
 // All HIP code here is built with packed-fp32 instructions disabled.
 
@@ -271,15 +272,19 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
     int64_t panel = -1;  // the unit's panel (element offset of its first half) in both pools
     if (in_table && blk >= 0 && blk < p.N)
         panel = (((int64_t)blk * p.Hkv + h) * p.BS + ((int)w.lo % p.BS - w.r0)) * D;
+    // Only the new rows are written: their K runs, and the V quads (4 rows, whole 128-byte lines) that hold them; a
+    // quad that also holds old rows is read here and written back with those unchanged.
     const bool keep_old = panel >= 0 && !whole;
-    const __amdgpu_buffer_rsrc_t ok_r = rsrc(keep_old ? p.k_pool + panel : p.k_pool, keep_old && has_k ? 32 * D : 0);
+    auto quad_new = [&](int q) {  // V chunk q's quad of rows holds a new row
+        const int vr = 4 * (q / (D / 2));
+        return vr + 3 >= w.r0 && vr < w.r0 + w.rows;
+    };
     const __amdgpu_buffer_rsrc_t ov_r = rsrc(keep_old ? p.v_pool + panel : p.v_pool, keep_old && has_v ? 32 * D : 0);
-    h8 ok[CPT], ov[CPT];
+    h8 ov[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const int q = tid + kThreads * c;
-        const uint32_t off = q < CHUNKS ? (uint32_t)(16 * q) : kPast;
-        ok[c] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(ok_r, off, 0, 0));
+        const uint32_t off = q < CHUNKS && quad_new(q) ? (uint32_t)(16 * q) : kPast;
         ov[c] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(ov_r, off, 0, 0));
     }
 #pragma unroll
@@ -364,11 +369,11 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
         if (has_k) {
             // K panel [D/32][16][32], chunk q: dims 8 * (4 * (q / 64) + q % 4) .. +8 of row (q / 4) % 16
             const int kr = (q >> 2) & 15;
-            const h8 kn = *reinterpret_cast<const h8 *>(sk + kr * KS + 8 * (4 * (q >> 6) + (q & 3)));
-            const bool knew = whole || (kr >= w.r0 && kr < w.r0 + w.rows);
-            *reinterpret_cast<h8 *>(p.k_pool + panel + 8 * q) = knew ? kn : ok[c];
+            if (whole || (kr >= w.r0 && kr < w.r0 + w.rows))
+                *reinterpret_cast<h8 *>(p.k_pool + panel + 8 * q) =
+                    *reinterpret_cast<const h8 *>(sk + kr * KS + 8 * (4 * (q >> 6) + (q & 3)));
         }
-        if (has_v) {
+        if (has_v && (whole || quad_new(q))) {
             // V panel [4][D][4], chunk q: dims d0 = 2 * (q % (D/2)) and d0 + 1 of quad q / (D/2); element x is dim
             // d0 + x / 4 of row 4 * (q / (D/2)) + x % 4
             const int vq = q / (D / 2), d0 = 2 * (q % (D / 2));
