@@ -393,8 +393,8 @@ PKV_API int pkv_paged_varlen_attention(const uint16_t *q, const uint16_t *k_pool
  *   Launches: one pass with max_q_len <= 32 and no more workgroups than the
  *   device's CUs gives one launch whose workgroups write the new rows
  *   themselves (the new rows' K runs and the V lines of their quads of rows,
- *   other rows unchanged); otherwise a launch writes the new rows (as whole
- *   panels, and with a grid of more workgroups than CUs it ranks
+ *   other rows unchanged); otherwise a launch writes the new rows (the same
+ *   runs and quads, and with a grid of more workgroups than CUs it ranks
  *   the sequences for the attention launch's dispatch order), then attention
  *   runs.  Results are identical either way.
  *   k_new, v_new: [total_q_tokens][Hkv][D] fp16, 16-byte aligned.
