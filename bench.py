@@ -294,6 +294,110 @@ def cpu_baseline(case, seconds: float, window: int = 0):
                                         el, reps / el)}
 
 
+def floor_tiles(case, window: int, splits: int, varlen: bool, cus: int):
+    """The decode launch's tiles for the stream-read floor: (bytes read, bytes written) per workgroup in the order the
+    launch dispatches them -- one per (sequence, kv head) (times the splits of a fixed split count), the sequences
+    longest first when the grid has more workgroups than CUs, and then the longest split into pieces by the library's
+    rule (at least 1024 rows, else all rows x kv heads / CUs rounded up to 64; rows per piece rounded up to 64)."""
+    D, Hkv, G = case.D, case.Hkv, case.Hq // case.Hkv
+    if varlen:
+        rows = np.asarray(case.pos_offsets, np.int64) + np.diff(np.asarray(case.cu_seqlens_q, np.int64))
+        outs = np.diff(np.asarray(case.cu_seqlens_q, np.int64)) * G * D * 2
+    else:
+        rows = np.asarray(case.context_lens, np.int64)
+        rows = np.minimum(rows, window) if window > 0 else rows
+        outs = np.full(len(rows), G * D * 2, np.int64)
+    tiles = []  # (rows, out bytes) per (sequence or piece, kv head) in dispatch order
+    seqs = list(range(len(rows)))
+    multi = len(rows) * Hkv * max(1, splits) > cus
+    if multi:
+        seqs.sort(key=lambda i: (-rows[i], i))
+    C = None
+    if multi and splits <= 1 and window <= 0 and not varlen:
+        fair = (int(rows.sum()) * Hkv + cus - 1) // cus
+        C = max(1024, (fair + 63) // 64 * 64)
+    for i in seqs:
+        parts = [int(rows[i])]
+        if C is not None and rows[i] > C:
+            n = -(-int(rows[i]) // C)
+            pr = (-(-int(rows[i]) // n) + 63) // 64 * 64
+            k = -(-int(rows[i]) // pr)
+            parts = [pr] * (k - 1) + [int(rows[i]) - pr * (k - 1)]
+        elif splits > 1:
+            ch = -(-int(rows[i]) // splits)
+            parts = [max(0, min(ch, int(rows[i]) - j * ch)) for j in range(splits)]
+        for part in parts:
+            tiles.extend([(part * D * 4, int(outs[i]))] * Hkv)
+    return tiles
+
+
+def run_floor(args) -> int:
+    """bench.py --floor: time the stream-read probe (libpkvprobe.so) on the workload's exact tiles."""
+    import ctypes
+    import torch
+    from paged_kv_decode_04_amd import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_decode_04_amd", "libpkvprobe.so"))
+    lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    desc, default_splits, default_rot = WORKLOADS[args.config]
+    splits = default_splits if args.splits is None else args.splits
+    R = default_rot if args.rotations is None else args.rotations
+    varlen = args.config in W.VARLEN_CONFIGS
+    window = WINDOWS.get(args.config, 0)
+    if args.config in W.QKV_CONFIGS:
+        print("--floor covers the decode and varlen workloads", file=sys.stderr)
+        return 2
+    sets, total_read, total_written = [], 0, 0
+    for r in range(R):
+        if varlen:
+            c = W.VARLEN_CONFIGS[args.config](rotation=r)
+        elif window:
+            c = W.config_c2(rotation=r, with_pools=False)
+        else:
+            c = W.CONFIGS[args.config](rotation=r, with_pools=False)
+        tiles = floor_tiles(c, window, splits, varlen, cus)
+        len16 = np.array([(b + 15) // 16 for b, _ in tiles], np.int64)
+        off16 = np.concatenate([[0], np.cumsum(len16)[:-1]]).astype(np.int64)
+        wb = (max(o for _, o in tiles) + 15) // 16 * 16
+        x = torch.empty(int(len16.sum()) * 8 + 8, dtype=torch.float16, device=dev).normal_()
+        y = torch.empty(len(tiles) * wb // 2 + 8, dtype=torch.float16, device=dev)
+        sets.append((x, torch.from_numpy(off16).to(dev), torch.from_numpy(len16.astype(np.int32)).to(dev), y,
+                     len(tiles), wb))
+        total_read += int(len16.sum()) * 16
+        total_written += sum(o for _, o in tiles)
+        del c
+    st = torch.cuda.current_stream().cuda_stream
+    call = lambda k: lib.pkv_probe_stream_read(sets[k % R][0].data_ptr(), sets[k % R][0].numel() * 2,
+                                               sets[k % R][1].data_ptr(), sets[k % R][2].data_ptr(),
+                                               sets[k % R][3].data_ptr(), sets[k % R][4], sets[k % R][5], st)
+    for k in range(args.warmup):
+        if call(k) != 0:
+            print("probe launch failed", file=sys.stderr)
+            return 1
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(args.steps):
+        call(k)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    mb = total_read / R / 1e6
+    print(json.dumps({"floor": {"config": args.config, "probe": "pkv_probe_stream_read: one 512-thread workgroup "
+                                "per tile in dispatch order, contiguous non-temporal reads of the tile's K/V bytes, "
+                                "then its output bytes written", "workgroups": sets[0][4], "rotations": R,
+                                "us_per_launch": round(us, 2), "read_MB": round(mb, 2),
+                                "written_MB": round(total_written / R / 1e6, 3),
+                                "GBs": round(mb * 1e3 / us, 1), "frac_of_8TBs": round(mb / us / 8e6 * 1e6, 4)}}))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +419,9 @@ def main(argv=None) -> int:
                     help="append and attention as two launches instead of the library's step entry point")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph holding 32 consecutive steps instead of eager launches")
+    ap.add_argument("--floor", action="store_true",
+                    help="time the stream-read probe on the workload's exact tiles instead (the floor a decode "
+                         "kernel with one workgroup per tile cannot beat)")
     args = ap.parse_args(argv)
 
     if args.summarize_counters:
@@ -344,6 +451,9 @@ def main(argv=None) -> int:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
         return 0
+
+    if args.floor:
+        return run_floor(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

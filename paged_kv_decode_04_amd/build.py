@@ -26,6 +26,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = ["pkv_kernels.hip", "pkv_qkv.hip", "pkv_check.hip", "pkv_geometry.hip", "pkv_api.hip"]
+# the measurement probe (not part of the attention path): its own library, libpkvprobe.so
+PROBE_SRC = os.path.join(PKG, "probe", "pkv_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libpkvprobe.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -48,7 +51,7 @@ def _run(cmd):
 
 def _check_asm(src: str, tmp: str) -> None:
     """Compile one source to gfx950 assembly and fail on packed-FP32 arithmetic or scratch use."""
-    asm = os.path.join(tmp, src + ".s")
+    asm = os.path.join(tmp, os.path.basename(src) + ".s")
     _run([HIPCC] + COMMON + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
     with open(asm) as f:
         scan_asm(src, f.read())
@@ -95,15 +98,19 @@ def build(verbose: bool = False) -> str:
         objs = [os.path.join(tmp, src + ".o") for src in SOURCES]
         compiles = [pool.submit(_run, [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj])
                     for src, obj in zip(SOURCES, objs)]
-        checks = [pool.submit(_check_asm, src, tmp) for src in SOURCES]
+        checks = [pool.submit(_check_asm, src, tmp) for src in SOURCES + [PROBE_SRC]]
+        probe_tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+        probe = pool.submit(_run, [HIPCC] + COMMON + ["-shared", PROBE_SRC, "-o", probe_tmp])
         out = "\n".join(f.result() for f in compiles)
         lib_tmp = LIB + ".tmp%d" % os.getpid()
         out += _run([HIPCC, "--offload-arch=" + ARCH, "-fPIC", "-shared", "-o", lib_tmp] + objs)
+        out += probe.result()
         for f in checks:
             f.result()
     if verbose and out.strip():
         print(out)
     os.replace(lib_tmp, LIB)
+    os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 

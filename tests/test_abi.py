@@ -244,3 +244,23 @@ def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(pkv, "_lib", None)
     with pytest.raises(pkv.PkvError):
         pkv.load(str(tmp_path / "missing.so"))
+
+
+def test_probe_library_exports_the_probe_and_rejects_bad_arguments():
+    """libpkvprobe.so (the stream-read floor probe beside the library) exports what include/pkv_probe.h declares and
+    refuses bad arguments before launching anything (no device needed for these)."""
+    path = os.path.join(ROOT, "paged_kv_decode_04_amd", "libpkvprobe.so")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pkv_probe.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+    assert declared == ["pkv_probe_stream_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", path], stdout=subprocess.PIPE, text=True, check=True).stdout
+    assert set(re.findall(r"\bT (pkv_\w+)", out)) == set(declared)
+    lib = ctypes.CDLL(path)
+    f = lib.pkv_probe_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32,
+                                                                             ctypes.c_void_p]
+    assert f(None, 0, None, None, None, 0, 0, None) == 0  # nothing to do
+    assert f(None, 0, None, None, None, -1, 0, None) == 1  # negative count
+    assert f(None, 0, None, None, None, 4, 12, None) == 1  # write size not a multiple of 16
+    assert f(None, -16, None, None, None, 4, 0, None) == 1  # negative size
+    assert f(None, 0, None, None, None, 4, 0, None) == 1  # null buffers

@@ -96,3 +96,40 @@ def test_slot_checks(torch_cuda):
     slots[[300, 650]] = cap
     assert run(slots) == [0, 0, 300, 2]                           # several workgroups
     say("slot checks: ok")
+
+
+@pytest.mark.gpu
+def test_stream_read_probe_reads_every_run_and_writes_its_outputs():
+    """The floor probe (libpkvprobe.so): output chunk j of a workgroup carries the XOR of the words of the chunks its
+    thread j read (chunks j, j + 512, ... of the run) and the index j, so a wrong offset or a dropped load shows."""
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ctypes, os
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                   "paged_kv_decode_04_amd", "libpkvprobe.so"))
+    f = lib.pkv_probe_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32,
+                                                                             ctypes.c_void_p]
+    rng = np.random.default_rng(5)
+    len16 = np.array([0, 1, 7, 4096, 5000, 33], np.int64)
+    off16 = np.concatenate([[0], np.cumsum(len16)[:-1]]).astype(np.int64)
+    words = rng.integers(0, 2**32, size=int(len16.sum()) * 4, dtype=np.uint64).astype(np.uint32)
+    x = torch.from_numpy(words.view(np.int32)).cuda()
+    y = torch.zeros(len(len16) * 64 // 4, dtype=torch.int32, device="cuda")  # 64 bytes per workgroup
+    # every device buffer stays referenced until the launch is done (a temporary's block could be handed to the
+    # next allocation before the kernel reads it)
+    off_d = torch.from_numpy(off16).cuda()
+    len_d = torch.from_numpy(len16.astype(np.int32)).cuda()
+    assert off_d.data_ptr() != len_d.data_ptr()
+    rc = f(x.data_ptr(), x.numel() * 4, off_d.data_ptr(), len_d.data_ptr(), y.data_ptr(), len(len16), 64,
+           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    got = y.cpu().numpy().view(np.uint32).reshape(len(len16), 4, 4)
+    for g in range(len(len16)):
+        run = words[off16[g] * 4:(off16[g] + len16[g]) * 4].reshape(-1, 4)
+        for j in range(4):
+            mine = run[j::512]
+            acc = np.bitwise_xor.reduce(mine.reshape(-1)) if mine.size else np.uint32(0)
+            assert got[g, j, 0] == acc and got[g, j, 1] == acc ^ 1 and got[g, j, 2] == acc ^ 2 and got[g, j, 3] == j
