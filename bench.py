@@ -420,8 +420,8 @@ def main(argv=None) -> int:
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph holding 32 consecutive steps instead of eager launches")
     ap.add_argument("--floor", action="store_true",
-                    help="time the stream-read probe on the workload's exact tiles instead (the floor a decode "
-                         "kernel with one workgroup per tile cannot beat)")
+                    help="time the stream-read probe on the workload's exact tiles instead (the plainest kernel "
+                         "with one workgroup per tile: a reference for the decode launch)")
     args = ap.parse_args(argv)
 
     if args.summarize_counters:

@@ -5,8 +5,8 @@
  * dispatches its tiles) reads its own contiguous run of 16-byte chunks x[off16[g] .. off16[g] + len16[g]) (clamped
  * into the x_bytes of x)
  * (non-temporal loads, eight in flight per thread) and then writes write_bytes of y at y + g * write_bytes.
- * bench.py --floor times it on a workload's exact tile sizes: a decode kernel with one workgroup per tile cannot run
- * faster.
+ * bench.py --floor times it on a workload's exact tile sizes: what the plainest kernel with one workgroup per tile
+ * takes, a reference for the decode launch (not a bound: pipelined waves can keep more bytes in flight).
  *   x: device, 16-byte aligned, x_bytes long; off16: device, [groups] int64 chunk offsets; len16: device,
  *   [groups] int32 chunk counts (negative reads as 0); y: device, 16-byte aligned, groups * write_bytes bytes (may be
  *   null when write_bytes is 0);

@@ -3,8 +3,9 @@
 // launch dispatches its tiles) streams its own contiguous slice of x -- len16[g] 16-byte chunks from chunk off16[g],
 // eight of them in flight per thread, non-temporal -- and, if write_bytes > 0, writes that many bytes of y at its end
 // (the tile's output), so
-// bench.py can time what the tiles' sizes alone cost on this GPU: the floor a decode kernel with that decomposition
-// cannot beat.  Built into its own library (libpkvprobe.so); all HIP code here is built with packed-fp32
+// bench.py can time what the tiles' sizes alone cost on this GPU with the plainest kernel of that decomposition (a
+// reference, not a bound: eight pipelined waves per tile keep more bytes in flight on long tiles than its one
+// pass).  Built into its own library (libpkvprobe.so); all HIP code here is built with packed-fp32
 // instructions disabled.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
