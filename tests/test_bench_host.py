@@ -80,3 +80,28 @@ def test_counter_summary_scales_by_the_copy_kernel(tmp_path):
     k = rec["kernels"]["pkv::decode_kernel<128, 16, 8, false, true, false, false>"]
     assert k["fetch_bytes"] == 100000 * 1024 * 2 and k["write_bytes"] == 2000 * 1024 and k["dispatches"] == 2
     assert rec["hbm_bytes_per_step"] == 100000 * 1024 * 2 + 2000 * 1024  # the append is not counted
+
+
+def test_floor_tiles_follow_the_launch_decomposition():
+    """bench.py --floor's tiles: one per (sequence, kv head) in id order for one round of CUs, longest first with the
+    pieces rule for more (c4's 16384-row sequence in two pieces of 8192 rows), fixed splits for c3; every tile reads
+    its rows' K and V (D * 4 bytes a row) and writes G * D * 2 bytes."""
+    import numpy as np
+    from paged_kv_decode_04_amd import workloads as W
+    c = W.config_c2(with_pools=False)
+    t = bench.floor_tiles(c, 0, 1, False, 256)
+    assert len(t) == 32 * 8
+    assert [b for b, _ in t[:8]] == [int(c.context_lens[0]) * 128 * 4] * 8  # id order: sequence 0's heads first
+    assert sum(b for b, _ in t) == int(c.context_lens.sum()) * 8 * 128 * 4 and {o for _, o in t} == {4 * 128 * 2}
+    c = W.config_c4(with_pools=False)
+    t = bench.floor_tiles(c, 0, 1, False, 256)
+    L = np.sort(c.context_lens)[::-1]
+    assert L[0] == 16384 and len(t) == (256 + 1) * 8
+    assert [b for b, _ in t[:16]] == [8192 * 512] * 16  # the two pieces of the longest sequence lead
+    assert sum(b for b, _ in t) == int(c.context_lens.sum()) * 8 * 512
+    assert all(t[i][0] >= t[i + 8][0] for i in range(16, len(t) - 8, 8))  # longest first after them
+    c = W.config_c3(with_pools=False)
+    t = bench.floor_tiles(c, 0, 8, False, 256)
+    assert len(t) == 4 * 8 * 8 and {b for b, _ in t} == {32768 // 8 * 512}
+    t = bench.floor_tiles(W.config_c2(with_pools=False), 512, 1, False, 256)
+    assert {b for b, _ in t} == {512 * 512}  # a window of 512 rows
