@@ -452,14 +452,13 @@ def main(argv=None) -> int:
         print(json.dumps(rec))
         return 0
 
-    if args.floor:
-        return run_floor(args)
-
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only (the decode-attention hot path has no cross-GPU "
               "exchange); run with --gpus 1", file=sys.stderr)
         return 2
+    if args.floor:
+        return run_floor(args)
 
     import torch
     from paged_kv_decode_04_amd import pkv
