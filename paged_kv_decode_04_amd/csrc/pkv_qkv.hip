@@ -260,8 +260,10 @@ __global__ __launch_bounds__(kThreads) void qkv_cache_kernel(QkvParams p) {
         source(idx, rr, hs, piece);
         const int head = hs < p.G ? h * p.G + hs : (hs == p.G ? p.Hq + h : p.Hq + p.Hkv + h);
         const uint32_t off = idx < lanes ? (uint32_t)(2 * (rr * width + head * D + 4 * piece)) : kPast;
-        const h4 a = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(qkv_r, off, 0, 0));
-        const h4 b = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(qkv_r, off, 2 * HALF, 0));
+        // the QKV rows are read once: non-temporal, as the attention kernels stream K and V (r2: 15.16 -> 14.61 us)
+        const h4 a = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(qkv_r, off, 0, kKvLoadPolicy));
+        const h4 b = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(qkv_r, off, 2 * HALF,
+                                                                                 kKvLoadPolicy));
         return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     };
     h8 raw[kBatch];
